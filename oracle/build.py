@@ -1,0 +1,28 @@
+"""Builds ``liboracle.so`` from ``kda_oracle.c`` with gcc (plain C, OpenMP, fp64).
+
+Test infrastructure: the GPU library never links this.
+"""
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def oracle_lib_path() -> str:
+    return _LIB
+
+
+def build_oracle(verbose: bool = False) -> str:
+    """Compile the oracle. FP contraction is off so the arithmetic is the plain
+    sequence of fp64 multiplies and adds written in the source."""
+    cmd = [
+        "gcc", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math",
+        "-fopenmp", "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB

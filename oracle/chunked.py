@@ -1,0 +1,183 @@
+"""Chunkwise (WY / UT transform) form of the KDA recurrence -- test infrastructure.
+
+These functions pin the algebra the GPU kernels implement against the
+sequential oracle on the CPU. They share no code with the GPU library.
+
+Chunking follows "From GPT-2 to Kimi K3" digest, section "DeltaNet 병렬화 --
+청크 단위 학습" (split T into chunks of C; in-chunk work is masked attention, the
+rest is carried by the state), and the GeekNews "Kimi Linear" summary, section
+"청크 단위 병렬 알고리듬": a WY representation packs the chunk's rank-one updates,
+the UT transform applies (I + A)^{-1}, and the lower-triangular inverse is found
+row by row by forward substitution.
+
+Per chunk (rows r, s; g_r = sum_{j<=r} log_alpha_j per channel; S_0 the state
+entering the chunk):
+    A_rs = beta_r sum_c k_rc k_sc e^{g_rc - g_sc}              (s < r)
+    T    = (I + A)^{-1}
+    W    = T diag(beta) (K * e^G) ,  U = T diag(beta) V
+    U~   = U - W S_0
+    P_rs = sum_c q_rc k_sc e^{g_rc - g_sc}                      (s <= r)
+    O    = (Q * e^G) S_0 + P U~
+    S_C  = Diag(e^{g_C}) S_0 + (K * e^{g_C - G})^T U~
+Derivation: write S_t = Diag(alpha_t) S_{t-1} + k_t u_t^T with
+u_t = beta_t (v_t - (Diag(alpha_t) S_{t-1})^T k_t); unrolling inside the chunk gives
+(I + A) U~ = diag(beta) (V - (K * e^G) S_0).
+"""
+import numpy as np
+
+LOG2E = 1.4426950408889634
+
+
+def forward_substitution_inverse(A):
+    """T = (I + A)^{-1} for strictly lower-triangular A, one row at a time:
+    T_r = e_r - sum_{s<r} A_rs T_s (Gaussian elimination, forward substitution)."""
+    C = A.shape[0]
+    T = np.zeros_like(A)
+    for r in range(C):
+        row = np.zeros(C, dtype=A.dtype)
+        row[r] = 1.0
+        for s in range(r):
+            row = row - A[r, s] * T[s]
+        T[r] = row
+    return T
+
+
+def chunk_step(q, k, v, log_alpha, beta, S0):
+    """One chunk of the plain chunked form in fp64 with e^{+-G} taken directly.
+    q, k, log_alpha: [C, dk]; v: [C, dv]; beta: [C]; S0: [dk, dv]."""
+    g = np.cumsum(log_alpha, axis=0)
+    C = q.shape[0]
+    Kp, Km = k * np.exp(g), k * np.exp(-g)
+    A = np.tril(beta[:, None] * (Kp @ Km.T), -1)
+    T = forward_substitution_inverse(A)
+    W = T @ (beta[:, None] * Kp)
+    U = T @ (beta[:, None] * v)
+    Ut = U - W @ S0
+    P = np.tril((q * np.exp(g)) @ Km.T)
+    O = (q * np.exp(g)) @ S0 + P @ Ut
+    gC = g[C - 1]
+    S = np.exp(gC)[:, None] * S0 + (k * np.exp(gC[None, :] - g)).T @ Ut
+    return O, S
+
+
+def forward(q, k, v, log_alpha, beta, S0=None, chunk=64, step=chunk_step):
+    """Chunked fp64 KDA for one sequence of one head. The last chunk may be
+    partial. q, k, log_alpha: [T, dk]; v: [T, dv]; beta: [T]."""
+    q, k, v, log_alpha, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, log_alpha, beta))
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        o[t0:t1], S = step(q[t0:t1], k[t0:t1], v[t0:t1], log_alpha[t0:t1], beta[t0:t1], S)
+    return o, S
+
+
+# ---------------------------------------------------------------------------
+# In-chunk decay factoring with a fallback, emulated on the CPU.
+#
+# e^{g_r - g_s} with g_r - g_s <= 0 is always safe, but the matmul form splits it
+# into e^{g_r} * e^{-g_s}, which overflows for fast decays (the GeekNews summary,
+# section "일반 DPLR보다 줄어든 연산량", notes that fine-grained decay makes in-chunk
+# division numerically delicate; GLA handles it with log-space, full-precision
+# secondary chunking). The scheme here works in log2 units, splits the chunk into
+# sub-chunks of `sub` rows, and chooses reference points so that no factor can
+# overflow:
+#   b_0 = 0, b_I = gh[sub*I - 1]  (gh = log2-domain cumsum, b at each sub-chunk's top)
+#   plus_r  = 2^(gh_r - b_I)      (r in sub-chunk I)      in (0, 1]
+#   minus_s = 2^(b_{J+1} - gh_s)  (s in sub-chunk J)      in (0, 1]
+#   off-diagonal I > J: 2^(gh_r - gh_s) = [plus_r 2^(b_I - b_{J+1})] * minus_s   (both <= 1)
+#   diagonal I:         2^(gh_r - gh_s) = [plus_r 2^(R_I/2)] * [minus_s 2^(R_I/2)],
+#                       R_I = b_I - b_{I+1} per channel; both factors in [2^-R/2, 2^R/2]
+#   when max_c R_I > threshold the diagonal block falls back to 2^(gh_r - gh_s)
+#   element by element (exponent <= 0). Masked entries are discarded by selection.
+#   Q~ = q * plus * 2^(b_I);  K~ = k * plus * 2^(b_I);  K~end_s = k_s * minus_s * 2^(b_n - b_{J+1});
+#   gamma = 2^(b_n).
+# ---------------------------------------------------------------------------
+
+def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.float64):
+    """Forms A, P, Q~, K~, K~end, gamma of one chunk with the factored scheme, in
+    ``dtype`` arithmetic. Returns a dict with those and ``fallback`` (list of the
+    diagonal sub-blocks that took the element-wise path)."""
+    f = np.dtype(dtype).type
+    C, dk = q.shape
+    n_sub = (C + sub - 1) // sub
+    la2 = (np.asarray(log_alpha, dtype=np.float64) * LOG2E).astype(dtype)
+    gh = np.cumsum(la2, axis=0, dtype=dtype)
+    b = np.zeros((n_sub + 1, dk), dtype=dtype)
+    for I in range(1, n_sub + 1):
+        b[I] = gh[min(sub * I, C) - 1]
+    q = np.asarray(q, dtype=dtype)
+    k = np.asarray(k, dtype=dtype)
+    beta = np.asarray(beta, dtype=dtype)
+    plus = np.zeros((C, dk), dtype=dtype)
+    minus = np.zeros((C, dk), dtype=dtype)
+    for r in range(C):
+        I = r // sub
+        plus[r] = np.exp2(gh[r] - b[I])
+        minus[r] = np.exp2(b[I + 1] - gh[r])
+    A = np.zeros((C, C), dtype=dtype)
+    P = np.zeros((C, C), dtype=dtype)
+    fallback = []
+    with np.errstate(over="raise", invalid="raise"):
+        for I in range(n_sub):
+            rI = slice(sub * I, min(C, sub * (I + 1)))
+            for J in range(I + 1):
+                sJ = slice(sub * J, min(C, sub * (J + 1)))
+                if J < I:
+                    sc = np.exp2(b[I] - b[J + 1])
+                    lhs_k = k[rI] * plus[rI] * sc
+                    lhs_q = q[rI] * plus[rI] * sc
+                    rhs = k[sJ] * minus[sJ]
+                    A[rI, sJ] = lhs_k @ rhs.T
+                    P[rI, sJ] = lhs_q @ rhs.T
+                else:
+                    R = b[I] - b[I + 1]
+                    if np.max(R) <= threshold:
+                        half = np.exp2(R * f(0.5))
+                        lhs_k = k[rI] * plus[rI] * half
+                        lhs_q = q[rI] * plus[rI] * half
+                        rhs = k[sJ] * minus[sJ] * half
+                        blkA = lhs_k @ rhs.T
+                        blkP = lhs_q @ rhs.T
+                    else:
+                        fallback.append(I)
+                        rows = range(rI.start, rI.stop)
+                        cols = range(sJ.start, sJ.stop)
+                        blkA = np.zeros((len(rows), len(cols)), dtype=dtype)
+                        blkP = np.zeros_like(blkA)
+                        for a, r in enumerate(rows):
+                            for c, s in enumerate(cols):
+                                if s <= r:
+                                    e = np.exp2(gh[r] - gh[s])
+                                    blkA[a, c] = np.sum(k[r] * k[s] * e)
+                                    blkP[a, c] = np.sum(q[r] * k[s] * e)
+                    n = blkA.shape[0]
+                    A[rI, sJ] = np.where(np.tril(np.ones((n, n), bool), -1), blkA, 0)
+                    P[rI, sJ] = np.where(np.tril(np.ones((n, n), bool), 0), blkP, 0)
+        A = beta[:, None] * A
+        blk_of = np.arange(C) // sub
+        top = b[blk_of]
+        Qt = q * plus * np.exp2(top)
+        Kt = k * plus * np.exp2(top)
+        Kend = k * minus * np.exp2(b[n_sub][None, :] - b[blk_of + 1])
+        gamma = np.exp2(b[n_sub])
+    return dict(A=A, P=P, Qt=Qt, Kt=Kt, Kend=Kend, gamma=gamma, fallback=fallback)
+
+
+def factored_chunk_step(q, k, v, log_alpha, beta, S0, sub=16, threshold=120.0):
+    """A chunk step in which every decay factor comes from the factored scheme."""
+    op = factored_operands(q, k, log_alpha, beta, sub=sub, threshold=threshold)
+    T = forward_substitution_inverse(op["A"])
+    W = T @ (beta[:, None] * op["Kt"])
+    U = T @ (beta[:, None] * v)
+    Ut = U - W @ S0
+    O = op["Qt"] @ S0 + op["P"] @ Ut
+    S = op["gamma"][:, None] * S0 + op["Kend"].T @ Ut
+    return O, S
+
+
+def factored_forward(q, k, v, log_alpha, beta, S0=None, chunk=64, sub=16, threshold=120.0):
+    return forward(q, k, v, log_alpha, beta, S0, chunk,
+                   step=lambda *a: factored_chunk_step(*a, sub=sub, threshold=threshold))

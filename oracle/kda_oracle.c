@@ -1,0 +1,186 @@
+/*
+ * Oracle for the Kimi Delta Attention (KDA) recurrence -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, sequential fp64 definition that the GPU path is
+ * checked against. It shares no code with the GPU library. Only the tests, the
+ * smoke check and the bench's CPU-baseline leg may load it.
+ *
+ * What it computes, per sequence n and head h, token by token:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T ,   o_t = S_t^T q_t
+ *
+ * with S in R^{dk x dv} (row i = key channel, column j = value channel),
+ * alpha_t = exp(log_alpha_t) one decay per key channel, beta_t one scalar per
+ * (token, head). Sources:
+ *   - "From GPT-2 to Kimi K3" digest, section "DeltaNet -- 유한한 캐시의 덮어쓰기":
+ *     the delta rule reads what the current key retrieves, subtracts it from the
+ *     new value and writes the difference back along the key.
+ *   - same digest, section "Gated DeltaNet -- 망각을 더하다": a data-dependent
+ *     decay alpha in [0,1] on the previous state; alpha = 1 is the pure delta rule.
+ *   - same digest, section "Kimi Linear (KDA) -- 채널별 세밀한 게이팅", and the
+ *     GeekNews "Kimi Linear" summary, section "Kimi Delta Attention의 세밀한 메모리
+ *     제어": the scalar decay becomes a per-channel diagonal Diag(alpha).
+ *   - GeekNews "Kimi Linear" summary, section "선형 어텐션에서 Gated DeltaNet까지":
+ *     the rank-one update is a generalised Householder transform.
+ *
+ * The rank-one form used below is the same map written without the dk x dk
+ * matrix:  S' = Diag(alpha) S ;  e = v - S'^T k ;  S = S' + beta k e^T ;  o = S^T q.
+ * (Expand (I - beta k k^T) S' + beta k v^T = S' + beta k (v - S'^T k)^T.)
+ * The output reads the state after the update of its own token.
+ *
+ * Value columns of S evolve independently (column j only ever reads column j),
+ * so the work is split over (sequence, head, column block) with OpenMP; no
+ * floating-point operation is reordered by the split, so the result is bitwise
+ * identical for any thread count.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, k, log_alpha : [T_total][H][dk]   float32 (carries bf16 or fp32 values exactly)
+ *   v               : [T_total][H][dv]   float32
+ *   beta            : [T_total][H]       float32
+ *   seq_starts      : [num_seqs + 1]     int64, sequence n = rows [seq_starts[n], seq_starts[n+1])
+ *   initial_state   : [num_seqs][H][dk][dv] float64, or NULL for zeros
+ * Outputs are written only for the selected heads and the value columns
+ * [col_begin, col_end), compactly:
+ *   o_sel     : [T_total][n_heads_sel][ncols]          float64 (may be NULL)
+ *   final_sel : [num_seqs][n_heads_sel][dk][ncols]     float64 (may be NULL)
+ * heads == NULL selects all H heads in order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_COL_BLOCK 16
+
+int kda_oracle_abi_version(void) { return 1; }
+
+int kda_oracle_forward(const float *q, const float *k, const float *v,
+                       const float *log_alpha, const float *beta,
+                       const double *initial_state, const int64_t *seq_starts,
+                       int num_seqs, int H, int dk, int dv, const int *heads,
+                       int n_heads_sel, int col_begin, int col_end,
+                       double *o_sel, double *final_sel, int num_threads) {
+  if (!q || !k || !v || !log_alpha || !beta || !seq_starts) return -1;
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (col_begin < 0 || col_end > dv || col_begin > col_end) return -1;
+  if (heads == NULL) n_heads_sel = H;
+  if (n_heads_sel <= 0) return -1;
+  for (int n = 0; n < num_seqs; ++n)
+    if (seq_starts[n + 1] < seq_starts[n]) return -1;
+  const int ncols = col_end - col_begin;
+  if (ncols == 0 || num_seqs == 0) return 0;
+  const int nblk = (ncols + ORACLE_COL_BLOCK - 1) / ORACLE_COL_BLOCK;
+  const long long ntask = (long long)num_seqs * n_heads_sel * nblk;
+
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (long long task = 0; task < ntask; ++task) {
+    const int blk = (int)(task % nblk);
+    const int hs = (int)((task / nblk) % n_heads_sel);
+    const int n = (int)(task / ((long long)nblk * n_heads_sel));
+    const int h = heads ? heads[hs] : hs;
+    const int c0 = col_begin + blk * ORACLE_COL_BLOCK;
+    const int c1 = (c0 + ORACLE_COL_BLOCK < col_end) ? c0 + ORACLE_COL_BLOCK : col_end;
+    const int w = c1 - c0;
+
+    double *S = (double *)malloc(sizeof(double) * (size_t)dk * w);
+    double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+    double e[ORACLE_COL_BLOCK];
+
+    /* S_0: the given initial state, or zeros */
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < w; ++j)
+        S[(size_t)i * w + j] =
+            initial_state
+                ? initial_state[(((size_t)n * H + h) * dk + i) * dv + (c0 + j)]
+                : 0.0;
+
+    for (int64_t t = seq_starts[n]; t < seq_starts[n + 1]; ++t) {
+      const size_t rk = ((size_t)t * H + h) * dk;
+      const size_t rv = ((size_t)t * H + h) * dv;
+      const double b = (double)beta[(size_t)t * H + h];
+      /* S' = Diag(alpha_t) S_{t-1}: row i scaled by alpha_i = exp(log_alpha_i) */
+      for (int i = 0; i < dk; ++i) alpha[i] = exp((double)log_alpha[rk + i]);
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < w; ++j) S[(size_t)i * w + j] *= alpha[i];
+      /* e = v_t - S'^T k_t: what the key reads back, subtracted from the new value */
+      for (int j = 0; j < w; ++j) e[j] = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        const double ki = (double)k[rk + i];
+        for (int j = 0; j < w; ++j) e[j] += ki * S[(size_t)i * w + j];
+      }
+      for (int j = 0; j < w; ++j) e[j] = (double)v[rv + c0 + j] - e[j];
+      /* S_t = S' + beta_t k_t e^T: the difference written back along the key */
+      for (int i = 0; i < dk; ++i) {
+        const double bki = b * (double)k[rk + i];
+        for (int j = 0; j < w; ++j) S[(size_t)i * w + j] += bki * e[j];
+      }
+      /* o_t = S_t^T q_t */
+      if (o_sel) {
+        double acc[ORACLE_COL_BLOCK];
+        for (int j = 0; j < w; ++j) acc[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          const double qi = (double)q[rk + i];
+          for (int j = 0; j < w; ++j) acc[j] += qi * S[(size_t)i * w + j];
+        }
+        double *orow = o_sel + ((size_t)t * n_heads_sel + hs) * ncols + (c0 - col_begin);
+        for (int j = 0; j < w; ++j) orow[j] = acc[j];
+      }
+    }
+
+    if (final_sel)
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < w; ++j)
+          final_sel[(((size_t)n * n_heads_sel + hs) * dk + i) * ncols + (c0 - col_begin) + j] =
+              S[(size_t)i * w + j];
+    free(alpha);
+    free(S);
+  }
+  return 0;
+}
+
+/*
+ * One decode step for a batch of independent (sequence, head) states, in place:
+ * the same recurrence for a single token. state: [N][H][dk][dv] float64 in/out;
+ * q, k, log_alpha: [N][H][dk]; v: [N][H][dv]; beta: [N][H]; o: [N][H][dv] float64.
+ */
+int kda_oracle_decode_step(const float *q, const float *k, const float *v,
+                           const float *log_alpha, const float *beta,
+                           double *state, double *o, int N, int H, int dk, int dv,
+                           int num_threads) {
+  if (!q || !k || !v || !log_alpha || !beta || !state || !o) return -1;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  const long long ntask = (long long)N * H;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(static)
+#endif
+  for (long long nh = 0; nh < ntask; ++nh) {
+    double *S = state + (size_t)nh * dk * dv;
+    const float *qq = q + (size_t)nh * dk, *kk = k + (size_t)nh * dk;
+    const float *la = log_alpha + (size_t)nh * dk, *vv = v + (size_t)nh * dv;
+    const double b = (double)beta[nh];
+    double *oo = o + (size_t)nh * dv;
+    for (int i = 0; i < dk; ++i) {
+      const double a = exp((double)la[i]);
+      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+    }
+    for (int j = 0; j < dv; ++j) {
+      double r = 0.0;
+      for (int i = 0; i < dk; ++i) r += (double)kk[i] * S[(size_t)i * dv + j];
+      const double ej = (double)vv[j] - r;
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        S[(size_t)i * dv + j] += b * (double)kk[i] * ej;
+        acc += (double)qq[i] * S[(size_t)i * dv + j];
+      }
+      oo[j] = acc;
+    }
+  }
+  return 0;
+}
