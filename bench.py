@@ -1,0 +1,232 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill over a 131072-token sequence with 32 heads of
+dimension 128 (bf16 q/k/v, fp32 decays and state, chunk 64), followed by
+``--decode-per-step`` decode steps over 256 sequences x 32 heads of persisted fp32
+128 x 128 states (bf16 q/k/v). Inputs are synthetic, seeded and resident in HBM
+before timing starts.
+
+Prints one JSON line. ``value`` is prefill tokens/s (a token = one position across
+all 32 heads), from HIP events recorded by the library on the stream its kernels
+run on. Decode throughput (GB/s of state + vectors, fraction of HBM peak), the
+algorithmic fraction of bf16 MFMA peak, per-kernel roofline figures and the CPU
+oracle's throughput on a sample of the same workload are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+D = 128
+CHUNK = 64
+# algorithmic flops per (token, head) of the chunked prefill at C = 64, d = 128 (triangles
+# counted exactly): state products 6 d^2, A (C-1) d, P (C+1) d, P U~ (C+1) d, T [bK | bV] (C-1) 2d
+FLOP_PER_TOK_HEAD = 6 * D * D + (CHUNK - 1) * D + (CHUNK + 1) * D + (CHUNK + 1) * D + (CHUNK - 1) * 2 * D
+# bytes every prefill must move per (token, head): q, k, v bf16, log_alpha fp32, beta fp32, o bf16
+PATH_BYTES_PER_TOK_HEAD = 3 * 2 * D + 4 * D + 4 + 2 * D
+# per-(chunk, head) record written by the intra-chunk kernel and read by the inter-chunk kernel
+RECORD_BYTES_BF16_C64 = 74240
+# one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
+DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
+
+PREFILL_T, PREFILL_H = 131072, 32
+DEC_N, DEC_H = 256, 32
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, src_hash):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != src_hash:
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, sample_tokens):
+    """The fp64 sequential oracle on the first ``sample_tokens`` tokens of the same
+    prefill workload (all heads), on this host's cores."""
+    import numpy as np
+    import oracle
+
+    S = min(sample_tokens, inp.q.shape[1])
+    f = lambda t: t[:, :S].float().cpu().numpy()
+    q, k, v, la, beta = f(inp.q), f(inp.k), f(inp.v), f(inp.log_alpha), f(inp.beta)
+    threads = oracle.seq.default_threads()
+    t0 = time.perf_counter()
+    o, fin = oracle.forward(q, k, v, la, beta, num_threads=threads)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(o).all()
+    return {"value": S / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {inp.q.shape[1]} tokens of the prefill workload, all {inp.q.shape[2]} heads "
+                      f"(fp64 sequential recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-per-step", type=int, default=8)
+    ap.add_argument("--decode-inputs", type=int, default=1024, help="distinct decode tokens, cycled")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=PREFILL_T)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device copy of 1 GiB (for counter calibration) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the KDA path "
+              "here has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_57_amd import inputs, kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+        return
+
+    t_gen = time.perf_counter()
+    pre = inputs.make_workload(3, device=dev)
+    dec = inputs.make_decode(N=DEC_N, H=DEC_H, n_steps=args.decode_inputs, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    B, T, H = pre.q.shape[:3]
+    ws = torch.empty(kda.workspace_size(B, T, H, 0, CHUNK, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(pre.v)
+    fin = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    state = dec.initial_state.clone()
+    o_dec = torch.empty(DEC_N, DEC_H, D, dtype=torch.bfloat16, device=dev)
+    n_dec_in = dec.q.shape[0]
+    dec_i = [0]
+
+    def step():
+        kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin,
+                      workspace=ws)
+        for _ in range(args.decode_per_step):
+            i = dec_i[0] % n_dec_in
+            kda.decode_step(dec.q[i], dec.k[i], dec.v[i], dec.log_alpha[i], dec.beta[i], state, o=o_dec)
+            dec_i[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timing = kda.timing_read()
+    kda.timing_enable(False)
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ms = {name: tot / max(cnt, 1) for name, (tot, cnt) in timing.items()}
+    prefill_ms = ms["plan"] + ms["intra"] + ms["inter"]
+    tokens_per_s = T / (prefill_ms * 1e-3)
+    tok_heads = T * H
+    flops = FLOP_PER_TOK_HEAD * tok_heads
+    prefill_tflops = flops / (prefill_ms * 1e-3) / 1e12
+    n_chunks = (T + CHUNK - 1) // CHUNK
+    rec_bytes = n_chunks * H * RECORD_BYTES_BF16_C64
+    in_bytes = tok_heads * (3 * 2 * D + 4 * D + 4)
+    out_bytes = tok_heads * 2 * D
+    kernel_bytes = {
+        "intra": in_bytes + rec_bytes,            # reads the chunk's inputs, writes its record
+        "inter": rec_bytes + out_bytes,            # reads the records once per head, writes o
+        "decode": DEC_N * DEC_H * DECODE_BYTES_PER_HEAD,
+    }
+    src_hash = kernel_source_hash()
+    kernels = {}
+    for name in ("intra", "inter", "decode"):
+        t_s = ms[name] * 1e-3
+        gbs = kernel_bytes[name] / t_s / 1e9
+        traffic = traffic_from_profiles(name, src_hash)
+        kernels[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "avg_ms": round(ms[name], 4), "launches": timing[name][1],
+                         "algorithmic_bytes_per_launch": kernel_bytes[name]}
+    per_step = {"intra": ms["intra"], "inter": ms["inter"], "decode": ms["decode"] * args.decode_per_step}
+    dominant = max(per_step, key=per_step.get)
+    roof = {k: kernels[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dominant
+    dec_gbs = kernel_bytes["decode"] / (ms["decode"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "KDA prefill tokens/s (H=32,d=128) + %MFMA peak; decode GB/s %HBM peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_prefill_T131072_H32_bf16", "T": T, "H": H, "d": D, "chunk": CHUNK,
+                   "decode_workload": "kda_decode_N256_H32_bf16", "decode_per_step": args.decode_per_step,
+                   "parallelism": "single GPU"},
+        "prefill": {"ms": round(prefill_ms, 4), "tokens_per_s": round(tokens_per_s, 1),
+                    "algorithmic_tflops": round(prefill_tflops, 2),
+                    "mfma_frac_algorithmic": round(prefill_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "path_hbm_frac_ideal": round(PATH_BYTES_PER_TOK_HEAD * tok_heads / (prefill_ms * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 4),
+                    "kernel_ms": {"plan": round(ms["plan"], 4), "intra": round(ms["intra"], 4),
+                                  "inter": round(ms["inter"], 4)}},
+        "decode": {"ms_per_step": round(ms["decode"], 4), "GBps": round(dec_gbs, 1),
+                   "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "tokens_per_s": round(DEC_N / (ms["decode"] * 1e-3), 1)},
+        "roofline": roof,
+        "kernels": kernels,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+// C ABI of libkda.so (declared in include/kda.h): argument validation on the
+// host, workspace handling and dispatch to the kernel launchers. Every check runs
+// before the first HIP call, so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared checks of the prefill arguments; returns KDA_OK or a status with the
+// reason recorded.
+int check_prefill(int B, int T, int H, int num_seqs, bool varlen, int dk, int dv, int chunk, int dtype) {
+  if (dtype != KDA_BF16 && dtype != KDA_FP32) return fail(KDA_ERR_UNSUPPORTED, "dtype %d is not KDA_BF16 or KDA_FP32", dtype);
+  if (dk != 128 || dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d: only 128 is supported", dk, dv);
+  if (chunk != 16 && chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 16 and 64 are supported", chunk);
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d T=%d must be >= 0", B, T);
+  if (H <= 0) return fail(KDA_ERR_INVALID_ARG, "H=%d must be > 0", H);
+  if (varlen) {
+    if (B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens requires B == 1 (got B=%d)", B);
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", num_seqs);
+    if (num_seqs == 0 && T > 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs=0 with T=%d tokens", T);
+  }
+  // token indices are int32 on the device; element offsets are 64-bit
+  if ((int64_t)B * T > (int64_t)INT32_MAX - 64) return fail(KDA_ERR_INVALID_ARG, "B*T=%lld is too large", (long long)B * T);
+  if ((int64_t)(varlen ? num_seqs : B) * H > (int64_t)INT32_MAX / 64)
+    return fail(KDA_ERR_INVALID_ARG, "too many (sequence, head) pairs");
+  return KDA_OK;
+}
+
+// ---- per-kernel timing (tracing aid) ------------------------------------------
+struct TraceRec {
+  hipStream_t stream;
+  int kernel;  // -1: start of a call
+  hipEvent_t ev;
+};
+std::mutex g_trace_mu;
+bool g_trace_on = false;
+std::vector<TraceRec> g_trace;
+std::vector<hipEvent_t> g_event_pool;
+
+void trace_record(hipStream_t s, int kernel) {
+  std::lock_guard<std::mutex> lock(g_trace_mu);
+  if (!g_trace_on) return;
+  hipEvent_t ev;
+  if (!g_event_pool.empty()) {
+    ev = g_event_pool.back();
+    g_event_pool.pop_back();
+  } else if (hipEventCreate(&ev) != hipSuccess) {
+    return;
+  }
+  if (hipEventRecord(ev, s) != hipSuccess) {
+    g_event_pool.push_back(ev);
+    return;
+  }
+  g_trace.push_back({s, kernel, ev});
+}
+
+void trace_clear_locked() {
+  for (auto& r : g_trace) g_event_pool.push_back(r.ev);
+  g_trace.clear();
+}
+
+}  // namespace
+
+namespace kda {
+void trace_begin(hipStream_t stream) { trace_record(stream, -1); }
+void trace_mark(hipStream_t stream, int kernel_id) { trace_record(stream, kernel_id); }
+}  // namespace kda
+
+extern "C" {
+
+int kda_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_trace_mu);
+  trace_clear_locked();
+  g_trace_on = on != 0;
+  return ok();
+}
+
+int kda_timing_read(double* total_ms, int* launches, int n) {
+  if (n < 0) return fail(KDA_ERR_INVALID_ARG, "n=%d must be >= 0", n);
+  std::lock_guard<std::mutex> lock(g_trace_mu);
+  for (int i = 0; i < n; ++i) {
+    if (total_ms) total_ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  int status = KDA_OK;
+  if (!g_trace.empty()) {
+    hipError_t e = hipEventSynchronize(g_trace.back().ev);
+    for (size_t i = 0; e == hipSuccess && i < g_trace.size(); ++i) e = hipEventSynchronize(g_trace[i].ev);
+    if (e != hipSuccess) {
+      status = fail(KDA_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
+    } else {
+      for (size_t i = 0; i < g_trace.size(); ++i) {
+        const TraceRec& r = g_trace[i];
+        if (r.kernel < 0) continue;
+        // the previous event recorded on the same stream opens this kernel's interval
+        for (size_t j = i; j-- > 0;) {
+          if (g_trace[j].stream != r.stream) continue;
+          float ms = 0.f;
+          if (hipEventElapsedTime(&ms, g_trace[j].ev, r.ev) == hipSuccess && r.kernel < n) {
+            if (total_ms) total_ms[r.kernel] += ms;
+            if (launches) launches[r.kernel] += 1;
+          }
+          break;
+        }
+      }
+    }
+  }
+  trace_clear_locked();
+  return status == KDA_OK ? ok() : status;
+}
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported configuration";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+    case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE: HIP runtime error";
+    default: return "unknown kda status";
+  }
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype) {
+  // Without cu_seqlens, num_seqs is ignored; with it the caller passes B = 1.
+  const bool varlen = num_seqs > 0 && B == 1;
+  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, chunk, dtype) != KDA_OK) return 0;
+  return kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
+                  float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  int st = check_prefill(B, T, H, num_seqs, varlen, dk, dv, chunk, dtype);
+  if (st != KDA_OK) return st;
+  const int64_t tokens = (int64_t)B * T;
+  if (tokens > 0) {
+    if (!q || !k || !v || !log_alpha || !beta || !o)
+      return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must be non-null when B*T > 0");
+  }
+  const void* ptrs[] = {q, k, v, log_alpha, beta, o, initial_state, final_state};
+  const char* names[] = {"q", "k", "v", "log_alpha", "beta", "o", "initial_state", "final_state"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+  if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const int N = varlen ? num_seqs : B;
+  if (N == 0) return ok();
+  const size_t need = kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+  }
+  hipError_t e = kda::launch_prefill(dtype, chunk, q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o,
+                                     final_state, B, T, H, ws, s);
+  if (!workspace) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                    float* state, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+  if (dtype != KDA_BF16 && dtype != KDA_FP32) return fail(KDA_ERR_UNSUPPORTED, "dtype %d is not KDA_BF16 or KDA_FP32", dtype);
+  if (dk != 128 || dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d: only 128 is supported", dk, dv);
+  if (N < 0) return fail(KDA_ERR_INVALID_ARG, "N=%d must be >= 0", N);
+  if (H <= 0) return fail(KDA_ERR_INVALID_ARG, "H=%d must be > 0", H);
+  if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N*H is too large");
+  if (N == 0) return ok();
+  const void* ptrs[] = {q, k, v, log_alpha, beta, state, o};
+  const char* names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s must be non-null", names[i]);
+    if (!aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  hipError_t e = kda::launch_decode(dtype, q, k, v, log_alpha, beta, state, o, N, H,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

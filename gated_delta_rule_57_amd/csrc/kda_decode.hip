@@ -1,0 +1,118 @@
+// Single-token KDA decode step on gfx950.
+//
+// One new token per (sequence, head) against a persisted 128 x 128 fp32 state,
+// updated in place. The recurrence (GeekNews "Kimi Linear" summary, section
+// "Kimi Delta Attention의 세밀한 메모리 제어"; "From GPT-2 to Kimi K3" digest,
+// sections "DeltaNet -- 유한한 캐시의 덮어쓰기" and "Kimi Linear (KDA) -- 채널별
+// 세밀한 게이팅"), expanded so that the state is read once and written once:
+//     S' = Diag(alpha) S ; r = S'^T k ; p = S'^T q ; u = beta (v - r)
+//     S  = S' + k u^T    ; o = S^T q = p + (k^T q) u
+// Work is bound by HBM: 64 KiB read + 64 KiB written per (sequence, head),
+// against ~7 flops per state element. Each work-group owns one state: 256 threads,
+// thread (rg, cg) holds rows 16 rg .. 16 rg + 15 and columns 4 cg .. 4 cg + 3 in
+// registers (16 float4 loads, streamed with non-temporal hints because the state
+// of a batch is larger than the last-level cache and is not reused within a step).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename E>
+__global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                     const E* __restrict__ v,
+                                                     const float* __restrict__ log_alpha,
+                                                     const float* __restrict__ beta,
+                                                     float* __restrict__ state, E* __restrict__ o) {
+  __shared__ float s_ka[D];      // alpha_i k_i
+  __shared__ float s_qa[D];      // alpha_i q_i
+  __shared__ float s_alpha[D];
+  __shared__ float s_k[D];
+  __shared__ float s_kq;
+  __shared__ floatx4 s_part[8][32][2];  // per row group: partial r and p for 4 columns
+
+  const int t = threadIdx.x;
+  const size_t nh = blockIdx.x;
+  const int cg = t & 31, rg = t >> 5;
+  float* S = state + nh * (size_t)(D * D);
+
+  // Issue the state loads first: they are the bulk of the traffic.
+  floatx4 srow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    srow[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (size_t)(16 * rg + i) * D + 4 * cg));
+
+  if (t < D) {
+    const float a = __expf(log_alpha[nh * D + t]);
+    const float kk = to_f(k[nh * D + t]);
+    const float qq = to_f(q[nh * D + t]);
+    s_alpha[t] = a;
+    s_k[t] = kk;
+    s_ka[t] = a * kk;
+    s_qa[t] = a * qq;
+    // k^T q over the 128 channels: wave-level tree reduction (waves 0 and 1).
+    float prod = kk * qq;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) prod += __shfl_xor(prod, off, 64);
+    if ((t & 63) == 0) s_part[0][t >> 6][0][0] = prod;  // scratch slot, consumed below
+  }
+  __syncthreads();
+  if (t == 0) s_kq = s_part[0][0][0][0] + s_part[0][1][0][0];
+
+  floatx4 r = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float ka = s_ka[16 * rg + i], qa = s_qa[16 * rg + i];
+    r += ka * srow[i];
+    p += qa * srow[i];
+  }
+  __syncthreads();  // s_part scratch use above is finished
+  s_part[rg][cg][0] = r;
+  s_part[rg][cg][1] = p;
+  __syncthreads();
+
+  floatx4 rs = {0.f, 0.f, 0.f, 0.f}, ps = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rs += s_part[j][cg][0];
+    ps += s_part[j][cg][1];
+  }
+  float vv[4];
+  load4f(v + nh * D + 4 * cg, vv);
+  const float b = beta[nh];
+  const float kq = s_kq;
+  floatx4 u, out;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    u[jj] = b * (vv[jj] - rs[jj]);
+    out[jj] = ps[jj] + kq * u[jj];
+  }
+  if (rg == 0) {
+    float ov[4] = {out[0], out[1], out[2], out[3]};
+    store4f(o + nh * D + 4 * cg, ov);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = s_alpha[16 * rg + i], kk = s_k[16 * rg + i];
+    floatx4 nv = a * srow[i] + kk * u;
+    __builtin_nontemporal_store(nv, reinterpret_cast<floatx4*>(S + (size_t)(16 * rg + i) * D + 4 * cg));
+  }
+}
+
+hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, float* state, void* o, int N, int H, hipStream_t stream) {
+  const size_t units = (size_t)N * H;
+  if (units == 0) return hipSuccess;
+  dim3 grid((unsigned)units), block(256);
+  trace_begin(stream);
+  if (dtype == 0)
+    hipLaunchKernelGGL(decode_kernel<__bf16>, grid, block, 0, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, log_alpha, beta, state, (__bf16*)o);
+  else
+    hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, log_alpha, beta, state, (float*)o);
+  hipError_t e = hipGetLastError();
+  trace_mark(stream, 3);
+  return e;
+}
+
+}  // namespace kda

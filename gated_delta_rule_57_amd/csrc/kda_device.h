@@ -1,0 +1,123 @@
+// Device helpers for the KDA kernels on gfx950 (CDNA4): element types, MFMA
+// fragments and the fragment convention shared by the prefill kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int D = 128;  // head dimension (dk = dv)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+// float -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return (__bf16)x; }
+
+// Four consecutive elements, as one 8-byte (bf16) or 16-byte (fp32) access.
+template <typename E> struct Vec4;
+template <> struct Vec4<float> { typedef floatx4 T; };
+template <> struct Vec4<__bf16> { typedef bf16x4 T; };
+
+template <typename E>
+__device__ __forceinline__ void load4f(const E* p, float out[4]) {
+  typename Vec4<E>::T v = *reinterpret_cast<const typename Vec4<E>::T*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = to_f(v[i]);
+}
+template <typename E>
+__device__ __forceinline__ void store4f(E* p, const float in[4]) {
+  typename Vec4<E>::T v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = from_f<E>(in[i]);
+  *reinterpret_cast<typename Vec4<E>::T*>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.
+//
+// A product D(16x16) += A(16 x 32) * B(32 x 16) over one "k-block" of 32 is done
+// with v_mfma_f32_16x16x32_bf16 (one instruction) or with eight
+// v_mfma_f32_16x16x4_f32. Lane l = m + 16 g (m = l & 15, g = l >> 4) holds eight
+// operand elements in slots s = 0..7:
+//     A: A[m][koff(g, s)]       B: B[koff(g, s)][m]
+//     koff(g, s) = 4 g + s          for s < 4
+//                = 16 + 4 g + s - 4 for s >= 4
+// and receives D[4 g + i][m] in accumulator element i (i = 0..3).
+// Because A and B use the same (g, s) -> k map, the map only has to be a
+// permutation of 0..31; this one is chosen so that two stacked accumulator tiles
+// (rows 0..15 and 16..31 of a 32 x 16 result) are, element for element, the B
+// fragment of the next product. Results therefore chain from one MFMA into the
+// next in registers, with no shuffle and no LDS round trip.
+// ---------------------------------------------------------------------------
+template <typename E> struct Frag;
+template <> struct Frag<__bf16> { typedef bf16x8 T; };
+template <> struct Frag<float> { typedef floatx8 T; };
+
+__device__ __forceinline__ int koff(int g, int s) { return s < 4 ? 4 * g + s : 12 + 4 * g + s; }
+
+__device__ __forceinline__ void mma(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(floatx4& acc, const floatx8& a, const floatx8& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+// Two accumulator tiles (rows 0..15 -> slots 0..3, rows 16..31 -> slots 4..7) as a B
+// fragment of element type E.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T acc_pair_to_frag(const floatx4& lo, const floatx4& hi) {
+  typename Frag<E>::T f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = from_f<E>(lo[i]);
+    f[4 + i] = from_f<E>(hi[i]);
+  }
+  return f;
+}
+
+// Fragment whose k runs along a row of a row-major matrix M (row stride ld
+// elements): slot s = M[row][kb + koff(g, s)]. Two 4-element reads.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T frag_rowk(const E* M, int ld, int row, int kb, int g) {
+  typename Frag<E>::T f;
+  const E* p = M + (size_t)row * ld + kb + 4 * g;
+  typename Vec4<E>::T a = *reinterpret_cast<const typename Vec4<E>::T*>(p);
+  typename Vec4<E>::T b = *reinterpret_cast<const typename Vec4<E>::T*>(p + 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = a[i];
+    f[4 + i] = b[i];
+  }
+  return f;
+}
+
+// Fragment whose k runs down a column of a row-major matrix M: slot s =
+// M[kb + koff(g, s)][col]. Eight strided reads.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T frag_colk(const E* M, int ld, int col, int kb, int g) {
+  typename Frag<E>::T f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f[s] = M[(size_t)(kb + koff(g, s)) * ld + col];
+  return f;
+}
+
+// Global fragment store / load: one lane's eight elements, contiguous.
+template <typename E>
+__device__ __forceinline__ void store_frag(E* p, const typename Frag<E>::T& f) {
+  *reinterpret_cast<typename Frag<E>::T*>(p) = f;
+}
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T load_frag(const E* p) {
+  return *reinterpret_cast<const typename Frag<E>::T*>(p);
+}
+
+}  // namespace kda

@@ -1,0 +1,36 @@
+// Internal interface between the C ABI layer (kda_api.hip) and the kernel
+// launchers. Not installed; callers use include/kda.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Tracing hooks (see kda_timing_enable in include/kda.h): trace_begin before a
+// call's first launch, trace_mark(kernel id) after each launch. No-ops unless
+// timing is enabled.
+void trace_begin(hipStream_t stream);
+void trace_mark(hipStream_t stream, int kernel_id);
+
+// dtype: 0 = bf16, 1 = fp32 (the kda_dtype values).
+hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, float* state, void* o, int N, int H, hipStream_t stream);
+
+// Upper bound on the number of chunks of a batch: B sequences of T tokens, or
+// num_seqs packed sequences totalling T tokens.
+int64_t max_chunks(int B, int T, int num_seqs, bool varlen, int chunk);
+
+// Bytes of one per-(chunk, head) record written by the intra-chunk kernel.
+size_t chunk_record_bytes(int dtype, int chunk);
+
+// Workspace bytes for a prefill call.
+size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype);
+
+hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
+                          int T, int H, void* workspace, hipStream_t stream);
+
+}  // namespace kda

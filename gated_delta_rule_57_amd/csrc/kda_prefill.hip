@@ -1,0 +1,701 @@
+// Chunked KDA prefill on gfx950: chunk plan, intra-chunk kernel, inter-chunk
+// state-and-output kernel.
+//
+// Method (GeekNews "Kimi Linear" summary, section "청크 단위 병렬 알고리듬";
+// "From GPT-2 to Kimi K3" digest, section "DeltaNet 병렬화 -- 청크 단위 학습"):
+// each sequence is cut into chunks of C tokens. Inside a chunk (rows r, s;
+// g_r = sum_{j<=r} log_alpha_j per channel; S_0 the state entering the chunk):
+//   A    = tril_strict(beta (K e^G)(K e^-G)^T)           decay-weighted key products
+//   T    = (I + A)^{-1}                                   forward substitution (UT transform)
+//   W    = T diag(beta)(K e^G) ,  U = T diag(beta) V      WY factors
+//   U~   = U - W S_0
+//   P    = tril((Q e^G)(K e^-G)^T)                        causal in-chunk scores
+//   O    = (Q e^G) S_0 + P U~
+//   S_C  = Diag(e^{g_C}) S_0 + (K e^{g_C - G})^T U~
+// The diagonal-plus-low-rank transition has both low-rank factors tied to k, so a
+// chunk needs only the two C x C matrices A and P (section "일반 DPLR보다 줄어든
+// 연산량").
+//
+// Kernels (all launched on the caller's stream):
+//   plan_kernel   cu_seqlens (or B fixed-length rows) -> per-sequence first chunk and
+//                 per-chunk (first token, length).
+//   intra_kernel  one work-group per (chunk, head), fully parallel: everything that
+//                 does not depend on the state -- G, A, T, W, U, Q e^G, P,
+//                 K e^{g_C-G}, e^{g_C} -- written to a per-(chunk, head) record in
+//                 the MFMA fragment order the next kernel consumes.
+//   inter_kernel  one wave per (sequence, head, 16 value columns), serial over the
+//                 sequence's chunks with its 128 x 16 slab of the fp32 state held in
+//                 accumulator registers: U~, O and the state update chain from one
+//                 MFMA to the next without leaving registers. The value columns of
+//                 S evolve independently, which is what makes the slab split exact.
+//
+// In-chunk decay (the pages note that fine-grained decay makes the in-chunk
+// division numerically delicate): everything is done in log2 units, and the
+// chunk's rows are grouped in sub-chunks of 16 with reference points at the
+// sub-chunk boundaries, b_0 = 0 and b_I = gh[16 I - 1]:
+//   plus_r  = 2^(gh_r - b_I) <= 1 for r in sub-chunk I
+//   lhs     = x_r plus_r                              (x = k for A, q for P)
+//   rhs_s   = k_s 2^(b_I - gh_s)                      for s in sub-chunks J <= I
+// For J < I the rhs exponent is <= 0; for J = I it is in [0, R_I] with
+// R_I = b_I - b_{I+1}. When max over channels of R_I exceeds 120 the diagonal
+// block is instead summed on the VALU with 2^(gh_r - gh_s) per element, so no
+// factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C} only
+// need exponents <= 0 and are taken directly.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float DIAG_RANGE_LIMIT = 120.f;  // log2 units
+
+__host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+__host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-(chunk, head) record, element offsets for element type E and chunk C.
+template <typename E, int C>
+struct Rec {
+  static constexpr int NRT = C / 16;           // 16-row tiles of the chunk
+  static constexpr int NKC = (C + 31) / 32;    // 32-row k-blocks over the chunk
+  static constexpr int FR = 64 * 8;            // one fragment block: 64 lanes x 8 elements
+  static constexpr size_t WN = 0;                                   // [NRT][4][64][8]   -W
+  static constexpr size_t QT = WN + (size_t)NRT * 4 * FR;           // [NRT][4][64][8]   Q e^G
+  static constexpr size_t KE = QT + (size_t)NRT * 4 * FR;           // [8][NKC][64][8]   (K e^{g_C-G})^T
+  static constexpr size_t PP = KE + (size_t)8 * NKC * FR;           // [NRT][NKC][64][8] P
+  static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;         // [NRT][8][64][4]   U, accumulator order
+  static constexpr size_t END = UU + (size_t)NRT * 8 * 64 * 4;
+  static constexpr size_t GAMMA_BYTES = al256(END * sizeof(E));      // float[128] e^{g_C}
+  static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
+};
+
+// Shared-memory plan of the intra-chunk kernel (byte offsets).
+template <typename E, int C>
+struct Smem {
+  static constexpr int NSUB = C / 16;
+  static constexpr int CK = C < 32 ? 32 : C;   // chunk rows padded to whole k-blocks
+  static constexpr int NKC = CK / 32;
+  static constexpr int LD = D + 8;             // row stride of [rows][128] E matrices
+  static constexpr int LDC = C + 1;            // row stride of [C][C] fp32 matrices
+  static constexpr int LDK = CK + 8;           // row stride of E matrices indexed by chunk row
+  // phase A: log-decay cumsum and the A / P operands
+  static constexpr size_t G = 0;                                   // float[C][D]
+  static constexpr size_t K = G + (size_t)C * D * 4;               // E[C][LD] raw k
+  static constexpr size_t LK = K + al16((size_t)C * LD * sizeof(E));   // E[C][LD] k * plus
+  static constexpr size_t LQ = LK + al16((size_t)C * LD * sizeof(E));  // E[C][LD] q * plus
+  static constexpr size_t A_END = LQ + al16((size_t)C * LD * sizeof(E));
+  // phase B: A, P, T, T diag(beta), K e^G, V, staging
+  static constexpr size_t MA = 0;                                  // float[C][LDC]
+  static constexpr size_t MP = MA + al16((size_t)C * LDC * 4);     // float[C][LDC]
+  static constexpr size_t MT = MP + al16((size_t)C * LDC * 4);     // float[C][LDC]
+  static constexpr size_t MX = MT + al16((size_t)C * LDC * 4);     // float[16][LDC]
+  static constexpr size_t TB = MX + al16((size_t)16 * LDC * 4);    // E[C][LDK]
+  static constexpr size_t KT = TB + al16((size_t)C * LDK * sizeof(E));   // E[CK][LD]
+  static constexpr size_t VV = KT + al16((size_t)CK * LD * sizeof(E));   // E[CK][LD]
+  static constexpr size_t B_MAIN_END = VV + al16((size_t)CK * LD * sizeof(E));
+  // E[D][LDK] (K e^{g_C-G})^T staging: over MA..MX once they are dead when it fits there
+  static constexpr size_t KET_SIZE = al16((size_t)D * LDK * sizeof(E));
+  static constexpr size_t KET = KET_SIZE <= TB ? 0 : B_MAIN_END;
+  static constexpr size_t B_END = cmax(B_MAIN_END, KET + KET_SIZE);
+  static constexpr size_t WS = KT;   // E[C][LD] -W staging, over KT once dead
+  // tables that live through every phase
+  static constexpr size_t TBL = cmax(A_END, B_END);
+  static constexpr size_t BND = TBL;                              // float[NSUB+1][D] b_I
+  static constexpr size_t P2B = BND + (size_t)(NSUB + 1) * D * 4; // float[NSUB][D] 2^{b_I}
+  static constexpr size_t TEND = P2B + (size_t)NSUB * D * 4;      // float[NSUB][D] 2^{b_NSUB - b_{I+1}}
+  static constexpr size_t BETA = TEND + (size_t)NSUB * D * 4;     // float[CK]
+  static constexpr size_t FLAG = BETA + (size_t)CK * 4;           // int[NSUB]
+  static constexpr size_t TOTAL = al16(FLAG + 4 * NSUB);
+  static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Chunk plan. One work-group of 1024 threads. Sequence n is rows [start, end) of
+// the packed token axis; it owns chunks [chunk_off[n], chunk_off[n+1]).
+// info[c] = (first token, number of tokens) of chunk c.
+// Sequence bounds are clamped to [0, total_tokens] and the chunk count to the
+// workspace's capacity, so cu_seqlens that break their precondition give
+// unspecified results but never an access outside the buffers.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_seqlens, int N, int T,
+                                                    int total_tokens, int C, int capacity,
+                                                    int32_t* __restrict__ chunk_off, int2* __restrict__ info) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_carry;
+  const int t = threadIdx.x;
+  auto clampt = [&](int x) { return min(max(x, 0), total_tokens); };
+  auto seq_start = [&](int n) { return cu_seqlens ? clampt(cu_seqlens[n]) : n * T; };
+  auto seq_end = [&](int n) { return cu_seqlens ? clampt(cu_seqlens[n + 1]) : (n + 1) * T; };
+  if (t == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + t;
+    int cnt = 0;
+    if (n < N) {
+      const int len = seq_end(n) - seq_start(n);
+      cnt = len > 0 ? (len + C - 1) / C : 0;
+    }
+    s_scan[t] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int x = t >= off ? s_scan[t - off] : 0;
+      __syncthreads();
+      s_scan[t] += x;
+      __syncthreads();
+    }
+    const int carry = s_carry;
+    if (n < N) chunk_off[n] = min(carry + s_scan[t] - cnt, capacity);
+    __syncthreads();
+    if (t == 1023) s_carry = min(carry + s_scan[1023], capacity);
+    __syncthreads();
+  }
+  const int total = s_carry;
+  if (t == 0) chunk_off[N] = total;
+  __syncthreads();
+  for (int c = t; c < total; c += 1024) {
+    // the largest n with chunk_off[n] <= c; empty sequences are skipped because they
+    // share their offset with the next sequence
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_off[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    const int tok0 = seq_start(lo) + (c - chunk_off[lo]) * C;
+    const int len = min(C, seq_end(lo) - tok0);
+    info[c] = make_int2(tok0, len);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk kernel: one work-group (4 waves) per (chunk, head).
+// Thread t owns channels 4 (t & 31) .. + 3 of rows (t >> 5) + 8 i for the
+// element-wise phases.
+// ---------------------------------------------------------------------------
+template <typename E, int C>
+__global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                    const E* __restrict__ v, const float* __restrict__ log_alpha,
+                                                    const float* __restrict__ beta,
+                                                    const int32_t* __restrict__ total_chunks,
+                                                    const int2* __restrict__ info, int H,
+                                                    char* __restrict__ records) {
+  using SM = Smem<E, C>;
+  using RC = Rec<E, C>;
+  typedef typename Frag<E>::T FragT;
+  constexpr int NSUB = SM::NSUB, CK = SM::CK, NKC = SM::NKC, LD = SM::LD, LDC = SM::LDC, LDK = SM::LDK;
+  constexpr int NRT = C / 16;
+  constexpr int RPT = C / 8;  // rows per thread in element-wise phases
+
+  __shared__ __attribute__((aligned(16))) char smem[SM::TOTAL];
+  float* sG = reinterpret_cast<float*>(smem + SM::G);
+  E* sK = reinterpret_cast<E*>(smem + SM::K);
+  E* sLK = reinterpret_cast<E*>(smem + SM::LK);
+  E* sLQ = reinterpret_cast<E*>(smem + SM::LQ);
+  float* sA = reinterpret_cast<float*>(smem + SM::MA);
+  float* sP = reinterpret_cast<float*>(smem + SM::MP);
+  float* sT = reinterpret_cast<float*>(smem + SM::MT);
+  float* sX = reinterpret_cast<float*>(smem + SM::MX);
+  E* sTb = reinterpret_cast<E*>(smem + SM::TB);
+  E* sKt = reinterpret_cast<E*>(smem + SM::KT);
+  E* sV = reinterpret_cast<E*>(smem + SM::VV);
+  E* sKeT = reinterpret_cast<E*>(smem + SM::KET);
+  E* sW = reinterpret_cast<E*>(smem + SM::WS);
+  float* sBnd = reinterpret_cast<float*>(smem + SM::BND);
+  float* sP2b = reinterpret_cast<float*>(smem + SM::P2B);
+  float* sTend = reinterpret_cast<float*>(smem + SM::TEND);
+  float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
+  int* sFlag = reinterpret_cast<int*>(smem + SM::FLAG);
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= *total_chunks) return;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
+  const int cq = t & 31, ch0 = 4 * cq, rbase = t >> 5;
+  const int2 inf = info[c];
+  const int tok0 = inf.x, len = inf.y;
+  const size_t HD = (size_t)H * D;
+  E* rec = reinterpret_cast<E*>(records + ((size_t)c * H + h) * RC::BYTES);
+  float* rec_gamma = reinterpret_cast<float*>(records + ((size_t)c * H + h) * RC::BYTES + RC::GAMMA_BYTES);
+
+  // ---- P1: load the chunk; log2-domain decays into sG ---------------------------
+  float kr[RPT][4], qr[RPT][4], vr[RPT][4];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+    floatx4 la = {0.f, 0.f, 0.f, 0.f};
+    if (r < len) {
+      const size_t off = (size_t)(tok0 + r) * HD + (size_t)h * D + ch0;
+      la = *reinterpret_cast<const floatx4*>(log_alpha + off);
+      load4f(k + off, kr[i]);
+      load4f(q + off, qr[i]);
+      load4f(v + off, vr[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[i][j] = qr[i][j] = vr[i][j] = 0.f;
+    }
+    floatx4 l2 = {la[0] * LOG2E_F, la[1] * LOG2E_F, la[2] * LOG2E_F, la[3] * LOG2E_F};
+    *reinterpret_cast<floatx4*>(sG + r * D + ch0) = l2;
+  }
+  if (t < CK) sBeta[t] = (t < len) ? beta[(size_t)(tok0 + t) * H + h] : 0.f;
+  if (t < NSUB) sFlag[t] = 0;
+  __syncthreads();
+  {  // cumulative sum over the chunk's rows, per channel: two halves, then a carry
+    const int chn = t & 127, half = t >> 7;
+    constexpr int HR = C / 2;
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < HR; ++r) {
+      run += sG[(half * HR + r) * D + chn];
+      sG[(half * HR + r) * D + chn] = run;
+    }
+    __syncthreads();
+    if (half == 1) {
+      const float carry = sG[(HR - 1) * D + chn];
+#pragma unroll
+      for (int r = 0; r < HR; ++r) sG[(HR + r) * D + chn] += carry;
+    }
+  }
+  __syncthreads();
+  if (t < D) {
+    float bnd[NSUB + 1];
+    bnd[0] = 0.f;
+#pragma unroll
+    for (int I = 1; I <= NSUB; ++I) bnd[I] = sG[(16 * I - 1) * D + t];
+#pragma unroll
+    for (int I = 0; I <= NSUB; ++I) sBnd[I * D + t] = bnd[I];
+    int over = 0;
+#pragma unroll
+    for (int I = 0; I < NSUB; ++I) {
+      sP2b[I * D + t] = fast_exp2(bnd[I]);
+      sTend[I * D + t] = fast_exp2(bnd[NSUB] - bnd[I + 1]);
+      if (!(bnd[I] - bnd[I + 1] <= DIAG_RANGE_LIMIT)) over |= 1 << I;
+    }
+    rec_gamma[t] = fast_exp2(bnd[NSUB]);
+#pragma unroll
+    for (int I = 0; I < NSUB; ++I)
+      if (over & (1 << I)) atomicOr(&sFlag[I], 1);
+  }
+  __syncthreads();
+
+  // ---- P2: element-wise operands ------------------------------------------------
+  float ktr[RPT][4], ker[RPT][4];  // K e^G and K e^{g_C - G}, kept for phase B
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+    const int I = r >> 4;
+    const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * D + ch0);
+    const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
+    const floatx4 b1 = *reinterpret_cast<const floatx4*>(sBnd + (I + 1) * D + ch0);
+    const floatx4 p2 = *reinterpret_cast<const floatx4*>(sP2b + I * D + ch0);
+    const floatx4 te = *reinterpret_cast<const floatx4*>(sTend + I * D + ch0);
+    float lk[4], lq[4], qt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float plus = fast_exp2(gr[j] - b0[j]);
+      const float minus = fast_exp2(b1[j] - gr[j]);
+      lk[j] = kr[i][j] * plus;
+      lq[j] = qr[i][j] * plus;
+      const float eg = plus * p2[j];        // 2^{gh_r}
+      qt[j] = qr[i][j] * eg;
+      ktr[i][j] = kr[i][j] * eg;
+      ker[i][j] = kr[i][j] * (minus * te[j]);  // 2^{gh_C - gh_r}
+    }
+    store4f(sK + r * LD + ch0, kr[i]);
+    store4f(sLK + r * LD + ch0, lk);
+    store4f(sLQ + r * LD + ch0, lq);
+    // Q e^G straight to its fragment slot: 4 consecutive channels are half a lane's fragment
+    const int kb = ch0 >> 5, co = ch0 & 31;
+    const int fg = (co & 15) >> 2, fh = co >> 4;
+    store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+  }
+  __syncthreads();
+
+  // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time -------------
+  constexpr int NBLK = NSUB * (NSUB + 1) / 2;
+  constexpr int BPW = (NBLK + 3) / 4;
+  floatx4 accA[BPW], accP[BPW];
+#pragma unroll
+  for (int bi = 0; bi < BPW; ++bi) {
+    accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+    accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int idx = w + 4 * bi;
+    if (idx >= NBLK) break;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+    const int J = idx - I * (I + 1) / 2;
+    if (J == I && sFlag[I]) {
+      // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 16 * I + 4 * g + ii, s = 16 * J + m;
+        float sa = 0.f, sp = 0.f;
+        if (s <= r) {
+          for (int ch = 0; ch < D; ++ch) {
+            const float e = fast_exp2(sG[r * D + ch] - sG[s * D + ch]);
+            const float ks = to_f(sK[s * LD + ch]) * e;
+            sa += to_f(sK[r * LD + ch]) * ks;
+            const float qv = (r < len) ? to_f(q[(size_t)(tok0 + r) * HD + (size_t)h * D + ch]) : 0.f;
+            sp += qv * ks;
+          }
+        }
+        accA[bi][ii] = sa;
+        accP[bi][ii] = sp;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const FragT lk = frag_rowk(sLK, LD, 16 * I + m, 32 * kb, g);
+        const FragT lq = frag_rowk(sLQ, LD, 16 * I + m, 32 * kb, g);
+        const int srow = 16 * J + m;
+        FragT rhs;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ch = 32 * kb + 16 * hh + 4 * g;
+          float kk[4];
+          load4f(sK + srow * LD + ch, kk);
+          const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * D + ch);
+          const floatx4 bi4 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rhs[4 * hh + j] = from_f<E>(kk[j] * fast_exp2(bi4[j] - gs[j]));
+        }
+        mma(accA[bi], lk, rhs);
+        mma(accP[bi], lq, rhs);
+      }
+    }
+  }
+  __syncthreads();  // phase A buffers are dead from here on
+
+  // ---- B0: A (rows scaled by beta, strictly lower) and P (lower) -----------------
+#pragma unroll
+  for (int bi = 0; bi < BPW; ++bi) {
+    const int idx = w + 4 * bi;
+    if (idx >= NBLK) break;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+    const int J = idx - I * (I + 1) / 2;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int r = 16 * I + 4 * g + ii, s = 16 * J + m;
+      sA[r * LDC + s] = (s < r) ? sBeta[r] * accA[bi][ii] : 0.f;
+      sP[r * LDC + s] = (s <= r) ? accP[bi][ii] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- B1: P to the record; T = (I + A)^{-1} by forward substitution -------------
+  for (int pi = w; pi < NRT * NKC; pi += 4) {
+    const int rt = pi / NKC, kb = pi % NKC;
+    const int row = 16 * rt + m;
+    FragT f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int col = 32 * kb + koff(g, s);
+      f[s] = from_f<E>((col <= row && col < C) ? sP[row * LDC + col] : 0.f);
+    }
+    store_frag<E>(rec + RC::PP + ((size_t)pi * 64 + lane) * 8, f);
+  }
+  if (w < NSUB && lane < 16) {
+    // diagonal block w: column j = lane, rows solved in order
+    const int j = lane, o0 = 16 * w;
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float val = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) val -= sA[(o0 + r) * LDC + o0 + s] * col[s];
+      col[r] = val;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(o0 + r) * LDC + o0 + j] = col[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int I = 1; I < NSUB; ++I) {
+    // block row I: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, for every J < I
+    const int r = t >> 4, cc = t & 15;
+    for (int J = 0; J < I; ++J) {
+      float x = 0.f;
+      for (int K = J; K < I; ++K)
+#pragma unroll
+        for (int mm = 0; mm < 16; ++mm) x += sA[(16 * I + r) * LDC + 16 * K + mm] * sT[(16 * K + mm) * LDC + 16 * J + cc];
+      sX[r * LDC + 16 * J + cc] = x;
+    }
+    __syncthreads();
+    for (int J = 0; J < I; ++J) {
+      float y = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < 16; ++mm) y += sT[(16 * I + r) * LDC + 16 * I + mm] * sX[mm * LDC + 16 * J + cc];
+      sT[(16 * I + r) * LDC + 16 * J + cc] = -y;
+    }
+    __syncthreads();
+  }
+
+  // ---- B2: T diag(beta) (lower, zero-padded); K e^G and V --------------------------
+  for (int e = t; e < C * CK; e += 256) {
+    const int r = e / CK, s = e % CK;
+    sTb[r * LDK + s] = from_f<E>((s <= r && s < C) ? sT[r * LDC + s] * sBeta[s] : 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+    store4f(sKt + r * LD + ch0, ktr[i]);
+    store4f(sV + r * LD + ch0, vr[i]);
+  }
+  if (CK > C) {
+    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = C + rbase; r < CK; r += 8) {
+      store4f(sKt + r * LD + ch0, z);
+      store4f(sV + r * LD + ch0, z);
+    }
+  }
+  __syncthreads();
+
+  // ---- B3: W = T diag(beta) K e^G and U = T diag(beta) V --------------------------
+  floatx4 accW[2][NRT];
+#pragma unroll
+  for (int cl = 0; cl < 2; ++cl) {
+    const int ct = 2 * w + cl;
+    FragT bK[NKC], bV[NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
+      bK[kb] = frag_colk(sKt, LD, 16 * ct + m, 32 * kb, g);
+      bV[kb] = frag_colk(sV, LD, 16 * ct + m, 32 * kb, g);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      floatx4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
+        mma(aw, aT, bK[kb]);
+        mma(au, aT, bV[kb]);
+      }
+      accW[cl][rt] = aw;
+      float uo[4] = {au[0], au[1], au[2], au[3]};
+      store4f(rec + RC::UU + ((size_t)(rt * 8 + ct) * 64 + lane) * 4, uo);
+    }
+  }
+  // (K e^{g_C - G})^T staged as [channel][chunk row] over the dead A / P / T area
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sKeT[(ch0 + j) * LDK + r] = from_f<E>(ker[i][j]);
+  }
+  if (CK > C)
+    for (int e = t; e < D * (CK - C); e += 256) sKeT[(e / (CK - C)) * LDK + C + e % (CK - C)] = from_f<E>(0.f);
+  __syncthreads();
+
+  // ---- B4: -W staged over the dead K e^G area; fragments out ----------------------
+#pragma unroll
+  for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sW[(16 * rt + 4 * g + ii) * LD + 16 * (2 * w + cl) + m] = from_f<E>(-accW[cl][rt][ii]);
+  __syncthreads();
+  for (int pi = w; pi < NRT * 4; pi += 4) {
+    const int rt = pi >> 2, kb = pi & 3;
+    store_frag<E>(rec + RC::WN + ((size_t)pi * 64 + lane) * 8, frag_rowk(sW, LD, 16 * rt + m, 32 * kb, g));
+  }
+  for (int pi = w; pi < 8 * NKC; pi += 4) {
+    const int ct = pi / NKC, kb = pi % NKC;
+    store_frag<E>(rec + RC::KE + ((size_t)pi * 64 + lane) * 8, frag_rowk(sKeT, LDK, 16 * ct + m, 32 * kb, g));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inter-chunk kernel: one wave per (sequence, head, 16-column slab), serial over
+// the sequence's chunks. Work-group ids are laid out so that the eight slabs of
+// one (sequence, head) land on the same XCD (ids are dealt to the 8 XCDs round
+// robin), where they share that XCD's L2 copy of the chunk records.
+// ---------------------------------------------------------------------------
+template <typename E, int C>
+__global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ records,
+                                                   const int32_t* __restrict__ chunk_off,
+                                                   const int2* __restrict__ info,
+                                                   const float* __restrict__ initial_state,
+                                                   float* __restrict__ final_state, E* __restrict__ o, int N,
+                                                   int H) {
+  using RC = Rec<E, C>;
+  typedef typename Frag<E>::T FragT;
+  constexpr int NRT = RC::NRT, NKC = RC::NKC;
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, rest = b >> 3;
+  const int ct = rest & 7, slot = rest >> 3;
+  const int u = slot * 8 + xcd;
+  if (u >= N * H) return;
+  const int n = u / H, h = u - n * H;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const size_t HD = (size_t)H * D;
+  const size_t sbase = (size_t)u * D * D + 16 * ct + m;
+
+  floatx4 S[8];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[rt][i] = initial_state ? initial_state[sbase + (size_t)(16 * rt + 4 * g + i) * D] : 0.f;
+
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+  for (int c = c_begin; c < c_end; ++c) {
+    const char* rb = records + ((size_t)c * H + h) * RC::BYTES;
+    const E* rec = reinterpret_cast<const E*>(rb);
+    const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
+    const int2 inf = info[c];
+
+    FragT Sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<E>(S[2 * kb], S[2 * kb + 1]);
+
+    // U~ = U - W S  (the record holds -W)
+    floatx4 Ut[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      float u4[4];
+      load4f(rec + RC::UU + ((size_t)(rt * 8 + ct) * 64 + lane) * 4, u4);
+      Ut[rt] = floatx4{u4[0], u4[1], u4[2], u4[3]};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mma(Ut[rt], load_frag<E>(rec + RC::WN + ((size_t)(rt * 4 + kb) * 64 + lane) * 8), Sb[kb]);
+    }
+    // (Q e^G) S
+    floatx4 X[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      X[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mma(X[rt], load_frag<E>(rec + RC::QT + ((size_t)(rt * 4 + kb) * 64 + lane) * 8), Sb[kb]);
+    }
+    FragT Ub[NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb)
+      Ub[kb] = acc_pair_to_frag<E>(Ut[2 * kb], (2 * kb + 1 < NRT) ? Ut[2 * kb + 1] : floatx4{0.f, 0.f, 0.f, 0.f});
+    // O = (Q e^G) S + P U~, causal: row tile rt needs k-blocks <= rt / 2
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+      for (int kb = 0; kb <= (rt >> 1); ++kb)
+        mma(X[rt], load_frag<E>(rec + RC::PP + ((size_t)(rt * NKC + kb) * 64 + lane) * 8), Ub[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt + 4 * g + i;
+        if (row < inf.y) o[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[rt][i]);
+      }
+    }
+    // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      const floatx4 gv = *reinterpret_cast<const floatx4*>(gam + 16 * rt + 4 * g);
+      S[rt] = gv * S[rt];
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+        mma(S[rt], load_frag<E>(rec + RC::KE + ((size_t)(rt * NKC + kb) * 64 + lane) * 8), Ub[kb]);
+    }
+  }
+  if (final_state) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) final_state[sbase + (size_t)(16 * rt + 4 * g + i) * D] = S[rt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+int64_t max_chunks(int B, int T, int num_seqs, bool varlen, int chunk) {
+  const int64_t per = ((int64_t)T + chunk - 1) / chunk;
+  return varlen ? per + num_seqs : (int64_t)B * per;
+}
+
+size_t chunk_record_bytes(int dtype, int chunk) {
+  if (dtype == 0) return chunk == 16 ? Rec<__bf16, 16>::BYTES : Rec<__bf16, 64>::BYTES;
+  return chunk == 16 ? Rec<float, 16>::BYTES : Rec<float, 64>::BYTES;
+}
+
+namespace {
+struct WsLayout {
+  size_t off_chunk_off, off_info, off_records, total;
+};
+WsLayout ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
+  const int N = varlen ? num_seqs : B;
+  const int64_t mc = max_chunks(B, T, num_seqs, varlen, chunk);
+  WsLayout l;
+  l.off_chunk_off = 0;
+  l.off_info = al256((size_t)(N + 1) * sizeof(int32_t));
+  l.off_records = l.off_info + al256((size_t)mc * sizeof(int2));
+  l.total = l.off_records + (size_t)mc * H * chunk_record_bytes(dtype, chunk);
+  return l;
+}
+
+template <typename E, int C>
+hipError_t launch_typed(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                        float* final_state, int T, int H, int64_t mc, const WsLayout& l, char* ws,
+                        hipStream_t stream) {
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + l.off_chunk_off);
+  int2* info = reinterpret_cast<int2*>(ws + l.off_info);
+  char* records = ws + l.off_records;
+  trace_begin(stream);
+  const int total_tokens = cu_seqlens ? T : N * T;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, total_tokens, C, (int)mc,
+                     chunk_off, info);
+  hipError_t e = hipGetLastError();
+  trace_mark(stream, 0);
+  if (e != hipSuccess) return e;
+  if (mc > 0) {
+    hipLaunchKernelGGL((intra_kernel<E, C>), dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream,
+                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, records);
+    e = hipGetLastError();
+    trace_mark(stream, 1);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t units = (int64_t)N * H;
+  const int64_t slots = (units + 7) / 8;
+  if (slots > 0) {
+    hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+                       info, initial_state, final_state, (E*)o, N, H);
+    e = hipGetLastError();
+    trace_mark(stream, 2);
+  }
+  return e;
+}
+}  // namespace
+
+size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
+  return ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;
+}
+
+hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
+                          int T, int H, void* workspace, hipStream_t stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  const int N = varlen ? num_seqs : B;
+  const WsLayout l = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype);
+  const int64_t mc = max_chunks(B, T, num_seqs, varlen, chunk);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == 0) {
+    if (chunk == 16)
+      return launch_typed<__bf16, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
+                                      mc, l, ws, stream);
+    return launch_typed<__bf16, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
+                                    mc, l, ws, stream);
+  }
+  if (chunk == 16)
+    return launch_typed<float, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
+                                   mc, l, ws, stream);
+  return launch_typed<float, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H, mc,
+                                 l, ws, stream);
+}
+
+}  // namespace kda

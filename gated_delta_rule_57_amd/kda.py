@@ -1,0 +1,187 @@
+"""Python binding of libkda.so: argument marshalling only.
+
+Every step of the computation runs in the HIP library; this module checks that
+torch tensors have the layout the C ABI documents (include/kda.h), passes their
+device pointers and the current HIP stream, and turns status codes into
+exceptions. PyTorch supplies device memory and streams, nothing else. Importing
+this module fails loudly when the library is missing: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16 = 0
+KDA_FP32 = 1
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_DEVICE = -4
+
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_fwd", "kda_decode_step", "kda_timing_enable", "kda_timing_read")
+
+KERNEL_NAMES = ("plan", "intra", "inter", "decode")  # KDA_KERNEL_* ids
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkda.so is not built at {LIB_PATH}; run __graft_entry__.build() "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_abi_version.restype = I
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_chunk_fwd_workspace_size.restype = Z
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.kda_decode_step.restype = I
+    lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.kda_timing_enable.restype = I
+    lib.kda_timing_enable.argtypes = [I]
+    lib.kda_timing_read.restype = I
+    lib.kda_timing_read.argtypes = [P, P, I]
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != KDA_OK:
+        raise KdaError(status, lib.kda_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(B, T, H, num_seqs=0, chunk=64, dtype=KDA_BF16) -> int:
+    return int(lib.kda_chunk_fwd_workspace_size(B, T, H, num_seqs, chunk, dtype))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
+              output_final_state=True, o=None, final_state=None, workspace=None):
+    """Chunked KDA prefill through ``kda_chunk_fwd``.
+
+    q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
+    log_alpha: [B, T, H, 128] fp32; beta: [B, T, H] fp32;
+    initial_state: [N, H, 128, 128] fp32 or None; cu_seqlens: int32 [N+1] device
+    tensor (B must be 1) or None. Returns (o, final_state or None).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dcode = _dtype_code(q)
+    _need(q, "q", dt, (B, T, H, dk))
+    _need(k, "k", dt, (B, T, H, dk))
+    _need(v, "v", dt, (B, T, H, dv))
+    _need(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    else:
+        _need(o, "o", dt, (B, T, H, dv))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        ws_bytes = workspace.numel()
+    _check(lib.kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
+        _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, state, o=None):
+    """One decode step through ``kda_decode_step``; ``state`` [N, H, 128, 128] fp32
+    is updated in place. q, k, v: [N, H, 128]; log_alpha: [N, H, 128] fp32;
+    beta: [N, H] fp32. Returns o [N, H, 128]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dcode = _dtype_code(q)
+    _need(q, "q", dt, (N, H, dk))
+    _need(k, "k", dt, (N, H, dk))
+    _need(v, "v", dt, (N, H, dv))
+    _need(log_alpha, "log_alpha", torch.float32, (N, H, dk))
+    _need(beta, "beta", torch.float32, (N, H))
+    _need(state, "state", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    else:
+        _need(o, "o", dt, (N, H, dv))
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
+                               N, H, dk, dv, dcode, _stream(q.device)))
+    return o
+
+
+def timing_enable(on: bool = True):
+    """Start (and clear) or stop per-kernel event timing in the library."""
+    _check(lib.kda_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """Per-kernel totals since the last enable/read: {name: (total_ms, launches)}."""
+    n = len(KERNEL_NAMES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    _check(lib.kda_timing_read(ms, cnt, n))
+    return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(n)}

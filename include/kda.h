@@ -1,0 +1,157 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) forward on AMD MI355X (gfx950).
+ *
+ * KDA is the delta-rule linear-attention recurrence with a per-channel forget gate.
+ * Per sequence and head, token by token,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T ,   o_t = S_t^T q_t ,
+ *
+ * with S in R^{dk x dv}, alpha_t = exp(log_alpha_t) one decay per key channel and
+ * beta_t one write strength per (token, head). The output reads the state after its
+ * own token's update. Sources (web pages on the method):
+ *   - "From GPT-2 to Kimi K3" digest, sections "DeltaNet -- 유한한 캐시의 덮어쓰기"
+ *     (read with the key, subtract, write the difference back along the key),
+ *     "Gated DeltaNet -- 망각을 더하다" (a decay alpha in [0,1]; 1 = pure delta rule)
+ *     and "Kimi Linear (KDA) -- 채널별 세밀한 게이팅" (the scalar becomes Diag(alpha));
+ *   - GeekNews "Kimi Linear" summary, sections "Kimi Delta Attention의 세밀한 메모리
+ *     제어" (per-channel diagonal gate, DPLR transition tied to k), "청크 단위 병렬
+ *     알고리듬" (chunkwise WY/UT algorithm, forward substitution) and "Kimi Linear
+ *     모델 구성" (L2-normalised q and k; head dimension 128).
+ *
+ * Common conventions
+ *   - Every pointer passed to a compute entry point is a DEVICE pointer on the
+ *     current HIP device, owned by the caller. The library keeps no pointer after it
+ *     returns. Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream); buffers must stay alive until that stream has finished.
+ *   - All argument checks run on the host before any HIP call and return a status;
+ *     nothing is ever thrown across the ABI. A device fault surfaces at the caller's
+ *     next synchronisation of the stream.
+ *   - dk = dv = 128 only (the head dimension the pages use for all experiments);
+ *     any other value returns KDA_ERR_UNSUPPORTED.
+ *   - q, k, v and o have dtype `dtype` (KDA_BF16 or KDA_FP32). log_alpha, beta,
+ *     initial_state, final_state and the decode state are always float32.
+ *   - Every tensor pointer must be 16-byte aligned (KDA_ERR_INVALID_ARG otherwise).
+ *   - Value preconditions (documented, not checked): q and k are L2-normalised per
+ *     (token, head) by the caller; log_alpha is finite and <= 0; beta is in [0, 1].
+ *     Outside them the result is unspecified but every kernel still terminates.
+ *   - No scale is applied to q.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Element type of q, k, v and o. */
+typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
+
+/* Return codes of every entry point. */
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = -1, /* null required pointer, bad shape, misalignment, bad cu_seqlens use */
+  KDA_ERR_UNSUPPORTED = -2, /* dk/dv != 128, chunk not in {16, 64}, unknown dtype */
+  KDA_ERR_WORKSPACE = -3,   /* caller workspace smaller than kda_chunk_fwd_workspace_size() */
+  KDA_ERR_DEVICE = -4       /* a HIP call failed; kda_last_error() holds its message */
+} kda_status;
+
+/* Version of this ABI (KDA_ABI_VERSION of the built library). */
+int kda_abi_version(void);
+
+/* Static text for a status code. */
+const char *kda_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for this problem (an upper bound
+ * that does not depend on the sequence lengths inside cu_seqlens). Returns 0 for
+ * arguments kda_chunk_fwd would reject. With cu_seqlens, pass B = 1 and num_seqs =
+ * its number of sequences; without, num_seqs is ignored (B sequences of T tokens).
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype);
+
+/*
+ * Chunked prefill: runs the recurrence over whole sequences.
+ *
+ * The chunkwise algorithm (GeekNews "Kimi Linear" summary, section "청크 단위 병렬
+ * 알고리듬"; "From GPT-2 to Kimi K3" digest, section "DeltaNet 병렬화 -- 청크 단위
+ * 학습"): each sequence is cut into chunks of `chunk` tokens from its own start (the
+ * last one may be partial); a fully parallel kernel forms each chunk's decay-weighted
+ * A = tril(beta (K e^G)(K e^-G)^T), inverts I + A by forward substitution and builds
+ * the WY factors; a second kernel carries the fp32 state across the chunks of each
+ * sequence and writes the outputs. The result does not depend on `chunk` except for
+ * rounding.
+ *
+ *   q, k        [B, T, H, dk]  dtype      o          [B, T, H, dv]  dtype (written)
+ *   v           [B, T, H, dv]  dtype      log_alpha  [B, T, H, dk]  float32
+ *   beta        [B, T, H]      float32
+ *   initial_state [N, H, dk, dv] float32 or NULL (zeros); S[i][j] = key channel i, value channel j
+ *   final_state   [N, H, dk, dv] float32 or NULL (not written); may equal initial_state
+ *   cu_seqlens  int32 [num_seqs + 1] or NULL. With it, B must be 1 and sequence n is
+ *               tokens [cu_seqlens[n], cu_seqlens[n+1]) of the T packed tokens; the
+ *               entries must be non-decreasing with cu_seqlens[0] = 0 and
+ *               cu_seqlens[num_seqs] = T (a precondition: it lives on the device and
+ *               is not read by the host). Zero-length sequences are allowed
+ *               (final = initial). Without it, N = B sequences of T tokens.
+ *   chunk       16 or 64.
+ *   workspace   device buffer of at least kda_chunk_fwd_workspace_size() bytes, or
+ *               NULL: the library then allocates and frees it in stream order.
+ * T = 0 (or B = 0) is a valid call that copies initial_state to final_state (zeros
+ * if initial_state is NULL). `o` must not alias any input.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  int num_seqs, void *o, float *final_state, int B, int T, int H, int dk,
+                  int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * One decode step for N independent sequences: the recurrence applied to a single
+ * new token per (sequence, head), on a persisted state updated in place. It reads
+ * and writes each 128 x 128 fp32 state once.
+ *
+ *   q, k        [N, H, dk] dtype      v, o  [N, H, dv] dtype (o written)
+ *   log_alpha   [N, H, dk] float32    beta  [N, H]     float32
+ *   state       [N, H, dk, dv] float32, in/out
+ * N = 0 is a valid no-op. `o` must not alias any input or the state.
+ */
+int kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                    const float *beta, float *state, void *o, int N, int H, int dk, int dv,
+                    int dtype, void *stream);
+
+/*
+ * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd and
+ * kda_decode_step call records HIP events on its stream before its first kernel
+ * and after each kernel it launches, so the durations are measured on the stream
+ * the kernels run on. Kernel ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA
+ * (intra-chunk), KDA_KERNEL_INTER (inter-chunk state and output), KDA_KERNEL_DECODE.
+ *
+ * kda_timing_enable(1) starts recording (and discards anything recorded before);
+ * kda_timing_enable(0) stops. kda_timing_read() waits for the recorded events,
+ * writes for each kernel id < n the total milliseconds and the launch count since
+ * the last enable/read into total_ms[id] and launches[id] (either may be NULL),
+ * and clears the record. Returns KDA_OK, KDA_ERR_INVALID_ARG for n < 0, or
+ * KDA_ERR_DEVICE. Recording is process-wide and serialised by a lock; the events
+ * cost a few microseconds per launch.
+ */
+#define KDA_KERNEL_PLAN 0
+#define KDA_KERNEL_INTRA 1
+#define KDA_KERNEL_INTER 2
+#define KDA_KERNEL_DECODE 3
+#define KDA_NUM_KERNELS 4
+
+int kda_timing_enable(int on);
+int kda_timing_read(double *total_ms, int *launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU parity tests: run the library, run the oracle on the
+same inputs, and measure the normwise error max|gpu - ref| / max|ref|.
+
+Tolerances: fp32 inputs 1e-4, bf16 inputs 2e-2, on both o and the final state
+(normwise, because element-wise relative error is ill-defined where the reference
+is near zero).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def normwise(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    denom = np.max(np.abs(ref))
+    num = np.max(np.abs(gpu - ref))
+    if denom == 0:
+        return float(num)
+    return float(num / denom)
+
+
+def gpu_prefill(inp, chunk=None, **kw):
+    from gated_delta_rule_57_amd import kda
+    o, fin = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.log_alpha, inp.beta, initial_state=inp.initial_state,
+                           cu_seqlens=inp.cu_seqlens, chunk=chunk or inp.chunk, **kw)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def oracle_prefill(inp, heads=None, cols=None):
+    x = inp.numpy()
+    s0 = None if x["initial_state"] is None else x["initial_state"].astype(np.float64)
+    return oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], s0, cu_seqlens=x["cu_seqlens"],
+                          heads=heads, cols=cols)
+
+
+def compare_prefill(inp, heads=None, cols=None, chunk=None, tol=None, label=""):
+    """Runs both sides; asserts o and final state are within tolerance. Returns the
+    two errors."""
+    say(f"[parity] {label} dtype={inp.dtype} shape={tuple(inp.q.shape)} chunk={chunk or inp.chunk} "
+        f"seqs={inp.num_seqs} heads={heads} cols={cols}")
+    o, fin = gpu_prefill(inp, chunk=chunk)
+    o_ref, fin_ref = oracle_prefill(inp, heads=heads, cols=cols)
+    hs = slice(None) if heads is None else list(heads)
+    c0, c1 = (0, inp.v.shape[-1]) if cols is None else cols
+    o_g = o.float().cpu().numpy()[:, :, hs, c0:c1]
+    f_g = fin.cpu().numpy()[:, hs, :, c0:c1]
+    eo, ef = normwise(o_g, o_ref), normwise(f_g, fin_ref)
+    tol = tol if tol is not None else TOL[inp.dtype]
+    say(f"[parity] {label}: err_o={eo:.3e} err_state={ef:.3e} tol={tol:.0e}")
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(f_g))
+    assert eo <= tol, f"o error {eo} > {tol}"
+    assert ef <= tol, f"final state error {ef} > {tol}"
+    return eo, ef

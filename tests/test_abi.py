@@ -1,0 +1,116 @@
+"""The C ABI of libkda.so on the CPU: the library loads, exports every entry point
+include/kda.h declares, and every invalid argument is rejected with its status
+before any HIP call is made (so none of these tests touches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+from gated_delta_rule_57_amd import kda  # noqa: E402  (loads libkda.so; fails loudly if missing)
+
+L = kda.lib
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced by the host checks
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert L.kda_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert L.kda_status_string(st).decode().startswith("KDA_")
+    assert b"unknown" in L.kda_status_string(7)
+
+
+def chunk_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num_seqs=0, o=FAKE, fin=FAKE,
+               B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0, ws=None, ws_bytes=0):
+    return L.kda_chunk_fwd(q, k, v, la, beta, s0, cu, num_seqs, o, fin, B, T, H, dk, dv, chunk, dtype, ws,
+                           ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=0), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=-2), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(k=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(v=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(la=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(q=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(fin=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(s0=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=0, T=10), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=ctypes.c_void_p((1 << 20) + 2), num_seqs=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 30), kda.KDA_ERR_INVALID_ARG),
+    (dict(ws=FAKE, ws_bytes=16), kda.KDA_ERR_WORKSPACE),
+    (dict(B=1 << 16, T=1 << 16), kda.KDA_ERR_INVALID_ARG),
+])
+def test_chunk_fwd_rejects(kw, status):
+    assert chunk_call(**kw) == status
+    assert L.kda_last_error().decode() != ""
+
+
+def test_chunk_fwd_empty_batch_is_ok_without_device():
+    assert chunk_call(B=0, q=None, k=None, v=None, la=None, beta=None, o=None, fin=None) == kda.KDA_OK
+    assert L.kda_last_error().decode() == ""
+    assert chunk_call(cu=FAKE, num_seqs=0, T=0) == kda.KDA_OK
+
+
+def decode_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, state=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=0):
+    return L.kda_decode_step(q, k, v, la, beta, state, o, N, H, dk, dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=-1), kda.KDA_ERR_UNSUPPORTED),
+    (dict(N=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(state=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+])
+def test_decode_rejects(kw, status):
+    assert decode_call(**kw) == status
+
+
+def test_decode_empty_batch_is_ok():
+    assert decode_call(N=0, q=None, state=None) == kda.KDA_OK
+
+
+def test_workspace_size():
+    ws = L.kda_chunk_fwd_workspace_size
+    assert ws(1, 64, 1, 0, 16, 1) > 0
+    assert ws(1, 4096, 16, 0, 64, 0) < ws(1, 8192, 16, 0, 64, 0) < ws(1, 8192, 32, 0, 64, 0)
+    assert ws(1, 4096, 16, 0, 64, 0) < ws(1, 4096, 16, 0, 64, 1)
+    # a varlen query bounds every split of the same tokens
+    assert ws(1, 32768, 32, 4, 64, 0) >= ws(1, 32768, 32, 0, 64, 0)
+    assert ws(1, 64, 1, 0, 32, 0) == 0
+    assert ws(1, 64, 0, 0, 64, 0) == 0
+    assert ws(1, 64, 1, 0, 64, 9) == 0
