@@ -168,10 +168,11 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
     if (!q || !k || !v || !log_alpha || !beta || !o)
       return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must be non-null when B*T > 0");
   }
-  const void* ptrs[] = {q, k, v, log_alpha, beta, o, initial_state, final_state};
-  const char* names[] = {"q", "k", "v", "log_alpha", "beta", "o", "initial_state", "final_state"};
-  for (int i = 0; i < 8; ++i)
+  const void* ptrs[] = {q, k, v, log_alpha, o, initial_state, final_state};
+  const char* names[] = {"q", "k", "v", "log_alpha", "o", "initial_state", "final_state"};
+  for (int i = 0; i < 7; ++i)
     if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (beta && !aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARG, "beta is not 4-byte aligned");
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
   if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   const int N = varlen ? num_seqs : B;
@@ -208,7 +209,8 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
   const char* names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
   for (int i = 0; i < 7; ++i) {
     if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s must be non-null", names[i]);
-    if (!aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    const size_t need = (ptrs[i] == (const void*)beta) ? 4 : 16;
+    if (!aligned(ptrs[i], need)) return fail(KDA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", names[i], need);
   }
   hipError_t e = kda::launch_decode(dtype, q, k, v, log_alpha, beta, state, o, N, H,
                                     reinterpret_cast<hipStream_t>(stream));

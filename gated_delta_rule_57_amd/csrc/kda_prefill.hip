@@ -41,6 +41,10 @@
 // block is instead summed on the VALU with 2^(gh_r - gh_s) per element, so no
 // factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C} only
 // need exponents <= 0 and are taken directly.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -67,7 +71,7 @@ struct Rec {
   static constexpr size_t QT = WN + (size_t)NRT * 4 * FR;           // [NRT][4][64][8]   Q e^G
   static constexpr size_t KE = QT + (size_t)NRT * 4 * FR;           // [8][NKC][64][8]   (K e^{g_C-G})^T
   static constexpr size_t PP = KE + (size_t)8 * NKC * FR;           // [NRT][NKC][64][8] P
-  static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;         // [NRT][8][64][4]   U, accumulator order
+  static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;         // [8][NRT][64][4]   U, accumulator order
   static constexpr size_t END = UU + (size_t)NRT * 8 * 64 * 4;
   static constexpr size_t GAMMA_BYTES = al256(END * sizeof(E));      // float[128] e^{g_C}
   static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
                                                     const E* __restrict__ v, const float* __restrict__ log_alpha,
                                                     const float* __restrict__ beta,
                                                     const int32_t* __restrict__ total_chunks,
-                                                    const int2* __restrict__ info, int H,
+                                                    const int2* __restrict__ info, int H, int mc,
                                                     char* __restrict__ records) {
   using SM = Smem<E, C>;
   using RC = Rec<E, C>;
@@ -220,8 +224,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   const int2 inf = info[c];
   const int tok0 = inf.x, len = inf.y;
   const size_t HD = (size_t)H * D;
-  E* rec = reinterpret_cast<E*>(records + ((size_t)c * H + h) * RC::BYTES);
-  float* rec_gamma = reinterpret_cast<float*>(records + ((size_t)c * H + h) * RC::BYTES + RC::GAMMA_BYTES);
+  char* rec_base = records + ((size_t)h * mc + c) * RC::BYTES;  // head-major: a head's chunks are contiguous
+  E* rec = reinterpret_cast<E*>(rec_base);
+  float* rec_gamma = reinterpret_cast<float*>(rec_base + RC::GAMMA_BYTES);
 
   // ---- P1: load the chunk; log2-domain decays into sG ---------------------------
   float kr[RPT][4], qr[RPT][4], vr[RPT][4];
@@ -478,7 +483,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       accW[cl][rt] = aw;
       float uo[4] = {au[0], au[1], au[2], au[3]};
-      store4f(rec + RC::UU + ((size_t)(rt * 8 + ct) * 64 + lane) * 4, uo);
+      store4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, uo);
     }
   }
   // (K e^{g_C - G})^T staged as [channel][chunk row] over the dead A / P / T area
@@ -522,7 +527,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
                                                    const int2* __restrict__ info,
                                                    const float* __restrict__ initial_state,
                                                    float* __restrict__ final_state, E* __restrict__ o, int N,
-                                                   int H) {
+                                                   int H, int mc) {
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
   constexpr int NRT = RC::NRT, NKC = RC::NKC;
@@ -539,14 +544,17 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 
   floatx4 S[8];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+  for (int rt = 0; rt < 8; ++rt) S[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (initial_state) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[rt][i] = initial_state ? initial_state[sbase + (size_t)(16 * rt + 4 * g + i) * D] : 0.f;
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[rt][i] = initial_state[sbase + (size_t)(16 * rt + 4 * g + i) * D];
+  }
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   for (int c = c_begin; c < c_end; ++c) {
-    const char* rb = records + ((size_t)c * H + h) * RC::BYTES;
+    const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
     const E* rec = reinterpret_cast<const E*>(rb);
     const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
     const int2 inf = info[c];
@@ -560,7 +568,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       float u4[4];
-      load4f(rec + RC::UU + ((size_t)(rt * 8 + ct) * 64 + lane) * 4, u4);
+      load4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, u4);
       Ut[rt] = floatx4{u4[0], u4[1], u4[2], u4[3]};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -610,6 +618,208 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 }
 
 // ---------------------------------------------------------------------------
+// Inter-chunk kernel, bf16 records of 64-token chunks, with the records streamed
+// through LDS. Each wave owns NCT 16-column slabs of one (sequence, head) and
+// keeps them in accumulator registers. While it computes chunk c from one LDS
+// stage, the record of chunk c+1 is already on its way into the other stage by
+// asynchronous global->LDS copies (global_load_lds_dwordx4: 64 lanes x 16 bytes
+// land as one contiguous 1 KiB block, the size of one MFMA fragment block of the
+// record). Only the blocks the wave uses are copied: -W, Q e^G, (K e^{g_C-G})^T,
+// the six causal P blocks, the wave's U slabs and e^{g_C}. The copies are tracked
+// by the wave's vector-memory counter and waited on explicitly; with at most one
+// chunk in flight they stay below the counter's 63 outstanding operations.
+// ---------------------------------------------------------------------------
+namespace {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+}  // namespace
+
+template <int NCT>
+__global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ records,
+                                                       const int32_t* __restrict__ chunk_off,
+                                                       const int32_t* __restrict__ cu_seqlens, int T,
+                                                       int total_tokens, const float* __restrict__ initial_state,
+                                                       float* __restrict__ final_state, __bf16* __restrict__ o,
+                                                       int N, int H, int mc) {
+  using RC = Rec<__bf16, 64>;
+  typedef bf16x8 FragT;
+  constexpr int SPU = 8 / NCT;  // waves per (sequence, head)
+  constexpr int B_WQK = 48;     // -W, Q e^G, K_end^T: 48 contiguous 1 KiB blocks at the head of the record
+  constexpr int B_P = 6;        // causal P blocks (row tile, k-block) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  constexpr int OFF_P = B_WQK * 1024;
+  constexpr int OFF_U = OFF_P + B_P * 1024;
+  constexpr int OFF_G = OFF_U + NCT * 2048;
+  constexpr int STAGE = OFF_G + 512;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, rest = b >> 3;
+  const int grp = rest % SPU, slot = rest / SPU;
+  const int u = slot * 8 + xcd;
+  if (u >= N * H) return;
+  const int n = u / H, h = u - n * H;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const int ct0 = grp * NCT;
+  const size_t HD = (size_t)H * D;
+
+  int s_start, s_end;
+  if (cu_seqlens) {
+    s_start = min(max(cu_seqlens[n], 0), total_tokens);
+    s_end = min(max(cu_seqlens[n + 1], 0), total_tokens);
+  } else {
+    s_start = n * T;
+    s_end = s_start + T;
+  }
+
+  floatx4 S[NCT][8];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) S[j][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (initial_state) {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[j][rt][i] = initial_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * (ct0 + j) + m];
+  }
+
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+  const char* head_records = records + (size_t)h * mc * RC::BYTES;
+  auto issue = [&](int c, int st) {
+    const char* rb = head_records + (size_t)c * RC::BYTES + lane * 16;
+    char* L = smem + st * STAGE;
+#pragma unroll
+    for (int j = 0; j < B_WQK; ++j) dma16(rb + j * 1024, L + j * 1024);
+    const int pblk[B_P] = {0, 2, 4, 5, 6, 7};
+#pragma unroll
+    for (int j = 0; j < B_P; ++j) dma16(rb + RC::PP * 2 + pblk[j] * 1024, L + OFF_P + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 2 * NCT; ++j) dma16(rb + RC::UU * 2 + ct0 * 2048 + j * 1024, L + OFF_U + j * 1024);
+    const char* rg = head_records + (size_t)c * RC::BYTES + RC::GAMMA_BYTES + lane * 4;
+    dma4(rg, L + OFF_G);
+    dma4(rg + 256, L + OFF_G + 256);
+  };
+
+  if (c_begin < c_end) issue(c_begin, 0);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int st = (c - c_begin) & 1;
+    // chunk c's copies (and the previous chunk's output stores) must be complete
+    wait_vmcnt<0>();
+    compiler_fence();
+    if (c + 1 < c_end) issue(c + 1, st ^ 1);
+    compiler_fence();
+    const char* L = smem + st * STAGE;
+    const int tok0 = s_start + (c - c_begin) * 64;
+    const int len = min(64, s_end - tok0);
+
+    // All of the chunk's fragments are read from LDS up front, so their latency is
+    // paid once per chunk rather than once per MFMA.
+    FragT aw[16], aq[16], ak[16], ap[B_P];
+    bf16x4 uv[NCT][4];
+    floatx4 gv[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      aw[i] = *reinterpret_cast<const FragT*>(L + i * 1024 + lane * 16);
+      aq[i] = *reinterpret_cast<const FragT*>(L + (16 + i) * 1024 + lane * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) uv[j][rt] = *reinterpret_cast<const bf16x4*>(L + OFF_U + j * 2048 + (rt * 64 + lane) * 8);
+#pragma unroll
+    for (int i = 0; i < B_P; ++i) ap[i] = *reinterpret_cast<const FragT*>(L + OFF_P + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ak[i] = *reinterpret_cast<const FragT*>(L + (32 + i) * 1024 + lane * 16);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) gv[rt] = *reinterpret_cast<const floatx4*>(L + OFF_G + (16 * rt + 4 * g) * 4);
+    compiler_fence();
+
+    FragT Sb[NCT][4];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sb[j][kb] = acc_pair_to_frag<__bf16>(S[j][2 * kb], S[j][2 * kb + 1]);
+
+    // U~ = U - W S, and (Q e^G) S
+    floatx4 Ut[NCT][4], X[NCT][4];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Ut[j][rt] = floatx4{(float)uv[j][rt][0], (float)uv[j][rt][1], (float)uv[j][rt][2], (float)uv[j][rt][3]};
+        X[j][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          mma(Ut[j][rt], aw[rt * 4 + kb], Sb[j][kb]);
+          mma(X[j][rt], aq[rt * 4 + kb], Sb[j][kb]);
+        }
+    FragT Ub[NCT][2];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      Ub[j][0] = acc_pair_to_frag<__bf16>(Ut[j][0], Ut[j][1]);
+      Ub[j][1] = acc_pair_to_frag<__bf16>(Ut[j][2], Ut[j][3]);
+    }
+    // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) S[j][rt] = gv[rt] * S[j][rt];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) mma(S[j][rt], ak[rt * 2 + kb], Ub[j][kb]);
+    // O = (Q e^G) S + P U~ (causal blocks only), then store
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int kb = 0; kb <= (rt >> 1); ++kb)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) mma(X[j][rt], ap[rt < 2 ? rt : 2 + 2 * (rt - 2) + kb], Ub[j][kb]);
+#pragma unroll
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * g + i;
+          if (row < len) o[(size_t)(tok0 + row) * HD + (size_t)h * D + 16 * (ct0 + j) + m] = (__bf16)X[j][rt][i];
+        }
+    }
+    compiler_fence();
+  }
+  if (final_state) {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          final_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * (ct0 + j) + m] = S[j][rt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 int64_t max_chunks(int B, int T, int num_seqs, bool varlen, int chunk) {
@@ -623,6 +833,16 @@ size_t chunk_record_bytes(int dtype, int chunk) {
 }
 
 namespace {
+// Value columns per wave of the bf16 chunk-64 inter-chunk kernel: 16 (default) or
+// 32, chosen by KDA_INTER_COLS_PER_WAVE (a tuning knob; both give the same result).
+int inter_cols_per_wave() {
+  static const int v = [] {
+    const char* e = getenv("KDA_INTER_COLS_PER_WAVE");
+    return (e && atoi(e) == 32) ? 32 : 16;
+  }();
+  return v;
+}
+
 struct WsLayout {
   size_t off_chunk_off, off_info, off_records, total;
 };
@@ -654,7 +874,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   if (e != hipSuccess) return e;
   if (mc > 0) {
     hipLaunchKernelGGL((intra_kernel<E, C>), dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, records);
+                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
+                       records);
     e = hipGetLastError();
     trace_mark(stream, 1);
     if (e != hipSuccess) return e;
@@ -662,8 +883,19 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   const int64_t units = (int64_t)N * H;
   const int64_t slots = (units + 7) / 8;
   if (slots > 0) {
-    hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
-                       info, initial_state, final_state, (E*)o, N, H);
+    if constexpr (std::is_same<E, __bf16>::value && C == 64) {
+      if (inter_cols_per_wave() == 32)
+        hipLaunchKernelGGL((inter_dma_kernel<2>), dim3((unsigned)(slots * 32)), dim3(64), 0, stream, records,
+                           chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H,
+                           (int)mc);
+      else
+        hipLaunchKernelGGL((inter_dma_kernel<1>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
+                           chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H,
+                           (int)mc);
+    } else {
+      hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
+                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);
+    }
     e = hipGetLastError();
     trace_mark(stream, 2);
   }

@@ -30,7 +30,8 @@
  *     any other value returns KDA_ERR_UNSUPPORTED.
  *   - q, k, v and o have dtype `dtype` (KDA_BF16 or KDA_FP32). log_alpha, beta,
  *     initial_state, final_state and the decode state are always float32.
- *   - Every tensor pointer must be 16-byte aligned (KDA_ERR_INVALID_ARG otherwise).
+ *   - Every tensor pointer must be 16-byte aligned, except beta and cu_seqlens (4
+ *     bytes) and the workspace (256 bytes); KDA_ERR_INVALID_ARG otherwise.
  *   - Value preconditions (documented, not checked): q and k are L2-normalised per
  *     (token, head) by the caller; log_alpha is finite and <= 0; beta is in [0, 1].
  *     Outside them the result is unspecified but every kernel still terminates.

@@ -63,6 +63,7 @@ def chunk_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num
     (dict(q=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
     (dict(fin=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
     (dict(s0=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=ctypes.c_void_p((1 << 20) + 2)), kda.KDA_ERR_INVALID_ARG),
     (dict(cu=FAKE, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
     (dict(cu=FAKE, num_seqs=-1), kda.KDA_ERR_INVALID_ARG),
     (dict(cu=FAKE, num_seqs=0, T=10), kda.KDA_ERR_INVALID_ARG),
@@ -94,7 +95,8 @@ def decode_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, state=FAKE, o=FAKE, 
     (dict(state=None), kda.KDA_ERR_INVALID_ARG),
     (dict(o=None), kda.KDA_ERR_INVALID_ARG),
     (dict(q=None), kda.KDA_ERR_INVALID_ARG),
-    (dict(beta=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=ctypes.c_void_p((1 << 20) + 2)), kda.KDA_ERR_INVALID_ARG),
+    (dict(state=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects(kw, status):
     assert decode_call(**kw) == status
