@@ -77,41 +77,32 @@ struct Rec {
   static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
 };
 
-// Shared-memory plan of the intra-chunk kernel (byte offsets).
+// Shared-memory plan of the intra-chunk kernel (byte offsets). Phase A buffers are
+// dead once the A / P blocks are formed; phase B buffers reuse the same space.
 template <typename E, int C>
 struct Smem {
   static constexpr int NSUB = C / 16;
   static constexpr int CK = C < 32 ? 32 : C;   // chunk rows padded to whole k-blocks
   static constexpr int NKC = CK / 32;
   static constexpr int LD = D + 8;             // row stride of [rows][128] E matrices
-  static constexpr int LDC = C + 1;            // row stride of [C][C] fp32 matrices
+  static constexpr int GLD = D + 4;            // row stride of the fp32 decay cumsum
+  static constexpr int LDC = C + 4;            // row stride of the fp32 A matrix
   static constexpr int LDK = CK + 8;           // row stride of E matrices indexed by chunk row
-  // phase A: log-decay cumsum and the A / P operands
-  static constexpr size_t G = 0;                                   // float[C][D]
-  static constexpr size_t K = G + (size_t)C * D * 4;               // E[C][LD] raw k
-  static constexpr size_t LK = K + al16((size_t)C * LD * sizeof(E));   // E[C][LD] k * plus
-  static constexpr size_t LQ = LK + al16((size_t)C * LD * sizeof(E));  // E[C][LD] q * plus
-  static constexpr size_t A_END = LQ + al16((size_t)C * LD * sizeof(E));
-  // phase B: A, P, T, T diag(beta), K e^G, V, staging
-  static constexpr size_t MA = 0;                                  // float[C][LDC]
-  static constexpr size_t MP = MA + al16((size_t)C * LDC * 4);     // float[C][LDC]
-  static constexpr size_t MT = MP + al16((size_t)C * LDC * 4);     // float[C][LDC]
-  static constexpr size_t MX = MT + al16((size_t)C * LDC * 4);     // float[16][LDC]
-  static constexpr size_t TB = MX + al16((size_t)16 * LDC * 4);    // E[C][LDK]
-  static constexpr size_t KT = TB + al16((size_t)C * LDK * sizeof(E));   // E[CK][LD]
-  static constexpr size_t VV = KT + al16((size_t)CK * LD * sizeof(E));   // E[CK][LD]
-  static constexpr size_t B_MAIN_END = VV + al16((size_t)CK * LD * sizeof(E));
-  // E[D][LDK] (K e^{g_C-G})^T staging: over MA..MX once they are dead when it fits there
-  static constexpr size_t KET_SIZE = al16((size_t)D * LDK * sizeof(E));
-  static constexpr size_t KET = KET_SIZE <= TB ? 0 : B_MAIN_END;
-  static constexpr size_t B_END = cmax(B_MAIN_END, KET + KET_SIZE);
-  static constexpr size_t WS = KT;   // E[C][LD] -W staging, over KT once dead
+  // phase A: log2-decay cumsum, raw k and q
+  static constexpr size_t G = 0;                                          // float[C][GLD]
+  static constexpr size_t K = G + al16((size_t)C * GLD * 4);              // E[C][LD]
+  static constexpr size_t Q = K + al16((size_t)C * LD * sizeof(E));       // E[C][LD]
+  static constexpr size_t A_END = Q + al16((size_t)C * LD * sizeof(E));
+  // phase B: A, diagonal blocks of T, T diag(beta), K e^G, V
+  static constexpr size_t MA = 0;                                         // float[C][LDC]
+  static constexpr size_t TD = MA + al16((size_t)C * LDC * 4);            // float[NSUB][16][20]
+  static constexpr size_t TB = TD + al16((size_t)NSUB * 16 * 20 * 4);     // E[C][LDK]
+  static constexpr size_t KT = TB + al16((size_t)C * LDK * sizeof(E));    // E[CK][LD]
+  static constexpr size_t VV = KT + al16((size_t)CK * LD * sizeof(E));    // E[CK][LD]
+  static constexpr size_t B_END = VV + al16((size_t)CK * LD * sizeof(E));
   // tables that live through every phase
-  static constexpr size_t TBL = cmax(A_END, B_END);
-  static constexpr size_t BND = TBL;                              // float[NSUB+1][D] b_I
-  static constexpr size_t P2B = BND + (size_t)(NSUB + 1) * D * 4; // float[NSUB][D] 2^{b_I}
-  static constexpr size_t TEND = P2B + (size_t)NSUB * D * 4;      // float[NSUB][D] 2^{b_NSUB - b_{I+1}}
-  static constexpr size_t BETA = TEND + (size_t)NSUB * D * 4;     // float[CK]
+  static constexpr size_t BND = cmax(A_END, B_END);               // float[NSUB+1][D] b_I
+  static constexpr size_t BETA = BND + (size_t)(NSUB + 1) * D * 4; // float[CK]
   static constexpr size_t FLAG = BETA + (size_t)CK * 4;           // int[NSUB]
   static constexpr size_t TOTAL = al16(FLAG + 4 * NSUB);
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
@@ -179,8 +170,22 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Intra-chunk kernel: one work-group (4 waves) per (chunk, head).
-// Thread t owns channels 4 (t & 31) .. + 3 of rows (t >> 5) + 8 i for the
-// element-wise phases.
+//
+// Thread t owns channels 4 (t & 31) .. + 3 of rows (t >> 5) + 8 i in the
+// element-wise phases. MFMA products that feed the record are taken in the
+// orientation whose accumulator layout already is the fragment layout the
+// inter-chunk kernel reads (see kda_device.h): P and -W are computed transposed,
+// so each lane stores its four accumulator values as one 8-byte write, with no
+// transposition through LDS. Phases (barriers in between):
+//   P1  load the chunk (all loads issued before any is waited on); log2 decays
+//   P1b cumulative sum over the rows, sub-chunk boundaries, fallback flags
+//   P2  Q e^G to the record; K e^G kept in registers; raw q, k to LDS
+//   P3  A and P blocks by MFMA (operands built from k, q and G on the fly),
+//       P and K e^{g_C-G} to the record
+//   B0  beta-scaled, masked A to LDS; K e^G and V to LDS
+//   B1  diagonal 16 x 16 blocks of T = (I + A)^{-1} by forward substitution
+//   B2  off-diagonal blocks of T, one block column per wave, by fp32 MFMA
+//   B3  W = T diag(beta) K e^G (stored as -W) and U = T diag(beta) V
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
@@ -192,27 +197,21 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   using SM = Smem<E, C>;
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
-  constexpr int NSUB = SM::NSUB, CK = SM::CK, NKC = SM::NKC, LD = SM::LD, LDC = SM::LDC, LDK = SM::LDK;
+  constexpr int NSUB = SM::NSUB, CK = SM::CK, NKC = SM::NKC, LD = SM::LD, GLD = SM::GLD, LDC = SM::LDC,
+                LDK = SM::LDK;
   constexpr int NRT = C / 16;
   constexpr int RPT = C / 8;  // rows per thread in element-wise phases
 
   __shared__ __attribute__((aligned(16))) char smem[SM::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + SM::G);
   E* sK = reinterpret_cast<E*>(smem + SM::K);
-  E* sLK = reinterpret_cast<E*>(smem + SM::LK);
-  E* sLQ = reinterpret_cast<E*>(smem + SM::LQ);
+  E* sQ = reinterpret_cast<E*>(smem + SM::Q);
   float* sA = reinterpret_cast<float*>(smem + SM::MA);
-  float* sP = reinterpret_cast<float*>(smem + SM::MP);
-  float* sT = reinterpret_cast<float*>(smem + SM::MT);
-  float* sX = reinterpret_cast<float*>(smem + SM::MX);
+  float* sTd = reinterpret_cast<float*>(smem + SM::TD);
   E* sTb = reinterpret_cast<E*>(smem + SM::TB);
   E* sKt = reinterpret_cast<E*>(smem + SM::KT);
   E* sV = reinterpret_cast<E*>(smem + SM::VV);
-  E* sKeT = reinterpret_cast<E*>(smem + SM::KET);
-  E* sW = reinterpret_cast<E*>(smem + SM::WS);
   float* sBnd = reinterpret_cast<float*>(smem + SM::BND);
-  float* sP2b = reinterpret_cast<float*>(smem + SM::P2B);
-  float* sTend = reinterpret_cast<float*>(smem + SM::TEND);
   float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
   int* sFlag = reinterpret_cast<int*>(smem + SM::FLAG);
 
@@ -228,42 +227,53 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   E* rec = reinterpret_cast<E*>(rec_base);
   float* rec_gamma = reinterpret_cast<float*>(rec_base + RC::GAMMA_BYTES);
 
-  // ---- P1: load the chunk; log2-domain decays into sG ---------------------------
+  // ---- P1: every load of the chunk in flight at once (rows past len read row 0 and
+  //          are zeroed), then log2-domain decays into sG ----------------------------
   float kr[RPT][4], qr[RPT][4], vr[RPT][4];
+  floatx4 la[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rbase + 8 * i;
-    floatx4 la = {0.f, 0.f, 0.f, 0.f};
-    if (r < len) {
-      const size_t off = (size_t)(tok0 + r) * HD + (size_t)h * D + ch0;
-      la = *reinterpret_cast<const floatx4*>(log_alpha + off);
-      load4f(k + off, kr[i]);
-      load4f(q + off, qr[i]);
-      load4f(v + off, vr[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kr[i][j] = qr[i][j] = vr[i][j] = 0.f;
-    }
-    floatx4 l2 = {la[0] * LOG2E_F, la[1] * LOG2E_F, la[2] * LOG2E_F, la[3] * LOG2E_F};
-    *reinterpret_cast<floatx4*>(sG + r * D + ch0) = l2;
+    const int rr = r < len ? r : 0;
+    const size_t off = (size_t)(tok0 + rr) * HD + (size_t)h * D + ch0;
+    la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
+    load4f(k + off, kr[i]);
+    load4f(q + off, qr[i]);
+    load4f(v + off, vr[i]);
   }
   if (t < CK) sBeta[t] = (t < len) ? beta[(size_t)(tok0 + t) * H + h] : 0.f;
   if (t < NSUB) sFlag[t] = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+    const bool valid = r < len;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kr[i][j] = valid ? kr[i][j] : 0.f;
+      qr[i][j] = valid ? qr[i][j] : 0.f;
+      vr[i][j] = valid ? vr[i][j] : 0.f;
+    }
+    floatx4 l2 = valid ? la[i] * LOG2E_F : floatx4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<floatx4*>(sG + r * GLD + ch0) = l2;
+  }
   __syncthreads();
-  {  // cumulative sum over the chunk's rows, per channel: two halves, then a carry
+  {  // ---- P1b: cumulative sum over the rows per channel: two halves, then a carry
     const int chn = t & 127, half = t >> 7;
     constexpr int HR = C / 2;
-    float run = 0.f;
+    float vals[HR];
 #pragma unroll
-    for (int r = 0; r < HR; ++r) {
-      run += sG[(half * HR + r) * D + chn];
-      sG[(half * HR + r) * D + chn] = run;
+    for (int r = 0; r < HR; ++r) vals[r] = sG[(half * HR + r) * GLD + chn];
+#pragma unroll
+    for (int r = 1; r < HR; ++r) vals[r] += vals[r - 1];
+    if (half == 0) {
+#pragma unroll
+      for (int r = 0; r < HR; ++r) sG[r * GLD + chn] = vals[r];
     }
     __syncthreads();
     if (half == 1) {
-      const float carry = sG[(HR - 1) * D + chn];
+      const float carry = sG[(HR - 1) * GLD + chn];
 #pragma unroll
-      for (int r = 0; r < HR; ++r) sG[(HR + r) * D + chn] += carry;
+      for (int r = 0; r < HR; ++r) sG[(HR + r) * GLD + chn] = vals[r] + carry;
     }
   }
   __syncthreads();
@@ -271,57 +281,41 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     float bnd[NSUB + 1];
     bnd[0] = 0.f;
 #pragma unroll
-    for (int I = 1; I <= NSUB; ++I) bnd[I] = sG[(16 * I - 1) * D + t];
+    for (int I = 1; I <= NSUB; ++I) bnd[I] = sG[(16 * I - 1) * GLD + t];
 #pragma unroll
     for (int I = 0; I <= NSUB; ++I) sBnd[I * D + t] = bnd[I];
-    int over = 0;
-#pragma unroll
-    for (int I = 0; I < NSUB; ++I) {
-      sP2b[I * D + t] = fast_exp2(bnd[I]);
-      sTend[I * D + t] = fast_exp2(bnd[NSUB] - bnd[I + 1]);
-      if (!(bnd[I] - bnd[I + 1] <= DIAG_RANGE_LIMIT)) over |= 1 << I;
-    }
     rec_gamma[t] = fast_exp2(bnd[NSUB]);
 #pragma unroll
     for (int I = 0; I < NSUB; ++I)
-      if (over & (1 << I)) atomicOr(&sFlag[I], 1);
+      if (!(bnd[I] - bnd[I + 1] <= DIAG_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
   }
-  __syncthreads();
 
-  // ---- P2: element-wise operands ------------------------------------------------
-  float ktr[RPT][4], ker[RPT][4];  // K e^G and K e^{g_C - G}, kept for phase B
+  // ---- P2: Q e^G straight to its fragment slot (4 consecutive channels are half of a
+  //          lane's fragment); K e^G kept for B0; raw q, k to LDS ----------------------
+  float ktr[RPT][4];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rbase + 8 * i;
-    const int I = r >> 4;
-    const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * D + ch0);
-    const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
-    const floatx4 b1 = *reinterpret_cast<const floatx4*>(sBnd + (I + 1) * D + ch0);
-    const floatx4 p2 = *reinterpret_cast<const floatx4*>(sP2b + I * D + ch0);
-    const floatx4 te = *reinterpret_cast<const floatx4*>(sTend + I * D + ch0);
-    float lk[4], lq[4], qt[4];
+    const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+    float qt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float plus = fast_exp2(gr[j] - b0[j]);
-      const float minus = fast_exp2(b1[j] - gr[j]);
-      lk[j] = kr[i][j] * plus;
-      lq[j] = qr[i][j] * plus;
-      const float eg = plus * p2[j];        // 2^{gh_r}
+      const float eg = fast_exp2(gr[j]);  // exponent <= 0
       qt[j] = qr[i][j] * eg;
       ktr[i][j] = kr[i][j] * eg;
-      ker[i][j] = kr[i][j] * (minus * te[j]);  // 2^{gh_C - gh_r}
     }
     store4f(sK + r * LD + ch0, kr[i]);
-    store4f(sLK + r * LD + ch0, lk);
-    store4f(sLQ + r * LD + ch0, lq);
-    // Q e^G straight to its fragment slot: 4 consecutive channels are half a lane's fragment
+    store4f(sQ + r * LD + ch0, qr[i]);
     const int kb = ch0 >> 5, co = ch0 & 31;
     const int fg = (co & 15) >> 2, fh = co >> 4;
     store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
   }
   __syncthreads();
 
-  // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time -------------
+  // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time. Computed
+  //          transposed: lane (m, g), element ii holds entry (r = 16 I + m,
+  //          s = 16 J + 4 g + ii). lhs_r = x_r 2^(gh_r - b_I) (x = k or q),
+  //          rhs_s = k_s 2^(b_I - gh_s). -----------------------------------------------
   constexpr int NBLK = NSUB * (NSUB + 1) / 2;
   constexpr int BPW = (NBLK + 3) / 4;
   floatx4 accA[BPW], accP[BPW];
@@ -336,47 +330,80 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     const int J = idx - I * (I + 1) / 2;
     if (J == I && sFlag[I]) {
       // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
+      const int r = 16 * I + m;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * I + 4 * g + ii, s = 16 * J + m;
+        const int s = 16 * J + 4 * g + ii;
         float sa = 0.f, sp = 0.f;
         if (s <= r) {
           for (int ch = 0; ch < D; ++ch) {
-            const float e = fast_exp2(sG[r * D + ch] - sG[s * D + ch]);
-            const float ks = to_f(sK[s * LD + ch]) * e;
+            const float ks = to_f(sK[s * LD + ch]) * fast_exp2(sG[r * GLD + ch] - sG[s * GLD + ch]);
             sa += to_f(sK[r * LD + ch]) * ks;
-            const float qv = (r < len) ? to_f(q[(size_t)(tok0 + r) * HD + (size_t)h * D + ch]) : 0.f;
-            sp += qv * ks;
+            sp += to_f(sQ[r * LD + ch]) * ks;
           }
         }
         accA[bi][ii] = sa;
         accP[bi][ii] = sp;
       }
     } else {
+      const int rrow = 16 * I + m, srow = 16 * J + m;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const FragT lk = frag_rowk(sLK, LD, 16 * I + m, 32 * kb, g);
-        const FragT lq = frag_rowk(sLQ, LD, 16 * I + m, 32 * kb, g);
-        const int srow = 16 * J + m;
-        FragT rhs;
+        FragT lk, lq, rhs;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int ch = 32 * kb + 16 * hh + 4 * g;
-          float kk[4];
-          load4f(sK + srow * LD + ch, kk);
-          const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * D + ch);
-          const floatx4 bi4 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
+          float kk[4], qq[4], ks[4];
+          load4f(sK + rrow * LD + ch, kk);
+          load4f(sQ + rrow * LD + ch, qq);
+          load4f(sK + srow * LD + ch, ks);
+          const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + rrow * GLD + ch);
+          const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * GLD + ch);
+          const floatx4 bI = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) rhs[4 * hh + j] = from_f<E>(kk[j] * fast_exp2(bi4[j] - gs[j]));
+          for (int j = 0; j < 4; ++j) {
+            const float pl = fast_exp2(gr[j] - bI[j]);
+            lk[4 * hh + j] = from_f<E>(kk[j] * pl);
+            lq[4 * hh + j] = from_f<E>(qq[j] * pl);
+            rhs[4 * hh + j] = from_f<E>(ks[j] * fast_exp2(bI[j] - gs[j]));
+          }
         }
-        mma(accA[bi], lk, rhs);
-        mma(accP[bi], lq, rhs);
+        mma(accA[bi], rhs, lk);
+        mma(accP[bi], rhs, lq);
       }
     }
+    // P to the record: this block is half of fragment (I, J / 2)
+    const int r = 16 * I + m;
+    float pv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
+    store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+  }
+  // zero halves of the P fragments above the diagonal (J > I, J < 2 NKC)
+  for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
+    const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
+    if (J > I) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
+    }
+  }
+  // (K e^{g_C - G})^T to the record: thread item = (channel, 4 consecutive chunk rows),
+  // which is half of one lane's fragment
+  for (int it = t; it < D * (CK / 4); it += 256) {
+    const int ch = it & (D - 1), s0 = 4 * (it >> 7);
+    float kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = s0 + j;
+      kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
+    }
+    const int kb = s0 >> 5, so = s0 & 31;
+    const int fg = (so & 15) >> 2, fh = so >> 4;
+    store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
   }
   __syncthreads();  // phase A buffers are dead from here on
 
-  // ---- B0: A (rows scaled by beta, strictly lower) and P (lower) -----------------
+  // ---- B0: A (row r scaled by beta_r, strictly lower) to LDS; K e^G and V ----------
 #pragma unroll
   for (int bi = 0; bi < BPW; ++bi) {
     const int idx = w + 4 * bi;
@@ -384,67 +411,12 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     int I = 0;
     while ((I + 1) * (I + 2) / 2 <= idx) ++I;
     const int J = idx - I * (I + 1) / 2;
+    const int r = 16 * I + m;
+    const float br = sBeta[r];
+    floatx4 a;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * I + 4 * g + ii, s = 16 * J + m;
-      sA[r * LDC + s] = (s < r) ? sBeta[r] * accA[bi][ii] : 0.f;
-      sP[r * LDC + s] = (s <= r) ? accP[bi][ii] : 0.f;
-    }
-  }
-  __syncthreads();
-
-  // ---- B1: P to the record; T = (I + A)^{-1} by forward substitution -------------
-  for (int pi = w; pi < NRT * NKC; pi += 4) {
-    const int rt = pi / NKC, kb = pi % NKC;
-    const int row = 16 * rt + m;
-    FragT f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int col = 32 * kb + koff(g, s);
-      f[s] = from_f<E>((col <= row && col < C) ? sP[row * LDC + col] : 0.f);
-    }
-    store_frag<E>(rec + RC::PP + ((size_t)pi * 64 + lane) * 8, f);
-  }
-  if (w < NSUB && lane < 16) {
-    // diagonal block w: column j = lane, rows solved in order
-    const int j = lane, o0 = 16 * w;
-    float col[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float val = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) val -= sA[(o0 + r) * LDC + o0 + s] * col[s];
-      col[r] = val;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(o0 + r) * LDC + o0 + j] = col[r];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int I = 1; I < NSUB; ++I) {
-    // block row I: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, for every J < I
-    const int r = t >> 4, cc = t & 15;
-    for (int J = 0; J < I; ++J) {
-      float x = 0.f;
-      for (int K = J; K < I; ++K)
-#pragma unroll
-        for (int mm = 0; mm < 16; ++mm) x += sA[(16 * I + r) * LDC + 16 * K + mm] * sT[(16 * K + mm) * LDC + 16 * J + cc];
-      sX[r * LDC + 16 * J + cc] = x;
-    }
-    __syncthreads();
-    for (int J = 0; J < I; ++J) {
-      float y = 0.f;
-#pragma unroll
-      for (int mm = 0; mm < 16; ++mm) y += sT[(16 * I + r) * LDC + 16 * I + mm] * sX[mm * LDC + 16 * J + cc];
-      sT[(16 * I + r) * LDC + 16 * J + cc] = -y;
-    }
-    __syncthreads();
-  }
-
-  // ---- B2: T diag(beta) (lower, zero-padded); K e^G and V --------------------------
-  for (int e = t; e < C * CK; e += 256) {
-    const int r = e / CK, s = e % CK;
-    sTb[r * LDK + s] = from_f<E>((s <= r && s < C) ? sT[r * LDC + s] * sBeta[s] : 0.f);
+    for (int ii = 0; ii < 4; ++ii) a[ii] = (16 * J + 4 * g + ii < r) ? br * accA[bi][ii] : 0.f;
+    *reinterpret_cast<floatx4*>(sA + r * LDC + 16 * J + 4 * g) = a;
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -459,10 +431,69 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       store4f(sV + r * LD + ch0, z);
     }
   }
+  // T diag(beta) above the diagonal blocks and in the k padding is zero
+  for (int e = t; e < C * CK; e += 256) {
+    const int r = e / CK, s = e % CK;
+    if ((s >> 4) > (r >> 4)) sTb[r * LDK + s] = from_f<E>(0.f);
+  }
   __syncthreads();
 
-  // ---- B3: W = T diag(beta) K e^G and U = T diag(beta) V --------------------------
-  floatx4 accW[2][NRT];
+  // ---- B1: diagonal blocks T_II = (I + A_II)^{-1}, row by row (lane j = column j) ---
+  if (w < NSUB && lane < 16) {
+    const int j = lane, o0 = 16 * w;
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float val = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) val -= sA[(o0 + r) * LDC + o0 + s] * col[s];
+      col[r] = val;
+    }
+    const float bj = sBeta[o0 + j];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sTd[(w * 16 + r) * 20 + j] = col[r];
+      sTb[(o0 + r) * LDK + o0 + j] = from_f<E>(col[r] * bj);
+    }
+  }
+  __syncthreads();
+
+  // ---- B2: off-diagonal blocks of T, block column J per wave:
+  //          T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, in fp32 MFMA ------------------------
+  if (w < NSUB - 1) {
+    const int J = w;
+    floatx4 Tcol[NSUB];  // T_KJ in accumulator layout, K = J .. I-1 (compile-time indices only)
+#pragma unroll
+    for (int K = 0; K < NSUB; ++K) {
+      Tcol[K] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (K == J)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) Tcol[K][ii] = sTd[(K * 16 + 4 * g + ii) * 20 + m];
+    }
+    const float bm = sBeta[16 * J + m];
+#pragma unroll
+    for (int I = 1; I < NSUB; ++I) {
+      if (I <= J) continue;
+      floatx4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < I; ++K) {
+        if (K < J) continue;
+        const floatx4 a = *reinterpret_cast<const floatx4*>(sA + (16 * I + m) * LDC + 16 * K + 4 * g);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj], Tcol[K][jj], X, 0, 0, 0);
+      }
+      const floatx4 tii = *reinterpret_cast<const floatx4*>(sTd + (I * 16 + m) * 20 + 4 * g);
+      floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tii[jj], X[jj], Y, 0, 0, 0);
+      Tcol[I] = -Y;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sTb[(16 * I + 4 * g + ii) * LDK + 16 * J + m] = from_f<E>(-Y[ii] * bm);
+    }
+  }
+  __syncthreads();
+
+  // ---- B3: W (computed transposed, stored as -W in fragment order) and U -----------
 #pragma unroll
   for (int cl = 0; cl < 2; ++cl) {
     const int ct = 2 * w + cl;
@@ -478,40 +509,14 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb) {
         const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
-        mma(aw, aT, bK[kb]);
-        mma(au, aT, bV[kb]);
+        mma(aw, bK[kb], aT);   // lane (m, g): W[16 rt + m][16 ct + 4 g + ii]
+        mma(au, aT, bV[kb]);   // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
       }
-      accW[cl][rt] = aw;
-      float uo[4] = {au[0], au[1], au[2], au[3]};
+      const float wn[4] = {-aw[0], -aw[1], -aw[2], -aw[3]};
+      store4f(rec + RC::WN + ((size_t)(rt * 4 + (ct >> 1)) * 64 + lane) * 8 + 4 * (ct & 1), wn);
+      const float uo[4] = {au[0], au[1], au[2], au[3]};
       store4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, uo);
     }
-  }
-  // (K e^{g_C - G})^T staged as [channel][chunk row] over the dead A / P / T area
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sKeT[(ch0 + j) * LDK + r] = from_f<E>(ker[i][j]);
-  }
-  if (CK > C)
-    for (int e = t; e < D * (CK - C); e += 256) sKeT[(e / (CK - C)) * LDK + C + e % (CK - C)] = from_f<E>(0.f);
-  __syncthreads();
-
-  // ---- B4: -W staged over the dead K e^G area; fragments out ----------------------
-#pragma unroll
-  for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sW[(16 * rt + 4 * g + ii) * LD + 16 * (2 * w + cl) + m] = from_f<E>(-accW[cl][rt][ii]);
-  __syncthreads();
-  for (int pi = w; pi < NRT * 4; pi += 4) {
-    const int rt = pi >> 2, kb = pi & 3;
-    store_frag<E>(rec + RC::WN + ((size_t)pi * 64 + lane) * 8, frag_rowk(sW, LD, 16 * rt + m, 32 * kb, g));
-  }
-  for (int pi = w; pi < 8 * NKC; pi += 4) {
-    const int ct = pi / NKC, kb = pi % NKC;
-    store_frag<E>(rec + RC::KE + ((size_t)pi * 64 + lane) * 8, frag_rowk(sKeT, LDK, 16 * ct + m, 32 * kb, g));
   }
 }
 
@@ -716,13 +721,33 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
     dma4(rg + 256, L + OFF_G + 256);
   };
 
+  // The outputs of chunk c are stored at the start of iteration c+1, after the
+  // copies of chunk c+2 are issued, so that their completion overlaps a chunk of
+  // compute instead of being waited on right away.
+  floatx4 Oprev[NCT][4];
+  int prev_tok0 = 0, prev_len = 0;
+  auto store_prev = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * g + i;
+          if (row < prev_len)
+            o[(size_t)(prev_tok0 + row) * HD + (size_t)h * D + 16 * (ct0 + j) + m] = (__bf16)Oprev[j][rt][i];
+        }
+  };
+
   if (c_begin < c_end) issue(c_begin, 0);
   for (int c = c_begin; c < c_end; ++c) {
     const int st = (c - c_begin) & 1;
-    // chunk c's copies (and the previous chunk's output stores) must be complete
+    // chunk c's copies and the stores of chunk c-2 must be complete
     wait_vmcnt<0>();
     compiler_fence();
     if (c + 1 < c_end) issue(c + 1, st ^ 1);
+    compiler_fence();
+    if (c > c_begin) store_prev();
     compiler_fence();
     const char* L = smem + st * STAGE;
     const int tok0 = s_start + (c - c_begin) * 64;
@@ -798,16 +823,16 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
       for (int kb = 0; kb <= (rt >> 1); ++kb)
 #pragma unroll
         for (int j = 0; j < NCT; ++j) mma(X[j][rt], ap[rt < 2 ? rt : 2 + 2 * (rt - 2) + kb], Ub[j][kb]);
-#pragma unroll
-      for (int j = 0; j < NCT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rt + 4 * g + i;
-          if (row < len) o[(size_t)(tok0 + row) * HD + (size_t)h * D + 16 * (ct0 + j) + m] = (__bf16)X[j][rt][i];
-        }
     }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Oprev[j][rt] = X[j][rt];
+    prev_tok0 = tok0;
+    prev_len = len;
     compiler_fence();
   }
+  if (c_begin < c_end) store_prev();
   if (final_state) {
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
