@@ -41,8 +41,6 @@
 // block is instead summed on the VALU with 2^(gh_r - gh_s) per element, so no
 // factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C} only
 // need exponents <= 0 and are taken directly.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "kda_device.h"
@@ -638,12 +636,6 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_wave_base, 4, 0, 0);
-}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
@@ -652,7 +644,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 }  // namespace
 
-template <int NCT>
 __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ records,
                                                        const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ cu_seqlens, int T,
@@ -661,23 +652,22 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
                                                        int N, int H, int mc) {
   using RC = Rec<__bf16, 64>;
   typedef bf16x8 FragT;
-  constexpr int SPU = 8 / NCT;  // waves per (sequence, head)
   constexpr int B_WQK = 48;     // -W, Q e^G, K_end^T: 48 contiguous 1 KiB blocks at the head of the record
   constexpr int B_P = 6;        // causal P blocks (row tile, k-block) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
   constexpr int OFF_P = B_WQK * 1024;
   constexpr int OFF_U = OFF_P + B_P * 1024;
-  constexpr int OFF_G = OFF_U + NCT * 2048;
+  constexpr int OFF_G = OFF_U + 2048;
   constexpr int STAGE = OFF_G + 512;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int OFF_O = 2 * STAGE;            // bf16 [64][16] output tile of the previous chunk
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 64 * 16 * 2];
 
   const int b = blockIdx.x;
   const int xcd = b & 7, rest = b >> 3;
-  const int grp = rest % SPU, slot = rest / SPU;
+  const int ct = rest & 7, slot = rest >> 3;
   const int u = slot * 8 + xcd;
   if (u >= N * H) return;
   const int n = u / H, h = u - n * H;
   const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
-  const int ct0 = grp * NCT;
   const size_t HD = (size_t)H * D;
 
   int s_start, s_end;
@@ -689,60 +679,76 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
     s_end = s_start + T;
   }
 
-  floatx4 S[NCT][8];
+  floatx4 S[8];
 #pragma unroll
-  for (int j = 0; j < NCT; ++j)
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) S[j][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < 8; ++rt) S[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (initial_state) {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[j][rt][i] = initial_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * (ct0 + j) + m];
+      for (int i = 0; i < 4; ++i)
+        S[rt][i] = initial_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * ct + m];
   }
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const char* head_records = records + (size_t)h * mc * RC::BYTES;
+  // Copies of chunk c into stage st. Runs of consecutive 1 KiB blocks share one
+  // address and one M0 value; the instruction offset moves the global and the LDS
+  // address together.
   auto issue = [&](int c, int st) {
-    const char* rb = head_records + (size_t)c * RC::BYTES + lane * 16;
+    const char* rb = head_records + (size_t)c * RC::BYTES;
     char* L = smem + st * STAGE;
+    const int lo = lane * 16;
 #pragma unroll
-    for (int j = 0; j < B_WQK; ++j) dma16(rb + j * 1024, L + j * 1024);
-    const int pblk[B_P] = {0, 2, 4, 5, 6, 7};
-#pragma unroll
-    for (int j = 0; j < B_P; ++j) dma16(rb + RC::PP * 2 + pblk[j] * 1024, L + OFF_P + j * 1024);
-#pragma unroll
-    for (int j = 0; j < 2 * NCT; ++j) dma16(rb + RC::UU * 2 + ct0 * 2048 + j * 1024, L + OFF_U + j * 1024);
-    const char* rg = head_records + (size_t)c * RC::BYTES + RC::GAMMA_BYTES + lane * 4;
-    dma4(rg, L + OFF_G);
-    dma4(rg + 256, L + OFF_G + 256);
+    for (int q4 = 0; q4 < B_WQK / 4; ++q4) {
+      const char* gq = rb + q4 * 4096;
+      char* lq = L + q4 * 4096;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 1024, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 2048, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 3072, 0);
+    }
+    const char* gp = rb + RC::PP * 2;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + lo), (lds_void_t*)(L + OFF_P), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 2048 + lo), (lds_void_t*)(L + OFF_P + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 1024, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 2048, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 3072, 0);
+    const char* gu = rb + RC::UU * 2 + ct * 2048;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gu + lo), (lds_void_t*)(L + OFF_U), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gu + lo), (lds_void_t*)(L + OFF_U), 16, 1024, 0);
+    const char* gg = rb + RC::GAMMA_BYTES;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gg + lane * 4), (lds_void_t*)(L + OFF_G), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gg + lane * 4), (lds_void_t*)(L + OFF_G), 4, 256, 0);
   };
 
-  // The outputs of chunk c are stored at the start of iteration c+1, after the
-  // copies of chunk c+2 are issued, so that their completion overlaps a chunk of
-  // compute instead of being waited on right away.
-  floatx4 Oprev[NCT][4];
+  // Outputs: chunk c's 64 x 16 tile goes to LDS at the end of iteration c and is
+  // written to HBM at the start of iteration c+1, after the copies of chunk c+2 are
+  // issued, as four 8-byte stores per lane (row lane/4 + 16 j, columns 4 (lane%4)..+3)
+  // whose completion overlaps the compute of chunk c+1.
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
+  const int orow = lane >> 2, ocol = 4 * (lane & 3);
   int prev_tok0 = 0, prev_len = 0;
   auto store_prev = [&]() {
+    __bf16* ob = o + (size_t)prev_tok0 * HD + (size_t)h * D + 16 * ct + ocol;
+    bf16x4 vals[4];
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+    for (int j = 0; j < 4; ++j) vals[j] = *reinterpret_cast<const bf16x4*>(sO + (orow + 16 * j) * 16 + ocol);
+    if (prev_len == 64) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x4*>(ob + (size_t)(orow + 16 * j) * HD) = vals[j];
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rt + 4 * g + i;
-          if (row < prev_len)
-            o[(size_t)(prev_tok0 + row) * HD + (size_t)h * D + 16 * (ct0 + j) + m] = (__bf16)Oprev[j][rt][i];
-        }
+      for (int j = 0; j < 4; ++j)
+        if (orow + 16 * j < prev_len) *reinterpret_cast<bf16x4*>(ob + (size_t)(orow + 16 * j) * HD) = vals[j];
+    }
   };
 
   if (c_begin < c_end) issue(c_begin, 0);
   for (int c = c_begin; c < c_end; ++c) {
     const int st = (c - c_begin) & 1;
-    // chunk c's copies and the stores of chunk c-2 must be complete
+    // chunk c's copies (and the stores of chunk c-2) are complete
     wait_vmcnt<0>();
     compiler_fence();
     if (c + 1 < c_end) issue(c + 1, st ^ 1);
@@ -756,7 +762,7 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
     // All of the chunk's fragments are read from LDS up front, so their latency is
     // paid once per chunk rather than once per MFMA.
     FragT aw[16], aq[16], ak[16], ap[B_P];
-    bf16x4 uv[NCT][4];
+    bf16x4 uv[4];
     floatx4 gv[8];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -764,9 +770,7 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
       aq[i] = *reinterpret_cast<const FragT*>(L + (16 + i) * 1024 + lane * 16);
     }
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) uv[j][rt] = *reinterpret_cast<const bf16x4*>(L + OFF_U + j * 2048 + (rt * 64 + lane) * 8);
+    for (int rt = 0; rt < 4; ++rt) uv[rt] = *reinterpret_cast<const bf16x4*>(L + OFF_U + (rt * 64 + lane) * 8);
 #pragma unroll
     for (int i = 0; i < B_P; ++i) ap[i] = *reinterpret_cast<const FragT*>(L + OFF_P + i * 1024 + lane * 16);
 #pragma unroll
@@ -775,59 +779,42 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
     for (int rt = 0; rt < 8; ++rt) gv[rt] = *reinterpret_cast<const floatx4*>(L + OFF_G + (16 * rt + 4 * g) * 4);
     compiler_fence();
 
-    FragT Sb[NCT][4];
+    FragT Sb[4];
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Sb[j][kb] = acc_pair_to_frag<__bf16>(S[j][2 * kb], S[j][2 * kb + 1]);
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<__bf16>(S[2 * kb], S[2 * kb + 1]);
 
     // U~ = U - W S, and (Q e^G) S
-    floatx4 Ut[NCT][4], X[NCT][4];
+    floatx4 Ut[4], X[4];
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        Ut[j][rt] = floatx4{(float)uv[j][rt][0], (float)uv[j][rt][1], (float)uv[j][rt][2], (float)uv[j][rt][3]};
-        X[j][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int rt = 0; rt < 4; ++rt) {
+      Ut[rt] = floatx4{(float)uv[rt][0], (float)uv[rt][1], (float)uv[rt][2], (float)uv[rt][3]};
+      X[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          mma(Ut[j][rt], aw[rt * 4 + kb], Sb[j][kb]);
-          mma(X[j][rt], aq[rt * 4 + kb], Sb[j][kb]);
-        }
-    FragT Ub[NCT][2];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      Ub[j][0] = acc_pair_to_frag<__bf16>(Ut[j][0], Ut[j][1]);
-      Ub[j][1] = acc_pair_to_frag<__bf16>(Ut[j][2], Ut[j][3]);
-    }
+      for (int rt = 0; rt < 4; ++rt) {
+        mma(Ut[rt], aw[rt * 4 + kb], Sb[kb]);
+        mma(X[rt], aq[rt * 4 + kb], Sb[kb]);
+      }
+    FragT Ub[2];
+    Ub[0] = acc_pair_to_frag<__bf16>(Ut[0], Ut[1]);
+    Ub[1] = acc_pair_to_frag<__bf16>(Ut[2], Ut[3]);
     // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) S[j][rt] = gv[rt] * S[j][rt];
+    for (int rt = 0; rt < 8; ++rt) S[rt] = gv[rt] * S[rt];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) mma(S[j][rt], ak[rt * 2 + kb], Ub[j][kb]);
-    // O = (Q e^G) S + P U~ (causal blocks only), then store
+      for (int rt = 0; rt < 8; ++rt) mma(S[rt], ak[rt * 2 + kb], Ub[kb]);
+    // O = (Q e^G) S + P U~ (causal blocks only), to the LDS output tile
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-      for (int kb = 0; kb <= (rt >> 1); ++kb)
+      for (int kb = 0; kb <= (rt >> 1); ++kb) mma(X[rt], ap[rt < 2 ? rt : 2 + 2 * (rt - 2) + kb], Ub[kb]);
 #pragma unroll
-        for (int j = 0; j < NCT; ++j) mma(X[j][rt], ap[rt < 2 ? rt : 2 + 2 * (rt - 2) + kb], Ub[j][kb]);
+      for (int i = 0; i < 4; ++i) sO[(16 * rt + 4 * g + i) * 16 + m] = (__bf16)X[rt][i];
     }
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) Oprev[j][rt] = X[j][rt];
     prev_tok0 = tok0;
     prev_len = len;
     compiler_fence();
@@ -835,12 +822,10 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
   if (c_begin < c_end) store_prev();
   if (final_state) {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          final_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * (ct0 + j) + m] = S[j][rt][i];
+      for (int i = 0; i < 4; ++i)
+        final_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * ct + m] = S[rt][i];
   }
 }
 
@@ -858,16 +843,6 @@ size_t chunk_record_bytes(int dtype, int chunk) {
 }
 
 namespace {
-// Value columns per wave of the bf16 chunk-64 inter-chunk kernel: 16 (default) or
-// 32, chosen by KDA_INTER_COLS_PER_WAVE (a tuning knob; both give the same result).
-int inter_cols_per_wave() {
-  static const int v = [] {
-    const char* e = getenv("KDA_INTER_COLS_PER_WAVE");
-    return (e && atoi(e) == 32) ? 32 : 16;
-  }();
-  return v;
-}
-
 struct WsLayout {
   size_t off_chunk_off, off_info, off_records, total;
 };
@@ -909,14 +884,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   const int64_t slots = (units + 7) / 8;
   if (slots > 0) {
     if constexpr (std::is_same<E, __bf16>::value && C == 64) {
-      if (inter_cols_per_wave() == 32)
-        hipLaunchKernelGGL((inter_dma_kernel<2>), dim3((unsigned)(slots * 32)), dim3(64), 0, stream, records,
-                           chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H,
-                           (int)mc);
-      else
-        hipLaunchKernelGGL((inter_dma_kernel<1>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
-                           chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H,
-                           (int)mc);
+      hipLaunchKernelGGL(inter_dma_kernel, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+                         cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H, (int)mc);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
                          chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);
