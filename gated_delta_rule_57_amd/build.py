@@ -28,6 +28,9 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: the kernels post-process accumulators with VALU
+        # instructions, which would otherwise need AGPR<->VGPR copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         *extra_flags,
         "-o", out_tmp,
