@@ -15,7 +15,6 @@ oracle's throughput on a sample of the same workload are reported beside it.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -44,12 +43,8 @@ DEC_N, DEC_H = 256, 32
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+    from gated_delta_rule_57_amd.profiling import kernel_source_hash as source_hash
+    return source_hash(ROOT)
 
 
 def traffic_from_profiles(kernel, src_hash):

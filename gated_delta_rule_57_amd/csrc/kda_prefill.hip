@@ -23,11 +23,13 @@
 //                 does not depend on the state -- G, A, T, W, U, Q e^G, P,
 //                 K e^{g_C-G}, e^{g_C} -- written to a per-(chunk, head) record in
 //                 the MFMA fragment order the next kernel consumes.
-//   inter_kernel  one wave per (sequence, head, 16 value columns), serial over the
-//                 sequence's chunks with its 128 x 16 slab of the fp32 state held in
+//   inter kernels one work-group per (sequence, head, 16 value columns), serial over
+//                 the sequence's chunks with its 128 x 16 slab of the fp32 state held in
 //                 accumulator registers: U~, O and the state update chain from one
 //                 MFMA to the next without leaving registers. The value columns of
 //                 S evolve independently, which is what makes the slab split exact.
+//                 inter_wg_kernel (bf16, 64-token chunks) spreads a slab over four
+//                 waves; inter_kernel (fp32 or 16-token chunks) uses one wave.
 //
 // In-chunk decay (the pages note that fine-grained decay makes the in-chunk
 // division numerically delicate): everything is done in log2 units, and the
@@ -122,6 +124,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   __shared__ int s_scan[1024];
   __shared__ int s_carry;
   const int t = threadIdx.x;
+
   auto clampt = [&](int x) { return min(max(x, 0), total_tokens); };
   auto seq_start = [&](int n) { return cu_seqlens ? clampt(cu_seqlens[n]) : n * T; };
   auto seq_end = [&](int n) { return cu_seqlens ? clampt(cu_seqlens[n + 1]) : (n + 1) * T; };
@@ -621,53 +624,64 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk kernel, bf16 records of 64-token chunks, with the records streamed
-// through LDS. Each wave owns NCT 16-column slabs of one (sequence, head) and
-// keeps them in accumulator registers. While it computes chunk c from one LDS
-// stage, the record of chunk c+1 is already on its way into the other stage by
-// asynchronous global->LDS copies (global_load_lds_dwordx4: 64 lanes x 16 bytes
-// land as one contiguous 1 KiB block, the size of one MFMA fragment block of the
-// record). Only the blocks the wave uses are copied: -W, Q e^G, (K e^{g_C-G})^T,
-// the six causal P blocks, the wave's U slabs and e^{g_C}. The copies are tracked
-// by the wave's vector-memory counter and waited on explicitly; with at most one
-// chunk in flight they stay below the counter's 63 outstanding operations.
+// Inter-chunk kernel, bf16 records of 64-token chunks, four waves per (sequence,
+// head, 16-column slab). The work of one chunk is split over the four SIMDs of a
+// CU, wave w taking
+//   U~ rows 16w..16w+15          U~_w = U_w - W_w S         (4 MFMAs)
+//   O  rows 16w..16w+15          O_w  = (Q e^G)_w S + P_w U~ (5-6 MFMAs)
+//   state rows 32w..32w+31       S_w <- e^{g_C} S_w + (K e^{g_C-G})^T_w U~ (4 MFMAs)
+// so that every record fragment is read by exactly one wave, straight from global
+// memory into registers. The waves exchange two small bf16 operands per chunk
+// through LDS: each wave's 32 state rows as one 1 KiB B fragment (all waves need
+// the whole S for U~ and O), and each wave's 16 rows of U~ (all waves need the
+// whole U~ for the state update and O). Loads run LA chunks ahead of the compute,
+// in registers. O is formed transposed (operands of the MFMA swapped), which puts
+// four consecutive output columns of one row in each lane: one 8-byte store per
+// lane, no staging.
 // ---------------------------------------------------------------------------
 namespace {
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// s_waitcnt with lgkmcnt(0) and the vector-memory counter left free
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// work-group barrier for LDS exchanges that leaves in-flight global loads alone
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// chunks of record data in flight ahead of the one being computed
+constexpr int INTER_LOOKAHEAD = 1;
+
+struct InterStage {
+  bf16x8 wn[4], qt[4], ke[4], pp[2];
+  bf16x4 uu;
+  floatx4 gm[2];
+};
+
 }  // namespace
 
-__global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ records,
+template <int LA>
+__global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ records,
                                                        const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ cu_seqlens, int T,
                                                        int total_tokens, const float* __restrict__ initial_state,
                                                        float* __restrict__ final_state, __bf16* __restrict__ o,
                                                        int N, int H, int mc) {
   using RC = Rec<__bf16, 64>;
-  typedef bf16x8 FragT;
-  constexpr int B_WQK = 48;     // -W, Q e^G, K_end^T: 48 contiguous 1 KiB blocks at the head of the record
-  constexpr int B_P = 6;        // causal P blocks (row tile, k-block) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-  constexpr int OFF_P = B_WQK * 1024;
-  constexpr int OFF_U = OFF_P + B_P * 1024;
-  constexpr int OFF_G = OFF_U + 2048;
-  constexpr int STAGE = OFF_G + 512;
-  constexpr int OFF_O = 2 * STAGE;            // bf16 [64][16] output tile of the previous chunk
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 64 * 16 * 2];
+  static_assert(RC::NRT == 4 && RC::NKC == 2, "layout below assumes 64-token chunks");
+  __shared__ __attribute__((aligned(16))) bf16x8 xS[4 * 64];  // state B fragments, k-block kb = 32 rows
+  __shared__ __attribute__((aligned(16))) bf16x8 xU[2 * 64];  // U~ B fragments, k-block kb = 32 chunk rows
 
   const int b = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int xcd = b & 7, rest = b >> 3;
   const int ct = rest & 7, slot = rest >> 3;
   const int u = slot * 8 + xcd;
-  if (u >= N * H) return;
+  if (u >= N * H) return;  // uniform over the work-group
   const int n = u / H, h = u - n * H;
-  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
   const size_t HD = (size_t)H * D;
 
   int s_start, s_end;
@@ -679,153 +693,105 @@ __global__ void __launch_bounds__(64) inter_dma_kernel(const char* __restrict__ 
     s_end = s_start + T;
   }
 
-  floatx4 S[8];
+  // state rows 32w + 16j + 4g + i, column 16ct + m
+  const size_t sidx = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
+  floatx4 Sw[2];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) S[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (initial_state) {
+  for (int j = 0; j < 2; ++j) {
+    Sw[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (initial_state) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[rt][i] = initial_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * ct + m];
+      for (int i = 0; i < 4; ++i) Sw[j][i] = initial_state[sidx + (size_t)(16 * j + i) * D];
+    }
   }
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const char* head_records = records + (size_t)h * mc * RC::BYTES;
-  // Copies of chunk c into stage st. Runs of consecutive 1 KiB blocks share one
-  // address and one M0 value; the instruction offset moves the global and the LDS
-  // address together.
-  auto issue = [&](int c, int st) {
+  const int lo16 = lane * 16;
+  auto load = [&](InterStage& st, int c) {
     const char* rb = head_records + (size_t)c * RC::BYTES;
-    char* L = smem + st * STAGE;
-    const int lo = lane * 16;
 #pragma unroll
-    for (int q4 = 0; q4 < B_WQK / 4; ++q4) {
-      const char* gq = rb + q4 * 4096;
-      char* lq = L + q4 * 4096;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 1024, 0);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 2048, 0);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gq + lo), (lds_void_t*)lq, 16, 3072, 0);
+    for (int kb = 0; kb < 4; ++kb) {
+      st.wn[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::WN * 2) + (4 * w + kb) * 1024 + lo16);
+      st.qt[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::QT * 2) + (4 * w + kb) * 1024 + lo16);
+      st.ke[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::KE * 2) + (4 * w + kb) * 1024 + lo16);
     }
-    const char* gp = rb + RC::PP * 2;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + lo), (lds_void_t*)(L + OFF_P), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 2048 + lo), (lds_void_t*)(L + OFF_P + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 1024, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 2048, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gp + 4096 + lo), (lds_void_t*)(L + OFF_P + 2048), 16, 3072, 0);
-    const char* gu = rb + RC::UU * 2 + ct * 2048;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gu + lo), (lds_void_t*)(L + OFF_U), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gu + lo), (lds_void_t*)(L + OFF_U), 16, 1024, 0);
-    const char* gg = rb + RC::GAMMA_BYTES;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gg + lane * 4), (lds_void_t*)(L + OFF_G), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gg + lane * 4), (lds_void_t*)(L + OFF_G), 4, 256, 0);
-  };
-
-  // Outputs: chunk c's 64 x 16 tile goes to LDS at the end of iteration c and is
-  // written to HBM at the start of iteration c+1, after the copies of chunk c+2 are
-  // issued, as four 8-byte stores per lane (row lane/4 + 16 j, columns 4 (lane%4)..+3)
-  // whose completion overlaps the compute of chunk c+1.
-  __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
-  const int orow = lane >> 2, ocol = 4 * (lane & 3);
-  int prev_tok0 = 0, prev_len = 0;
-  auto store_prev = [&]() {
-    __bf16* ob = o + (size_t)prev_tok0 * HD + (size_t)h * D + 16 * ct + ocol;
-    bf16x4 vals[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vals[j] = *reinterpret_cast<const bf16x4*>(sO + (orow + 16 * j) * 16 + ocol);
-    if (prev_len == 64) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x4*>(ob + (size_t)(orow + 16 * j) * HD) = vals[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (orow + 16 * j < prev_len) *reinterpret_cast<bf16x4*>(ob + (size_t)(orow + 16 * j) * HD) = vals[j];
-    }
-  };
-
-  if (c_begin < c_end) issue(c_begin, 0);
-  for (int c = c_begin; c < c_end; ++c) {
-    const int st = (c - c_begin) & 1;
-    // chunk c's copies (and the stores of chunk c-2) are complete
-    wait_vmcnt<0>();
-    compiler_fence();
-    if (c + 1 < c_end) issue(c + 1, st ^ 1);
-    compiler_fence();
-    if (c > c_begin) store_prev();
-    compiler_fence();
-    const char* L = smem + st * STAGE;
-    const int tok0 = s_start + (c - c_begin) * 64;
-    const int len = min(64, s_end - tok0);
-
-    // All of the chunk's fragments are read from LDS up front, so their latency is
-    // paid once per chunk rather than once per MFMA.
-    FragT aw[16], aq[16], ak[16], ap[B_P];
-    bf16x4 uv[4];
-    floatx4 gv[8];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      aw[i] = *reinterpret_cast<const FragT*>(L + i * 1024 + lane * 16);
-      aq[i] = *reinterpret_cast<const FragT*>(L + (16 + i) * 1024 + lane * 16);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) uv[rt] = *reinterpret_cast<const bf16x4*>(L + OFF_U + (rt * 64 + lane) * 8);
-#pragma unroll
-    for (int i = 0; i < B_P; ++i) ap[i] = *reinterpret_cast<const FragT*>(L + OFF_P + i * 1024 + lane * 16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ak[i] = *reinterpret_cast<const FragT*>(L + (32 + i) * 1024 + lane * 16);
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) gv[rt] = *reinterpret_cast<const floatx4*>(L + OFF_G + (16 * rt + 4 * g) * 4);
-    compiler_fence();
-
-    FragT Sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<__bf16>(S[2 * kb], S[2 * kb + 1]);
-
-    // U~ = U - W S, and (Q e^G) S
-    floatx4 Ut[4], X[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Ut[rt] = floatx4{(float)uv[rt][0], (float)uv[rt][1], (float)uv[rt][2], (float)uv[rt][3]};
-      X[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        mma(Ut[rt], aw[rt * 4 + kb], Sb[kb]);
-        mma(X[rt], aq[rt * 4 + kb], Sb[kb]);
-      }
-    FragT Ub[2];
-    Ub[0] = acc_pair_to_frag<__bf16>(Ut[0], Ut[1]);
-    Ub[1] = acc_pair_to_frag<__bf16>(Ut[2], Ut[3]);
-    // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) S[rt] = gv[rt] * S[rt];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
+      st.pp[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::PP * 2) + (2 * w + kb) * 1024 + lo16);
+    st.uu = *reinterpret_cast<const bf16x4*>(rb + (RC::UU * 2) + ((ct * 4 + w) * 64 + lane) * 8);
+    const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt) mma(S[rt], ak[rt * 2 + kb], Ub[kb]);
-    // O = (Q e^G) S + P U~ (causal blocks only), to the LDS output tile
+    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
+  };
+
+  auto compute = [&](const InterStage& st, int c) {
+    // this wave's 32 state rows as a B fragment, for every wave
+    xS[w * 64 + lane] = acc_pair_to_frag<__bf16>(Sw[0], Sw[1]);
+    lds_barrier();
+    bf16x8 Sb[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = xS[kb * 64 + lane];
+    // U~_w = U_w - W_w S  (the record holds -W)
+    floatx4 ut = floatx4{(float)st.uu[0], (float)st.uu[1], (float)st.uu[2], (float)st.uu[3]};
 #pragma unroll
-      for (int kb = 0; kb <= (rt >> 1); ++kb) mma(X[rt], ap[rt < 2 ? rt : 2 + 2 * (rt - 2) + kb], Ub[kb]);
+    for (int kb = 0; kb < 4; ++kb) mma(ut, st.wn[kb], Sb[kb]);
+    {
+      bf16x4 uh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sO[(16 * rt + 4 * g + i) * 16 + m] = (__bf16)X[rt][i];
+      for (int i = 0; i < 4; ++i) uh[i] = (__bf16)ut[i];
+      // rows 16w + 4g + i are slots 4 (w & 1) + i of k-block w >> 1
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(xU) + ((w >> 1) * 64 + lane) * 16 + (w & 1) * 8) = uh;
     }
-    prev_tok0 = tok0;
-    prev_len = len;
-    compiler_fence();
+    // e^{g_C} S_w, ahead of the barrier
+#pragma unroll
+    for (int j = 0; j < 2; ++j) Sw[j] = st.gm[j] * Sw[j];
+    lds_barrier();
+    bf16x8 Ub[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Ub[kb] = xU[kb * 64 + lane];
+    // O_w^T = S^T (Q e^G)_w^T : lane (m, g) holds row 16w + m, columns 4g..4g+3
+    floatx4 xt = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma(xt, Sb[kb], st.qt[kb]);
+    // S_w += (K e^{g_C-G})^T_w U~
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(Sw[j], st.ke[2 * j + kb], Ub[kb]);
+    // O_w^T += U~^T P_w^T, causal k-blocks only
+    mma(xt, Ub[0], st.pp[0]);
+    if (w >= 2) mma(xt, Ub[1], st.pp[1]);
+    const int tok0 = s_start + (c - c_begin) * 64;
+    const int row = 16 * w + m;
+    if (row < s_end - tok0) {
+      bf16x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = (__bf16)xt[i];
+      *reinterpret_cast<bf16x4*>(o + (size_t)(tok0 + row) * HD + (size_t)h * D + 16 * ct + 4 * g) = ov;
+    }
+  };
+
+  InterStage st[LA + 1];
+#pragma unroll
+  for (int r = 0; r < LA; ++r)
+    if (c_begin < c_end) load(st[r], min(c_begin + r, c_end - 1));
+  for (int c0 = c_begin; c0 < c_end; c0 += LA + 1) {
+#pragma unroll
+    for (int r = 0; r <= LA; ++r) {
+      const int c = c0 + r;
+      // the stage consumed one step earlier takes chunk c + LA; past the end the
+      // final record is loaded again, so every step issues the same loads and the
+      // register stages rotate without leaving the loop body
+      load(st[(r + LA) % (LA + 1)], min(c + LA, c_end - 1));
+      if (c < c_end) compute(st[r], c);
+    }
   }
-  if (c_begin < c_end) store_prev();
   if (final_state) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        final_state[(size_t)u * D * D + (size_t)(16 * rt + 4 * g + i) * D + 16 * ct + m] = S[rt][i];
+      for (int i = 0; i < 4; ++i) final_state[sidx + (size_t)(16 * j + i) * D] = Sw[j][i];
   }
 }
 
@@ -884,8 +850,9 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   const int64_t slots = (units + 7) / 8;
   if (slots > 0) {
     if constexpr (std::is_same<E, __bf16>::value && C == 64) {
-      hipLaunchKernelGGL(inter_dma_kernel, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
-                         cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N, H, (int)mc);
+      hipLaunchKernelGGL(inter_wg_kernel<INTER_LOOKAHEAD>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream,
+                         records, chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N,
+                         H, (int)mc);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
                          chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);

@@ -19,19 +19,21 @@ import json
 import os
 import sys
 
-KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_dma_kernel", "inter"),
+KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
            ("inter_kernel", "inter"), ("decode_kernel", "decode"))
 COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash(root=None):
-    """Hash of the HIP sources, the same one bench.py reports."""
+    """Hash of the HIP sources and of the build script that sets the compiler flags,
+    the same one bench.py reports."""
     root = root or os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    csrc = os.path.join(root, "gated_delta_rule_57_amd", "csrc")
+    pkg = os.path.join(root, "gated_delta_rule_57_amd")
+    csrc = os.path.join(pkg, "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    for path in [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))] + [os.path.join(pkg, "build.py")]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
