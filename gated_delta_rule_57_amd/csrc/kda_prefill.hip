@@ -34,15 +34,18 @@
 // In-chunk decay (the pages note that fine-grained decay makes the in-chunk
 // division numerically delicate): everything is done in log2 units, and the
 // chunk's rows are grouped in sub-chunks of 16 with reference points at the
-// sub-chunk boundaries, b_0 = 0 and b_I = gh[16 I - 1]:
-//   plus_r  = 2^(gh_r - b_I) <= 1 for r in sub-chunk I
-//   lhs     = x_r plus_r                              (x = k for A, q for P)
-//   rhs_s   = k_s 2^(b_I - gh_s)                      for s in sub-chunks J <= I
-// For J < I the rhs exponent is <= 0; for J = I it is in [0, R_I] with
-// R_I = b_I - b_{I+1}. When max over channels of R_I exceeds 120 the diagonal
-// block is instead summed on the VALU with 2^(gh_r - gh_s) per element, so no
-// factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C} only
-// need exponents <= 0 and are taken directly.
+// sub-chunk boundaries, b_0 = 0 and b_I = gh[16 I - 1]. For an A / P block (I, J),
+// r in sub-chunk I and s in sub-chunk J <= I:
+//   2^(gh_r - gh_s) = 2^(gh_r - b_I) * 2^(b_I - b_{J+1}) * 2^(b_{J+1} - gh_s)
+// The first and last factors have exponents <= 0 and belong to one row each, so
+// they are applied once per row (lhs_r = x_r 2^(gh_r - b_I), x = k for A, q for P;
+// rhs_s = k_s 2^(b_{J+1} - gh_s)); the middle one is a per-channel scale of the
+// block, <= 1 off the diagonal and 2^(R_I) on it, R_I = b_I - b_{I+1}. When max
+// over channels of R_I exceeds 120 for some sub-chunk, the chunk instead takes an
+// exact path: off-diagonal blocks with rhs_s = k_s 2^(b_I - gh_s) built per block,
+// and that diagonal block summed on the VALU with 2^(gh_r - gh_s) per element,
+// so no factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C}
+// only need exponents <= 0 and are taken directly.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -88,11 +91,19 @@ struct Smem {
   static constexpr int GLD = D + 4;            // row stride of the fp32 decay cumsum
   static constexpr int LDC = C + 4;            // row stride of the fp32 A matrix
   static constexpr int LDK = CK + 8;           // row stride of E matrices indexed by chunk row
-  // phase A: log2-decay cumsum, raw k and q
+  // phase A, exact path: log2-decay cumsum, raw k and q
   static constexpr size_t G = 0;                                          // float[C][GLD]
   static constexpr size_t K = G + al16((size_t)C * GLD * 4);              // E[C][LD]
   static constexpr size_t Q = K + al16((size_t)C * LD * sizeof(E));       // E[C][LD]
   static constexpr size_t A_END = Q + al16((size_t)C * LD * sizeof(E));
+  // phase A, factored path: the cumsum (at G) is replaced by the per-row factored
+  // operands once every thread holds its own decays in registers; RR does not
+  // overlap G, so it is written before that hand-over
+  static constexpr size_t LK = 0;                                         // E[C][LD]     k_r 2^(gh_r - b_I)
+  static constexpr size_t LQ = LK + al16((size_t)C * LD * sizeof(E));     // E[C][LD]     q_r 2^(gh_r - b_I)
+  static constexpr size_t RR = LQ + al16((size_t)C * LD * sizeof(E));     // float[C][GLD] k_s 2^(b_{J+1} - gh_s)
+  static constexpr size_t F_END = RR + al16((size_t)C * GLD * 4);
+  static_assert(G + (size_t)C * GLD * 4 <= RR, "the factored rhs must not overlap the cumsum");
   // phase B: A, diagonal blocks of T, T diag(beta), K e^G, V
   static constexpr size_t MA = 0;                                         // float[C][LDC]
   static constexpr size_t TD = MA + al16((size_t)C * LDC * 4);            // float[NSUB][16][20]
@@ -101,8 +112,13 @@ struct Smem {
   static constexpr size_t VV = KT + al16((size_t)CK * LD * sizeof(E));    // E[CK][LD]
   static constexpr size_t B_END = VV + al16((size_t)CK * LD * sizeof(E));
   // tables that live through every phase
-  static constexpr size_t BND = cmax(A_END, B_END);               // float[NSUB+1][D] b_I
-  static constexpr size_t BETA = BND + (size_t)(NSUB + 1) * D * 4; // float[CK]
+  static constexpr size_t BND = cmax(cmax(A_END, F_END), B_END);  // float[NSUB+1][D] b_I
+  // per-channel block scales 2^(b_I - b_{J+1}): entry I (I + 1) / 2 + J for the A / P
+  // block (I, J <= I), entry NBLK + J for (chunk end, J)
+  static constexpr int NBLK = NSUB * (NSUB + 1) / 2;
+  static constexpr int NSCALE = NBLK + NSUB;
+  static constexpr size_t SCL = BND + (size_t)(NSUB + 1) * D * 4;  // float[NSCALE][D]
+  static constexpr size_t BETA = SCL + (size_t)NSCALE * D * 4;     // float[CK]
   static constexpr size_t FLAG = BETA + (size_t)CK * 4;           // int[NSUB]
   static constexpr size_t TOTAL = al16(FLAG + 4 * NSUB);
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
@@ -198,6 +214,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   using SM = Smem<E, C>;
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
+  typedef typename Vec4<E>::T V4;
   constexpr int NSUB = SM::NSUB, CK = SM::CK, NKC = SM::NKC, LD = SM::LD, GLD = SM::GLD, LDC = SM::LDC,
                 LDK = SM::LDK;
   constexpr int NRT = C / 16;
@@ -278,6 +295,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     }
   }
   __syncthreads();
+  float* sScl = reinterpret_cast<float*>(smem + SM::SCL);
   if (t < D) {
     float bnd[NSUB + 1];
     bnd[0] = 0.f;
@@ -289,118 +307,234 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
     for (int I = 0; I < NSUB; ++I)
       if (!(bnd[I] - bnd[I + 1] <= DIAG_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
-  }
-
-  // ---- P2: Q e^G straight to its fragment slot (4 consecutive channels are half of a
-  //          lane's fragment); K e^G kept for B0; raw q, k to LDS ----------------------
-  float ktr[RPT][4];
+    // block scales: <= 1 off the diagonal, 2^(R_I) on it (used only while R_I <= the limit)
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
-    const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
-    float qt[4];
+    for (int I = 0; I < NSUB; ++I)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float eg = fast_exp2(gr[j]);  // exponent <= 0
-      qt[j] = qr[i][j] * eg;
-      ktr[i][j] = kr[i][j] * eg;
-    }
-    store4f(sK + r * LD + ch0, kr[i]);
-    store4f(sQ + r * LD + ch0, qr[i]);
-    const int kb = ch0 >> 5, co = ch0 & 31;
-    const int fg = (co & 15) >> 2, fh = co >> 4;
-    store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      for (int J = 0; J <= I; ++J) sScl[(I * (I + 1) / 2 + J) * D + t] = fast_exp2(bnd[I] - bnd[J + 1]);
+#pragma unroll
+    for (int J = 0; J < NSUB; ++J) sScl[(SM::NBLK + J) * D + t] = fast_exp2(bnd[NSUB] - bnd[J + 1]);
   }
   __syncthreads();
+  bool exact = false;  // some diagonal block exceeds the range limit: per-element path
+#pragma unroll
+  for (int I = 0; I < NSUB; ++I) exact |= sFlag[I] != 0;
 
-  // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time. Computed
-  //          transposed: lane (m, g), element ii holds entry (r = 16 I + m,
-  //          s = 16 J + 4 g + ii). lhs_r = x_r 2^(gh_r - b_I) (x = k or q),
-  //          rhs_s = k_s 2^(b_I - gh_s). -----------------------------------------------
-  constexpr int NBLK = NSUB * (NSUB + 1) / 2;
+  constexpr int NBLK = SM::NBLK;
   constexpr int BPW = (NBLK + 3) / 4;
+  float ktr[RPT][4];
   floatx4 accA[BPW], accP[BPW];
+  if (!exact) {
+    // ---- P2 (factored path): Q e^G to the record, K e^G kept for B0, and per row
+    //      the operands of every A / P block:
+    //        lhs_r = x_r 2^(gh_r - b_I)        (x = k or q; I = r's sub-chunk)
+    //        rhs_s = k_s 2^(b_{J+1} - gh_s)    (J = s's sub-chunk)
+    //      both with exponents <= 0. Block (I, J) is lhs_I diag(2^(b_I - b_{J+1})) rhs_J^T,
+    //      the per-channel scale taken from the table above.
+    E* sLK = reinterpret_cast<E*>(smem + SM::LK);
+    E* sLQ = reinterpret_cast<E*>(smem + SM::LQ);
+    float* sRR = reinterpret_cast<float*>(smem + SM::RR);
+    V4 lkv[RPT], lqv[RPT];
 #pragma unroll
-  for (int bi = 0; bi < BPW; ++bi) {
-    accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-    accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int idx = w + 4 * bi;
-    if (idx >= NBLK) break;
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-    const int J = idx - I * (I + 1) / 2;
-    if (J == I && sFlag[I]) {
-      // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
-      const int r = 16 * I + m;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i, I = r >> 4;
+      const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
+      const floatx4 b1 = *reinterpret_cast<const floatx4*>(sBnd + (I + 1) * D + ch0);
+      float qt[4];
+      floatx4 rr;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int s = 16 * J + 4 * g + ii;
-        float sa = 0.f, sp = 0.f;
-        if (s <= r) {
-          for (int ch = 0; ch < D; ++ch) {
-            const float ks = to_f(sK[s * LD + ch]) * fast_exp2(sG[r * GLD + ch] - sG[s * GLD + ch]);
-            sa += to_f(sK[r * LD + ch]) * ks;
-            sp += to_f(sQ[r * LD + ch]) * ks;
-          }
-        }
-        accA[bi][ii] = sa;
-        accP[bi][ii] = sp;
+      for (int j = 0; j < 4; ++j) {
+        const float kk = kr[i][j], qq = qr[i][j];
+        const float eg = fast_exp2(gr[j]);          // exponent <= 0
+        const float pl = fast_exp2(gr[j] - b0[j]);  // exponent <= 0
+        qt[j] = qq * eg;
+        ktr[i][j] = kk * eg;
+        lkv[i][j] = from_f<E>(kk * pl);
+        lqv[i][j] = from_f<E>(qq * pl);
+        rr[j] = kk * fast_exp2(b1[j] - gr[j]);     // exponent <= 0
       }
-    } else {
+      *reinterpret_cast<floatx4*>(sRR + r * GLD + ch0) = rr;
+      const int kb = ch0 >> 5, co = ch0 & 31;
+      const int fg = (co & 15) >> 2, fh = co >> 4;
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+    }
+    __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i;
+      *reinterpret_cast<V4*>(sLK + r * LD + ch0) = lkv[i];
+      *reinterpret_cast<V4*>(sLQ + r * LD + ch0) = lqv[i];
+    }
+    __syncthreads();
+
+    // ---- P3 (factored path): one 16 x 16 block (I, J <= I) per wave at a time,
+    //      computed transposed as in the exact path ------------------------------
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int idx = w + 4 * bi;
+      if (idx >= NBLK) break;
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+      const int J = idx - I * (I + 1) / 2;
       const int rrow = 16 * I + m, srow = 16 * J + m;
+      const float* scl = sScl + (size_t)idx * D;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         FragT lk, lq, rhs;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int ch = 32 * kb + 16 * hh + 4 * g;
-          float kk[4], qq[4], ks[4];
-          load4f(sK + rrow * LD + ch, kk);
-          load4f(sQ + rrow * LD + ch, qq);
-          load4f(sK + srow * LD + ch, ks);
-          const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + rrow * GLD + ch);
-          const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * GLD + ch);
-          const floatx4 bI = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
+          const V4 a = *reinterpret_cast<const V4*>(sLK + rrow * LD + ch);
+          const V4 bq = *reinterpret_cast<const V4*>(sLQ + rrow * LD + ch);
+          const floatx4 rv = *reinterpret_cast<const floatx4*>(sRR + srow * GLD + ch);
+          const floatx4 sc = *reinterpret_cast<const floatx4*>(scl + ch);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float pl = fast_exp2(gr[j] - bI[j]);
-            lk[4 * hh + j] = from_f<E>(kk[j] * pl);
-            lq[4 * hh + j] = from_f<E>(qq[j] * pl);
-            rhs[4 * hh + j] = from_f<E>(ks[j] * fast_exp2(bI[j] - gs[j]));
+            lk[4 * hh + j] = a[j];
+            lq[4 * hh + j] = bq[j];
+            rhs[4 * hh + j] = from_f<E>(rv[j] * sc[j]);
           }
         }
         mma(accA[bi], rhs, lk);
         mma(accP[bi], rhs, lq);
       }
-    }
-    // P to the record: this block is half of fragment (I, J / 2)
-    const int r = 16 * I + m;
-    float pv[4];
+      const int r = rrow;
+      float pv[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
-    store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
-  }
-  // zero halves of the P fragments above the diagonal (J > I, J < 2 NKC)
-  for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
-    const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
-    if (J > I) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
+      for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
+      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
     }
-  }
-  // (K e^{g_C - G})^T to the record: thread item = (channel, 4 consecutive chunk rows),
-  // which is half of one lane's fragment
-  for (int it = t; it < D * (CK / 4); it += 256) {
-    const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-    float kv[4];
+    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
+      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
+      if (J > I) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
+      }
+    }
+    // (K e^{g_C - G})^T = rhs_s 2^(g_C - b_{J+1}) to the record
+    for (int it = t; it < D * (CK / 4); it += 256) {
+      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
+      float kv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = s0 + j;
-      kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        kv[j] = (s < C) ? sRR[s * GLD + ch] * sScl[(NBLK + (s >> 4)) * D + ch] : 0.f;
+      }
+      const int kb = s0 >> 5, so = s0 & 31;
+      const int fg = (so & 15) >> 2, fh = so >> 4;
+      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
     }
-    const int kb = s0 >> 5, so = s0 & 31;
-    const int fg = (so & 15) >> 2, fh = so >> 4;
-    store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
+  } else {
+    // ---- P2 (exact path): Q e^G straight to its fragment slot (4 consecutive channels are half of a
+    //          lane's fragment); K e^G kept for B0; raw q, k to LDS ----------------------
+  #pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i;
+      const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      float qt[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float eg = fast_exp2(gr[j]);  // exponent <= 0
+        qt[j] = qr[i][j] * eg;
+        ktr[i][j] = kr[i][j] * eg;
+      }
+      store4f(sK + r * LD + ch0, kr[i]);
+      store4f(sQ + r * LD + ch0, qr[i]);
+      const int kb = ch0 >> 5, co = ch0 & 31;
+      const int fg = (co & 15) >> 2, fh = co >> 4;
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+    }
+    __syncthreads();
+
+    // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time. Computed
+    //          transposed: lane (m, g), element ii holds entry (r = 16 I + m,
+    //          s = 16 J + 4 g + ii). lhs_r = x_r 2^(gh_r - b_I) (x = k or q),
+    //          rhs_s = k_s 2^(b_I - gh_s). -----------------------------------------------
+  #pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int idx = w + 4 * bi;
+      if (idx >= NBLK) break;
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+      const int J = idx - I * (I + 1) / 2;
+      if (J == I && sFlag[I]) {
+        // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
+        const int r = 16 * I + m;
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 16 * J + 4 * g + ii;
+          float sa = 0.f, sp = 0.f;
+          if (s <= r) {
+            for (int ch = 0; ch < D; ++ch) {
+              const float ks = to_f(sK[s * LD + ch]) * fast_exp2(sG[r * GLD + ch] - sG[s * GLD + ch]);
+              sa += to_f(sK[r * LD + ch]) * ks;
+              sp += to_f(sQ[r * LD + ch]) * ks;
+            }
+          }
+          accA[bi][ii] = sa;
+          accP[bi][ii] = sp;
+        }
+      } else {
+        const int rrow = 16 * I + m, srow = 16 * J + m;
+  #pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          FragT lk, lq, rhs;
+  #pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int ch = 32 * kb + 16 * hh + 4 * g;
+            float kk[4], qq[4], ks[4];
+            load4f(sK + rrow * LD + ch, kk);
+            load4f(sQ + rrow * LD + ch, qq);
+            load4f(sK + srow * LD + ch, ks);
+            const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + rrow * GLD + ch);
+            const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * GLD + ch);
+            const floatx4 bI = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float pl = fast_exp2(gr[j] - bI[j]);
+              lk[4 * hh + j] = from_f<E>(kk[j] * pl);
+              lq[4 * hh + j] = from_f<E>(qq[j] * pl);
+              rhs[4 * hh + j] = from_f<E>(ks[j] * fast_exp2(bI[j] - gs[j]));
+            }
+          }
+          mma(accA[bi], rhs, lk);
+          mma(accP[bi], rhs, lq);
+        }
+      }
+      // P to the record: this block is half of fragment (I, J / 2)
+      const int r = 16 * I + m;
+      float pv[4];
+  #pragma unroll
+      for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
+      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+    }
+    // zero halves of the P fragments above the diagonal (J > I, J < 2 NKC)
+    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
+      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
+      if (J > I) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
+      }
+    }
+    // (K e^{g_C - G})^T to the record: thread item = (channel, 4 consecutive chunk rows),
+    // which is half of one lane's fragment
+    for (int it = t; it < D * (CK / 4); it += 256) {
+      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
+      float kv[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
+      }
+      const int kb = s0 >> 5, so = s0 & 31;
+      const int fg = (so & 15) >> 2, fh = so >> 4;
+      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
+    }
   }
   __syncthreads();  // phase A buffers are dead from here on
 

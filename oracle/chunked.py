@@ -87,11 +87,13 @@ def forward(q, k, v, log_alpha, beta, S0=None, chunk=64, step=chunk_step):
 #   b_0 = 0, b_I = gh[sub*I - 1]  (gh = log2-domain cumsum, b at each sub-chunk's top)
 #   plus_r  = 2^(gh_r - b_I)      (r in sub-chunk I)      in (0, 1]
 #   minus_s = 2^(b_{J+1} - gh_s)  (s in sub-chunk J)      in (0, 1]
-#   off-diagonal I > J: 2^(gh_r - gh_s) = [plus_r 2^(b_I - b_{J+1})] * minus_s   (both <= 1)
-#   diagonal I:         2^(gh_r - gh_s) = [plus_r 2^(R_I/2)] * [minus_s 2^(R_I/2)],
-#                       R_I = b_I - b_{I+1} per channel; both factors in [2^-R/2, 2^R/2]
-#   when max_c R_I > threshold the diagonal block falls back to 2^(gh_r - gh_s)
-#   element by element (exponent <= 0). Masked entries are discarded by selection.
+#   block (I, J <= I): 2^(gh_r - gh_s) = plus_r * [minus_s 2^(b_I - b_{J+1})]
+#     off the diagonal the block scale 2^(b_I - b_{J+1}) is <= 1;
+#     on the diagonal it is 2^(R_I), R_I = b_I - b_{I+1} per channel
+#   when max_c R_I > threshold for some sub-chunk, the chunk takes an exact path:
+#   every block uses plus_r * 2^(b_I - gh_s) (exponent <= 0 off the diagonal), and
+#   the diagonal blocks past the threshold fall back to 2^(gh_r - gh_s) element by
+#   element (exponent <= 0). Masked entries are discarded by selection.
 #   Q~ = q * plus * 2^(b_I);  K~ = k * plus * 2^(b_I);  K~end_s = k_s * minus_s * 2^(b_n - b_{J+1});
 #   gamma = 2^(b_n).
 # ---------------------------------------------------------------------------
@@ -100,7 +102,6 @@ def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.f
     """Forms A, P, Q~, K~, K~end, gamma of one chunk with the factored scheme, in
     ``dtype`` arithmetic. Returns a dict with those and ``fallback`` (list of the
     diagonal sub-blocks that took the element-wise path)."""
-    f = np.dtype(dtype).type
     C, dk = q.shape
     n_sub = (C + sub - 1) // sub
     la2 = (np.asarray(log_alpha, dtype=np.float64) * LOG2E).astype(dtype)
@@ -120,25 +121,28 @@ def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.f
     A = np.zeros((C, C), dtype=dtype)
     P = np.zeros((C, C), dtype=dtype)
     fallback = []
+    over = [I for I in range(n_sub) if np.max(b[I] - b[I + 1]) > threshold]
+    exact = len(over) > 0
     with np.errstate(over="raise", invalid="raise"):
         for I in range(n_sub):
             rI = slice(sub * I, min(C, sub * (I + 1)))
+            lhs_k = k[rI] * plus[rI]
+            lhs_q = q[rI] * plus[rI]
             for J in range(I + 1):
                 sJ = slice(sub * J, min(C, sub * (J + 1)))
                 if J < I:
-                    sc = np.exp2(b[I] - b[J + 1])
-                    lhs_k = k[rI] * plus[rI] * sc
-                    lhs_q = q[rI] * plus[rI] * sc
-                    rhs = k[sJ] * minus[sJ]
+                    if exact:
+                        rhs = k[sJ] * np.exp2(b[I][None, :] - gh[sJ])
+                    else:
+                        rhs = k[sJ] * minus[sJ] * np.exp2(b[I] - b[J + 1])
                     A[rI, sJ] = lhs_k @ rhs.T
                     P[rI, sJ] = lhs_q @ rhs.T
                 else:
-                    R = b[I] - b[I + 1]
-                    if np.max(R) <= threshold:
-                        half = np.exp2(R * f(0.5))
-                        lhs_k = k[rI] * plus[rI] * half
-                        lhs_q = q[rI] * plus[rI] * half
-                        rhs = k[sJ] * minus[sJ] * half
+                    if I not in over:
+                        if exact:
+                            rhs = k[sJ] * np.exp2(b[I][None, :] - gh[sJ])
+                        else:
+                            rhs = k[sJ] * minus[sJ] * np.exp2(b[I] - b[I + 1])
                         blkA = lhs_k @ rhs.T
                         blkP = lhs_q @ rhs.T
                     else:
