@@ -17,6 +17,9 @@ Contents
     factoring, each checked against the sequential recurrence.
 ``exact``
     Exact rational evaluation of the dense form for the golden fixtures.
+``fused``
+    The layer's prologue (q, k L2 normalisation, gate and beta activations) and
+    epilogue (output RMSNorm and gate) around the recurrence.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test; none is
 "parity unpinned".

@@ -55,14 +55,60 @@
 
 #define ORACLE_COL_BLOCK 16
 
-int kda_oracle_abi_version(void) { return 1; }
+int kda_oracle_abi_version(void) { return 2; }
 
-int kda_oracle_forward(const float *q, const float *k, const float *v,
-                       const float *log_alpha, const float *beta,
-                       const double *initial_state, const int64_t *seq_starts,
-                       int num_seqs, int H, int dk, int dv, const int *heads,
-                       int n_heads_sel, int col_begin, int col_end,
-                       double *o_sel, double *final_sel, int num_threads) {
+/*
+ * Optional prologue on the raw projections, as the Kimi Linear layer applies it
+ * before the recurrence (GeekNews "Kimi Linear" summary, section "Kimi Linear 모델
+ * 구성": q and k get an L2 normalisation for eigenvalue stability; the per-channel
+ * decay gate uses a GDN/Mamba-like decay function of a low-rank projection).
+ * Readings where the page leaves a step open:
+ *   ORACLE_NORM_QK  q_t <- q_t / sqrt(sum_i q_ti^2 + eps), the same for k_t
+ *   ORACLE_GATE_PRE log_alpha holds a pre-activation a: log alpha = -softplus(a)
+ *   ORACLE_BETA_PRE beta holds a pre-activation b: beta = sigmoid(b)
+ */
+#define ORACLE_NORM_QK 1
+#define ORACLE_GATE_PRE 2
+#define ORACLE_BETA_PRE 4
+
+static double softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+static double sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* One token's inputs in fp64 after the prologue: kd, qd = key and query,
+ * alpha = per-channel decay, *b = beta. */
+static void token_inputs(const float *k, const float *q, const float *log_alpha, float beta, int dk, int flags,
+                         double qk_eps, double *kd, double *qd, double *alpha, double *b) {
+  double sk = 0.0, sq = 0.0;
+  for (int i = 0; i < dk; ++i) {
+    kd[i] = (double)k[i];
+    qd[i] = (double)q[i];
+    sk += kd[i] * kd[i];
+    sq += qd[i] * qd[i];
+  }
+  if (flags & ORACLE_NORM_QK) {
+    const double ik = 1.0 / sqrt(sk + qk_eps), iq = 1.0 / sqrt(sq + qk_eps);
+    for (int i = 0; i < dk; ++i) {
+      kd[i] *= ik;
+      qd[i] *= iq;
+    }
+  }
+  for (int i = 0; i < dk; ++i) {
+    const double la = (flags & ORACLE_GATE_PRE) ? -softplus((double)log_alpha[i]) : (double)log_alpha[i];
+    alpha[i] = exp(la);
+  }
+  *b = (flags & ORACLE_BETA_PRE) ? sigmoid((double)beta) : (double)beta;
+}
+
+int kda_oracle_forward_ex(const float *q, const float *k, const float *v,
+                          const float *log_alpha, const float *beta,
+                          const double *initial_state, const int64_t *seq_starts,
+                          int num_seqs, int H, int dk, int dv, const int *heads,
+                          int n_heads_sel, int col_begin, int col_end,
+                          double *o_sel, double *final_sel, int num_threads, int flags, double qk_eps) {
   if (!q || !k || !v || !log_alpha || !beta || !seq_starts) return -1;
   if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   if (col_begin < 0 || col_end > dv || col_begin > col_end) return -1;
@@ -89,7 +135,8 @@ int kda_oracle_forward(const float *q, const float *k, const float *v,
     const int w = c1 - c0;
 
     double *S = (double *)malloc(sizeof(double) * (size_t)dk * w);
-    double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *tok = (double *)malloc(sizeof(double) * (size_t)dk * 3);
+    double *kt = tok, *qt = tok + dk, *alpha = tok + 2 * dk;
     double e[ORACLE_COL_BLOCK];
 
     /* S_0: the given initial state, or zeros */
@@ -103,21 +150,21 @@ int kda_oracle_forward(const float *q, const float *k, const float *v,
     for (int64_t t = seq_starts[n]; t < seq_starts[n + 1]; ++t) {
       const size_t rk = ((size_t)t * H + h) * dk;
       const size_t rv = ((size_t)t * H + h) * dv;
-      const double b = (double)beta[(size_t)t * H + h];
-      /* S' = Diag(alpha_t) S_{t-1}: row i scaled by alpha_i = exp(log_alpha_i) */
-      for (int i = 0; i < dk; ++i) alpha[i] = exp((double)log_alpha[rk + i]);
+      double b;
+      token_inputs(k + rk, q + rk, log_alpha + rk, beta[(size_t)t * H + h], dk, flags, qk_eps, kt, qt, alpha, &b);
+      /* S' = Diag(alpha_t) S_{t-1}: row i scaled by alpha_i */
       for (int i = 0; i < dk; ++i)
         for (int j = 0; j < w; ++j) S[(size_t)i * w + j] *= alpha[i];
       /* e = v_t - S'^T k_t: what the key reads back, subtracted from the new value */
       for (int j = 0; j < w; ++j) e[j] = 0.0;
       for (int i = 0; i < dk; ++i) {
-        const double ki = (double)k[rk + i];
+        const double ki = kt[i];
         for (int j = 0; j < w; ++j) e[j] += ki * S[(size_t)i * w + j];
       }
       for (int j = 0; j < w; ++j) e[j] = (double)v[rv + c0 + j] - e[j];
       /* S_t = S' + beta_t k_t e^T: the difference written back along the key */
       for (int i = 0; i < dk; ++i) {
-        const double bki = b * (double)k[rk + i];
+        const double bki = b * kt[i];
         for (int j = 0; j < w; ++j) S[(size_t)i * w + j] += bki * e[j];
       }
       /* o_t = S_t^T q_t */
@@ -125,7 +172,7 @@ int kda_oracle_forward(const float *q, const float *k, const float *v,
         double acc[ORACLE_COL_BLOCK];
         for (int j = 0; j < w; ++j) acc[j] = 0.0;
         for (int i = 0; i < dk; ++i) {
-          const double qi = (double)q[rk + i];
+          const double qi = qt[i];
           for (int j = 0; j < w; ++j) acc[j] += qi * S[(size_t)i * w + j];
         }
         double *orow = o_sel + ((size_t)t * n_heads_sel + hs) * ncols + (c0 - col_begin);
@@ -138,10 +185,20 @@ int kda_oracle_forward(const float *q, const float *k, const float *v,
         for (int j = 0; j < w; ++j)
           final_sel[(((size_t)n * n_heads_sel + hs) * dk + i) * ncols + (c0 - col_begin) + j] =
               S[(size_t)i * w + j];
-    free(alpha);
+    free(tok);
     free(S);
   }
   return 0;
+}
+
+int kda_oracle_forward(const float *q, const float *k, const float *v,
+                       const float *log_alpha, const float *beta,
+                       const double *initial_state, const int64_t *seq_starts,
+                       int num_seqs, int H, int dk, int dv, const int *heads,
+                       int n_heads_sel, int col_begin, int col_end,
+                       double *o_sel, double *final_sel, int num_threads) {
+  return kda_oracle_forward_ex(q, k, v, log_alpha, beta, initial_state, seq_starts, num_seqs, H, dk, dv, heads,
+                               n_heads_sel, col_begin, col_end, o_sel, final_sel, num_threads, 0, 0.0);
 }
 
 /*
@@ -149,10 +206,10 @@ int kda_oracle_forward(const float *q, const float *k, const float *v,
  * the same recurrence for a single token. state: [N][H][dk][dv] float64 in/out;
  * q, k, log_alpha: [N][H][dk]; v: [N][H][dv]; beta: [N][H]; o: [N][H][dv] float64.
  */
-int kda_oracle_decode_step(const float *q, const float *k, const float *v,
-                           const float *log_alpha, const float *beta,
-                           double *state, double *o, int N, int H, int dk, int dv,
-                           int num_threads) {
+int kda_oracle_decode_step_ex(const float *q, const float *k, const float *v,
+                              const float *log_alpha, const float *beta,
+                              double *state, double *o, int N, int H, int dk, int dv,
+                              int num_threads, int flags, double qk_eps) {
   if (!q || !k || !v || !log_alpha || !beta || !state || !o) return -1;
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const long long ntask = (long long)N * H;
@@ -162,25 +219,36 @@ int kda_oracle_decode_step(const float *q, const float *k, const float *v,
 #endif
   for (long long nh = 0; nh < ntask; ++nh) {
     double *S = state + (size_t)nh * dk * dv;
-    const float *qq = q + (size_t)nh * dk, *kk = k + (size_t)nh * dk;
-    const float *la = log_alpha + (size_t)nh * dk, *vv = v + (size_t)nh * dv;
-    const double b = (double)beta[nh];
+    const float *vv = v + (size_t)nh * dv;
     double *oo = o + (size_t)nh * dv;
+    double *tok = (double *)malloc(sizeof(double) * (size_t)dk * 3);
+    double *kt = tok, *qt = tok + dk, *alpha = tok + 2 * dk;
+    double b;
+    token_inputs(k + (size_t)nh * dk, q + (size_t)nh * dk, log_alpha + (size_t)nh * dk, beta[nh], dk, flags, qk_eps,
+                 kt, qt, alpha, &b);
     for (int i = 0; i < dk; ++i) {
-      const double a = exp((double)la[i]);
+      const double a = alpha[i];
       for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
     }
     for (int j = 0; j < dv; ++j) {
       double r = 0.0;
-      for (int i = 0; i < dk; ++i) r += (double)kk[i] * S[(size_t)i * dv + j];
+      for (int i = 0; i < dk; ++i) r += kt[i] * S[(size_t)i * dv + j];
       const double ej = (double)vv[j] - r;
       double acc = 0.0;
       for (int i = 0; i < dk; ++i) {
-        S[(size_t)i * dv + j] += b * (double)kk[i] * ej;
-        acc += (double)qq[i] * S[(size_t)i * dv + j];
+        S[(size_t)i * dv + j] += b * kt[i] * ej;
+        acc += qt[i] * S[(size_t)i * dv + j];
       }
       oo[j] = acc;
     }
+    free(tok);
   }
   return 0;
+}
+
+int kda_oracle_decode_step(const float *q, const float *k, const float *v,
+                           const float *log_alpha, const float *beta,
+                           double *state, double *o, int N, int H, int dk, int dv,
+                           int num_threads) {
+  return kda_oracle_decode_step_ex(q, k, v, log_alpha, beta, state, o, N, H, dk, dv, num_threads, 0, 0.0);
 }

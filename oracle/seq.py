@@ -28,10 +28,15 @@ def load_library(path=None):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
+    D = ctypes.c_double
     lib.kda_oracle_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P, P, I]
     lib.kda_oracle_forward.restype = I
+    lib.kda_oracle_forward_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P, P, I, I, D]
+    lib.kda_oracle_forward_ex.restype = I
     lib.kda_oracle_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
     lib.kda_oracle_decode_step.restype = I
+    lib.kda_oracle_decode_step_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D]
+    lib.kda_oracle_decode_step_ex.restype = I
     lib.kda_oracle_abi_version.restype = I
     if own:
         _lib = lib
@@ -46,6 +51,15 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+# prologue flags of the C oracle (see kda_oracle.c)
+NORM_QK, GATE_PRE, BETA_PRE = 1, 2, 4
+
+
+def prologue_flags(normalize_qk=False, gate_preactivation=False, beta_preactivation=False):
+    return (NORM_QK if normalize_qk else 0) | (GATE_PRE if gate_preactivation else 0) | \
+        (BETA_PRE if beta_preactivation else 0)
+
+
 def default_threads() -> int:
     try:
         return max(1, len(os.sched_getaffinity(0)))
@@ -54,7 +68,8 @@ def default_threads() -> int:
 
 
 def forward(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None,
-            heads=None, cols=None, num_threads=None, want_o=True, want_final=True, lib=None):
+            heads=None, cols=None, num_threads=None, want_o=True, want_final=True, lib=None,
+            flags=0, qk_eps=0.0):
     """Sequential fp64 KDA over every sequence.
 
     q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H].
@@ -65,7 +80,9 @@ def forward(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None,
     columns to compute (default all). Returns (o, final):
     o [B, T, len(heads), c1-c0] float64, final [N, len(heads), dk, c1-c0] float64.
     ``lib`` substitutes another build of the same C source (used by the test that
-    plants mistakes in copies of the oracle).
+    plants mistakes in copies of the oracle). ``flags`` (from ``prologue_flags``)
+    and ``qk_eps`` select the prologue on raw inputs: q, k L2 normalisation,
+    log_alpha = -softplus(preactivation), beta = sigmoid(preactivation).
     """
     lib = lib or load_library()
     q, k, v, log_alpha, beta = map(_f32, (q, k, v, log_alpha, beta))
@@ -94,16 +111,16 @@ def forward(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None,
         assert s0.shape == (N, H, dk, dv)
     o = np.zeros((B, T, nh, c1 - c0), dtype=np.float64) if want_o else None
     fin = np.zeros((N, nh, dk, c1 - c0), dtype=np.float64) if want_final else None
-    rc = lib.kda_oracle_forward(
+    rc = lib.kda_oracle_forward_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0), _ptr(starts),
         N, H, dk, dv, _ptr(heads_arr), nh, c0, c1, _ptr(o), _ptr(fin),
-        num_threads or default_threads())
+        num_threads or default_threads(), int(flags), float(qk_eps))
     if rc != 0:
         raise ValueError(f"kda_oracle_forward rejected its arguments (status {rc})")
     return o, fin
 
 
-def decode_step(q, k, v, log_alpha, beta, state, num_threads=None):
+def decode_step(q, k, v, log_alpha, beta, state, num_threads=None, flags=0, qk_eps=0.0):
     """One in-place fp64 decode step. q, k, log_alpha: [N, H, dk]; v: [N, H, dv];
     beta: [N, H]; state: [N, H, dk, dv] float64 (updated in place). Returns o
     [N, H, dv] float64."""
@@ -114,9 +131,9 @@ def decode_step(q, k, v, log_alpha, beta, state, num_threads=None):
     dv = v.shape[-1]
     assert state.shape == (N, H, dk, dv)
     o = np.zeros((N, H, dv), dtype=np.float64)
-    rc = lib.kda_oracle_decode_step(
+    rc = lib.kda_oracle_decode_step_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
-        N, H, dk, dv, num_threads or default_threads())
+        N, H, dk, dv, num_threads or default_threads(), int(flags), float(qk_eps))
     if rc != 0:
         raise ValueError(f"kda_oracle_decode_step rejected its arguments (status {rc})")
     return o

@@ -23,13 +23,11 @@ SRC = os.path.join(os.path.dirname(HERE), "oracle", "kda_oracle.c")
 MUTANTS = {
     "decay_dropped": ("S[(size_t)i * w + j] *= alpha[i];", "(void)alpha;"),
     "delta_sign": ("e[j] = (double)v[rv + c0 + j] - e[j];", "e[j] = (double)v[rv + c0 + j] + e[j];"),
-    "beta_dropped": ("const double bki = b * (double)k[rk + i];", "const double bki = (double)k[rk + i]; (void)b;"),
-    "decay_channel_shift": ("alpha[i] = exp((double)log_alpha[rk + i]);",
-                            "alpha[i] = exp((double)log_alpha[rk + (i + 1) % dk]);"),
-    "read_with_q": ("const double ki = (double)k[rk + i];\n        for (int j = 0; j < w; ++j) e[j] += ki",
-                    "const double ki = (double)q[rk + i];\n        for (int j = 0; j < w; ++j) e[j] += ki"),
-    "output_with_k": ("const double qi = (double)q[rk + i];", "const double qi = (double)k[rk + i];"),
-    "decay_exponent": ("alpha[i] = exp((double)log_alpha[rk + i]);", "alpha[i] = exp(0.5 * (double)log_alpha[rk + i]);"),
+    "beta_dropped": ("const double bki = b * kt[i];", "const double bki = kt[i]; (void)b;"),
+    "decay_channel_shift": (": (double)log_alpha[i];", ": (double)log_alpha[(i + 1) % dk];"),
+    "read_with_q": ("const double ki = kt[i];", "const double ki = qt[i];"),
+    "output_with_k": ("const double qi = qt[i];", "const double qi = kt[i];"),
+    "decay_exponent": ("alpha[i] = exp(la);", "alpha[i] = exp(0.5 * la);"),
 }
 
 
