@@ -81,6 +81,50 @@ def cpu_baseline(inp, sample_tokens):
                       f"(fp64 sequential recurrence, {dt:.1f} s)"}
 
 
+def fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec, runs=5):
+    """The fused layer core on the same shapes: the prefill on raw q, k and gate /
+    beta pre-activations with the output RMSNorm and gate, and the fused decode
+    step. Timed by the library's events, outside the headline steps."""
+    B, T, H = pre.q.shape[:3]
+    raw = inputs.make_raw_prefill(3, B=B, T=T, H=H, dtype="bf16", device=dev)
+    fu = kda.fusion(out_gate=raw.out_gate, norm_weight=raw.norm_weight)
+    z_dec = torch.randn(o_dec.shape, device=dev).to(o_dec.dtype)
+    fu_dec = kda.fusion(out_gate=z_dec, norm_weight=raw.norm_weight)
+
+    def prefill():
+        kda.chunk_fwd(raw.q, raw.k, raw.v, raw.gate, raw.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws,
+                      fusion=fu)
+
+    def decode(i):
+        kda.decode_step(dec.q[i], dec.k[i], dec.v[i], dec.log_alpha[i], dec.beta[i], state, o=o_dec, fusion=fu_dec)
+
+    for i in range(2):
+        prefill()
+        decode(i)
+    torch.cuda.synchronize()
+    kda.timing_enable(True)
+    for i in range(runs):
+        prefill()
+        for j in range(8):
+            decode((i * 8 + j) % dec.q.shape[0])
+    torch.cuda.synchronize()
+    t = kda.timing_read()
+    kda.timing_enable(False)
+    ms = {name: tot / max(cnt, 1) for name, (tot, cnt) in t.items()}
+    prefill_ms = ms["plan"] + ms["intra"] + ms["inter"] + ms["outnorm"]
+    rows = T * H
+    outnorm_bytes = rows * 3 * 2 * D + 4 * D
+    dec_bytes = DEC_N * DEC_H * (DECODE_BYTES_PER_HEAD + 2 * D)
+    print(f"[bench] fused prefill {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"workload": "kda_prefill_T131072_H32_bf16 raw inputs (q, k unnormalised; gate and beta "
+                        "pre-activations; output RMSNorm and sigmoid gate) + kda_decode_N256_H32_bf16",
+            "prefill_ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
+            "kernel_ms": {k: round(ms[k], 4) for k in ("plan", "intra", "inter", "outnorm")},
+            "outnorm_GBps": round(outnorm_bytes / (ms["outnorm"] * 1e-3) / 1e9, 1),
+            "decode_ms_per_step": round(ms["decode"], 4),
+            "decode_GBps": round(dec_bytes / (ms["decode"] * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +134,8 @@ def main():
     ap.add_argument("--decode-inputs", type=int, default=1024, help="distinct decode tokens, cycled")
     ap.add_argument("--cpu-sample-tokens", type=int, default=PREFILL_T)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the timing of the fused layer core (prologue and epilogue in the kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of 1 GiB (for counter calibration) and exit")
     args = ap.parse_args()
@@ -217,6 +263,8 @@ def main():
         "kernels": kernels,
         "kernel_source_hash": src_hash,
     }
+    if not args.no_fused:
+        result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)

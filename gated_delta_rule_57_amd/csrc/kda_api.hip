@@ -156,12 +156,42 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk
   return kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype);
 }
 
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                  const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
-                  float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+namespace {
+int check_fusion(const kda_fusion* f) {
+  if (!f) return KDA_OK;
+  if (!(f->qk_eps >= 0.f) || !(f->norm_eps >= 0.f))
+    return fail(KDA_ERR_INVALID_ARG, "qk_eps and norm_eps must be >= 0");
+  if (f->out_gate) {
+    if (!f->norm_weight) return fail(KDA_ERR_INVALID_ARG, "out_gate needs norm_weight");
+    if (!aligned(f->out_gate, 16) || !aligned(f->norm_weight, 16))
+      return fail(KDA_ERR_INVALID_ARG, "out_gate and norm_weight must be 16-byte aligned");
+  }
+  return KDA_OK;
+}
+
+kda::Fusion to_internal(const kda_fusion* f) {
+  kda::Fusion u{};
+  if (f) {
+    u.normalize_qk = f->normalize_qk != 0;
+    u.qk_eps = f->qk_eps;
+    u.gate_preactivation = f->gate_preactivation != 0;
+    u.beta_preactivation = f->beta_preactivation != 0;
+    u.out_gate = f->out_gate;
+    u.norm_weight = f->out_gate ? f->norm_weight : nullptr;
+    u.norm_eps = f->norm_eps;
+  }
+  return u;
+}
+}  // namespace
+
+int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
+                        float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                        const kda_fusion* fusion, void* workspace, size_t workspace_bytes, void* stream) {
   const bool varlen = cu_seqlens != nullptr;
   int st = check_prefill(B, T, H, num_seqs, varlen, dk, dv, chunk, dtype);
+  if (st != KDA_OK) return st;
+  st = check_fusion(fusion);
   if (st != KDA_OK) return st;
   const int64_t tokens = (int64_t)B * T;
   if (tokens > 0) {
@@ -188,7 +218,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
     if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
   }
   hipError_t e = kda::launch_prefill(dtype, chunk, q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o,
-                                     final_state, B, T, H, ws, s);
+                                     final_state, B, T, H, to_internal(fusion), ws, s);
   if (!workspace) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;
@@ -197,13 +227,24 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
   return ok();
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                    float* state, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
+                  float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return kda_chunk_fwd_fused(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o, final_state, B, T, H,
+                             dk, dv, chunk, dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kda_decode_step_fused(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                          float* state, void* o, int N, int H, int dk, int dv, int dtype, const kda_fusion* fusion,
+                          void* stream) {
   if (dtype != KDA_BF16 && dtype != KDA_FP32) return fail(KDA_ERR_UNSUPPORTED, "dtype %d is not KDA_BF16 or KDA_FP32", dtype);
   if (dk != 128 || dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d: only 128 is supported", dk, dv);
   if (N < 0) return fail(KDA_ERR_INVALID_ARG, "N=%d must be >= 0", N);
   if (H <= 0) return fail(KDA_ERR_INVALID_ARG, "H=%d must be > 0", H);
   if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N*H is too large");
+  int st = check_fusion(fusion);
+  if (st != KDA_OK) return st;
   if (N == 0) return ok();
   const void* ptrs[] = {q, k, v, log_alpha, beta, state, o};
   const char* names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
@@ -212,9 +253,36 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
     const size_t need = (ptrs[i] == (const void*)beta) ? 4 : 16;
     if (!aligned(ptrs[i], need)) return fail(KDA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", names[i], need);
   }
-  hipError_t e = kda::launch_decode(dtype, q, k, v, log_alpha, beta, state, o, N, H,
+  hipError_t e = kda::launch_decode(dtype, q, k, v, log_alpha, beta, state, o, N, H, to_internal(fusion),
                                     reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                    float* state, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+  return kda_decode_step_fused(q, k, v, log_alpha, beta, state, o, N, H, dk, dv, dtype, nullptr, stream);
+}
+
+int kda_output_norm_gate(const void* o, const void* gate, const float* weight, void* out, int64_t rows, int dv,
+                         float eps, int dtype, void* stream) {
+  if (dtype != KDA_BF16 && dtype != KDA_FP32) return fail(KDA_ERR_UNSUPPORTED, "dtype %d is not KDA_BF16 or KDA_FP32", dtype);
+  if (dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dv=%d: only 128 is supported", dv);
+  if (rows < 0) return fail(KDA_ERR_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
+  if (rows > ((int64_t)1 << 34)) return fail(KDA_ERR_INVALID_ARG, "rows=%lld is too large", (long long)rows);
+  if (!(eps >= 0.f)) return fail(KDA_ERR_INVALID_ARG, "eps must be >= 0");
+  if (rows == 0) return ok();
+  const void* ptrs[] = {o, gate, weight, out};
+  const char* names[] = {"o", "gate", "weight", "out"};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s must be non-null", names[i]);
+    if (!aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  if (gate == out) return fail(KDA_ERR_INVALID_ARG, "gate must not alias out");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  kda::trace_begin(s);
+  hipError_t e = kda::launch_output_norm_gate(dtype, o, gate, weight, out, rows, eps, s);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "output norm launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -13,6 +13,7 @@
 // registers (16 float4 loads, streamed with non-temporal hints because the state
 // of a batch is larger than the last-level cache and is not reused within a step).
 #include "kda_device.h"
+#include "kda_fusion_dev.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -22,12 +23,12 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
                                                      const E* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
                                                      const float* __restrict__ beta,
-                                                     float* __restrict__ state, E* __restrict__ o) {
+                                                     float* __restrict__ state, E* __restrict__ o, Fusion fu) {
   __shared__ float s_ka[D];      // alpha_i k_i
   __shared__ float s_qa[D];      // alpha_i q_i
   __shared__ float s_alpha[D];
   __shared__ float s_k[D];
-  __shared__ float s_kq;
+  __shared__ float s_red[2][3];  // per wave of the first two: k.k, q.q, k.q
   __shared__ floatx4 s_part[8][32][2];  // per row group: partial r and p for 4 columns
 
   const int t = threadIdx.x;
@@ -41,22 +42,45 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
   for (int i = 0; i < 16; ++i)
     srow[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (size_t)(16 * rg + i) * D + 4 * cg));
 
+  // k^T k, q^T q and k^T q over the 128 channels: wave-level tree reductions in
+  // waves 0 and 1, combined through LDS
+  float kk = 0.f, qq = 0.f, a = 0.f;
   if (t < D) {
-    const float a = __expf(log_alpha[nh * D + t]);
-    const float kk = to_f(k[nh * D + t]);
-    const float qq = to_f(q[nh * D + t]);
+    float la = log_alpha[nh * D + t];
+    if (fu.gate_preactivation) la = -softplus_f(la);
+    a = __expf(la);
+    kk = to_f(k[nh * D + t]);
+    qq = to_f(q[nh * D + t]);
+    float pk = kk * kk, pq = qq * qq, pkq = kk * qq;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      pk += __shfl_xor(pk, off, 64);
+      pq += __shfl_xor(pq, off, 64);
+      pkq += __shfl_xor(pkq, off, 64);
+    }
+    if ((t & 63) == 0) {
+      s_red[t >> 6][0] = pk;
+      s_red[t >> 6][1] = pq;
+      s_red[t >> 6][2] = pkq;
+    }
+  }
+  __syncthreads();
+  // prologue on raw inputs: L2-normalise k and q
+  float ik = 1.f, iq = 1.f;
+  if (fu.normalize_qk) {
+    ik = rsqrtf(s_red[0][0] + s_red[1][0] + fu.qk_eps);
+    iq = rsqrtf(s_red[0][1] + s_red[1][1] + fu.qk_eps);
+  }
+  const float kq = (s_red[0][2] + s_red[1][2]) * ik * iq;
+  if (t < D) {
+    kk *= ik;
+    qq *= iq;
     s_alpha[t] = a;
     s_k[t] = kk;
     s_ka[t] = a * kk;
     s_qa[t] = a * qq;
-    // k^T q over the 128 channels: wave-level tree reduction (waves 0 and 1).
-    float prod = kk * qq;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) prod += __shfl_xor(prod, off, 64);
-    if ((t & 63) == 0) s_part[0][t >> 6][0][0] = prod;  // scratch slot, consumed below
   }
   __syncthreads();
-  if (t == 0) s_kq = s_part[0][0][0][0] + s_part[0][1][0][0];
 
   floatx4 r = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -65,7 +89,6 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
     r += ka * srow[i];
     p += qa * srow[i];
   }
-  __syncthreads();  // s_part scratch use above is finished
   s_part[rg][cg][0] = r;
   s_part[rg][cg][1] = p;
   __syncthreads();
@@ -78,8 +101,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
   }
   float vv[4];
   load4f(v + nh * D + 4 * cg, vv);
-  const float b = beta[nh];
-  const float kq = s_kq;
+  const float b = fu.beta_preactivation ? sigmoid_f(beta[nh]) : beta[nh];
   floatx4 u, out;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -88,6 +110,17 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
   }
   if (rg == 0) {
     float ov[4] = {out[0], out[1], out[2], out[3]};
+    if (fu.out_gate) {
+      // epilogue: RMSNorm over the 128 outputs (the 32 lanes of this half-wave hold
+      // them all), times the weight and the sigmoid output gate
+      const float inv = rsqrtf(half_wave_sum(ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3]) *
+                               (1.f / D) + fu.norm_eps);
+      float z[4];
+      load4f(reinterpret_cast<const E*>(fu.out_gate) + nh * D + 4 * cg, z);
+      const floatx4 wv = *reinterpret_cast<const floatx4*>(fu.norm_weight + 4 * cg);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) ov[jj] = ov[jj] * inv * wv[jj] * sigmoid_f(z[jj]);
+    }
     store4f(o + nh * D + 4 * cg, ov);
   }
 #pragma unroll
@@ -99,17 +132,18 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
 }
 
 hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                         const float* beta, float* state, void* o, int N, int H, hipStream_t stream) {
+                         const float* beta, float* state, void* o, int N, int H, const Fusion& fusion,
+                         hipStream_t stream) {
   const size_t units = (size_t)N * H;
   if (units == 0) return hipSuccess;
   dim3 grid((unsigned)units), block(256);
   trace_begin(stream);
   if (dtype == 0)
     hipLaunchKernelGGL(decode_kernel<__bf16>, grid, block, 0, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, log_alpha, beta, state, (__bf16*)o);
+                       (const __bf16*)v, log_alpha, beta, state, (__bf16*)o, fusion);
   else
     hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, stream, (const float*)q, (const float*)k,
-                       (const float*)v, log_alpha, beta, state, (float*)o);
+                       (const float*)v, log_alpha, beta, state, (float*)o, fusion);
   hipError_t e = hipGetLastError();
   trace_mark(stream, 3);
   return e;

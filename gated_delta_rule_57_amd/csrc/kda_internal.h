@@ -14,9 +14,27 @@ namespace kda {
 void trace_begin(hipStream_t stream);
 void trace_mark(hipStream_t stream, int kernel_id);
 
+// The layer's prologue (on raw q, k, gate and beta inputs) and epilogue (output
+// RMSNorm times a sigmoid gate), as described for kda_fusion in include/kda.h.
+// Passed to kernels by value; all-zero = the plain recurrence.
+struct Fusion {
+  int normalize_qk;
+  float qk_eps;
+  int gate_preactivation;
+  int beta_preactivation;
+  const void* out_gate;      // nullable; o's layout and dtype
+  const float* norm_weight;  // [128], with out_gate
+  float norm_eps;
+};
+
 // dtype: 0 = bf16, 1 = fp32 (the kda_dtype values).
 hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                         const float* beta, float* state, void* o, int N, int H, hipStream_t stream);
+                         const float* beta, float* state, void* o, int N, int H, const Fusion& fusion,
+                         hipStream_t stream);
+
+// out = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate), rows of 128 values; out may equal o.
+hipError_t launch_output_norm_gate(int dtype, const void* o, const void* gate, const float* weight, void* out,
+                                   int64_t rows, float eps, hipStream_t stream);
 
 // Upper bound on the number of chunks of a batch: B sequences of T tokens, or
 // num_seqs packed sequences totalling T tokens.
@@ -31,6 +49,6 @@ size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, i
 hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* initial_state,
                           const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
-                          int T, int H, void* workspace, hipStream_t stream);
+                          int T, int H, const Fusion& fusion, void* workspace, hipStream_t stream);
 
 }  // namespace kda

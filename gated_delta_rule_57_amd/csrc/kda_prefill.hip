@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "kda_device.h"
+#include "kda_fusion_dev.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
                                                     const float* __restrict__ beta,
                                                     const int32_t* __restrict__ total_chunks,
                                                     const int2* __restrict__ info, int H, int mc,
-                                                    char* __restrict__ records) {
+                                                    char* __restrict__ records, Fusion fu) {
   using SM = Smem<E, C>;
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
@@ -259,8 +260,40 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     load4f(q + off, qr[i]);
     load4f(v + off, vr[i]);
   }
-  if (t < CK) sBeta[t] = (t < len) ? beta[(size_t)(tok0 + t) * H + h] : 0.f;
+  if (t < CK) {
+    float bt = 0.f;
+    if (t < len) {
+      bt = beta[(size_t)(tok0 + t) * H + h];
+      if (fu.beta_preactivation) bt = sigmoid_f(bt);
+    }
+    sBeta[t] = bt;
+  }
   if (t < NSUB) sFlag[t] = 0;
+  // prologue on raw inputs: a row's 128 channels are spread over the 32 lanes of one
+  // half-wave (4 each), so its squared norm is a half-wave sum
+  if (fu.normalize_qk) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sk += kr[i][j] * kr[i][j];
+        sq += qr[i][j] * qr[i][j];
+      }
+      const float ik = rsqrtf(half_wave_sum(sk) + fu.qk_eps), iq = rsqrtf(half_wave_sum(sq) + fu.qk_eps);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kr[i][j] *= ik;
+        qr[i][j] *= iq;
+      }
+    }
+  }
+  if (fu.gate_preactivation) {  // log alpha = -softplus(a), kept in natural-log units here
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) la[i][j] = -softplus_f(la[i][j]);
+  }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rbase + 8 * i;
@@ -961,7 +994,7 @@ template <typename E, int C>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                         const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
                         float* final_state, int T, int H, int64_t mc, const WsLayout& l, char* ws,
-                        hipStream_t stream) {
+                        const Fusion& fusion, hipStream_t stream) {
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + l.off_chunk_off);
   int2* info = reinterpret_cast<int2*>(ws + l.off_info);
   char* records = ws + l.off_records;
@@ -975,7 +1008,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   if (mc > 0) {
     hipLaunchKernelGGL((intra_kernel<E, C>), dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
-                       records);
+                       records, fusion);
     e = hipGetLastError();
     trace_mark(stream, 1);
     if (e != hipSuccess) return e;
@@ -993,6 +1026,12 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
     }
     e = hipGetLastError();
     trace_mark(stream, 2);
+    if (e != hipSuccess) return e;
+  }
+  if (fusion.out_gate) {
+    const int64_t rows = (int64_t)(cu_seqlens ? T : (int64_t)N * T) * H;
+    e = launch_output_norm_gate(std::is_same<E, float>::value ? 1 : 0, o, fusion.out_gate, fusion.norm_weight, o,
+                                rows, fusion.norm_eps, stream);
   }
   return e;
 }
@@ -1005,7 +1044,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, i
 hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* initial_state,
                           const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
-                          int T, int H, void* workspace, hipStream_t stream) {
+                          int T, int H, const Fusion& fusion, void* workspace, hipStream_t stream) {
   const bool varlen = cu_seqlens != nullptr;
   const int N = varlen ? num_seqs : B;
   const WsLayout l = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype);
@@ -1014,15 +1053,15 @@ hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, co
   if (dtype == 0) {
     if (chunk == 16)
       return launch_typed<__bf16, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
-                                      mc, l, ws, stream);
+                                      mc, l, ws, fusion, stream);
     return launch_typed<__bf16, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
-                                    mc, l, ws, stream);
+                                    mc, l, ws, fusion, stream);
   }
   if (chunk == 16)
     return launch_typed<float, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H,
-                                   mc, l, ws, stream);
+                                   mc, l, ws, fusion, stream);
   return launch_typed<float, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, o, final_state, T, H, mc,
-                                 l, ws, stream);
+                                 l, ws, fusion, stream);
 }
 
 }  // namespace kda

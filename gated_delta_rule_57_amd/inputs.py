@@ -163,3 +163,57 @@ def make_decode(seed: int = 4, N: int = 256, H: int = 32, n_steps: int = 1024, d
         bs.append(torch.sigmoid(_normal(g, (N, H), device)))
     st = lambda xs: torch.stack(xs).contiguous()
     return DecodeInputs(s0, st(qs), st(ks), st(vs), st(las), st(bs), dtype)
+
+
+@dataclass
+class RawPrefillInputs:
+    """Inputs of the fused layer core (kda_fusion): raw projections and pre-activations."""
+    q: torch.Tensor            # [B, T, H, dk] compute dtype, not normalised
+    k: torch.Tensor            # [B, T, H, dk] compute dtype, not normalised
+    v: torch.Tensor            # [B, T, H, dv] compute dtype
+    gate: torch.Tensor         # [B, T, H, dk] fp32 pre-activation of the decay (log alpha = -softplus)
+    beta: torch.Tensor         # [B, T, H] fp32 pre-activation of beta (beta = sigmoid)
+    out_gate: torch.Tensor     # [B, T, H, dv] compute dtype, pre-activation of the output gate
+    norm_weight: torch.Tensor  # [dv] fp32 RMSNorm weight
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    dtype: str
+    chunk: int
+
+    @property
+    def num_seqs(self):
+        return self.q.shape[0] if self.cu_seqlens is None else self.cu_seqlens.numel() - 1
+
+    def numpy(self):
+        f = lambda t: None if t is None else t.detach().float().cpu().numpy()
+        cu = None if self.cu_seqlens is None else self.cu_seqlens.cpu().numpy().astype(np.int64)
+        return dict(q=f(self.q), k=f(self.k), v=f(self.v), gate=f(self.gate), beta=f(self.beta),
+                    out_gate=f(self.out_gate), norm_weight=f(self.norm_weight),
+                    initial_state=f(self.initial_state), cu_seqlens=cu)
+
+
+def make_raw_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64, gate_shift: float = -3.0,
+                     qk_scale: float = 3.0, s0_std: float = 0.0, num_seqs: Optional[int] = None, device="cuda",
+                     dk: int = D, dv: int = D) -> RawPrefillInputs:
+    """Raw layer inputs: q, k ~ qk_scale * N(0, 1) (not normalised); v ~ N(0, 1);
+    gate ~ N(gate_shift, 1) (gate_shift = -3 gives log alpha = -softplus(gate) near
+    -0.05, the decay range of the standard workloads); beta, out_gate ~ N(0, 1);
+    norm_weight ~ U(0.5, 1.5). Draw order: cut points, q, k, v, gate, beta, out_gate,
+    norm_weight, initial state."""
+    g = _gen(seed, device)
+    cu = None
+    if num_seqs is not None:
+        assert B == 1
+        cu = uniform_composition(g, T, num_seqs, device)
+    td = TORCH_DTYPE[dtype]
+    q = (qk_scale * _normal(g, (B, T, H, dk), device)).to(td)
+    k = (qk_scale * _normal(g, (B, T, H, dk), device)).to(td)
+    v = _normal(g, (B, T, H, dv), device).to(td)
+    gate = _normal(g, (B, T, H, dk), device) + gate_shift
+    beta = _normal(g, (B, T, H), device)
+    out_gate = _normal(g, (B, T, H, dv), device).to(td)
+    w = 0.5 + torch.rand((dv,), generator=g, device=device, dtype=torch.float32)
+    N = B if cu is None else cu.numel() - 1
+    s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
+    return RawPrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(), gate.contiguous(), beta.contiguous(),
+                            out_gate.contiguous(), w, s0, cu, dtype, chunk)

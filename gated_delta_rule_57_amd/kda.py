@@ -23,9 +23,18 @@ KDA_ERR_WORKSPACE = -3
 KDA_ERR_DEVICE = -4
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_fwd_workspace_size",
-           "kda_chunk_fwd", "kda_decode_step", "kda_timing_enable", "kda_timing_read")
+           "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused", "kda_decode_step_fused",
+           "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read")
 
-KERNEL_NAMES = ("plan", "intra", "inter", "decode")  # KDA_KERNEL_* ids
+KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm")  # KDA_KERNEL_* ids
+
+
+class Fusion(ctypes.Structure):
+    """kda_fusion (include/kda.h): the layer prologue and epilogue around the
+    recurrence. Build one with ``fusion()``."""
+    _fields_ = [("normalize_qk", ctypes.c_int), ("qk_eps", ctypes.c_float),
+                ("gate_preactivation", ctypes.c_int), ("beta_preactivation", ctypes.c_int),
+                ("out_gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):
@@ -52,6 +61,12 @@ def _load():
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.kda_decode_step.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.kda_chunk_fwd_fused.restype = I
+    lib.kda_chunk_fwd_fused.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, P, Z, P]
+    lib.kda_decode_step_fused.restype = I
+    lib.kda_decode_step_fused.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.kda_output_norm_gate.restype = I
+    lib.kda_output_norm_gate.argtypes = [P, P, P, P, ctypes.c_int64, I, ctypes.c_float, I, P]
     lib.kda_timing_enable.restype = I
     lib.kda_timing_enable.argtypes = [I]
     lib.kda_timing_read.restype = I
@@ -100,9 +115,35 @@ def workspace_size(B, T, H, num_seqs=0, chunk=64, dtype=KDA_BF16) -> int:
     return int(lib.kda_chunk_fwd_workspace_size(B, T, H, num_seqs, chunk, dtype))
 
 
+def fusion(normalize_qk=True, qk_eps=1e-6, gate_preactivation=True, beta_preactivation=True,
+           out_gate=None, norm_weight=None, norm_eps=1e-6):
+    """A kda_fusion for ``chunk_fwd`` / ``decode_step``. ``out_gate`` (o's shape and
+    dtype) and ``norm_weight`` (fp32 [128]) are device tensors or None; the returned
+    object keeps them referenced while it lives."""
+    if out_gate is not None:
+        if norm_weight is None:
+            raise ValueError("out_gate needs norm_weight")
+        _need(norm_weight, "norm_weight", torch.float32, (norm_weight.numel(),))
+        if not out_gate.is_contiguous():
+            raise ValueError("out_gate must be contiguous")
+    f = Fusion(int(bool(normalize_qk)), float(qk_eps), int(bool(gate_preactivation)), int(bool(beta_preactivation)),
+               None if out_gate is None else out_gate.data_ptr(),
+               None if out_gate is None else norm_weight.data_ptr(), float(norm_eps))
+    f._keep = (out_gate, norm_weight)
+    return f
+
+
+def _check_out_gate(f, o):
+    if f is not None and f.out_gate:
+        g = f._keep[0]
+        if g.dtype != o.dtype or tuple(g.shape) != tuple(o.shape) or g.device != o.device:
+            raise ValueError(f"out_gate must match o: {tuple(o.shape)} {o.dtype}")
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
-              output_final_state=True, o=None, final_state=None, workspace=None):
-    """Chunked KDA prefill through ``kda_chunk_fwd``.
+              output_final_state=True, o=None, final_state=None, workspace=None, fusion=None):
+    """Chunked KDA prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_fused`` when
+    ``fusion`` is given; see ``fusion()``).
 
     q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
     log_alpha: [B, T, H, 128] fp32; beta: [B, T, H] fp32;
@@ -141,17 +182,25 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 device tensor")
         ws_bytes = workspace.numel()
-    _check(lib.kda_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
-        N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
-        _ptr(workspace), ws_bytes, _stream(q.device)))
+    if fusion is None:
+        _check(lib.kda_chunk_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
+            _ptr(workspace), ws_bytes, _stream(q.device)))
+    else:
+        _check_out_gate(fusion, o)
+        _check(lib.kda_chunk_fwd_fused(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
+            ctypes.byref(fusion), _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, final_state
 
 
-def decode_step(q, k, v, log_alpha, beta, state, o=None):
-    """One decode step through ``kda_decode_step``; ``state`` [N, H, 128, 128] fp32
-    is updated in place. q, k, v: [N, H, 128]; log_alpha: [N, H, 128] fp32;
-    beta: [N, H] fp32. Returns o [N, H, 128]."""
+def decode_step(q, k, v, log_alpha, beta, state, o=None, fusion=None):
+    """One decode step through ``kda_decode_step`` (``kda_decode_step_fused`` when
+    ``fusion`` is given); ``state`` [N, H, 128, 128] fp32 is updated in place.
+    q, k, v: [N, H, 128]; log_alpha: [N, H, 128] fp32; beta: [N, H] fp32.
+    Returns o [N, H, 128]."""
     if q.dim() != 3:
         raise ValueError("q must be [N, H, dk]")
     N, H, dk = q.shape
@@ -168,9 +217,33 @@ def decode_step(q, k, v, log_alpha, beta, state, o=None):
         o = torch.empty((N, H, dv), dtype=dt, device=q.device)
     else:
         _need(o, "o", dt, (N, H, dv))
-    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
-                               N, H, dk, dv, dcode, _stream(q.device)))
+    if fusion is None:
+        _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                   N, H, dk, dv, dcode, _stream(q.device)))
+    else:
+        _check_out_gate(fusion, o)
+        _check(lib.kda_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state),
+                                         _ptr(o), N, H, dk, dv, dcode, ctypes.byref(fusion), _stream(q.device)))
     return o
+
+
+def output_norm_gate(o, gate, weight, eps=1e-6, out=None):
+    """``kda_output_norm_gate``: out = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate)
+    over the last axis (128). o, gate, out: same shape and dtype; weight: fp32 [128].
+    ``out`` may be ``o`` (in place)."""
+    dcode = _dtype_code(o)
+    dv = o.shape[-1]
+    _need(o, "o", o.dtype, tuple(o.shape))
+    _need(gate, "gate", o.dtype, tuple(o.shape))
+    _need(weight, "weight", torch.float32, (dv,))
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _need(out, "out", o.dtype, tuple(o.shape))
+    rows = o.numel() // dv
+    _check(lib.kda_output_norm_gate(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, dv, float(eps), dcode,
+                                    _stream(o.device)))
+    return out
 
 
 def timing_enable(on: bool = True):

@@ -20,7 +20,8 @@ import os
 import sys
 
 KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
-           ("inter_kernel", "inter"), ("decode_kernel", "decode"))
+           ("inter_kernel", "inter"), ("decode_kernel", "decode"),
+           ("output_norm_gate_kernel", "outnorm"))
 COPY_BYTES = 1 << 30
 
 

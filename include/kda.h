@@ -33,7 +33,8 @@
  *   - Every tensor pointer must be 16-byte aligned, except beta and cu_seqlens (4
  *     bytes) and the workspace (256 bytes); KDA_ERR_INVALID_ARG otherwise.
  *   - Value preconditions (documented, not checked): q and k are L2-normalised per
- *     (token, head) by the caller; log_alpha is finite and <= 0; beta is in [0, 1].
+ *     (token, head) by the caller; log_alpha is finite and <= 0; beta is in [0, 1]
+ *     (unless the kda_fusion prologue below derives them from raw inputs).
  *     Outside them the result is unspecified but every kernel still terminates.
  *   - No scale is applied to q.
  */
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Element type of q, k, v and o. */
 typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
@@ -128,11 +129,69 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *lo
                     int dtype, void *stream);
 
 /*
+ * The layer's prologue and epilogue, fused around the recurrence. The Kimi Linear
+ * layer (GeekNews "Kimi Linear" summary, section "Kimi Linear 모델 구성") L2-normalises
+ * each head's query and key for eigenvalue stability, takes the per-channel decay
+ * from a GDN/Mamba-like decay function of a low-rank projection, and applies a
+ * per-head RMSNorm and a data-dependent output gate before the output projection.
+ * Readings where the page is silent (the same as the oracle's):
+ *   normalize_qk        q and k are raw: each (token, head) row x becomes
+ *                       x / sqrt(sum_i x_i^2 + qk_eps)           (qk_eps >= 0)
+ *   gate_preactivation  log_alpha holds a pre-activation a: log alpha = -softplus(a)
+ *   beta_preactivation  beta holds a pre-activation b: beta = sigmoid(b)
+ *   out_gate            NULL, or z with o's layout and dtype: each output row becomes
+ *                       o / sqrt(mean_j o_j^2 + norm_eps) * norm_weight * sigmoid(z)
+ *                       (norm_weight: float32 [dv], shared by the heads, 16-byte
+ *                       aligned, required with out_gate; norm_eps >= 0)
+ * Zero-initialised = the plain recurrence. The prologue runs inside the kernels that
+ * read q, k, log_alpha and beta; the prefill epilogue is one more pass over o (a row
+ * needs all dv values, which the state kernel spreads over work-groups); the decode
+ * epilogue runs inside the decode kernel.
+ */
+typedef struct kda_fusion {
+  int normalize_qk;
+  float qk_eps;
+  int gate_preactivation;
+  int beta_preactivation;
+  const void *out_gate;
+  const float *norm_weight;
+  float norm_eps;
+} kda_fusion;
+
+/*
+ * kda_chunk_fwd with the prologue / epilogue of `fusion` (NULL = kda_chunk_fwd).
+ * All other arguments, the workspace and the errors are those of kda_chunk_fwd;
+ * a bad fusion field (negative eps, out_gate without norm_weight, misalignment)
+ * returns KDA_ERR_INVALID_ARG. With out_gate, o receives the gated, normalised output.
+ */
+int kda_chunk_fwd_fused(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                        int num_seqs, void *o, float *final_state, int B, int T, int H, int dk,
+                        int dv, int chunk, int dtype, const kda_fusion *fusion, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* kda_decode_step with the prologue / epilogue of `fusion` (NULL = kda_decode_step). */
+int kda_decode_step_fused(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, float *state, void *o, int N, int H, int dk, int dv,
+                          int dtype, const kda_fusion *fusion, void *stream);
+
+/*
+ * The output epilogue on its own: for each of `rows` rows of dv values,
+ * out = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate). o, gate and out have
+ * dtype `dtype` and the same [rows, dv] layout; weight is float32 [dv]; out may
+ * equal o (in place), gate must not alias out. dv = 128 only; rows = 0 is a no-op.
+ */
+int kda_output_norm_gate(const void *o, const void *gate, const float *weight, void *out, int64_t rows,
+                         int dv, float eps, int dtype, void *stream);
+
+/*
  * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd and
  * kda_decode_step call records HIP events on its stream before its first kernel
  * and after each kernel it launches, so the durations are measured on the stream
- * the kernels run on. Kernel ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA
- * (intra-chunk), KDA_KERNEL_INTER (inter-chunk state and output), KDA_KERNEL_DECODE.
+ * the kernels run on (the fused variants and kda_output_norm_gate included). Kernel
+ * ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA (intra-chunk), KDA_KERNEL_INTER
+ * (inter-chunk state and output), KDA_KERNEL_DECODE, KDA_KERNEL_OUTNORM (output
+ * RMSNorm and gate).
  *
  * kda_timing_enable(1) starts recording (and discards anything recorded before);
  * kda_timing_enable(0) stops. kda_timing_read() waits for the recorded events,
@@ -146,7 +205,8 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *lo
 #define KDA_KERNEL_INTRA 1
 #define KDA_KERNEL_INTER 2
 #define KDA_KERNEL_DECODE 3
-#define KDA_NUM_KERNELS 4
+#define KDA_KERNEL_OUTNORM 4
+#define KDA_NUM_KERNELS 5
 
 int kda_timing_enable(int on);
 int kda_timing_read(double *total_ms, int *launches, int n);

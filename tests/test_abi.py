@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.kda_abi_version() == 1
+    version = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.kda_abi_version() == version == 2
     for st in (0, -1, -2, -3, -4):
         assert L.kda_status_string(st).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(7)
@@ -116,3 +117,64 @@ def test_workspace_size():
     assert ws(1, 64, 1, 0, 32, 0) == 0
     assert ws(1, 64, 0, 0, 64, 0) == 0
     assert ws(1, 64, 1, 0, 64, 9) == 0
+
+
+def fused_chunk_call(fusion, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num_seqs=0, o=FAKE, fin=None,
+                B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0)
+    args.update(kw)
+    a = args
+    return L.kda_chunk_fwd_fused(a["q"], a["k"], a["v"], a["la"], a["beta"], a["s0"], a["cu"], a["num_seqs"],
+                                 a["o"], a["fin"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["dtype"],
+                                 None if fusion is None else ctypes.byref(fusion), None, 0, None)
+
+
+def make_fusion(**kw):
+    f = kda.Fusion(1, 1e-6, 1, 1, None, None, 1e-6)
+    for k, v in kw.items():
+        setattr(f, k, v)
+    return f
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qk_eps=-1.0),
+    dict(norm_eps=float("nan")),
+    dict(out_gate=1 << 20),                              # no norm weight
+    dict(out_gate=(1 << 20) + 8, norm_weight=1 << 20),   # misaligned gate
+    dict(out_gate=1 << 20, norm_weight=(1 << 20) + 4),   # misaligned weight
+])
+def test_fused_entry_points_reject_bad_fusion(kw):
+    f = make_fusion(**kw)
+    assert fused_chunk_call(f) == kda.KDA_ERR_INVALID_ARG
+    assert L.kda_decode_step_fused(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 128, 0,
+                                   ctypes.byref(f), None) == kda.KDA_ERR_INVALID_ARG
+
+
+def test_fused_entry_points_keep_the_plain_checks():
+    f = make_fusion()
+    assert fused_chunk_call(f, dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert fused_chunk_call(f, q=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert fused_chunk_call(f, B=0, q=None, k=None, v=None, la=None, beta=None, o=None) == kda.KDA_OK
+    assert fused_chunk_call(None, B=0, q=None) == kda.KDA_OK
+    assert L.kda_decode_step_fused(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 2, 128, 128, 0,
+                                   ctypes.byref(f), None) == kda.KDA_ERR_INVALID_ARG
+    assert L.kda_decode_step_fused(None, None, None, None, None, None, None, 0, 2, 128, 128, 0,
+                                   ctypes.byref(f), None) == kda.KDA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dv=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=3), kda.KDA_ERR_UNSUPPORTED),
+    (dict(rows=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(gate=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(weight=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(gate=ctypes.c_void_p(1 << 22), out=ctypes.c_void_p(1 << 22)), kda.KDA_ERR_INVALID_ARG),
+    (dict(rows=0, o=None, gate=None), kda.KDA_OK),
+])
+def test_output_norm_gate_rejects(kw, status):
+    a = dict(o=FAKE, gate=ctypes.c_void_p(1 << 21), weight=FAKE, out=ctypes.c_void_p(1 << 23), rows=16, dv=128,
+             eps=1e-6, dtype=0)
+    a.update(kw)
+    assert L.kda_output_norm_gate(a["o"], a["gate"], a["weight"], a["out"], a["rows"], a["dv"], a["eps"],
+                                  a["dtype"], None) == status
