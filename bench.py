@@ -125,6 +125,41 @@ def fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec, ru
             "decode_GBps": round(dec_bytes / (ms["decode"] * 1e-3) / 1e9, 1)}
 
 
+def gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec, runs=5):
+    """The scalar-gate (one decay per token and head) and no-decay paths on the
+    headline prefill shape and the decode batch, timed by the library's events."""
+    B, T, H = pre.q.shape[:3]
+    la_head = pre.log_alpha[..., 0].contiguous()
+    la_dec = dec.log_alpha[..., 0].contiguous()
+    out = {}
+    for name, la, lad in (("gated_deltanet", la_head, la_dec), ("deltanet", None, None)):
+        def run(i):
+            kda.chunk_fwd(pre.q, pre.k, pre.v, la, pre.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws)
+            for j in range(8):
+                d = (i * 8 + j) % dec.q.shape[0]
+                kda.decode_step(dec.q[d], dec.k[d], dec.v[d], None if lad is None else lad[d], dec.beta[d], state,
+                                o=o_dec)
+        run(0)
+        torch.cuda.synchronize()
+        kda.timing_enable(True)
+        for i in range(runs):
+            run(i + 1)
+        torch.cuda.synchronize()
+        t = kda.timing_read()
+        kda.timing_enable(False)
+        ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items()}
+        prefill_ms = ms["plan"] + ms["intra"] + ms["inter"]
+        tok_heads = T * H
+        gate_bytes = 0 if la is None else 4
+        intra_bytes = tok_heads * (3 * 2 * D + gate_bytes + 4) + (T // CHUNK) * H * RECORD_BYTES_BF16_C64
+        out[name] = {"prefill_ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
+                     "kernel_ms": {k: round(ms[k], 4) for k in ("plan", "intra", "inter")},
+                     "intra_GBps": round(intra_bytes / (ms["intra"] * 1e-3) / 1e9, 1),
+                     "decode_ms_per_step": round(ms["decode"], 4)}
+        print(f"[bench] {name} prefill {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +169,8 @@ def main():
     ap.add_argument("--decode-inputs", type=int, default=1024, help="distinct decode tokens, cycled")
     ap.add_argument("--cpu-sample-tokens", type=int, default=PREFILL_T)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gates", action="store_true",
+                    help="skip the timing of the scalar-gate (Gated DeltaNet) and no-decay (DeltaNet) paths")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the timing of the fused layer core (prologue and epilogue in the kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -265,6 +302,8 @@ def main():
     }
     if not args.no_fused:
         result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec)
+    if not args.no_gates:
+        result["gates"] = gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)

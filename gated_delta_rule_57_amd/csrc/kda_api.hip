@@ -161,6 +161,8 @@ int check_fusion(const kda_fusion* f) {
   if (!f) return KDA_OK;
   if (!(f->qk_eps >= 0.f) || !(f->norm_eps >= 0.f))
     return fail(KDA_ERR_INVALID_ARG, "qk_eps and norm_eps must be >= 0");
+  if (f->gate_kind < KDA_GATE_CHANNEL || f->gate_kind > KDA_GATE_NONE)
+    return fail(KDA_ERR_INVALID_ARG, "gate_kind %d is not a kda_gate", f->gate_kind);
   if (f->out_gate) {
     if (!f->norm_weight) return fail(KDA_ERR_INVALID_ARG, "out_gate needs norm_weight");
     if (!aligned(f->out_gate, 16) || !aligned(f->norm_weight, 16))
@@ -179,6 +181,7 @@ kda::Fusion to_internal(const kda_fusion* f) {
     u.out_gate = f->out_gate;
     u.norm_weight = f->out_gate ? f->norm_weight : nullptr;
     u.norm_eps = f->norm_eps;
+    u.gate_kind = f->gate_kind;
   }
   return u;
 }
@@ -193,15 +196,19 @@ int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float
   if (st != KDA_OK) return st;
   st = check_fusion(fusion);
   if (st != KDA_OK) return st;
+  const int gate = fusion ? fusion->gate_kind : KDA_GATE_CHANNEL;
   const int64_t tokens = (int64_t)B * T;
   if (tokens > 0) {
-    if (!q || !k || !v || !log_alpha || !beta || !o)
-      return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must be non-null when B*T > 0");
+    if (!q || !k || !v || !beta || !o || (!log_alpha && gate != KDA_GATE_NONE))
+      return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha (unless gate_kind is KDA_GATE_NONE), beta and o must be "
+                                       "non-null when B*T > 0");
   }
-  const void* ptrs[] = {q, k, v, log_alpha, o, initial_state, final_state};
-  const char* names[] = {"q", "k", "v", "log_alpha", "o", "initial_state", "final_state"};
-  for (int i = 0; i < 7; ++i)
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state};
+  const char* names[] = {"q", "k", "v", "o", "initial_state", "final_state"};
+  for (int i = 0; i < 6; ++i)
     if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (gate != KDA_GATE_NONE && log_alpha && !aligned(log_alpha, gate == KDA_GATE_HEAD ? 4 : 16))
+    return fail(KDA_ERR_INVALID_ARG, "log_alpha is not %d-byte aligned", gate == KDA_GATE_HEAD ? 4 : 16);
   if (beta && !aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARG, "beta is not 4-byte aligned");
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
   if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -246,11 +253,14 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
   int st = check_fusion(fusion);
   if (st != KDA_OK) return st;
   if (N == 0) return ok();
+  const int gate = fusion ? fusion->gate_kind : KDA_GATE_CHANNEL;
   const void* ptrs[] = {q, k, v, log_alpha, beta, state, o};
   const char* names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
   for (int i = 0; i < 7; ++i) {
+    const bool is_gate = i == 3;
+    if (is_gate && gate == KDA_GATE_NONE) continue;
     if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s must be non-null", names[i]);
-    const size_t need = (ptrs[i] == (const void*)beta) ? 4 : 16;
+    const size_t need = (i == 4 || (is_gate && gate == KDA_GATE_HEAD)) ? 4 : 16;
     if (!aligned(ptrs[i], need)) return fail(KDA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", names[i], need);
   }
   hipError_t e = kda::launch_decode(dtype, q, k, v, log_alpha, beta, state, o, N, H, to_internal(fusion),

@@ -46,8 +46,11 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
   // waves 0 and 1, combined through LDS
   float kk = 0.f, qq = 0.f, a = 0.f;
   if (t < D) {
-    float la = log_alpha[nh * D + t];
-    if (fu.gate_preactivation) la = -softplus_f(la);
+    // decay: per key channel, one per (sequence, head), or none (alpha = 1)
+    float la = 0.f;
+    if (fu.gate_kind == 0) la = log_alpha[nh * D + t];
+    else if (fu.gate_kind == 1) la = log_alpha[nh];
+    if (fu.gate_kind != 2 && fu.gate_preactivation) la = -softplus_f(la);
     a = __expf(la);
     kk = to_f(k[nh * D + t]);
     qq = to_f(q[nh * D + t]);

@@ -25,6 +25,7 @@ struct Fusion {
   const void* out_gate;      // nullable; o's layout and dtype
   const float* norm_weight;  // [128], with out_gate
   float norm_eps;
+  int gate_kind;             // 0: per channel, 1: per (token, head), 2: none
 };
 
 // dtype: 0 = bf16, 1 = fp32 (the kda_dtype values).

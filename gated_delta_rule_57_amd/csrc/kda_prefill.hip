@@ -59,6 +59,10 @@ namespace {
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float DIAG_RANGE_LIMIT = 120.f;  // log2 units
 
+// decay granularity (kda_fusion.gate_kind): one per key channel (KDA), one per
+// (token, head) (Gated DeltaNet), none (DeltaNet)
+constexpr int GATE_CHANNEL = 0, GATE_HEAD = 1, GATE_NONE = 2;
+
 __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 __host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
@@ -205,7 +209,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 //   B2  off-diagonal blocks of T, one block column per wave, by fp32 MFMA
 //   B3  W = T diag(beta) K e^G (stored as -W) and U = T diag(beta) V
 // ---------------------------------------------------------------------------
-template <typename E, int C>
+template <typename E, int C, int GATE>
 __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const float* __restrict__ log_alpha,
                                                     const float* __restrict__ beta,
@@ -255,16 +259,21 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     const int r = rbase + 8 * i;
     const int rr = r < len ? r : 0;
     const size_t off = (size_t)(tok0 + rr) * HD + (size_t)h * D + ch0;
-    la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
+    if constexpr (GATE == GATE_CHANNEL) la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
     load4f(k + off, kr[i]);
     load4f(q + off, qr[i]);
     load4f(v + off, vr[i]);
   }
+  float la_row = 0.f;  // scalar gate: log decay of row t (t < CK), natural-log units
   if (t < CK) {
     float bt = 0.f;
     if (t < len) {
       bt = beta[(size_t)(tok0 + t) * H + h];
       if (fu.beta_preactivation) bt = sigmoid_f(bt);
+      if constexpr (GATE == GATE_HEAD) {
+        la_row = log_alpha[(size_t)(tok0 + t) * H + h];
+        if (fu.gate_preactivation) la_row = -softplus_f(la_row);
+      }
     }
     sBeta[t] = bt;
   }
@@ -288,12 +297,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
     }
   }
-  if (fu.gate_preactivation) {  // log alpha = -softplus(a), kept in natural-log units here
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) la[i][j] = -softplus_f(la[i][j]);
-  }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rbase + 8 * i;
@@ -304,7 +307,22 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       qr[i][j] = valid ? qr[i][j] : 0.f;
       vr[i][j] = valid ? vr[i][j] : 0.f;
     }
-    floatx4 l2 = valid ? la[i] * LOG2E_F : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  constexpr int NBLK = SM::NBLK;
+  constexpr int BPW = (NBLK + 3) / 4;
+  float ktr[RPT][4];
+  floatx4 accA[BPW], accP[BPW];
+  if constexpr (GATE == GATE_CHANNEL) {
+  if (fu.gate_preactivation) {  // log alpha = -softplus(a), kept in natural-log units here
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) la[i][j] = -softplus_f(la[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rbase + 8 * i;
+    floatx4 l2 = r < len ? la[i] * LOG2E_F : floatx4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<floatx4*>(sG + r * GLD + ch0) = l2;
   }
   __syncthreads();
@@ -353,10 +371,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
   for (int I = 0; I < NSUB; ++I) exact |= sFlag[I] != 0;
 
-  constexpr int NBLK = SM::NBLK;
-  constexpr int BPW = (NBLK + 3) / 4;
-  float ktr[RPT][4];
-  floatx4 accA[BPW], accP[BPW];
   if (!exact) {
     // ---- P2 (factored path): Q e^G to the record, K e^G kept for B0, and per row
     //      the operands of every A / P block:
@@ -563,6 +577,106 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       for (int j = 0; j < 4; ++j) {
         const int s = s0 + j;
         kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
+      }
+      const int kb = s0 >> 5, so = s0 & 31;
+      const int fg = (so & 15) >> 2, fh = so >> 4;
+      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
+    }
+  }
+  } else {
+    // ---- scalar gate: one decay per (token, head) (GATE_HEAD), or none (GATE_NONE).
+    //      The decay of a row pair is the scalar 2^(gh_r - gh_s), exponent <= 0 for
+    //      s <= r, so the raw products k k^T and q k^T are scaled per element after
+    //      the MFMA and no factoring or fallback is needed ------------------------
+    float* sGs = sG;  // float[CK]: log2-domain cumsum of the row decays
+    if (w == 0) {     // one wave holds every row (CK <= 64)
+      float x = 0.f;
+      if constexpr (GATE == GATE_HEAD) x = la_row * LOG2E_F;  // zero past len
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (lane < CK) sGs[lane] = x;
+    }
+    __syncthreads();
+    const float gC = sGs[C - 1];
+    if (t < D) rec_gamma[t] = fast_exp2(gC);
+    // ---- P2 (scalar): Q e^G to the record, K e^G kept for B0, raw q, k to LDS --
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i;
+      const float eg = GATE == GATE_NONE ? 1.f : fast_exp2(sGs[r]);
+      float qt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qt[j] = qr[i][j] * eg;
+        ktr[i][j] = kr[i][j] * eg;
+      }
+      store4f(sK + r * LD + ch0, kr[i]);
+      store4f(sQ + r * LD + ch0, qr[i]);
+      const int kb = ch0 >> 5, co = ch0 & 31;
+      const int fg = (co & 15) >> 2, fh = co >> 4;
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+    }
+    __syncthreads();
+    // ---- P3 (scalar): raw block products, then the pair decay per element ------
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int idx = w + 4 * bi;
+      if (idx >= NBLK) break;
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+      const int J = idx - I * (I + 1) / 2;
+      const int rrow = 16 * I + m, srow = 16 * J + m;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        FragT lk, lq, rhs;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ch = 32 * kb + 16 * hh + 4 * g;
+          const V4 a = *reinterpret_cast<const V4*>(sK + rrow * LD + ch);
+          const V4 bq = *reinterpret_cast<const V4*>(sQ + rrow * LD + ch);
+          const V4 bs = *reinterpret_cast<const V4*>(sK + srow * LD + ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            lk[4 * hh + j] = a[j];
+            lq[4 * hh + j] = bq[j];
+            rhs[4 * hh + j] = bs[j];
+          }
+        }
+        mma(accA[bi], rhs, lk);
+        mma(accP[bi], rhs, lq);
+      }
+      const int r = rrow;
+      float pv[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 16 * J + 4 * g + ii;
+        const float f = s <= r ? (GATE == GATE_NONE ? 1.f : fast_exp2(sGs[r] - sGs[s])) : 0.f;
+        accA[bi][ii] *= f;
+        accP[bi][ii] *= f;
+        pv[ii] = accP[bi][ii];
+      }
+      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+    }
+    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
+      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
+      if (J > I) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
+      }
+    }
+    // (K e^{g_C - G})^T to the record
+    for (int it = t; it < D * (CK / 4); it += 256) {
+      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
+      float kv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(gC - sGs[s])) : 0.f;
       }
       const int kb = s0 >> 5, so = s0 & 31;
       const int fg = (so & 15) >> 2, fh = so >> 4;
@@ -1006,9 +1120,11 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   trace_mark(stream, 0);
   if (e != hipSuccess) return e;
   if (mc > 0) {
-    hipLaunchKernelGGL((intra_kernel<E, C>), dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
-                       records, fusion);
+    auto* kern = fusion.gate_kind == GATE_HEAD   ? intra_kernel<E, C, GATE_HEAD>
+                 : fusion.gate_kind == GATE_NONE ? intra_kernel<E, C, GATE_NONE>
+                                                 : intra_kernel<E, C, GATE_CHANNEL>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream, (const E*)q, (const E*)k,
+                       (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, records, fusion);
     e = hipGetLastError();
     trace_mark(stream, 1);
     if (e != hipSuccess) return e;

@@ -96,7 +96,9 @@ def uniform_composition(g, total: int, parts: int, device) -> torch.Tensor:
 
 def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64, la_mode: str = "scaled",
                  la_scale: float = 0.1, s0_std: float = 0.0, num_seqs: Optional[int] = None,
-                 cu_seqlens=None, device="cuda", dk: int = D, dv: int = D) -> PrefillInputs:
+                 cu_seqlens=None, device="cuda", dk: int = D, dv: int = D, gate: str = "channel") -> PrefillInputs:
+    """``gate``: "channel" (log_alpha [B, T, H, dk]), "head" (one decay per (token,
+    head): log_alpha [B, T, H], drawn like one channel) or "none" (log_alpha None)."""
     g = _gen(seed, device)
     cu = None
     if cu_seqlens is not None:
@@ -109,8 +111,13 @@ def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64,
     q = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
     k = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
     v = _normal(g, (B, T, H, dv), device).to(td)
-    z = _normal(g, (B, T, H, dk), device)
-    if la_mode == "scaled":
+    z = _normal(g, (B, T, H, dk) if gate == "channel" else (B, T, H), device)
+    if gate == "head":
+        assert la_mode == "scaled"
+        log_alpha = -la_scale * torch.nn.functional.softplus(z)
+    elif gate == "none":
+        log_alpha = None
+    elif la_mode == "scaled":
         log_alpha = -la_scale * torch.nn.functional.softplus(z)
     elif la_mode == "mixed":
         log_alpha = -torch.nn.functional.softplus(z)
@@ -122,8 +129,9 @@ def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64,
     beta = torch.sigmoid(_normal(g, (B, T, H), device))
     N = B if cu is None else cu.numel() - 1
     s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
-    return PrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(), log_alpha.contiguous(), beta.contiguous(),
-                         s0, cu, dtype, chunk, dict(seed=seed, la_mode=la_mode, la_scale=la_scale))
+    return PrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(),
+                         None if log_alpha is None else log_alpha.contiguous(), beta.contiguous(),
+                         s0, cu, dtype, chunk, dict(seed=seed, la_mode=la_mode, la_scale=la_scale, gate=gate))
 
 
 def make_workload(idx: int, device="cuda", **overrides) -> PrefillInputs:

@@ -34,7 +34,11 @@ class Fusion(ctypes.Structure):
     recurrence. Build one with ``fusion()``."""
     _fields_ = [("normalize_qk", ctypes.c_int), ("qk_eps", ctypes.c_float),
                 ("gate_preactivation", ctypes.c_int), ("beta_preactivation", ctypes.c_int),
-                ("out_gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+                ("out_gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("gate_kind", ctypes.c_int)]
+
+
+KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 
 
 class KdaError(RuntimeError):
@@ -128,8 +132,31 @@ def fusion(normalize_qk=True, qk_eps=1e-6, gate_preactivation=True, beta_preacti
             raise ValueError("out_gate must be contiguous")
     f = Fusion(int(bool(normalize_qk)), float(qk_eps), int(bool(gate_preactivation)), int(bool(beta_preactivation)),
                None if out_gate is None else out_gate.data_ptr(),
-               None if out_gate is None else norm_weight.data_ptr(), float(norm_eps))
+               None if out_gate is None else norm_weight.data_ptr(), float(norm_eps), KDA_GATE_CHANNEL)
     f._keep = (out_gate, norm_weight)
+    return f
+
+
+def _gate_kind(log_alpha, lead, dk):
+    """The kda_gate of a log_alpha argument: [..., dk] per channel, [...] per
+    (token, head), None for no decay."""
+    if log_alpha is None:
+        return KDA_GATE_NONE
+    if tuple(log_alpha.shape) == tuple(lead):
+        _need(log_alpha, "log_alpha", torch.float32, lead)
+        return KDA_GATE_HEAD
+    _need(log_alpha, "log_alpha", torch.float32, tuple(lead) + (dk,))
+    return KDA_GATE_CHANNEL
+
+
+def _with_gate(f, gate):
+    """The Fusion to pass for ``gate``: ``f`` with its gate_kind set, a plain one
+    when only the gate differs from the default, or None for the plain call."""
+    if f is None and gate == KDA_GATE_CHANNEL:
+        return None
+    if f is None:
+        f = fusion(normalize_qk=False, gate_preactivation=False, beta_preactivation=False)
+    f.gate_kind = gate
     return f
 
 
@@ -143,10 +170,11 @@ def _check_out_gate(f, o):
 def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
               output_final_state=True, o=None, final_state=None, workspace=None, fusion=None):
     """Chunked KDA prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_fused`` when
-    ``fusion`` is given; see ``fusion()``).
+    ``fusion`` is given, see ``fusion()``, or the gate is not per channel).
 
     q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
-    log_alpha: [B, T, H, 128] fp32; beta: [B, T, H] fp32;
+    log_alpha: [B, T, H, 128] fp32 (KDA), [B, T, H] fp32 (one decay per token and
+    head: Gated DeltaNet) or None (no decay: DeltaNet); beta: [B, T, H] fp32;
     initial_state: [N, H, 128, 128] fp32 or None; cu_seqlens: int32 [N+1] device
     tensor (B must be 1) or None. Returns (o, final_state or None).
     """
@@ -159,8 +187,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
     _need(q, "q", dt, (B, T, H, dk))
     _need(k, "k", dt, (B, T, H, dk))
     _need(v, "v", dt, (B, T, H, dv))
-    _need(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    gate = _gate_kind(log_alpha, (B, T, H), dk)
     _need(beta, "beta", torch.float32, (B, T, H))
+    fusion = _with_gate(fusion, gate)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
             raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
@@ -198,8 +227,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
 
 def decode_step(q, k, v, log_alpha, beta, state, o=None, fusion=None):
     """One decode step through ``kda_decode_step`` (``kda_decode_step_fused`` when
-    ``fusion`` is given); ``state`` [N, H, 128, 128] fp32 is updated in place.
-    q, k, v: [N, H, 128]; log_alpha: [N, H, 128] fp32; beta: [N, H] fp32.
+    ``fusion`` is given or the gate is not per channel); ``state`` [N, H, 128, 128]
+    fp32 is updated in place. q, k, v: [N, H, 128]; log_alpha: [N, H, 128] fp32,
+    [N, H] fp32 or None (as in ``chunk_fwd``); beta: [N, H] fp32.
     Returns o [N, H, 128]."""
     if q.dim() != 3:
         raise ValueError("q must be [N, H, dk]")
@@ -210,9 +240,10 @@ def decode_step(q, k, v, log_alpha, beta, state, o=None, fusion=None):
     _need(q, "q", dt, (N, H, dk))
     _need(k, "k", dt, (N, H, dk))
     _need(v, "v", dt, (N, H, dv))
-    _need(log_alpha, "log_alpha", torch.float32, (N, H, dk))
+    gate = _gate_kind(log_alpha, (N, H), dk)
     _need(beta, "beta", torch.float32, (N, H))
     _need(state, "state", torch.float32, (N, H, dk, dv))
+    fusion = _with_gate(fusion, gate)
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=q.device)
     else:

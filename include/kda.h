@@ -156,7 +156,22 @@ typedef struct kda_fusion {
   const void *out_gate;
   const float *norm_weight;
   float norm_eps;
+  int gate_kind; /* a kda_gate value, see below */
 } kda_fusion;
+
+/*
+ * Decay granularity (kda_fusion.gate_kind). The pages trace KDA back through two
+ * special cases ("From GPT-2 to Kimi K3" digest, sections "DeltaNet -- 유한한 캐시의
+ * 덮어쓰기" and "Gated DeltaNet -- 망각을 더하다"; GeekNews "Kimi Linear" summary,
+ * section "선형 어텐션에서 Gated DeltaNet까지"): Gated DeltaNet has one scalar decay per
+ * (token, head) and DeltaNet none (alpha = 1). They run on dedicated paths that need
+ * no per-channel decay factoring:
+ *   KDA_GATE_CHANNEL  log_alpha [.., H, dk], one decay per key channel (KDA; the default)
+ *   KDA_GATE_HEAD     log_alpha [.., H], one decay per (token, head), 4-byte aligned
+ *   KDA_GATE_NONE     alpha = 1; log_alpha is not read and may be NULL
+ * gate_preactivation applies to the gate that is read.
+ */
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate;
 
 /*
  * kda_chunk_fwd with the prologue / epilogue of `fusion` (NULL = kda_chunk_fwd).

@@ -178,3 +178,18 @@ def test_output_norm_gate_rejects(kw, status):
     a.update(kw)
     assert L.kda_output_norm_gate(a["o"], a["gate"], a["weight"], a["out"], a["rows"], a["dv"], a["eps"],
                                   a["dtype"], None) == status
+
+
+@pytest.mark.parametrize("gate,la,status", [
+    (3, FAKE, kda.KDA_ERR_INVALID_ARG),                                  # not a kda_gate
+    (-1, FAKE, kda.KDA_ERR_INVALID_ARG),
+    (kda.KDA_GATE_HEAD, ctypes.c_void_p((1 << 20) + 2), kda.KDA_ERR_INVALID_ARG),     # scalar gate: 4-byte aligned
+    (kda.KDA_GATE_CHANNEL, ctypes.c_void_p((1 << 20) + 4), kda.KDA_ERR_INVALID_ARG),  # channel gate: 16-byte
+    (kda.KDA_GATE_CHANNEL, None, kda.KDA_ERR_INVALID_ARG),               # only the no-decay kind may omit it
+    (kda.KDA_GATE_HEAD, None, kda.KDA_ERR_INVALID_ARG),
+])
+def test_gate_kind_checks(gate, la, status):
+    f = make_fusion(gate_kind=gate)
+    assert fused_chunk_call(f, la=la) == status
+    assert L.kda_decode_step_fused(FAKE, FAKE, FAKE, la, FAKE, FAKE, FAKE, 4, 2, 128, 128, 0,
+                                   ctypes.byref(f), None) == status
