@@ -1,14 +1,17 @@
 """Turns rocprofv3 CSV output into the short summaries kept under profiles/.
 
-    python -m gated_delta_rule_57_amd.profiling trace <trace_dir> <out.md> "<command>"
-        kernel-trace statistics (rocprofv3 --kernel-trace --stats --output-format csv)
+    python -m gated_delta_rule_57_amd.profiling trace <trace_dir> <out.md> "<command>" [names]
+        kernel-trace statistics (rocprofv3 --kernel-trace --stats --output-format csv);
+        names, comma-separated short names, keeps only those rows
     python -m gated_delta_rule_57_amd.profiling traffic <pmc_root> <out.json> "<commands>"
         HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter runs, each scaled by
         what the same counter reads for a device copy of 1 GiB. <pmc_root> holds the
         rocprofv3 output directories copy_FETCH_SIZE, copy_WRITE_SIZE, bench_FETCH_SIZE
         and bench_WRITE_SIZE.
 
-Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode).
+Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode,
+outnorm); the intra-chunk kernel's scalar-gate and no-decay instantiations become
+intra_gdn and intra_deltanet.
 The traffic summary records a hash of the kernel sources it was taken on; bench.py
 reports the traffic only while that hash matches the sources.
 """
@@ -17,6 +20,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
@@ -38,24 +42,35 @@ def kernel_source_hash(root=None):
     return h.hexdigest()[:16]
 
 
+# the gate template argument of intra_kernel, in mangled (..Li64ELi1EE..) or
+# demangled (<.., 64, 1>) names
+_GATE_ARG = re.compile(r"intra_kernel(?:I\w*?Li\d+ELi(\d)E|<[^>]*,\s*(\d)>)")
+
+
 def short_name(name):
     for key, short in KERNELS:
         if key in name:
+            if short == "intra":
+                m = _GATE_ARG.search(name)
+                gate = m.group(1) or m.group(2) if m else None
+                return {"1": "intra_gdn", "2": "intra_deltanet"}.get(gate, "intra")
             return short
     return None
 
 
-def summarize_trace(trace_dir, out_md, command):
+def summarize_trace(trace_dir, out_md, command, names=None):
+    keep = set(names.split(",")) if names else None
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     rows = list(csv.DictReader(open(stats[0])))
     lines = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
+             f"Kernel sources: hash {kernel_source_hash()}" + (f"; rows kept: {names}" if names else ""), "",
              "| kernel | calls | total ms | average us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for r in rows:
         s = short_name(r["Name"])
-        if s is None:
+        if s is None or (keep is not None and s not in keep):
             continue
         lines.append(f"| {s} (`{r['Name'][:60]}`) | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
@@ -107,6 +122,7 @@ def summarize_traffic(pmc_root, out_json, commands):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) != 5 or sys.argv[1] not in ("trace", "traffic"):
+    if len(sys.argv) not in (5, 6) or sys.argv[1] not in ("trace", "traffic") or \
+            (sys.argv[1] == "traffic" and len(sys.argv) != 5):
         raise SystemExit(__doc__)
-    {"trace": summarize_trace, "traffic": summarize_traffic}[sys.argv[1]](sys.argv[2], sys.argv[3], sys.argv[4])
+    {"trace": summarize_trace, "traffic": summarize_traffic}[sys.argv[1]](*sys.argv[2:])
