@@ -29,7 +29,9 @@
 //                 MFMA to the next without leaving registers. The value columns of
 //                 S evolve independently, which is what makes the slab split exact.
 //                 inter_wg_kernel (bf16, 64-token chunks) spreads a slab over four
-//                 waves; inter_kernel (fp32 or 16-token chunks) uses one wave.
+//                 waves and has each record line pulled into L2 by one wave of the
+//                 head a few chunks ahead; inter_kernel (fp32 or 16-token chunks)
+//                 uses one wave.
 //
 // In-chunk decay (the pages note that fine-grained decay makes the in-chunk
 // division numerically delicate): everything is done in log2 units, and the
@@ -934,6 +936,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // chunks of record data in flight ahead of the one being computed
 constexpr int INTER_LOOKAHEAD = 1;
+// chunks beyond the lookahead whose record lines are pulled into L2 ahead of use
+constexpr int INTER_TOUCH_AHEAD = 2;
 
 struct InterStage {
   bf16x8 wn[4], qt[4], ke[4], pp[2];
@@ -1053,6 +1057,18 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
     }
   };
 
+  // L2 touch. The eight slab work-groups of a head read every record line, and
+  // without help all eight wait out the same DRAM fill together, which caps each
+  // CU's request rate. So each line of chunk c + LA + INTER_TOUCH_AHEAD is first
+  // read (one dword) by a single wave of the head, spread over its 32 waves, and
+  // the eight real reads of it then hit in L2. The words are XOR-folded into
+  // tacc, which only a never-taken branch stores: that keeps the loads alive
+  // without making any step wait for them before the next one.
+  constexpr int REC_LINES = (int)(RC::BYTES / 128);
+  static_assert(RC::BYTES % 128 == 0 && REC_LINES <= 32 * 64, "one touch per lane per line");
+  const int touch_line = (ct * 4 + w) + 32 * lane;
+  unsigned tacc = 0u, tv[LA + 1] = {};
+
   InterStage st[LA + 1];
 #pragma unroll
   for (int r = 0; r < LA; ++r)
@@ -1065,9 +1081,16 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
       // final record is loaded again, so every step issues the same loads and the
       // register stages rotate without leaving the loop body
       load(st[(r + LA) % (LA + 1)], min(c + LA, c_end - 1));
+      if (touch_line < REC_LINES)
+        tv[r] = *reinterpret_cast<const unsigned*>(
+            head_records + (size_t)min(c + LA + INTER_TOUCH_AHEAD, c_end - 1) * RC::BYTES + (size_t)touch_line * 128);
       if (c < c_end) compute(st[r], c);
+      // the word touched one step earlier has had a whole step to arrive
+      tacc ^= tv[(r + LA) % (LA + 1)];
     }
   }
+  // total_tokens is never negative (the host rejects it), so this never stores
+  if (total_tokens < 0 && tacc == 0u) o[lane] = (__bf16)0.f;
   if (final_state) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
