@@ -48,6 +48,9 @@ int check_prefill(int B, int T, int H, int num_seqs, bool varlen, int dk, int dv
   if ((int64_t)B * T > (int64_t)INT32_MAX - 64) return fail(KDA_ERR_INVALID_ARG, "B*T=%lld is too large", (long long)B * T);
   if ((int64_t)(varlen ? num_seqs : B) * H > (int64_t)INT32_MAX / 64)
     return fail(KDA_ERR_INVALID_ARG, "too many (sequence, head) pairs");
+  // the intra-chunk kernel runs one work-group per (chunk, head) on a 1-D grid
+  if (kda::max_chunks(B, T, num_seqs, varlen, chunk) * H > (int64_t)INT32_MAX)
+    return fail(KDA_ERR_INVALID_ARG, "too many (chunk, head) pairs");
   return KDA_OK;
 }
 

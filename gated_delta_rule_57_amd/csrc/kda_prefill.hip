@@ -240,7 +240,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
   int* sFlag = reinterpret_cast<int*>(smem + SM::FLAG);
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  // heads vary fastest over the work-group ids: the work-groups in flight together
+  // cover whole token rows of q, k, v and the gates, not one head's 256-byte pieces
+  const int c = blockIdx.x / H, h = blockIdx.x - c * H;
   if (c >= *total_chunks) return;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
@@ -1146,7 +1148,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
     auto* kern = fusion.gate_kind == GATE_HEAD   ? intra_kernel<E, C, GATE_HEAD>
                  : fusion.gate_kind == GATE_NONE ? intra_kernel<E, C, GATE_NONE>
                                                  : intra_kernel<E, C, GATE_CHANNEL>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)mc, (unsigned)H), dim3(256), 0, stream, (const E*)q, (const E*)k,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q, (const E*)k,
                        (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, records, fusion);
     e = hipGetLastError();
     trace_mark(stream, 1);

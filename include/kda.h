@@ -106,7 +106,10 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk
  *   workspace   device buffer of at least kda_chunk_fwd_workspace_size() bytes, or
  *               NULL: the library then allocates and frees it in stream order.
  * T = 0 (or B = 0) is a valid call that copies initial_state to final_state (zeros
- * if initial_state is NULL). `o` must not alias any input.
+ * if initial_state is NULL). `o` must not alias any input. Size limits, each
+ * KDA_ERR_INVALID_ARG: B*T below 2^31 - 64 tokens, N*H below 2^25 (sequence, head)
+ * pairs, and (chunks, bounded by B*ceil(T/chunk) or ceil(T/chunk) + num_seqs) * H
+ * below 2^31.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,

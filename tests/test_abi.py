@@ -72,6 +72,8 @@ def chunk_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num
     (dict(ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 30), kda.KDA_ERR_INVALID_ARG),
     (dict(ws=FAKE, ws_bytes=16), kda.KDA_ERR_WORKSPACE),
     (dict(B=1 << 16, T=1 << 16), kda.KDA_ERR_INVALID_ARG),
+    # 2^26 chunks of 16 tokens times 64 heads: more (chunk, head) work-groups than a 1-D grid holds
+    (dict(T=1 << 30, H=64, chunk=16), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_chunk_fwd_rejects(kw, status):
     assert chunk_call(**kw) == status
