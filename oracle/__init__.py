@@ -20,11 +20,14 @@ Contents
 ``fused``
     The layer's prologue (q, k L2 normalisation, gate and beta activations) and
     epilogue (output RMSNorm and gate) around the recurrence.
+``backward``
+    Gradients of the recurrence with respect to q, k, v, log_alpha, beta and the
+    initial state, by reverse mode through the sequential fp64 form in C.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test; none is
 "parity unpinned".
 """
 from .build import build_oracle, oracle_lib_path
-from .seq import forward, decode_step, load_library
+from .seq import backward, forward, decode_step, load_library
 
-__all__ = ["build_oracle", "oracle_lib_path", "forward", "decode_step", "load_library"]
+__all__ = ["build_oracle", "oracle_lib_path", "forward", "decode_step", "backward", "load_library"]

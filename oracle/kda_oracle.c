@@ -55,7 +55,7 @@
 
 #define ORACLE_COL_BLOCK 16
 
-int kda_oracle_abi_version(void) { return 2; }
+int kda_oracle_abi_version(void) { return 3; }
 
 /*
  * Optional prologue on the raw projections, as the Kimi Linear layer applies it
@@ -251,4 +251,180 @@ int kda_oracle_decode_step(const float *q, const float *k, const float *v,
                            double *state, double *o, int N, int H, int dk, int dv,
                            int num_threads) {
   return kda_oracle_decode_step_ex(q, k, v, log_alpha, beta, state, o, N, H, dk, dv, num_threads, 0, 0.0);
+}
+
+/*
+ * Reverse-mode derivative of the recurrence above (the plain recurrence, no
+ * prologue), for training: given the cotangents d_o of every output and d_final
+ * of every final state, the gradient of
+ *
+ *     L = sum_t <o_t, d_o_t> + sum_n <S_final[n], d_final[n]>
+ *
+ * with respect to q, k, v, log_alpha, beta and the initial state. The pages present
+ * the chunked form as the device that makes KDA efficient to train ("From GPT-2 to
+ * Kimi K3" digest, section on chunked computation; GeekNews "Kimi Linear" summary,
+ * section "청크 단위 병렬화"), so its gradients are the derivatives of this map.
+ *
+ * One token, forward (as above):  S' = Diag(a) S ;  e = v - S'^T k ;
+ * S_t = S' + b k e^T ;  o_t = S_t^T q.  Backward, with L_t the gradient of L with
+ * respect to S_t (everything that reads S_t, the output included):
+ *     L_t   += q do^T                          (o_t = S_t^T q)
+ *     dq     = S_t do
+ *     r      = L_t^T k ;  de = b r ;  db = r . e ;  dk = b L_t e
+ *     dS'    = L_t - k de^T ;  dk -= S' de ;  dv = de
+ *     dlog_a = a o (rowsum of dS' o S)          (S' = Diag(a) S, a = exp(log_a))
+ *     L_{t-1} = Diag(a) dS'
+ *
+ * The states are recomputed forward from checkpoints every ORACLE_BWD_SEG tokens,
+ * with the same operations as the forward pass, so memory stays bounded. Work is
+ * split over (sequence, head); the gradients of q, k, log_alpha and beta sum over
+ * all value columns, so columns are not split here.
+ *
+ * Layouts as kda_oracle_forward, all heads and columns:
+ *   d_o        [T_total][H][dv] float32, or NULL for zeros
+ *   d_final    [num_seqs][H][dk][dv] float64, or NULL for zeros
+ *   dq, dk_out, dlog_alpha [T_total][H][dk]; dv_out [T_total][H][dv];
+ *   dbeta [T_total][H]; d_initial [num_seqs][H][dk][dv] (NULL: not written),
+ * all float64 and written in full for every token of every sequence.
+ */
+#define ORACLE_BWD_SEG 64
+
+static void fwd_token(double *S, const double *kt, const float *v, const double *alpha, double b, int dk, int dv) {
+  double e[512];
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];
+  for (int j = 0; j < dv; ++j) e[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) e[j] += kt[i] * S[(size_t)i * dv + j];
+  for (int j = 0; j < dv; ++j) e[j] = (double)v[j] - e[j];
+  for (int i = 0; i < dk; ++i) {
+    const double bki = b * kt[i];
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bki * e[j];
+  }
+}
+
+int kda_oracle_backward(const float *q, const float *k, const float *v, const float *log_alpha,
+                        const float *beta, const double *initial_state, const int64_t *seq_starts,
+                        int num_seqs, int H, int dk, int dv, const float *d_o, const double *d_final,
+                        double *dq, double *dk_out, double *dv_out, double *dlog_alpha, double *dbeta,
+                        double *d_initial, int num_threads) {
+  if (!q || !k || !v || !log_alpha || !beta || !seq_starts) return -1;
+  if (!dq || !dk_out || !dv_out || !dlog_alpha || !dbeta) return -1;
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || dv > 512) return -1;
+  for (int n = 0; n < num_seqs; ++n)
+    if (seq_starts[n + 1] < seq_starts[n]) return -1;
+  const long long ntask = (long long)num_seqs * H;
+  const size_t dd = (size_t)dk * dv;
+
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (long long task = 0; task < ntask; ++task) {
+    const int h = (int)(task % H);
+    const int n = (int)(task / H);
+    const int64_t t0 = seq_starts[n], t1 = seq_starts[n + 1];
+    const int64_t len = t1 - t0;
+    const int64_t nseg = (len + ORACLE_BWD_SEG - 1) / ORACLE_BWD_SEG;
+    /* ck[m] = state before token t0 + m * SEG; seg[s] = state before token s of the segment */
+    double *ck = (double *)malloc(sizeof(double) * dd * (size_t)(nseg > 0 ? nseg : 1));
+    double *seg = (double *)malloc(sizeof(double) * dd * (ORACLE_BWD_SEG + 1));
+    double *L = (double *)malloc(sizeof(double) * dd);
+    double *dSp = (double *)malloc(sizeof(double) * dd);
+    double *tok = (double *)malloc(sizeof(double) * (size_t)dk * 3);
+    double *kt = tok, *qt = tok + dk, *alpha = tok + 2 * dk;
+    double e[512], r[512], de[512], dov[512];
+
+    double *S = seg;
+    for (size_t x = 0; x < dd; ++x) S[x] = initial_state ? initial_state[((size_t)n * H + h) * dd + x] : 0.0;
+    for (int64_t m = 0; m < nseg; ++m) {
+      memcpy(ck + (size_t)m * dd, S, sizeof(double) * dd);
+      const int64_t a0 = t0 + m * ORACLE_BWD_SEG;
+      const int64_t a1 = (a0 + ORACLE_BWD_SEG < t1) ? a0 + ORACLE_BWD_SEG : t1;
+      for (int64_t t = a0; t < a1; ++t) {
+        const size_t rk = ((size_t)t * H + h) * dk;
+        double b;
+        token_inputs(k + rk, q + rk, log_alpha + rk, beta[(size_t)t * H + h], dk, 0, 0.0, kt, qt, alpha, &b);
+        fwd_token(S, kt, v + ((size_t)t * H + h) * dv, alpha, b, dk, dv);
+      }
+    }
+    /* L = gradient with respect to the final state */
+    for (size_t x = 0; x < dd; ++x) L[x] = d_final ? d_final[((size_t)n * H + h) * dd + x] : 0.0;
+
+    for (int64_t m = nseg - 1; m >= 0; --m) {
+      const int64_t a0 = t0 + m * ORACLE_BWD_SEG;
+      const int64_t a1 = (a0 + ORACLE_BWD_SEG < t1) ? a0 + ORACLE_BWD_SEG : t1;
+      /* states before every token of the segment, and after its last one */
+      memcpy(seg, ck + (size_t)m * dd, sizeof(double) * dd);
+      for (int64_t t = a0; t < a1; ++t) {
+        const size_t rk = ((size_t)t * H + h) * dk;
+        double b;
+        token_inputs(k + rk, q + rk, log_alpha + rk, beta[(size_t)t * H + h], dk, 0, 0.0, kt, qt, alpha, &b);
+        double *nxt = seg + (size_t)(t - a0 + 1) * dd;
+        memcpy(nxt, seg + (size_t)(t - a0) * dd, sizeof(double) * dd);
+        fwd_token(nxt, kt, v + ((size_t)t * H + h) * dv, alpha, b, dk, dv);
+      }
+      for (int64_t t = a1 - 1; t >= a0; --t) {
+        const size_t rk = ((size_t)t * H + h) * dk;
+        const size_t rv = ((size_t)t * H + h) * dv;
+        double b;
+        token_inputs(k + rk, q + rk, log_alpha + rk, beta[(size_t)t * H + h], dk, 0, 0.0, kt, qt, alpha, &b);
+        const double *Sprev = seg + (size_t)(t - a0) * dd; /* S_{t-1} */
+        const double *St = seg + (size_t)(t - a0 + 1) * dd; /* S_t */
+        for (int j = 0; j < dv; ++j) dov[j] = d_o ? (double)d_o[rv + j] : 0.0;
+        /* e = v - (Diag(a) S_{t-1})^T k, as in the forward step */
+        for (int j = 0; j < dv; ++j) e[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) e[j] += kt[i] * (Sprev[(size_t)i * dv + j] * alpha[i]);
+        for (int j = 0; j < dv; ++j) e[j] = (double)v[rv + j] - e[j];
+        /* the output reads S_t along q */
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] += qt[i] * dov[j];
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += St[(size_t)i * dv + j] * dov[j];
+          dq[rk + i] = acc;
+        }
+        /* S_t = S' + b k e^T */
+        for (int j = 0; j < dv; ++j) r[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) r[j] += kt[i] * L[(size_t)i * dv + j];
+        double db = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          de[j] = b * r[j];
+          db += r[j] * e[j];
+        }
+        dbeta[(size_t)t * H + h] = db;
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += L[(size_t)i * dv + j] * e[j];
+          dk_out[rk + i] = b * acc;
+        }
+        /* e = v - S'^T k: dS' = L - k de^T, dk -= S' de, dv = de */
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) dSp[(size_t)i * dv + j] = L[(size_t)i * dv + j] - kt[i] * de[j];
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += (Sprev[(size_t)i * dv + j] * alpha[i]) * de[j];
+          dk_out[rk + i] -= acc;
+        }
+        for (int j = 0; j < dv; ++j) dv_out[rv + j] = de[j];
+        /* S' = Diag(a) S_{t-1} */
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += dSp[(size_t)i * dv + j] * Sprev[(size_t)i * dv + j];
+          dlog_alpha[rk + i] = alpha[i] * acc;
+          for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] = alpha[i] * dSp[(size_t)i * dv + j];
+        }
+      }
+    }
+    if (d_initial)
+      for (size_t x = 0; x < dd; ++x) d_initial[((size_t)n * H + h) * dd + x] = L[x];
+    free(tok);
+    free(dSp);
+    free(L);
+    free(seg);
+    free(ck);
+  }
+  return 0;
 }

@@ -37,6 +37,8 @@ def load_library(path=None):
     lib.kda_oracle_decode_step.restype = I
     lib.kda_oracle_decode_step_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D]
     lib.kda_oracle_decode_step_ex.restype = I
+    lib.kda_oracle_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P, I]
+    lib.kda_oracle_backward.restype = I
     lib.kda_oracle_abi_version.restype = I
     if own:
         _lib = lib
@@ -137,3 +139,47 @@ def decode_step(q, k, v, log_alpha, beta, state, num_threads=None, flags=0, qk_e
     if rc != 0:
         raise ValueError(f"kda_oracle_decode_step rejected its arguments (status {rc})")
     return o
+
+
+def backward(q, k, v, log_alpha, beta, d_o=None, initial_state=None, d_final=None, cu_seqlens=None,
+             num_threads=None, lib=None):
+    """fp64 gradients of L = sum <o, d_o> + sum <final_state, d_final> with respect to
+    q, k, v, log_alpha, beta and initial_state, by reverse-mode through the sequential
+    recurrence (``kda_oracle_backward``).
+
+    Shapes as ``forward``; d_o: [B, T, H, dv] (None: zeros); d_final: [N, H, dk, dv]
+    (None: zeros). Returns a dict of float64 arrays: dq, dk, dlog_alpha [B, T, H, dk],
+    dv [B, T, H, dv], dbeta [B, T, H], d_initial [N, H, dk, dv].
+    """
+    lib = lib or load_library()
+    q, k, v, log_alpha, beta = map(_f32, (q, k, v, log_alpha, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and log_alpha.shape == q.shape
+    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    if cu_seqlens is None:
+        starts = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        assert B == 1
+        starts = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int64)
+        assert starts[0] == 0 and starts[-1] == T
+    N = len(starts) - 1
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    df = None if d_final is None else np.ascontiguousarray(d_final, dtype=np.float64)
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    if df is not None:
+        assert df.shape == (N, H, dk, dv)
+    do = None if d_o is None else _f32(d_o)
+    if do is not None:
+        assert do.shape == v.shape
+    out = {name: np.zeros(shape, dtype=np.float64) for name, shape in (
+        ("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", q.shape), ("dbeta", beta.shape),
+        ("d_initial", (N, H, dk, dv)))}
+    rc = lib.kda_oracle_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0), _ptr(starts), N, H, dk, dv,
+        _ptr(do), _ptr(df), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+        _ptr(out["dbeta"]), _ptr(out["d_initial"]), num_threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kda_oracle_backward rejected its arguments (status {rc})")
+    return out
