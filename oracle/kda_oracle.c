@@ -298,8 +298,8 @@ static void fwd_token(double *S, const double *kt, const float *v, const double 
     for (int j = 0; j < dv; ++j) e[j] += kt[i] * S[(size_t)i * dv + j];
   for (int j = 0; j < dv; ++j) e[j] = (double)v[j] - e[j];
   for (int i = 0; i < dk; ++i) {
-    const double bki = b * kt[i];
-    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bki * e[j];
+    const double bk = b * kt[i];
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bk * e[j];
   }
 }
 
