@@ -237,6 +237,60 @@ int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float
   return ok();
 }
 
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int num_seqs, int dtype) {
+  const bool varlen = num_seqs > 0 && B == 1;
+  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, kda::BWD_CHUNK, dtype) != KDA_OK) return 0;
+  return kda::backward_workspace_bytes(B, T, H, num_seqs, varlen, dtype);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int num_seqs, const void* grad_o,
+                  const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v, float* grad_log_alpha,
+                  float* grad_beta, float* grad_initial_state, int B, int T, int H, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  int st = check_prefill(B, T, H, num_seqs, varlen, dk, dv, kda::BWD_CHUNK, dtype);
+  if (st != KDA_OK) return st;
+  const int64_t tokens = (int64_t)B * T;
+  if (tokens > 0) {
+    if (!q || !k || !v || !log_alpha || !beta || !grad_o || !grad_q || !grad_k || !grad_v || !grad_log_alpha ||
+        !grad_beta)
+      return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta, grad_o and the five token gradients must be "
+                                       "non-null when B*T > 0");
+  }
+  const void* ptrs[] = {q, k, v, log_alpha, grad_o, grad_q, grad_k, grad_v, grad_log_alpha, initial_state,
+                        grad_final_state, grad_initial_state};
+  const char* names[] = {"q", "k", "v", "log_alpha", "grad_o", "grad_q", "grad_k", "grad_v", "grad_log_alpha",
+                         "initial_state", "grad_final_state", "grad_initial_state"};
+  for (int i = 0; i < 12; ++i)
+    if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (beta && !aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARG, "beta is not 4-byte aligned");
+  if (grad_beta && !aligned(grad_beta, 4)) return fail(KDA_ERR_INVALID_ARG, "grad_beta is not 4-byte aligned");
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+  if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const int N = varlen ? num_seqs : B;
+  if (N == 0) return ok();
+  const size_t need = kda::backward_workspace_bytes(B, T, H, num_seqs, varlen, dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+  }
+  hipError_t e = kda::launch_backward(dtype, q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, grad_o,
+                                      grad_final_state, grad_q, grad_k, grad_v, grad_log_alpha, grad_beta,
+                                      grad_initial_state, B, T, H, ws, s);
+  if (!workspace) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                   const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
                   float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* workspace,

@@ -52,4 +52,39 @@ hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, co
                           const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
                           int T, int H, const Fusion& fusion, void* workspace, hipStream_t stream);
 
+// Byte offsets of a prefill workspace: chunk plan (chunk_off [N+1], info [mc]
+// int2) and the per-(head, chunk) records.
+struct PrefillWs {
+  size_t off_chunk_off, off_info, off_records, total;
+};
+PrefillWs prefill_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype);
+
+// Chunk length of the backward pass.
+constexpr int BWD_CHUNK = 16;
+
+// The forward pass at BWD_CHUNK-token chunks for the backward: plan, records, and
+// per (head, chunk) the state entering the chunk (states, [H][mc][128][128]) and
+// U~ = U - W S ([H][mc][BWD_CHUNK][128]), both in the input dtype. workspace is laid
+// out by prefill_ws_layout(..., BWD_CHUNK, dtype). No output, no final state.
+// Backward workspace: the forward's (at BWD_CHUNK), then the backward records, the
+// chunk-entry states, the chunk-end state gradients, U~ and dU~ per (head, chunk).
+struct BackwardWs {
+  PrefillWs fwd;
+  size_t off_brec, off_states, off_dstates, off_ut, off_dut, total;
+};
+BackwardWs backward_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int dtype);
+size_t backward_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int dtype);
+
+// Gradients of the plain recurrence (see kda_chunk_bwd in include/kda.h).
+hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                           const void* dout, const float* d_final, void* dq, void* dk, void* dv, float* dlog_alpha,
+                           float* dbeta, float* d_initial, int B, int T, int H, void* workspace,
+                           hipStream_t stream);
+
+hipError_t launch_forward_states(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, int B, int T, int H, void* workspace, void* states, void* ut,
+                                 hipStream_t stream);
+
 }  // namespace kda

@@ -811,6 +811,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 // the sequence's chunks. Work-group ids are laid out so that the eight slabs of
 // one (sequence, head) land on the same XCD (ids are dealt to the 8 XCDs round
 // robin), where they share that XCD's L2 copy of the chunk records.
+// For the backward pass it can also keep, per (head, chunk), the state entering
+// the chunk (states, [H][mc][128][128]) and U~ = U - W S ([H][mc][C][128]); o may
+// then be null.
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ records,
@@ -818,7 +821,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
                                                    const int2* __restrict__ info,
                                                    const float* __restrict__ initial_state,
                                                    float* __restrict__ final_state, E* __restrict__ o, int N,
-                                                   int H, int mc) {
+                                                   int H, int mc, E* __restrict__ states, E* __restrict__ ut) {
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
   constexpr int NRT = RC::NRT, NKC = RC::NKC;
@@ -853,6 +856,13 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
     FragT Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<E>(S[2 * kb], S[2 * kb + 1]);
+    if (states) {
+      E* sp = states + ((size_t)h * mc + c) * D * D + 16 * ct + m;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * rt + 4 * g + i) * D] = from_f<E>(S[rt][i]);
+    }
 
     // U~ = U - W S  (the record holds -W)
     floatx4 Ut[NRT];
@@ -864,6 +874,11 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         mma(Ut[rt], load_frag<E>(rec + RC::WN + ((size_t)(rt * 4 + kb) * 64 + lane) * 8), Sb[kb]);
+      if (ut) {
+        E* up = ut + ((size_t)h * mc + c) * C * D + 16 * ct + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up[(size_t)(16 * rt + 4 * g + i) * D] = from_f<E>(Ut[rt][i]);
+      }
     }
     // (Q e^G) S
     floatx4 X[NRT];
@@ -887,7 +902,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rt + 4 * g + i;
-        if (row < inf.y) o[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[rt][i]);
+        if (o && row < inf.y) o[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[rt][i]);
       }
     }
     // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
@@ -1114,19 +1129,21 @@ size_t chunk_record_bytes(int dtype, int chunk) {
   return chunk == 16 ? Rec<float, 16>::BYTES : Rec<float, 64>::BYTES;
 }
 
-namespace {
-struct WsLayout {
-  size_t off_chunk_off, off_info, off_records, total;
-};
-WsLayout ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
+PrefillWs prefill_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
   const int N = varlen ? num_seqs : B;
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, chunk);
-  WsLayout l;
+  PrefillWs l;
   l.off_chunk_off = 0;
   l.off_info = al256((size_t)(N + 1) * sizeof(int32_t));
   l.off_records = l.off_info + al256((size_t)mc * sizeof(int2));
   l.total = l.off_records + (size_t)mc * H * chunk_record_bytes(dtype, chunk);
   return l;
+}
+
+namespace {
+using WsLayout = PrefillWs;
+inline WsLayout ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
+  return prefill_ws_layout(B, T, H, num_seqs, varlen, chunk, dtype);
 }
 
 template <typename E, int C>
@@ -1163,7 +1180,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
                          H, (int)mc);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
-                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);
+                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr,
+                         (E*)nullptr);
     }
     e = hipGetLastError();
     trace_mark(stream, 2);
@@ -1177,6 +1195,59 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   return e;
 }
 }  // namespace
+
+namespace {
+template <typename E>
+hipError_t launch_states_typed(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* initial_state, const int32_t* cu_seqlens, int N,
+                               int T, int H, int64_t mc, const WsLayout& l, char* ws, void* states, void* ut,
+                               hipStream_t stream) {
+  constexpr int C = BWD_CHUNK;
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + l.off_chunk_off);
+  int2* info = reinterpret_cast<int2*>(ws + l.off_info);
+  char* records = ws + l.off_records;
+  const int total_tokens = cu_seqlens ? T : N * T;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, total_tokens, C, (int)mc,
+                     chunk_off, info);
+  hipError_t e = hipGetLastError();
+  trace_mark(stream, 0);
+  if (e != hipSuccess) return e;
+  if (mc > 0) {
+    const Fusion plain{};
+    hipLaunchKernelGGL((intra_kernel<E, C, GATE_CHANNEL>), dim3((unsigned)(mc * H)), dim3(256), 0, stream,
+                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
+                       records, plain);
+    e = hipGetLastError();
+    trace_mark(stream, 1);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t slots = ((int64_t)N * H + 7) / 8;
+  if (slots > 0) {
+    hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
+                       chunk_off, info, initial_state, (float*)nullptr, (E*)nullptr, N, H, (int)mc, (E*)states,
+                       (E*)ut);
+    e = hipGetLastError();
+    trace_mark(stream, 2);
+  }
+  return e;
+}
+}  // namespace
+
+hipError_t launch_forward_states(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, int B, int T, int H, void* workspace, void* states, void* ut,
+                                 hipStream_t stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  const int N = varlen ? num_seqs : B;
+  const WsLayout l = ws_layout(B, T, H, num_seqs, varlen, BWD_CHUNK, dtype);
+  const int64_t mc = max_chunks(B, T, num_seqs, varlen, BWD_CHUNK);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == 0)
+    return launch_states_typed<__bf16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T, H, mc, l, ws,
+                                       states, ut, stream);
+  return launch_states_typed<float>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, N, T, H, mc, l, ws,
+                                    states, ut, stream);
+}
 
 size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
   return ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;

@@ -134,6 +134,18 @@ def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64,
                          s0, cu, dtype, chunk, dict(seed=seed, la_mode=la_mode, la_scale=la_scale, gate=gate))
 
 
+def make_cotangents(seed: int, inp: PrefillInputs, final_std: float = 0.1, device="cuda"):
+    """Cotangents for a backward call on ``inp``: grad_o ~ N(0, 1) in the input dtype,
+    shaped like o, and grad_final_state ~ N(0, final_std^2) fp32 [N, H, dk, dv]
+    (None when final_std is 0)."""
+    g = _gen(seed + 1000, device)
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    grad_o = _normal(g, (B, T, H, dv), device).to(inp.q.dtype).contiguous()
+    gf = final_std * _normal(g, (inp.num_seqs, H, dk, dv), device) if final_std > 0 else None
+    return grad_o, gf
+
+
 def make_workload(idx: int, device="cuda", **overrides) -> PrefillInputs:
     """Prefill workload ``idx`` (0-3), seed = idx; ``overrides`` may change sizes for
     quicker variants (their draws then differ from the full size)."""

@@ -24,9 +24,11 @@ KDA_ERR_DEVICE = -4
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused", "kda_decode_step_fused",
-           "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read")
+           "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read", "kda_chunk_bwd_workspace_size",
+           "kda_chunk_bwd")
 
-KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm")  # KDA_KERNEL_* ids
+KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm", "bwd_local", "bwd_state",
+                "bwd_chunk")  # KDA_KERNEL_* ids
 
 
 class Fusion(ctypes.Structure):
@@ -71,6 +73,10 @@ def _load():
     lib.kda_decode_step_fused.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.kda_output_norm_gate.restype = I
     lib.kda_output_norm_gate.argtypes = [P, P, P, P, ctypes.c_int64, I, ctypes.c_float, I, P]
+    lib.kda_chunk_bwd_workspace_size.restype = Z
+    lib.kda_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I]
+    lib.kda_chunk_bwd.restype = I
+    lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
     lib.kda_timing_enable.restype = I
     lib.kda_timing_enable.argtypes = [I]
     lib.kda_timing_read.restype = I
@@ -223,6 +229,59 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
             N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
             ctypes.byref(fusion), _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, final_state
+
+
+def bwd_workspace_size(B, T, H, num_seqs=0, dtype=KDA_BF16) -> int:
+    return int(lib.kda_chunk_bwd_workspace_size(B, T, H, num_seqs, dtype))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, grad_o, initial_state=None, grad_final_state=None, cu_seqlens=None,
+              workspace=None, want_grad_initial_state=True):
+    """Gradients of the plain recurrence through ``kda_chunk_bwd``: for the loss
+    sum <o, grad_o> + sum <final_state, grad_final_state>, with respect to q, k, v,
+    log_alpha, beta and initial_state. Shapes as ``chunk_fwd`` (per-channel
+    log_alpha); grad_o has o's shape and dtype; grad_final_state is fp32
+    [N, H, 128, 128] or None. Returns a dict of tensors: grad_q, grad_k, grad_v
+    (input dtype), grad_log_alpha, grad_beta (fp32) and grad_initial_state (fp32,
+    or None when not wanted).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dcode = _dtype_code(q)
+    _need(q, "q", dt, (B, T, H, dk))
+    _need(k, "k", dt, (B, T, H, dk))
+    _need(v, "v", dt, (B, T, H, dv))
+    _need(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(grad_o, "grad_o", dt, (B, T, H, dv))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if grad_final_state is not None:
+        _need(grad_final_state, "grad_final_state", torch.float32, (N, H, dk, dv))
+    out = {"grad_q": torch.empty_like(q), "grad_k": torch.empty_like(k), "grad_v": torch.empty_like(v),
+           "grad_log_alpha": torch.empty_like(log_alpha), "grad_beta": torch.empty_like(beta),
+           "grad_initial_state": (torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+                                  if want_grad_initial_state else None)}
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        ws_bytes = workspace.numel()
+    _check(lib.kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        N if cu_seqlens is not None else 0, _ptr(grad_o), _ptr(grad_final_state), _ptr(out["grad_q"]),
+        _ptr(out["grad_k"]), _ptr(out["grad_v"]), _ptr(out["grad_log_alpha"]), _ptr(out["grad_beta"]),
+        _ptr(out["grad_initial_state"]), B, T, H, dk, dv, dcode, _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out
 
 
 def decode_step(q, k, v, log_alpha, beta, state, o=None, fusion=None):

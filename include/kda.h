@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* Element type of q, k, v and o. */
 typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
@@ -203,13 +203,54 @@ int kda_output_norm_gate(const void *o, const void *gate, const float *weight, v
                          int dv, float eps, int dtype, void *stream);
 
 /*
- * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd and
- * kda_decode_step call records HIP events on its stream before its first kernel
+ * Backward of kda_chunk_fwd (the plain recurrence, no kda_fusion): the gradients of
+ *
+ *     L = sum over tokens of <o_t, grad_o_t> + sum over sequences of <final_state, grad_final_state>
+ *
+ * with respect to q, k, v, log_alpha, beta and initial_state. The pages present
+ * the chunked WY / UT form as what makes KDA efficient to train ("From GPT-2 to
+ * Kimi K3" digest, section on chunked computation; GeekNews "Kimi Linear" summary,
+ * section "청크 단위 병렬화"). It recomputes the forward internally (16-token
+ * chunks, keeping each chunk's entry state), runs the state gradient backwards
+ * through the chunks, then forms every chunk's gradients in parallel.
+ *
+ *   q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, B, T, H, dk,
+ *               dv, dtype: as kda_chunk_fwd (the inputs of the forward call).
+ *   grad_o             [B, T, H, dv]  dtype, required when B*T > 0
+ *   grad_final_state   [N, H, dk, dv] float32, or NULL for zeros
+ *   grad_q, grad_k     [B, T, H, dk]  dtype (written)
+ *   grad_v             [B, T, H, dv]  dtype (written)
+ *   grad_log_alpha     [B, T, H, dk]  float32 (written)
+ *   grad_beta          [B, T, H]      float32 (written)
+ *   grad_initial_state [N, H, dk, dv] float32 (written), or NULL
+ *   workspace          at least kda_chunk_bwd_workspace_size() bytes (256-byte
+ *                      aligned), or NULL: allocated and freed in stream order. It
+ *                      holds two 128 x 128 matrices in dtype per (16-token chunk,
+ *                      head): 64 KiB (bf16) per 16 tokens and head.
+ * Alignment: 16 bytes for every tensor except beta, grad_beta and cu_seqlens (4).
+ * The written gradients must not alias any input. Returns KDA_OK,
+ * KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED (dk or dv != 128, bad dtype),
+ * KDA_ERR_WORKSPACE or KDA_ERR_DEVICE, with the same checks as kda_chunk_fwd.
+ * T = 0 (or B = 0) writes grad_initial_state = grad_final_state (zeros if NULL).
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int num_seqs, int dtype);
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  int num_seqs, const void *grad_o, const float *grad_final_state, void *grad_q,
+                  void *grad_k, void *grad_v, float *grad_log_alpha, float *grad_beta,
+                  float *grad_initial_state, int B, int T, int H, int dk, int dv, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd, kda_chunk_bwd
+ * and kda_decode_step call records HIP events on its stream before its first kernel
  * and after each kernel it launches, so the durations are measured on the stream
  * the kernels run on (the fused variants and kda_output_norm_gate included). Kernel
  * ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA (intra-chunk), KDA_KERNEL_INTER
  * (inter-chunk state and output), KDA_KERNEL_DECODE, KDA_KERNEL_OUTNORM (output
- * RMSNorm and gate).
+ * RMSNorm and gate), and for kda_chunk_bwd, whose internal forward reports under the
+ * first three, KDA_KERNEL_BWD_LOCAL (per-chunk backward record), KDA_KERNEL_BWD_STATE
+ * (state gradient through the chunks) and KDA_KERNEL_BWD_CHUNK (per-chunk gradients).
  *
  * kda_timing_enable(1) starts recording (and discards anything recorded before);
  * kda_timing_enable(0) stops. kda_timing_read() waits for the recorded events,
@@ -224,7 +265,10 @@ int kda_output_norm_gate(const void *o, const void *gate, const float *weight, v
 #define KDA_KERNEL_INTER 2
 #define KDA_KERNEL_DECODE 3
 #define KDA_KERNEL_OUTNORM 4
-#define KDA_NUM_KERNELS 5
+#define KDA_KERNEL_BWD_LOCAL 5
+#define KDA_KERNEL_BWD_STATE 6
+#define KDA_KERNEL_BWD_CHUNK 7
+#define KDA_NUM_KERNELS 8
 
 int kda_timing_enable(int on);
 int kda_timing_read(double *total_ms, int *launches, int n);

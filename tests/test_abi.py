@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     version = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.kda_abi_version() == version == 2
+    assert L.kda_abi_version() == version == 3
     for st in (0, -1, -2, -3, -4):
         assert L.kda_status_string(st).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(7)
@@ -195,3 +195,48 @@ def test_gate_kind_checks(gate, la, status):
     assert fused_chunk_call(f, la=la) == status
     assert L.kda_decode_step_fused(FAKE, FAKE, FAKE, la, FAKE, FAKE, FAKE, 4, 2, 128, 128, 0,
                                    ctypes.byref(f), None) == status
+
+
+def bwd_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num_seqs=0, do=FAKE, dfin=None,
+             dq=FAKE, dk_=FAKE, dv_=FAKE, dla=FAKE, db=FAKE, ds0=None, B=1, T=64, H=2, dk=128, dv=128, dtype=0,
+             ws=None, ws_bytes=0):
+    return L.kda_chunk_bwd(q, k, v, la, beta, s0, cu, num_seqs, do, dfin, dq, dk_, dv_, dla, db, ds0, B, T, H, dk, dv,
+                           dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(do=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(dq=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(dla=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(db=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(la=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(do=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(dla=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(ds0=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(dfin=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(db=ctypes.c_void_p((1 << 20) + 2)), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(ws=FAKE, ws_bytes=16), kda.KDA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 40), kda.KDA_ERR_INVALID_ARG),
+])
+def test_chunk_bwd_rejects(kw, status):
+    assert bwd_call(**kw) == status
+    assert L.kda_last_error()
+
+
+def test_chunk_bwd_empty_batch_is_ok_without_device():
+    assert bwd_call(B=0, T=0) == kda.KDA_OK
+    assert bwd_call(cu=FAKE, num_seqs=0, T=0) == kda.KDA_OK
+
+
+def test_bwd_workspace_size():
+    # two 128 x 128 bf16 matrices per (16-token chunk, head) dominate
+    n = kda.bwd_workspace_size(1, 4096, 16)
+    assert n >= 4096 // 16 * 16 * 2 * 128 * 128 * 2
+    assert kda.bwd_workspace_size(1, 4096, 16, dtype=kda.KDA_FP32) > n
+    assert kda.bwd_workspace_size(1, 4096, 16, num_seqs=3) >= n
+    assert kda.bwd_workspace_size(1, 64, 0) == 0
