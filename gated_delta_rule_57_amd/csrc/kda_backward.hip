@@ -64,16 +64,34 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// Plain per-(head, chunk) record for the reverse state pass, row-major.
+// Per-(head, chunk) record for the reverse state pass, in the MFMA operand order
+// bwd_state_kernel consumes (lane l = m + 16 g; the fragment convention of
+// kda_device.h, chunk rows padded to 32 with zeros):
+//   WT   [8 rt][64][4]  slot s of the A fragment of (-W)^T, channel tile rt: -W[4g+s][16rt+m]
+//   QTT  [8 rt][64][4]  the same for (Q e^G)^T
+//   KEF  [4 kb][64][8]  A fragment of K e^{g_C-G} (rows m, channels 32 kb + koff(g, s))
+//   PT   [64][4]        A fragment of P^T: P[4g+s][m]
+//   GAM  float[128]     e^{g_C}
 template <typename E>
 struct BRec {
-  static constexpr size_t W = 0;                                 // E[16][128]   W = T diag(beta) K e^G
-  static constexpr size_t QT = W + (size_t)BC * D * sizeof(E);   // E[16][128]   Q e^G
-  static constexpr size_t KE = QT + (size_t)BC * D * sizeof(E);  // E[16][128]   K e^{g_C - G}
-  static constexpr size_t P = KE + (size_t)BC * D * sizeof(E);   // float[16][16] P (s <= r, else 0)
-  static constexpr size_t GAM = P + (size_t)BC * BC * 4;         // float[128]   e^{g_C}
+  static constexpr size_t WT = 0;
+  static constexpr size_t QTT = WT + (size_t)8 * 64 * 4 * sizeof(E);
+  static constexpr size_t KEF = QTT + (size_t)8 * 64 * 4 * sizeof(E);
+  static constexpr size_t PT = KEF + (size_t)4 * 64 * 8 * sizeof(E);
+  static constexpr size_t GAM = bal256(PT + (size_t)64 * 4 * sizeof(E));
   static constexpr size_t BYTES = bal256(GAM + D * 4);
 };
+
+// (row, channel) of a 16 x 128 chunk matrix -> element index in the A fragment of its
+// transpose (tile rt = channel / 16: lane (channel % 16) + 16 (row / 4), slot row % 4)
+__device__ __forceinline__ int tfrag_index(int row, int ch) { return ((ch >> 4) * 64 + (row >> 2) * 16 + (ch & 15)) * 4 + (row & 3); }
+// (row, channel) -> element index in the A fragment of the matrix itself (k = channel)
+__device__ __forceinline__ int afrag_index(int row, int ch) {
+  const int kb = ch >> 5, ko = ch & 31;
+  const int gg = ko < 16 ? ko >> 2 : (ko - 16) >> 2;
+  const int ss = ko < 16 ? ko & 3 : 4 + ((ko - 16) & 3);
+  return (kb * 64 + gg * 16 + row) * 8 + ss;
+}
 
 // Element-wise phases: thread t owns row r = t >> 4 and channels 8 (t & 15) .. +7.
 struct RowMap {
@@ -166,13 +184,16 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
     }
   }
   __syncthreads();
-  if (t < BC) {  // T = (I + A)^-1 by forward substitution, one column per thread
+  if (t < BC) {  // T = (I + A)^-1 by forward substitution, one column per thread, in registers
     const int cc = t;
+    float tc[BC];
 #pragma unroll
     for (int r = 0; r < BC; ++r) {
-      float x = r == cc ? 1.f : 0.f;
-      for (int s = cc; s < r; ++s) x -= L.beta[r] * L.M[r][s] * L.T[s][cc];
-      L.T[r][cc] = r < cc ? 0.f : x;
+      float x = r == cc ? 1.f : 0.f;  // rows above cc stay exactly 0
+#pragma unroll
+      for (int s = 0; s < r; ++s) x -= L.beta[r] * L.M[r][s] * tc[s];
+      tc[r] = x;
+      L.T[r][cc] = x;
     }
   }
   __syncthreads();
@@ -197,22 +218,24 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   local_forward<E, true>(L, q, k, log_alpha, beta, inf.x, inf.y, h, H, t);
 
   char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
+  E* wt = reinterpret_cast<E*>(rb + BR::WT);
+  E* qtt = reinterpret_cast<E*>(rb + BR::QTT);
+  E* kef = reinterpret_cast<E*>(rb + BR::KEF);
   const RowMap rm(t);
-  float w[8], qt[8], ke[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ch = rm.c0 + i;
     const float gr = L.G[rm.r][ch];
     float acc = 0.f;
     for (int s = 0; s <= rm.r; ++s) acc += L.T[rm.r][s] * L.beta[s] * L.K[s][ch] * exp2_hw(L.G[s][ch]);
-    w[i] = acc;
-    qt[i] = L.Q[rm.r][ch] * exp2_hw(gr);
-    ke[i] = L.K[rm.r][ch] * exp2_hw(L.G[BC - 1][ch] - gr);
+    wt[tfrag_index(rm.r, ch)] = from_f<E>(-acc);
+    qtt[tfrag_index(rm.r, ch)] = from_f<E>(L.Q[rm.r][ch] * exp2_hw(gr));
+    kef[afrag_index(rm.r, ch)] = from_f<E>(L.K[rm.r][ch] * exp2_hw(L.G[BC - 1][ch] - gr));
   }
-  store8(reinterpret_cast<E*>(rb + BR::W), D, rm.r, rm.c0, w);
-  store8(reinterpret_cast<E*>(rb + BR::QT), D, rm.r, rm.c0, qt);
-  store8(reinterpret_cast<E*>(rb + BR::KE), D, rm.r, rm.c0, ke);
-  reinterpret_cast<float*>(rb + BR::P)[t] = L.Pm[t >> 4][t & 15];
+  {  // P^T fragment: thread t = (row r, column m) of P
+    const int r = t >> 4, mm = t & 15;
+    reinterpret_cast<E*>(rb + BR::PT)[((r >> 2) * 16 + mm) * 4 + (r & 3)] = from_f<E>(L.Pm[r][mm]);
+  }
   if (t < D) reinterpret_cast<float*>(rb + BR::GAM)[t] = exp2_hw(L.G[BC - 1][t]);
 }
 
@@ -231,6 +254,15 @@ __global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ 
                                                        int mc) {
   using BR = BRec<E>;
   typedef typename Frag<E>::T FragT;
+  typedef typename Vec4<E>::T V4;
+  // four elements kept as raw 32-bit words in the register stage (packed bf16
+  // vectors in a struct array otherwise end up in scratch)
+  typedef unsigned int RawV __attribute__((ext_vector_type(sizeof(V4) / 4)));
+  constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
+  constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
+  __shared__ __attribute__((aligned(16))) E xs[D * XW];
+  __shared__ __attribute__((aligned(16))) float xg[D];
+
   const int b = blockIdx.x;
   const int xcd = b & 7, rest = b >> 3;
   const int ct = rest & 7, slot = rest >> 3;
@@ -251,64 +283,105 @@ __global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ 
     }
   }
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-
-  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
-  for (int c = c_end - 1; c >= c_begin; --c) {
-    const char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
-    const E* W = reinterpret_cast<const E*>(rb + BR::W);
-    const E* QT = reinterpret_cast<const E*>(rb + BR::QT);
-    const E* KE = reinterpret_cast<const E*>(rb + BR::KE);
-    const float* P = reinterpret_cast<const float*>(rb + BR::P);
-    const float* gam = reinterpret_cast<const float*>(rb + BR::GAM);
-    const int2 inf = info[c];
-
-    // the gradient at the chunk's end, for the per-chunk kernel
-    {
-      E* dp = dstates + ((size_t)h * mc + c) * D * D + 16 * ct + m;
+  // slots 0..3 from a 4-vector, slots 4..7 (chunk rows 16..31) zero
+  auto half_frag = [](const RawV& raw) {
+    const V4 x = __builtin_bit_cast(V4, raw);
+    FragT f;
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dp[(size_t)(16 * rt + 4 * g + i) * D] = from_f<E>(Lm[rt][i]);
+    for (int s = 0; s < 4; ++s) {
+      f[s] = x[s];
+      f[4 + s] = from_f<E>(0.f);
     }
-    // B fragment of dO over the chunk rows (k = row; rows 16..31 are padding)
-    FragT dOb, Pa;
+    return f;
+  };
+
+  // operands are kept as whole fragments (chunk rows 16..31 zero): a stage of
+  // half-width vectors gets merged into wide loads that keep it out of registers
+  struct Stage {
+    FragT wt[8], qt[8], pt, dov;
+    FragT ke[4];
+    floatx4 gm;
+    int2 inf;
+  };
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+  auto load = [&](Stage& st, int c) {
+    const char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
+    const E* wt = reinterpret_cast<const E*>(rb + BR::WT);
+    const E* qt = reinterpret_cast<const E*>(rb + BR::QTT);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      st.wt[rt] = half_frag(*reinterpret_cast<const RawV*>(wt + ((size_t)rt * 64 + lane) * 4));
+      st.qt[rt] = half_frag(*reinterpret_cast<const RawV*>(qt + ((size_t)rt * 64 + lane) * 4));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      st.ke[kb] = load_frag<E>(reinterpret_cast<const E*>(rb + BR::KEF) + ((size_t)kb * 64 + lane) * 8);
+    st.pt = half_frag(*reinterpret_cast<const RawV*>(reinterpret_cast<const E*>(rb + BR::PT) + (size_t)lane * 4));
+    st.gm = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(rb + BR::GAM) + 4 * (lane & 31));
+    const int2 inf = info[c];
+    st.inf = inf;
+    V4 d;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int row = 4 * g + s;
-      dOb[s] = row < inf.y ? dout[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] : from_f<E>(0.f);
-      dOb[4 + s] = from_f<E>(0.f);
-      Pa[s] = from_f<E>(P[row * BC + m]);  // A fragment of P^T: A[m][row] = P[row][m]
-      Pa[4 + s] = from_f<E>(0.f);
+      d[s] = row < inf.y ? dout[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] : from_f<E>(0.f);
     }
+    st.dov = half_frag(__builtin_bit_cast(RawV, d));
+  };
+
+  auto compute = [&](const Stage& st, int c) {
+    {  // the gradient at the chunk's end, for the per-chunk kernel, as 16-byte row pieces
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[(16 * rt + 4 * g + i) * XW + m] = from_f<E>(Lm[rt][i]);
+      __syncthreads();
+      E* dp = dstates + ((size_t)h * mc + c) * D * D + 16 * ct;
+#pragma unroll
+      for (int j = 0; j < 2 * (int)sizeof(E); ++j) {
+        const int piece = lane + 64 * j, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(dp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      }
+      __syncthreads();
+    }
+    const FragT dOb = st.dov;  // B fragment of dO over the chunk rows
     // dU~ = P^T dO + (K e^{g_C-G}) dS_C
     floatx4 du = zero4;
-    mma(du, Pa, dOb);
+    mma(du, st.pt, dOb);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mma(du, frag_rowk<E>(KE, D, m, 32 * kb, g), acc_pair_to_frag<E>(Lm[2 * kb], Lm[2 * kb + 1]));
+    for (int kb = 0; kb < 4; ++kb) mma(du, st.ke[kb], acc_pair_to_frag<E>(Lm[2 * kb], Lm[2 * kb + 1]));
     {
-      E* up = dut + ((size_t)h * mc + c) * BC * D + 16 * ct + m;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) up[(size_t)(4 * g + i) * D] = from_f<E>(du[i]);
+      for (int i = 0; i < 4; ++i) xs[(4 * g + i) * XW + m] = from_f<E>(du[i]);
+      if (lane < 32) *reinterpret_cast<floatx4*>(&xg[4 * lane]) = st.gm;
+      __syncthreads();
+      if (lane < 16 * (16 / VE)) {
+        const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(dut + ((size_t)h * mc + c) * BC * D + (size_t)row * D + 16 * ct + col) =
+            *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      }
     }
     const FragT dUb = acc_pair_to_frag<E>(du, zero4);
-    // dS0 = e^{g_C} o dS_C + (Q e^G)^T dO - W^T dU~
+    // dS0 = e^{g_C} o dS_C + (Q e^G)^T dO + (-W)^T dU~
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
-      const floatx4 gv = *reinterpret_cast<const floatx4*>(gam + 16 * rt + 4 * g);
+      const floatx4 gv = *reinterpret_cast<const floatx4*>(&xg[16 * rt + 4 * g]);
       Lm[rt] = gv * Lm[rt];
-      FragT qa, wa;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const size_t e = (size_t)(4 * g + s) * D + 16 * rt + m;
-        qa[s] = QT[e];
-        wa[s] = from_f<E>(-to_f(W[e]));
-        qa[4 + s] = from_f<E>(0.f);
-        wa[4 + s] = from_f<E>(0.f);
-      }
-      mma(Lm[rt], qa, dOb);
-      mma(Lm[rt], wa, dUb);
+      mma(Lm[rt], st.qt[rt], dOb);
+      mma(Lm[rt], st.wt[rt], dUb);
     }
+    __syncthreads();
+  };
+
+  // two named stages: each step loads chunk c - 1 into the stage consumed one step
+  // earlier (past the start, the first chunk again: every step issues the same loads)
+  Stage sa, sb;
+  if (c_begin < c_end) load(sa, c_end - 1);
+  for (int c0 = c_end - 1; c0 >= c_begin; c0 -= 2) {
+    load(sb, max(c0 - 1, c_begin));
+    compute(sa, c0);
+    load(sa, max(c0 - 2, c_begin));
+    if (c0 - 1 >= c_begin) compute(sb, c0 - 1);
   }
   if (d_initial) {
 #pragma unroll
@@ -339,7 +412,7 @@ __device__ __forceinline__ typename Frag<E>::T zero_frag() {
 }
 
 template <typename E>
-__global__ void __launch_bounds__(256) bwd_chunk_kernel(
+__global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const E* __restrict__ dout, const E* __restrict__ states,
     const E* __restrict__ dstates, const E* __restrict__ ut, const E* __restrict__ dut,
@@ -464,47 +537,52 @@ __global__ void __launch_bounds__(256) bwd_chunk_kernel(
   float dqv[8], dkv[8], dgv[8], kex[8];
   {
     const float br = L.beta[r];
-    float dbk[8], dbv[8];
+    float dbk[8], dbv[8], kr[8], qr[8], gr[8];
+    float ra[8], rp[8], rat[8], rpt[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      dbk[i] = 0.f;
-      dbv[i] = 0.f;
+      dbk[i] = dbv[i] = ra[i] = rp[i] = rat[i] = rpt[i] = 0.f;
+      kr[i] = L.K[r][rm.c0 + i];
+      qr[i] = L.Q[r][rm.c0 + i];
+      gr[i] = L.G[r][rm.c0 + i];
     }
-    for (int u = r; u < BC; ++u) {  // T is lower: T[u][r] = 0 for u < r
-      const float tur = L.T[u][r];
+    // One pass over the chunk's rows s. T is lower (T[s][r] = 0 for s < r), dA
+    // strictly lower and dP lower, so row s < r only feeds the sums along row r
+    // (ra, rp: weights e^{g_r - g_s}) and row s > r only those down column r
+    // (rat, rpt: weights e^{g_s - g_r}); with g non-increasing both weights are
+    // 2^-|g_r - g_s|, and the other side's coefficients are exact zeros.
+#pragma unroll 2
+    for (int s = 0; s < BC; ++s) {
+      const float tsr = L.T[s][r];
+      const float a_rs = S.dT[r][s], p_rs = S.dP[r][s];                  // dA, dP along row r
+      const float a_sr = L.beta[s] * S.dT[s][r], p_sr = S.dP[s][r];      // down column r
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        dbk[i] -= tur * S.X2[u][rm.c0 + i];  // dB_K = T^T dW
-        dbv[i] += tur * S.dU[u][rm.c0 + i];  // dB_V = T^T dU
+        const int ch = rm.c0 + i;
+        dbk[i] -= tsr * S.X2[s][ch];  // dB_K = T^T dW
+        dbv[i] += tsr * S.dU[s][ch];  // dB_V = T^T dU
+        const float ks = L.K[s][ch], qs = L.Q[s][ch];
+        const float f = exp2_hw(-fabsf(gr[i] - L.G[s][ch]));
+        ra[i] += a_rs * ks * f;
+        rp[i] += p_rs * ks * f;
+        rat[i] += a_sr * ks * f;
+        rpt[i] += p_sr * qs * f;
       }
     }
     float dbeta_part = 0.f, dvv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ch = rm.c0 + i;
-      const float kr = L.K[r][ch], qr = L.Q[r][ch], gr = L.G[r][ch];
-      const float eg = exp2_hw(gr);
-      dbeta_part += dbk[i] * kr * eg + dbv[i] * S.V[r][ch];
+      const float eg = exp2_hw(gr[i]);
+      const float el = exp2_hw(L.G[BC - 1][ch] - gr[i]);
+      dbeta_part += dbk[i] * kr[i] * eg + dbv[i] * S.V[r][ch];
       dvv[i] = br * dbv[i];
-      // decay-weighted sums over the chunk's other rows
-      float ra = 0.f, rp = 0.f, rat = 0.f, rpt = 0.f;
-      for (int s = 0; s <= r; ++s) {
-        const float f = exp2_hw(gr - L.G[s][ch]);  // exponent <= 0
-        const float ks = L.K[s][ch] * f;
-        ra += S.dT[r][s] * ks;  // dA (zero on the diagonal)
-        rp += S.dP[r][s] * ks;
-      }
-      for (int uu = r; uu < BC; ++uu) {
-        const float f = exp2_hw(L.G[uu][ch] - gr);  // exponent <= 0
-        rat += L.beta[uu] * S.dT[uu][r] * L.K[uu][ch] * f;
-        rpt += S.dP[uu][r] * L.Q[uu][ch] * f;
-      }
       const float x1 = S.X1[r][ch], x3 = S.X3[r][ch];
-      const float ke = kr * exp2_hw(L.G[BC - 1][ch] - gr);
-      dqv[i] = x1 * eg + rp;
-      dkv[i] = br * dbk[i] * eg + br * ra + rat + rpt + x3 * exp2_hw(L.G[BC - 1][ch] - gr);
-      kex[i] = x3 * ke;
-      dgv[i] = x1 * qr * eg + rp * qr + br * dbk[i] * kr * eg + br * ra * kr - rat * kr - rpt * kr - kex[i];
+      dqv[i] = x1 * eg + rp[i];
+      dkv[i] = br * dbk[i] * eg + br * ra[i] + rat[i] + rpt[i] + x3 * el;
+      kex[i] = x3 * kr[i] * el;
+      dgv[i] = x1 * qr[i] * eg + rp[i] * qr[i] + br * dbk[i] * kr[i] * eg + br * ra[i] * kr[i] - rat[i] * kr[i] -
+               rpt[i] * kr[i] - kex[i];
     }
     dbeta_part = sum16(dbeta_part);
     if ((t & 15) == 0 && r < len) {

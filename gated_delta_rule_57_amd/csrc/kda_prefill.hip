@@ -924,6 +924,149 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 }
 
 // ---------------------------------------------------------------------------
+// Inter-chunk kernel for 16-token chunks: one wave per (sequence, head, 16-column
+// slab), laid out like inter_kernel, with the next chunk's record fragments loaded
+// into registers while the current chunk is computed (a 16-token chunk is only a
+// few MFMAs deep, so without the lookahead every chunk waits out a memory round
+// trip). The per-chunk outputs of the backward pass (states, U~) are transposed
+// through LDS and written as whole 16-byte row pieces.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ records,
+                                                     const int32_t* __restrict__ chunk_off,
+                                                     const int2* __restrict__ info,
+                                                     const float* __restrict__ initial_state,
+                                                     float* __restrict__ final_state, E* __restrict__ o, int N, int H,
+                                                     int mc, E* __restrict__ states, E* __restrict__ ut) {
+  using RC = Rec<E, 16>;
+  typedef typename Frag<E>::T FragT;
+  static_assert(RC::NRT == 1 && RC::NKC == 1, "16-token chunks");
+  constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
+  constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
+  __shared__ __attribute__((aligned(16))) E xs[D * XW];
+  __shared__ __attribute__((aligned(16))) float xg[D];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, rest = b >> 3;
+  const int ct = rest & 7, slot = rest >> 3;
+  const int u = slot * 8 + xcd;
+  if (u >= N * H) return;
+  const int n = u / H, h = u - n * H;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const size_t HD = (size_t)H * D;
+  const size_t sbase = (size_t)u * D * D + 16 * ct + m;
+
+  floatx4 S[8];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) S[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (initial_state) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[rt][i] = initial_state[sbase + (size_t)(16 * rt + 4 * g + i) * D];
+  }
+
+  struct Stage {
+    FragT wn[4], qt[4], ke[8], pp;
+    float uu[4];
+    floatx4 gm;  // lanes 0..31: e^{g_C} of channels 4 lane .. 4 lane + 3
+    int2 inf;
+  };
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+  auto load = [&](Stage& st, int c) {
+    const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
+    const E* rec = reinterpret_cast<const E*>(rb);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      st.wn[kb] = load_frag<E>(rec + RC::WN + ((size_t)kb * 64 + lane) * 8);
+      st.qt[kb] = load_frag<E>(rec + RC::QT + ((size_t)kb * 64 + lane) * 8);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) st.ke[rt] = load_frag<E>(rec + RC::KE + ((size_t)rt * 64 + lane) * 8);
+    st.pp = load_frag<E>(rec + RC::PP + (size_t)lane * 8);
+    load4f(rec + RC::UU + ((size_t)ct * 64 + lane) * 4, st.uu);
+    st.gm = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES) + 4 * (lane & 31));
+    st.inf = info[c];
+  };
+
+  auto compute = [&](const Stage& st, int c) {
+    FragT Sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<E>(S[2 * kb], S[2 * kb + 1]);
+    if (states) {  // the slab of the state entering the chunk, as 16-byte row pieces
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[(16 * rt + 4 * g + i) * XW + m] = from_f<E>(S[rt][i]);
+      __syncthreads();
+      E* sp = states + ((size_t)h * mc + c) * D * D + 16 * ct;
+#pragma unroll
+      for (int j = 0; j < 2 * (int)sizeof(E); ++j) {
+        const int piece = lane + 64 * j, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(sp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      }
+      __syncthreads();
+    }
+    // U~ = U - W S  (the record holds -W)
+    floatx4 Ut = floatx4{st.uu[0], st.uu[1], st.uu[2], st.uu[3]};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma(Ut, st.wn[kb], Sb[kb]);
+    if (ut) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
+      __syncthreads();
+      if (lane < 16 * (16 / VE)) {
+        const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(ut + ((size_t)h * mc + c) * 16 * D + (size_t)row * D + 16 * ct + col) =
+            *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      }
+      __syncthreads();
+    }
+    const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});
+    if (o) {  // O = (Q e^G) S + P U~
+      floatx4 X = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(X, st.qt[kb], Sb[kb]);
+      mma(X, st.pp, Ub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row < st.inf.y) o[(size_t)(st.inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[i]);
+      }
+    }
+    // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
+    if (lane < 32) *reinterpret_cast<floatx4*>(&xg[4 * lane]) = st.gm;
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      const floatx4 gv = *reinterpret_cast<const floatx4*>(&xg[16 * rt + 4 * g]);
+      S[rt] = gv * S[rt];
+      mma(S[rt], st.ke[rt], Ub);
+    }
+    __syncthreads();
+  };
+
+  Stage st[2];
+  if (c_begin < c_end) load(st[0], c_begin);
+  for (int c0 = c_begin; c0 < c_end; c0 += 2) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = c0 + r;
+      // the stage consumed one step earlier takes chunk c + 1 (past the end, the
+      // last chunk again: every step issues the same loads)
+      load(st[r ^ 1], min(c + 1, c_end - 1));
+      if (c < c_end) compute(st[r], c);
+    }
+  }
+  if (final_state) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) final_state[sbase + (size_t)(16 * rt + 4 * g + i) * D] = S[rt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Inter-chunk kernel, bf16 records of 64-token chunks, four waves per (sequence,
 // head, 16-column slab). The work of one chunk is split over the four SIMDs of a
 // CU, wave w taking
@@ -1178,6 +1321,9 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
       hipLaunchKernelGGL(inter_wg_kernel<INTER_LOOKAHEAD>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream,
                          records, chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N,
                          H, (int)mc);
+    } else if constexpr (C == 16) {
+      hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+                         info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr, (E*)nullptr);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
                          chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr,
@@ -1223,9 +1369,8 @@ hipError_t launch_states_typed(const void* q, const void* k, const void* v, cons
   }
   const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
-    hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
-                       chunk_off, info, initial_state, (float*)nullptr, (E*)nullptr, N, H, (int)mc, (E*)states,
-                       (E*)ut);
+    hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+                       info, initial_state, (float*)nullptr, (E*)nullptr, N, H, (int)mc, (E*)states, (E*)ut);
     e = hipGetLastError();
     trace_mark(stream, 2);
   }
