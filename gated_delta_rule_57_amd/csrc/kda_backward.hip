@@ -47,7 +47,7 @@ namespace {
 
 constexpr int BC = BWD_CHUNK;
 static_assert(BC == 16, "the backward kernels are written for 16-token chunks");
-constexpr int LDP = D + 4;  // row stride of the fp32 [16][128] LDS matrices
+constexpr int LDP = D;  // row stride of the fp32 [16][128] LDS matrices (see RowMap)
 constexpr int LDS16 = BC + 1;
 constexpr float LOG2E_B = 1.4426950408889634f;
 
@@ -93,10 +93,15 @@ __device__ __forceinline__ int afrag_index(int row, int ch) {
   return (kb * 64 + gg * 16 + row) * 8 + ss;
 }
 
-// Element-wise phases: thread t owns row r = t >> 4 and channels 8 (t & 15) .. +7.
+// Element-wise phases: thread t owns row r = t >> 4. It loads channels
+// c0 .. c0 + 7 (c0 = 8 (t & 15)) from global memory, and computes on channels
+// ch(i) = (t & 15) + 16 i, i = 0..7: the sixteen lanes of a row then touch sixteen
+// consecutive words of any LDS row, one per bank, and the four rows of a wave read
+// the same words of another row (a broadcast) in the loops over the chunk's rows.
 struct RowMap {
-  int r, c0;
-  __device__ RowMap(int t) : r(t >> 4), c0(8 * (t & 15)) {}
+  int r, c0, cg;
+  __device__ RowMap(int t) : r(t >> 4), c0(8 * (t & 15)), cg(t & 15) {}
+  __device__ int ch(int i) const { return cg + 16 * i; }
 };
 
 // Loads eight consecutive values of row r (zeros past len) as fp32.
@@ -109,11 +114,6 @@ __device__ __forceinline__ void load8(const E* base, size_t row_stride, int r, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = 0.f;
   }
-}
-template <typename E>
-__device__ __forceinline__ void store8(E* base, size_t row_stride, int r, int c0, const float in[8]) {
-  store4f(base + (size_t)r * row_stride + c0, in);
-  store4f(base + (size_t)r * row_stride + c0 + 4, in + 4);
 }
 
 // The state-independent part shared by both per-chunk kernels: q, k (and v) rows,
@@ -160,9 +160,9 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
     float kr[8], qr[8], gr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      kr[i] = L.K[rm.r][rm.c0 + i];
-      qr[i] = L.Q[rm.r][rm.c0 + i];
-      gr[i] = L.G[rm.r][rm.c0 + i];
+      kr[i] = L.K[rm.r][rm.ch(i)];
+      qr[i] = L.Q[rm.r][rm.ch(i)];
+      gr[i] = L.G[rm.r][rm.ch(i)];
     }
 #pragma unroll
     for (int s = 0; s < BC; ++s) {
@@ -170,7 +170,7 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
       if (s <= rm.r) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float ks = L.K[s][rm.c0 + i] * exp2_hw(gr[i] - L.G[s][rm.c0 + i]);  // exponent <= 0
+          const float ks = L.K[s][rm.ch(i)] * exp2_hw(gr[i] - L.G[s][rm.ch(i)]);  // exponent <= 0
           pk += kr[i] * ks;
           if constexpr (WANT_P) pq += qr[i] * ks;
         }
@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   const RowMap rm(t);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int ch = rm.c0 + i;
+    const int ch = rm.ch(i);
     const float gr = L.G[rm.r][ch];
     float acc = 0.f;
     for (int s = 0; s <= rm.r; ++s) acc += L.T[rm.r][s] * L.beta[s] * L.K[s][ch] * exp2_hw(L.G[s][ch]);
@@ -497,15 +497,15 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     float x2r[8], dur[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      x2r[i] = S.X2[rm.r][rm.c0 + i];
-      dur[i] = S.dU[rm.r][rm.c0 + i];
+      x2r[i] = S.X2[rm.r][rm.ch(i)];
+      dur[i] = S.dU[rm.r][rm.ch(i)];
     }
 #pragma unroll
     for (int s = 0; s < BC; ++s) {
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int ch = rm.c0 + i;
+        const int ch = rm.ch(i);
         acc += -x2r[i] * L.K[s][ch] * exp2_hw(L.G[s][ch]) + dur[i] * S.V[s][ch];
       }
       acc = sum16(acc) * L.beta[s];
@@ -542,9 +542,9 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       dbk[i] = dbv[i] = ra[i] = rp[i] = rat[i] = rpt[i] = 0.f;
-      kr[i] = L.K[r][rm.c0 + i];
-      qr[i] = L.Q[r][rm.c0 + i];
-      gr[i] = L.G[r][rm.c0 + i];
+      kr[i] = L.K[r][rm.ch(i)];
+      qr[i] = L.Q[r][rm.ch(i)];
+      gr[i] = L.G[r][rm.ch(i)];
     }
     // One pass over the chunk's rows s. T is lower (T[s][r] = 0 for s < r), dA
     // strictly lower and dP lower, so row s < r only feeds the sums along row r
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       const float a_sr = L.beta[s] * S.dT[s][r], p_sr = S.dP[s][r];      // down column r
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int ch = rm.c0 + i;
+        const int ch = rm.ch(i);
         dbk[i] -= tsr * S.X2[s][ch];  // dB_K = T^T dW
         dbv[i] += tsr * S.dU[s][ch];  // dB_V = T^T dU
         const float ks = L.K[s][ch], qs = L.Q[s][ch];
@@ -572,7 +572,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     float dbeta_part = 0.f, dvv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int ch = rm.c0 + i;
+      const int ch = rm.ch(i);
       const float eg = exp2_hw(gr[i]);
       const float el = exp2_hw(L.G[BC - 1][ch] - gr[i]);
       dbeta_part += dbk[i] * kr[i] * eg + dbv[i] * S.V[r][ch];
@@ -591,16 +591,20 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       dbeta[(size_t)(tok0 + r) * H + h] = dbeta_part + am;
     }
     if (r < len) {
-      store8(dv + rowbase, HD, r, rm.c0, dvv);
-      store8(dq + rowbase, HD, r, rm.c0, dqv);
-      store8(dk + rowbase, HD, r, rm.c0, dkv);
+      const size_t ro = rowbase + (size_t)r * HD;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dv[ro + rm.ch(i)] = from_f<E>(dvv[i]);
+        dq[ro + rm.ch(i)] = from_f<E>(dqv[i]);
+        dk[ro + rm.ch(i)] = from_f<E>(dkv[i]);
+      }
     }
   }
   __syncthreads();  // every read of X2 and dU is done
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    S.X2[r][rm.c0 + i] = dgv[i];
-    S.dU[r][rm.c0 + i] = kex[i];
+    S.X2[r][rm.ch(i)] = dgv[i];
+    S.dU[r][rm.ch(i)] = kex[i];
   }
   __syncthreads();
   if (t < D) {  // g_C = G at the last row: its gradient gathers the K e^{g_C-G} and e^{g_C} terms
