@@ -931,6 +931,8 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 // trip). The per-chunk outputs of the backward pass (states, U~) are transposed
 // through LDS and written as whole 16-byte row pieces.
 // ---------------------------------------------------------------------------
+constexpr int INTER16_TOUCH_AHEAD = 4;
+
 template <typename E>
 __global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ records,
                                                      const int32_t* __restrict__ chunk_off,
@@ -1046,6 +1048,15 @@ __global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ re
     __syncthreads();
   };
 
+  // L2 touch INTER16_TOUCH_AHEAD chunks beyond the register stage: each of the
+  // head's eight slab waves reads one word of every eighth line of the record, so
+  // the real loads hit in L2 (the words are XOR-folded into tacc, stored only by a
+  // never-taken branch, which keeps the loads without waiting for them)
+  constexpr int LINES = (int)(RC::BYTES / 128);
+  static_assert(RC::BYTES % 128 == 0 && LINES <= 8 * 64, "one touch per lane");
+  const int touch_line = ct + 8 * lane;
+  unsigned tacc = 0u, tv[2] = {0u, 0u};
+
   Stage st[2];
   if (c_begin < c_end) load(st[0], c_begin);
   for (int c0 = c_begin; c0 < c_end; c0 += 2) {
@@ -1055,9 +1066,16 @@ __global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ re
       // the stage consumed one step earlier takes chunk c + 1 (past the end, the
       // last chunk again: every step issues the same loads)
       load(st[r ^ 1], min(c + 1, c_end - 1));
+      if (touch_line < LINES)
+        tv[r] = *reinterpret_cast<const unsigned*>(
+            records + ((size_t)h * mc + min(c + 1 + INTER16_TOUCH_AHEAD, c_end - 1)) * RC::BYTES +
+            (size_t)touch_line * 128);
       if (c < c_end) compute(st[r], c);
+      tacc ^= tv[r ^ 1];
     }
   }
+  // mc is never negative (the host sizes it from the shapes), so this never stores
+  if (mc < 0 && tacc == 0u) o[lane] = from_f<E>(0.f);
   if (final_state) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
