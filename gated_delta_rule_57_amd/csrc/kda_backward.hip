@@ -24,19 +24,22 @@
 //   the forward at 16-token chunks (plan, intra_kernel, inter_kernel) keeping, per
 //     (head, chunk), the state entering the chunk and U~;
 //   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
-//                      e^{g_C} in plain row-major form;
+//                      e^{g_C}, in the fragment order bwd_state_kernel reads;
 //   bwd_state_kernel   one wave per (sequence, head, 16-column slab), serial over the
 //                      chunks in reverse, the 128 x 16 fp32 slab of the state
 //                      gradient in accumulator registers: keeps dS_C and dU~ per chunk,
 //                      writes the initial-state gradient;
 //   bwd_chunk_kernel   one work-group per (chunk, head): everything local to the
 //                      chunk. X1, X2, X3 and dgamma are bf16 (or fp32) MFMA products
-//                      whose operands come straight from row-major global memory; the
-//                      16 x 16 matrices and the decay-weighted sums run on the VALU in
-//                      fp32.
-// In-chunk decays are evaluated per element as 2^(g_r - g_s) with r >= s, so every
-// exponent is <= 0 for any input that meets the log_alpha <= 0 precondition: no
-// factoring or overflow guard is needed at 16 rows.
+//                      whose operands come straight from row-major global memory;
+//                      dT, dB_K, dB_V and the decay-weighted sums over the chunk's rows
+//                      are MFMAs too, on operands built in LDS; 16 x 16 algebra (T,
+//                      dA) and the element-wise terms run on the VALU in fp32.
+// In-chunk decays (log2 units) are factored around a per-channel reference in the
+// middle of the chunk's decay range, so both factors stay within 2^(+-60) while the
+// range is at most 120; a chunk with a wider range in any channel evaluates every
+// term as 2^-|g_r - g_s| instead (exponent <= 0 for any input meeting the
+// log_alpha <= 0 precondition).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -47,7 +50,8 @@ namespace {
 
 constexpr int BC = BWD_CHUNK;
 static_assert(BC == 16, "the backward kernels are written for 16-token chunks");
-constexpr int LDP = D;  // row stride of the fp32 [16][128] LDS matrices (see RowMap)
+constexpr int LDP = D + 4;  // row stride of the fp32 [16][128] LDS matrices: rows 4 apart fall
+                            // 16 banks apart, so accumulator-layout reads are conflict-free
 constexpr int LDS16 = BC + 1;
 constexpr float LOG2E_B = 1.4426950408889634f;
 
@@ -82,9 +86,6 @@ struct BRec {
   static constexpr size_t BYTES = bal256(GAM + D * 4);
 };
 
-// (row, channel) of a 16 x 128 chunk matrix -> element index in the A fragment of its
-// transpose (tile rt = channel / 16: lane (channel % 16) + 16 (row / 4), slot row % 4)
-__device__ __forceinline__ int tfrag_index(int row, int ch) { return ((ch >> 4) * 64 + (row >> 2) * 16 + (ch & 15)) * 4 + (row & 3); }
 // (row, channel) -> element index in the A fragment of the matrix itself (k = channel)
 __device__ __forceinline__ int afrag_index(int row, int ch) {
   const int kb = ch >> 5, ko = ch & 31;
@@ -116,22 +117,48 @@ __device__ __forceinline__ void load8(const E* base, size_t row_stride, int r, i
   }
 }
 
-// The state-independent part shared by both per-chunk kernels: q, k (and v) rows,
-// the log2-unit decay cumsum G, M_rs = sum_i k_ri k_si 2^(G_ri - G_si) for s < r,
-// optionally P_rs = sum_i q_ri k_si 2^(G_ri - G_si) for s <= r, and T = (I + A)^-1
-// with A_rs = beta_r M_rs. Ends with a barrier.
+// The state-independent part shared by both per-chunk kernels: q, k rows, the
+// log2-unit decay cumsum G, the per-channel reference b, M_rs = sum_i k_ri k_si
+// 2^(G_ri - G_si) for s < r, optionally P_rs = sum_i q_ri k_si 2^(G_ri - G_si) for
+// s <= r, and T = (I + A)^-1 with A_rs = beta_r M_rs. Ends with a barrier.
+//
+// Decay factoring: with R = G_0 - G_15 (per channel, >= 0) and b = (G_0 + G_15) / 2,
+// 2^(G_r - G_s) = 2^(G_r - b) 2^(b - G_s) with both factors in [2^(-R/2), 2^(R/2)], so
+// a decay-weighted sum over the chunk's rows is a plain product of factored
+// operands (an MFMA) whose every term, masked ones included, stays finite while
+// R <= FACTOR_MAX_RANGE. A chunk with a wider range in any channel ("exact") takes
+// the element-wise path, 2^-|G_r - G_s| per term.
+constexpr float FACTOR_MAX_RANGE = 120.f;
+
 struct LocalLds {
   float K[BC][LDP], Q[BC][LDP], G[BC][LDP];
   float M[BC][LDS16], T[BC][LDS16], Pm[BC][LDS16];
   float beta[BC];
+  float bref[D];
+  int exact;
 };
+
+// Fragments over the chunk's rows (k < 16; slots 4..7, rows 16..31, are zero):
+// A operand, row m: slot s = f(4 g + s); B operand, column m: slot s = f(4 g + s).
+template <typename E, typename F>
+__device__ __forceinline__ typename Frag<E>::T rows_frag(int g, F f) {
+  typename Frag<E>::T x;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    x[s] = from_f<E>(f(4 * g + s));
+    x[4 + s] = from_f<E>(0.f);
+  }
+  return x;
+}
 
 template <typename E, bool WANT_P>
 __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __restrict__ k,
                               const float* __restrict__ log_alpha, const float* __restrict__ beta, int tok0, int len,
                               int h, int H, int t) {
+  typedef typename Frag<E>::T FragT;
   const size_t HD = (size_t)H * D;
   const RowMap rm(t);
+  const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   {
     const size_t base = (size_t)tok0 * HD + (size_t)h * D;
     float x[8];
@@ -145,18 +172,46 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
 #pragma unroll
     for (int i = 0; i < 8; ++i) L.G[rm.r][rm.c0 + i] = x[i];
     if (t < BC) L.beta[t] = t < len ? beta[(size_t)(tok0 + t) * H + h] : 0.f;
+    if (t == 0) L.exact = 0;
   }
   __syncthreads();
   if (t < D) {  // cumulative log2 decay down the chunk, one channel per thread
-    float run = 0.f;
+    float run = 0.f, g0 = 0.f;
 #pragma unroll
     for (int r = 0; r < BC; ++r) {
       run += L.G[r][t] * LOG2E_B;
       L.G[r][t] = run;
+      if (r == 0) g0 = run;
     }
+    L.bref[t] = 0.5f * (g0 + run);
+    if (g0 - run > FACTOR_MAX_RANGE) L.exact = 1;
   }
   __syncthreads();
-  {
+  if (!L.exact) {
+    if (w == 0) {  // M (and P) as factored products over the 128 channels
+      floatx4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        FragT lk, rk, lq;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int ch = 32 * kb + koff(g, s);
+          const float kv = L.K[m][ch], d = L.G[m][ch] - L.bref[ch];
+          lk[s] = from_f<E>(kv * exp2_hw(d));
+          rk[s] = from_f<E>(kv * exp2_hw(-d));
+          if constexpr (WANT_P) lq[s] = from_f<E>(L.Q[m][ch] * exp2_hw(d));
+        }
+        mma(pk, lk, rk);  // lane (m, g): sum_ch Lk[4g+i][ch] Rk[m][ch]
+        if constexpr (WANT_P) mma(pq, lq, rk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        L.M[r][m] = m < r ? pk[i] : 0.f;
+        if constexpr (WANT_P) L.Pm[r][m] = m <= r ? pq[i] : 0.f;
+      }
+    }
+  } else {
     float kr[8], qr[8], gr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -200,7 +255,9 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
 }
 
 // ---------------------------------------------------------------------------
-// bwd_local_kernel: the backward record of one (chunk, head).
+// bwd_local_kernel: the backward record of one (chunk, head). W = T diag(beta) K e^G
+// is one MFMA per 16-channel tile; its accumulator layout is the fragment order of
+// the record, so W, Q e^G and P leave as one 8-byte store per lane and tile.
 // ---------------------------------------------------------------------------
 template <typename E>
 __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
@@ -210,10 +267,13 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
                                                         const int2* __restrict__ info, int H, int mc,
                                                         char* __restrict__ brec) {
   using BR = BRec<E>;
+  typedef typename Frag<E>::T FragT;
+  typedef typename Vec4<E>::T V4;
   __shared__ LocalLds L;
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
   if (c >= *total_chunks) return;
   const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   const int2 inf = info[c];
   local_forward<E, true>(L, q, k, log_alpha, beta, inf.x, inf.y, h, H, t);
 
@@ -221,20 +281,29 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   E* wt = reinterpret_cast<E*>(rb + BR::WT);
   E* qtt = reinterpret_cast<E*>(rb + BR::QTT);
   E* kef = reinterpret_cast<E*>(rb + BR::KEF);
-  const RowMap rm(t);
+  const FragT ta = rows_frag<E>(g, [&](int u) { return L.T[m][u]; });  // A: row m of T
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ch = rm.ch(i);
-    const float gr = L.G[rm.r][ch];
-    float acc = 0.f;
-    for (int s = 0; s <= rm.r; ++s) acc += L.T[rm.r][s] * L.beta[s] * L.K[s][ch] * exp2_hw(L.G[s][ch]);
-    wt[tfrag_index(rm.r, ch)] = from_f<E>(-acc);
-    qtt[tfrag_index(rm.r, ch)] = from_f<E>(L.Q[rm.r][ch] * exp2_hw(gr));
-    kef[afrag_index(rm.r, ch)] = from_f<E>(L.K[rm.r][ch] * exp2_hw(L.G[BC - 1][ch] - gr));
+  for (int j = 0; j < 2; ++j) {
+    const int nt = 2 * w + j, ch = 16 * nt + m;
+    floatx4 wacc = {0.f, 0.f, 0.f, 0.f};
+    mma(wacc, ta, rows_frag<E>(g, [&](int u) { return L.beta[u] * L.K[u][ch] * exp2_hw(L.G[u][ch]); }));
+    V4 wv, qv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // element i: row 4g+i, channel ch
+      const int r = 4 * g + i;
+      const float gr = L.G[r][ch];
+      wv[i] = from_f<E>(-wacc[i]);
+      qv[i] = from_f<E>(L.Q[r][ch] * exp2_hw(gr));
+      kef[afrag_index(r, ch)] = from_f<E>(L.K[r][ch] * exp2_hw(L.G[BC - 1][ch] - gr));
+    }
+    *reinterpret_cast<V4*>(wt + ((size_t)nt * 64 + lane) * 4) = wv;
+    *reinterpret_cast<V4*>(qtt + ((size_t)nt * 64 + lane) * 4) = qv;
   }
-  {  // P^T fragment: thread t = (row r, column m) of P
-    const int r = t >> 4, mm = t & 15;
-    reinterpret_cast<E*>(rb + BR::PT)[((r >> 2) * 16 + mm) * 4 + (r & 3)] = from_f<E>(L.Pm[r][mm]);
+  if (w == 0) {
+    V4 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = from_f<E>(L.Pm[4 * g + i][m]);
+    *reinterpret_cast<V4*>(reinterpret_cast<E*>(rb + BR::PT) + (size_t)lane * 4) = pv;
   }
   if (t < D) reinterpret_cast<float*>(rb + BR::GAM)[t] = exp2_hw(L.G[BC - 1][t]);
 }
@@ -416,15 +485,21 @@ __global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_chunk_kernel: the gradients of one (chunk, head).
+// bwd_chunk_kernel: the gradients of one (chunk, head). After the state products,
+// wave w owns channels 32 w .. 32 w + 31 (two 16-channel tiles) and works in the
+// MFMA accumulator layout: lane (m, g), element i is row 4 g + i, channel 16 nt + m.
+// dB_K = T^T dW, dB_V = T^T dU and the four decay-weighted sums over the chunk's
+// rows are MFMAs on factored operands (element-wise on the exact path).
 // ---------------------------------------------------------------------------
 struct ChunkLds {
   LocalLds L;
   float V[BC][LDP];
-  float dU[BC][LDP];                   // dU~; later the per-row KE terms of dG
-  float X1[BC][LDP], X2[BC][LDP], X3[BC][LDP];  // X2 is later dG
+  float dU[BC][LDP];  // dU~
+  float X2[BC][LDP];  // dU~ S0^T
   float dP[BC][LDS16], dT[BC][LDS16], dA[BC][LDS16];
+  float dTp[4][BC][LDS16];
   float dgam[D];
+  float dbp[4][BC];
 };
 
 template <typename E>
@@ -473,6 +548,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 
   // ---- state products: wave w forms channel tiles 2w and 2w+1 of
   //      X1 = dO S0^T, X2 = dU~ S0^T, X3 = U~ dS_C^T, and dgamma = rowsum(dS_C o S0)
+  floatx4 x1r[2], x3r[2];
   {
     FragT a1[4], a2[4], a3[4];
 #pragma unroll
@@ -499,12 +575,10 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       dg += __shfl_xor(dg, 16);
       dg += __shfl_xor(dg, 32);
       if (g == 0) S.dgam[16 * nt + m] = dg;
+      x1r[j] = x1;
+      x3r[j] = x3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        S.X1[4 * g + i][16 * nt + m] = x1[i];
-        S.X2[4 * g + i][16 * nt + m] = x2[i];
-        S.X3[4 * g + i][16 * nt + m] = x3[i];
-      }
+      for (int i = 0; i < 4; ++i) S.X2[4 * g + i][16 * nt + m] = x2[i];
     }
     if (w == 0) {  // dP = tril(dO U~^T)
       floatx4 p = {0.f, 0.f, 0.f, 0.f};
@@ -516,25 +590,29 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
   }
   __syncthreads();
 
-  // ---- dT = dW (diag(beta) K e^G)^T + dU (diag(beta) V)^T, dW = -X2 -------------
+  // ---- dT = (dW (K e^G)^T + dU V^T) diag(beta), dW = -X2: wave w sums channels
+  //      32w .. 32w+31 (one MFMA pair), the four partials are added below
   {
-    float x2r[8], dur[8];
+    FragT ax, bk, au, bv;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x2r[i] = S.X2[rm.r][rm.ch(i)];
-      dur[i] = S.dU[rm.r][rm.ch(i)];
+    for (int s = 0; s < 8; ++s) {
+      const int ch = 32 * w + koff(g, s);
+      ax[s] = from_f<E>(-S.X2[m][ch]);
+      bk[s] = from_f<E>(L.K[m][ch] * exp2_hw(L.G[m][ch]));
+      au[s] = from_f<E>(S.dU[m][ch]);
+      bv[s] = from_f<E>(S.V[m][ch]);
     }
+    floatx4 p = {0.f, 0.f, 0.f, 0.f};
+    mma(p, ax, bk);
+    mma(p, au, bv);
 #pragma unroll
-    for (int s = 0; s < BC; ++s) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = rm.ch(i);
-        acc += -x2r[i] * L.K[s][ch] * exp2_hw(L.G[s][ch]) + dur[i] * S.V[s][ch];
-      }
-      acc = sum16(acc) * L.beta[s];
-      if ((t & 15) == 0) S.dT[rm.r][s] = s < rm.r ? acc : 0.f;  // only the strictly lower part of T varies
-    }
+    for (int i = 0; i < 4; ++i) S.dTp[w][4 * g + i][m] = p[i];
+  }
+  __syncthreads();
+  {
+    const int r = t >> 4, s = t & 15;
+    const float a = S.dTp[0][r][s] + S.dTp[1][r][s] + S.dTp[2][r][s] + S.dTp[3][r][s];
+    S.dT[r][s] = s < r ? a * L.beta[s] : 0.f;  // only the strictly lower part of T varies
   }
   __syncthreads();
   // ---- dA = -T^T dT T^T, strictly lower: Y = dT T^T into dA, then -T^T Y into dT --
@@ -556,90 +634,109 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
   }
   __syncthreads();
 
-  // ---- per (row, 8 channels): dv, dbeta, dq, dk and dG --------------------------
-  const int r = rm.r;
-  float dqv[8], dkv[8], dgv[8], kex[8];
-  {
-    const float br = L.beta[r];
-    float dbk[8], dbv[8], kr[8], qr[8], gr[8];
-    float ra[8], rp[8], rat[8], rpt[8];
+  // ---- per element (row 4g+i, channel 16nt+m): dq, dk, dv, dG, dbeta partials ----
+  const bool exact = L.exact != 0;
+  const FragT aTt = rows_frag<E>(g, [&](int u) { return L.T[u][m]; });                   // T^T, row m
+  const FragT adA = rows_frag<E>(g, [&](int u) { return S.dT[m][u]; });                  // dA
+  const FragT adAt = rows_frag<E>(g, [&](int u) { return L.beta[u] * S.dT[u][m]; });     // (diag(beta) dA)^T
+  const FragT adP = rows_frag<E>(g, [&](int u) { return S.dP[m][u]; });                  // dP
+  const FragT adPt = rows_frag<E>(g, [&](int u) { return S.dP[u][m]; });                 // dP^T
+  float dbr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      dbk[i] = dbv[i] = ra[i] = rp[i] = rat[i] = rpt[i] = 0.f;
-      kr[i] = L.K[r][rm.ch(i)];
-      qr[i] = L.Q[r][rm.ch(i)];
-      gr[i] = L.G[r][rm.ch(i)];
-    }
-    // One pass over the chunk's rows s. T is lower (T[s][r] = 0 for s < r), dA
-    // strictly lower and dP lower, so row s < r only feeds the sums along row r
-    // (ra, rp: weights e^{g_r - g_s}) and row s > r only those down column r
-    // (rat, rpt: weights e^{g_s - g_r}); with g non-increasing both weights are
-    // 2^-|g_r - g_s|, and the other side's coefficients are exact zeros.
-#pragma unroll 2
-    for (int s = 0; s < BC; ++s) {
-      const float tsr = L.T[s][r];
-      const float a_rs = S.dT[r][s], p_rs = S.dP[r][s];                  // dA, dP along row r
-      const float a_sr = L.beta[s] * S.dT[s][r], p_sr = S.dP[s][r];      // down column r
+  for (int j = 0; j < 2; ++j) {
+    const int ch = 16 * (2 * w + j) + m;
+    const float bch = L.bref[ch];
+    floatx4 dbk = {0.f, 0.f, 0.f, 0.f}, dbv = dbk, ra = dbk, rp = dbk, rat = dbk, rpt = dbk;
+    mma(dbk, aTt, rows_frag<E>(g, [&](int u) { return S.X2[u][ch]; }));  // T^T X2 = -dB_K
+    mma(dbv, aTt, rows_frag<E>(g, [&](int u) { return S.dU[u][ch]; }));  // T^T dU = dB_V
+    if (!exact) {
+      const FragT brk = rows_frag<E>(g, [&](int u) { return L.K[u][ch] * exp2_hw(bch - L.G[u][ch]); });
+      mma(ra, adA, brk);
+      mma(rp, adP, brk);
+      mma(rat, adAt, rows_frag<E>(g, [&](int u) { return L.K[u][ch] * exp2_hw(L.G[u][ch] - bch); }));
+      mma(rpt, adPt, rows_frag<E>(g, [&](int u) { return L.Q[u][ch] * exp2_hw(L.G[u][ch] - bch); }));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = rm.ch(i);
-        dbk[i] -= tsr * S.X2[s][ch];  // dB_K = T^T dW
-        dbv[i] += tsr * S.dU[s][ch];  // dB_V = T^T dU
-        const float ks = L.K[s][ch], qs = L.Q[s][ch];
-        const float f = exp2_hw(-fabsf(gr[i] - L.G[s][ch]));
-        ra[i] += a_rs * ks * f;
-        rp[i] += p_rs * ks * f;
-        rat[i] += a_sr * ks * f;
-        rpt[i] += p_sr * qs * f;
+      for (int i = 0; i < 4; ++i) {
+        const float d = L.G[4 * g + i][ch] - bch;
+        const float lr = exp2_hw(d), rr = exp2_hw(-d);
+        ra[i] *= lr;
+        rp[i] *= lr;
+        rat[i] *= rr;
+        rpt[i] *= rr;
+      }
+    } else {
+      // T, dA strictly lower and dP lower: row u < r only feeds the sums along row r,
+      // row u > r only those down column r, both weighted 2^-|G_r - G_u|
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const float gr = L.G[r][ch];
+        for (int u = 0; u < BC; ++u) {
+          const float f = exp2_hw(-fabsf(gr - L.G[u][ch]));
+          const float ku = L.K[u][ch] * f;
+          ra[i] += S.dT[r][u] * ku;
+          rp[i] += S.dP[r][u] * ku;
+          rat[i] += L.beta[u] * S.dT[u][r] * ku;
+          rpt[i] += S.dP[u][r] * L.Q[u][ch] * f;
+        }
       }
     }
-    float dbeta_part = 0.f, dvv[8];
+    const float gl = L.G[BC - 1][ch];
+    float dgr[4], kexs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ch = rm.ch(i);
-      const float eg = exp2_hw(gr[i]);
-      const float el = exp2_hw(L.G[BC - 1][ch] - gr[i]);
-      dbeta_part += dbk[i] * kr[i] * eg + dbv[i] * S.V[r][ch];
-      dvv[i] = br * dbv[i];
-      const float x1 = S.X1[r][ch], x3 = S.X3[r][ch];
-      dqv[i] = x1 * eg + rp[i];
-      dkv[i] = br * dbk[i] * eg + br * ra[i] + rat[i] + rpt[i] + x3 * el;
-      kex[i] = x3 * kr[i] * el;
-      dgv[i] = x1 * qr[i] * eg + rp[i] * qr[i] + br * dbk[i] * kr[i] * eg + br * ra[i] * kr[i] - rat[i] * kr[i] -
-               rpt[i] * kr[i] - kex[i];
-    }
-    dbeta_part = sum16(dbeta_part);
-    if ((t & 15) == 0 && r < len) {
-      float am = 0.f;
-      for (int s = 0; s < r; ++s) am += S.dT[r][s] * L.M[r][s];
-      dbeta[(size_t)(tok0 + r) * H + h] = dbeta_part + am;
-    }
-    if (r < len) {
-      const size_t ro = rowbase + (size_t)r * HD;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dv[ro + rm.ch(i)] = from_f<E>(dvv[i]);
-        dq[ro + rm.ch(i)] = from_f<E>(dqv[i]);
-        dk[ro + rm.ch(i)] = from_f<E>(dkv[i]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      const float gr = L.G[r][ch], er = exp2_hw(gr), el = exp2_hw(gl - gr);
+      const float kr = L.K[r][ch], qr = L.Q[r][ch], br = L.beta[r];
+      const float bk_ = -dbk[i], bv_ = dbv[i], x1 = x1r[j][i], x3 = x3r[j][i];
+      const float dqv = x1 * er + rp[i];
+      const float dkv = br * bk_ * er + br * ra[i] + rat[i] + rpt[i] + x3 * el;
+      const float kex = x3 * kr * el;
+      dgr[i] = x1 * qr * er + rp[i] * qr + br * bk_ * kr * er + br * ra[i] * kr - rat[i] * kr - rpt[i] * kr - kex;
+      dbr[i] += bk_ * kr * er + bv_ * S.V[r][ch];
+      kexs += kex;
+      if (r < len) {
+        const size_t o = rowbase + (size_t)r * HD + ch;
+        dq[o] = from_f<E>(dqv);
+        dk[o] = from_f<E>(dkv);
+        dv[o] = from_f<E>(br * bv_);
       }
+    }
+    // dlog_alpha = reverse cumulative sum of dG over the rows (4 per lane, lanes
+    // m + 16 g in order), plus the terms of g_C (the last row): sum_r K e^{g_C-G}
+    // terms and dgamma e^{g_C}, which every row's sum includes
+    const float blk = dgr[0] + dgr[1] + dgr[2] + dgr[3];
+    kexs += __shfl_xor(kexs, 16);
+    kexs += __shfl_xor(kexs, 32);
+    float above = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const float b = __shfl(blk, m + 16 * gg);
+      if (gg > g) above += b;
+    }
+    float run = above + kexs + S.dgam[ch] * exp2_hw(gl);
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      run += dgr[i];
+      const int r = 4 * g + i;
+      if (r < len) dlog_alpha[rowbase + (size_t)r * HD + ch] = run;
     }
   }
-  __syncthreads();  // every read of X2 and dU is done
+  // dbeta = sum over channels of (dB_K o K e^G + dB_V o V) + sum_s dA_rs M_rs
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    S.X2[r][rm.ch(i)] = dgv[i];
-    S.dU[r][rm.ch(i)] = kex[i];
+  for (int i = 0; i < 4; ++i) {
+    float x = dbr[i];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    if (m == 0) S.dbp[w][4 * g + i] = x;
   }
   __syncthreads();
-  if (t < D) {  // g_C = G at the last row: its gradient gathers the K e^{g_C-G} and e^{g_C} terms
-    float extra = S.dgam[t] * exp2_hw(L.G[BC - 1][t]);
-#pragma unroll
-    for (int rr = 0; rr < BC; ++rr) extra += S.dU[rr][t];
-    float run = extra;
-    for (int rr = BC - 1; rr >= 0; --rr) {
-      run += S.X2[rr][t];
-      if (rr < len) dlog_alpha[rowbase + (size_t)rr * HD + t] = run;
-    }
+  if (t < len) {
+    float am = 0.f;
+    for (int s = 0; s < t; ++s) am += S.dT[t][s] * L.M[t][s];
+    dbeta[(size_t)(tok0 + t) * H + h] = S.dbp[0][t] + S.dbp[1][t] + S.dbp[2][t] + S.dbp[3][t] + am;
   }
 }
 

@@ -78,6 +78,14 @@ def test_strong_decay_exact_per_element():
     run_case(small(25, T=64, H=2, dtype="fp32", la_scale=4.0), label="strong-decay")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decay_range_beyond_the_factoring_limit(dtype):
+    """log alpha = -12 softplus(N(0,1)): chunks whose in-chunk decay range exceeds
+    120 log2 units in some channel take the element-wise path, the others the
+    factored MFMA path; both must hold the tolerance."""
+    run_case(small(29, T=80, H=2, dtype=dtype, la_scale=12.0), label=f"exact-path-{dtype}")
+
+
 def test_no_decay_is_deltanet():
     """log alpha = 0: the gradients of DeltaNet."""
     inp = small(26, T=50, H=2, dtype="fp32")
