@@ -38,6 +38,20 @@ RECORD_BYTES_BF16_C64 = 74240
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
+# backward (16-token chunks, bf16): per (chunk, head) the forward record (22016 B), the
+# backward record (13312 B), the chunk-entry state and the chunk-end state gradient
+# (2 x 32768 B) and U~, dU~ (2 x 4096 B); per (token, head) algorithmic bytes of each kernel
+BWD_CHUNK = 16
+BWD_BYTES_PER_TOK_HEAD = {
+    "intra": 3 * 2 * D + 4 * D + 4 + 22016 // BWD_CHUNK,                    # inputs in, record out
+    "inter": 22016 // BWD_CHUNK + (32768 + 4096) // BWD_CHUNK,              # record in, states and U~ out
+    "bwd_local": 2 * 2 * D + 4 * D + 4 + 13312 // BWD_CHUNK,                # q, k, gate in, record out
+    "bwd_state": 13312 // BWD_CHUNK + 2 * D + (32768 + 4096) // BWD_CHUNK,  # record, grad_o in, dS_C, dU~ out
+    "bwd_chunk": 4 * 2 * D + 4 * D + 4 + 2 * (32768 + 4096) // BWD_CHUNK + 3 * 2 * D + 4 * D + 4,
+}
+# bytes any backward must move per (token, head): q, k, v, grad_o, log_alpha, beta in; the five gradients out
+BWD_PATH_BYTES_PER_TOK_HEAD = 4 * 2 * D + 4 * D + 4 + 3 * 2 * D + 4 * D + 4
+
 PREFILL_T, PREFILL_H = 131072, 32
 DEC_N, DEC_H = 256, 32
 
@@ -125,6 +139,46 @@ def fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec, ru
             "decode_GBps": round(dec_bytes / (ms["decode"] * 1e-3) / 1e9, 1)}
 
 
+def backward_timing(inputs, kda, torch, pre, runs=3):
+    """The backward (kda_chunk_bwd) on the headline prefill shape: gradients of q, k,
+    v, log_alpha, beta and the initial state for a random output cotangent and a
+    final-state cotangent, timed by the library's events."""
+    B, T, H = pre.q.shape[:3]
+    grad_o, gfin = inputs.make_cotangents(3, pre)
+    ws = torch.empty(kda.bwd_workspace_size(B, T, H, dtype=kda.KDA_BF16), dtype=torch.uint8, device=pre.q.device)
+
+    def run():
+        return kda.chunk_bwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, grad_o, initial_state=pre.initial_state,
+                             grad_final_state=gfin, workspace=ws)
+
+    g = run()
+    torch.cuda.synchronize()
+    kda.timing_enable(True)
+    for _ in range(runs):
+        g = run()
+    torch.cuda.synchronize()
+    t = kda.timing_read()
+    kda.timing_enable(False)
+    ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items() if cnt}
+    names = ("plan", "intra", "inter", "bwd_local", "bwd_state", "bwd_chunk")
+    total = sum(ms.get(n, 0.0) for n in names)
+    tok_heads = T * H
+    gbps = {n: round(BWD_BYTES_PER_TOK_HEAD[n] * tok_heads / (ms[n] * 1e-3) / 1e9, 1)
+            for n in names if n in BWD_BYTES_PER_TOK_HEAD}
+    finite = all(bool(torch.isfinite(x).all()) for x in g.values() if x is not None)
+    del g, ws, grad_o
+    torch.cuda.empty_cache()
+    print(f"[bench] backward {total:.3f} ms", file=sys.stderr, flush=True)
+    return {"workload": "kda_backward_T131072_H32_bf16 (gradients of q, k, v, log_alpha, beta and the initial "
+                        "state; 16-token chunks)",
+            "ms": round(total, 4), "tokens_per_s": round(T / (total * 1e-3), 1),
+            "kernel_ms": {n: round(ms.get(n, 0.0), 4) for n in names},
+            "kernel_GBps_algorithmic": gbps,
+            "path_hbm_frac_ideal": round(BWD_PATH_BYTES_PER_TOK_HEAD * tok_heads / (total * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+            "finite": finite}
+
+
 def gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec, runs=5):
     """The scalar-gate (one decay per token and head) and no-decay paths on the
     headline prefill shape and the decode batch, timed by the library's events."""
@@ -173,6 +227,8 @@ def main():
                     help="skip the timing of the scalar-gate (Gated DeltaNet) and no-decay (DeltaNet) paths")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the timing of the fused layer core (prologue and epilogue in the kernels)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward (kda_chunk_bwd) on the prefill shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of 1 GiB (for counter calibration) and exit")
     args = ap.parse_args()
@@ -304,6 +360,8 @@ def main():
         result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec)
     if not args.no_gates:
         result["gates"] = gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec)
+    if not args.no_backward:
+        result["backward"] = backward_timing(inputs, kda, torch, pre)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)

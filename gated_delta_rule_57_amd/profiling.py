@@ -10,8 +10,10 @@
         and bench_WRITE_SIZE.
 
 Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode,
-outnorm); the intra-chunk kernel's scalar-gate and no-decay instantiations become
-intra_gdn and intra_deltanet.
+outnorm, bwd_local, bwd_state, bwd_chunk); the intra-chunk kernel's scalar-gate and
+no-decay instantiations become intra_gdn and intra_deltanet, its 16-token-chunk
+instantiation (the backward's forward pass) intra16, and the 16-token state
+kernel inter16.
 The traffic summary records a hash of the kernel sources it was taken on; bench.py
 reports the traffic only while that hash matches the sources.
 """
@@ -24,8 +26,9 @@ import re
 import sys
 
 KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
-           ("inter_kernel", "inter"), ("decode_kernel", "decode"),
-           ("output_norm_gate_kernel", "outnorm"))
+           ("inter16_kernel", "inter16"), ("inter_kernel", "inter"), ("decode_kernel", "decode"),
+           ("output_norm_gate_kernel", "outnorm"), ("bwd_local_kernel", "bwd_local"),
+           ("bwd_state_kernel", "bwd_state"), ("bwd_chunk_kernel", "bwd_chunk"))
 COPY_BYTES = 1 << 30
 
 
@@ -42,9 +45,9 @@ def kernel_source_hash(root=None):
     return h.hexdigest()[:16]
 
 
-# the gate template argument of intra_kernel, in mangled (..Li64ELi1EE..) or
-# demangled (<.., 64, 1>) names
-_GATE_ARG = re.compile(r"intra_kernel(?:I\w*?Li\d+ELi(\d)E|<[^>]*,\s*(\d)>)")
+# the chunk and gate template arguments of intra_kernel, in mangled (..Li64ELi1EE..)
+# or demangled (<.., 64, 1>) names
+_GATE_ARG = re.compile(r"intra_kernel(?:I\w*?Li(\d+)ELi(\d)E|<[^>]*,\s*(\d+),\s*(\d)>)")
 
 
 def short_name(name):
@@ -52,8 +55,10 @@ def short_name(name):
         if key in name:
             if short == "intra":
                 m = _GATE_ARG.search(name)
-                gate = m.group(1) or m.group(2) if m else None
-                return {"1": "intra_gdn", "2": "intra_deltanet"}.get(gate, "intra")
+                chunk = (m.group(1) or m.group(3)) if m else None
+                gate = (m.group(2) or m.group(4)) if m else None
+                base = {"1": "intra_gdn", "2": "intra_deltanet"}.get(gate, "intra")
+                return base + "16" if chunk == "16" else base
             return short
     return None
 

@@ -10,13 +10,20 @@ def test_short_names_split_intra_by_gate():
     s = profiling.short_name
     assert s("_ZN3kda12intra_kernelIDF16bLi64ELi0EEEvPKT_S3_") == "intra"
     assert s("_ZN3kda12intra_kernelIDF16bLi64ELi1EEEvPKT_S3_") == "intra_gdn"
-    assert s("_ZN3kda12intra_kernelIfLi16ELi2EEEvPKT_S3_") == "intra_deltanet"
+    assert s("_ZN3kda12intra_kernelIfLi64ELi2EEEvPKT_S3_") == "intra_deltanet"
+    assert s("_ZN3kda12intra_kernelIfLi16ELi2EEEvPKT_S3_") == "intra_deltanet16"
     assert s("void kda::intra_kernel<__bf16, 64, 1>(__bf16 const*)") == "intra_gdn"
     assert s("void kda::inter_wg_kernel<1>(char const*, int const*)") == "inter"
     assert s("_ZN3kda13decode_kernelIDF16bEEvPKT_") == "decode"
     assert s("_ZN3kda23output_norm_gate_kernelIDF16bEEvPKT_") == "outnorm"
     assert s("kda::plan_kernel(int const*, int)") == "plan"
     assert s("__amd_rocclr_copyBuffer") is None
+    assert s("_ZN3kda12intra_kernelIDF16bLi16ELi0EEEvPKT_S3_") == "intra16"
+    assert s("void kda::intra_kernel<__bf16, 16, 0>(__bf16 const*)") == "intra16"
+    assert s("void kda::inter16_kernel<__bf16>(char const*, int const*)") == "inter16"
+    assert s("_ZN3kda12_GLOBAL__N_116bwd_chunk_kernelIDF16bEEvPKT_") == "bwd_chunk"
+    assert s("_ZN3kda12_GLOBAL__N_116bwd_state_kernelIDF16bEEvPKc") == "bwd_state"
+    assert s("_ZN3kda12_GLOBAL__N_116bwd_local_kernelIDF16bEEvPKT_") == "bwd_local"
 
 
 def _write_counters(path, rows):
@@ -44,3 +51,17 @@ def test_traffic_scaling(tmp_path):
     assert d["kernels"]["plan"]["fetch_size_bytes_scaled"] == 20.0 * 1024 * 2
     assert d["kernels"]["plan"]["write_size_bytes_scaled"] == 4.0 * 1024
     assert d["kernels"]["plan"]["hbm_bytes_per_launch"] == 20.0 * 1024 * 2 + 4.0 * 1024
+
+
+def test_bench_backward_byte_counts_match_the_workspace_layout():
+    """The per-(chunk, head) sizes behind bench.py's backward byte counts (forward
+    record 22016 B; backward record, two 128 x 128 bf16 matrices and two 16 x 128
+    ones 87040 B) agree with the library's workspace queries."""
+    import bench
+    from gated_delta_rule_57_amd import kda
+    T, H = 4096, 16
+    mc = T // bench.BWD_CHUNK
+    fwd = kda.workspace_size(1, T, H, chunk=16)
+    bwd = kda.bwd_workspace_size(1, T, H)
+    assert abs(fwd / (mc * H) - 22016) < 1
+    assert (bwd - fwd) == mc * H * (13312 + 2 * 32768 + 2 * 4096)
