@@ -25,10 +25,10 @@
 //     (head, chunk), the state entering the chunk and U~;
 //   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
 //                      e^{g_C}, in the fragment order bwd_state_kernel reads;
-//   bwd_state_kernel   one wave per (sequence, head, 16-column slab), serial over the
-//                      chunks in reverse, the 128 x 16 fp32 slab of the state
-//                      gradient in accumulator registers: keeps dS_C and dU~ per chunk,
-//                      writes the initial-state gradient;
+//   bwd_state_kernel   four waves per (sequence, head, 16-column slab), serial over
+//                      the chunks in reverse, the 128 x 16 fp32 slab of the state
+//                      gradient in accumulator registers (32 rows per wave): keeps
+//                      dS_C and dU~ per chunk, writes the initial-state gradient;
 //   bwd_chunk_kernel   one work-group per (chunk, head): everything local to the
 //                      chunk. X1, X2, X3 and dgamma are bf16 (or fp32) MFMA products
 //                      whose operands come straight from row-major global memory;
@@ -309,48 +309,52 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// bwd_state_kernel: one wave per (sequence, head, 16-column slab), chunks in
-// reverse. Lane (m, g) keeps dS[16 rt + 4 g + i][16 ct + m] in Lm[rt][i], the layout
-// of the forward state kernel, so Lm pairs are B fragments as they stand. Work-group
-// ids are dealt so that the eight slabs of a head share one XCD's L2.
+// bwd_state_kernel: four waves per (sequence, head, 16-column slab), chunks in
+// reverse. Wave w keeps dS rows 32w + 16j + 4g + i (j = 0, 1), column 16ct + m, in
+// Lm[j], the layout whose pair is a B fragment over its 32 rows. Per chunk, wave w
+// forms its k-block's part of dU~ = P^T dO + (K e^{g_C-G}) dS (P^T dO once, in wave
+// 0), the parts are summed through LDS behind one barrier that leaves global loads
+// in flight, and each wave updates its own rows. Work-group ids are dealt so that
+// the eight slabs of a head share one XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int STATE_TOUCH_AHEAD = 4;
 
 template <typename E>
-__global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ brec,
-                                                       const int32_t* __restrict__ chunk_off,
-                                                       const int2* __restrict__ info, const E* __restrict__ dout,
-                                                       const float* __restrict__ d_final, float* __restrict__ d_initial,
-                                                       E* __restrict__ dstates, E* __restrict__ dut, int N, int H,
-                                                       int mc) {
+__global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__ brec,
+                                                        const int32_t* __restrict__ chunk_off,
+                                                        const int2* __restrict__ info, const E* __restrict__ dout,
+                                                        const float* __restrict__ d_final,
+                                                        float* __restrict__ d_initial, E* __restrict__ dstates,
+                                                        E* __restrict__ dut, int N, int H, int mc) {
   using BR = BRec<E>;
   typedef typename Frag<E>::T FragT;
   typedef typename Vec4<E>::T V4;
-  // four elements kept as raw 32-bit words in the register stage (packed bf16
-  // vectors in a struct array otherwise end up in scratch)
+  // four elements kept as raw 32-bit words while loading (packed bf16 vectors in a
+  // struct otherwise end up in scratch)
   typedef unsigned int RawV __attribute__((ext_vector_type(sizeof(V4) / 4)));
   constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
   constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
-  __shared__ __attribute__((aligned(16))) E xs[D * XW];
-  __shared__ __attribute__((aligned(16))) float xg[D];
+  __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
+  __shared__ floatx4 xp[2][4][64];                           // dU~ parts, by chunk parity
 
   const int b = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int xcd = b & 7, rest = b >> 3;
   const int ct = rest & 7, slot = rest >> 3;
   const int u = slot * 8 + xcd;
-  if (u >= N * H) return;
+  if (u >= N * H) return;  // uniform over the work-group
   const int n = u / H, h = u - n * H;
-  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
   const size_t HD = (size_t)H * D;
-  const size_t sbase = (size_t)u * D * D + 16 * ct + m;
+  const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
 
-  floatx4 Lm[8];
+  floatx4 Lm[2];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) {
-    Lm[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; ++j) {
+    Lm[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (d_final) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Lm[rt][i] = d_final[sbase + (size_t)(16 * rt + 4 * g + i) * D];
+      for (int i = 0; i < 4; ++i) Lm[j][i] = d_final[sbase + (size_t)(16 * j + i) * D];
     }
   }
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -366,13 +370,21 @@ __global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ 
     return f;
   };
 
-  // operands are kept as whole fragments (chunk rows 16..31 zero): a stage of
-  // half-width vectors gets merged into wide loads that keep it out of registers
+  // a stage holds what the loads return (four elements as raw 32-bit words, grad_o
+  // as four scalars): building fragments at load time would make the wave wait for
+  // the data one step early; they are built where they are used
+  constexpr int RW = (int)(sizeof(V4) / 4);
   struct Stage {
-    FragT wt[8], qt[8], pt, dov;
-    FragT ke[4];
-    floatx4 gm;
-    int2 inf;
+    unsigned wt[2][RW], qt[2][RW], pt[RW];
+    E dov[4];
+    FragT ke;
+    floatx4 gm[2];
+  };
+  auto raw_frag = [&](const unsigned* r) {
+    RawV x;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) x[i] = r[i];
+    return half_frag(x);
   };
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   auto load = [&](Stage& st, int c) {
@@ -380,107 +392,128 @@ __global__ void __launch_bounds__(64) bwd_state_kernel(const char* __restrict__ 
     const E* wt = reinterpret_cast<const E*>(rb + BR::WT);
     const E* qt = reinterpret_cast<const E*>(rb + BR::QTT);
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      st.wt[rt] = half_frag(*reinterpret_cast<const RawV*>(wt + ((size_t)rt * 64 + lane) * 4));
-      st.qt[rt] = half_frag(*reinterpret_cast<const RawV*>(qt + ((size_t)rt * 64 + lane) * 4));
-    }
+    for (int j = 0; j < 2; ++j) {
+      const RawV a = *reinterpret_cast<const RawV*>(wt + ((size_t)(2 * w + j) * 64 + lane) * 4);
+      const RawV q = *reinterpret_cast<const RawV*>(qt + ((size_t)(2 * w + j) * 64 + lane) * 4);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      st.ke[kb] = load_frag<E>(reinterpret_cast<const E*>(rb + BR::KEF) + ((size_t)kb * 64 + lane) * 8);
-    st.pt = half_frag(*reinterpret_cast<const RawV*>(reinterpret_cast<const E*>(rb + BR::PT) + (size_t)lane * 4));
-    st.gm = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(rb + BR::GAM) + 4 * (lane & 31));
+      for (int i = 0; i < RW; ++i) {
+        st.wt[j][i] = a[i];
+        st.qt[j][i] = q[i];
+      }
+    }
+    st.ke = load_frag<E>(reinterpret_cast<const E*>(rb + BR::KEF) + ((size_t)w * 64 + lane) * 8);
+    {
+      const RawV p4 = *reinterpret_cast<const RawV*>(reinterpret_cast<const E*>(rb + BR::PT) + (size_t)lane * 4);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) st.pt[i] = p4[i];
+    }
+    const float* gam = reinterpret_cast<const float*>(rb + BR::GAM);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
     const int2 inf = info[c];
-    st.inf = inf;
-    V4 d;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int row = 4 * g + s;
-      d[s] = row < inf.y ? dout[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] : from_f<E>(0.f);
+      st.dov[s] = row < inf.y ? dout[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] : from_f<E>(0.f);
     }
-    st.dov = half_frag(__builtin_bit_cast(RawV, d));
   };
 
-  auto compute = [&](const Stage& st, int c) {
-    {  // the gradient at the chunk's end, for the per-chunk kernel, as 16-byte row pieces
+  auto compute = [&](const Stage& st, int c, int buf) {
+    E* xw = xs[w];
+    {  // this wave's 32 rows of the gradient at the chunk's end, as 16-byte row pieces
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[(16 * rt + 4 * g + i) * XW + m] = from_f<E>(Lm[rt][i]);
-      __syncthreads();
-      E* dp = dstates + ((size_t)h * mc + c) * D * D + 16 * ct;
+        for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(Lm[j][i]);
+      compiler_fence();
+      E* dp = dstates + ((size_t)h * mc + c) * D * D + (size_t)(32 * w) * D + 16 * ct;
 #pragma unroll
-      for (int j = 0; j < 2 * (int)sizeof(E); ++j) {
-        const int piece = lane + 64 * j, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(dp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      for (int p = 0; p < (int)sizeof(E) / 2; ++p) {
+        const int piece = lane + 64 * p, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(dp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
       }
-      __syncthreads();
+      compiler_fence();
     }
-    const FragT dOb = st.dov;  // B fragment of dO over the chunk rows
-    // dU~ = P^T dO + (K e^{g_C-G}) dS_C
-    floatx4 du = zero4;
-    mma(du, st.pt, dOb);
+    FragT dOb;  // B fragment of dO over the chunk rows
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma(du, st.ke[kb], acc_pair_to_frag<E>(Lm[2 * kb], Lm[2 * kb + 1]));
-    {
+    for (int s = 0; s < 4; ++s) {
+      dOb[s] = st.dov[s];
+      dOb[4 + s] = from_f<E>(0.f);
+    }
+    // this wave's part of dU~ = P^T dO + (K e^{g_C-G}) dS
+    floatx4 dp4 = zero4;
+    if (w == 0) mma(dp4, raw_frag(st.pt), dOb);
+    mma(dp4, st.ke, acc_pair_to_frag<E>(Lm[0], Lm[1]));
+    xp[buf][w][lane] = dp4;
+    lds_barrier();
+    const floatx4 du = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
+    if (w == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[(4 * g + i) * XW + m] = from_f<E>(du[i]);
-      if (lane < 32) *reinterpret_cast<floatx4*>(&xg[4 * lane]) = st.gm;
-      __syncthreads();
+      for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(du[i]);
+      compiler_fence();
       if (lane < 16 * (16 / VE)) {
         const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
         *reinterpret_cast<uint4*>(dut + ((size_t)h * mc + c) * BC * D + (size_t)row * D + 16 * ct + col) =
-            *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+            *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
       }
+      compiler_fence();
     }
     const FragT dUb = acc_pair_to_frag<E>(du, zero4);
-    // dS0 = e^{g_C} o dS_C + (Q e^G)^T dO + (-W)^T dU~
+    // dS0_w = e^{g_C} o dS_w + (Q e^G)^T_w dO + (-W)^T_w dU~
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      const floatx4 gv = *reinterpret_cast<const floatx4*>(&xg[16 * rt + 4 * g]);
-      Lm[rt] = gv * Lm[rt];
-      mma(Lm[rt], st.qt[rt], dOb);
-      mma(Lm[rt], st.wt[rt], dUb);
+    for (int j = 0; j < 2; ++j) {
+      Lm[j] = st.gm[j] * Lm[j];
+      mma(Lm[j], raw_frag(st.qt[j]), dOb);
+      mma(Lm[j], raw_frag(st.wt[j]), dUb);
     }
-    __syncthreads();
   };
 
-  // L2 touch STATE_TOUCH_AHEAD chunks beyond the register stage: the head's eight
-  // slab waves each read one word of every eighth record line, so the real loads
-  // hit in L2 (the words are XOR-folded into tacc, stored only by a never-taken
-  // branch). No address here depends on a load: that would make the wave wait.
+  // L2 touch STATE_TOUCH_AHEAD chunks beyond the register stage: each record line is
+  // read (one word) by one of the head's 32 waves, so the real loads hit in L2 (the
+  // words are XOR-folded into tacc, stored only by a never-taken branch). No address
+  // here depends on a load: that would make the wave wait.
   constexpr int LINES = (int)(BR::BYTES / 128);
-  static_assert(BR::BYTES % 128 == 0 && LINES <= 8 * 64, "one touch per lane");
-  const int touch_line = ct + 8 * lane;
+  static_assert(BR::BYTES % 128 == 0 && LINES <= 32 * 64, "one touch per lane");
+  // lanes past the record's last line touch that line again (an unconditional load
+  // is never merged with an old value)
+  const int touch_line = min((ct * 4 + w) + 32 * lane, LINES - 1);
   unsigned tacc = 0u;
   auto touch = [&](int c) {
-    unsigned x = 0u;
-    if (touch_line < LINES)
-      x = *reinterpret_cast<const unsigned*>(brec + ((size_t)h * mc + c) * BR::BYTES + (size_t)touch_line * 128);
-    return x;
+    return *reinterpret_cast<const unsigned*>(brec + ((size_t)h * mc + c) * BR::BYTES + (size_t)touch_line * 128);
   };
 
   // two named stages: each step loads chunk c - 1 into the stage consumed one step
-  // earlier (past the start, the first chunk again: every step issues the same loads)
+  // earlier (past the start, the first chunk again: every step issues the same
+  // loads). Four touch words in flight: step r folds in the word it loaded four steps
+  // earlier before loading the next one into the same variable, so no register copy
+  // has to wait for a load.
   Stage sa, sb;
-  unsigned ta = 0u, tb = 0u;
   if (c_begin < c_end) load(sa, c_end - 1);
-  for (int c0 = c_end - 1; c0 >= c_begin; c0 -= 2) {
+  for (int c0 = c_end - 1; c0 >= c_begin; c0 -= 4) {
+    // the iteration's four chunks: the first step touches the four beyond the touch
+    // distance; the words are folded in after the last step (none lives across the
+    // back edge, where a register copy would wait for it)
     load(sb, max(c0 - 1, c_begin));
-    ta = touch(max(c0 - 1 - STATE_TOUCH_AHEAD, c_begin));
-    compute(sa, c0);
-    tacc ^= tb;
+    const unsigned t0 = touch(max(c0 - 1 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t1 = touch(max(c0 - 2 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t2 = touch(max(c0 - 3 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t3 = touch(max(c0 - 4 - STATE_TOUCH_AHEAD, c_begin));
+    compute(sa, c0, 0);
     load(sa, max(c0 - 2, c_begin));
-    tb = touch(max(c0 - 2 - STATE_TOUCH_AHEAD, c_begin));
-    if (c0 - 1 >= c_begin) compute(sb, c0 - 1);
-    tacc ^= ta;
+    if (c0 - 1 >= c_begin) compute(sb, c0 - 1, 1);
+    load(sb, max(c0 - 3, c_begin));
+    if (c0 - 2 >= c_begin) compute(sa, c0 - 2, 0);
+    load(sa, max(c0 - 4, c_begin));
+    if (c0 - 3 >= c_begin) compute(sb, c0 - 3, 1);
+    tacc ^= t0 ^ t1 ^ t2 ^ t3;
   }
   // mc is never negative (the host sizes it from the shapes), so this never stores
   if (mc < 0 && tacc == 0u) dut[lane] = from_f<E>(0.f);
   if (d_initial) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d_initial[sbase + (size_t)(16 * rt + 4 * g + i) * D] = Lm[rt][i];
+      for (int i = 0; i < 4; ++i) d_initial[sbase + (size_t)(16 * j + i) * D] = Lm[j][i];
   }
 }
 
@@ -792,7 +825,7 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   }
   const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
-    hipLaunchKernelGGL(bwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, brec, chunk_off,
+    hipLaunchKernelGGL(bwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, brec, chunk_off,
                        info, (const E*)dout, d_final, d_initial, dstates, dut, N, H, (int)mc);
     e = hipGetLastError();
     trace_mark(stream, 6);

@@ -120,4 +120,16 @@ __device__ __forceinline__ typename Frag<E>::T load_frag(const E* p) {
   return *reinterpret_cast<const typename Frag<E>::T*>(p);
 }
 
+// Ordering helpers for LDS exchanges between the waves of a work-group.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// s_waitcnt with lgkmcnt(0) and the vector-memory counter left free
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// work-group barrier for LDS exchanges that leaves in-flight global loads alone
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
 }  // namespace kda

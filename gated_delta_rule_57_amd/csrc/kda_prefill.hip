@@ -28,10 +28,10 @@
 //                 accumulator registers: U~, O and the state update chain from one
 //                 MFMA to the next without leaving registers. The value columns of
 //                 S evolve independently, which is what makes the slab split exact.
-//                 inter_wg_kernel (bf16, 64-token chunks) spreads a slab over four
-//                 waves and has each record line pulled into L2 by one wave of the
-//                 head a few chunks ahead; inter_kernel (fp32 or 16-token chunks)
-//                 uses one wave.
+//                 inter_wg_kernel (bf16, 64-token chunks) and inter16_kernel
+//                 (16-token chunks) spread a slab over four waves and have each
+//                 record line pulled into L2 by one wave of the head a few chunks
+//                 ahead; inter_kernel (fp32, 64-token chunks) uses one wave.
 //
 // In-chunk decay (the pages note that fine-grained decay makes the in-chunk
 // division numerically delicate): everything is done in log2 units, and the
@@ -924,111 +924,122 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk kernel for 16-token chunks: one wave per (sequence, head, 16-column
-// slab), laid out like inter_kernel, with the next chunk's record fragments loaded
-// into registers while the current chunk is computed (a 16-token chunk is only a
-// few MFMAs deep, so without the lookahead every chunk waits out a memory round
-// trip). The per-chunk outputs of the backward pass (states, U~) are transposed
-// through LDS and written as whole 16-byte row pieces.
+// Inter-chunk kernel for 16-token chunks: four waves per (sequence, head, 16-column
+// slab), wave w keeping state rows 32w .. 32w+31. Per chunk, wave w forms its
+// k-block's part of U~ = U - W S (and of (Q e^G) S), the four parts are summed
+// through LDS behind one barrier that leaves global loads in flight, and each wave
+// updates its own rows. The next chunk's fragments are loaded into registers while
+// the current one is computed, and each record line is touched in L2 a few chunks
+// ahead by one wave of the head. The per-chunk outputs of the backward pass (states,
+// U~) are transposed through LDS and written as 16-byte row pieces.
 // ---------------------------------------------------------------------------
 constexpr int INTER16_TOUCH_AHEAD = 4;
 
 template <typename E>
-__global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ records,
-                                                     const int32_t* __restrict__ chunk_off,
-                                                     const int2* __restrict__ info,
-                                                     const float* __restrict__ initial_state,
-                                                     float* __restrict__ final_state, E* __restrict__ o, int N, int H,
-                                                     int mc, E* __restrict__ states, E* __restrict__ ut) {
+__global__ void __launch_bounds__(256) inter16_kernel(const char* __restrict__ records,
+                                                      const int32_t* __restrict__ chunk_off,
+                                                      const int2* __restrict__ info,
+                                                      const float* __restrict__ initial_state,
+                                                      float* __restrict__ final_state, E* __restrict__ o, int N, int H,
+                                                      int mc, E* __restrict__ states, E* __restrict__ ut) {
   using RC = Rec<E, 16>;
   typedef typename Frag<E>::T FragT;
   static_assert(RC::NRT == 1 && RC::NKC == 1, "16-token chunks");
   constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
   constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
-  __shared__ __attribute__((aligned(16))) E xs[D * XW];
-  __shared__ __attribute__((aligned(16))) float xg[D];
+  __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
+  __shared__ floatx4 xp[2][4][64];                           // U~ parts, by chunk parity
+  __shared__ floatx4 xq[2][4][64];                           // (Q e^G) S parts
 
   const int b = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int xcd = b & 7, rest = b >> 3;
   const int ct = rest & 7, slot = rest >> 3;
   const int u = slot * 8 + xcd;
-  if (u >= N * H) return;
+  if (u >= N * H) return;  // uniform over the work-group
   const int n = u / H, h = u - n * H;
-  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
   const size_t HD = (size_t)H * D;
-  const size_t sbase = (size_t)u * D * D + 16 * ct + m;
+  // state rows 32w + 16j + 4g + i, column 16ct + m
+  const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
 
-  floatx4 S[8];
+  floatx4 S[2];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) S[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (initial_state) {
+  for (int j = 0; j < 2; ++j) {
+    S[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (initial_state) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[rt][i] = initial_state[sbase + (size_t)(16 * rt + 4 * g + i) * D];
+      for (int i = 0; i < 4; ++i) S[j][i] = initial_state[sbase + (size_t)(16 * j + i) * D];
+    }
   }
 
+  // a stage holds what the loads return, unconverted: converting at load time would
+  // make the wave wait for the data one step early
   struct Stage {
-    FragT wn[4], qt[4], ke[8], pp;
-    float uu[4];
-    floatx4 gm;  // lanes 0..31: e^{g_C} of channels 4 lane .. 4 lane + 3
+    FragT wn, qt, ke[2], pp;
+    typename Vec4<E>::T uu;
+    floatx4 gm[2];
     int2 inf;
   };
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   auto load = [&](Stage& st, int c) {
     const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
     const E* rec = reinterpret_cast<const E*>(rb);
+    st.wn = load_frag<E>(rec + RC::WN + ((size_t)w * 64 + lane) * 8);
+    st.qt = load_frag<E>(rec + RC::QT + ((size_t)w * 64 + lane) * 8);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      st.wn[kb] = load_frag<E>(rec + RC::WN + ((size_t)kb * 64 + lane) * 8);
-      st.qt[kb] = load_frag<E>(rec + RC::QT + ((size_t)kb * 64 + lane) * 8);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) st.ke[rt] = load_frag<E>(rec + RC::KE + ((size_t)rt * 64 + lane) * 8);
+    for (int j = 0; j < 2; ++j) st.ke[j] = load_frag<E>(rec + RC::KE + ((size_t)(2 * w + j) * 64 + lane) * 8);
     st.pp = load_frag<E>(rec + RC::PP + (size_t)lane * 8);
-    load4f(rec + RC::UU + ((size_t)ct * 64 + lane) * 4, st.uu);
-    st.gm = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES) + 4 * (lane & 31));
+    st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
+    const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
     st.inf = info[c];
   };
 
-  auto compute = [&](const Stage& st, int c) {
-    FragT Sb[4];
+  auto compute = [&](const Stage& st, int c, int buf) {
+    const FragT Sb = acc_pair_to_frag<E>(S[0], S[1]);  // k-block w of the state
+    E* xw = xs[w];
+    if (states) {  // this wave's 32 rows of the state entering the chunk
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<E>(S[2 * kb], S[2 * kb + 1]);
-    if (states) {  // the slab of the state entering the chunk, as 16-byte row pieces
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+        for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(S[j][i]);
+      compiler_fence();
+      E* sp = states + ((size_t)h * mc + c) * D * D + (size_t)(32 * w) * D + 16 * ct;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[(16 * rt + 4 * g + i) * XW + m] = from_f<E>(S[rt][i]);
-      __syncthreads();
-      E* sp = states + ((size_t)h * mc + c) * D * D + 16 * ct;
-#pragma unroll
-      for (int j = 0; j < 2 * (int)sizeof(E); ++j) {
-        const int piece = lane + 64 * j, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(sp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+      for (int p = 0; p < (int)sizeof(E) / 2; ++p) {
+        const int piece = lane + 64 * p, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(sp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
       }
-      __syncthreads();
+      compiler_fence();
     }
-    // U~ = U - W S  (the record holds -W)
-    floatx4 Ut = floatx4{st.uu[0], st.uu[1], st.uu[2], st.uu[3]};
+    // parts over this wave's 32 state rows: U - W S (U added once, by wave 0) and (Q e^G) S
+    floatx4 up = w == 0 ? floatx4{to_f(st.uu[0]), to_f(st.uu[1]), to_f(st.uu[2]), to_f(st.uu[3])}
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+    mma(up, st.wn, Sb);
+    xp[buf][w][lane] = up;
+    if (o) {
+      floatx4 xpart = {0.f, 0.f, 0.f, 0.f};
+      mma(xpart, st.qt, Sb);
+      xq[buf][w][lane] = xpart;
+    }
+    lds_barrier();
+    const floatx4 Ut = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
+    if (ut && w == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma(Ut, st.wn[kb], Sb[kb]);
-    if (ut) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
-      __syncthreads();
+      for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
+      compiler_fence();
       if (lane < 16 * (16 / VE)) {
         const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
         *reinterpret_cast<uint4*>(ut + ((size_t)h * mc + c) * 16 * D + (size_t)row * D + 16 * ct + col) =
-            *reinterpret_cast<const uint4*>(&xs[row * XW + col]);
+            *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
       }
-      __syncthreads();
+      compiler_fence();
     }
     const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});
-    if (o) {  // O = (Q e^G) S + P U~
-      floatx4 X = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(X, st.qt[kb], Sb[kb]);
+    if (o && w == 1) {  // O = (Q e^G) S + P U~
+      floatx4 X = xq[buf][0][lane] + xq[buf][1][lane] + xq[buf][2][lane] + xq[buf][3][lane];
       mma(X, st.pp, Ub);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1036,51 +1047,56 @@ __global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ re
         if (row < st.inf.y) o[(size_t)(st.inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[i]);
       }
     }
-    // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~
-    if (lane < 32) *reinterpret_cast<floatx4*>(&xg[4 * lane]) = st.gm;
-    __syncthreads();
+    // S_w = Diag(e^{g_C}) S_w + (K e^{g_C - G})^T_w U~
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      const floatx4 gv = *reinterpret_cast<const floatx4*>(&xg[16 * rt + 4 * g]);
-      S[rt] = gv * S[rt];
-      mma(S[rt], st.ke[rt], Ub);
+    for (int j = 0; j < 2; ++j) {
+      S[j] = st.gm[j] * S[j];
+      mma(S[j], st.ke[j], Ub);
     }
-    __syncthreads();
   };
 
-  // L2 touch INTER16_TOUCH_AHEAD chunks beyond the register stage: each of the
-  // head's eight slab waves reads one word of every eighth line of the record, so
-  // the real loads hit in L2 (the words are XOR-folded into tacc, stored only by a
-  // never-taken branch, which keeps the loads without waiting for them)
+  // L2 touch INTER16_TOUCH_AHEAD chunks beyond the register stage: each line of the
+  // record is read (one word) by one of the head's 32 waves, so the real loads hit in
+  // L2 (the words are XOR-folded into tacc, stored only by a never-taken branch)
   constexpr int LINES = (int)(RC::BYTES / 128);
-  static_assert(RC::BYTES % 128 == 0 && LINES <= 8 * 64, "one touch per lane");
-  const int touch_line = ct + 8 * lane;
-  unsigned tacc = 0u, tv[2] = {0u, 0u};
+  static_assert(RC::BYTES % 128 == 0 && LINES <= 32 * 64, "one touch per lane");
+  // lanes past the record's last line touch that line again (an unconditional load
+  // is never merged with an old value)
+  const int touch_line = min((ct * 4 + w) + 32 * lane, LINES - 1);
+  // each loop iteration covers four chunks: its first step touches the next four
+  // beyond the touch distance and the words are folded in after its last step, so
+  // no touched word lives across the back edge (where a copy would wait for it)
+  unsigned tacc = 0u;
 
   Stage st[2];
   if (c_begin < c_end) load(st[0], c_begin);
-  for (int c0 = c_begin; c0 < c_end; c0 += 2) {
+  for (int c0 = c_begin; c0 < c_end; c0 += 4) {
+    unsigned tv[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int c = c0 + r;
       // the stage consumed one step earlier takes chunk c + 1 (past the end, the
       // last chunk again: every step issues the same loads)
-      load(st[r ^ 1], min(c + 1, c_end - 1));
-      if (touch_line < LINES)
-        tv[r] = *reinterpret_cast<const unsigned*>(
-            records + ((size_t)h * mc + min(c + 1 + INTER16_TOUCH_AHEAD, c_end - 1)) * RC::BYTES +
-            (size_t)touch_line * 128);
-      if (c < c_end) compute(st[r], c);
-      tacc ^= tv[r ^ 1];
+      load(st[(r + 1) & 1], min(c + 1, c_end - 1));
+      if (r == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tv[j] = *reinterpret_cast<const unsigned*>(
+              records + ((size_t)h * mc + min(c0 + 1 + INTER16_TOUCH_AHEAD + j, c_end - 1)) * RC::BYTES +
+              (size_t)touch_line * 128);
+      }
+      if (c < c_end) compute(st[r & 1], c, r & 1);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tacc ^= tv[j];
   }
   // mc is never negative (the host sizes it from the shapes), so this never stores
   if (mc < 0 && tacc == 0u) o[lane] = from_f<E>(0.f);
   if (final_state) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) final_state[sbase + (size_t)(16 * rt + 4 * g + i) * D] = S[rt][i];
+      for (int i = 0; i < 4; ++i) final_state[sbase + (size_t)(16 * j + i) * D] = S[j][i];
   }
 }
 
@@ -1101,21 +1117,10 @@ __global__ void __launch_bounds__(64) inter16_kernel(const char* __restrict__ re
 // lane, no staging.
 // ---------------------------------------------------------------------------
 namespace {
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-// s_waitcnt with lgkmcnt(0) and the vector-memory counter left free
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// work-group barrier for LDS exchanges that leaves in-flight global loads alone
-__device__ __forceinline__ void lds_barrier() {
-  compiler_fence();
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-}
-
 // chunks of record data in flight ahead of the one being computed
 constexpr int INTER_LOOKAHEAD = 1;
 // chunks beyond the lookahead whose record lines are pulled into L2 ahead of use
-constexpr int INTER_TOUCH_AHEAD = 2;
+constexpr int INTER_TOUCH_AHEAD = 4;
 
 struct InterStage {
   bf16x8 wn[4], qt[4], ke[4], pp[2];
@@ -1244,28 +1249,41 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
   // without making any step wait for them before the next one.
   constexpr int REC_LINES = (int)(RC::BYTES / 128);
   static_assert(RC::BYTES % 128 == 0 && REC_LINES <= 32 * 64, "one touch per lane per line");
-  const int touch_line = (ct * 4 + w) + 32 * lane;
-  unsigned tacc = 0u, tv[LA + 1] = {};
+  // lanes past the record's last line touch that line again: the load stays
+  // unconditional, so its destination register is never merged with an old value
+  const int touch_line = min((ct * 4 + w) + 32 * lane, REC_LINES - 1);
+  // Each loop iteration covers TOUCH_STEPS chunks: its first step touches the next
+  // TOUCH_STEPS chunks beyond the touch distance, and the words are folded in after
+  // its last step. No touched word lives across the loop's back edge, where a
+  // register copy would have to wait for it.
+  constexpr int TOUCH_STEPS = 4;
+  static_assert(TOUCH_STEPS % (LA + 1) == 0, "steps per loop iteration");
+  unsigned tacc = 0u;
 
   InterStage st[LA + 1];
 #pragma unroll
   for (int r = 0; r < LA; ++r)
     if (c_begin < c_end) load(st[r], min(c_begin + r, c_end - 1));
-  for (int c0 = c_begin; c0 < c_end; c0 += LA + 1) {
+  for (int c0 = c_begin; c0 < c_end; c0 += TOUCH_STEPS) {
+    unsigned tv[TOUCH_STEPS];
 #pragma unroll
-    for (int r = 0; r <= LA; ++r) {
+    for (int r = 0; r < TOUCH_STEPS; ++r) {
       const int c = c0 + r;
       // the stage consumed one step earlier takes chunk c + LA; past the end the
       // final record is loaded again, so every step issues the same loads and the
       // register stages rotate without leaving the loop body
       load(st[(r + LA) % (LA + 1)], min(c + LA, c_end - 1));
-      if (touch_line < REC_LINES)
-        tv[r] = *reinterpret_cast<const unsigned*>(
-            head_records + (size_t)min(c + LA + INTER_TOUCH_AHEAD, c_end - 1) * RC::BYTES + (size_t)touch_line * 128);
-      if (c < c_end) compute(st[r], c);
-      // the word touched one step earlier has had a whole step to arrive
-      tacc ^= tv[(r + LA) % (LA + 1)];
+      if (r == 0) {
+#pragma unroll
+        for (int j = 0; j < TOUCH_STEPS; ++j)
+          tv[j] = *reinterpret_cast<const unsigned*>(
+              head_records + (size_t)min(c0 + LA + INTER_TOUCH_AHEAD + j, c_end - 1) * RC::BYTES +
+              (size_t)touch_line * 128);
+      }
+      if (c < c_end) compute(st[r % (LA + 1)], c);
     }
+#pragma unroll
+    for (int j = 0; j < TOUCH_STEPS; ++j) tacc ^= tv[j];
   }
   // total_tokens is never negative (the host rejects it), so this never stores
   if (total_tokens < 0 && tacc == 0u) o[lane] = (__bf16)0.f;
@@ -1340,7 +1358,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
                          records, chunk_off, cu_seqlens, T, total_tokens, initial_state, final_state, (__bf16*)o, N,
                          H, (int)mc);
     } else if constexpr (C == 16) {
-      hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+      hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, records, chunk_off,
                          info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr, (E*)nullptr);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
@@ -1387,7 +1405,7 @@ hipError_t launch_states_typed(const void* q, const void* k, const void* v, cons
   }
   const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
-    hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records, chunk_off,
+    hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, records, chunk_off,
                        info, initial_state, (float*)nullptr, (E*)nullptr, N, H, (int)mc, (E*)states, (E*)ut);
     e = hipGetLastError();
     trace_mark(stream, 2);
