@@ -21,14 +21,17 @@
 // dlog_alpha = reverse cumulative sum of dG over the chunk's rows.
 //
 // Kernels, in launch order:
-//   the forward at 16-token chunks (plan, intra_kernel, inter_kernel) keeping, per
-//     (head, chunk), the state entering the chunk and U~;
+//   the forward's plan and records at 16-token chunks (plan_kernel, intra_kernel);
+//   fwd_state_kernel   the forward state pass (inter16_body), four waves per
+//                      (sequence, head, 16-column slab): keeps the state entering
+//                      every chunk and U~;
 //   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
-//                      e^{g_C}, in the fragment order bwd_state_kernel reads;
-//   bwd_state_kernel   four waves per (sequence, head, 16-column slab), serial over
-//                      the chunks in reverse, the 128 x 16 fp32 slab of the state
-//                      gradient in accumulator registers (32 rows per wave): keeps
-//                      dS_C and dU~ per chunk, writes the initial-state gradient;
+//                      e^{g_C}, in the fragment order the reverse state pass reads;
+//   bwd_state_kernel   the reverse state pass (bwd_state_body), four waves per
+//                      (sequence, head, 16-column slab), over the chunks in reverse
+//                      with the 128 x 16 fp32 slab of the state gradient in
+//                      accumulator registers: keeps dS_C and dU~ per chunk and writes
+//                      the initial-state gradient;
 //   bwd_chunk_kernel   one work-group per (chunk, head): everything local to the
 //                      chunk. X1, X2, X3 and dgamma are bf16 (or fp32) MFMA products
 //                      whose operands come straight from row-major global memory;
@@ -43,7 +46,9 @@
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
+#include "kda_inter16.h"
 #include "kda_internal.h"
+#include "kda_record.h"
 
 namespace kda {
 namespace {
@@ -69,7 +74,7 @@ __device__ __forceinline__ float sum16(float x) {
 }
 
 // Per-(head, chunk) record for the reverse state pass, in the MFMA operand order
-// bwd_state_kernel consumes (lane l = m + 16 g; the fragment convention of
+// reverse state pass consumes (lane l = m + 16 g; the fragment convention of
 // kda_device.h, chunk rows padded to 32 with zeros):
 //   WT   [8 rt][64][4]  slot s of the A fragment of (-W)^T, channel tile rt: -W[4g+s][16rt+m]
 //   QTT  [8 rt][64][4]  the same for (Q e^G)^T
@@ -309,8 +314,8 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// bwd_state_kernel: four waves per (sequence, head, 16-column slab), chunks in
-// reverse. Wave w keeps dS rows 32w + 16j + 4g + i (j = 0, 1), column 16ct + m, in
+// The reverse state pass (bwd_state_body): four waves per (sequence, head,
+// 16-column slab), chunks in reverse. Wave w keeps dS rows 32w + 16j + 4g + i (j = 0, 1), column 16ct + m, in
 // Lm[j], the layout whose pair is a B fragment over its 32 rows. Per chunk, wave w
 // forms its k-block's part of dU~ = P^T dO + (K e^{g_C-G}) dS (P^T dO once, in wave
 // 0), the parts are summed through LDS behind one barrier that leaves global loads
@@ -320,12 +325,11 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
 constexpr int STATE_TOUCH_AHEAD = 4;
 
 template <typename E>
-__global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__ brec,
-                                                        const int32_t* __restrict__ chunk_off,
-                                                        const int2* __restrict__ info, const E* __restrict__ dout,
-                                                        const float* __restrict__ d_final,
-                                                        float* __restrict__ d_initial, E* __restrict__ dstates,
-                                                        E* __restrict__ dut, int N, int H, int mc) {
+__device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ brec,
+                                               const int32_t* __restrict__ chunk_off, const int2* __restrict__ info,
+                                               const E* __restrict__ dout, const float* __restrict__ d_final,
+                                               float* __restrict__ d_initial, E* __restrict__ dstates,
+                                               E* __restrict__ dut, int N, int H, int mc) {
   using BR = BRec<E>;
   typedef typename Frag<E>::T FragT;
   typedef typename Vec4<E>::T V4;
@@ -337,7 +341,6 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__
   __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
   __shared__ floatx4 xp[2][4][64];                           // dU~ parts, by chunk parity
 
-  const int b = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const int xcd = b & 7, rest = b >> 3;
@@ -487,24 +490,31 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__
   // loads). Four touch words in flight: step r folds in the word it loaded four steps
   // earlier before loading the next one into the same variable, so no register copy
   // has to wait for a load.
-  Stage sa, sb;
-  if (c_begin < c_end) load(sa, c_end - 1);
+  // four named stages, three chunks of operands in flight: step r of an iteration
+  // loads chunk c - 3 into the stage consumed one step earlier (past the start, the
+  // first chunk again: every step issues the same loads)
+  Stage sa, sb, sc, sd;
+  if (c_begin < c_end) {
+    load(sa, c_end - 1);
+    load(sb, max(c_end - 2, c_begin));
+    load(sc, max(c_end - 3, c_begin));
+  }
   for (int c0 = c_end - 1; c0 >= c_begin; c0 -= 4) {
     // the iteration's four chunks: the first step touches the four beyond the touch
     // distance; the words are folded in after the last step (none lives across the
     // back edge, where a register copy would wait for it)
-    load(sb, max(c0 - 1, c_begin));
-    const unsigned t0 = touch(max(c0 - 1 - STATE_TOUCH_AHEAD, c_begin));
-    const unsigned t1 = touch(max(c0 - 2 - STATE_TOUCH_AHEAD, c_begin));
-    const unsigned t2 = touch(max(c0 - 3 - STATE_TOUCH_AHEAD, c_begin));
-    const unsigned t3 = touch(max(c0 - 4 - STATE_TOUCH_AHEAD, c_begin));
+    load(sd, max(c0 - 3, c_begin));
+    const unsigned t0 = touch(max(c0 - 3 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t1 = touch(max(c0 - 4 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t2 = touch(max(c0 - 5 - STATE_TOUCH_AHEAD, c_begin));
+    const unsigned t3 = touch(max(c0 - 6 - STATE_TOUCH_AHEAD, c_begin));
     compute(sa, c0, 0);
-    load(sa, max(c0 - 2, c_begin));
-    if (c0 - 1 >= c_begin) compute(sb, c0 - 1, 1);
-    load(sb, max(c0 - 3, c_begin));
-    if (c0 - 2 >= c_begin) compute(sa, c0 - 2, 0);
     load(sa, max(c0 - 4, c_begin));
-    if (c0 - 3 >= c_begin) compute(sb, c0 - 3, 1);
+    if (c0 - 1 >= c_begin) compute(sb, c0 - 1, 1);
+    load(sb, max(c0 - 5, c_begin));
+    if (c0 - 2 >= c_begin) compute(sc, c0 - 2, 0);
+    load(sc, max(c0 - 6, c_begin));
+    if (c0 - 3 >= c_begin) compute(sd, c0 - 3, 1);
     tacc ^= t0 ^ t1 ^ t2 ^ t3;
   }
   // mc is never negative (the host sizes it from the shapes), so this never stores
@@ -515,6 +525,28 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) d_initial[sbase + (size_t)(16 * j + i) * D] = Lm[j][i];
   }
+}
+
+// The two serial state passes run as separate launches, one work-group per CU each.
+// Run side by side in one launch (one work-group of each per CU) they take longer
+// than one after the other: each already saturates a per-CU resource.
+template <typename E>
+__global__ void __launch_bounds__(256) fwd_state_kernel(const char* __restrict__ records,
+                                                        const int32_t* __restrict__ chunk_off,
+                                                        const int2* __restrict__ info,
+                                                        const float* __restrict__ initial_state, int N, int H, int mc,
+                                                        E* __restrict__ states, E* __restrict__ ut) {
+  inter16_body<E>(blockIdx.x, records, chunk_off, info, initial_state, nullptr, nullptr, N, H, mc, states, ut);
+}
+
+template <typename E>
+__global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__ brec,
+                                                        const int32_t* __restrict__ chunk_off,
+                                                        const int2* __restrict__ info, const E* __restrict__ dout,
+                                                        const float* __restrict__ d_final,
+                                                        float* __restrict__ d_initial, E* __restrict__ dstates,
+                                                        E* __restrict__ dut, int N, int H, int mc) {
+  bwd_state_body<E>(blockIdx.x, brec, chunk_off, info, dout, d_final, d_initial, dstates, dut, N, H, mc);
 }
 
 // ---------------------------------------------------------------------------
@@ -813,9 +845,18 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   const int dtype = std::is_same<E, float>::value ? 1 : 0;
 
   trace_begin(stream);
-  hipError_t e = launch_forward_states(dtype, q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, B, T,
-                                       H, workspace, states, ut, stream);
+  hipError_t e = launch_forward_records(dtype, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, B, T, H, workspace,
+                                        stream);
   if (e != hipSuccess) return e;
+  const char* records = ws + l.fwd.off_records;
+  const int64_t slots = ((int64_t)N * H + 7) / 8;
+  if (slots > 0) {
+    hipLaunchKernelGGL(fwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, records, chunk_off,
+                       info, initial_state, N, H, (int)mc, states, ut);
+    e = hipGetLastError();
+    trace_mark(stream, 2);
+    if (e != hipSuccess) return e;
+  }
   if (mc > 0) {
     hipLaunchKernelGGL(bwd_local_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
                        (const E*)k, log_alpha, beta, chunk_off + N, info, H, (int)mc, brec);
@@ -823,7 +864,6 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
     trace_mark(stream, 5);
     if (e != hipSuccess) return e;
   }
-  const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
     hipLaunchKernelGGL(bwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, brec, chunk_off,
                        info, (const E*)dout, d_final, d_initial, dstates, dut, N, H, (int)mc);

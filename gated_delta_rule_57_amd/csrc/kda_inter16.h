@@ -1,0 +1,195 @@
+// Inter-chunk state pass for 16-token chunks (bf16 or fp32 records), shared by the
+// chunk-16 prefill and the backward's forward state pass.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_record.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------------------
+// Inter-chunk kernel for 16-token chunks: four waves per (sequence, head, 16-column
+// slab), wave w keeping state rows 32w .. 32w+31. Per chunk, wave w forms its
+// k-block's part of U~ = U - W S (and of (Q e^G) S), the four parts are summed
+// through LDS behind one barrier that leaves global loads in flight, and each wave
+// updates its own rows. The next chunk's fragments are loaded into registers while
+// the current one is computed, and each record line is touched in L2 a few chunks
+// ahead by one wave of the head. The per-chunk outputs of the backward pass (states,
+// U~) are transposed through LDS and written as 16-byte row pieces.
+// ---------------------------------------------------------------------------
+constexpr int INTER16_LOOKAHEAD = 3;
+constexpr int INTER16_TOUCH_AHEAD = 4;
+
+// The body of one work-group (256 threads) with work-group index b, laid out like
+// the 64-token kernel: b & 7 selects the XCD, (b >> 3) & 7 the slab, b >> 6 the
+// (sequence, head) group. Called by inter16_kernel and by the backward's combined
+// state-pass kernel.
+template <typename E>
+__device__ __forceinline__ void inter16_body(int b, const char* __restrict__ records,
+                                             const int32_t* __restrict__ chunk_off, const int2* __restrict__ info,
+                                             const float* __restrict__ initial_state, float* __restrict__ final_state,
+                                             E* __restrict__ o, int N, int H, int mc, E* __restrict__ states,
+                                             E* __restrict__ ut) {
+  using RC = Rec<E, 16>;
+  typedef typename Frag<E>::T FragT;
+  static_assert(RC::NRT == 1 && RC::NKC == 1, "16-token chunks");
+  constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
+  constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
+  __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
+  __shared__ floatx4 xp[2][4][64];                           // U~ parts, by chunk parity
+  __shared__ floatx4 xq[2][4][64];                           // (Q e^G) S parts
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const int xcd = b & 7, rest = b >> 3;
+  const int ct = rest & 7, slot = rest >> 3;
+  const int u = slot * 8 + xcd;
+  if (u >= N * H) return;  // uniform over the work-group
+  const int n = u / H, h = u - n * H;
+  const size_t HD = (size_t)H * D;
+  // state rows 32w + 16j + 4g + i, column 16ct + m
+  const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
+
+  floatx4 S[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    S[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (initial_state) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[j][i] = initial_state[sbase + (size_t)(16 * j + i) * D];
+    }
+  }
+
+  // a stage holds what the loads return, unconverted: converting at load time would
+  // make the wave wait for the data one step early
+  struct Stage {
+    FragT wn, qt, ke[2], pp;
+    typename Vec4<E>::T uu;
+    floatx4 gm[2];
+    int2 inf;
+  };
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+  auto load = [&](Stage& st, int c) {
+    const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
+    const E* rec = reinterpret_cast<const E*>(rb);
+    st.wn = load_frag<E>(rec + RC::WN + ((size_t)w * 64 + lane) * 8);
+    st.qt = load_frag<E>(rec + RC::QT + ((size_t)w * 64 + lane) * 8);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.ke[j] = load_frag<E>(rec + RC::KE + ((size_t)(2 * w + j) * 64 + lane) * 8);
+    st.pp = load_frag<E>(rec + RC::PP + (size_t)lane * 8);
+    st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
+    const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
+    st.inf = info[c];
+  };
+
+  auto compute = [&](const Stage& st, int c, int buf) {
+    const FragT Sb = acc_pair_to_frag<E>(S[0], S[1]);  // k-block w of the state
+    E* xw = xs[w];
+    if (states) {  // this wave's 32 rows of the state entering the chunk
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(S[j][i]);
+      compiler_fence();
+      E* sp = states + ((size_t)h * mc + c) * D * D + (size_t)(32 * w) * D + 16 * ct;
+#pragma unroll
+      for (int p = 0; p < (int)sizeof(E) / 2; ++p) {
+        const int piece = lane + 64 * p, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(sp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
+      }
+      compiler_fence();
+    }
+    // parts over this wave's 32 state rows: U - W S (U added once, by wave 0) and (Q e^G) S
+    floatx4 up = w == 0 ? floatx4{to_f(st.uu[0]), to_f(st.uu[1]), to_f(st.uu[2]), to_f(st.uu[3])}
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+    mma(up, st.wn, Sb);
+    xp[buf][w][lane] = up;
+    if (o) {
+      floatx4 xpart = {0.f, 0.f, 0.f, 0.f};
+      mma(xpart, st.qt, Sb);
+      xq[buf][w][lane] = xpart;
+    }
+    lds_barrier();
+    const floatx4 Ut = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
+    if (ut && w == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
+      compiler_fence();
+      if (lane < 16 * (16 / VE)) {
+        const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
+        *reinterpret_cast<uint4*>(ut + ((size_t)h * mc + c) * 16 * D + (size_t)row * D + 16 * ct + col) =
+            *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
+      }
+      compiler_fence();
+    }
+    const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});
+    if (o && w == 1) {  // O = (Q e^G) S + P U~
+      floatx4 X = xq[buf][0][lane] + xq[buf][1][lane] + xq[buf][2][lane] + xq[buf][3][lane];
+      mma(X, st.pp, Ub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row < st.inf.y) o[(size_t)(st.inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[i]);
+      }
+    }
+    // S_w = Diag(e^{g_C}) S_w + (K e^{g_C - G})^T_w U~
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      S[j] = st.gm[j] * S[j];
+      mma(S[j], st.ke[j], Ub);
+    }
+  };
+
+  // L2 touch INTER16_TOUCH_AHEAD chunks beyond the register stage: each line of the
+  // record is read (one word) by one of the head's 32 waves, so the real loads hit in
+  // L2 (the words are XOR-folded into tacc, stored only by a never-taken branch)
+  constexpr int LINES = (int)(RC::BYTES / 128);
+  static_assert(RC::BYTES % 128 == 0 && LINES <= 32 * 64, "one touch per lane");
+  // lanes past the record's last line touch that line again (an unconditional load
+  // is never merged with an old value)
+  const int touch_line = min((ct * 4 + w) + 32 * lane, LINES - 1);
+  // each loop iteration covers four chunks: its first step touches the next four
+  // beyond the touch distance and the words are folded in after its last step, so
+  // no touched word lives across the back edge (where a copy would wait for it)
+  unsigned tacc = 0u;
+
+  // INTER16_LOOKAHEAD chunks of operands in flight in registers
+  constexpr int LA = INTER16_LOOKAHEAD;
+  static_assert(4 % (LA + 1) == 0, "four steps per loop iteration");
+  Stage st[LA + 1];
+#pragma unroll
+  for (int r = 0; r < LA; ++r)
+    if (c_begin < c_end) load(st[r], min(c_begin + r, c_end - 1));
+  for (int c0 = c_begin; c0 < c_end; c0 += 4) {
+    unsigned tv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = c0 + r;
+      // the stage consumed one step earlier takes chunk c + LA (past the end, the
+      // last chunk again: every step issues the same loads)
+      load(st[(r + LA) % (LA + 1)], min(c + LA, c_end - 1));
+      if (r == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tv[j] = *reinterpret_cast<const unsigned*>(
+              records + ((size_t)h * mc + min(c0 + LA + INTER16_TOUCH_AHEAD + j, c_end - 1)) * RC::BYTES +
+              (size_t)touch_line * 128);
+      }
+      if (c < c_end) compute(st[r % (LA + 1)], c, r & 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tacc ^= tv[j];
+  }
+  // mc is never negative (the host sizes it from the shapes), so this never stores
+  if (mc < 0 && tacc == 0u) o[lane] = from_f<E>(0.f);
+  if (final_state) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) final_state[sbase + (size_t)(16 * j + i) * D] = S[j][i];
+  }
+}
+
+}  // namespace kda

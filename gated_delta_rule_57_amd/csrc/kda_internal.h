@@ -62,10 +62,6 @@ PrefillWs prefill_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int 
 // Chunk length of the backward pass.
 constexpr int BWD_CHUNK = 16;
 
-// The forward pass at BWD_CHUNK-token chunks for the backward: plan, records, and
-// per (head, chunk) the state entering the chunk (states, [H][mc][128][128]) and
-// U~ = U - W S ([H][mc][BWD_CHUNK][128]), both in the input dtype. workspace is laid
-// out by prefill_ws_layout(..., BWD_CHUNK, dtype). No output, no final state.
 // Backward workspace: the forward's (at BWD_CHUNK), then the backward records, the
 // chunk-entry states, the chunk-end state gradients, U~ and dU~ per (head, chunk).
 struct BackwardWs {
@@ -82,9 +78,12 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
                            float* dbeta, float* d_initial, int B, int T, int H, void* workspace,
                            hipStream_t stream);
 
-hipError_t launch_forward_states(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                                 const float* beta, const float* initial_state, const int32_t* cu_seqlens,
-                                 int num_seqs, int B, int T, int H, void* workspace, void* states, void* ut,
-                                 hipStream_t stream);
+// The first part of the forward pass at BWD_CHUNK-token chunks, for the backward:
+// the chunk plan and the per-(head, chunk) records, in a workspace laid out by
+// prefill_ws_layout(..., BWD_CHUNK, dtype). The backward launches the forward
+// state pass (chunk-entry states and U~) itself.
+hipError_t launch_forward_records(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                                  const float* beta, const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                                  void* workspace, hipStream_t stream);
 
 }  // namespace kda

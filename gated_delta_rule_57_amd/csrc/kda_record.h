@@ -1,0 +1,28 @@
+// Layout of the per-(chunk, head) record that the intra-chunk kernel writes and the
+// inter-chunk kernels read (shared by the prefill and the backward's forward pass).
+#pragma once
+
+#include "kda_device.h"
+
+namespace kda {
+
+__host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Per-(chunk, head) record, element offsets for element type E and chunk C.
+template <typename E, int C>
+struct Rec {
+  static constexpr int NRT = C / 16;           // 16-row tiles of the chunk
+  static constexpr int NKC = (C + 31) / 32;    // 32-row k-blocks over the chunk
+  static constexpr int FR = 64 * 8;            // one fragment block: 64 lanes x 8 elements
+  static constexpr size_t WN = 0;                                   // [NRT][4][64][8]   -W
+  static constexpr size_t QT = WN + (size_t)NRT * 4 * FR;           // [NRT][4][64][8]   Q e^G
+  static constexpr size_t KE = QT + (size_t)NRT * 4 * FR;           // [8][NKC][64][8]   (K e^{g_C-G})^T
+  static constexpr size_t PP = KE + (size_t)8 * NKC * FR;           // [NRT][NKC][64][8] P
+  static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;         // [8][NRT][64][4]   U, accumulator order
+  static constexpr size_t END = UU + (size_t)NRT * 8 * 64 * 4;
+  static constexpr size_t GAMMA_BYTES = al256(END * sizeof(E));      // float[128] e^{g_C}
+  static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
+};
+
+}  // namespace kda

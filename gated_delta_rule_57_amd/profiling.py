@@ -26,7 +26,7 @@ import re
 import sys
 
 KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
-           ("inter16_kernel", "inter16"), ("inter_kernel", "inter"), ("decode_kernel", "decode"),
+           ("inter16_kernel", "inter16"), ("fwd_state_kernel", "inter16"), ("inter_kernel", "inter"), ("decode_kernel", "decode"),
            ("output_norm_gate_kernel", "outnorm"), ("bwd_local_kernel", "bwd_local"),
            ("bwd_state_kernel", "bwd_state"), ("bwd_chunk_kernel", "bwd_chunk"))
 COPY_BYTES = 1 << 30

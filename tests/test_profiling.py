@@ -23,6 +23,7 @@ def test_short_names_split_intra_by_gate():
     assert s("void kda::inter16_kernel<__bf16>(char const*, int const*)") == "inter16"
     assert s("_ZN3kda12_GLOBAL__N_116bwd_chunk_kernelIDF16bEEvPKT_") == "bwd_chunk"
     assert s("_ZN3kda12_GLOBAL__N_116bwd_state_kernelIDF16bEEvPKc") == "bwd_state"
+    assert s("_ZN3kda12_GLOBAL__N_116fwd_state_kernelIDF16bEEvPKc") == "inter16"
     assert s("_ZN3kda12_GLOBAL__N_116bwd_local_kernelIDF16bEEvPKT_") == "bwd_local"
 
 
