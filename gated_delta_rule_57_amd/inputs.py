@@ -237,3 +237,78 @@ def make_raw_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int =
     s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
     return RawPrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(), gate.contiguous(), beta.contiguous(),
                             out_gate.contiguous(), w, s0, cu, dtype, chunk)
+
+
+@dataclass
+class DplrInputs:
+    """Inputs of the general diagonal-plus-low-rank recurrence
+    S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T."""
+    q: torch.Tensor          # [B, T, H, dk] compute dtype
+    k: torch.Tensor          # [B, T, H, dk] compute dtype
+    v: torch.Tensor          # [B, T, H, dv] compute dtype
+    a: torch.Tensor          # [B, T, H, dk] compute dtype
+    b: torch.Tensor          # [B, T, H, dk] compute dtype
+    log_alpha: torch.Tensor  # [B, T, H, dk] fp32
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    dtype: str
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self):
+        return self.q.shape[0] if self.cu_seqlens is None else self.cu_seqlens.numel() - 1
+
+    def numpy(self):
+        f = lambda t: None if t is None else t.detach().float().cpu().numpy()
+        cu = None if self.cu_seqlens is None else self.cu_seqlens.cpu().numpy().astype(np.int64)
+        return dict(q=f(self.q), k=f(self.k), v=f(self.v), a=f(self.a), b=f(self.b), log_alpha=f(self.log_alpha),
+                    initial_state=f(self.initial_state), cu_seqlens=cu)
+
+
+def make_dplr(seed: int, B: int, T: int, H: int, dtype: str, la_mode: str = "scaled", la_scale: float = 0.1,
+              s0_std: float = 0.0, num_seqs: Optional[int] = None, lowrank: str = "tied", ab_scale: float = 1.0,
+              device="cuda", dk: int = D, dv: int = D) -> DplrInputs:
+    """Inputs of the general DPLR recurrence. q, k, v and log_alpha are drawn as in
+    ``make_prefill`` (same draw order up to log_alpha). The low-rank pair:
+      "tied": u ~ N(0, 1) L2-normalised per (token, head) and rounded to the compute
+              dtype gives b = u; a = -2^-j b with 2^-j = sigmoid(N(0, 1)) rounded to a
+              power of two (j >= 1), which is exact in the compute dtype. The
+              transition Diag(alpha) - 2^-j b b^T is then symmetric with eigenvalues
+              in (-1, 1] whatever the rounding, so the state stays bounded at any length.
+      "free": a, b ~ ab_scale N(0, 1/dk) independently (short sequences only).
+    Draw order: cut points, q, k, v, log-decay normals, slow-channel choice (mixed),
+    then u and the strength normals (tied) or a and b (free), then the initial state."""
+    g = _gen(seed, device)
+    cu = None
+    if num_seqs is not None:
+        assert B == 1
+        cu = uniform_composition(g, T, num_seqs, device)
+    td = TORCH_DTYPE[dtype]
+    q = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
+    k = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
+    v = _normal(g, (B, T, H, dv), device).to(td)
+    z = _normal(g, (B, T, H, dk), device)
+    if la_mode == "scaled":
+        log_alpha = -la_scale * torch.nn.functional.softplus(z)
+    elif la_mode == "mixed":
+        log_alpha = -torch.nn.functional.softplus(z)
+        for h in range(H):
+            slow = torch.randperm(dk, generator=g, device=device)[: dk // 2]
+            log_alpha[:, :, h, slow] = -1e-3
+    else:
+        raise ValueError(la_mode)
+    if lowrank == "tied":
+        b = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
+        strength = torch.sigmoid(_normal(g, (B, T, H), device))
+        j = torch.clamp(torch.round(-torch.log2(strength)), min=1.0)
+        a = (-torch.exp2(-j)[..., None] * b.float()).to(td)
+    elif lowrank == "free":
+        a = (ab_scale / dk ** 0.5 * _normal(g, (B, T, H, dk), device)).to(td)
+        b = (ab_scale / dk ** 0.5 * _normal(g, (B, T, H, dk), device)).to(td)
+    else:
+        raise ValueError(lowrank)
+    N = B if cu is None else cu.numel() - 1
+    s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
+    return DplrInputs(q.contiguous(), k.contiguous(), v.contiguous(), a.contiguous(), b.contiguous(),
+                      log_alpha.contiguous(), s0, cu, dtype,
+                      dict(seed=seed, la_mode=la_mode, la_scale=la_scale, lowrank=lowrank))

@@ -20,6 +20,11 @@ Contents
 ``fused``
     The layer's prologue (q, k L2 normalisation, gate and beta activations) and
     epilogue (output RMSNorm and gate) around the recurrence.
+``dplr_forward``
+    The general diagonal-plus-low-rank recurrence
+    S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T, sequential fp64 in C; the
+    comparison point for KDA's chunk kernel. ``reference`` and ``chunked`` hold its
+    dense product, gated-linear-attention and chunkwise forms.
 ``backward``
     Gradients of the recurrence with respect to q, k, v, log_alpha, beta and the
     initial state, by reverse mode through the sequential fp64 form in C.
@@ -28,6 +33,6 @@ Parity status: every function here is pinned by a ``-m "not gpu"`` test; none is
 "parity unpinned".
 """
 from .build import build_oracle, oracle_lib_path
-from .seq import backward, forward, decode_step, load_library
+from .seq import backward, decode_step, dplr_forward, forward, load_library
 
-__all__ = ["build_oracle", "oracle_lib_path", "forward", "decode_step", "backward", "load_library"]
+__all__ = ["build_oracle", "oracle_lib_path", "forward", "decode_step", "backward", "dplr_forward", "load_library"]

@@ -14,6 +14,10 @@ def oracle_lib_path() -> str:
     return _LIB
 
 
+def oracle_source_path() -> str:
+    return _SRC
+
+
 def build_oracle(verbose: bool = False) -> str:
     """Compile the oracle. FP contraction is off so the arithmetic is the plain
     sequence of fp64 multiplies and adds written in the source."""

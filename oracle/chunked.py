@@ -185,3 +185,56 @@ def factored_chunk_step(q, k, v, log_alpha, beta, S0, sub=16, threshold=120.0):
 def factored_forward(q, k, v, log_alpha, beta, S0=None, chunk=64, sub=16, threshold=120.0):
     return forward(q, k, v, log_alpha, beta, S0, chunk,
                    step=lambda *a: factored_chunk_step(*a, sub=sub, threshold=threshold))
+
+
+# ---------------------------------------------------------------------------
+# Chunkwise form of the general DPLR recurrence
+#     S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T ,  o_t = S_t^T q_t
+# (GeekNews "Kimi Linear" summary, section "일반 DPLR보다 줄어든 연산량": a general
+# DPLR transition needs four secondary C x C matrices per chunk where KDA needs two).
+# With w_t = S_{t-1}^T b_t the state is S_t = Diag(alpha_t) S_{t-1} + a_t w_t^T +
+# k_t v_t^T. Per chunk (g inclusive and g^- = g - log_alpha exclusive cumulative
+# log-decays, S_0 the state entering the chunk):
+#   M_ba[r,s] = sum_c b_rc a_sc e^{g^-_rc - g_sc}   (s < r)     M_bk: k_s in place of a_s
+#   M_qa[r,s] = sum_c q_rc a_sc e^{g_rc - g_sc}     (s <= r)    M_qk: k_s in place of a_s
+#   T   = (I - M_ba)^{-1}
+#   W   = T (B * e^{G^-}) S_0 + T M_bk V                        (rows w_r)
+#   O   = (Q * e^G) S_0 + M_qa W + M_qk V
+#   S_C = Diag(e^{g_C}) S_0 + (A * e^{g_C - G})^T W + (K * e^{g_C - G})^T V
+# Derivation: unrolling inside the chunk, w_r = S_0^T (b_r e^{g^-_r}) + sum_{s<r}
+# [M_ba]_rs w_s + [M_bk]_rs v_s, i.e. (I - M_ba) W = (B e^{G^-}) S_0 + M_bk V; the
+# output and the chunk-end state follow by substituting S_r.
+# ---------------------------------------------------------------------------
+def dplr_chunk_step(q, k, v, a, b, log_alpha, S0):
+    """One chunk of the DPLR chunked form in fp64, exponentials taken directly."""
+    g = np.cumsum(log_alpha, axis=0)
+    gm = g - log_alpha
+    C = q.shape[0]
+    lower = np.tril(np.ones((C, C)), -1)
+    incl = np.tril(np.ones((C, C)))
+    d_ex = np.exp(gm[:, None, :] - g[None, :, :])   # [r, s, c] e^{g^-_r - g_s}
+    d_in = np.exp(g[:, None, :] - g[None, :, :])    # [r, s, c] e^{g_r - g_s}
+    M_ba = lower * np.einsum("rc,sc,rsc->rs", b, a, d_ex * lower[:, :, None])
+    M_bk = lower * np.einsum("rc,sc,rsc->rs", b, k, d_ex * lower[:, :, None])
+    M_qa = incl * np.einsum("rc,sc,rsc->rs", q, a, d_in * incl[:, :, None])
+    M_qk = incl * np.einsum("rc,sc,rsc->rs", q, k, d_in * incl[:, :, None])
+    T = np.linalg.inv(np.eye(C) - M_ba)
+    W = T @ (b * np.exp(gm)) @ S0 + T @ M_bk @ v
+    O = (q * np.exp(g)) @ S0 + M_qa @ W + M_qk @ v
+    gC = g[C - 1]
+    S = np.exp(gC)[:, None] * S0 + (a * np.exp(gC[None, :] - g)).T @ W + (k * np.exp(gC[None, :] - g)).T @ v
+    return O, S
+
+
+def dplr_forward(q, k, v, a, b, log_alpha, S0=None, chunk=64):
+    """Chunked fp64 DPLR for one sequence of one head (the last chunk may be partial).
+    q, k, a, b, log_alpha: [T, dk]; v: [T, dv]."""
+    q, k, v, a, b, log_alpha = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b, log_alpha))
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        o[t0:t1], S = dplr_chunk_step(q[t0:t1], k[t0:t1], v[t0:t1], a[t0:t1], b[t0:t1], log_alpha[t0:t1], S)
+    return o, S

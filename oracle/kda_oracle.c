@@ -55,7 +55,7 @@
 
 #define ORACLE_COL_BLOCK 16
 
-int kda_oracle_abi_version(void) { return 3; }
+int kda_oracle_abi_version(void) { return 4; }
 
 /*
  * Optional prologue on the raw projections, as the Kimi Linear layer applies it
@@ -425,6 +425,100 @@ int kda_oracle_backward(const float *q, const float *k, const float *v, const fl
     free(L);
     free(seg);
     free(ck);
+  }
+  return 0;
+}
+
+/*
+ * General diagonal-plus-low-rank (DPLR) recurrence -- the comparison point the
+ * GeekNews "Kimi Linear" summary measures KDA against (section "일반 DPLR보다 줄어든
+ * 연산량": KDA and a general DPLR transition both allow fine-grained decay; KDA ties
+ * the transition's two low-rank vectors to the key). The pages do not write the
+ * general form out; the reading taken here is the rank-one diagonal-plus-low-rank
+ * transition with two free vectors a_t, b_t, and a separate key-value write:
+ *
+ *     S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T ,   o_t = S_t^T q_t
+ *
+ * KDA is the case a_t = -beta_t k_t, b_t = alpha_t * k_t (element-wise), with the
+ * written key beta_t k_t.
+ *
+ * Rank-one form used below (no dk x dk matrix is formed):
+ *     w = S_{t-1}^T b_t ;  S_t = Diag(alpha_t) S_{t-1} + a_t w^T + k_t v_t^T ;  o_t = S_t^T q_t
+ * w reads the state before this token's decay. Columns of S evolve independently,
+ * so the same (sequence, head, column block) split as above is exact.
+ *
+ * Layouts as kda_oracle_forward_ex, with a and b laid out like k.
+ */
+int dplr_oracle_forward(const float *q, const float *k, const float *v, const float *a, const float *b,
+                        const float *log_alpha, const double *initial_state, const int64_t *seq_starts,
+                        int num_seqs, int H, int dk, int dv, const int *heads, int n_heads_sel, int col_begin,
+                        int col_end, double *o_sel, double *final_sel, int num_threads) {
+  if (!q || !k || !v || !a || !b || !log_alpha || !seq_starts) return -1;
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (col_begin < 0 || col_end > dv || col_begin > col_end) return -1;
+  if (heads == NULL) n_heads_sel = H;
+  if (n_heads_sel <= 0) return -1;
+  for (int n = 0; n < num_seqs; ++n)
+    if (seq_starts[n + 1] < seq_starts[n]) return -1;
+  const int ncols = col_end - col_begin;
+  if (ncols == 0 || num_seqs == 0) return 0;
+  const int nblk = (ncols + ORACLE_COL_BLOCK - 1) / ORACLE_COL_BLOCK;
+  const long long ntask = (long long)num_seqs * n_heads_sel * nblk;
+
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (long long task = 0; task < ntask; ++task) {
+    const int blk = (int)(task % nblk);
+    const int hs = (int)((task / nblk) % n_heads_sel);
+    const int n = (int)(task / ((long long)nblk * n_heads_sel));
+    const int h = heads ? heads[hs] : hs;
+    const int c0 = col_begin + blk * ORACLE_COL_BLOCK;
+    const int c1 = (c0 + ORACLE_COL_BLOCK < col_end) ? c0 + ORACLE_COL_BLOCK : col_end;
+    const int w = c1 - c0;
+
+    double *S = (double *)malloc(sizeof(double) * (size_t)dk * w);
+    double wv[ORACLE_COL_BLOCK];
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < w; ++j)
+        S[(size_t)i * w + j] =
+            initial_state ? initial_state[(((size_t)n * H + h) * dk + i) * dv + (c0 + j)] : 0.0;
+
+    for (int64_t t = seq_starts[n]; t < seq_starts[n + 1]; ++t) {
+      const size_t rk = ((size_t)t * H + h) * dk;
+      const size_t rv = ((size_t)t * H + h) * dv;
+      /* w = S_{t-1}^T b_t: the low-rank read of the previous state */
+      for (int j = 0; j < w; ++j) wv[j] = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        const double bi = (double)b[rk + i];
+        for (int j = 0; j < w; ++j) wv[j] += bi * S[(size_t)i * w + j];
+      }
+      /* S_t = Diag(alpha_t) S_{t-1} + a_t w^T + k_t v_t^T */
+      for (int i = 0; i < dk; ++i) {
+        const double al = exp((double)log_alpha[rk + i]);
+        const double ai = (double)a[rk + i], ki = (double)k[rk + i];
+        for (int j = 0; j < w; ++j)
+          S[(size_t)i * w + j] = al * S[(size_t)i * w + j] + ai * wv[j] + ki * (double)v[rv + c0 + j];
+      }
+      /* o_t = S_t^T q_t */
+      if (o_sel) {
+        double acc[ORACLE_COL_BLOCK];
+        for (int j = 0; j < w; ++j) acc[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          const double qi = (double)q[rk + i];
+          for (int j = 0; j < w; ++j) acc[j] += qi * S[(size_t)i * w + j];
+        }
+        double *orow = o_sel + ((size_t)t * n_heads_sel + hs) * ncols + (c0 - col_begin);
+        for (int j = 0; j < w; ++j) orow[j] = acc[j];
+      }
+    }
+    if (final_sel)
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < w; ++j)
+          final_sel[(((size_t)n * n_heads_sel + hs) * dk + i) * ncols + (c0 - col_begin) + j] =
+              S[(size_t)i * w + j];
+    free(S);
   }
   return 0;
 }

@@ -83,3 +83,63 @@ def gated_deltanet(q, k, v, log_gate, beta, S0=None):
         S = np.exp(log_gate[t]) * (I - beta[t] * np.outer(k[t], k[t])) @ S + beta[t] * np.outer(k[t], v[t])
         o[t] = S.T @ q[t]
     return o, S
+
+
+def dplr_transition(a, b, log_alpha):
+    """N_t = Diag(alpha_t) + a_t b_t^T, the general rank-one diagonal-plus-low-rank
+    transition (GeekNews "Kimi Linear" summary, section "일반 DPLR보다 줄어든 연산량")."""
+    a, b = (np.asarray(x, dtype=np.float64) for x in (a, b))
+    return np.diag(np.exp(np.asarray(log_alpha, np.float64))) + np.outer(a, b)
+
+
+def dplr_dense_closed_form(q, k, v, a, b, log_alpha, S0=None):
+    """Explicit product of dense DPLR transitions for one sequence of one head:
+
+        S_t = (N_t ... N_1) S_0 + sum_{s<=t} (N_t ... N_{s+1}) k_s v_s^T ,  o_t = S_t^T q_t.
+
+    q, k, a, b, log_alpha: [T, dk]; v: [T, dv]. Tiny inputs only. Returns o, S_T."""
+    q, k, v, a, b, log_alpha = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b, log_alpha))
+    T, dk = k.shape
+    dv = v.shape[1]
+    S0 = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, dtype=np.float64)
+    Ns = [dplr_transition(a[t], b[t], log_alpha[t]) for t in range(T)]
+
+    def prod(hi, lo):  # N_hi ... N_lo (empty product = I), 0-based inclusive
+        P = np.eye(dk)
+        for j in range(lo, hi + 1):
+            P = Ns[j] @ P
+        return P
+
+    o = np.zeros((T, dv))
+    S = S0.copy()
+    for t in range(T):
+        S = prod(t, 0) @ S0
+        for s in range(t + 1):
+            S = S + prod(t, s + 1) @ np.outer(k[s], v[s])
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def gated_linear_attention(q, k, v, log_alpha, S0=None):
+    """Per-channel gated linear attention written as an explicit double sum (the
+    DPLR recurrence with a zero low-rank term):
+
+        o_t = sum_{s<=t} v_s sum_c q_tc k_sc e^{g_tc - g_sc} + S_0^T (q_t * e^{g_t}) ,
+        g_t = sum_{j<=t} log_alpha_j.
+
+    q, k, log_alpha: [T, dk]; v: [T, dv]. Returns o and S_T = Diag(e^{g_T}) S_0 +
+    sum_s (k_s * e^{g_T - g_s}) v_s^T."""
+    q, k, v, log_alpha = (np.asarray(x, dtype=np.float64) for x in (q, k, v, log_alpha))
+    T, dk = k.shape
+    dv = v.shape[1]
+    S0 = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, dtype=np.float64)
+    g = np.cumsum(log_alpha, axis=0)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        o[t] = S0.T @ (q[t] * np.exp(g[t]))
+        for s in range(t + 1):
+            o[t] += np.sum(q[t] * k[s] * np.exp(g[t] - g[s])) * v[s]
+    S = np.exp(g[T - 1])[:, None] * S0 if T else S0.copy()
+    for s in range(T):
+        S = S + np.outer(k[s] * np.exp(g[T - 1] - g[s]), v[s])
+    return o, S

@@ -9,7 +9,7 @@ import os
 
 import numpy as np
 
-from .build import build_oracle, oracle_lib_path
+from .build import build_oracle, oracle_lib_path, oracle_source_path
 
 _lib = None
 
@@ -23,7 +23,7 @@ def load_library(path=None):
     own = path is None
     if own:
         path = oracle_lib_path()
-        if not os.path.exists(path):
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(oracle_source_path()):
             build_oracle()
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
@@ -39,6 +39,8 @@ def load_library(path=None):
     lib.kda_oracle_decode_step_ex.restype = I
     lib.kda_oracle_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P, I]
     lib.kda_oracle_backward.restype = I
+    lib.dplr_oracle_forward.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P, P, I]
+    lib.dplr_oracle_forward.restype = I
     lib.kda_oracle_abi_version.restype = I
     if own:
         _lib = lib
@@ -183,3 +185,48 @@ def backward(q, k, v, log_alpha, beta, d_o=None, initial_state=None, d_final=Non
     if rc != 0:
         raise ValueError(f"kda_oracle_backward rejected its arguments (status {rc})")
     return out
+
+
+def dplr_forward(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None, heads=None, cols=None,
+                 num_threads=None, want_o=True, want_final=True, lib=None):
+    """Sequential fp64 general-DPLR recurrence over every sequence:
+
+        S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T ,   o_t = S_t^T q_t
+
+    (the comparison point of the GeekNews "Kimi Linear" summary, section "일반 DPLR보다
+    줄어든 연산량"). q, k, a, b, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; the rest
+    as ``forward``. Returns (o, final) in float64.
+    """
+    lib = lib or load_library()
+    q, k, v, a, b, log_alpha = map(_f32, (q, k, v, a, b, log_alpha))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for x in (k, a, b, log_alpha):
+        assert x.shape == q.shape
+    assert v.shape == (B, T, H, dv)
+    if cu_seqlens is None:
+        starts = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        assert B == 1
+        starts = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int64)
+        assert starts[0] == 0 and starts[-1] == T
+    N = len(starts) - 1
+    if heads is None:
+        heads_arr, nh = None, H
+    else:
+        heads_arr = np.ascontiguousarray(np.asarray(heads), dtype=np.int32)
+        assert heads_arr.min() >= 0 and heads_arr.max() < H
+        nh = len(heads_arr)
+    c0, c1 = (0, dv) if cols is None else cols
+    s0 = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(initial_state, dtype=np.float64)
+        assert s0.shape == (N, H, dk, dv)
+    o = np.zeros((B, T, nh, c1 - c0), dtype=np.float64) if want_o else None
+    fin = np.zeros((N, nh, dk, c1 - c0), dtype=np.float64) if want_final else None
+    rc = lib.dplr_oracle_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), _ptr(s0), _ptr(starts),
+        N, H, dk, dv, _ptr(heads_arr), nh, c0, c1, _ptr(o), _ptr(fin), num_threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"dplr_oracle_forward rejected its arguments (status {rc})")
+    return o, fin
