@@ -291,6 +291,51 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_
   return ok();
 }
 
+size_t kda_dplr_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int dtype) {
+  const bool varlen = num_seqs > 0 && B == 1;
+  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, 64, dtype) != KDA_OK) return 0;
+  return kda::dplr_workspace_bytes(B, T, H, num_seqs, varlen, dtype);
+}
+
+int kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const void* b,
+                       const float* log_alpha, const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                       void* o, float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: the DPLR forward supports 64 only", chunk);
+  int st = check_prefill(B, T, H, num_seqs, varlen, dk, dv, chunk, dtype);
+  if (st != KDA_OK) return st;
+  const int64_t tokens = (int64_t)B * T;
+  if (tokens > 0 && (!q || !k || !v || !a || !b || !log_alpha || !o))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, a, b, log_alpha and o must be non-null when B*T > 0");
+  const void* ptrs[] = {q, k, v, a, b, log_alpha, o, initial_state, final_state};
+  const char* names[] = {"q", "k", "v", "a", "b", "log_alpha", "o", "initial_state", "final_state"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+  if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const int N = varlen ? num_seqs : B;
+  if (N == 0) return ok();
+  const size_t need = kda::dplr_workspace_bytes(B, T, H, num_seqs, varlen, dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+  }
+  hipError_t e = kda::launch_dplr(dtype, q, k, v, a, b, log_alpha, initial_state, cu_seqlens, num_seqs, o,
+                                  final_state, B, T, H, ws, s);
+  if (!workspace) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "DPLR launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                   const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
                   float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* workspace,

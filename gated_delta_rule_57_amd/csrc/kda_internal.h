@@ -58,6 +58,13 @@ struct PrefillWs {
   size_t off_chunk_off, off_info, off_records, total;
 };
 PrefillWs prefill_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype);
+// The same layout for records of record_bytes each.
+PrefillWs plan_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int chunk, size_t record_bytes);
+
+// The chunk plan: per-sequence first chunk (chunk_off [N+1]) and per-chunk (first
+// token, length) (info [mc]) for chunks of the given length.
+hipError_t launch_plan(const int32_t* cu_seqlens, int N, int T, int total_tokens, int chunk, int64_t mc,
+                       int32_t* chunk_off, int2* info, hipStream_t stream);
 
 // Chunk length of the backward pass.
 constexpr int BWD_CHUNK = 16;
@@ -85,5 +92,12 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
 hipError_t launch_forward_records(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
                                   const float* beta, const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
                                   void* workspace, hipStream_t stream);
+
+// The general diagonal-plus-low-rank forward (see kda_dplr_chunk_fwd in
+// include/kda.h), 64-token chunks.
+size_t dplr_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int dtype);
+hipError_t launch_dplr(int dtype, const void* q, const void* k, const void* v, const void* a, const void* b,
+                       const float* log_alpha, const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                       void* o, float* final_state, int B, int T, int H, void* workspace, hipStream_t stream);
 
 }  // namespace kda

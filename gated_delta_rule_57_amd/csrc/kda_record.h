@@ -25,4 +25,36 @@ struct Rec {
   static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
 };
 
+// Per-(chunk, head) record of the general diagonal-plus-low-rank recurrence
+// S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T, element offsets. The first
+// five fields play the roles of the KDA record's, so the state pass reads them the
+// same way (W below is the matrix of rows w_r = S_{r-1}^T b_r, which takes the
+// place of U~):
+//   WN   W_b = T (B e^{G^-})       W = U + W_b S_0
+//   QT   Q e^G                      O = Q e^G S_0 + P W + M_qk V
+//   KE   (A e^{g_C-G})^T            S_C = e^{g_C} S_0 + KE W + KV V
+//   PP   P = M_qa
+//   UU   U = T M_bk V
+// and three more:
+//   KV   (K e^{g_C-G})^T            [8][NKC][64][8]
+//   VB   V as B fragments           [8 column slabs][NKC][64][8]
+//   OI   M_qk V                     [C][128] row-major
+template <typename E, int C>
+struct RecD {
+  static constexpr int NRT = C / 16;
+  static constexpr int NKC = (C + 31) / 32;
+  static constexpr int FR = 64 * 8;
+  static constexpr size_t WN = 0;
+  static constexpr size_t QT = WN + (size_t)NRT * 4 * FR;
+  static constexpr size_t KE = QT + (size_t)NRT * 4 * FR;
+  static constexpr size_t PP = KE + (size_t)8 * NKC * FR;
+  static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;
+  static constexpr size_t KV = UU + (size_t)NRT * 8 * 64 * 4;
+  static constexpr size_t VB = KV + (size_t)8 * NKC * FR;
+  static constexpr size_t OI = VB + (size_t)8 * NKC * FR;
+  static constexpr size_t END = OI + (size_t)C * D;
+  static constexpr size_t GAMMA_BYTES = al256(END * sizeof(E));
+  static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
+};
+
 }  // namespace kda

@@ -25,7 +25,7 @@ KDA_ERR_DEVICE = -4
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused", "kda_decode_step_fused",
            "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read", "kda_chunk_bwd_workspace_size",
-           "kda_chunk_bwd")
+           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd")
 
 KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm", "bwd_local", "bwd_state",
                 "bwd_chunk")  # KDA_KERNEL_* ids
@@ -77,6 +77,10 @@ def _load():
     lib.kda_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I]
     lib.kda_chunk_bwd.restype = I
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.kda_dplr_chunk_fwd_workspace_size.restype = Z
+    lib.kda_dplr_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I]
+    lib.kda_dplr_chunk_fwd.restype = I
+    lib.kda_dplr_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.kda_timing_enable.restype = I
     lib.kda_timing_enable.argtypes = [I]
     lib.kda_timing_read.restype = I
@@ -282,6 +286,55 @@ def chunk_bwd(q, k, v, log_alpha, beta, grad_o, initial_state=None, grad_final_s
         _ptr(out["grad_k"]), _ptr(out["grad_v"]), _ptr(out["grad_log_alpha"]), _ptr(out["grad_beta"]),
         _ptr(out["grad_initial_state"]), B, T, H, dk, dv, dcode, _ptr(workspace), ws_bytes, _stream(q.device)))
     return out
+
+
+def dplr_workspace_size(B, T, H, num_seqs=0, dtype=KDA_BF16) -> int:
+    return int(lib.kda_dplr_chunk_fwd_workspace_size(B, T, H, num_seqs, dtype))
+
+
+def dplr_chunk_fwd(q, k, v, a, b, log_alpha, initial_state=None, cu_seqlens=None, output_final_state=True,
+                   o=None, final_state=None, workspace=None, chunk=64):
+    """Chunked forward of the general DPLR recurrence
+    S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, through
+    ``kda_dplr_chunk_fwd``. q, k, a, b: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or
+    fp32, all the same); log_alpha: [B, T, H, 128] fp32; initial_state,
+    cu_seqlens as ``chunk_fwd``. Returns (o, final_state or None)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dcode = _dtype_code(q)
+    for t, name in ((q, "q"), (k, "k"), (a, "a"), (b, "b")):
+        _need(t, name, dt, (B, T, H, dk))
+    _need(v, "v", dt, (B, T, H, dv))
+    _need(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    else:
+        _need(o, "o", dt, (B, T, H, dv))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        ws_bytes = workspace.numel()
+    _check(lib.kda_dplr_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), _ptr(initial_state), _ptr(cu_seqlens),
+        N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
+        _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, final_state
 
 
 def decode_step(q, k, v, log_alpha, beta, state, o=None, fusion=None):

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Element type of q, k, v and o. */
 typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
@@ -242,8 +242,39 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd, kda_chunk_bwd
- * and kda_decode_step call records HIP events on its stream before its first kernel
+ * Chunked forward of the general diagonal-plus-low-rank (DPLR) recurrence, the
+ * comparison point the GeekNews "Kimi Linear" summary measures KDA's chunk kernel
+ * against (section "일반 DPLR보다 줄어든 연산량": KDA ties the DPLR transition's two
+ * low-rank vectors to the key, which halves the secondary C x C matrices per chunk
+ * and removes three matrix products). The pages do not write the general form out;
+ * this is the rank-one reading, per sequence and head, token by token:
+ *
+ *     S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T ,   o_t = S_t^T q_t
+ *
+ * KDA is the case a_t = -beta_t k_t, b_t = alpha_t * k_t with written key beta_t k_t.
+ *
+ *   q, k, a, b   [B, T, H, dk]  dtype
+ *   v, o         [B, T, H, dv]  dtype (o written)
+ *   log_alpha    [B, T, H, dk]  float32, alpha_t = exp(log_alpha_t)
+ *   initial_state, final_state, cu_seqlens, num_seqs, B, T, H, dk, dv, dtype,
+ *   workspace, stream: as kda_chunk_fwd, with kda_dplr_chunk_fwd_workspace_size().
+ *   chunk        64 only (KDA_ERR_UNSUPPORTED otherwise).
+ * Alignment: 16 bytes for every tensor except cu_seqlens (4). o must not alias an
+ * input; final_state may equal initial_state. Value preconditions (documented,
+ * not checked): log_alpha finite and <= 0, and the transitions keep the state
+ * finite. Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_WORKSPACE or KDA_ERR_DEVICE. Timing ids as kda_chunk_fwd (plan, intra,
+ * inter).
+ */
+size_t kda_dplr_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int dtype);
+int kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                       const float *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
+                       int num_seqs, void *o, float *final_state, int B, int T, int H, int dk, int dv,
+                       int chunk, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-kernel timing, a tracing aid. While enabled, every kda_chunk_fwd, kda_chunk_bwd,
+ * kda_dplr_chunk_fwd and kda_decode_step call records HIP events on its stream before its first kernel
  * and after each kernel it launches, so the durations are measured on the stream
  * the kernels run on (the fused variants and kda_output_norm_gate included). Kernel
  * ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA (intra-chunk), KDA_KERNEL_INTER

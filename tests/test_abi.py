@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     version = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.kda_abi_version() == version == 3
+    assert L.kda_abi_version() == version == 4
     for st in (0, -1, -2, -3, -4):
         assert L.kda_status_string(st).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(7)
@@ -240,3 +240,46 @@ def test_bwd_workspace_size():
     assert kda.bwd_workspace_size(1, 4096, 16, dtype=kda.KDA_FP32) > n
     assert kda.bwd_workspace_size(1, 4096, 16, num_seqs=3) >= n
     assert kda.bwd_workspace_size(1, 64, 0) == 0
+
+
+def dplr_call(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, la=FAKE, s0=None, cu=None, num_seqs=0, o=FAKE, fin=None,
+              B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0, ws=None, ws_bytes=0):
+    return L.kda_dplr_chunk_fwd(q, k, v, a, b, la, s0, cu, num_seqs, o, fin, B, T, H, dk, dv, chunk, dtype, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(a=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(b=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(la=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(a=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(b=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(fin=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(ws=FAKE, ws_bytes=16), kda.KDA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 40), kda.KDA_ERR_INVALID_ARG),
+])
+def test_dplr_rejects(kw, status):
+    assert dplr_call(**kw) == status
+    assert L.kda_last_error()
+
+
+def test_dplr_empty_batch_is_ok_without_device():
+    assert dplr_call(B=0, T=0) == kda.KDA_OK
+    assert dplr_call(cu=FAKE, num_seqs=0, T=0) == kda.KDA_OK
+
+
+def test_dplr_workspace_size():
+    # one record of about 120 KiB (bf16) per (64-token chunk, head) dominates
+    n = kda.dplr_workspace_size(1, 4096, 16)
+    assert n >= 4096 // 64 * 16 * 120 * 1024
+    assert kda.dplr_workspace_size(1, 4096, 16, dtype=kda.KDA_FP32) > n
+    assert kda.dplr_workspace_size(1, 4096, 16, num_seqs=3) >= n
+    assert kda.dplr_workspace_size(1, 64, 0) == 0
+    assert kda.dplr_workspace_size(1, 64, 2) > kda.workspace_size(1, 64, 2)
