@@ -52,6 +52,10 @@ BWD_BYTES_PER_TOK_HEAD = {
 # bytes any backward must move per (token, head): q, k, v, grad_o, log_alpha, beta in; the five gradients out
 BWD_PATH_BYTES_PER_TOK_HEAD = 4 * 2 * D + 4 * D + 4 + 3 * 2 * D + 4 * D + 4
 
+# general DPLR forward (64-token chunks, bf16): per (chunk, head) record of 123392 B
+DPLR_RECORD_BYTES_BF16 = 123392
+DPLR_IN_BYTES_PER_TOK_HEAD = 5 * 2 * D + 4 * D   # q, k, v, a, b bf16, log_alpha fp32
+
 PREFILL_T, PREFILL_H = 131072, 32
 DEC_N, DEC_H = 256, 32
 
@@ -214,6 +218,58 @@ def gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec, runs=5):
     return out
 
 
+def dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=(4096, 16384, 65536, 131072), runs=3):
+    """KDA's chunked forward against the general DPLR chunked forward
+    (kda_dplr_chunk_fwd) on the same shapes: H = 32, d = 128, bf16, 64-token chunks,
+    over input lengths. Prefixes of one 131072-token input set per method (KDA: the
+    headline workload; DPLR: the stable tied recipe with the same mixed decays).
+    Times are the library's per-kernel events (plan + intra + inter)."""
+    B, Tmax, H = pre.q.shape[:3]
+    x = inputs.make_dplr(3, B=1, T=Tmax, H=H, dtype="bf16", la_mode="mixed", device=dev)
+    ws_d = torch.empty(kda.dplr_workspace_size(1, Tmax, H, 0, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(pre.v)
+    fin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        kda.timing_enable(True)
+        for _ in range(runs):
+            fn()
+        torch.cuda.synchronize()
+        t = kda.timing_read()
+        kda.timing_enable(False)
+        ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items() if cnt}
+        return {n: ms.get(n, 0.0) for n in ("plan", "intra", "inter")}
+
+    rows = []
+    for T in lengths:
+        if T > Tmax:
+            continue
+        sl = lambda t: t[:, :T]
+        km = timed(lambda: kda.chunk_fwd(sl(pre.q), sl(pre.k), sl(pre.v), sl(pre.log_alpha), sl(pre.beta),
+                                         chunk=CHUNK, o=o[:, :T], final_state=fin, workspace=ws))
+        dm = timed(lambda: kda.dplr_chunk_fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.a), sl(x.b), sl(x.log_alpha),
+                                              o=o[:, :T], final_state=fin, workspace=ws_d))
+        kt, dt = sum(km.values()), sum(dm.values())
+        tok_heads = T * H
+        d_intra_bytes = tok_heads * DPLR_IN_BYTES_PER_TOK_HEAD + (T // CHUNK) * H * DPLR_RECORD_BYTES_BF16
+        d_inter_bytes = (T // CHUNK) * H * DPLR_RECORD_BYTES_BF16 + tok_heads * 2 * D
+        rows.append({"T": T, "kda_ms": round(kt, 4), "dplr_ms": round(dt, 4),
+                     "dplr_over_kda": round(dt / kt, 3),
+                     "kda_tokens_per_s": round(T / (kt * 1e-3), 1), "dplr_tokens_per_s": round(T / (dt * 1e-3), 1),
+                     "kda_kernel_ms": {n: round(v, 4) for n, v in km.items()},
+                     "dplr_kernel_ms": {n: round(v, 4) for n, v in dm.items()},
+                     "dplr_intra_GBps": round(d_intra_bytes / (dm["intra"] * 1e-3) / 1e9, 1),
+                     "dplr_inter_GBps": round(d_inter_bytes / (dm["inter"] * 1e-3) / 1e9, 1)})
+        print(f"[bench] T={T}: kda {kt:.3f} ms, dplr {dt:.3f} ms ({dt / kt:.2f}x)", file=sys.stderr, flush=True)
+    del x, ws_d, o, fin
+    torch.cuda.empty_cache()
+    return {"workload": "kda_vs_dplr_H32_bf16_c64 (prefill at several lengths; the general DPLR transition "
+                        "Diag(alpha) + a b^T with free a, b against KDA's key-tied one)",
+            "lengths": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +285,8 @@ def main():
                     help="skip the timing of the fused layer core (prologue and epilogue in the kernels)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timing of the backward (kda_chunk_bwd) on the prefill shape")
+    ap.add_argument("--no-dplr", action="store_true",
+                    help="skip the KDA versus general-DPLR forward comparison over input lengths")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of 1 GiB (for counter calibration) and exit")
     args = ap.parse_args()
@@ -362,6 +420,8 @@ def main():
         result["gates"] = gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec)
     if not args.no_backward:
         result["backward"] = backward_timing(inputs, kda, torch, pre)
+    if not args.no_dplr:
+        result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, ws)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)

@@ -66,3 +66,14 @@ def test_bench_backward_byte_counts_match_the_workspace_layout():
     bwd = kda.bwd_workspace_size(1, T, H)
     assert abs(fwd / (mc * H) - 22016) < 1
     assert (bwd - fwd) == mc * H * (13312 + 2 * 32768 + 2 * 4096)
+
+
+def test_bench_record_byte_counts_match_the_workspace_queries():
+    """The per-(64-token chunk, head) record sizes behind bench.py's KDA and DPLR
+    byte counts agree with the library's workspace queries."""
+    import bench
+    from gated_delta_rule_57_amd import kda
+    T, H = 4096, 16
+    mc = T // bench.CHUNK
+    assert abs(kda.workspace_size(1, T, H, chunk=64) / (mc * H) - bench.RECORD_BYTES_BF16_C64) < 1
+    assert abs(kda.dplr_workspace_size(1, T, H) / (mc * H) - bench.DPLR_RECORD_BYTES_BF16) < 1
