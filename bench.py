@@ -287,6 +287,8 @@ def main():
                     help="skip the timing of the backward (kda_chunk_bwd) on the prefill shape")
     ap.add_argument("--no-dplr", action="store_true",
                     help="skip the KDA versus general-DPLR forward comparison over input lengths")
+    ap.add_argument("--dplr-lengths", default="4096,16384,65536,131072",
+                    help="comma-separated sequence lengths of the DPLR comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of 1 GiB (for counter calibration) and exit")
     args = ap.parse_args()
@@ -421,7 +423,8 @@ def main():
     if not args.no_backward:
         result["backward"] = backward_timing(inputs, kda, torch, pre)
     if not args.no_dplr:
-        result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, ws)
+        lengths = tuple(int(x) for x in args.dplr_lengths.split(",") if x)
+        result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=lengths)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)

@@ -13,7 +13,8 @@ Kernel names are shortened to the library's kernel ids (plan, intra, inter, deco
 outnorm, bwd_local, bwd_state, bwd_chunk); the intra-chunk kernel's scalar-gate and
 no-decay instantiations become intra_gdn and intra_deltanet, its 16-token-chunk
 instantiation (the backward's forward pass) intra16, and the 16-token state
-kernel inter16.
+kernel inter16. The general-DPLR forward's kernels are dplr_intra and dplr_inter
+(the inter kernels instantiated with their DPLR flag set).
 The traffic summary records a hash of the kernel sources it was taken on; bench.py
 reports the traffic only while that hash matches the sources.
 """
@@ -25,7 +26,8 @@ import os
 import re
 import sys
 
-KERNELS = (("plan_kernel", "plan"), ("intra_kernel", "intra"), ("inter_wg_kernel", "inter"),
+KERNELS = (("plan_kernel", "plan"), ("dplr_intra_kernel", "dplr_intra"), ("intra_kernel", "intra"),
+           ("inter_wg_kernel", "inter"),
            ("inter16_kernel", "inter16"), ("fwd_state_kernel", "inter16"), ("inter_kernel", "inter"), ("decode_kernel", "decode"),
            ("output_norm_gate_kernel", "outnorm"), ("bwd_local_kernel", "bwd_local"),
            ("bwd_state_kernel", "bwd_state"), ("bwd_chunk_kernel", "bwd_chunk"))
@@ -59,6 +61,8 @@ def short_name(name):
                 gate = (m.group(2) or m.group(4)) if m else None
                 base = {"1": "intra_gdn", "2": "intra_deltanet"}.get(gate, "intra")
                 return base + "16" if chunk == "16" else base
+            if short == "inter" and (re.search(r"inter_w?g?_?kernelI\w*?Lb1E", name) or "true>" in name):
+                return "dplr_inter"
             return short
     return None
 

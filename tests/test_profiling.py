@@ -24,6 +24,12 @@ def test_short_names_split_intra_by_gate():
     assert s("_ZN3kda12_GLOBAL__N_116bwd_chunk_kernelIDF16bEEvPKT_") == "bwd_chunk"
     assert s("_ZN3kda12_GLOBAL__N_116bwd_state_kernelIDF16bEEvPKc") == "bwd_state"
     assert s("_ZN3kda12_GLOBAL__N_116fwd_state_kernelIDF16bEEvPKc") == "inter16"
+    assert s("_ZN3kda15inter_wg_kernelILi1ELb0EEEvPKcPKiS4_iiPKfPfPDF16biii") == "inter"
+    assert s("_ZN3kda15inter_wg_kernelILi1ELb1EEEvPKcPKiS4_iiPKfPfPDF16biii") == "dplr_inter"
+    assert s("_ZN3kda12inter_kernelIfLi64ELb1EEEvPKcPKiPK15HIP_vector_typeIiLj2EE") == "dplr_inter"
+    assert s("_ZN3kda12inter_kernelIfLi64ELb0EEEvPKcPKiPK15HIP_vector_typeIiLj2EE") == "inter"
+    assert s("void kda::inter_wg_kernel<1, true>(char const*)") == "dplr_inter"
+    assert s("_ZN3kda17dplr_intra_kernelIDF16bEEvPKT_S3_S3_S3_S3_PKfPKiPK15HIP_vector_typeIiLj2EEiiPc") == "dplr_intra"
     assert s("_ZN3kda12_GLOBAL__N_116bwd_local_kernelIDF16bEEvPKT_") == "bwd_local"
 
 
