@@ -41,6 +41,8 @@ namespace kda {
 namespace {
 
 constexpr int DC = 64;                      // chunk length
+constexpr int DWAVES = 8;                   // waves per intra-chunk work-group
+constexpr int DTHREADS = 64 * DWAVES;
 constexpr float DP_LOG2E = 1.4426950408889634f;
 constexpr float DP_RANGE_LIMIT = 120.f;     // log2 units
 
@@ -95,10 +97,12 @@ __device__ __forceinline__ void block_of(int idx, int& I, int& J) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: one work-group (4 waves) per (chunk, head). Thread t owns
-// channels 4 (t & 31) .. + 3 of rows (t >> 5) + 8 i in the element-wise phases.
-// The four C x C matrices are computed transposed, one 16 x 16 block (I, J <= I)
-// per wave at a time (lane (m, g), element ii = entry (16 I + m, 16 J + 4 g + ii)).
+// Intra-chunk kernel: one work-group of 8 waves per (chunk, head); its LDS plan
+// allows one work-group per CU, so the eight waves (two per SIMD) are what hides
+// latency. Thread t owns channels 4 (t & 31) .. + 3 of rows (t >> 5) + 16 i in the
+// element-wise phases. The four C x C matrices are computed transposed, one
+// 16 x 16 block (I, J <= I) per wave at a time (lane (m, g), element ii = entry
+// (16 I + m, 16 J + 4 g + ii)); wave w takes value columns 16 w .. 16 w + 15 in B3.
 // Phases (barriers in between):
 //   P1  loads of q, k, v, a, b and log_alpha; log2 cumulative sum, sub-chunk
 //       boundaries and block scales, range flags
@@ -111,7 +115,7 @@ __device__ __forceinline__ void block_of(int idx, int& I, int& J) {
 //       U = T (M_bk V) to the record
 // ---------------------------------------------------------------------------
 template <typename E>
-__global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                          const E* __restrict__ v, const E* __restrict__ a,
                                                          const E* __restrict__ b, const float* __restrict__ log_alpha,
                                                          const int32_t* __restrict__ total_chunks,
@@ -122,8 +126,9 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   typedef typename Frag<E>::T FragT;
   typedef typename Vec4<E>::T V4;
   constexpr int C = DC, NSUB = SM::NSUB, LD = SM::LD, GLD = SM::GLD, LDC = SM::LDC, LDK = SM::LDK;
-  constexpr int NRT = C / 16, NKC = C / 32, RPT = C / 8;
-  constexpr int NBLK = SM::NBLK, BPW = (NBLK + 3) / 4;
+  constexpr int NRT = C / 16, NKC = C / 32, RG = DTHREADS / 32, RPT = C / RG;
+  constexpr int NBLK = SM::NBLK, BPW = (NBLK + DWAVES - 1) / DWAVES;
+  static_assert(DWAVES == D / 16, "B3 gives each wave one 16-column slab");
 
   __shared__ __attribute__((aligned(16))) char smem[SM::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + SM::G);
@@ -148,7 +153,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   floatx4 la[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
+    const int r = rbase + RG * i;
     const size_t off = (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D + ch0;
     la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
     qv[i] = *reinterpret_cast<const V4*>(q + off);
@@ -157,32 +162,30 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     av[i] = *reinterpret_cast<const V4*>(a + off);
     bv[i] = *reinterpret_cast<const V4*>(b + off);
   }
-  auto val = [&](const V4& x, int i, int j) { return rbase + 8 * i < len ? to_f(x[j]) : 0.f; };
+  auto val = [&](const V4& x, int i, int j) { return rbase + RG * i < len ? to_f(x[j]) : 0.f; };
   if (t < NSUB) sFlag[t] = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
+    const int r = rbase + RG * i;
     *reinterpret_cast<floatx4*>(sG + r * GLD + ch0) = r < len ? la[i] * DP_LOG2E : floatx4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
-  {  // cumulative sum over the rows per channel: two halves, then a carry
-    const int chn = t & 127, half = t >> 7;
-    constexpr int HR = C / 2;
-    float x[HR];
+  {  // cumulative sum over the rows per channel: NP row ranges, then the carries
+    constexpr int NP = DTHREADS / D, PR = C / NP;
+    const int chn = t & (D - 1), part = t / D;
+    float x[PR];
 #pragma unroll
-    for (int r = 0; r < HR; ++r) x[r] = sG[(half * HR + r) * GLD + chn];
+    for (int r = 0; r < PR; ++r) x[r] = sG[(part * PR + r) * GLD + chn];
 #pragma unroll
-    for (int r = 1; r < HR; ++r) x[r] += x[r - 1];
-    if (half == 0) {
+    for (int r = 1; r < PR; ++r) x[r] += x[r - 1];
 #pragma unroll
-      for (int r = 0; r < HR; ++r) sG[r * GLD + chn] = x[r];
-    }
+    for (int r = 0; r < PR; ++r) sG[(part * PR + r) * GLD + chn] = x[r];
     __syncthreads();
-    if (half == 1) {
-      const float carry = sG[(HR - 1) * GLD + chn];
+    float carry = 0.f;
+    for (int p2 = 0; p2 < part; ++p2) carry += sG[(p2 * PR + PR - 1) * GLD + chn];
+    __syncthreads();  // every carry is read before any range is shifted
 #pragma unroll
-      for (int r = 0; r < HR; ++r) sG[(HR + r) * GLD + chn] = x[r] + carry;
-    }
+    for (int r = 0; r < PR; ++r) sG[(part * PR + r) * GLD + chn] = x[r] + carry;
   }
   __syncthreads();
   if (t < D) {
@@ -239,7 +242,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     V4 lbv[RPT], lqv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rbase + 8 * i, I = r >> 4;
+      const int r = rbase + RG * i, I = r >> 4;
       const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
       const floatx4 gx = r > 0 ? *reinterpret_cast<const floatx4*>(sG + (r - 1) * GLD + ch0)
                                : floatx4{0.f, 0.f, 0.f, 0.f};
@@ -265,7 +268,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     __syncthreads();  // every thread has its decays; the row operands overwrite the cumsum
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rbase + 8 * i;
+      const int r = rbase + RG * i;
       *reinterpret_cast<V4*>(sLB + r * LD + ch0) = lbv[i];
       *reinterpret_cast<V4*>(sLQ + r * LD + ch0) = lqv[i];
     }
@@ -274,7 +277,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       aBA[bi] = aBK[bi] = aQA[bi] = aQK[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + 4 * bi;
+      const int idx = w + DWAVES * bi;
       if (idx >= NBLK) break;
       int I, J;
       block_of(idx, I, J);
@@ -307,7 +310,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
       store_pp(I, J, aQA[bi]);
     }
     // (A e^{g_C-G})^T and (K e^{g_C-G})^T: rhs_s 2^(g_C - b_{J+1})
-    for (int it = t; it < D * (C / 4); it += 256) {
+    for (int it = t; it < D * (C / 4); it += DTHREADS) {
       const int ch = it & (D - 1), s0 = 4 * (it >> 7);
       float ae[4], ke[4];
 #pragma unroll
@@ -324,7 +327,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     // ---- P2 (exact) ---------------------------------------------------------------
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rbase + 8 * i;
+      const int r = rbase + RG * i;
       const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
       const floatx4 gx = r > 0 ? *reinterpret_cast<const floatx4*>(sG + (r - 1) * GLD + ch0)
                                : floatx4{0.f, 0.f, 0.f, 0.f};
@@ -344,7 +347,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       aBA[bi] = aBK[bi] = aQA[bi] = aQK[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + 4 * bi;
+      const int idx = w + DWAVES * bi;
       if (idx >= NBLK) break;
       int I, J;
       block_of(idx, I, J);
@@ -376,7 +379,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
       }
       store_pp(I, J, aQA[bi]);
     }
-    for (int it = t; it < D * (C / 4); it += 256) {
+    for (int it = t; it < D * (C / 4); it += DTHREADS) {
       const int ch = it & (D - 1), s0 = 4 * (it >> 7);
       const float gC = sBnd[NSUB * D + ch];
       float ae[4], ke[4];
@@ -392,7 +395,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     }
   }
   // zero halves of the P fragments above the diagonal (J > I)
-  for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
+  for (int zi = t; zi < NRT * 2 * NKC * 64; zi += DTHREADS) {
     const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
     if (J > I) {
       const float z[4] = {0.f, 0.f, 0.f, 0.f};
@@ -413,7 +416,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   // ---- B0: -M_ba (fp32), M_bk, M_qk (E), masked; B e^{G^-} and V -----------------------
 #pragma unroll
   for (int bi = 0; bi < BPW; ++bi) {
-    const int idx = w + 4 * bi;
+    const int idx = w + DWAVES * bi;
     if (idx >= NBLK) break;
     int I, J;
     block_of(idx, I, J);
@@ -433,7 +436,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
+    const int r = rbase + RG * i;
     float vr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vr[j] = val(vv[i], i, j);
@@ -441,7 +444,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
     store4f(sV + r * LD + ch0, vr);
   }
   // T, M_bk and M_qk above the diagonal blocks are zero
-  for (int e = t; e < C * C; e += 256) {
+  for (int e = t; e < C * C; e += DTHREADS) {
     const int r = e / C, s = e % C;
     if ((s >> 4) > (r >> 4)) {
       sTb[r * LDK + s] = from_f<E>(0.f);
@@ -452,7 +455,7 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   __syncthreads();
 
   // ---- B1: diagonal blocks T_II = (I + A_II)^{-1}, A = -M_ba (lane j = column j) -----
-  if (lane < 16) {
+  if (w < NSUB && lane < 16) {
     const int j = lane, o0 = 16 * w;
     float col[16];
 #pragma unroll
@@ -503,60 +506,62 @@ __global__ void __launch_bounds__(256) dplr_intra_kernel(const E* __restrict__ q
   }
 
   // ---- B3a: V fragments and M_qk V to the record; M_bk V in registers ----------------
-  floatx4 yk[2][NRT];
-#pragma unroll
-  for (int cl = 0; cl < 2; ++cl) {
-    const int ct = 2 * w + cl;
+  const int ct = w;  // this wave's 16 value columns
+  floatx4 yk[NRT];
+  {
     FragT bV[NKC];
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb) {
       bV[kb] = frag_colk(sV, LD, 16 * ct + m, 32 * kb, g);
       store_frag<E>(rec + RC::VB + ((size_t)(ct * NKC + kb) * 64 + lane) * 8, bV[kb]);
     }
+    floatx4 ao[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      floatx4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+      yk[rt] = ao[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb <= (rt >> 1); ++kb) {  // both matrices are lower triangular
-        mma(ay, frag_rowk(sMB, LDK, 16 * rt + m, 32 * kb, g), bV[kb]);  // (M_bk V)[16 rt + 4 g + ii][16 ct + m]
-        mma(ao, bV[kb], frag_rowk(sMQ, LDK, 16 * rt + m, 32 * kb, g));  // (M_qk V)[16 rt + m][16 ct + 4 g + ii]
+        mma(yk[rt], frag_rowk(sMB, LDK, 16 * rt + m, 32 * kb, g), bV[kb]);  // (M_bk V)[16 rt + 4 g + ii][16 ct + m]
+        mma(ao[rt], bV[kb], frag_rowk(sMQ, LDK, 16 * rt + m, 32 * kb, g));  // (M_qk V)[16 rt + m][16 ct + 4 g + ii]
       }
-      yk[cl][rt] = ay;
-      const float oo[4] = {ao[0], ao[1], ao[2], ao[3]};
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const float oo[4] = {ao[rt][0], ao[rt][1], ao[rt][2], ao[rt][3]};
       store4f(rec + RC::OI + (size_t)(16 * rt + m) * D + 16 * ct + 4 * g, oo);
     }
   }
   __syncthreads();  // M_bk and M_qk are read; T is complete
 #pragma unroll
-  for (int cl = 0; cl < 2; ++cl)
+  for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sY[(16 * rt + 4 * g + ii) * LD + 16 * (2 * w + cl) + m] = from_f<E>(yk[cl][rt][ii]);
+    for (int ii = 0; ii < 4; ++ii) sY[(16 * rt + 4 * g + ii) * LD + 16 * ct + m] = from_f<E>(yk[rt][ii]);
   __syncthreads();
 
   // ---- B3b: W_b = T (B e^{G^-}) (computed transposed, fragment order) and U = T (M_bk V)
-#pragma unroll
-  for (int cl = 0; cl < 2; ++cl) {
-    const int ct = 2 * w + cl;
+  {
     FragT bK[NKC], bY[NKC];
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb) {
       bK[kb] = frag_colk(sKt, LD, 16 * ct + m, 32 * kb, g);
       bY[kb] = frag_colk(sY, LD, 16 * ct + m, 32 * kb, g);
     }
+    floatx4 aw[NRT], au[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      floatx4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+      aw[rt] = au[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb <= (rt >> 1); ++kb) {  // T is lower triangular
         const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
-        mma(aw, bK[kb], aT);  // lane (m, g): W_b[16 rt + m][16 ct + 4 g + ii]
-        mma(au, aT, bY[kb]);  // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
+        mma(aw[rt], bK[kb], aT);  // lane (m, g): W_b[16 rt + m][16 ct + 4 g + ii]
+        mma(au[rt], aT, bY[kb]);  // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
       }
-      const float wb[4] = {aw[0], aw[1], aw[2], aw[3]};
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const float wb[4] = {aw[rt][0], aw[rt][1], aw[rt][2], aw[rt][3]};
       store4f(rec + RC::WN + ((size_t)(rt * 4 + (ct >> 1)) * 64 + lane) * 8 + 4 * (ct & 1), wb);
-      const float uo[4] = {au[0], au[1], au[2], au[3]};
+      const float uo[4] = {au[rt][0], au[rt][1], au[rt][2], au[rt][3]};
       store4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, uo);
     }
   }
@@ -590,7 +595,7 @@ hipError_t launch_dplr_typed(const void* q, const void* k, const void* v, const 
   trace_mark(stream, 0);
   if (e != hipSuccess) return e;
   if (mc > 0) {
-    hipLaunchKernelGGL(dplr_intra_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
+    hipLaunchKernelGGL(dplr_intra_kernel<E>, dim3((unsigned)(mc * H)), dim3(DTHREADS), 0, stream, (const E*)q,
                        (const E*)k, (const E*)v, (const E*)a, (const E*)b, log_alpha, chunk_off + N, info, H, (int)mc,
                        records);
     e = hipGetLastError();
