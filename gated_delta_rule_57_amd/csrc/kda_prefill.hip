@@ -116,6 +116,28 @@ struct Smem {
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
+// Which 16 x 16 block (I, J <= I) of A and P wave w forms in its bi-th slot. The two
+// blocks J = 2 kb and 2 kb + 1 of a block row I fill one 16-byte fragment slot of P
+// per lane, so they go to the same wave, one after the other, and P leaves the
+// kernel as whole slots (half-slot stores cost the kernel several percent). With
+// four sub-chunks the waves take 3, 3, 2 and 2 blocks, as a round-robin split would.
+template <int NSUB>
+__device__ __forceinline__ bool wave_block(int w, int bi, int& I, int& J) {
+  if constexpr (NSUB == 1) {
+    I = J = 0;
+    return w == 0 && bi == 0;
+  } else {
+    static_assert(NSUB == 4, "block assignment for 16- and 64-token chunks");
+    if (bi < 2) {  // (1,0) (1,1) | (2,0) (2,1) | (3,0) (3,1) | (3,2) (3,3)
+      I = w < 3 ? w + 1 : 3;
+      J = (w < 3 ? 0 : 2) + bi;
+      return true;
+    }
+    I = J = 2 * w;  // (0,0) | (2,2)
+    return bi == 2 && w < 2;
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -299,6 +321,47 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   }
   constexpr int NBLK = SM::NBLK;
   constexpr int BPW = (NBLK + 3) / 4;
+  static_assert(NBLK <= 10, "wave_block covers up to four sub-chunks");
+  // P to the record in whole 16-byte slots: block (I, J) is half of slot (I, J / 2);
+  // an even block waits in p_lo for its odd partner unless it is the last of its row
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  floatx4 p_lo = zero4;
+  auto emit_p = [&](int I, int J, const floatx4& acc) {
+    floatx4 pv;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= 16 * I + m) ? acc[ii] : 0.f;
+    E* dst = rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8;
+    if (J & 1)
+      store_frag<E>(dst, acc_pair_to_frag<E>(p_lo, pv));
+    else if (J == I)
+      store_frag<E>(dst, acc_pair_to_frag<E>(pv, zero4));
+    else
+      p_lo = pv;
+  };
+  // the slots wholly above the diagonal, (0, 1) and (1, 1), from the waves with two blocks
+  auto emit_p_zero_slots = [&]() {
+    if constexpr (NSUB == 4) {
+      if (w >= 2)
+        store_frag<E>(rec + RC::PP + ((size_t)((w - 2) * NKC + 1) * 64 + lane) * 8, acc_pair_to_frag<E>(zero4, zero4));
+    }
+  };
+  // (K e^{g_C - G})^T to the record: item (channel, 4-row group fg, k-block kb) is one
+  // lane's whole slot, rows 32 kb + 4 fg + j and 32 kb + 16 + 4 fg + j; 16 consecutive
+  // items fill 256 contiguous bytes. kval(s, ch) gives the value of chunk row s < C.
+  auto emit_ke = [&](auto kval) {
+    for (int it = t; it < D * NKC * 4; it += 256) {
+      const int ch = it & (D - 1), fg = (it >> 7) & 3, kb = it >> 9;
+      floatx4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s0 = 32 * kb + 4 * fg + j, s1 = s0 + 16;
+        lo[j] = s0 < C ? kval(s0, ch) : 0.f;
+        hi[j] = s1 < C ? kval(s1, ch) : 0.f;
+      }
+      store_frag<E>(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8,
+                    acc_pair_to_frag<E>(lo, hi));
+    }
+  };
   float ktr[RPT][4];
   floatx4 accA[BPW], accP[BPW];
   if constexpr (GATE == GATE_CHANNEL) {
@@ -410,13 +473,10 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     for (int bi = 0; bi < BPW; ++bi) {
       accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
       accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + 4 * bi;
-      if (idx >= NBLK) break;
-      int I = 0;
-      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-      const int J = idx - I * (I + 1) / 2;
+      int I, J;
+      if (!wave_block<NSUB>(w, bi, I, J)) break;
       const int rrow = 16 * I + m, srow = 16 * J + m;
-      const float* scl = sScl + (size_t)idx * D;
+      const float* scl = sScl + (size_t)(I * (I + 1) / 2 + J) * D;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         FragT lk, lq, rhs;
@@ -437,32 +497,11 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
         mma(accA[bi], rhs, lk);
         mma(accP[bi], rhs, lq);
       }
-      const int r = rrow;
-      float pv[4];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
-      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+      emit_p(I, J, accP[bi]);
     }
-    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
-      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
-      if (J > I) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
-      }
-    }
+    emit_p_zero_slots();
     // (K e^{g_C - G})^T = rhs_s 2^(g_C - b_{J+1}) to the record
-    for (int it = t; it < D * (CK / 4); it += 256) {
-      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-      float kv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        kv[j] = (s < C) ? sRR[s * GLD + ch] * sScl[(NBLK + (s >> 4)) * D + ch] : 0.f;
-      }
-      const int kb = s0 >> 5, so = s0 & 31;
-      const int fg = (so & 15) >> 2, fh = so >> 4;
-      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
-    }
+    emit_ke([&](int s, int ch) { return sRR[s * GLD + ch] * sScl[(NBLK + (s >> 4)) * D + ch]; });
   } else {
     // ---- P2 (exact path): Q e^G straight to its fragment slot (4 consecutive channels are half of a
     //          lane's fragment); K e^G kept for B0; raw q, k to LDS ----------------------
@@ -493,11 +532,8 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     for (int bi = 0; bi < BPW; ++bi) {
       accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
       accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + 4 * bi;
-      if (idx >= NBLK) break;
-      int I = 0;
-      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-      const int J = idx - I * (I + 1) / 2;
+      int I, J;
+      if (!wave_block<NSUB>(w, bi, I, J)) break;
       if (J == I && sFlag[I]) {
         // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
         const int r = 16 * I + m;
@@ -542,35 +578,11 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
           mma(accP[bi], rhs, lq);
         }
       }
-      // P to the record: this block is half of fragment (I, J / 2)
-      const int r = 16 * I + m;
-      float pv[4];
-  #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? accP[bi][ii] : 0.f;
-      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+      emit_p(I, J, accP[bi]);
     }
-    // zero halves of the P fragments above the diagonal (J > I, J < 2 NKC)
-    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
-      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
-      if (J > I) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
-      }
-    }
-    // (K e^{g_C - G})^T to the record: thread item = (channel, 4 consecutive chunk rows),
-    // which is half of one lane's fragment
-    for (int it = t; it < D * (CK / 4); it += 256) {
-      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-      float kv[4];
-  #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
-      }
-      const int kb = s0 >> 5, so = s0 & 31;
-      const int fg = (so & 15) >> 2, fh = so >> 4;
-      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
-    }
+    emit_p_zero_slots();
+    // (K e^{g_C - G})^T to the record
+    emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]); });
   }
   } else {
     // ---- scalar gate: one decay per (token, head) (GATE_HEAD), or none (GATE_NONE).
@@ -614,11 +626,8 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     for (int bi = 0; bi < BPW; ++bi) {
       accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
       accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + 4 * bi;
-      if (idx >= NBLK) break;
-      int I = 0;
-      while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-      const int J = idx - I * (I + 1) / 2;
+      int I, J;
+      if (!wave_block<NSUB>(w, bi, I, J)) break;
       const int rrow = 16 * I + m, srow = 16 * J + m;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -640,48 +649,26 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
         mma(accP[bi], rhs, lq);
       }
       const int r = rrow;
-      float pv[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int s = 16 * J + 4 * g + ii;
         const float f = s <= r ? (GATE == GATE_NONE ? 1.f : fast_exp2(sGs[r] - sGs[s])) : 0.f;
         accA[bi][ii] *= f;
         accP[bi][ii] *= f;
-        pv[ii] = accP[bi][ii];
       }
-      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+      emit_p(I, J, accP[bi]);
     }
-    for (int zi = t; zi < NRT * 2 * NKC * 64; zi += 256) {
-      const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
-      if (J > I) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
-      }
-    }
+    emit_p_zero_slots();
     // (K e^{g_C - G})^T to the record
-    for (int it = t; it < D * (CK / 4); it += 256) {
-      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-      float kv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        kv[j] = (s < C) ? to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(gC - sGs[s])) : 0.f;
-      }
-      const int kb = s0 >> 5, so = s0 & 31;
-      const int fg = (so & 15) >> 2, fh = so >> 4;
-      store4f(rec + RC::KE + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, kv);
-    }
+    emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(gC - sGs[s])); });
   }
   __syncthreads();  // phase A buffers are dead from here on
 
   // ---- B0: A (row r scaled by beta_r, strictly lower) to LDS; K e^G and V ----------
 #pragma unroll
   for (int bi = 0; bi < BPW; ++bi) {
-    const int idx = w + 4 * bi;
-    if (idx >= NBLK) break;
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-    const int J = idx - I * (I + 1) / 2;
+    int I, J;
+    if (!wave_block<NSUB>(w, bi, I, J)) break;
     const int r = 16 * I + m;
     const float br = sBeta[r];
     floatx4 a;
