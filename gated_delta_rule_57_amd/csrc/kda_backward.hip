@@ -91,14 +91,6 @@ struct BRec {
   static constexpr size_t BYTES = bal256(GAM + D * 4);
 };
 
-// (row, channel) -> element index in the A fragment of the matrix itself (k = channel)
-__device__ __forceinline__ int afrag_index(int row, int ch) {
-  const int kb = ch >> 5, ko = ch & 31;
-  const int gg = ko < 16 ? ko >> 2 : (ko - 16) >> 2;
-  const int ss = ko < 16 ? ko & 3 : 4 + ((ko - 16) & 3);
-  return (kb * 64 + gg * 16 + row) * 8 + ss;
-}
-
 // Element-wise phases: thread t owns row r = t >> 4. It loads channels
 // c0 .. c0 + 7 (c0 = 8 (t & 15)) from global memory, and computes on channels
 // ch(i) = (t & 15) + 16 i, i = 0..7: the sixteen lanes of a row then touch sixteen
@@ -299,10 +291,19 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
       const float gr = L.G[r][ch];
       wv[i] = from_f<E>(-wacc[i]);
       qv[i] = from_f<E>(L.Q[r][ch] * exp2_hw(gr));
-      kef[afrag_index(r, ch)] = from_f<E>(L.K[r][ch] * exp2_hw(L.G[BC - 1][ch] - gr));
     }
     *reinterpret_cast<V4*>(wt + ((size_t)nt * 64 + lane) * 4) = wv;
     *reinterpret_cast<V4*>(qtt + ((size_t)nt * 64 + lane) * 4) = qv;
+  }
+  {  // K e^{g_C-G} as the A fragment of k-block w: lane (m, g) builds its whole slot (row
+     // m, channels 32 w + koff(g, s)), so each wave writes 1 KiB contiguously
+    FragT kf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int ch = 32 * w + koff(g, s);
+      kf[s] = from_f<E>(L.K[m][ch] * exp2_hw(L.G[BC - 1][ch] - L.G[m][ch]));
+    }
+    store_frag<E>(kef + ((size_t)w * 64 + lane) * 8, kf);
   }
   if (w == 0) {
     V4 pv;
