@@ -88,10 +88,19 @@ struct DSmem {
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-__device__ __forceinline__ void block_of(int idx, int& I, int& J) {
-  I = 0;
-  while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-  J = idx - I * (I + 1) / 2;
+// Which 16 x 16 block (I, J <= I) of the four C x C matrices wave w forms in its
+// bi-th slot (bi < 2). The blocks J = 2 kb and 2 kb + 1 of a block row fill one
+// 16-byte slot of P per lane, so they go to the same wave and P leaves as whole
+// slots: waves 0-3 take the pairs of block rows 1-3, waves 4 and 5 the single blocks
+// (0, 0) and (2, 2); waves 6 and 7 write the two slots wholly above the diagonal.
+__device__ __forceinline__ bool dwave_block(int w, int bi, int& I, int& J) {
+  if (w < 4) {  // (1,0) (1,1) | (2,0) (2,1) | (3,0) (3,1) | (3,2) (3,3)
+    I = w < 3 ? w + 1 : 3;
+    J = (w < 3 ? 0 : 2) + bi;
+    return true;
+  }
+  I = J = 2 * (w - 4);  // (0,0) | (2,2)
+  return bi == 0 && w < 6;
 }
 
 }  // namespace
@@ -128,7 +137,7 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
   constexpr int C = DC, NSUB = SM::NSUB, LD = SM::LD, GLD = SM::GLD, LDC = SM::LDC, LDK = SM::LDK;
   constexpr int NRT = C / 16, NKC = C / 32, RG = DTHREADS / 32, RPT = C / RG;
   constexpr int NBLK = SM::NBLK, BPW = (NBLK + DWAVES - 1) / DWAVES;
-  static_assert(DWAVES == D / 16, "B3 gives each wave one 16-column slab");
+  static_assert(DWAVES == D / 16 && NSUB == 4 && BPW == 2, "the wave assignment below is for 8 waves, C = 64");
 
   __shared__ __attribute__((aligned(16))) char smem[SM::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + SM::G);
@@ -217,18 +226,44 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
     const int fg = (co & 15) >> 2, fh = co >> 4;
     store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
   };
-  // (X e^{g_C-G})^T to a transposed fragment: item = (channel, 4 consecutive chunk rows)
-  auto store_end = [&](size_t field, int ch, int s0, const float x[4]) {
-    const int kb = s0 >> 5, so = s0 & 31;
-    const int fg = (so & 15) >> 2, fh = so >> 4;
-    store4f(rec + field + ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8 + 4 * fh, x);
-  };
-  auto store_pp = [&](int I, int J, const floatx4& acc) {
-    const int r = 16 * I + m;
-    float pv[4];
+  // (A e^{g_C-G})^T and (K e^{g_C-G})^T as transposed fragments, whole 16-byte slots:
+  // item (channel, 4-row group fg, k-block kb) holds rows 32 kb + 4 fg + j and
+  // 32 kb + 16 + 4 fg + j; 16 consecutive items fill 256 contiguous bytes.
+  // ends(s, ch, ae, ke) gives both values of chunk row s.
+  auto emit_ends = [&](auto ends) {
+    for (int it = t; it < D * NKC * 4; it += DTHREADS) {
+      const int ch = it & (D - 1), fg = (it >> 7) & 3, kb = it >> 9;
+      floatx4 alo, ahi, klo, khi;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= r) ? acc[ii] : 0.f;
-    store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8 + 4 * (J & 1), pv);
+      for (int j = 0; j < 4; ++j) {
+        float a0, k0, a1, k1;
+        ends(32 * kb + 4 * fg + j, ch, a0, k0);
+        ends(32 * kb + 16 + 4 * fg + j, ch, a1, k1);
+        alo[j] = a0;
+        klo[j] = k0;
+        ahi[j] = a1;
+        khi[j] = k1;
+      }
+      const size_t slot = ((size_t)((ch >> 4) * NKC + kb) * 64 + (ch & 15) + 16 * fg) * 8;
+      store_frag<E>(rec + RC::KE + slot, acc_pair_to_frag<E>(alo, ahi));
+      store_frag<E>(rec + RC::KV + slot, acc_pair_to_frag<E>(klo, khi));
+    }
+  };
+  // P = M_qa in whole slots: an even block waits in p_lo for its odd partner unless it
+  // is the last of its block row
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  floatx4 p_lo = zero4;
+  auto emit_p = [&](int I, int J, const floatx4& acc) {
+    floatx4 pv;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= 16 * I + m) ? acc[ii] : 0.f;
+    E* dst = rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8;
+    if (J & 1)
+      store_frag<E>(dst, acc_pair_to_frag<E>(p_lo, pv));
+    else if (J == I)
+      store_frag<E>(dst, acc_pair_to_frag<E>(pv, zero4));
+    else
+      p_lo = pv;
   };
 
   float bt[RPT][4];  // B e^{G^-}, kept for phase B
@@ -277,12 +312,10 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       aBA[bi] = aBK[bi] = aQA[bi] = aQK[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + DWAVES * bi;
-      if (idx >= NBLK) break;
       int I, J;
-      block_of(idx, I, J);
+      if (!dwave_block(w, bi, I, J)) break;
       const int rrow = 16 * I + m, srow = 16 * J + m;
-      const float* scl = sScl + (size_t)idx * D;
+      const float* scl = sScl + (size_t)(I * (I + 1) / 2 + J) * D;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         FragT flb, flq, fra, frk;
@@ -307,22 +340,14 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
         mma(aQA[bi], fra, flq);
         mma(aQK[bi], frk, flq);
       }
-      store_pp(I, J, aQA[bi]);
+      emit_p(I, J, aQA[bi]);
     }
     // (A e^{g_C-G})^T and (K e^{g_C-G})^T: rhs_s 2^(g_C - b_{J+1})
-    for (int it = t; it < D * (C / 4); it += DTHREADS) {
-      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-      float ae[4], ke[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        const float f = sScl[(NBLK + (s >> 4)) * D + ch];
-        ae[j] = sRA[s * GLD + ch] * f;
-        ke[j] = sRK[s * GLD + ch] * f;
-      }
-      store_end(RC::KE, ch, s0, ae);
-      store_end(RC::KV, ch, s0, ke);
-    }
+    emit_ends([&](int s, int ch, float& ae, float& ke) {
+      const float f = sScl[(NBLK + (s >> 4)) * D + ch];
+      ae = sRA[s * GLD + ch] * f;
+      ke = sRK[s * GLD + ch] * f;
+    });
   } else {
     // ---- P2 (exact) ---------------------------------------------------------------
 #pragma unroll
@@ -347,10 +372,8 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       aBA[bi] = aBK[bi] = aQA[bi] = aQK[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int idx = w + DWAVES * bi;
-      if (idx >= NBLK) break;
       int I, J;
-      block_of(idx, I, J);
+      if (!dwave_block(w, bi, I, J)) break;
       const int r = 16 * I + m;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -377,31 +400,16 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
         aQA[bi][ii] = qa;
         aQK[bi][ii] = qk;
       }
-      store_pp(I, J, aQA[bi]);
+      emit_p(I, J, aQA[bi]);
     }
-    for (int it = t; it < D * (C / 4); it += DTHREADS) {
-      const int ch = it & (D - 1), s0 = 4 * (it >> 7);
-      const float gC = sBnd[NSUB * D + ch];
-      float ae[4], ke[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        const float f = s < len ? dexp2(gC - sG[s * GLD + ch]) : 0.f;
-        ae[j] = s < len ? to_f(ah[(size_t)s * HD + ch]) * f : 0.f;
-        ke[j] = s < len ? to_f(kh[(size_t)s * HD + ch]) * f : 0.f;
-      }
-      store_end(RC::KE, ch, s0, ae);
-      store_end(RC::KV, ch, s0, ke);
-    }
+    emit_ends([&](int s, int ch, float& ae, float& ke) {
+      const float f = s < len ? dexp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]) : 0.f;
+      ae = s < len ? to_f(ah[(size_t)s * HD + ch]) * f : 0.f;
+      ke = s < len ? to_f(kh[(size_t)s * HD + ch]) * f : 0.f;
+    });
   }
-  // zero halves of the P fragments above the diagonal (J > I)
-  for (int zi = t; zi < NRT * 2 * NKC * 64; zi += DTHREADS) {
-    const int ln = zi & 63, blk = zi >> 6, I = blk / (2 * NKC), J = blk % (2 * NKC);
-    if (J > I) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      store4f(rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + ln) * 8 + 4 * (J & 1), z);
-    }
-  }
+  // the two slots of P wholly above the diagonal, (0, 1) and (1, 1)
+  if (w >= 6) store_frag<E>(rec + RC::PP + ((size_t)((w - 6) * NKC + 1) * 64 + lane) * 8, acc_pair_to_frag<E>(zero4, zero4));
   __syncthreads();  // phase A buffers are dead from here on
 
   float* sA = reinterpret_cast<float*>(smem + SM::MA);
@@ -416,10 +424,8 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
   // ---- B0: -M_ba (fp32), M_bk, M_qk (E), masked; B e^{G^-} and V -----------------------
 #pragma unroll
   for (int bi = 0; bi < BPW; ++bi) {
-    const int idx = w + DWAVES * bi;
-    if (idx >= NBLK) break;
     int I, J;
-    block_of(idx, I, J);
+    if (!dwave_block(w, bi, I, J)) break;
     const int r = 16 * I + m;
     floatx4 ma;
     float mb[4], mq[4];
@@ -526,9 +532,9 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {  // accumulator order per (slab, row tile): 512 contiguous bytes
       const float oo[4] = {ao[rt][0], ao[rt][1], ao[rt][2], ao[rt][3]};
-      store4f(rec + RC::OI + (size_t)(16 * rt + m) * D + 16 * ct + 4 * g, oo);
+      store4f(rec + RC::OI + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, oo);
     }
   }
   __syncthreads();  // M_bk and M_qk are read; T is complete
@@ -538,31 +544,39 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
     for (int ii = 0; ii < 4; ++ii) sY[(16 * rt + 4 * g + ii) * LD + 16 * ct + m] = from_f<E>(yk[rt][ii]);
   __syncthreads();
 
-  // ---- B3b: W_b = T (B e^{G^-}) (computed transposed, fragment order) and U = T (M_bk V)
+  // ---- B3b: W_b = T (B e^{G^-}) (computed transposed, fragment order) and U = T (M_bk V).
+  //      Wave w takes the slab pair 2 (w & 3), 2 (w & 3) + 1 and the row tiles
+  //      2 (w >> 2), 2 (w >> 2) + 1, so both halves of a W_b slot come from one wave.
   {
-    FragT bK[NKC], bY[NKC];
+    const int ct0 = 2 * (w & 3), rt0 = 2 * (w >> 2);
+    FragT bK[2][NKC], bY[2][NKC];
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      bK[kb] = frag_colk(sKt, LD, 16 * ct + m, 32 * kb, g);
-      bY[kb] = frag_colk(sY, LD, 16 * ct + m, 32 * kb, g);
-    }
-    floatx4 aw[NRT], au[NRT];
+    for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      aw[rt] = au[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb <= (rt >> 1); ++kb) {  // T is lower triangular
-        const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
-        mma(aw[rt], bK[kb], aT);  // lane (m, g): W_b[16 rt + m][16 ct + 4 g + ii]
-        mma(au[rt], aT, bY[kb]);  // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
+      for (int kb = 0; kb < NKC; ++kb) {
+        bK[cl][kb] = frag_colk(sKt, LD, 16 * (ct0 + cl) + m, 32 * kb, g);
+        bY[cl][kb] = frag_colk(sY, LD, 16 * (ct0 + cl) + m, 32 * kb, g);
       }
-    }
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const float wb[4] = {aw[rt][0], aw[rt][1], aw[rt][2], aw[rt][3]};
-      store4f(rec + RC::WN + ((size_t)(rt * 4 + (ct >> 1)) * 64 + lane) * 8 + 4 * (ct & 1), wb);
-      const float uo[4] = {au[rt][0], au[rt][1], au[rt][2], au[rt][3]};
-      store4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, uo);
+    for (int rl = 0; rl < 2; ++rl) {
+      const int rt = rt0 + rl;
+      floatx4 aw[2] = {zero4, zero4}, au[2] = {zero4, zero4};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        if (kb > (rt >> 1)) break;  // T is lower triangular (rt is uniform over the wave)
+        const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+          mma(aw[cl], bK[cl][kb], aT);  // lane (m, g): W_b[16 rt + m][16 (ct0 + cl) + 4 g + ii]
+          mma(au[cl], aT, bY[cl][kb]);  // lane (m, g): U[16 rt + 4 g + ii][16 (ct0 + cl) + m]
+        }
+      }
+      store_frag<E>(rec + RC::WN + ((size_t)(rt * 4 + (w & 3)) * 64 + lane) * 8, acc_pair_to_frag<E>(aw[0], aw[1]));
+#pragma unroll
+      for (int cl = 0; cl < 2; ++cl) {
+        const float uo[4] = {au[cl][0], au[cl][1], au[cl][2], au[cl][3]};
+        store4f(rec + RC::UU + ((size_t)((ct0 + cl) * NRT + rt) * 64 + lane) * 4, uo);
+      }
     }
   }
 }

@@ -109,7 +109,8 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
         mma(X[rt], load_frag<E>(rec + RC::PP + ((size_t)(rt * NKC + kb) * 64 + lane) * 8), Ub[kb]);
       if constexpr (DP) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[rt][i] += to_f(rec[RC::OI + (size_t)(16 * rt + 4 * g + i) * D + 16 * ct + m]);
+        for (int i = 0; i < 4; ++i)  // row 16 rt + 4 g + i, column 16 ct + m of the transposed tile
+          X[rt][i] += to_f(rec[RC::OI + ((size_t)(ct * NRT + rt) * 64 + 4 * g + i + 16 * (m >> 2)) * 4 + (m & 3)]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         st.vb[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::VB * 2) + (2 * ct + kb) * 1024 + lo16);
-      st.oi = *reinterpret_cast<const bf16x4*>(rb + (RC::OI * 2) + ((16 * w + m) * D + 16 * ct + 4 * g) * 2);
+      st.oi = *reinterpret_cast<const bf16x4*>(rb + (RC::OI * 2) + ((ct * 4 + w) * 64 + lane) * 8);
     }
     const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
 #pragma unroll

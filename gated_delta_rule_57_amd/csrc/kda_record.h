@@ -38,7 +38,9 @@ struct Rec {
 // and three more:
 //   KV   (K e^{g_C-G})^T            [8][NKC][64][8]
 //   VB   V as B fragments           [8 column slabs][NKC][64][8]
-//   OI   M_qk V                     [C][128] row-major
+//   OI   M_qk V                     [8 column slabs][NRT][64][4], transposed accumulator
+//                                   order: lane (m, g) holds row 16 rt + m, columns
+//                                   16 ct + 4 g .. + 3
 template <typename E, int C>
 struct RecD {
   static constexpr int NRT = C / 16;
