@@ -33,8 +33,11 @@ CHUNK = 64
 FLOP_PER_TOK_HEAD = 6 * D * D + (CHUNK - 1) * D + (CHUNK + 1) * D + (CHUNK + 1) * D + (CHUNK - 1) * 2 * D
 # bytes every prefill must move per (token, head): q, k, v bf16, log_alpha fp32, beta fp32, o bf16
 PATH_BYTES_PER_TOK_HEAD = 3 * 2 * D + 4 * D + 4 + 2 * D
-# per-(chunk, head) record written by the intra-chunk kernel and read by the inter-chunk kernel
+# per-(chunk, head) record written by the intra-chunk kernel and read by the inter-chunk kernel:
+# its size in the workspace, and the bytes actually moved (the two all-zero P slots above the
+# diagonal, 2 x 1 KiB, are neither written nor read)
 RECORD_BYTES_BF16_C64 = 74240
+RECORD_MOVED_BYTES_BF16_C64 = RECORD_BYTES_BF16_C64 - 2048
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
@@ -54,6 +57,7 @@ BWD_PATH_BYTES_PER_TOK_HEAD = 4 * 2 * D + 4 * D + 4 + 3 * 2 * D + 4 * D + 4
 
 # general DPLR forward (64-token chunks, bf16): per (chunk, head) record of 123392 B
 DPLR_RECORD_BYTES_BF16 = 123392
+DPLR_RECORD_MOVED_BYTES_BF16 = DPLR_RECORD_BYTES_BF16 - 2048
 DPLR_IN_BYTES_PER_TOK_HEAD = 5 * 2 * D + 4 * D   # q, k, v, a, b bf16, log_alpha fp32
 
 PREFILL_T, PREFILL_H = 131072, 32
@@ -209,7 +213,7 @@ def gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec, runs=5):
         prefill_ms = ms["plan"] + ms["intra"] + ms["inter"]
         tok_heads = T * H
         gate_bytes = 0 if la is None else 4
-        intra_bytes = tok_heads * (3 * 2 * D + gate_bytes + 4) + (T // CHUNK) * H * RECORD_BYTES_BF16_C64
+        intra_bytes = tok_heads * (3 * 2 * D + gate_bytes + 4) + (T // CHUNK) * H * RECORD_MOVED_BYTES_BF16_C64
         out[name] = {"prefill_ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
                      "kernel_ms": {k: round(ms[k], 4) for k in ("plan", "intra", "inter")},
                      "intra_GBps": round(intra_bytes / (ms["intra"] * 1e-3) / 1e9, 1),
@@ -253,8 +257,8 @@ def dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=(4096, 16384, 6553
                                               o=o[:, :T], final_state=fin, workspace=ws_d))
         kt, dt = sum(km.values()), sum(dm.values())
         tok_heads = T * H
-        d_intra_bytes = tok_heads * DPLR_IN_BYTES_PER_TOK_HEAD + (T // CHUNK) * H * DPLR_RECORD_BYTES_BF16
-        d_inter_bytes = (T // CHUNK) * H * DPLR_RECORD_BYTES_BF16 + tok_heads * 2 * D
+        d_intra_bytes = tok_heads * DPLR_IN_BYTES_PER_TOK_HEAD + (T // CHUNK) * H * DPLR_RECORD_MOVED_BYTES_BF16
+        d_inter_bytes = (T // CHUNK) * H * DPLR_RECORD_MOVED_BYTES_BF16 + tok_heads * 2 * D
         rows.append({"T": T, "kda_ms": round(kt, 4), "dplr_ms": round(dt, 4),
                      "dplr_over_kda": round(dt / kt, 3),
                      "kda_tokens_per_s": round(T / (kt * 1e-3), 1), "dplr_tokens_per_s": round(T / (dt * 1e-3), 1),
@@ -362,7 +366,7 @@ def main():
     flops = FLOP_PER_TOK_HEAD * tok_heads
     prefill_tflops = flops / (prefill_ms * 1e-3) / 1e12
     n_chunks = (T + CHUNK - 1) // CHUNK
-    rec_bytes = n_chunks * H * RECORD_BYTES_BF16_C64
+    rec_bytes = n_chunks * H * RECORD_MOVED_BYTES_BF16_C64
     in_bytes = tok_heads * (3 * 2 * D + 4 * D + 4)
     out_bytes = tok_heads * 2 * D
     kernel_bytes = {

@@ -92,7 +92,8 @@ struct DSmem {
 // bi-th slot (bi < 2). The blocks J = 2 kb and 2 kb + 1 of a block row fill one
 // 16-byte slot of P per lane, so they go to the same wave and P leaves as whole
 // slots: waves 0-3 take the pairs of block rows 1-3, waves 4 and 5 the single blocks
-// (0, 0) and (2, 2); waves 6 and 7 write the two slots wholly above the diagonal.
+// (0, 0) and (2, 2). The two slots wholly above the diagonal are never read and
+// not written.
 __device__ __forceinline__ bool dwave_block(int w, int bi, int& I, int& J) {
   if (w < 4) {  // (1,0) (1,1) | (2,0) (2,1) | (3,0) (3,1) | (3,2) (3,3)
     I = w < 3 ? w + 1 : 3;
@@ -408,8 +409,6 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
       ke = s < len ? to_f(kh[(size_t)s * HD + ch]) * f : 0.f;
     });
   }
-  // the two slots of P wholly above the diagonal, (0, 1) and (1, 1)
-  if (w >= 6) store_frag<E>(rec + RC::PP + ((size_t)((w - 6) * NKC + 1) * 64 + lane) * 8, acc_pair_to_frag<E>(zero4, zero4));
   __syncthreads();  // phase A buffers are dead from here on
 
   float* sA = reinterpret_cast<float*>(smem + SM::MA);

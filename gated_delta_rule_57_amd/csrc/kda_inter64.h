@@ -231,9 +231,10 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
       st.qt[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::QT * 2) + (4 * w + kb) * 1024 + lo16);
       st.ke[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::KE * 2) + (4 * w + kb) * 1024 + lo16);
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      st.pp[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::PP * 2) + (2 * w + kb) * 1024 + lo16);
+    // P is causal: rows 0..31 (waves 0 and 1) have no second k-block, and those slots
+    // are neither written nor read (w is uniform over the wave)
+    st.pp[0] = *reinterpret_cast<const bf16x8*>(rb + (RC::PP * 2) + (2 * w) * 1024 + lo16);
+    if (w >= 2) st.pp[1] = *reinterpret_cast<const bf16x8*>(rb + (RC::PP * 2) + (2 * w + 1) * 1024 + lo16);
     st.uu = *reinterpret_cast<const bf16x4*>(rb + (RC::UU * 2) + ((ct * 4 + w) * 64 + lane) * 8);
     if constexpr (DP) {
 #pragma unroll

@@ -338,13 +338,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     else
       p_lo = pv;
   };
-  // the slots wholly above the diagonal, (0, 1) and (1, 1), from the waves with two blocks
-  auto emit_p_zero_slots = [&]() {
-    if constexpr (NSUB == 4) {
-      if (w >= 2)
-        store_frag<E>(rec + RC::PP + ((size_t)((w - 2) * NKC + 1) * 64 + lane) * 8, acc_pair_to_frag<E>(zero4, zero4));
-    }
-  };
   // (K e^{g_C - G})^T to the record: item (channel, 4-row group fg, k-block kb) is one
   // lane's whole slot, rows 32 kb + 4 fg + j and 32 kb + 16 + 4 fg + j; 16 consecutive
   // items fill 256 contiguous bytes. kval(s, ch) gives the value of chunk row s < C.
@@ -499,7 +492,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       emit_p(I, J, accP[bi]);
     }
-    emit_p_zero_slots();
     // (K e^{g_C - G})^T = rhs_s 2^(g_C - b_{J+1}) to the record
     emit_ke([&](int s, int ch) { return sRR[s * GLD + ch] * sScl[(NBLK + (s >> 4)) * D + ch]; });
   } else {
@@ -580,7 +572,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       emit_p(I, J, accP[bi]);
     }
-    emit_p_zero_slots();
     // (K e^{g_C - G})^T to the record
     emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]); });
   }
@@ -658,7 +649,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       emit_p(I, J, accP[bi]);
     }
-    emit_p_zero_slots();
     // (K e^{g_C - G})^T to the record
     emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(gC - sGs[s])); });
   }

@@ -18,7 +18,8 @@ struct Rec {
   static constexpr size_t WN = 0;                                   // [NRT][4][64][8]   -W
   static constexpr size_t QT = WN + (size_t)NRT * 4 * FR;           // [NRT][4][64][8]   Q e^G
   static constexpr size_t KE = QT + (size_t)NRT * 4 * FR;           // [8][NKC][64][8]   (K e^{g_C-G})^T
-  static constexpr size_t PP = KE + (size_t)8 * NKC * FR;           // [NRT][NKC][64][8] P
+  static constexpr size_t PP = KE + (size_t)8 * NKC * FR;           // [NRT][NKC][64][8] P (causal: the
+                                                                    // slots above the diagonal are not written)
   static constexpr size_t UU = PP + (size_t)NRT * NKC * FR;         // [8][NRT][64][4]   U, accumulator order
   static constexpr size_t END = UU + (size_t)NRT * 8 * 64 * 4;
   static constexpr size_t GAMMA_BYTES = al256(END * sizeof(E));      // float[128] e^{g_C}
