@@ -537,7 +537,8 @@ __global__ void __launch_bounds__(256) fwd_state_kernel(const char* __restrict__
                                                         const int2* __restrict__ info,
                                                         const float* __restrict__ initial_state, int N, int H, int mc,
                                                         E* __restrict__ states, E* __restrict__ ut) {
-  inter16_body<E>(blockIdx.x, records, chunk_off, info, initial_state, nullptr, nullptr, N, H, mc, states, ut);
+  inter16_body<E, false>(blockIdx.x, records, chunk_off, info, initial_state, nullptr, nullptr, N, H, mc, states,
+                         ut);
 }
 
 template <typename E>

@@ -22,9 +22,10 @@ constexpr int INTER16_TOUCH_AHEAD = 4;
 
 // The body of one work-group (256 threads) with work-group index b, laid out like
 // the 64-token kernel: b & 7 selects the XCD, (b >> 3) & 7 the slab, b >> 6 the
-// (sequence, head) group. Called by inter16_kernel and by the backward's combined
-// state-pass kernel.
-template <typename E>
+// (sequence, head) group. Called by inter16_kernel (WANT_O, o non-null) and by the
+// backward's forward state pass (no output: Q e^G and P are neither loaded nor
+// touched in L2, which leaves fewer than half of the bytes per chunk).
+template <typename E, bool WANT_O>
 __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ records,
                                              const int32_t* __restrict__ chunk_off, const int2* __restrict__ info,
                                              const float* __restrict__ initial_state, float* __restrict__ final_state,
@@ -73,10 +74,12 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
     const E* rec = reinterpret_cast<const E*>(rb);
     st.wn = load_frag<E>(rec + RC::WN + ((size_t)w * 64 + lane) * 8);
-    st.qt = load_frag<E>(rec + RC::QT + ((size_t)w * 64 + lane) * 8);
+    if constexpr (WANT_O) {
+      st.qt = load_frag<E>(rec + RC::QT + ((size_t)w * 64 + lane) * 8);
+      if (w == 1) st.pp = load_frag<E>(rec + RC::PP + (size_t)lane * 8);  // used by wave 1 only
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) st.ke[j] = load_frag<E>(rec + RC::KE + ((size_t)(2 * w + j) * 64 + lane) * 8);
-    st.pp = load_frag<E>(rec + RC::PP + (size_t)lane * 8);
     st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
     const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
 #pragma unroll
@@ -106,7 +109,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
                         : floatx4{0.f, 0.f, 0.f, 0.f};
     mma(up, st.wn, Sb);
     xp[buf][w][lane] = up;
-    if (o) {
+    if constexpr (WANT_O) {
       floatx4 xpart = {0.f, 0.f, 0.f, 0.f};
       mma(xpart, st.qt, Sb);
       xq[buf][w][lane] = xpart;
@@ -125,7 +128,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
       compiler_fence();
     }
     const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});
-    if (o && w == 1) {  // O = (Q e^G) S + P U~
+    if (WANT_O && w == 1) {  // O = (Q e^G) S + P U~
       floatx4 X = xq[buf][0][lane] + xq[buf][1][lane] + xq[buf][2][lane] + xq[buf][3][lane];
       mma(X, st.pp, Ub);
 #pragma unroll
@@ -143,13 +146,25 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   };
 
   // L2 touch INTER16_TOUCH_AHEAD chunks beyond the register stage: each line of the
-  // record is read (one word) by one of the head's 32 waves, so the real loads hit in
-  // L2 (the words are XOR-folded into tacc, stored only by a never-taken branch)
+  // record that the loads above read is read first (one word) by one of the head's 32
+  // waves, so the real loads hit in L2 (the words are XOR-folded into tacc, stored
+  // only by a never-taken branch). Without the output only the W, K e^{g_C-G}, U and
+  // e^{g_C} lines are needed.
   constexpr int LINES = (int)(RC::BYTES / 128);
   static_assert(RC::BYTES % 128 == 0 && LINES <= 32 * 64, "one touch per lane");
-  // lanes past the record's last line touch that line again (an unconditional load
-  // is never merged with an old value)
-  const int touch_line = min((ct * 4 + w) + 32 * lane, LINES - 1);
+  constexpr int WN_L = (int)((RC::QT - RC::WN) * sizeof(E) / 128);
+  constexpr int KE_L = (int)((RC::PP - RC::KE) * sizeof(E) / 128);
+  constexpr int UU_L = (int)(RC::GAMMA_BYTES / 128) - (int)(RC::UU * sizeof(E) / 128);
+  constexpr int NEED = WANT_O ? LINES : WN_L + KE_L + UU_L + (LINES - (int)(RC::GAMMA_BYTES / 128));
+  static_assert((RC::QT * sizeof(E)) % 128 == 0 && (RC::KE * sizeof(E)) % 128 == 0 &&
+                (RC::PP * sizeof(E)) % 128 == 0 && (RC::UU * sizeof(E)) % 128 == 0, "line-aligned parts");
+  // lanes past the last needed line touch that line again (an unconditional load is
+  // never merged with an old value)
+  const int tl = min((ct * 4 + w) + 32 * lane, NEED - 1);
+  const int touch_line = WANT_O ? tl
+                         : tl < WN_L        ? tl
+                         : tl < WN_L + KE_L ? (int)(RC::KE * sizeof(E) / 128) + (tl - WN_L)
+                                            : (int)(RC::UU * sizeof(E) / 128) + (tl - WN_L - KE_L);
   // each loop iteration covers four chunks: its first step touches the next four
   // beyond the touch distance and the words are folded in after its last step, so
   // no touched word lives across the back edge (where a copy would wait for it)

@@ -784,7 +784,7 @@ __global__ void __launch_bounds__(256) inter16_kernel(const char* __restrict__ r
                                                       const float* __restrict__ initial_state,
                                                       float* __restrict__ final_state, E* __restrict__ o, int N, int H,
                                                       int mc, E* __restrict__ states, E* __restrict__ ut) {
-  inter16_body<E>(blockIdx.x, records, chunk_off, info, initial_state, final_state, o, N, H, mc, states, ut);
+  inter16_body<E, true>(blockIdx.x, records, chunk_off, info, initial_state, final_state, o, N, H, mc, states, ut);
 }
 
 // ---------------------------------------------------------------------------
