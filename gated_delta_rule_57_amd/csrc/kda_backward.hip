@@ -135,6 +135,23 @@ struct LocalLds {
   int exact;
 };
 
+// Fragment over row 16 nt + m of a tiled 128 x 128 matrix (state_tile_index), k running
+// over columns 32 kb + koff(g, s): slots 0..3 come from tile (nt, 2 kb) and 4..7 from
+// tile (nt, 2 kb + 1), lane m + 16 g in both, so each is one contiguous load per wave.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T tile_frag(const E* __restrict__ M, int nt, int kb, int lane) {
+  typedef typename Vec4<E>::T V4;
+  const V4 lo = *reinterpret_cast<const V4*>(M + ((size_t)(nt * 8 + 2 * kb) * 64 + lane) * 4);
+  const V4 hi = *reinterpret_cast<const V4*>(M + ((size_t)(nt * 8 + 2 * kb + 1) * 64 + lane) * 4);
+  typename Frag<E>::T f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = lo[i];
+    f[4 + i] = hi[i];
+  }
+  return f;
+}
+
 // Fragments over the chunk's rows (k < 16; slots 4..7, rows 16..31, are zero):
 // A operand, row m: slot s = f(4 g + s); B operand, column m: slot s = f(4 g + s).
 template <typename E, typename F>
@@ -424,18 +441,17 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
 
   auto compute = [&](const Stage& st, int c, int buf) {
     E* xw = xs[w];
-    {  // this wave's 32 rows of the gradient at the chunk's end, as 16-byte row pieces
+    {  // this wave's 32 rows of the gradient at the chunk's end: two whole tiles
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(Lm[j][i]);
       compiler_fence();
-      E* dp = dstates + ((size_t)h * mc + c) * D * D + (size_t)(32 * w) * D + 16 * ct;
+      E* dp = dstates + ((size_t)h * mc + c) * D * D;
 #pragma unroll
-      for (int p = 0; p < (int)sizeof(E) / 2; ++p) {
-        const int piece = lane + 64 * p, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(dp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
-      }
+      for (int j = 0; j < 2; ++j)  // lane (m, g): row 32w + 16j + m, columns 16ct + 4g .. + 3
+        *reinterpret_cast<V4*>(dp + state_tile_index(32 * w + 16 * j + m, 16 * ct + 4 * g)) =
+            *reinterpret_cast<const V4*>(&xw[(16 * j + m) * XW + 4 * g]);
       compiler_fence();
     }
     FragT dOb;  // B fragment of dO over the chunk rows
@@ -631,8 +647,9 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       float dg = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const FragT bs = frag_rowk<E>(S0, D, 16 * nt + m, 32 * kb, g);
-        const FragT bd = frag_rowk<E>(dSC, D, 16 * nt + m, 32 * kb, g);
+        // row 16 nt + m over columns 32 kb + koff(g, s): tiles (nt, 2 kb) and (nt, 2 kb + 1)
+        const FragT bs = tile_frag<E>(S0, nt, kb, lane);
+        const FragT bd = tile_frag<E>(dSC, nt, kb, lane);
         mma(x1, a1[kb], bs);
         mma(x2, a2[kb], bs);
         mma(x3, a3[kb], bd);

@@ -90,18 +90,17 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   auto compute = [&](const Stage& st, int c, int buf) {
     const FragT Sb = acc_pair_to_frag<E>(S[0], S[1]);  // k-block w of the state
     E* xw = xs[w];
-    if (states) {  // this wave's 32 rows of the state entering the chunk
+    if (states) {  // this wave's 32 rows of the state entering the chunk: two whole tiles
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(S[j][i]);
       compiler_fence();
-      E* sp = states + ((size_t)h * mc + c) * D * D + (size_t)(32 * w) * D + 16 * ct;
+      E* sp = states + ((size_t)h * mc + c) * D * D;
 #pragma unroll
-      for (int p = 0; p < (int)sizeof(E) / 2; ++p) {
-        const int piece = lane + 64 * p, row = piece / (16 / VE), col = (piece % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(sp + (size_t)row * D + col) = *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
-      }
+      for (int j = 0; j < 2; ++j)  // lane (m, g): row 32w + 16j + m, columns 16ct + 4g .. + 3
+        *reinterpret_cast<typename Vec4<E>::T*>(sp + state_tile_index(32 * w + 16 * j + m, 16 * ct + 4 * g)) =
+            *reinterpret_cast<const typename Vec4<E>::T*>(&xw[(16 * j + m) * XW + 4 * g]);
       compiler_fence();
     }
     // parts over this wave's 32 state rows: U - W S (U added once, by wave 0) and (Q e^G) S

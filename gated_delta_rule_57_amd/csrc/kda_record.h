@@ -60,4 +60,15 @@ struct RecD {
   static constexpr size_t BYTES = al256(GAMMA_BYTES + D * sizeof(float));
 };
 
+// The backward's per-chunk 128 x 128 matrices (the state entering each chunk and the
+// state gradient at its end) are kept in 16 x 16 tiles in fragment order: element
+// (i, j) at index ((i / 16 * 8 + j / 16) * 64 + i % 16 + 16 * (j % 16 / 4)) * 4 + j % 4.
+// A lane's four consecutive columns of one row are contiguous and every tile is one
+// contiguous block, so the serial pass that owns a 16-column slab writes whole
+// blocks, and the 32-wide k-block of a fragment over a row (k = column) is two
+// contiguous blocks: tiles (i / 16, 2 kb) and (i / 16, 2 kb + 1), lane i % 16 + 16 g.
+__host__ __device__ constexpr size_t state_tile_index(int i, int j) {
+  return ((size_t)((i >> 4) * 8 + (j >> 4)) * 64 + (i & 15) + 16 * ((j & 15) >> 2)) * 4 + (j & 3);
+}
+
 }  // namespace kda
