@@ -34,7 +34,8 @@
 //                      the initial-state gradient;
 //   bwd_chunk_kernel   one work-group per (chunk, head): everything local to the
 //                      chunk. X1, X2, X3 and dgamma are bf16 (or fp32) MFMA products
-//                      whose operands come straight from row-major global memory;
+//                      whose operands come straight from global memory (dO by rows;
+//                      the states, state gradients, U~ and dU~ in 16 x 16 tiles);
 //                      dT, dB_K, dB_V and the decay-weighted sums over the chunk's rows
 //                      are MFMAs too, on operands built in LDS; 16 x 16 algebra (T,
 //                      dA) and the element-wise terms run on the VALU in fp32.
@@ -355,7 +356,6 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   // struct otherwise end up in scratch)
   typedef unsigned int RawV __attribute__((ext_vector_type(sizeof(V4) / 4)));
   constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
-  constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
   __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
   __shared__ floatx4 xp[2][4][64];                           // dU~ parts, by chunk parity
 
@@ -471,11 +471,9 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
 #pragma unroll
       for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(du[i]);
       compiler_fence();
-      if (lane < 16 * (16 / VE)) {
-        const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(dut + ((size_t)h * mc + c) * BC * D + (size_t)row * D + 16 * ct + col) =
-            *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
-      }
+      // tile ct of this chunk's dU~, state tile order (row m, columns 16 ct + 4 g .. + 3)
+      *reinterpret_cast<typename Vec4<E>::T*>(dut + ((size_t)h * mc + c) * BC * D + ((size_t)ct * 64 + lane) * 4) =
+          *reinterpret_cast<const typename Vec4<E>::T*>(&xw[m * XW + 4 * g]);
       compiler_fence();
     }
     const FragT dUb = acc_pair_to_frag<E>(du, zero4);
@@ -623,7 +621,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     load8(v + rowbase, HD, rm.r, len, rm.c0, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) S.V[rm.r][rm.c0 + i] = x[i];
-    load8(dUt, D, rm.r, BC, rm.c0, x);
+    load4f(dUt + state_tile_index(rm.r, rm.c0), x);
+    load4f(dUt + state_tile_index(rm.r, rm.c0 + 4), x + 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) S.dU[rm.r][rm.c0 + i] = x[i];
   }
@@ -637,8 +636,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       a1[kb] = m < len ? frag_rowk<E>(dout + rowbase, (int)HD, m, 32 * kb, g) : zero_frag<E>();
-      a2[kb] = frag_rowk<E>(dUt, D, m, 32 * kb, g);
-      a3[kb] = frag_rowk<E>(Ut, D, m, 32 * kb, g);
+      a2[kb] = tile_frag<E>(dUt, 0, kb, lane);
+      a3[kb] = tile_frag<E>(Ut, 0, kb, lane);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -667,7 +666,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     if (w == 0) {  // dP = tril(dO U~^T)
       floatx4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(p, a1[kb], frag_rowk<E>(Ut, D, m, 32 * kb, g));
+      for (int kb = 0; kb < 4; ++kb) mma(p, a1[kb], tile_frag<E>(Ut, 0, kb, lane));
 #pragma unroll
       for (int i = 0; i < 4; ++i) S.dP[4 * g + i][m] = m <= 4 * g + i ? p[i] : 0.f;
     }

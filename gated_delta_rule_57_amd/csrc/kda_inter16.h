@@ -35,7 +35,6 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   typedef typename Frag<E>::T FragT;
   static_assert(RC::NRT == 1 && RC::NKC == 1, "16-token chunks");
   constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
-  constexpr int VE = 16 / (int)sizeof(E);       // elements per 16-byte store
   __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
   __shared__ floatx4 xp[2][4][64];                           // U~ parts, by chunk parity
   __shared__ floatx4 xq[2][4][64];                           // (Q e^G) S parts
@@ -119,11 +118,10 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
 #pragma unroll
       for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
       compiler_fence();
-      if (lane < 16 * (16 / VE)) {
-        const int row = lane / (16 / VE), col = (lane % (16 / VE)) * VE;
-        *reinterpret_cast<uint4*>(ut + ((size_t)h * mc + c) * 16 * D + (size_t)row * D + 16 * ct + col) =
-            *reinterpret_cast<const uint4*>(&xw[row * XW + col]);
-      }
+      // 16 x 16 tile ct of this chunk's U~ in the state tile order: lane (m, g) stores
+      // row m, columns 16 ct + 4 g .. + 3
+      *reinterpret_cast<typename Vec4<E>::T*>(ut + ((size_t)h * mc + c) * 16 * D + ((size_t)ct * 64 + lane) * 4) =
+          *reinterpret_cast<const typename Vec4<E>::T*>(&xw[m * XW + 4 * g]);
       compiler_fence();
     }
     const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});

@@ -61,7 +61,8 @@ struct RecD {
 };
 
 // The backward's per-chunk 128 x 128 matrices (the state entering each chunk and the
-// state gradient at its end) are kept in 16 x 16 tiles in fragment order: element
+// state gradient at its end), and its 16 x 128 U~ and dU~ (one row of tiles), are
+// kept in 16 x 16 tiles in fragment order: element
 // (i, j) at index ((i / 16 * 8 + j / 16) * 64 + i % 16 + 16 * (j % 16 / 4)) * 4 + j % 4.
 // A lane's four consecutive columns of one row are contiguous and every tile is one
 // contiguous block, so the serial pass that owns a 16-column slab writes whole
