@@ -22,13 +22,14 @@
 //
 // Kernels, in launch order:
 //   the forward's plan and records at 16-token chunks (plan_kernel, intra_kernel);
-//   fwd_state_kernel   the forward state pass (inter16_body), four waves per
-//                      (sequence, head, 16-column slab): keeps the state entering
-//                      every chunk and U~;
+//   fwd_state_kernel   the forward state pass (inter16_body), four compute waves
+//                      and a store wave per (sequence, head, 16-column slab): keeps
+//                      the state entering every chunk and U~;
 //   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
 //                      e^{g_C}, in the fragment order the reverse state pass reads;
-//   bwd_state_kernel   the reverse state pass (bwd_state_body), four waves per
-//                      (sequence, head, 16-column slab), over the chunks in reverse
+//   bwd_state_kernel   the reverse state pass (bwd_state_body), four compute waves
+//                      and a store wave per (sequence, head, 16-column slab), over
+//                      the chunks in reverse
 //                      with the 128 x 16 fp32 slab of the state gradient in
 //                      accumulator registers: keeps dS_C and dU~ per chunk and writes
 //                      the initial-state gradient;
@@ -339,7 +340,9 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
 // forms its k-block's part of dU~ = P^T dO + (K e^{g_C-G}) dS (P^T dO once, in wave
 // 0), the parts are summed through LDS behind one barrier that leaves global loads
 // in flight, and each wave updates its own rows. Work-group ids are dealt so that
-// the eight slabs of a head share one XCD's L2.
+// the eight slabs of a head share one XCD's L2. As in the forward pass, a fifth wave
+// stores the per-chunk dS_C and dU~ from LDS, so that no compute wave waits on store
+// acknowledgements when it waits for its next operands.
 // ---------------------------------------------------------------------------
 constexpr int STATE_TOUCH_AHEAD = 4;
 
@@ -355,9 +358,12 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   // four elements kept as raw 32-bit words while loading (packed bf16 vectors in a
   // struct otherwise end up in scratch)
   typedef unsigned int RawV __attribute__((ext_vector_type(sizeof(V4) / 4)));
-  constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
-  __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
-  __shared__ floatx4 xp[2][4][64];                           // dU~ parts, by chunk parity
+  __shared__ floatx4 xp[2][4][64];  // dU~ parts, by chunk parity
+  // by chunk parity: dS at the chunk's end, tile rt (rows 16 rt ..) of the slab at
+  // [rt][lane][4] in accumulator order (lane (m, g) holds rows 4g .. 4g+3 of column m),
+  // and dU~ the same way
+  __shared__ __attribute__((aligned(16))) E stg_s[2][8 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) E stg_u[2][64 * 4];
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
@@ -367,6 +373,36 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   if (u >= N * H) return;  // uniform over the work-group
   const int n = u / H, h = u - n * H;
   const size_t HD = (size_t)H * D;
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+
+  if (w == 4) {
+    // the store wave: one barrier per chunk, as the compute waves, and one after the
+    // last. After the barrier of the chunk i-th from the end, that chunk's dS_C and the
+    // dU~ of the chunk after it are in LDS until the next barrier but one. Lane (m, g)
+    // stores row m, columns 16 ct + 4 g .. + 3 of each tile, reading the four values
+    // from lanes 4 g .. 4 g + 3, slot m % 4, of the accumulator order.
+    auto gather = [&](const E* tile) {
+      V4 x;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) x[s4] = tile[(4 * g + s4 + 16 * (m >> 2)) * 4 + (m & 3)];
+      return x;
+    };
+    E* dut_h = dut + (size_t)h * mc * BC * D + ((size_t)ct * 64 + lane) * 4;
+    for (int i = 0; c_end - 1 - i >= c_begin; ++i) {
+      lds_barrier();
+      const int c = c_end - 1 - i;
+      E* dp = dstates + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+        *reinterpret_cast<V4*>(dp + (size_t)rt * 8 * 64 * 4) = gather(&stg_s[i & 1][rt * 64 * 4]);
+      if (i > 0) *reinterpret_cast<V4*>(dut_h + (size_t)(c + 1) * BC * D) = gather(stg_u[(i - 1) & 1]);
+    }
+    lds_barrier();
+    if (c_end > c_begin)
+      *reinterpret_cast<V4*>(dut_h + (size_t)c_begin * BC * D) = gather(stg_u[(c_end - c_begin - 1) & 1]);
+    return;
+  }
+
   const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
 
   floatx4 Lm[2];
@@ -407,7 +443,6 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     for (int i = 0; i < RW; ++i) x[i] = r[i];
     return half_frag(x);
   };
-  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   auto load = [&](Stage& st, int c) {
     const char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
     const E* wt = reinterpret_cast<const E*>(rb + BR::WT);
@@ -440,19 +475,12 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   };
 
   auto compute = [&](const Stage& st, int c, int buf) {
-    E* xw = xs[w];
-    {  // this wave's 32 rows of the gradient at the chunk's end: two whole tiles
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {  // this wave's two tiles of the gradient at the chunk's end, to LDS
+      V4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(Lm[j][i]);
-      compiler_fence();
-      E* dp = dstates + ((size_t)h * mc + c) * D * D;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)  // lane (m, g): row 32w + 16j + m, columns 16ct + 4g .. + 3
-        *reinterpret_cast<V4*>(dp + state_tile_index(32 * w + 16 * j + m, 16 * ct + 4 * g)) =
-            *reinterpret_cast<const V4*>(&xw[(16 * j + m) * XW + 4 * g]);
-      compiler_fence();
+      for (int i = 0; i < 4; ++i) x[i] = from_f<E>(Lm[j][i]);
+      *reinterpret_cast<V4*>(&stg_s[buf][((2 * w + j) * 64 + lane) * 4]) = x;
     }
     FragT dOb;  // B fragment of dO over the chunk rows
 #pragma unroll
@@ -467,14 +495,11 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     xp[buf][w][lane] = dp4;
     lds_barrier();
     const floatx4 du = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
-    if (w == 0) {
+    if (w == 0) {  // dU~ to LDS, for the store wave after the next barrier
+      V4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(du[i]);
-      compiler_fence();
-      // tile ct of this chunk's dU~, state tile order (row m, columns 16 ct + 4 g .. + 3)
-      *reinterpret_cast<typename Vec4<E>::T*>(dut + ((size_t)h * mc + c) * BC * D + ((size_t)ct * 64 + lane) * 4) =
-          *reinterpret_cast<const typename Vec4<E>::T*>(&xw[m * XW + 4 * g]);
-      compiler_fence();
+      for (int i = 0; i < 4; ++i) x[i] = from_f<E>(du[i]);
+      *reinterpret_cast<V4*>(&stg_u[buf][lane * 4]) = x;
     }
     const FragT dUb = acc_pair_to_frag<E>(du, zero4);
     // dS0_w = e^{g_C} o dS_w + (Q e^G)^T_w dO + (-W)^T_w dU~
@@ -500,11 +525,6 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     return *reinterpret_cast<const unsigned*>(brec + ((size_t)h * mc + c) * BR::BYTES + (size_t)touch_line * 128);
   };
 
-  // two named stages: each step loads chunk c - 1 into the stage consumed one step
-  // earlier (past the start, the first chunk again: every step issues the same
-  // loads). Four touch words in flight: step r folds in the word it loaded four steps
-  // earlier before loading the next one into the same variable, so no register copy
-  // has to wait for a load.
   // four named stages, three chunks of operands in flight: step r of an iteration
   // loads chunk c - 3 into the stage consumed one step earlier (past the start, the
   // first chunk again: every step issues the same loads)
@@ -532,6 +552,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     if (c0 - 3 >= c_begin) compute(sd, c0 - 3, 1);
     tacc ^= t0 ^ t1 ^ t2 ^ t3;
   }
+  lds_barrier();  // the store wave's last one: dU~ of the first chunk
   // mc is never negative (the host sizes it from the shapes), so this never stores
   if (mc < 0 && tacc == 0u) dut[lane] = from_f<E>(0.f);
   if (d_initial) {
@@ -546,7 +567,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
 // Run side by side in one launch (one work-group of each per CU) they take longer
 // than one after the other: each already saturates a per-CU resource.
 template <typename E>
-__global__ void __launch_bounds__(256) fwd_state_kernel(const char* __restrict__ records,
+__global__ void __launch_bounds__(320) fwd_state_kernel(const char* __restrict__ records,
                                                         const int32_t* __restrict__ chunk_off,
                                                         const int2* __restrict__ info,
                                                         const float* __restrict__ initial_state, int N, int H, int mc,
@@ -556,7 +577,7 @@ __global__ void __launch_bounds__(256) fwd_state_kernel(const char* __restrict__
 }
 
 template <typename E>
-__global__ void __launch_bounds__(256) bwd_state_kernel(const char* __restrict__ brec,
+__global__ void __launch_bounds__(320) bwd_state_kernel(const char* __restrict__ brec,
                                                         const int32_t* __restrict__ chunk_off,
                                                         const int2* __restrict__ info, const E* __restrict__ dout,
                                                         const float* __restrict__ d_final,
@@ -869,7 +890,7 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   const char* records = ws + l.fwd.off_records;
   const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
-    hipLaunchKernelGGL(fwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, records, chunk_off,
+    hipLaunchKernelGGL(fwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(320), 0, stream, records, chunk_off,
                        info, initial_state, N, H, (int)mc, states, ut);
     e = hipGetLastError();
     trace_mark(stream, 2);
@@ -883,7 +904,7 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
     if (e != hipSuccess) return e;
   }
   if (slots > 0) {
-    hipLaunchKernelGGL(bwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, brec, chunk_off,
+    hipLaunchKernelGGL(bwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(320), 0, stream, brec, chunk_off,
                        info, (const E*)dout, d_final, d_initial, dstates, dut, N, H, (int)mc);
     e = hipGetLastError();
     trace_mark(stream, 6);

@@ -14,16 +14,23 @@ namespace kda {
 // through LDS behind one barrier that leaves global loads in flight, and each wave
 // updates its own rows. The next chunk's fragments are loaded into registers while
 // the current one is computed, and each record line is touched in L2 a few chunks
-// ahead by one wave of the head. The per-chunk outputs of the backward pass (states,
-// U~) are transposed through LDS and written as 16-byte row pieces.
+// ahead by one wave of the head.
+// The backward's forward pass keeps the state entering every chunk and U~. Their
+// stores go out through a fifth wave: the four compute waves put their accumulator
+// registers into LDS (one 8-byte write per 16 x 16 tile and lane), and after the
+// chunk's barrier the store wave reads them back transposed and writes whole 16 x 16
+// tiles. On this architecture stores count in the same in-order counter as loads,
+// so a compute wave that stored would wait on its own store acknowledgements each
+// time it waits for the next chunk's operands.
 // ---------------------------------------------------------------------------
 constexpr int INTER16_LOOKAHEAD = 3;
 constexpr int INTER16_TOUCH_AHEAD = 4;
 
-// The body of one work-group (256 threads) with work-group index b, laid out like
-// the 64-token kernel: b & 7 selects the XCD, (b >> 3) & 7 the slab, b >> 6 the
-// (sequence, head) group. Called by inter16_kernel (WANT_O, o non-null) and by the
-// backward's forward state pass (no output: Q e^G and P are neither loaded nor
+// The body of one work-group with work-group index b, laid out like the 64-token
+// kernel: b & 7 selects the XCD, (b >> 3) & 7 the slab, b >> 6 the (sequence, head)
+// group. Called by inter16_kernel (WANT_O: 256 threads, o non-null, states and ut
+// null) and by the backward's forward state pass (!WANT_O: 320 threads, the fifth
+// wave storing states and ut, both non-null; Q e^G and P are neither loaded nor
 // touched in L2, which leaves fewer than half of the bytes per chunk).
 template <typename E, bool WANT_O>
 __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ records,
@@ -34,10 +41,15 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   using RC = Rec<E, 16>;
   typedef typename Frag<E>::T FragT;
   static_assert(RC::NRT == 1 && RC::NKC == 1, "16-token chunks");
-  constexpr int XW = 16 + 16 / (int)sizeof(E);  // LDS row stride (elements): 16 columns + 16 bytes
-  __shared__ __attribute__((aligned(16))) E xs[4][32 * XW];  // each wave's rows, transposed for stores
-  __shared__ floatx4 xp[2][4][64];                           // U~ parts, by chunk parity
-  __shared__ floatx4 xq[2][4][64];                           // (Q e^G) S parts
+  typedef typename Vec4<E>::T V4;
+  constexpr bool SW = !WANT_O;  // a store wave (wave 4) writes the states and U~
+  __shared__ floatx4 xp[2][4][64];  // U~ parts, by chunk parity
+  __shared__ floatx4 xq[WANT_O ? 2 : 1][4][WANT_O ? 64 : 1];  // (Q e^G) S parts
+  // by chunk parity: the state entering the chunk, tile rt (rows 16 rt ..) of the slab
+  // at [rt][lane][4] in accumulator order (lane (m, g) holds rows 4g .. 4g+3 of column
+  // m), and U~ the same way
+  __shared__ __attribute__((aligned(16))) E stg_s[SW ? 2 : 1][SW ? 8 * 64 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) E stg_u[SW ? 2 : 1][SW ? 64 * 4 : 4];
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
@@ -47,6 +59,38 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   if (u >= N * H) return;  // uniform over the work-group
   const int n = u / H, h = u - n * H;
   const size_t HD = (size_t)H * D;
+  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+
+  if constexpr (SW) {
+   if (w == 4) {
+    // the store wave: one barrier per chunk, as the compute waves, and one after the
+    // last. After the barrier of the chunk i-th from the start, that chunk's state
+    // and the previous chunk's U~ are in LDS until the next barrier but one. Lane
+    // (m, g) stores row m, columns 16 ct + 4 g .. + 3 of each tile, reading the four
+    // values from lanes 4 g .. 4 g + 3, slot m % 4, of the accumulator order.
+    auto gather = [&](const E* tile) {
+      V4 x;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) x[s4] = tile[(4 * g + s4 + 16 * (m >> 2)) * 4 + (m & 3)];
+      return x;
+    };
+    E* ut_h = ut + (size_t)h * mc * 16 * D + ((size_t)ct * 64 + lane) * 4;
+    for (int i = 0; c_begin + i < c_end; ++i) {
+      lds_barrier();
+      const int c = c_begin + i;
+      E* sp = states + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+        *reinterpret_cast<V4*>(sp + (size_t)rt * 8 * 64 * 4) = gather(&stg_s[i & 1][rt * 64 * 4]);
+      if (i > 0) *reinterpret_cast<V4*>(ut_h + (size_t)(c - 1) * 16 * D) = gather(stg_u[(i - 1) & 1]);
+    }
+    lds_barrier();
+    if (c_end > c_begin)
+      *reinterpret_cast<V4*>(ut_h + (size_t)(c_end - 1) * 16 * D) = gather(stg_u[(c_end - c_begin - 1) & 1]);
+    return;
+   }
+  }
+
   // state rows 32w + 16j + 4g + i, column 16ct + m
   const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
 
@@ -68,7 +112,6 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     floatx4 gm[2];
     int2 inf;
   };
-  const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   auto load = [&](Stage& st, int c) {
     const char* rb = records + ((size_t)h * mc + c) * RC::BYTES;
     const E* rec = reinterpret_cast<const E*>(rb);
@@ -88,19 +131,14 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
 
   auto compute = [&](const Stage& st, int c, int buf) {
     const FragT Sb = acc_pair_to_frag<E>(S[0], S[1]);  // k-block w of the state
-    E* xw = xs[w];
-    if (states) {  // this wave's 32 rows of the state entering the chunk: two whole tiles
+    if constexpr (SW) {  // this wave's two tiles of the state entering the chunk, to LDS
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        V4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xw[(16 * j + 4 * g + i) * XW + m] = from_f<E>(S[j][i]);
-      compiler_fence();
-      E* sp = states + ((size_t)h * mc + c) * D * D;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)  // lane (m, g): row 32w + 16j + m, columns 16ct + 4g .. + 3
-        *reinterpret_cast<typename Vec4<E>::T*>(sp + state_tile_index(32 * w + 16 * j + m, 16 * ct + 4 * g)) =
-            *reinterpret_cast<const typename Vec4<E>::T*>(&xw[(16 * j + m) * XW + 4 * g]);
-      compiler_fence();
+        for (int i = 0; i < 4; ++i) x[i] = from_f<E>(S[j][i]);
+        *reinterpret_cast<V4*>(&stg_s[buf][((2 * w + j) * 64 + lane) * 4]) = x;
+      }
     }
     // parts over this wave's 32 state rows: U - W S (U added once, by wave 0) and (Q e^G) S
     floatx4 up = w == 0 ? floatx4{to_f(st.uu[0]), to_f(st.uu[1]), to_f(st.uu[2]), to_f(st.uu[3])}
@@ -114,24 +152,24 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     }
     lds_barrier();
     const floatx4 Ut = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
-    if (ut && w == 0) {
+    if constexpr (SW) {
+      if (w == 0) {  // U~ to LDS, for the store wave after the next barrier
+        V4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xw[(4 * g + i) * XW + m] = from_f<E>(Ut[i]);
-      compiler_fence();
-      // 16 x 16 tile ct of this chunk's U~ in the state tile order: lane (m, g) stores
-      // row m, columns 16 ct + 4 g .. + 3
-      *reinterpret_cast<typename Vec4<E>::T*>(ut + ((size_t)h * mc + c) * 16 * D + ((size_t)ct * 64 + lane) * 4) =
-          *reinterpret_cast<const typename Vec4<E>::T*>(&xw[m * XW + 4 * g]);
-      compiler_fence();
+        for (int i = 0; i < 4; ++i) x[i] = from_f<E>(Ut[i]);
+        *reinterpret_cast<V4*>(&stg_u[buf][lane * 4]) = x;
+      }
     }
     const FragT Ub = acc_pair_to_frag<E>(Ut, floatx4{0.f, 0.f, 0.f, 0.f});
-    if (WANT_O && w == 1) {  // O = (Q e^G) S + P U~
-      floatx4 X = xq[buf][0][lane] + xq[buf][1][lane] + xq[buf][2][lane] + xq[buf][3][lane];
-      mma(X, st.pp, Ub);
+    if constexpr (WANT_O) {
+      if (w == 1) {  // O = (Q e^G) S + P U~
+        floatx4 X = xq[buf][0][lane] + xq[buf][1][lane] + xq[buf][2][lane] + xq[buf][3][lane];
+        mma(X, st.pp, Ub);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * g + i;
-        if (row < st.inf.y) o[(size_t)(st.inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * g + i;
+          if (row < st.inf.y) o[(size_t)(st.inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[i]);
+        }
       }
     }
     // S_w = Diag(e^{g_C}) S_w + (K e^{g_C - G})^T_w U~
@@ -194,6 +232,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
 #pragma unroll
     for (int j = 0; j < 4; ++j) tacc ^= tv[j];
   }
+  if constexpr (SW) lds_barrier();  // the store wave's last one: U~ of the last chunk
   // mc is never negative (the host sizes it from the shapes), so this never stores
   if (mc < 0 && tacc == 0u) o[lane] = from_f<E>(0.f);
   if (final_state) {
