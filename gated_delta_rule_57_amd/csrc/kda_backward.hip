@@ -394,16 +394,23 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
       E* dp = dstates + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-        *reinterpret_cast<V4*>(dp + (size_t)rt * 8 * 64 * 4) = gather(&stg_s[i & 1][rt * 64 * 4]);
-      if (i > 0) *reinterpret_cast<V4*>(dut_h + (size_t)(c + 1) * BC * D) = gather(stg_u[(i - 1) & 1]);
+        store_nt(reinterpret_cast<V4*>(dp + (size_t)rt * 8 * 64 * 4), gather(&stg_s[i & 1][rt * 64 * 4]));
+      if (i > 0) store_nt(reinterpret_cast<V4*>(dut_h + (size_t)(c + 1) * BC * D), gather(stg_u[(i - 1) & 1]));
     }
     lds_barrier();
     if (c_end > c_begin)
-      *reinterpret_cast<V4*>(dut_h + (size_t)c_begin * BC * D) = gather(stg_u[(c_end - c_begin - 1) & 1]);
+      store_nt(reinterpret_cast<V4*>(dut_h + (size_t)c_begin * BC * D), gather(stg_u[(c_end - c_begin - 1) & 1]));
     return;
   }
 
   const size_t sbase = (size_t)u * D * D + (size_t)(32 * w + 4 * g) * D + 16 * ct + m;
+  // first token and end of the sequence: chunk c starts at seq_t0 + (c - c_begin) BC
+  int seq_t0 = 0, seq_t1 = 0;
+  if (c_end > c_begin) {
+    const int2 first = info[c_begin], last = info[c_end - 1];
+    seq_t0 = first.x;
+    seq_t1 = last.x + last.y;
+  }
 
   floatx4 Lm[2];
 #pragma unroll
@@ -427,13 +434,15 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     return f;
   };
 
-  // a stage holds what the loads return (four elements as raw 32-bit words, grad_o
-  // as four scalars): building fragments at load time would make the wave wait for
-  // the data one step early; they are built where they are used
+  // a stage holds what the loads return (four elements as raw 32-bit words):
+  // building fragments at load time would make the wave wait for the data one step
+  // early; they are built where they are used. grad_o comes as one 4-element piece
+  // per lane, row lane / 4, columns 16 ct + 4 (lane % 4) .. + 3, and is regrouped
+  // into the fragment's columns by lane permutes (four scalar loads per lane, one per
+  // row, cost a sixth of the kernel's time).
   constexpr int RW = (int)(sizeof(V4) / 4);
   struct Stage {
-    unsigned wt[2][RW], qt[2][RW], pt[RW];
-    E dov[4];
+    unsigned wt[2][RW], qt[2][RW], pt[RW], dow[RW];
     FragT ke;
     floatx4 gm[2];
   };
@@ -466,15 +475,43 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     const float* gam = reinterpret_cast<const float*>(rb + BR::GAM);
 #pragma unroll
     for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
-    const int2 inf = info[c];
+    // the chunk's tokens follow from the sequence's (no address waits on a load);
+    // rows past len read row 0 and are zeroed
+    const int tok0 = seq_t0 + (c - c_begin) * BC, len = min(BC, seq_t1 - tok0);
+    const int r = lane >> 2;
+    const RawV d = *reinterpret_cast<const RawV*>(dout + (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D +
+                                                  16 * ct + 4 * (lane & 3));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int row = 4 * g + s;
-      st.dov[s] = row < inf.y ? dout[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] : from_f<E>(0.f);
-    }
+    for (int i = 0; i < RW; ++i) st.dow[i] = r < len ? d[i] : 0u;
   };
 
-  auto compute = [&](const Stage& st, int c, int buf) {
+  // B fragment of dO over the chunk rows: lane (m, g) takes row 4g + s, column m from
+  // lane (4g + s) * 4 + m / 4, element m % 4 (all 64 lanes active)
+  auto do_frag = [&](const Stage& st) {
+    FragT f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int src = ((4 * g + s) * 4 + (m >> 2)) * 4;  // byte address of the source lane
+      unsigned v[RW];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) v[i] = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)st.dow[i]);
+      if constexpr (RW == 2) {  // bf16: two elements per word
+        const unsigned wd = (m & 2) ? v[1] : v[0];
+        f[s] = __builtin_bit_cast(E, (unsigned short)((m & 1) ? (wd >> 16) : (wd & 0xffffu)));
+      } else {
+        const unsigned lo = (m & 1) ? v[1] : v[0], hi = (m & 1) ? v[3] : v[2];
+        f[s] = __builtin_bit_cast(E, (m & 2) ? hi : lo);
+      }
+      f[4 + s] = from_f<E>(0.f);
+    }
+    return f;
+  };
+  // the dO fragment of the chunk computed next, permuted one chunk early (after the
+  // barrier of the chunk before it), where its latency overlaps that chunk's work
+  FragT dOn;
+
+  auto compute = [&](const Stage& st, int c, int buf, const Stage& nx) {
+    const FragT dOb = dOn;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {  // this wave's two tiles of the gradient at the chunk's end, to LDS
       V4 x;
@@ -482,18 +519,13 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
       for (int i = 0; i < 4; ++i) x[i] = from_f<E>(Lm[j][i]);
       *reinterpret_cast<V4*>(&stg_s[buf][((2 * w + j) * 64 + lane) * 4]) = x;
     }
-    FragT dOb;  // B fragment of dO over the chunk rows
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      dOb[s] = st.dov[s];
-      dOb[4 + s] = from_f<E>(0.f);
-    }
     // this wave's part of dU~ = P^T dO + (K e^{g_C-G}) dS
     floatx4 dp4 = zero4;
     if (w == 0) mma(dp4, raw_frag(st.pt), dOb);
     mma(dp4, st.ke, acc_pair_to_frag<E>(Lm[0], Lm[1]));
     xp[buf][w][lane] = dp4;
     lds_barrier();
+    dOn = do_frag(nx);
     const floatx4 du = xp[buf][0][lane] + xp[buf][1][lane] + xp[buf][2][lane] + xp[buf][3][lane];
     if (w == 0) {  // dU~ to LDS, for the store wave after the next barrier
       V4 x;
@@ -511,18 +543,30 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     }
   };
 
-  // L2 touch STATE_TOUCH_AHEAD chunks beyond the register stage: each record line is
-  // read (one word) by one of the head's 32 waves, so the real loads hit in L2 (the
-  // words are XOR-folded into tacc, stored only by a never-taken branch). No address
-  // here depends on a load: that would make the wave wait.
+  // L2 touch STATE_TOUCH_AHEAD chunks beyond the register stage: each line of the
+  // record and of the chunk's grad_o rows is read (one word) by one of the head's 32
+  // waves, so the real loads hit in L2 (the words are XOR-folded into tacc, stored
+  // only by a never-taken branch). No address here depends on a load: that would make
+  // the wave wait.
   constexpr int LINES = (int)(BR::BYTES / 128);
-  static_assert(BR::BYTES % 128 == 0 && LINES <= 32 * 64, "one touch per lane");
-  // lanes past the record's last line touch that line again (an unconditional load
-  // is never merged with an old value)
+  constexpr int ROW_LINES = D * (int)sizeof(E) / 128;  // lines of one grad_o row of a head
+  constexpr int DO_PER_WAVE = BC * ROW_LINES / 32;     // grad_o lines each wave touches
+  static_assert(BR::BYTES % 128 == 0 && LINES <= 32 * (64 - DO_PER_WAVE), "one touch per lane");
+  // the last DO_PER_WAVE lanes touch grad_o; lanes past the record's last line touch
+  // that line again (an unconditional load is never merged with an old value)
+  const int do_line = (ct * 4 + w) * DO_PER_WAVE + (63 - lane);
+  const bool touch_do = lane >= 64 - DO_PER_WAVE;
   const int touch_line = min((ct * 4 + w) + 32 * lane, LINES - 1);
   unsigned tacc = 0u;
   auto touch = [&](int c) {
-    return *reinterpret_cast<const unsigned*>(brec + ((size_t)h * mc + c) * BR::BYTES + (size_t)touch_line * 128);
+    const int tok0 = seq_t0 + (c - c_begin) * BC, len = min(BC, seq_t1 - tok0);
+    const int r = do_line / ROW_LINES;
+    const unsigned* p =
+        touch_do ? reinterpret_cast<const unsigned*>(dout + (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D +
+                                                     (do_line % ROW_LINES) * (128 / (int)sizeof(E)))
+                 : reinterpret_cast<const unsigned*>(brec + ((size_t)h * mc + c) * BR::BYTES +
+                                                     (size_t)touch_line * 128);
+    return *p;
   };
 
   // four named stages, three chunks of operands in flight: step r of an iteration
@@ -533,6 +577,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     load(sa, c_end - 1);
     load(sb, max(c_end - 2, c_begin));
     load(sc, max(c_end - 3, c_begin));
+    dOn = do_frag(sa);
   }
   for (int c0 = c_end - 1; c0 >= c_begin; c0 -= 4) {
     // the iteration's four chunks: the first step touches the four beyond the touch
@@ -543,13 +588,13 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     const unsigned t1 = touch(max(c0 - 4 - STATE_TOUCH_AHEAD, c_begin));
     const unsigned t2 = touch(max(c0 - 5 - STATE_TOUCH_AHEAD, c_begin));
     const unsigned t3 = touch(max(c0 - 6 - STATE_TOUCH_AHEAD, c_begin));
-    compute(sa, c0, 0);
+    compute(sa, c0, 0, sb);
     load(sa, max(c0 - 4, c_begin));
-    if (c0 - 1 >= c_begin) compute(sb, c0 - 1, 1);
+    if (c0 - 1 >= c_begin) compute(sb, c0 - 1, 1, sc);
     load(sb, max(c0 - 5, c_begin));
-    if (c0 - 2 >= c_begin) compute(sc, c0 - 2, 0);
+    if (c0 - 2 >= c_begin) compute(sc, c0 - 2, 0, sd);
     load(sc, max(c0 - 6, c_begin));
-    if (c0 - 3 >= c_begin) compute(sd, c0 - 3, 1);
+    if (c0 - 3 >= c_begin) compute(sd, c0 - 3, 1, sa);
     tacc ^= t0 ^ t1 ^ t2 ^ t3;
   }
   lds_barrier();  // the store wave's last one: dU~ of the first chunk

@@ -122,6 +122,12 @@ __device__ __forceinline__ typename Frag<E>::T load_frag(const E* p) {
 
 // Ordering helpers for LDS exchanges between the waves of a work-group.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Non-temporal vector store of a 4-element vector (data read back only much later)
+template <typename V>
+__device__ __forceinline__ void store_nt(V* p, const V& x) {
+  typedef unsigned int U __attribute__((ext_vector_type(sizeof(V) / 4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(U, x), reinterpret_cast<U*>(p));
+}
 // s_waitcnt with lgkmcnt(0) and the vector-memory counter left free
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // work-group barrier for LDS exchanges that leaves in-flight global loads alone

@@ -19,9 +19,10 @@ namespace kda {
 // stores go out through a fifth wave: the four compute waves put their accumulator
 // registers into LDS (one 8-byte write per 16 x 16 tile and lane), and after the
 // chunk's barrier the store wave reads them back transposed and writes whole 16 x 16
-// tiles. On this architecture stores count in the same in-order counter as loads,
-// so a compute wave that stored would wait on its own store acknowledgements each
-// time it waits for the next chunk's operands.
+// tiles (non-temporal: only the gradient kernel reads them back). On this
+// architecture stores count in the same in-order counter as loads, so a compute
+// wave that stored would wait on its own store acknowledgements each time it waits
+// for the next chunk's operands.
 // ---------------------------------------------------------------------------
 constexpr int INTER16_LOOKAHEAD = 3;
 constexpr int INTER16_TOUCH_AHEAD = 4;
@@ -81,12 +82,12 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
       E* sp = states + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-        *reinterpret_cast<V4*>(sp + (size_t)rt * 8 * 64 * 4) = gather(&stg_s[i & 1][rt * 64 * 4]);
-      if (i > 0) *reinterpret_cast<V4*>(ut_h + (size_t)(c - 1) * 16 * D) = gather(stg_u[(i - 1) & 1]);
+        store_nt(reinterpret_cast<V4*>(sp + (size_t)rt * 8 * 64 * 4), gather(&stg_s[i & 1][rt * 64 * 4]));
+      if (i > 0) store_nt(reinterpret_cast<V4*>(ut_h + (size_t)(c - 1) * 16 * D), gather(stg_u[(i - 1) & 1]));
     }
     lds_barrier();
     if (c_end > c_begin)
-      *reinterpret_cast<V4*>(ut_h + (size_t)(c_end - 1) * 16 * D) = gather(stg_u[(c_end - c_begin - 1) & 1]);
+      store_nt(reinterpret_cast<V4*>(ut_h + (size_t)(c_end - 1) * 16 * D), gather(stg_u[(c_end - c_begin - 1) & 1]));
     return;
    }
   }
