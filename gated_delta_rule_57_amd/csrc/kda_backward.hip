@@ -78,8 +78,10 @@ __device__ __forceinline__ float sum16(float x) {
 // Per-(head, chunk) record for the reverse state pass, in the MFMA operand order
 // reverse state pass consumes (lane l = m + 16 g; the fragment convention of
 // kda_device.h, chunk rows padded to 32 with zeros):
-//   WT   [8 rt][64][4]  slot s of the A fragment of (-W)^T, channel tile rt: -W[4g+s][16rt+m]
-//   QTT  [8 rt][64][4]  the same for (Q e^G)^T
+//   WT   [4 w][64][2 j][4]  slot s of the A fragment of (-W)^T for channel tile
+//                           rt = 2w + j: -W[4g+s][16rt+m] (the two tiles that wave w of
+//                           the reverse pass uses are one 8-element piece per lane)
+//   QTT  [4 w][64][2 j][4]  the same for (Q e^G)^T
 //   KEF  [4 kb][64][8]  A fragment of K e^{g_C-G} (rows m, channels 32 kb + koff(g, s))
 //   PT   [64][4]        A fragment of P^T: P[4g+s][m]
 //   GAM  float[128]     e^{g_C}
@@ -298,22 +300,22 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   E* qtt = reinterpret_cast<E*>(rb + BR::QTT);
   E* kef = reinterpret_cast<E*>(rb + BR::KEF);
   const FragT ta = rows_frag<E>(g, [&](int u) { return L.T[m][u]; });  // A: row m of T
+  FragT wf, qf;  // channel tiles 2w and 2w + 1, one piece per lane
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int nt = 2 * w + j, ch = 16 * nt + m;
     floatx4 wacc = {0.f, 0.f, 0.f, 0.f};
     mma(wacc, ta, rows_frag<E>(g, [&](int u) { return L.beta[u] * L.K[u][ch] * exp2_hw(L.G[u][ch]); }));
-    V4 wv, qv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // element i: row 4g+i, channel ch
       const int r = 4 * g + i;
       const float gr = L.G[r][ch];
-      wv[i] = from_f<E>(-wacc[i]);
-      qv[i] = from_f<E>(L.Q[r][ch] * exp2_hw(gr));
+      wf[4 * j + i] = from_f<E>(-wacc[i]);
+      qf[4 * j + i] = from_f<E>(L.Q[r][ch] * exp2_hw(gr));
     }
-    *reinterpret_cast<V4*>(wt + ((size_t)nt * 64 + lane) * 4) = wv;
-    *reinterpret_cast<V4*>(qtt + ((size_t)nt * 64 + lane) * 4) = qv;
   }
+  store_frag<E>(wt + ((size_t)w * 64 + lane) * 8, wf);
+  store_frag<E>(qtt + ((size_t)w * 64 + lane) * 8, qf);
   {  // K e^{g_C-G} as the A fragment of k-block w: lane (m, g) builds its whole slot (row
      // m, channels 32 w + koff(g, s)), so each wave writes 1 KiB contiguously
     FragT kf;
@@ -358,6 +360,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   // four elements kept as raw 32-bit words while loading (packed bf16 vectors in a
   // struct otherwise end up in scratch)
   typedef unsigned int RawV __attribute__((ext_vector_type(sizeof(V4) / 4)));
+  typedef unsigned int RawV2 __attribute__((ext_vector_type(2 * sizeof(V4) / 4)));
   __shared__ floatx4 xp[2][4][64];  // dU~ parts, by chunk parity
   // by chunk parity: dS at the chunk's end, tile rt (rows 16 rt ..) of the slab at
   // [rt][lane][4] in accumulator order (lane (m, g) holds rows 4g .. 4g+3 of column m),
@@ -456,18 +459,19 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     const char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
     const E* wt = reinterpret_cast<const E*>(rb + BR::WT);
     const E* qt = reinterpret_cast<const E*>(rb + BR::QTT);
+    {  // channel tiles 2w and 2w + 1: one piece per lane
+      const RawV2 a = *reinterpret_cast<const RawV2*>(wt + ((size_t)w * 64 + lane) * 8);
+      const RawV2 q = *reinterpret_cast<const RawV2*>(qt + ((size_t)w * 64 + lane) * 8);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const RawV a = *reinterpret_cast<const RawV*>(wt + ((size_t)(2 * w + j) * 64 + lane) * 4);
-      const RawV q = *reinterpret_cast<const RawV*>(qt + ((size_t)(2 * w + j) * 64 + lane) * 4);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        st.wt[j][i] = a[i];
-        st.qt[j][i] = q[i];
-      }
+        for (int i = 0; i < RW; ++i) {
+          st.wt[j][i] = a[j * RW + i];
+          st.qt[j][i] = q[j * RW + i];
+        }
     }
     st.ke = load_frag<E>(reinterpret_cast<const E*>(rb + BR::KEF) + ((size_t)w * 64 + lane) * 8);
-    {
+    if (w == 0) {  // P^T dO is formed by wave 0 only (w is uniform over the wave)
       const RawV p4 = *reinterpret_cast<const RawV*>(reinterpret_cast<const E*>(rb + BR::PT) + (size_t)lane * 4);
 #pragma unroll
       for (int i = 0; i < RW; ++i) st.pt[i] = p4[i];
