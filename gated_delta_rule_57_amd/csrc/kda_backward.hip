@@ -447,7 +447,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   struct Stage {
     unsigned wt[2][RW], qt[2][RW], pt[RW], dow[RW];
     FragT ke;
-    floatx4 gm[2];
+    float gw;  // e^{g_C} of row 32w + row_word_index(m, g)
   };
   auto raw_frag = [&](const unsigned* r) {
     RawV x;
@@ -477,8 +477,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
       for (int i = 0; i < RW; ++i) st.pt[i] = p4[i];
     }
     const float* gam = reinterpret_cast<const float*>(rb + BR::GAM);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
+    st.gw = gam[32 * w + row_word_index(m, g)];
     // the chunk's tokens follow from the sequence's (no address waits on a load);
     // rows past len read row 0 and are zeroed
     const int tok0 = seq_t0 + (c - c_begin) * BC, len = min(BC, seq_t1 - tok0);
@@ -539,9 +538,11 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     }
     const FragT dUb = acc_pair_to_frag<E>(du, zero4);
     // dS0_w = e^{g_C} o dS_w + (Q e^G)^T_w dO + (-W)^T_w dU~
+    floatx4 gm[2];
+    rows_from_word(st.gw, m, gm);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      Lm[j] = st.gm[j] * Lm[j];
+      Lm[j] = gm[j] * Lm[j];
       mma(Lm[j], raw_frag(st.qt[j]), dOb);
       mma(Lm[j], raw_frag(st.wt[j]), dUb);
     }

@@ -122,6 +122,26 @@ __device__ __forceinline__ typename Frag<E>::T load_frag(const E* p) {
 
 // Ordering helpers for LDS exchanges between the waves of a work-group.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Per-row factors of a wave's 32 state rows in the accumulator layout (lane (m, g)
+// needs rows 16 j + 4 g + i, j = 0, 1, i = 0..3) from one word per lane: lane (m, g)
+// loads row row_word_index(m, g) = 16 ((m >> 3) & 1) + 4 g + (m & 3), and the eight
+// values it needs come from its own 16-lane row by DPP moves (a rotation by 8 for the
+// other j, a quad broadcast for each i), with no memory or LDS traffic.
+__device__ __forceinline__ int row_word_index(int m, int g) { return 16 * ((m >> 3) & 1) + 4 * g + (m & 3); }
+__device__ __forceinline__ void rows_from_word(float v, int m, floatx4 out[2]) {
+  const int own = __builtin_bit_cast(int, v);
+  const int other = __builtin_amdgcn_mov_dpp(own, 0x128, 0xF, 0xF, true);  // row_ror:8
+  const bool hi = ((m >> 3) & 1) != 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int x = (hi == (j == 1)) ? own : other;  // lane (m, g) now holds row 16 j + 4 g + (m & 3)
+    out[j][0] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, true));  // quad lane 0
+    out[j][1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, true));  // quad lane 1
+    out[j][2] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, true));  // quad lane 2
+    out[j][3] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, true));  // quad lane 3
+  }
+}
+
 // Non-temporal vector store of a 4-element vector (data read back only much later)
 template <typename V>
 __device__ __forceinline__ void store_nt(V* p, const V& x) {

@@ -110,7 +110,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
   struct Stage {
     FragT wn, qt, ke[2], pp;
     typename Vec4<E>::T uu;
-    floatx4 gm[2];
+    float gw;  // e^{g_C} of row 32w + row_word_index(m, g)
     int2 inf;
   };
   auto load = [&](Stage& st, int c) {
@@ -125,8 +125,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     for (int j = 0; j < 2; ++j) st.ke[j] = load_frag<E>(rec + RC::KE + ((size_t)(2 * w + j) * 64 + lane) * 8);
     st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
     const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
+    st.gw = gam[32 * w + row_word_index(m, g)];
     st.inf = info[c];
   };
 
@@ -174,9 +173,11 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
       }
     }
     // S_w = Diag(e^{g_C}) S_w + (K e^{g_C - G})^T_w U~
+    floatx4 gm[2];
+    rows_from_word(st.gw, m, gm);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      S[j] = st.gm[j] * S[j];
+      S[j] = gm[j] * S[j];
       mma(S[j], st.ke[j], Ub);
     }
   };
