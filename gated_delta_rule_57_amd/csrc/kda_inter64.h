@@ -164,15 +164,17 @@ constexpr int INTER_LOOKAHEAD = 1;
 // chunks beyond the lookahead whose record lines are pulled into L2 ahead of use
 constexpr int INTER_TOUCH_AHEAD = 4;
 
+// gw: e^{g_C} of state row 32 w + row_word_index(m, g) (spread to the lane's eight
+// rows by DPP moves where it is used)
 template <bool DP> struct InterStage {
   bf16x8 wn[4], qt[4], ke[4], pp[2];
   bf16x4 uu;
-  floatx4 gm[2];
+  float gw;
 };
 template <> struct InterStage<true> {
   bf16x8 wn[4], qt[4], ke[4], pp[2], kv[4], vb[2];
   bf16x4 uu, oi;
-  floatx4 gm[2];
+  float gw;
 };
 
 }  // namespace
@@ -245,9 +247,7 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
         st.vb[kb] = *reinterpret_cast<const bf16x8*>(rb + (RC::VB * 2) + (2 * ct + kb) * 1024 + lo16);
       st.oi = *reinterpret_cast<const bf16x4*>(rb + (RC::OI * 2) + ((ct * 4 + w) * 64 + lane) * 8);
     }
-    const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) st.gm[j] = *reinterpret_cast<const floatx4*>(gam + 32 * w + 16 * j + 4 * g);
+    st.gw = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES)[32 * w + row_word_index(m, g)];
   };
 
   auto compute = [&](const InterStage<DP>& st, int c) {
@@ -269,8 +269,10 @@ __global__ void __launch_bounds__(256) inter_wg_kernel(const char* __restrict__ 
       *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(xU) + ((w >> 1) * 64 + lane) * 16 + (w & 1) * 8) = uh;
     }
     // e^{g_C} S_w, ahead of the barrier
+    floatx4 gm[2];
+    rows_from_word(st.gw, m, gm);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Sw[j] = st.gm[j] * Sw[j];
+    for (int j = 0; j < 2; ++j) Sw[j] = gm[j] * Sw[j];
     lds_barrier();
     bf16x8 Ub[2];
 #pragma unroll
