@@ -47,6 +47,8 @@
 // log_alpha <= 0 precondition).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_inter16.h"
 #include "kda_internal.h"
@@ -60,6 +62,11 @@ static_assert(BC == 16, "the backward kernels are written for 16-token chunks");
 constexpr int LDP = D + 4;  // row stride of the fp32 [16][128] LDS matrices: rows 4 apart fall
                             // 16 banks apart, so accumulator-layout reads are conflict-free
 constexpr int LDS16 = BC + 1;
+// row stride of the [16][128] k and q LDS matrices by element type: bf16 rows 144
+// elements (72 words) apart put four consecutive rows 8 banks apart, so a wave reading
+// 16 consecutive channels of 4 rows touches 32 distinct banks
+template <typename E> struct LdsStride { static constexpr int v = LDP; };
+template <> struct LdsStride<__bf16> { static constexpr int v = D + 16; };
 constexpr float LOG2E_B = 1.4426950408889634f;
 
 __host__ __device__ constexpr size_t bal256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -118,6 +125,29 @@ __device__ __forceinline__ void load8(const E* base, size_t row_stride, int r, i
   }
 }
 
+// Copies eight consecutive values of row r (zeros past len) to dst, as KT.
+template <typename E, typename KT>
+__device__ __forceinline__ void copy8(const E* base, size_t row_stride, int r, int len, int c0, KT* dst) {
+  if constexpr (std::is_same<E, KT>::value) {
+    typedef typename Vec4<E>::T V4;
+    V4 a, b;
+    if (r < len) {
+      a = *reinterpret_cast<const V4*>(base + (size_t)r * row_stride + c0);
+      b = *reinterpret_cast<const V4*>(base + (size_t)r * row_stride + c0 + 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = b[i] = from_f<E>(0.f);
+    }
+    *reinterpret_cast<V4*>(dst) = a;
+    *reinterpret_cast<V4*>(dst + 4) = b;
+  } else {
+    float x[8];
+    load8(base, row_stride, r, len, c0, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = x[i];
+  }
+}
+
 // The state-independent part shared by both per-chunk kernels: q, k rows, the
 // log2-unit decay cumsum G, the per-channel reference b, M_rs = sum_i k_ri k_si
 // 2^(G_ri - G_si) for s < r, optionally P_rs = sum_i q_ri k_si 2^(G_ri - G_si) for
@@ -131,8 +161,12 @@ __device__ __forceinline__ void load8(const E* base, size_t row_stride, int r, i
 // the element-wise path, 2^-|G_r - G_s| per term.
 constexpr float FACTOR_MAX_RANGE = 120.f;
 
+// KT: element type of the k and q copies (the input type keeps them exact and halves
+// their LDS in bf16; the gradient kernel keeps fp32 copies)
+template <typename KT>
 struct LocalLds {
-  float K[BC][LDP], Q[BC][LDP], G[BC][LDP];
+  KT K[BC][LdsStride<KT>::v], Q[BC][LdsStride<KT>::v];
+  float G[BC][LDP];
   float M[BC][LDS16], T[BC][LDS16], Pm[BC][LDS16];
   float beta[BC];
   float bref[D];
@@ -169,8 +203,8 @@ __device__ __forceinline__ typename Frag<E>::T rows_frag(int g, F f) {
   return x;
 }
 
-template <typename E, bool WANT_P>
-__device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __restrict__ k,
+template <typename E, bool WANT_P, typename KT>
+__device__ void local_forward(LocalLds<KT>& L, const E* __restrict__ q, const E* __restrict__ k,
                               const float* __restrict__ log_alpha, const float* __restrict__ beta, int tok0, int len,
                               int h, int H, int t) {
   typedef typename Frag<E>::T FragT;
@@ -179,13 +213,9 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   {
     const size_t base = (size_t)tok0 * HD + (size_t)h * D;
+    copy8(k + base, HD, rm.r, len, rm.c0, &L.K[rm.r][rm.c0]);
+    copy8(q + base, HD, rm.r, len, rm.c0, &L.Q[rm.r][rm.c0]);
     float x[8];
-    load8(k + base, HD, rm.r, len, rm.c0, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L.K[rm.r][rm.c0 + i] = x[i];
-    load8(q + base, HD, rm.r, len, rm.c0, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L.Q[rm.r][rm.c0 + i] = x[i];
     load8(log_alpha + base, HD, rm.r, len, rm.c0, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) L.G[rm.r][rm.c0 + i] = x[i];
@@ -214,10 +244,10 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int ch = 32 * kb + koff(g, s);
-          const float kv = L.K[m][ch], d = L.G[m][ch] - L.bref[ch];
+          const float kv = to_f(L.K[m][ch]), d = L.G[m][ch] - L.bref[ch];
           lk[s] = from_f<E>(kv * exp2_hw(d));
           rk[s] = from_f<E>(kv * exp2_hw(-d));
-          if constexpr (WANT_P) lq[s] = from_f<E>(L.Q[m][ch] * exp2_hw(d));
+          if constexpr (WANT_P) lq[s] = from_f<E>(to_f(L.Q[m][ch]) * exp2_hw(d));
         }
         mma(pk, lk, rk);  // lane (m, g): sum_ch Lk[4g+i][ch] Rk[m][ch]
         if constexpr (WANT_P) mma(pq, lq, rk);
@@ -233,8 +263,8 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
     float kr[8], qr[8], gr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      kr[i] = L.K[rm.r][rm.ch(i)];
-      qr[i] = L.Q[rm.r][rm.ch(i)];
+      kr[i] = to_f(L.K[rm.r][rm.ch(i)]);
+      qr[i] = to_f(L.Q[rm.r][rm.ch(i)]);
       gr[i] = L.G[rm.r][rm.ch(i)];
     }
 #pragma unroll
@@ -243,7 +273,7 @@ __device__ void local_forward(LocalLds& L, const E* __restrict__ q, const E* __r
       if (s <= rm.r) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float ks = L.K[s][rm.ch(i)] * exp2_hw(gr[i] - L.G[s][rm.ch(i)]);  // exponent <= 0
+          const float ks = to_f(L.K[s][rm.ch(i)]) * exp2_hw(gr[i] - L.G[s][rm.ch(i)]);  // exponent <= 0
           pk += kr[i] * ks;
           if constexpr (WANT_P) pq += qr[i] * ks;
         }
@@ -287,7 +317,7 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   using BR = BRec<E>;
   typedef typename Frag<E>::T FragT;
   typedef typename Vec4<E>::T V4;
-  __shared__ LocalLds L;
+  __shared__ LocalLds<E> L;
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
   if (c >= *total_chunks) return;
   const int t = threadIdx.x;
@@ -305,13 +335,13 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   for (int j = 0; j < 2; ++j) {
     const int nt = 2 * w + j, ch = 16 * nt + m;
     floatx4 wacc = {0.f, 0.f, 0.f, 0.f};
-    mma(wacc, ta, rows_frag<E>(g, [&](int u) { return L.beta[u] * L.K[u][ch] * exp2_hw(L.G[u][ch]); }));
+    mma(wacc, ta, rows_frag<E>(g, [&](int u) { return L.beta[u] * to_f(L.K[u][ch]) * exp2_hw(L.G[u][ch]); }));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // element i: row 4g+i, channel ch
       const int r = 4 * g + i;
       const float gr = L.G[r][ch];
       wf[4 * j + i] = from_f<E>(-wacc[i]);
-      qf[4 * j + i] = from_f<E>(L.Q[r][ch] * exp2_hw(gr));
+      qf[4 * j + i] = from_f<E>(to_f(L.Q[r][ch]) * exp2_hw(gr));
     }
   }
   store_frag<E>(wt + ((size_t)w * 64 + lane) * 8, wf);
@@ -322,7 +352,7 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int ch = 32 * w + koff(g, s);
-      kf[s] = from_f<E>(L.K[m][ch] * exp2_hw(L.G[BC - 1][ch] - L.G[m][ch]));
+      kf[s] = from_f<E>(to_f(L.K[m][ch]) * exp2_hw(L.G[BC - 1][ch] - L.G[m][ch]));
     }
     store_frag<E>(kef + ((size_t)w * 64 + lane) * 8, kf);
   }
@@ -644,7 +674,7 @@ __global__ void __launch_bounds__(320) bwd_state_kernel(const char* __restrict__
 // rows are MFMAs on factored operands (element-wise on the exact path).
 // ---------------------------------------------------------------------------
 struct ChunkLds {
-  LocalLds L;
+  LocalLds<float> L;
   float V[BC][LDP];
   float dU[BC][LDP];  // dU~
   float X2[BC][LDP];  // dU~ S0^T
@@ -671,7 +701,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     E* __restrict__ dk, E* __restrict__ dv, float* __restrict__ dlog_alpha, float* __restrict__ dbeta) {
   typedef typename Frag<E>::T FragT;
   __shared__ ChunkLds S;
-  LocalLds& L = S.L;
+  LocalLds<float>& L = S.L;
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
   if (c >= *total_chunks) return;
   const int t = threadIdx.x;
@@ -752,7 +782,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     for (int s = 0; s < 8; ++s) {
       const int ch = 32 * w + koff(g, s);
       ax[s] = from_f<E>(-S.X2[m][ch]);
-      bk[s] = from_f<E>(L.K[m][ch] * exp2_hw(L.G[m][ch]));
+      bk[s] = from_f<E>(to_f(L.K[m][ch]) * exp2_hw(L.G[m][ch]));
       au[s] = from_f<E>(S.dU[m][ch]);
       bv[s] = from_f<E>(S.V[m][ch]);
     }
@@ -804,11 +834,11 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     mma(dbk, aTt, rows_frag<E>(g, [&](int u) { return S.X2[u][ch]; }));  // T^T X2 = -dB_K
     mma(dbv, aTt, rows_frag<E>(g, [&](int u) { return S.dU[u][ch]; }));  // T^T dU = dB_V
     if (!exact) {
-      const FragT brk = rows_frag<E>(g, [&](int u) { return L.K[u][ch] * exp2_hw(bch - L.G[u][ch]); });
+      const FragT brk = rows_frag<E>(g, [&](int u) { return to_f(L.K[u][ch]) * exp2_hw(bch - L.G[u][ch]); });
       mma(ra, adA, brk);
       mma(rp, adP, brk);
-      mma(rat, adAt, rows_frag<E>(g, [&](int u) { return L.K[u][ch] * exp2_hw(L.G[u][ch] - bch); }));
-      mma(rpt, adPt, rows_frag<E>(g, [&](int u) { return L.Q[u][ch] * exp2_hw(L.G[u][ch] - bch); }));
+      mma(rat, adAt, rows_frag<E>(g, [&](int u) { return to_f(L.K[u][ch]) * exp2_hw(L.G[u][ch] - bch); }));
+      mma(rpt, adPt, rows_frag<E>(g, [&](int u) { return to_f(L.Q[u][ch]) * exp2_hw(L.G[u][ch] - bch); }));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float d = L.G[4 * g + i][ch] - bch;
@@ -827,11 +857,11 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
         const float gr = L.G[r][ch];
         for (int u = 0; u < BC; ++u) {
           const float f = exp2_hw(-fabsf(gr - L.G[u][ch]));
-          const float ku = L.K[u][ch] * f;
+          const float ku = to_f(L.K[u][ch]) * f;
           ra[i] += S.dT[r][u] * ku;
           rp[i] += S.dP[r][u] * ku;
           rat[i] += L.beta[u] * S.dT[u][r] * ku;
-          rpt[i] += S.dP[u][r] * L.Q[u][ch] * f;
+          rpt[i] += S.dP[u][r] * to_f(L.Q[u][ch]) * f;
         }
       }
     }
@@ -841,7 +871,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
       const float gr = L.G[r][ch], er = exp2_hw(gr), el = exp2_hw(gl - gr);
-      const float kr = L.K[r][ch], qr = L.Q[r][ch], br = L.beta[r];
+      const float kr = to_f(L.K[r][ch]), qr = to_f(L.Q[r][ch]), br = L.beta[r];
       const float bk_ = -dbk[i], bv_ = dbv[i], x1 = x1r[j][i], x3 = x3r[j][i];
       const float dqv = x1 * er + rp[i];
       const float dkv = br * bk_ * er + br * ra[i] + rat[i] + rpt[i] + x3 * el;
