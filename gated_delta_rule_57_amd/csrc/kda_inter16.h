@@ -123,7 +123,8 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) st.ke[j] = load_frag<E>(rec + RC::KE + ((size_t)(2 * w + j) * 64 + lane) * 8);
-    st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
+    if (w == 0)  // U is added by wave 0 only (w is uniform over the wave)
+      st.uu = *reinterpret_cast<const typename Vec4<E>::T*>(rec + RC::UU + ((size_t)ct * 64 + lane) * 4);
     const float* gam = reinterpret_cast<const float*>(rb + RC::GAMMA_BYTES);
     st.gw = gam[32 * w + row_word_index(m, g)];
     st.inf = info[c];
