@@ -623,8 +623,7 @@ hipError_t launch_dplr_typed(const void* q, const void* k, const void* v, const 
                          (__bf16*)o, N, H, (int)mc);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, DC, true>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
-                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr,
-                         (E*)nullptr);
+                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);
     }
     e = hipGetLastError();
     trace_mark(stream, 2);

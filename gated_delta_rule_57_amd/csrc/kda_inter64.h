@@ -17,8 +17,6 @@ namespace kda {
 // the sequence's chunks. Work-group ids are laid out so that the eight slabs of
 // one (sequence, head) land on the same XCD (ids are dealt to the 8 XCDs round
 // robin), where they share that XCD's L2 copy of the chunk records.
-// It can also keep, per (head, chunk), the state entering the chunk (states,
-// [H][mc][128][128]) and U~ = U - W S ([H][mc][C][128]); o may then be null.
 // With DP set it runs the general diagonal-plus-low-rank recurrence from RecD
 // records: W = U + W_b S takes the place of U~, O gains M_qk V and the state
 // update gains (K e^{g_C-G})^T V.
@@ -29,7 +27,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
                                                    const int2* __restrict__ info,
                                                    const float* __restrict__ initial_state,
                                                    float* __restrict__ final_state, E* __restrict__ o, int N,
-                                                   int H, int mc, E* __restrict__ states, E* __restrict__ ut) {
+                                                   int H, int mc) {
   using RC = typename std::conditional<DP, RecD<E, C>, Rec<E, C>>::type;
   typedef typename Frag<E>::T FragT;
   constexpr int NRT = RC::NRT, NKC = RC::NKC;
@@ -64,13 +62,6 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
     FragT Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = acc_pair_to_frag<E>(S[2 * kb], S[2 * kb + 1]);
-    if (states) {
-      E* sp = states + ((size_t)h * mc + c) * D * D + 16 * ct + m;
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * rt + 4 * g + i) * D] = from_f<E>(S[rt][i]);
-    }
 
     // U~ = U - W S  (the record holds -W; for DP, W = U + W_b S with W_b held)
     floatx4 Ut[NRT];
@@ -82,11 +73,6 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         mma(Ut[rt], load_frag<E>(rec + RC::WN + ((size_t)(rt * 4 + kb) * 64 + lane) * 8), Sb[kb]);
-      if (ut) {
-        E* up = ut + ((size_t)h * mc + c) * C * D + 16 * ct + m;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) up[(size_t)(16 * rt + 4 * g + i) * D] = from_f<E>(Ut[rt][i]);
-      }
     }
     // (Q e^G) S
     floatx4 X[NRT];
@@ -115,7 +101,7 @@ __global__ void __launch_bounds__(64) inter_kernel(const char* __restrict__ reco
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rt + 4 * g + i;
-        if (o && row < inf.y) o[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[rt][i]);
+        if (row < inf.y) o[(size_t)(inf.x + row) * HD + (size_t)h * D + 16 * ct + m] = from_f<E>(X[rt][i]);
       }
     }
     // S = Diag(e^{g_C}) S + (K e^{g_C - G})^T U~   (DP: + (K e^{g_C-G})^T V)

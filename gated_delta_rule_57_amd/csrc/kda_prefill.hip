@@ -783,8 +783,9 @@ __global__ void __launch_bounds__(256) inter16_kernel(const char* __restrict__ r
                                                       const int2* __restrict__ info,
                                                       const float* __restrict__ initial_state,
                                                       float* __restrict__ final_state, E* __restrict__ o, int N, int H,
-                                                      int mc, E* __restrict__ states, E* __restrict__ ut) {
-  inter16_body<E, true>(blockIdx.x, records, chunk_off, info, initial_state, final_state, o, N, H, mc, states, ut);
+                                                      int mc) {
+  inter16_body<E, true>(blockIdx.x, records, chunk_off, info, initial_state, final_state, o, N, H, mc, nullptr,
+                        nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -862,11 +863,10 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
                          H, (int)mc);
     } else if constexpr (C == 16) {
       hipLaunchKernelGGL(inter16_kernel<E>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream, records, chunk_off,
-                         info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr, (E*)nullptr);
+                         info, initial_state, final_state, (E*)o, N, H, (int)mc);
     } else {
       hipLaunchKernelGGL((inter_kernel<E, C>), dim3((unsigned)(slots * 64)), dim3(64), 0, stream, records,
-                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc, (E*)nullptr,
-                         (E*)nullptr);
+                         chunk_off, info, initial_state, final_state, (E*)o, N, H, (int)mc);
     }
     e = hipGetLastError();
     trace_mark(stream, 2);
