@@ -173,14 +173,16 @@ struct LocalLds {
   int exact;
 };
 
-// Fragment over row 16 nt + m of a tiled 128 x 128 matrix (state_tile_index), k running
-// over columns 32 kb + koff(g, s): slots 0..3 come from tile (nt, 2 kb) and 4..7 from
-// tile (nt, 2 kb + 1), lane m + 16 g in both, so each is one contiguous load per wave.
-template <typename E>
+// Fragment over row 16 nt + m of a tiled matrix, k running over columns
+// 32 kb + koff(g, s): slots 0..3 come from tile (nt, 2 kb) and 4..7 from tile
+// (nt, 2 kb + 1), lane m + 16 g in both, so each is one contiguous load per wave.
+// TS: tile (r, t) starts at element (t * TS + r) * 256 (state_tile_index: TS = 8;
+// row_tile_index, one row of tiles: TS = 1, nt = 0).
+template <typename E, int TS>
 __device__ __forceinline__ typename Frag<E>::T tile_frag(const E* __restrict__ M, int nt, int kb, int lane) {
   typedef typename Vec4<E>::T V4;
-  const V4 lo = *reinterpret_cast<const V4*>(M + ((size_t)(nt * 8 + 2 * kb) * 64 + lane) * 4);
-  const V4 hi = *reinterpret_cast<const V4*>(M + ((size_t)(nt * 8 + 2 * kb + 1) * 64 + lane) * 4);
+  const V4 lo = *reinterpret_cast<const V4*>(M + ((size_t)(2 * kb * TS + nt) * 64 + lane) * 4);
+  const V4 hi = *reinterpret_cast<const V4*>(M + ((size_t)((2 * kb + 1) * TS + nt) * 64 + lane) * 4);
   typename Frag<E>::T f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -411,8 +413,8 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
   if (w == 4) {
     // the store wave: one barrier per chunk, as the compute waves, and one after the
     // last. After the barrier of the chunk i-th from the end, that chunk's dS_C and the
-    // dU~ of the chunk after it are in LDS until the next barrier but one. Lane (m, g)
-    // stores row m, columns 16 ct + 4 g .. + 3 of each tile, reading the four values
+    // dU~ of the chunk after it are in LDS until the next barrier but one. For dU~
+    // lane (m, g) stores row m, columns 16 ct + 4 g .. + 3, reading the four values
     // from lanes 4 g .. 4 g + 3, slot m % 4, of the accumulator order.
     auto gather = [&](const E* tile) {
       V4 x;
@@ -424,10 +426,7 @@ __device__ __forceinline__ void bwd_state_body(int b, const char* __restrict__ b
     for (int i = 0; c_end - 1 - i >= c_begin; ++i) {
       lds_barrier();
       const int c = c_end - 1 - i;
-      E* dp = dstates + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-        store_nt(reinterpret_cast<V4*>(dp + (size_t)rt * 8 * 64 * 4), gather(&stg_s[i & 1][rt * 64 * 4]));
+      store_state_slab(dstates + ((size_t)h * mc + c) * D * D + (size_t)ct * 2048, stg_s[i & 1], lane);
       if (i > 0) store_nt(reinterpret_cast<V4*>(dut_h + (size_t)(c + 1) * BC * D), gather(stg_u[(i - 1) & 1]));
     }
     lds_barrier();
@@ -722,8 +721,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     load8(v + rowbase, HD, rm.r, len, rm.c0, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) S.V[rm.r][rm.c0 + i] = x[i];
-    load4f(dUt + state_tile_index(rm.r, rm.c0), x);
-    load4f(dUt + state_tile_index(rm.r, rm.c0 + 4), x + 4);
+    load4f(dUt + row_tile_index(rm.r, rm.c0), x);
+    load4f(dUt + row_tile_index(rm.r, rm.c0 + 4), x + 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) S.dU[rm.r][rm.c0 + i] = x[i];
   }
@@ -737,8 +736,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       a1[kb] = m < len ? frag_rowk<E>(dout + rowbase, (int)HD, m, 32 * kb, g) : zero_frag<E>();
-      a2[kb] = tile_frag<E>(dUt, 0, kb, lane);
-      a3[kb] = tile_frag<E>(Ut, 0, kb, lane);
+      a2[kb] = tile_frag<E, 1>(dUt, 0, kb, lane);
+      a3[kb] = tile_frag<E, 1>(Ut, 0, kb, lane);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -748,8 +747,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         // row 16 nt + m over columns 32 kb + koff(g, s): tiles (nt, 2 kb) and (nt, 2 kb + 1)
-        const FragT bs = tile_frag<E>(S0, nt, kb, lane);
-        const FragT bd = tile_frag<E>(dSC, nt, kb, lane);
+        const FragT bs = tile_frag<E, 8>(S0, nt, kb, lane);
+        const FragT bd = tile_frag<E, 8>(dSC, nt, kb, lane);
         mma(x1, a1[kb], bs);
         mma(x2, a2[kb], bs);
         mma(x3, a3[kb], bd);
@@ -767,7 +766,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     if (w == 0) {  // dP = tril(dO U~^T)
       floatx4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(p, a1[kb], tile_frag<E>(Ut, 0, kb, lane));
+      for (int kb = 0; kb < 4; ++kb) mma(p, a1[kb], tile_frag<E, 1>(Ut, 0, kb, lane));
 #pragma unroll
       for (int i = 0; i < 4; ++i) S.dP[4 * g + i][m] = m <= 4 * g + i ? p[i] : 0.f;
     }

@@ -66,9 +66,9 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
    if (w == 4) {
     // the store wave: one barrier per chunk, as the compute waves, and one after the
     // last. After the barrier of the chunk i-th from the start, that chunk's state
-    // and the previous chunk's U~ are in LDS until the next barrier but one. Lane
-    // (m, g) stores row m, columns 16 ct + 4 g .. + 3 of each tile, reading the four
-    // values from lanes 4 g .. 4 g + 3, slot m % 4, of the accumulator order.
+    // and the previous chunk's U~ are in LDS until the next barrier but one. For U~
+    // lane (m, g) stores row m, columns 16 ct + 4 g .. + 3, reading the four values
+    // from lanes 4 g .. 4 g + 3, slot m % 4, of the accumulator order.
     auto gather = [&](const E* tile) {
       V4 x;
 #pragma unroll
@@ -79,10 +79,7 @@ __device__ __forceinline__ void inter16_body(int b, const char* __restrict__ rec
     for (int i = 0; c_begin + i < c_end; ++i) {
       lds_barrier();
       const int c = c_begin + i;
-      E* sp = states + ((size_t)h * mc + c) * D * D + ((size_t)ct * 64 + lane) * 4;
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-        store_nt(reinterpret_cast<V4*>(sp + (size_t)rt * 8 * 64 * 4), gather(&stg_s[i & 1][rt * 64 * 4]));
+      store_state_slab(states + ((size_t)h * mc + c) * D * D + (size_t)ct * 2048, stg_s[i & 1], lane);
       if (i > 0) store_nt(reinterpret_cast<V4*>(ut_h + (size_t)(c - 1) * 16 * D), gather(stg_u[(i - 1) & 1]));
     }
     lds_barrier();

@@ -61,15 +61,41 @@ struct RecD {
 };
 
 // The backward's per-chunk 128 x 128 matrices (the state entering each chunk and the
-// state gradient at its end), and its 16 x 128 U~ and dU~ (one row of tiles), are
-// kept in 16 x 16 tiles in fragment order: element
-// (i, j) at index ((i / 16 * 8 + j / 16) * 64 + i % 16 + 16 * (j % 16 / 4)) * 4 + j % 4.
+// state gradient at its end) are kept in 16 x 16 tiles in fragment order, the eight
+// tiles of a 16-column slab contiguous: element (i, j) at index
+//   ((j / 16 * 8 + i / 16) * 64 + i % 16 + 16 * (j % 16 / 4)) * 4 + j % 4.
 // A lane's four consecutive columns of one row are contiguous and every tile is one
-// contiguous block, so the serial pass that owns a 16-column slab writes whole
-// blocks, and the 32-wide k-block of a fragment over a row (k = column) is two
-// contiguous blocks: tiles (i / 16, 2 kb) and (i / 16, 2 kb + 1), lane i % 16 + 16 g.
+// contiguous 512-byte (bf16) block, so the serial pass that owns a slab writes 4 KiB
+// in a row, and the 32-wide k-block of a fragment over a row (k = column) is two
+// blocks: tiles (i / 16, 2 kb) and (i / 16, 2 kb + 1), lane i % 16 + 16 g in both.
 __host__ __device__ constexpr size_t state_tile_index(int i, int j) {
-  return ((size_t)((i >> 4) * 8 + (j >> 4)) * 64 + (i & 15) + 16 * ((j & 15) >> 2)) * 4 + (j & 3);
+  return ((size_t)((j >> 4) * 8 + (i >> 4)) * 64 + (i & 15) + 16 * ((j & 15) >> 2)) * 4 + (j & 3);
+}
+// The 16 x 128 U~ and dU~ in the same tiles (one row of them): element (i, j), i < 16,
+// at ((j / 16) * 64 + i + 16 * (j % 16 / 4)) * 4 + j % 4.
+__host__ __device__ constexpr size_t row_tile_index(int i, int j) {
+  return ((size_t)(j >> 4) * 64 + (i & 15) + 16 * ((j & 15) >> 2)) * 4 + (j & 3);
+}
+
+// The store of one 128 x 16 slab (slab ct: dst = matrix + ct * 2048) in
+// state_tile_index order from its eight tiles in accumulator order (stage [rt][lane][4],
+// lane (m, g) holding rows 4 g .. 4 g + 3 of column m): four stores, store q covering
+// tiles 2q and 2q + 1 (contiguous), lane l writing the pieces of tile lanes 2 (l % 32)
+// and 2 (l % 32) + 1 of tile 2q + l / 32. Non-temporal: the data is read back much later.
+template <typename E>
+__device__ __forceinline__ void store_state_slab(E* __restrict__ dst, const E* __restrict__ stage, int lane) {
+  typedef typename Frag<E>::T F8;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const E* tile = stage + (2 * q + (lane >> 5)) * 256;
+    F8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {  // tile lane tl = (mm, gg): row mm, column 4 gg + e % 4
+      const int tl = 2 * (lane & 31) + (e >> 2), mm = tl & 15, gg = tl >> 4;
+      x[e] = tile[(4 * gg + (e & 3) + 16 * (mm >> 2)) * 4 + (mm & 3)];
+    }
+    store_nt(reinterpret_cast<F8*>(dst + (size_t)q * 512 + lane * 8), x);
+  }
 }
 
 }  // namespace kda
