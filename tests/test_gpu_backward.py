@@ -121,3 +121,30 @@ def test_empty_sequence_passes_the_final_cotangent():
                       grad_final_state=gfin, cu_seqlens=inp.cu_seqlens)
     torch.cuda.synchronize()
     assert torch.equal(g["grad_initial_state"][0], gfin[0])
+
+
+@pytest.mark.timeout(900)
+def test_full_size_sampled_heads():
+    """T=131072, H=32, bf16: the prefill workload with the backward bench's cotangents
+    and launch (all 32 heads in one call). Heads 3 and 30 of every gradient against
+    the oracle run on those two heads alone, which is exact because heads evolve
+    independently."""
+    inp = inputs.make_workload(3)
+    grad_o, gfin = inputs.make_cotangents(3, inp)
+    say(f"[bwd-parity] full size shape={tuple(inp.q.shape)} s0={inp.initial_state is not None}")
+    g = kda.chunk_bwd(inp.q, inp.k, inp.v, inp.log_alpha, inp.beta, grad_o, initial_state=inp.initial_state,
+                      grad_final_state=gfin)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    f = lambda t: np.ascontiguousarray(t[:, :, heads].float().cpu().numpy())
+    s = lambda t: None if t is None else np.ascontiguousarray(t[:, heads].cpu().numpy().astype(np.float64))
+    ref = oracle.backward(f(inp.q), f(inp.k), f(inp.v), f(inp.log_alpha), f(inp.beta), d_o=f(grad_o),
+                          initial_state=s(inp.initial_state), d_final=s(gfin))
+    errs = {}
+    for gn, on in NAMES:
+        got = g[gn]
+        got = got[:, heads] if gn == "grad_initial_state" else got[:, :, heads]
+        errs[gn] = normwise(got.float().cpu().numpy(), ref[on])
+    say("[bwd-parity] full size " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for gn, e in errs.items():
+        assert e <= TOL["bf16"], (gn, e)
