@@ -118,3 +118,25 @@ def test_output_norm_gate_standalone(dtype):
     kda.output_norm_gate(o2, z, w, eps=NORM_EPS, out=o2)  # in place
     torch.cuda.synchronize()
     assert torch.equal(o2, y)
+
+
+@pytest.mark.timeout(900)
+def test_fused_full_size_sampled_heads():
+    """T=131072, H=32, bf16: the bench's fused workload (raw q, k, gate and beta
+    pre-activations, output RMSNorm and gate), all heads in one call; heads 3 and 30
+    against the oracle's prologue, recurrence and epilogue run on those two heads."""
+    r = inputs.make_raw_prefill(3, B=1, T=131072, H=32, dtype="bf16")
+    f = kda.fusion(qk_eps=QK_EPS, out_gate=r.out_gate, norm_weight=r.norm_weight, norm_eps=NORM_EPS)
+    say(f"[fused] full size shape={tuple(r.q.shape)}")
+    o, fin = kda.chunk_fwd(r.q, r.k, r.v, r.gate, r.beta, initial_state=r.initial_state, chunk=64, fusion=f)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    sl = lambda t: np.ascontiguousarray(t[:, :, heads].float().cpu().numpy())
+    s0 = None if r.initial_state is None else r.initial_state[:, heads].cpu().numpy().astype(np.float64)
+    o_ref, fin_ref = ofused.forward(sl(r.q), sl(r.k), sl(r.v), sl(r.gate), sl(r.beta), s0, None,
+                                    out_gate=sl(r.out_gate), norm_weight=r.norm_weight.float().cpu().numpy(),
+                                    qk_eps=QK_EPS, norm_eps=NORM_EPS)
+    eo = normwise(sl(o), o_ref)
+    ef = normwise(fin[:, heads].cpu().numpy(), fin_ref)
+    say(f"[fused] full size: err_o={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]

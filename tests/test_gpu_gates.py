@@ -109,3 +109,27 @@ def test_scalar_gate_with_prologue():
     eo, ef = normwise(o.float().cpu().numpy(), o_ref), normwise(fin.cpu().numpy(), f_ref)
     say(f"[gates] scalar gate + prologue: err_o={eo:.3e} err_state={ef:.3e}")
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("gate", ["head", "none"])
+def test_full_size_sampled_heads(gate):
+    """T=131072, H=32, bf16, chunk 64: the prefill workload with the scalar gate the
+    bench times (its per-channel decay's first channel, or none), all heads in one
+    call; heads 3 and 30 against the oracle run on those two heads alone."""
+    inp = inputs.make_workload(3)
+    la = inp.log_alpha[..., 0].contiguous() if gate == "head" else None
+    say(f"[gates] full size gate={gate} shape={tuple(inp.q.shape)}")
+    o, fin = kda.chunk_fwd(inp.q, inp.k, inp.v, la, inp.beta, initial_state=inp.initial_state, chunk=64)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    f = lambda t: np.ascontiguousarray(t[:, :, heads].float().cpu().numpy())
+    q = f(inp.q)
+    la_c = np.zeros(q.shape, np.float32) if la is None else \
+        np.ascontiguousarray(np.broadcast_to(f(la)[..., None], q.shape), dtype=np.float32)
+    s0 = None if inp.initial_state is None else inp.initial_state[:, heads].cpu().numpy().astype(np.float64)
+    o_ref, f_ref = oracle.forward(q, f(inp.k), f(inp.v), la_c, f(inp.beta), s0)
+    eo = normwise(f(o), o_ref)
+    ef = normwise(fin[:, heads].cpu().numpy(), f_ref)
+    say(f"[gates] full size {gate}: err_o={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
