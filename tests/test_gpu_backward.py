@@ -148,3 +148,22 @@ def test_full_size_sampled_heads():
     say("[bwd-parity] full size " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for gn, e in errs.items():
         assert e <= TOL["bf16"], (gn, e)
+
+
+def test_deterministic_and_race_free():
+    """Two calls on the same inputs give bitwise-equal gradients (the serial passes
+    hand per-chunk data between waves through LDS behind barriers; a missing wait
+    would show up as run-to-run differences). Packed sequences of every chunk count
+    modulo four, so each unrolled loop tail runs."""
+    lens = [5, 16, 30, 40, 64, 77, 150, 300, 1000, 2048]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    inp = small(30, T=int(cu[-1]), H=8, dtype="bf16", cu=cu)
+    grad_o, gfin = inputs.make_cotangents(30, inp)
+    runs = []
+    for _ in range(2):
+        g = kda.chunk_bwd(inp.q, inp.k, inp.v, inp.log_alpha, inp.beta, grad_o, initial_state=inp.initial_state,
+                          grad_final_state=gfin, cu_seqlens=inp.cu_seqlens)
+        torch.cuda.synchronize()
+        runs.append(g)
+    for gn, _ in NAMES:
+        assert torch.equal(runs[0][gn], runs[1][gn]), gn
