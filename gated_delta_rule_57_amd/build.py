@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_backward.hip", "kda_decode.hip", "kda_dplr.hip", "kda_norm.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.hip", "kda_backward.hip", "kda_decode.hip", "kda_dplr.hip", "kda_norm.hip", "kda_prefill.hip", "kda_seg.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

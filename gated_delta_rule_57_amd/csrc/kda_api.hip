@@ -152,12 +152,7 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
-size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype) {
-  // Without cu_seqlens, num_seqs is ignored; with it the caller passes B = 1.
-  const bool varlen = num_seqs > 0 && B == 1;
-  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, chunk, dtype) != KDA_OK) return 0;
-  return kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype);
-}
+}  // extern "C"
 
 namespace {
 int check_fusion(const kda_fusion* f) {
@@ -166,6 +161,8 @@ int check_fusion(const kda_fusion* f) {
     return fail(KDA_ERR_INVALID_ARG, "qk_eps and norm_eps must be >= 0");
   if (f->gate_kind < KDA_GATE_CHANNEL || f->gate_kind > KDA_GATE_NONE)
     return fail(KDA_ERR_INVALID_ARG, "gate_kind %d is not a kda_gate", f->gate_kind);
+  if (f->prefill_path < KDA_PATH_AUTO || f->prefill_path > KDA_PATH_RECORD_SEGMENTED)
+    return fail(KDA_ERR_INVALID_ARG, "prefill_path %d is not a kda_prefill_path", f->prefill_path);
   if (f->out_gate) {
     if (!f->norm_weight) return fail(KDA_ERR_INVALID_ARG, "out_gate needs norm_weight");
     if (!aligned(f->out_gate, 16) || !aligned(f->norm_weight, 16))
@@ -185,10 +182,30 @@ kda::Fusion to_internal(const kda_fusion* f) {
     u.norm_weight = f->out_gate ? f->norm_weight : nullptr;
     u.norm_eps = f->norm_eps;
     u.gate_kind = f->gate_kind;
+    u.prefill_path = f->prefill_path;
   }
   return u;
 }
 }  // namespace
+
+extern "C" {
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype) {
+  // Without cu_seqlens, num_seqs is ignored; with it the caller passes B = 1.
+  const bool varlen = num_seqs > 0 && B == 1;
+  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, chunk, dtype) != KDA_OK) return 0;
+  return kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype, KDA_PATH_AUTO);
+}
+
+size_t kda_chunk_fwd_fused_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype,
+                                          const kda_fusion* fusion) {
+  const bool varlen = num_seqs > 0 && B == 1;
+  if (check_prefill(B, T, H, varlen ? num_seqs : 0, varlen, 128, 128, chunk, dtype) != KDA_OK) return 0;
+  if (check_fusion(fusion) != KDA_OK) return 0;
+  return kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype,
+                                      fusion ? fusion->prefill_path : KDA_PATH_AUTO);
+}
+
 
 int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                         const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
@@ -217,7 +234,8 @@ int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float
   if (workspace && !aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   const int N = varlen ? num_seqs : B;
   if (N == 0) return ok();
-  const size_t need = kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype);
+  const int path = fusion ? fusion->prefill_path : KDA_PATH_AUTO;
+  const size_t need = kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype, path);
   if (workspace && workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
 

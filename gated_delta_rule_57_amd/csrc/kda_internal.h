@@ -26,6 +26,8 @@ struct Fusion {
   const float* norm_weight;  // [128], with out_gate
   float norm_eps;
   int gate_kind;             // 0: per channel, 1: per (token, head), 2: none
+  int prefill_path;          // kda_prefill_path: 0 automatic, 1 record + slab state, 2 single pass,
+                             // 3 record + segment-parallel state
 };
 
 // dtype: 0 = bf16, 1 = fp32 (the kda_dtype values).
@@ -44,8 +46,54 @@ int64_t max_chunks(int B, int T, int num_seqs, bool varlen, int chunk);
 // Bytes of one per-(chunk, head) record written by the intra-chunk kernel.
 size_t chunk_record_bytes(int dtype, int chunk);
 
-// Workspace bytes for a prefill call.
-size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype);
+// Workspace bytes for a prefill call on the given path (Fusion::prefill_path).
+size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path = 0);
+
+// The kernels a prefill runs, from its dtype, chunk and Fusion::prefill_path
+// (kda_prefill_path in include/kda.h). Only bf16 with 64-token chunks has a choice.
+enum PrefillKernels {
+  KERNELS_RECORD_SLAB = 0,  // intra-chunk records, state kernels per 16 value columns
+  KERNELS_RECORD_SEG = 1,   // intra-chunk records, segment-parallel full-width state kernels
+  KERNELS_SINGLE = 2        // segment-parallel single pass, no records
+};
+// The automatic path takes the segment-parallel state kernels when sequences average
+// at least SEG_MIN_AVG_CHUNKS chunks (measured on MI355X: they win from about 8K tokens
+// per sequence; below that the segment scan and the short segments cost more than the
+// slab kernels' repeated record reads).
+constexpr int SEG_MIN_AVG_CHUNKS = 96;
+inline int prefill_kernels(int dtype, int chunk, int path, int64_t max_chunks, int N) {
+  if (dtype != 0 || chunk != 64) return KERNELS_RECORD_SLAB;
+  if (path == 1) return KERNELS_RECORD_SLAB;
+  if (path == 2) return KERNELS_SINGLE;
+  if (path == 3) return KERNELS_RECORD_SEG;
+  return max_chunks >= (int64_t)SEG_MIN_AVG_CHUNKS * (N > 0 ? N : 1) ? KERNELS_RECORD_SEG : KERNELS_RECORD_SLAB;
+}
+
+// Segment-parallel passes (kda_seg.hip): about SEG_TARGET_GROUPS work-groups per
+// pass, segments of at least SEG_MIN_CHUNKS chunks.
+constexpr int SEG_TARGET_GROUPS = 256;
+constexpr int SEG_MIN_CHUNKS = 1;
+int seg_chunks_per_segment(int64_t max_chunks, int N, int H);
+// Workspace: segment offsets [N+1] int32, segment table [segments] int2, entry
+// states [segments][H][128*128] fp32, segment maps [segments][H][2][128*128] fp32.
+struct SegWs {
+  int lseg;
+  int64_t max_segments;
+  size_t off_seg_off, off_seg_info, off_seg_in, off_seg_map, total;
+};
+SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen);
+SegWs seg_ws_layout_for(int lseg, int64_t max_segments, int N, int H);
+// The single pass: every step of the prefill for bf16, 64-token chunks.
+hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                              int num_seqs, void* o, float* final_state, int B, int T, int H, const Fusion& fusion,
+                              void* workspace, hipStream_t stream);
+// The segment-parallel state kernels fed by bf16 64-token records (segment plan, first
+// pass, scan, second pass), with the output epilogue of `fusion` fused in.
+hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64_t mc, const int32_t* cu_seqlens,
+                            int N, int T, int H, const float* initial_state, float* final_state, void* o,
+                            const Fusion& fusion, void* seg_workspace, int lseg, int64_t max_segments,
+                            hipStream_t stream);
 
 hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* initial_state,

@@ -856,6 +856,15 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   }
   const int64_t units = (int64_t)N * H;
   const int64_t slots = (units + 7) / 8;
+  if constexpr (std::is_same<E, __bf16>::value && C == 64) {
+    if (slots > 0 && prefill_kernels(0, 64, fusion.prefill_path, mc, N) == KERNELS_RECORD_SEG) {
+      // segment-parallel full-width state kernels on the records (output epilogue fused in)
+      int B = cu_seqlens ? 1 : N;
+      const SegWs sl = seg_ws_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr);
+      return launch_state_seg(records, chunk_off, mc, cu_seqlens, N, T, H, initial_state, final_state, o, fusion,
+                              ws + al256(l.total), sl.lseg, sl.max_segments, stream);
+    }
+  }
   if (slots > 0) {
     if constexpr (std::is_same<E, __bf16>::value && C == 64) {
       hipLaunchKernelGGL(inter_wg_kernel<INTER_LOOKAHEAD>, dim3((unsigned)(slots * 64)), dim3(256), 0, stream,
@@ -922,8 +931,12 @@ hipError_t launch_forward_records(int dtype, const void* q, const void* k, const
   return launch_records_typed<float>(q, k, v, log_alpha, beta, cu_seqlens, N, T, H, mc, l, ws, stream);
 }
 
-size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype) {
-  return ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;
+size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path) {
+  const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), varlen ? num_seqs : B);
+  if (kern == KERNELS_SINGLE) return seg_ws_layout(B, T, H, num_seqs, varlen).total;
+  const size_t rec = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;
+  if (kern == KERNELS_RECORD_SEG) return al256(rec) + seg_ws_layout(B, T, H, num_seqs, varlen).total;
+  return rec;
 }
 
 hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
@@ -931,6 +944,11 @@ hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, co
                           const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
                           int T, int H, const Fusion& fusion, void* workspace, hipStream_t stream) {
   const bool varlen = cu_seqlens != nullptr;
+  const int kern = prefill_kernels(dtype, chunk, fusion.prefill_path, max_chunks(B, T, num_seqs, varlen, chunk),
+                                   varlen ? num_seqs : B);
+  if (kern == KERNELS_SINGLE)
+    return launch_prefill_seg(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o, final_state, B, T,
+                              H, fusion, workspace, stream);
   const int N = varlen ? num_seqs : B;
   const WsLayout l = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype);
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, chunk);

@@ -25,10 +25,11 @@ KDA_ERR_DEVICE = -4
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused", "kda_decode_step_fused",
            "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read", "kda_chunk_bwd_workspace_size",
-           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd")
+           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd",
+           "kda_chunk_fwd_fused_workspace_size")
 
 KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm", "bwd_local", "bwd_state",
-                "bwd_chunk")  # KDA_KERNEL_* ids
+                "bwd_chunk", "seg_first", "seg_scan", "seg_second")  # KDA_KERNEL_* ids
 
 
 class Fusion(ctypes.Structure):
@@ -37,10 +38,13 @@ class Fusion(ctypes.Structure):
     _fields_ = [("normalize_qk", ctypes.c_int), ("qk_eps", ctypes.c_float),
                 ("gate_preactivation", ctypes.c_int), ("beta_preactivation", ctypes.c_int),
                 ("out_gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
-                ("gate_kind", ctypes.c_int)]
+                ("gate_kind", ctypes.c_int), ("prefill_path", ctypes.c_int)]
 
 
 KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
+KDA_PATH_AUTO, KDA_PATH_RECORD, KDA_PATH_SINGLE_PASS, KDA_PATH_RECORD_SEGMENTED = 0, 1, 2, 3
+_PATHS = {"auto": KDA_PATH_AUTO, "record": KDA_PATH_RECORD, "single": KDA_PATH_SINGLE_PASS,
+          "segmented": KDA_PATH_RECORD_SEGMENTED}
 
 
 class KdaError(RuntimeError):
@@ -67,6 +71,8 @@ def _load():
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.kda_decode_step.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.kda_chunk_fwd_fused_workspace_size.restype = Z
+    lib.kda_chunk_fwd_fused_workspace_size.argtypes = [I, I, I, I, I, I, P]
     lib.kda_chunk_fwd_fused.restype = I
     lib.kda_chunk_fwd_fused.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, P, Z, P]
     lib.kda_decode_step_fused.restype = I
@@ -125,15 +131,29 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def workspace_size(B, T, H, num_seqs=0, chunk=64, dtype=KDA_BF16) -> int:
-    return int(lib.kda_chunk_fwd_workspace_size(B, T, H, num_seqs, chunk, dtype))
+def _path_code(path):
+    if path not in _PATHS:
+        raise ValueError(f"path must be one of {sorted(_PATHS)}, got {path!r}")
+    return _PATHS[path]
+
+
+def workspace_size(B, T, H, num_seqs=0, chunk=64, dtype=KDA_BF16, path="auto") -> int:
+    """Workspace bytes of ``chunk_fwd`` on ``path`` (kda_prefill_path: "auto", "record",
+    "single" or "segmented"; only bf16 with 64-token chunks has a choice)."""
+    code = _path_code(path)
+    if code == KDA_PATH_AUTO:
+        return int(lib.kda_chunk_fwd_workspace_size(B, T, H, num_seqs, chunk, dtype))
+    f = Fusion()
+    f.prefill_path = code
+    return int(lib.kda_chunk_fwd_fused_workspace_size(B, T, H, num_seqs, chunk, dtype, ctypes.byref(f)))
 
 
 def fusion(normalize_qk=True, qk_eps=1e-6, gate_preactivation=True, beta_preactivation=True,
-           out_gate=None, norm_weight=None, norm_eps=1e-6):
+           out_gate=None, norm_weight=None, norm_eps=1e-6, path="auto"):
     """A kda_fusion for ``chunk_fwd`` / ``decode_step``. ``out_gate`` (o's shape and
     dtype) and ``norm_weight`` (fp32 [128]) are device tensors or None; the returned
-    object keeps them referenced while it lives."""
+    object keeps them referenced while it lives. ``path`` selects the prefill kernels
+    (see ``workspace_size``)."""
     if out_gate is not None:
         if norm_weight is None:
             raise ValueError("out_gate needs norm_weight")
@@ -142,7 +162,8 @@ def fusion(normalize_qk=True, qk_eps=1e-6, gate_preactivation=True, beta_preacti
             raise ValueError("out_gate must be contiguous")
     f = Fusion(int(bool(normalize_qk)), float(qk_eps), int(bool(gate_preactivation)), int(bool(beta_preactivation)),
                None if out_gate is None else out_gate.data_ptr(),
-               None if out_gate is None else norm_weight.data_ptr(), float(norm_eps), KDA_GATE_CHANNEL)
+               None if out_gate is None else norm_weight.data_ptr(), float(norm_eps), KDA_GATE_CHANNEL,
+               _path_code(path))
     f._keep = (out_gate, norm_weight)
     return f
 
@@ -159,14 +180,18 @@ def _gate_kind(log_alpha, lead, dk):
     return KDA_GATE_CHANNEL
 
 
-def _with_gate(f, gate):
-    """The Fusion to pass for ``gate``: ``f`` with its gate_kind set, a plain one
-    when only the gate differs from the default, or None for the plain call."""
-    if f is None and gate == KDA_GATE_CHANNEL:
+def _with_gate(f, gate, path="auto"):
+    """The Fusion to pass for ``gate`` and ``path``: ``f`` with its gate_kind (and a
+    non-default path) set, a plain one when only the gate or the path differs from the
+    default, or None for the plain call."""
+    code = _path_code(path)
+    if f is None and gate == KDA_GATE_CHANNEL and code == KDA_PATH_AUTO:
         return None
     if f is None:
         f = fusion(normalize_qk=False, gate_preactivation=False, beta_preactivation=False)
     f.gate_kind = gate
+    if code != KDA_PATH_AUTO:
+        f.prefill_path = code
     return f
 
 
@@ -178,9 +203,10 @@ def _check_out_gate(f, o):
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
-              output_final_state=True, o=None, final_state=None, workspace=None, fusion=None):
+              output_final_state=True, o=None, final_state=None, workspace=None, fusion=None, path="auto"):
     """Chunked KDA prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_fused`` when
-    ``fusion`` is given, see ``fusion()``, or the gate is not per channel).
+    ``fusion`` is given, see ``fusion()``, the gate is not per channel or ``path`` is
+    "record").
 
     q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
     log_alpha: [B, T, H, 128] fp32 (KDA), [B, T, H] fp32 (one decay per token and
@@ -199,7 +225,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
     _need(v, "v", dt, (B, T, H, dv))
     gate = _gate_kind(log_alpha, (B, T, H), dk)
     _need(beta, "beta", torch.float32, (B, T, H))
-    fusion = _with_gate(fusion, gate)
+    fusion = _with_gate(fusion, gate, path)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
             raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")

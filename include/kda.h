@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /* Element type of q, k, v and o. */
 typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
@@ -85,10 +85,16 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk
  * The chunkwise algorithm (GeekNews "Kimi Linear" summary, section "청크 단위 병렬
  * 알고리듬"; "From GPT-2 to Kimi K3" digest, section "DeltaNet 병렬화 -- 청크 단위
  * 학습"): each sequence is cut into chunks of `chunk` tokens from its own start (the
- * last one may be partial); a fully parallel kernel forms each chunk's decay-weighted
- * A = tril(beta (K e^G)(K e^-G)^T), inverts I + A by forward substitution and builds
- * the WY factors; a second kernel carries the fp32 state across the chunks of each
- * sequence and writes the outputs. The result does not depend on `chunk` except for
+ * last one may be partial); each chunk's decay-weighted A = tril(beta (K e^G)(K e^-G)^T)
+ * is inverted as I + A by forward substitution into the WY factors, and the fp32
+ * state is carried across the chunks of each sequence while the outputs are written.
+ * For bf16 with 64-token chunks the default state step is segment-parallel: a
+ * work-group owns a run of chunks of one (sequence, head) and the whole 128 x 128
+ * state, reading each chunk's record once; the middle runs of a long sequence first
+ * compose their chunk maps (the state is an affine function of the state entering a
+ * run), a short scan gives every run its entry state, then the runs write their
+ * outputs. kda_fusion.prefill_path selects the other kernel sets (see
+ * kda_prefill_path). The result does not depend on `chunk` or the path except for
  * rounding.
  *
  *   q, k        [B, T, H, dk]  dtype      o          [B, T, H, dv]  dtype (written)
@@ -104,7 +110,11 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int num_seqs, int chunk
  *               (final = initial). Without it, N = B sequences of T tokens.
  *   chunk       16 or 64.
  *   workspace   device buffer of at least kda_chunk_fwd_workspace_size() bytes, or
- *               NULL: the library then allocates and frees it in stream order.
+ *               NULL: the library then allocates and frees it in stream order. It
+ *               holds one record per (chunk, head) (1.16 KB per token and head in
+ *               bf16) and, on the segment-parallel paths, three 128 x 128 fp32 states
+ *               per (segment, head) (about 60 MiB at 128K tokens x 32 heads; the single
+ *               pass needs only these).
  * T = 0 (or B = 0) is a valid call that copies initial_state to final_state (zeros
  * if initial_state is NULL). `o` must not alias any input. Size limits, each
  * KDA_ERR_INVALID_ARG: B*T below 2^31 - 64 tokens, N*H below 2^25 (sequence, head)
@@ -146,9 +156,12 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *lo
  *                       o / sqrt(mean_j o_j^2 + norm_eps) * norm_weight * sigmoid(z)
  *                       (norm_weight: float32 [dv], shared by the heads, 16-byte
  *                       aligned, required with out_gate; norm_eps >= 0)
- * Zero-initialised = the plain recurrence. The prologue runs inside the kernels that
- * read q, k, log_alpha and beta; the prefill epilogue is one more pass over o (a row
- * needs all dv values, which the state kernel spreads over work-groups); the decode
+ *   prefill_path        a kda_prefill_path value, see below
+ * Zero-initialised = the plain recurrence on the automatic path. The prologue runs
+ * inside the kernels that read q, k, log_alpha and beta. The prefill epilogue runs
+ * inside the segment-parallel state kernels, whose work-groups hold whole output rows;
+ * with the slab state kernels (KDA_PATH_RECORD, other dtypes and chunks) it is one
+ * more pass over o (a row's dv values are spread over work-groups there). The decode
  * epilogue runs inside the decode kernel.
  */
 typedef struct kda_fusion {
@@ -159,8 +172,35 @@ typedef struct kda_fusion {
   const void *out_gate;
   const float *norm_weight;
   float norm_eps;
-  int gate_kind; /* a kda_gate value, see below */
+  int gate_kind;    /* a kda_gate value, see below */
+  int prefill_path; /* a kda_prefill_path value, see below */
 } kda_fusion;
+
+/*
+ * Which kernels a prefill runs (kda_fusion.prefill_path). Only bf16 with 64-token
+ * chunks has a choice; every other dtype and chunk runs the record path.
+ *   KDA_PATH_AUTO         an intra-chunk kernel writes a record per (chunk, head); when
+ *                         sequences average at least 96 chunks (6144 tokens) the
+ *                         segment-parallel full-width state kernels read each record
+ *                         once per sequence segment, otherwise the KDA_PATH_RECORD state
+ *                         kernels run (the default; the faster of the two at each size)
+ *   KDA_PATH_RECORD       the same records; the state kernel runs one work-group per
+ *                         (sequence, head, 16 value columns) over the whole sequence,
+ *                         the structure kda_dplr_chunk_fwd also has
+ *   KDA_PATH_SINGLE_PASS  no records: the segment-parallel work-groups form each
+ *                         chunk's matrices themselves (the middle segments twice),
+ *                         with the least HBM traffic and a workspace of a few states
+ *                         per (segment, head)
+ *   KDA_PATH_RECORD_SEGMENTED  the records and the segment-parallel state kernels at
+ *                         any size
+ * All of them compute the same recurrence.
+ */
+typedef enum {
+  KDA_PATH_AUTO = 0,
+  KDA_PATH_RECORD = 1,
+  KDA_PATH_SINGLE_PASS = 2,
+  KDA_PATH_RECORD_SEGMENTED = 3
+} kda_prefill_path;
 
 /*
  * Decay granularity (kda_fusion.gate_kind). The pages trace KDA back through two
@@ -187,6 +227,11 @@ int kda_chunk_fwd_fused(const void *q, const void *k, const void *v, const float
                         int num_seqs, void *o, float *final_state, int B, int T, int H, int dk,
                         int dv, int chunk, int dtype, const kda_fusion *fusion, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of kda_chunk_fwd_fused with this `fusion` (its prefill_path decides);
+ * 0 for arguments the call would reject. */
+size_t kda_chunk_fwd_fused_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype,
+                                          const kda_fusion *fusion);
 
 /* kda_decode_step with the prologue / epilogue of `fusion` (NULL = kda_decode_step). */
 int kda_decode_step_fused(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -277,11 +322,15 @@ int kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *
  * kda_dplr_chunk_fwd and kda_decode_step call records HIP events on its stream before its first kernel
  * and after each kernel it launches, so the durations are measured on the stream
  * the kernels run on (the fused variants and kda_output_norm_gate included). Kernel
- * ids: KDA_KERNEL_PLAN (chunk plan), KDA_KERNEL_INTRA (intra-chunk), KDA_KERNEL_INTER
- * (inter-chunk state and output), KDA_KERNEL_DECODE, KDA_KERNEL_OUTNORM (output
- * RMSNorm and gate), and for kda_chunk_bwd, whose internal forward reports under the
- * first three, KDA_KERNEL_BWD_LOCAL (per-chunk backward record), KDA_KERNEL_BWD_STATE
- * (state gradient through the chunks) and KDA_KERNEL_BWD_CHUNK (per-chunk gradients).
+ * ids: KDA_KERNEL_PLAN (chunk or segment plan), KDA_KERNEL_INTRA (intra-chunk),
+ * KDA_KERNEL_INTER (inter-chunk state and output), KDA_KERNEL_DECODE,
+ * KDA_KERNEL_OUTNORM (output RMSNorm and gate), for kda_chunk_bwd, whose internal
+ * forward reports under the first three, KDA_KERNEL_BWD_LOCAL (per-chunk backward
+ * record), KDA_KERNEL_BWD_STATE (state gradient through the chunks) and
+ * KDA_KERNEL_BWD_CHUNK (per-chunk gradients), and for the segment-parallel prefill
+ * KDA_KERNEL_SEG_FIRST (first segments' outputs and the middle segments' maps),
+ * KDA_KERNEL_SEG_SCAN (segment entry states) and KDA_KERNEL_SEG_SECOND (the other
+ * segments' outputs).
  *
  * kda_timing_enable(1) starts recording (and discards anything recorded before);
  * kda_timing_enable(0) stops. kda_timing_read() waits for the recorded events,
@@ -299,7 +348,10 @@ int kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *
 #define KDA_KERNEL_BWD_LOCAL 5
 #define KDA_KERNEL_BWD_STATE 6
 #define KDA_KERNEL_BWD_CHUNK 7
-#define KDA_NUM_KERNELS 8
+#define KDA_KERNEL_SEG_FIRST 8
+#define KDA_KERNEL_SEG_SCAN 9
+#define KDA_KERNEL_SEG_SECOND 10
+#define KDA_NUM_KERNELS 11
 
 int kda_timing_enable(int on);
 int kda_timing_read(double *total_ms, int *launches, int n);

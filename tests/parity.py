@@ -48,12 +48,12 @@ def oracle_prefill(inp, heads=None, cols=None):
                           heads=heads, cols=cols)
 
 
-def compare_prefill(inp, heads=None, cols=None, chunk=None, tol=None, label=""):
+def compare_prefill(inp, heads=None, cols=None, chunk=None, tol=None, label="", **kw):
     """Runs both sides; asserts o and final state are within tolerance. Returns the
-    two errors."""
+    two errors. Extra keywords go to the library call (e.g. path)."""
     say(f"[parity] {label} dtype={inp.dtype} shape={tuple(inp.q.shape)} chunk={chunk or inp.chunk} "
-        f"seqs={inp.num_seqs} heads={heads} cols={cols}")
-    o, fin = gpu_prefill(inp, chunk=chunk)
+        f"seqs={inp.num_seqs} heads={heads} cols={cols} {kw}")
+    o, fin = gpu_prefill(inp, chunk=chunk, **kw)
     o_ref, fin_ref = oracle_prefill(inp, heads=heads, cols=cols)
     hs = slice(None) if heads is None else list(heads)
     c0, c1 = (0, inp.v.shape[-1]) if cols is None else cols

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     version = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.kda_abi_version() == version == 4
+    assert L.kda_abi_version() == version == 5
     for st in (0, -1, -2, -3, -4):
         assert L.kda_status_string(st).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(7)
@@ -109,16 +109,46 @@ def test_decode_empty_batch_is_ok():
     assert decode_call(N=0, q=None, state=None) == kda.KDA_OK
 
 
+def path_ws(path, B, T, H, num_seqs, chunk, dtype):
+    f = kda.Fusion()
+    f.prefill_path = path
+    return L.kda_chunk_fwd_fused_workspace_size(B, T, H, num_seqs, chunk, dtype, ctypes.byref(f))
+
+
+def record_ws(*args):
+    return path_ws(kda.KDA_PATH_RECORD, *args)
+
+
+def single_ws(*args):
+    return path_ws(kda.KDA_PATH_SINGLE_PASS, *args)
+
+
 def test_workspace_size():
     ws = L.kda_chunk_fwd_workspace_size
     assert ws(1, 64, 1, 0, 16, 1) > 0
-    assert ws(1, 4096, 16, 0, 64, 0) < ws(1, 8192, 16, 0, 64, 0) < ws(1, 8192, 32, 0, 64, 0)
-    assert ws(1, 4096, 16, 0, 64, 0) < ws(1, 4096, 16, 0, 64, 1)
+    # the record paths hold one record per (chunk, head): they grow with tokens and heads
+    assert record_ws(1, 4096, 16, 0, 64, 0) < record_ws(1, 8192, 16, 0, 64, 0) < record_ws(1, 8192, 32, 0, 64, 0)
+    assert record_ws(1, 4096, 16, 0, 64, 0) < record_ws(1, 4096, 16, 0, 64, 1)
+    # fp32 and 16-token chunks have one path; every path value gives its size
+    for path in (kda.KDA_PATH_AUTO, kda.KDA_PATH_RECORD, kda.KDA_PATH_SINGLE_PASS, kda.KDA_PATH_RECORD_SEGMENTED):
+        assert path_ws(path, 1, 4096, 16, 0, 64, 1) == record_ws(1, 4096, 16, 0, 64, 1)
+        assert path_ws(path, 1, 4096, 16, 0, 16, 0) == record_ws(1, 4096, 16, 0, 16, 0)
+    # bf16, 64-token chunks: the default adds a few states per (segment, head) to the
+    # records; the single pass holds those states only, bounded by the segment count
+    big = (1, 131072, 32, 0, 64, 0)
+    assert ws(*big) == path_ws(kda.KDA_PATH_AUTO, *big)
+    assert record_ws(*big) < ws(*big) < record_ws(*big) + single_ws(*big) + 4096
+    assert single_ws(*big) < 64 * 2**20 < record_ws(*big)
+    assert single_ws(*big) <= single_ws(1, 8192, 32, 0, 64, 0) * 1.5
     # a varlen query bounds every split of the same tokens
-    assert ws(1, 32768, 32, 4, 64, 0) >= ws(1, 32768, 32, 0, 64, 0)
+    for path in (kda.KDA_PATH_AUTO, kda.KDA_PATH_RECORD, kda.KDA_PATH_SINGLE_PASS, kda.KDA_PATH_RECORD_SEGMENTED):
+        assert path_ws(path, 1, 32768, 32, 4, 64, 0) >= path_ws(path, 1, 32768, 32, 0, 64, 0)
     assert ws(1, 64, 1, 0, 32, 0) == 0
     assert ws(1, 64, 0, 0, 64, 0) == 0
     assert ws(1, 64, 1, 0, 64, 9) == 0
+    bad = kda.Fusion()
+    bad.prefill_path = 7
+    assert L.kda_chunk_fwd_fused_workspace_size(1, 64, 1, 0, 64, 0, ctypes.byref(bad)) == 0
 
 
 def fused_chunk_call(fusion, **kw):
@@ -282,4 +312,4 @@ def test_dplr_workspace_size():
     assert kda.dplr_workspace_size(1, 4096, 16, dtype=kda.KDA_FP32) > n
     assert kda.dplr_workspace_size(1, 4096, 16, num_seqs=3) >= n
     assert kda.dplr_workspace_size(1, 64, 0) == 0
-    assert kda.dplr_workspace_size(1, 64, 2) > kda.workspace_size(1, 64, 2)
+    assert kda.dplr_workspace_size(1, 64, 2) > kda.workspace_size(1, 64, 2, path="record")

@@ -81,5 +81,5 @@ def test_bench_record_byte_counts_match_the_workspace_queries():
     from gated_delta_rule_57_amd import kda
     T, H = 4096, 16
     mc = T // bench.CHUNK
-    assert abs(kda.workspace_size(1, T, H, chunk=64) / (mc * H) - bench.RECORD_BYTES_BF16_C64) < 1
+    assert abs(kda.workspace_size(1, T, H, chunk=64, path="record") / (mc * H) - bench.RECORD_BYTES_BF16_C64) < 1
     assert abs(kda.dplr_workspace_size(1, T, H) / (mc * H) - bench.DPLR_RECORD_BYTES_BF16) < 1
