@@ -1,29 +1,40 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = one chunked prefill over a 131072-token sequence with 32 heads of
-dimension 128 (bf16 q/k/v, fp32 decays and state, chunk 64), followed by
-``--decode-per-step`` decode steps over 256 sequences x 32 heads of persisted fp32
-128 x 128 states (bf16 q/k/v). Inputs are synthetic, seeded and resident in HBM
-before timing starts.
+dimension 128 (bf16 q/k/v, fp32 decays and state, chunk 64, the library's automatic
+kernel choice), followed by ``--decode-per-step`` decode steps over 256 sequences x
+32 heads of persisted fp32 128 x 128 states (bf16 q/k/v). Inputs are synthetic,
+seeded (NumPy on the host, see gated_delta_rule_57_amd/inputs.py) and resident in
+HBM before timing starts.
 
 Prints one JSON line. ``value`` is prefill tokens/s (a token = one position across
-all 32 heads), from HIP events recorded by the library on the stream its kernels
-run on. Decode throughput (GB/s of state + vectors, fraction of HBM peak), the
-algorithmic fraction of bf16 MFMA peak, per-kernel roofline figures and the CPU
-oracle's throughput on a sample of the same workload are reported beside it.
+all 32 heads) from the median of the timed steps' prefill durations, measured with
+events on the stream the library's kernels run on. Beside it:
+  roofline      the whole prefill path against the HBM roofline: the method's
+                algorithmic bytes (q, k, v, log_alpha, beta in, o out: 1,540 B per
+                token and head) over the measured time, against 8 TB/s
+  mfma          algorithmic bf16 TFLOP/s and fraction of the 2.5 PFLOP/s dense peak;
+                the rocprof MFMA utilisation from the committed counter summary
+  kernels       each kernel of the path: average time, its design bytes (what it
+                moves by construction) and the HBM traffic measured by the counters
+  decode, configs, paths, fused, gates, backward, dplr_comparison, cpu_baseline(s),
+  environment
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
 import json
 import os
+import platform
+import statistics
+import subprocess
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
 D = 128
@@ -33,11 +44,18 @@ CHUNK = 64
 FLOP_PER_TOK_HEAD = 6 * D * D + (CHUNK - 1) * D + (CHUNK + 1) * D + (CHUNK + 1) * D + (CHUNK - 1) * 2 * D
 # bytes every prefill must move per (token, head): q, k, v bf16, log_alpha fp32, beta fp32, o bf16
 PATH_BYTES_PER_TOK_HEAD = 3 * 2 * D + 4 * D + 4 + 2 * D
-# per-(chunk, head) record written by the intra-chunk kernel and read by the inter-chunk kernel:
-# its size in the workspace, and the bytes actually moved (the two all-zero P slots above the
-# diagonal, 2 x 1 KiB, are neither written nor read)
+IN_BYTES_PER_TOK_HEAD = 3 * 2 * D + 4 * D + 4
+# per-(chunk, head) record written by the intra-chunk kernel: its size in the workspace, and
+# the bytes it writes (the two all-zero P slots above the diagonal, 2 x 1 KiB, are not written)
 RECORD_BYTES_BF16_C64 = 74240
 RECORD_MOVED_BYTES_BF16_C64 = RECORD_BYTES_BF16_C64 - 2048
+# what the segment-parallel state kernels read per chunk: the output pass the whole
+# record (fragment region, e^{g_C}, U), a map pass -W, (K e^{g_C-G})^T, e^{g_C} and the
+# U tiles of its B columns
+SEG_OUT_READ = RECORD_BYTES_BF16_C64
+SEG_MAP_READ = 16384 + 16384 + 512 + 16384
+# segment length rule of the library (SEG_TARGET_GROUPS, SEG_MIN_CHUNKS in kda_internal.h)
+SEG_TARGET_GROUPS, SEG_MIN_CHUNKS = 256, 1
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
@@ -62,6 +80,13 @@ DPLR_IN_BYTES_PER_TOK_HEAD = 5 * 2 * D + 4 * D   # q, k, v, a, b bf16, log_alpha
 
 PREFILL_T, PREFILL_H = 131072, 32
 DEC_N, DEC_H = 256, 32
+PREFILL_KERNELS = ("plan", "intra", "inter", "seg_first", "seg_scan", "seg_second", "outnorm")
+
+
+def stats(xs):
+    xs = sorted(xs)
+    return {"median": round(statistics.median(xs), 5), "min": round(xs[0], 5), "max": round(xs[-1], 5),
+            "runs": len(xs)}
 
 
 def kernel_source_hash():
@@ -69,82 +94,273 @@ def kernel_source_hash():
     return source_hash(ROOT)
 
 
-def traffic_from_profiles(kernel, src_hash):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+def committed_profile(name, src_hash):
+    """A committed counter summary under profiles/, if it was taken on the current
+    kernel sources; else None."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    if data.get("kernel_source_hash") != src_hash:
-        return None
-    ent = data.get("kernels", {}).get(kernel)
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    return data if data.get("kernel_source_hash") == src_hash else None
 
 
-def cpu_baseline(inp, sample_tokens):
-    """The fp64 sequential oracle on the first ``sample_tokens`` tokens of the same
-    prefill workload (all heads), on this host's cores."""
+def seg_plan(T, H, N=1):
+    """Segments per sequence of the segment-parallel state kernels for N sequences of T
+    tokens (the library's rule): (chunks per segment, segments)."""
+    mc = N * ((T + CHUNK - 1) // CHUNK)
+    target = SEG_TARGET_GROUPS + N * H
+    lseg = max(SEG_MIN_CHUNKS, (mc * H + target - 1) // target)
+    lseg = min(lseg, mc) if mc > 0 else 1
+    nc = (T + CHUNK - 1) // CHUNK
+    return lseg, max(1, (nc + lseg - 1) // lseg)
+
+
+def seg_design_bytes(T, H):
+    """Bytes the segment-parallel state kernels read and write by construction for one
+    T-token sequence of H heads: (first pass, second pass)."""
+    lseg, ns = seg_plan(T, H)
+    nc = (T + CHUNK - 1) // CHUNK
+    lens = [min(lseg, nc - j * lseg) for j in range(ns)]
+    o_per_chunk = CHUNK * 2 * D
+    first = H * (lens[0] * (SEG_OUT_READ + o_per_chunk) + sum(lens[1:ns - 1]) * SEG_MAP_READ)
+    second = H * sum(lens[1:]) * (SEG_OUT_READ + o_per_chunk)
+    return first, second
+
+
+def environment(torch):
+    env = {"python": platform.python_version(), "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        env.update(gpu=p.name, gcn_arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
+                   hbm_gib=round(p.total_memory / 2**30, 1))
+        clk = getattr(p, "clock_rate", None)
+        if clk:
+            env["gpu_clock_mhz"] = round(clk / 1000)
+    except Exception:  # noqa: BLE001 (best-effort environment record)
+        pass
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            env["rocm"] = open(path).read().strip()
+            break
+        except OSError:
+            pass
+    try:
+        env["amdgpu_driver"] = open("/sys/module/amdgpu/version").read().strip()
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        clocks = [ln.strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln]
+        if clocks:
+            env["rocm_smi_clocks"] = clocks[:4]
+    except Exception:  # noqa: BLE001
+        pass
+    env.update(host_cpu=cpu_model(), host_cores=host_cores(), omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+    return env
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or None
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count()
+
+
+class StreamTimer:
+    """Event pairs on the current stream (the one the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def __call__(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def time_fn(torch, fn, runs, warmup=2):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    tm = StreamTimer(torch)
+    for _ in range(runs):
+        tm("x", fn)
+    torch.cuda.synchronize()
+    return tm.ms("x")
+
+
+def cpu_baselines(inputs, pre, dec):
+    """The fp64 sequential oracle (the C recurrence of oracle/, OpenMP over sequences,
+    heads and 16-column blocks) on this host: the headline workload, the 4K and varlen
+    workloads, one thread on the 4K workload, and decode steps of the decode workload."""
     import numpy as np
     import oracle
-
-    S = min(sample_tokens, inp.q.shape[1])
-    f = lambda t: t[:, :S].float().cpu().numpy()
-    q, k, v, la, beta = f(inp.q), f(inp.k), f(inp.v), f(inp.log_alpha), f(inp.beta)
     threads = oracle.seq.default_threads()
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    out = {}
+
+    def prefill(label, inp, tokens=None, nt=threads):
+        S = inp.q.shape[1] if tokens is None else min(tokens, inp.q.shape[1])
+        x = [f(t[:, :S]) for t in (inp.q, inp.k, inp.v, inp.log_alpha, inp.beta)]
+        s0 = None if inp.initial_state is None else inp.initial_state.double().cpu().numpy()
+        cu = None if inp.cu_seqlens is None else inp.cu_seqlens.cpu().numpy().astype(np.int64)
+        t0 = time.perf_counter()
+        o, _ = oracle.forward(*x, s0, cu_seqlens=cu, num_threads=nt)
+        dt = time.perf_counter() - t0
+        assert np.isfinite(o).all()
+        out[label] = {"tokens_per_s": round(S * inp.q.shape[0] / dt, 1), "seconds": round(dt, 3), "threads": nt,
+                      "tokens": S * inp.q.shape[0], "heads": inp.q.shape[2]}
+        print(f"[bench] oracle {label}: {dt:.2f} s", file=sys.stderr, flush=True)
+
+    prefill("kda_prefill_T131072_H32_bf16", pre)
+    w1 = inputs.make_workload(1, device="cpu")
+    prefill("kda_prefill_T4096_H16_bf16", w1)
+    prefill("kda_prefill_T4096_H16_bf16_one_thread", w1, nt=1)
+    prefill("kda_varlen_4seq_T32768_H32_bf16", inputs.make_workload(2, device="cpu"))
+    steps = 32
+    state = dec.initial_state.double().cpu().numpy()
     t0 = time.perf_counter()
-    o, fin = oracle.forward(q, k, v, la, beta, num_threads=threads)
+    for i in range(steps):
+        oracle.decode_step(f(dec.q[i]), f(dec.k[i]), f(dec.v[i]), f(dec.log_alpha[i]), f(dec.beta[i]), state,
+                           num_threads=threads)
     dt = time.perf_counter() - t0
-    assert np.isfinite(o).all()
-    return {"value": S / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {S} of {inp.q.shape[1]} tokens of the prefill workload, all {inp.q.shape[2]} heads "
-                      f"(fp64 sequential recurrence, {dt:.1f} s)"}
+    out["kda_decode_N256_H32_bf16"] = {"tokens_per_s": round(DEC_N * steps / dt, 1), "seconds": round(dt, 3),
+                                       "threads": threads, "steps": steps}
+    print(f"[bench] oracle decode: {dt:.2f} s", file=sys.stderr, flush=True)
+    return out, threads
 
 
-def fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec, runs=5):
+def config_timing(inputs, kda, torch, dev, runs=20):
+    """The other prefill workloads on the GPU: the fp32 64-token latency case and the
+    4K and varlen throughput cases (median / min / max over ``runs``)."""
+    res = {}
+    w0 = inputs.make_workload(0, device=dev)
+    o = torch.empty_like(w0.v)
+    fin = torch.empty(1, 1, D, D, dtype=torch.float32, device=dev)
+    ms = time_fn(torch, lambda: kda.chunk_fwd(w0.q, w0.k, w0.v, w0.log_alpha, w0.beta, chunk=16, o=o,
+                                              final_state=fin), runs=50)
+    res["kda_fwd_T64_H1_fp32_c16"] = {"latency_us": {k: (round(v * 1e3, 2) if k != "runs" else v)
+                                                     for k, v in stats(ms).items()}}
+    for idx in (1, 2):
+        w = inputs.make_workload(idx, device=dev)
+        B, T, H = w.q.shape[:3]
+        n = w.num_seqs if w.cu_seqlens is not None else 0
+        ws = torch.empty(kda.workspace_size(B, T, H, n, 64, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(w.v)
+        fin = torch.empty(w.num_seqs, H, D, D, dtype=torch.float32, device=dev)
+        ms = time_fn(torch, lambda: kda.chunk_fwd(w.q, w.k, w.v, w.log_alpha, w.beta, initial_state=w.initial_state,
+                                                  cu_seqlens=w.cu_seqlens, chunk=64, o=o, final_state=fin,
+                                                  workspace=ws), runs=runs)
+        st = stats(ms)
+        med = st["median"] * 1e-3
+        res[inputs.WORKLOADS[idx]["name"]] = {
+            "ms": st, "tokens_per_s": round(B * T / med, 1),
+            "path_hbm_frac": round(PATH_BYTES_PER_TOK_HEAD * B * T * H / med / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] {inputs.WORKLOADS[idx]['name']}: {st['median']:.3f} ms", file=sys.stderr, flush=True)
+        del w, ws, o, fin
+    torch.cuda.empty_cache()
+    return res
+
+
+def path_timing(kda, torch, pre, runs=5):
+    """The headline prefill on each kernel set (kda_prefill_path)."""
+    B, T, H = pre.q.shape[:3]
+    out = {}
+    for path in ("record", "segmented", "single"):
+        ws = torch.empty(kda.workspace_size(B, T, H, 0, 64, kda.KDA_BF16, path=path), dtype=torch.uint8,
+                         device=pre.q.device)
+        o = torch.empty_like(pre.v)
+        fin = torch.empty(B, H, D, D, dtype=torch.float32, device=pre.q.device)
+
+        def run():
+            kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin,
+                          workspace=ws, path=path)
+        run()
+        torch.cuda.synchronize()
+        kda.timing_enable(True)
+        ms = time_fn(torch, run, runs=runs, warmup=0)
+        t = kda.timing_read()
+        kda.timing_enable(False)
+        km = {n: round(tot / cnt, 4) for n, (tot, cnt) in t.items() if cnt}
+        med = statistics.median(ms)
+        out[path] = {"ms": round(med, 4), "tokens_per_s": round(T / (med * 1e-3), 1), "kernel_ms": km,
+                     "workspace_bytes": ws.numel()}
+        print(f"[bench] path {path}: {med:.3f} ms", file=sys.stderr, flush=True)
+        del ws, o, fin
+    torch.cuda.empty_cache()
+    return out
+
+
+def fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec, runs=5):
     """The fused layer core on the same shapes: the prefill on raw q, k and gate /
     beta pre-activations with the output RMSNorm and gate, and the fused decode
-    step. Timed by the library's events, outside the headline steps."""
+    step."""
     B, T, H = pre.q.shape[:3]
     raw = inputs.make_raw_prefill(3, B=B, T=T, H=H, dtype="bf16", device=dev)
     fu = kda.fusion(out_gate=raw.out_gate, norm_weight=raw.norm_weight)
     z_dec = torch.randn(o_dec.shape, device=dev).to(o_dec.dtype)
     fu_dec = kda.fusion(out_gate=z_dec, norm_weight=raw.norm_weight)
-
-    def prefill():
-        kda.chunk_fwd(raw.q, raw.k, raw.v, raw.gate, raw.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws,
-                      fusion=fu)
-
-    def decode(i):
-        kda.decode_step(dec.q[i], dec.k[i], dec.v[i], dec.log_alpha[i], dec.beta[i], state, o=o_dec, fusion=fu_dec)
-
-    for i in range(2):
-        prefill()
-        decode(i)
-    torch.cuda.synchronize()
-    kda.timing_enable(True)
-    for i in range(runs):
-        prefill()
-        for j in range(8):
-            decode((i * 8 + j) % dec.q.shape[0])
-    torch.cuda.synchronize()
-    t = kda.timing_read()
-    kda.timing_enable(False)
-    ms = {name: tot / max(cnt, 1) for name, (tot, cnt) in t.items()}
-    prefill_ms = ms["plan"] + ms["intra"] + ms["inter"] + ms["outnorm"]
-    rows = T * H
-    outnorm_bytes = rows * 3 * 2 * D + 4 * D
+    o = torch.empty_like(pre.v)
+    fin = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(B, T, H, 0, 64, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+    prefill = lambda: kda.chunk_fwd(raw.q, raw.k, raw.v, raw.gate, raw.beta, chunk=CHUNK, o=o,  # noqa: E731
+                                    final_state=fin, workspace=ws, fusion=fu)
+    pms = time_fn(torch, prefill, runs=runs)
+    dms = time_fn(torch, lambda: kda.decode_step(dec.q[0], dec.k[0], dec.v[0], dec.log_alpha[0], dec.beta[0],
+                                                 state, o=o_dec, fusion=fu_dec), runs=16)
+    med = statistics.median(pms)
     dec_bytes = DEC_N * DEC_H * (DECODE_BYTES_PER_HEAD + 2 * D)
-    print(f"[bench] fused prefill {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] fused prefill {med:.3f} ms", file=sys.stderr, flush=True)
+    del raw, o, fin, ws
+    torch.cuda.empty_cache()
     return {"workload": "kda_prefill_T131072_H32_bf16 raw inputs (q, k unnormalised; gate and beta "
                         "pre-activations; output RMSNorm and sigmoid gate) + kda_decode_N256_H32_bf16",
-            "prefill_ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
-            "kernel_ms": {k: round(ms[k], 4) for k in ("plan", "intra", "inter", "outnorm")},
-            "outnorm_GBps": round(outnorm_bytes / (ms["outnorm"] * 1e-3) / 1e9, 1),
-            "decode_ms_per_step": round(ms["decode"], 4),
-            "decode_GBps": round(dec_bytes / (ms["decode"] * 1e-3) / 1e9, 1)}
+            "prefill_ms": stats(pms), "tokens_per_s": round(T / (med * 1e-3), 1),
+            "decode_ms_per_step": stats(dms),
+            "decode_GBps": round(dec_bytes / (statistics.median(dms) * 1e-3) / 1e9, 1)}
+
+
+def gate_timing(kda, torch, pre, dec, state, o_dec, runs=5):
+    """The scalar-gate (one decay per token and head) and no-decay paths on the
+    headline prefill shape and the decode batch."""
+    B, T, H = pre.q.shape[:3]
+    la_head = pre.log_alpha[..., 0].contiguous()
+    la_dec = dec.log_alpha[..., 0].contiguous()
+    o = torch.empty_like(pre.v)
+    fin = torch.empty(B, H, D, D, dtype=torch.float32, device=pre.q.device)
+    ws = torch.empty(kda.workspace_size(B, T, H, 0, 64, kda.KDA_BF16), dtype=torch.uint8, device=pre.q.device)
+    out = {}
+    for name, la, lad in (("gated_deltanet", la_head, la_dec), ("deltanet", None, None)):
+        pms = time_fn(torch, lambda: kda.chunk_fwd(pre.q, pre.k, pre.v, la, pre.beta, chunk=CHUNK, o=o,
+                                                   final_state=fin, workspace=ws), runs=runs)
+        dms = time_fn(torch, lambda: kda.decode_step(dec.q[0], dec.k[0], dec.v[0], None if lad is None else lad[0],
+                                                     dec.beta[0], state, o=o_dec), runs=16)
+        med = statistics.median(pms)
+        out[name] = {"prefill_ms": stats(pms), "tokens_per_s": round(T / (med * 1e-3), 1),
+                     "decode_ms_per_step": stats(dms)}
+        print(f"[bench] {name} prefill {med:.3f} ms", file=sys.stderr, flush=True)
+    del o, fin, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def backward_timing(inputs, kda, torch, pre, runs=3):
@@ -172,7 +388,7 @@ def backward_timing(inputs, kda, torch, pre, runs=3):
     total = sum(ms.get(n, 0.0) for n in names)
     tok_heads = T * H
     gbps = {n: round(BWD_BYTES_PER_TOK_HEAD[n] * tok_heads / (ms[n] * 1e-3) / 1e9, 1)
-            for n in names if n in BWD_BYTES_PER_TOK_HEAD}
+            for n in names if n in BWD_BYTES_PER_TOK_HEAD and n in ms}
     finite = all(bool(torch.isfinite(x).all()) for x in g.values() if x is not None)
     del g, ws, grad_o
     torch.cuda.empty_cache()
@@ -181,93 +397,45 @@ def backward_timing(inputs, kda, torch, pre, runs=3):
                         "state; 16-token chunks)",
             "ms": round(total, 4), "tokens_per_s": round(T / (total * 1e-3), 1),
             "kernel_ms": {n: round(ms.get(n, 0.0), 4) for n in names},
-            "kernel_GBps_algorithmic": gbps,
-            "path_hbm_frac_ideal": round(BWD_PATH_BYTES_PER_TOK_HEAD * tok_heads / (total * 1e-3) / 1e9
-                                         / HBM_PEAK_GBS, 4),
+            "kernel_GBps_design": gbps,
+            "path_hbm_frac": round(BWD_PATH_BYTES_PER_TOK_HEAD * tok_heads / (total * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "finite": finite}
 
 
-def gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec, runs=5):
-    """The scalar-gate (one decay per token and head) and no-decay paths on the
-    headline prefill shape and the decode batch, timed by the library's events."""
-    B, T, H = pre.q.shape[:3]
-    la_head = pre.log_alpha[..., 0].contiguous()
-    la_dec = dec.log_alpha[..., 0].contiguous()
-    out = {}
-    for name, la, lad in (("gated_deltanet", la_head, la_dec), ("deltanet", None, None)):
-        def run(i):
-            kda.chunk_fwd(pre.q, pre.k, pre.v, la, pre.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws)
-            for j in range(8):
-                d = (i * 8 + j) % dec.q.shape[0]
-                kda.decode_step(dec.q[d], dec.k[d], dec.v[d], None if lad is None else lad[d], dec.beta[d], state,
-                                o=o_dec)
-        run(0)
-        torch.cuda.synchronize()
-        kda.timing_enable(True)
-        for i in range(runs):
-            run(i + 1)
-        torch.cuda.synchronize()
-        t = kda.timing_read()
-        kda.timing_enable(False)
-        ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items()}
-        prefill_ms = ms["plan"] + ms["intra"] + ms["inter"]
-        tok_heads = T * H
-        gate_bytes = 0 if la is None else 4
-        intra_bytes = tok_heads * (3 * 2 * D + gate_bytes + 4) + (T // CHUNK) * H * RECORD_MOVED_BYTES_BF16_C64
-        out[name] = {"prefill_ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
-                     "kernel_ms": {k: round(ms[k], 4) for k in ("plan", "intra", "inter")},
-                     "intra_GBps": round(intra_bytes / (ms["intra"] * 1e-3) / 1e9, 1),
-                     "decode_ms_per_step": round(ms["decode"], 4)}
-        print(f"[bench] {name} prefill {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
-    return out
-
-
-def dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=(4096, 16384, 65536, 131072), runs=3):
+def dplr_comparison(inputs, kda, torch, dev, pre, lengths=(4096, 16384, 65536, 131072), runs=3):
     """KDA's chunked forward against the general DPLR chunked forward
     (kda_dplr_chunk_fwd) on the same shapes: H = 32, d = 128, bf16, 64-token chunks,
-    over input lengths. Prefixes of one 131072-token input set per method (KDA: the
-    headline workload; DPLR: the stable tied recipe with the same mixed decays).
-    Times are the library's per-kernel events (plan + intra + inter)."""
+    over input lengths. KDA runs the same kernel structure as the DPLR forward (the
+    record path: intra-chunk records, slab state kernels) and, beside it, its automatic
+    path. Prefixes of one 131072-token input set per method (KDA: the headline workload;
+    DPLR: the stable tied recipe with the same mixed decays)."""
     B, Tmax, H = pre.q.shape[:3]
     x = inputs.make_dplr(3, B=1, T=Tmax, H=H, dtype="bf16", la_mode="mixed", device=dev)
     ws_d = torch.empty(kda.dplr_workspace_size(1, Tmax, H, 0, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+    ws_k = torch.empty(kda.workspace_size(1, Tmax, H, 0, 64, kda.KDA_BF16, path="record"), dtype=torch.uint8,
+                       device=dev)
+    ws_a = torch.empty(kda.workspace_size(1, Tmax, H, 0, 64, kda.KDA_BF16), dtype=torch.uint8, device=dev)
     o = torch.empty_like(pre.v)
     fin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        kda.timing_enable(True)
-        for _ in range(runs):
-            fn()
-        torch.cuda.synchronize()
-        t = kda.timing_read()
-        kda.timing_enable(False)
-        ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items() if cnt}
-        return {n: ms.get(n, 0.0) for n in ("plan", "intra", "inter")}
-
     rows = []
     for T in lengths:
         if T > Tmax:
             continue
-        sl = lambda t: t[:, :T]
-        km = timed(lambda: kda.chunk_fwd(sl(pre.q), sl(pre.k), sl(pre.v), sl(pre.log_alpha), sl(pre.beta),
-                                         chunk=CHUNK, o=o[:, :T], final_state=fin, workspace=ws))
-        dm = timed(lambda: kda.dplr_chunk_fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.a), sl(x.b), sl(x.log_alpha),
-                                              o=o[:, :T], final_state=fin, workspace=ws_d))
-        kt, dt = sum(km.values()), sum(dm.values())
-        tok_heads = T * H
-        d_intra_bytes = tok_heads * DPLR_IN_BYTES_PER_TOK_HEAD + (T // CHUNK) * H * DPLR_RECORD_MOVED_BYTES_BF16
-        d_inter_bytes = (T // CHUNK) * H * DPLR_RECORD_MOVED_BYTES_BF16 + tok_heads * 2 * D
-        rows.append({"T": T, "kda_ms": round(kt, 4), "dplr_ms": round(dt, 4),
-                     "dplr_over_kda": round(dt / kt, 3),
-                     "kda_tokens_per_s": round(T / (kt * 1e-3), 1), "dplr_tokens_per_s": round(T / (dt * 1e-3), 1),
-                     "kda_kernel_ms": {n: round(v, 4) for n, v in km.items()},
-                     "dplr_kernel_ms": {n: round(v, 4) for n, v in dm.items()},
-                     "dplr_intra_GBps": round(d_intra_bytes / (dm["intra"] * 1e-3) / 1e9, 1),
-                     "dplr_inter_GBps": round(d_inter_bytes / (dm["inter"] * 1e-3) / 1e9, 1)})
-        print(f"[bench] T={T}: kda {kt:.3f} ms, dplr {dt:.3f} ms ({dt / kt:.2f}x)", file=sys.stderr, flush=True)
-    del x, ws_d, o, fin
+        sl = lambda t: t[:, :T]  # noqa: E731
+        kr = statistics.median(time_fn(torch, lambda: kda.chunk_fwd(
+            sl(pre.q), sl(pre.k), sl(pre.v), sl(pre.log_alpha), sl(pre.beta), chunk=CHUNK, o=o[:, :T],
+            final_state=fin, workspace=ws_k, path="record"), runs=runs))
+        ka = statistics.median(time_fn(torch, lambda: kda.chunk_fwd(
+            sl(pre.q), sl(pre.k), sl(pre.v), sl(pre.log_alpha), sl(pre.beta), chunk=CHUNK, o=o[:, :T],
+            final_state=fin, workspace=ws_a), runs=runs))
+        dm = statistics.median(time_fn(torch, lambda: kda.dplr_chunk_fwd(
+            sl(x.q), sl(x.k), sl(x.v), sl(x.a), sl(x.b), sl(x.log_alpha), o=o[:, :T], final_state=fin,
+            workspace=ws_d), runs=runs))
+        rows.append({"T": T, "kda_record_ms": round(kr, 4), "kda_auto_ms": round(ka, 4), "dplr_ms": round(dm, 4),
+                     "dplr_over_kda_same_kernels": round(dm / kr, 3), "dplr_over_kda_auto": round(dm / ka, 3),
+                     "kda_tokens_per_s": round(T / (ka * 1e-3), 1), "dplr_tokens_per_s": round(T / (dm * 1e-3), 1)})
+        print(f"[bench] T={T}: kda {kr:.3f} / {ka:.3f} ms, dplr {dm:.3f} ms", file=sys.stderr, flush=True)
+    del x, ws_d, ws_k, ws_a, o, fin
     torch.cuda.empty_cache()
     return {"workload": "kda_vs_dplr_H32_bf16_c64 (prefill at several lengths; the general DPLR transition "
                         "Diag(alpha) + a b^T with free a, b against KDA's key-tied one)",
@@ -277,20 +445,15 @@ def dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=(4096, 16384, 6553
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-per-step", type=int, default=8)
-    ap.add_argument("--decode-inputs", type=int, default=1024, help="distinct decode tokens, cycled")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=PREFILL_T)
+    ap.add_argument("--decode-inputs", type=int, default=256, help="distinct decode tokens, cycled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gates", action="store_true",
-                    help="skip the timing of the scalar-gate (Gated DeltaNet) and no-decay (DeltaNet) paths")
-    ap.add_argument("--no-fused", action="store_true",
-                    help="skip the timing of the fused layer core (prologue and epilogue in the kernels)")
-    ap.add_argument("--no-backward", action="store_true",
-                    help="skip the timing of the backward (kda_chunk_bwd) on the prefill shape")
-    ap.add_argument("--no-dplr", action="store_true",
-                    help="skip the KDA versus general-DPLR forward comparison over input lengths")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline steps (no configs, paths, fused, gates, backward, DPLR)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-dplr", action="store_true", help="skip the KDA versus general-DPLR comparison")
     ap.add_argument("--dplr-lengths", default="4096,16384,65536,131072",
                     help="comma-separated sequence lengths of the DPLR comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -333,17 +496,28 @@ def main():
     o_dec = torch.empty(DEC_N, DEC_H, D, dtype=torch.bfloat16, device=dev)
     n_dec_in = dec.q.shape[0]
     dec_i = [0]
+    tm = StreamTimer(torch)
 
-    def step():
-        kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin,
-                      workspace=ws)
-        for _ in range(args.decode_per_step):
-            i = dec_i[0] % n_dec_in
-            kda.decode_step(dec.q[i], dec.k[i], dec.v[i], dec.log_alpha[i], dec.beta[i], state, o=o_dec)
-            dec_i[0] += 1
+    def prefill():
+        kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws)
+
+    def decode():
+        i = dec_i[0] % n_dec_in
+        kda.decode_step(dec.q[i], dec.k[i], dec.v[i], dec.log_alpha[i], dec.beta[i], state, o=o_dec)
+        dec_i[0] += 1
+
+    def step(timed):
+        if timed:
+            tm("prefill", prefill)
+            for _ in range(args.decode_per_step):
+                tm("decode", decode)
+        else:
+            prefill()
+            for _ in range(args.decode_per_step):
+                decode()
 
     for _ in range(args.warmup):
-        step()
+        step(False)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
@@ -351,7 +525,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timing = kda.timing_read()
@@ -359,36 +533,71 @@ def main():
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     K = args.steps
-    ms = {name: tot / max(cnt, 1) for name, (tot, cnt) in timing.items()}
-    prefill_ms = ms["plan"] + ms["intra"] + ms["inter"]
+    pst, dst = stats(tm.ms("prefill")), stats(tm.ms("decode"))
+    prefill_ms, dec_ms = pst["median"], dst["median"]
     tokens_per_s = T / (prefill_ms * 1e-3)
     tok_heads = T * H
-    flops = FLOP_PER_TOK_HEAD * tok_heads
-    prefill_tflops = flops / (prefill_ms * 1e-3) / 1e12
-    n_chunks = (T + CHUNK - 1) // CHUNK
-    rec_bytes = n_chunks * H * RECORD_MOVED_BYTES_BF16_C64
-    in_bytes = tok_heads * (3 * 2 * D + 4 * D + 4)
-    out_bytes = tok_heads * 2 * D
-    kernel_bytes = {
-        "intra": in_bytes + rec_bytes,            # reads the chunk's inputs, writes its record
-        "inter": rec_bytes + out_bytes,            # reads the records once per head, writes o
-        "decode": DEC_N * DEC_H * DECODE_BYTES_PER_HEAD,
-    }
+    kms = {n: tot / cnt for n, (tot, cnt) in timing.items() if cnt}
     src_hash = kernel_source_hash()
+    traffic = committed_profile("pmc_traffic.json", src_hash)
+    mfma_prof = committed_profile("pmc_mfma.json", src_hash)
+
+    # the whole prefill path against the HBM roofline, on the method's bytes
+    path_bytes = PATH_BYTES_PER_TOK_HEAD * tok_heads
+    flops = FLOP_PER_TOK_HEAD * tok_heads
+    achieved = path_bytes / (prefill_ms * 1e-3) / 1e9
+    t_bound_ms = max(flops / (BF16_MFMA_PEAK_TFLOPS * 1e12), path_bytes / (HBM_PEAK_GBS * 1e9)) * 1e3
+    path_kernels = [n for n in PREFILL_KERNELS if n in kms]
+    path_traffic = None
+    if traffic:
+        per = traffic.get("kernels", {})
+        names = set(path_kernels) | ({"seg_plan"} if "seg_first" in path_kernels else set())
+        if all(n in per for n in path_kernels):
+            path_traffic = round(sum(per[n]["hbm_bytes_per_launch"] for n in names if n in per), 0)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": path_traffic,
+            "kernel": "prefill path (" + ", ".join(path_kernels) + ")",
+            "algorithmic_bytes": path_bytes, "t_bound_ms": round(t_bound_ms, 4),
+            "frac_t_bound_over_t": round(t_bound_ms / prefill_ms, 4)}
+
+    # each kernel of the path: design bytes (what it moves by construction) and counter traffic
+    n_chunks = (T + CHUNK - 1) // CHUNK
+    rec_moved = n_chunks * H * RECORD_MOVED_BYTES_BF16_C64
+    seg_a, seg_b = seg_design_bytes(T, H)
+    lseg, ns = seg_plan(T, H)
+    design = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD + rec_moved,
+              "inter": rec_moved + tok_heads * 2 * D,
+              "seg_first": seg_a, "seg_second": seg_b,
+              "seg_scan": H * max(0, ns - 2) * 3 * 4 * D * D,
+              "decode": DEC_N * DEC_H * DECODE_BYTES_PER_HEAD}
+    share = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD}  # the method's bytes each kernel is responsible for
+    share["seg_second" if "seg_second" in kms else "inter"] = tok_heads * 2 * D
     kernels = {}
-    for name in ("intra", "inter", "decode"):
-        t_s = ms[name] * 1e-3
-        gbs = kernel_bytes[name] / t_s / 1e9
-        traffic = traffic_from_profiles(name, src_hash)
-        kernels[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "avg_ms": round(ms[name], 4), "launches": timing[name][1],
-                         "algorithmic_bytes_per_launch": kernel_bytes[name]}
-    per_step = {"intra": ms["intra"], "inter": ms["inter"], "decode": ms["decode"] * args.decode_per_step}
-    dominant = max(per_step, key=per_step.get)
-    roof = {k: kernels[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
-    roof["kernel"] = dominant
-    dec_gbs = kernel_bytes["decode"] / (ms["decode"] * 1e-3) / 1e9
+    for name in path_kernels + ["decode"]:
+        avg = kms[name]
+        ent = {"avg_ms": round(avg, 4), "launches": timing[name][1]}
+        if name in design:
+            ent["design_bytes_per_launch"] = design[name]
+            ent["design_GBps"] = round(design[name] / (avg * 1e-3) / 1e9, 1)
+            ent["design_frac_of_hbm_peak"] = round(design[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if name in share:
+            ent["algorithmic_bytes_per_launch"] = share[name]
+        if traffic and name in traffic.get("kernels", {}):
+            tb = traffic["kernels"][name]["hbm_bytes_per_launch"]
+            ent["traffic_bytes"] = round(tb, 0)
+            if name in design:
+                ent["traffic_over_design"] = round(tb / design[name], 3)
+            if name in share:
+                ent["traffic_over_algorithmic"] = round(tb / share[name], 3)
+        kernels[name] = ent
+
+    dec_gbs = DEC_N * DEC_H * DECODE_BYTES_PER_HEAD / (dec_ms * 1e-3) / 1e9
+    mfma = {"algorithmic_tflops": round(flops / (prefill_ms * 1e-3) / 1e12, 2),
+            "algorithmic_frac_of_bf16_peak": round(flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_util_rocprof": None, "rocprof": None}
+    if mfma_prof and mfma_prof.get("summary"):
+        mfma["rocprof"] = mfma_prof["summary"]
+        mfma["mfma_util_rocprof"] = mfma_prof["summary"].get("prefill_mfma_util")
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + %MFMA peak; decode GB/s %HBM peak",
@@ -406,32 +615,40 @@ def main():
         "config": {"workload": "kda_prefill_T131072_H32_bf16", "T": T, "H": H, "d": D, "chunk": CHUNK,
                    "decode_workload": "kda_decode_N256_H32_bf16", "decode_per_step": args.decode_per_step,
                    "parallelism": "single GPU"},
-        "prefill": {"ms": round(prefill_ms, 4), "tokens_per_s": round(tokens_per_s, 1),
-                    "algorithmic_tflops": round(prefill_tflops, 2),
-                    "mfma_frac_algorithmic": round(prefill_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                    "path_hbm_frac_ideal": round(PATH_BYTES_PER_TOK_HEAD * tok_heads / (prefill_ms * 1e-3) / 1e9
-                                                 / HBM_PEAK_GBS, 4),
-                    "kernel_ms": {"plan": round(ms["plan"], 4), "intra": round(ms["intra"], 4),
-                                  "inter": round(ms["inter"], 4)}},
-        "decode": {"ms_per_step": round(ms["decode"], 4), "GBps": round(dec_gbs, 1),
-                   "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                   "tokens_per_s": round(DEC_N / (ms["decode"] * 1e-3), 1)},
+        "prefill": {"ms": pst, "tokens_per_s": round(tokens_per_s, 1),
+                    "path_hbm_frac": roof["frac"],
+                    "kernel_ms": {n: round(kms[n], 4) for n in path_kernels},
+                    "segments": {"chunks_per_segment": lseg, "segments_per_head": ns}},
+        "mfma": mfma,
+        "decode": {"ms_per_step": dst, "GBps": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "tokens_per_s": round(DEC_N / (dec_ms * 1e-3), 1)},
         "roofline": roof,
         "kernels": kernels,
         "kernel_source_hash": src_hash,
     }
-    if not args.no_fused:
-        result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, ws, o, fin, state, o_dec)
-    if not args.no_gates:
-        result["gates"] = gate_timing(kda, torch, pre, dec, ws, o, fin, state, o_dec)
-    if not args.no_backward:
-        result["backward"] = backward_timing(inputs, kda, torch, pre)
-    if not args.no_dplr:
-        lengths = tuple(int(x) for x in args.dplr_lengths.split(",") if x)
-        result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, ws, lengths=lengths)
+    if not args.no_extras:
+        result["configs"] = config_timing(inputs, kda, torch, dev)
+        result["paths"] = path_timing(kda, torch, pre)
+        result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec)
+        result["gates"] = gate_timing(kda, torch, pre, dec, state, o_dec)
+        if not args.no_backward:
+            del ws
+            torch.cuda.empty_cache()
+            result["backward"] = backward_timing(inputs, kda, torch, pre)
+        if not args.no_dplr:
+            lengths = tuple(int(x) for x in args.dplr_lengths.split(",") if x)
+            result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, lengths=lengths)
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_sample_tokens)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        base, threads = cpu_baselines(inputs, pre, dec)
+        head = base["kda_prefill_T131072_H32_bf16"]
+        result["cpu_baseline"] = {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"all {head['tokens']} tokens x {head['heads']} heads of the headline "
+                                            f"prefill workload (fp64 sequential recurrence, {head['seconds']} s)",
+                                  "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+        result["cpu_baselines"] = base
+    result["environment"] = environment(torch)
     print(json.dumps(result), flush=True)
 
 

@@ -2,24 +2,37 @@
 
 This module only draws random numbers and shapes them; it holds none of the
 recurrence's arithmetic. The tests of the GPU path, the oracle comparisons and
-the bench all take their inputs from here. Draws use a ``torch.Generator`` seeded
-with ``seed`` on the target device, in a fixed order: cut points (packed
-batches), q, k, v, log-decay normals, slow-channel choice (mixed mode), beta
-normals, initial state. The same seed on the same device type gives the same
-values; the CPU and GPU streams differ.
+the bench all take their inputs from here.
+
+The measured workloads (``make_prefill``, ``make_workload``, ``make_decode``) are
+drawn on the host with NumPy's ``default_rng`` in float64, so they can be
+reproduced on any machine: every draw takes the next child of
+``SeedSequence(seed)`` in a fixed order, and each block of ``BLOCK`` elements of a
+draw comes from its own child stream of that child (so the values do not depend on
+how many threads fill the blocks). Prefill draw order: cut points (packed batches),
+q, k, v, log-decay normals, slow-channel choice (mixed mode), beta normals, initial
+state. Decode: the initial state, then per step q, k, v, log-decay normals, beta
+normals.
 
 Distributions (the plainest reading of the workloads the library is measured on):
-  q, k      ~ N(0, 1), then L2-normalised per (token, head) in fp32 (the model
+  q, k      ~ N(0, 1), then L2-normalised per (token, head) in float64 (the model
               normalises q and k before the mixer; GeekNews "Kimi Linear" summary,
               section "Kimi Linear 모델 구성"), then rounded to the compute dtype
-              (bf16: round to nearest even)
+              (bf16: round to nearest even, by torch on the CPU)
   v         ~ N(0, 1), rounded to the compute dtype
-  log_alpha = -scale * softplus(N(0, 1)) per channel (fp32). In "mixed" mode a
-              seeded half of each head's channels is -1e-3 (slow) and the rest
-              -softplus(N(0, 1)) (fast), the same channels at every token
-  beta      = sigmoid(N(0, 1)) per (token, head) (fp32)
-  S_0       ~ N(0, s0_std) fp32, or None (zeros)
+  log_alpha = -scale * softplus(N(0, 1)) per channel, computed in float64 and
+              stored as float32. In "mixed" mode a seeded half of each head's
+              channels is -1e-3 (slow) and the rest -softplus(N(0, 1)) (fast), the
+              same channels at every token
+  beta      = sigmoid(N(0, 1)) per (token, head), float32
+  S_0       ~ N(0, s0_std) float32, or None (zeros)
+
+The other inputs (raw layer inputs, DPLR inputs, cotangents) use a seeded
+``torch.Generator`` on the target device.
 """
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -70,6 +83,82 @@ class PrefillInputs:
                     initial_state=f(self.initial_state), cu_seqlens=cu)
 
 
+#: Elements per independent stream of a host draw (a multiple of the head size).
+BLOCK = 1 << 22
+
+
+def _host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class HostDraws:
+    """Host draws of one input set: each call takes the next child of
+    ``SeedSequence(seed)``; block b of a draw (``BLOCK`` elements) comes from
+    ``default_rng`` on that child's b-th child."""
+
+    def __init__(self, seed: int):
+        self.root = np.random.SeedSequence(int(seed))
+
+    def child(self):
+        return self.root.spawn(1)[0]
+
+    def fill(self, n: int, fn, ss=None) -> np.ndarray:
+        """n float32 values, block by block: fn(rng, count) returns count float64 values."""
+        ss = ss if ss is not None else self.child()
+        nb = (n + BLOCK - 1) // BLOCK
+        kids = ss.spawn(nb)
+        out = np.empty(n, np.float32)
+
+        def work(b):
+            lo = b * BLOCK
+            c = min(BLOCK, n - lo)
+            out[lo:lo + c] = fn(np.random.default_rng(kids[b]), c)
+
+        if nb > 1:
+            with ThreadPoolExecutor(_host_threads()) as ex:
+                list(ex.map(work, range(nb)))
+        elif nb == 1:
+            work(0)
+        return out
+
+
+def _h_normal(rng, c):
+    return rng.standard_normal(c)
+
+
+def _h_unit_rows(rng, c, d=D):
+    x = rng.standard_normal(c).reshape(-1, d)
+    return (x / np.sqrt(np.sum(x * x, axis=1, keepdims=True))).ravel()
+
+
+def _h_softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _h_sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _to_device(a32: np.ndarray, shape, dtype: str, device):
+    """float32 host values -> the compute dtype (bf16 rounded to nearest even by torch
+    on the CPU) on ``device``."""
+    t = torch.from_numpy(a32).view(*shape)
+    if dtype != "fp32":
+        t = t.to(TORCH_DTYPE[dtype])
+    return t.to(device)
+
+
+def _host_composition(rng, total: int, parts: int) -> np.ndarray:
+    """cu_seqlens of ``parts`` positive lengths summing to ``total``: distinct cut
+    points drawn uniformly from [1, total-1] and sorted."""
+    cuts = np.sort(rng.choice(total - 1, size=parts - 1, replace=False) + 1)
+    return np.concatenate([[0], cuts, [total]]).astype(np.int32)
+
+
 def _gen(seed, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -99,36 +188,43 @@ def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64,
                  cu_seqlens=None, device="cuda", dk: int = D, dv: int = D, gate: str = "channel") -> PrefillInputs:
     """``gate``: "channel" (log_alpha [B, T, H, dk]), "head" (one decay per (token,
     head): log_alpha [B, T, H], drawn like one channel) or "none" (log_alpha None)."""
-    g = _gen(seed, device)
+    dr = HostDraws(seed)
     cu = None
     if cu_seqlens is not None:
         assert B == 1
         cu = torch.as_tensor(np.asarray(cu_seqlens), dtype=torch.int32).to(device)
     elif num_seqs is not None:
         assert B == 1
-        cu = uniform_composition(g, T, num_seqs, device)
-    td = TORCH_DTYPE[dtype]
-    q = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
-    k = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
-    v = _normal(g, (B, T, H, dv), device).to(td)
-    z = _normal(g, (B, T, H, dk) if gate == "channel" else (B, T, H), device)
-    if gate == "head":
-        assert la_mode == "scaled"
-        log_alpha = -la_scale * torch.nn.functional.softplus(z)
-    elif gate == "none":
+        cu = torch.from_numpy(_host_composition(np.random.default_rng(dr.child()), T, num_seqs)).to(device)
+    shape_k, shape_v = (B, T, H, dk), (B, T, H, dv)
+    nk, nv = B * T * H * dk, B * T * H * dv
+    q = _to_device(dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk)), shape_k, dtype, device)
+    k = _to_device(dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk)), shape_k, dtype, device)
+    v = _to_device(dr.fill(nv, _h_normal), shape_v, dtype, device)
+    if gate == "none":
         log_alpha = None
+    elif gate == "head":
+        assert la_mode == "scaled"
+        log_alpha = _to_device(dr.fill(B * T * H, lambda r, c: -la_scale * _h_softplus(r.standard_normal(c))),
+                               (B, T, H), "fp32", device)
     elif la_mode == "scaled":
-        log_alpha = -la_scale * torch.nn.functional.softplus(z)
+        log_alpha = _to_device(dr.fill(nk, lambda r, c: -la_scale * _h_softplus(r.standard_normal(c))), shape_k,
+                               "fp32", device)
     elif la_mode == "mixed":
-        log_alpha = -torch.nn.functional.softplus(z)
+        la = dr.fill(nk, lambda r, c: -_h_softplus(r.standard_normal(c))).reshape(B * T, H, dk)
+        rs = np.random.default_rng(dr.child())
         for h in range(H):
-            slow = torch.randperm(dk, generator=g, device=device)[: dk // 2]
-            log_alpha[:, :, h, slow] = -1e-3
+            slow = rs.permutation(dk)[: dk // 2]
+            la[:, h, slow] = np.float32(-1e-3)
+        log_alpha = _to_device(la.reshape(-1), shape_k, "fp32", device)
     else:
         raise ValueError(la_mode)
-    beta = torch.sigmoid(_normal(g, (B, T, H), device))
+    beta = _to_device(dr.fill(B * T * H, lambda r, c: _h_sigmoid(r.standard_normal(c))), (B, T, H), "fp32", device)
     N = B if cu is None else cu.numel() - 1
-    s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
+    s0 = None
+    if s0_std > 0:
+        s0 = _to_device(dr.fill(N * H * dk * dv, lambda r, c: s0_std * r.standard_normal(c)), (N, H, dk, dv), "fp32",
+                        device)
     return PrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(),
                          None if log_alpha is None else log_alpha.contiguous(), beta.contiguous(),
                          s0, cu, dtype, chunk, dict(seed=seed, la_mode=la_mode, la_scale=la_scale, gate=gate))
@@ -171,18 +267,25 @@ def make_decode(seed: int = 4, N: int = 256, H: int = 32, n_steps: int = 1024, d
                 la_scale: float = 0.1, s0_std: float = 0.02, device="cuda", dk: int = D, dv: int = D) -> DecodeInputs:
     """Decode workload: persisted states, then ``n_steps`` fresh single tokens per
     (sequence, head). Step i's draws do not depend on ``n_steps``."""
-    g = _gen(seed, device)
-    td = TORCH_DTYPE[dtype]
-    s0 = s0_std * _normal(g, (N, H, dk, dv), device)
-    qs, ks, vs, las, bs = [], [], [], [], []
-    for _ in range(n_steps):
-        qs.append(_unit_rows(_normal(g, (N, H, dk), device)).to(td))
-        ks.append(_unit_rows(_normal(g, (N, H, dk), device)).to(td))
-        vs.append(_normal(g, (N, H, dv), device).to(td))
-        las.append(-la_scale * torch.nn.functional.softplus(_normal(g, (N, H, dk), device)))
-        bs.append(torch.sigmoid(_normal(g, (N, H), device)))
-    st = lambda xs: torch.stack(xs).contiguous()
-    return DecodeInputs(s0, st(qs), st(ks), st(vs), st(las), st(bs), dtype)
+    dr = HostDraws(seed)
+    s0 = _to_device(dr.fill(N * H * dk * dv, lambda r, c: s0_std * r.standard_normal(c)), (N, H, dk, dv), "fp32",
+                    device)
+    kids = [[dr.child() for _ in range(5)] for _ in range(n_steps)]  # q, k, v, log-decay, beta per step
+    nk, nv = N * H * dk, N * H * dv
+
+    def step(i):
+        kq, kk, kv, kl, kb = kids[i]
+        # one block per draw (a step's draws are far below BLOCK)
+        return (dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk), kq), dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk), kk),
+                dr.fill(nv, _h_normal, kv), dr.fill(nk, lambda r, c: -la_scale * _h_softplus(r.standard_normal(c)), kl),
+                dr.fill(N * H, lambda r, c: _h_sigmoid(r.standard_normal(c)), kb))
+
+    with ThreadPoolExecutor(_host_threads()) as ex:
+        steps = list(ex.map(step, range(n_steps)))
+    st = lambda j, shape, dt: _to_device(np.concatenate([x[j] for x in steps]) if steps else np.zeros(0, np.float32),
+                                         (n_steps,) + shape, dt, device)
+    return DecodeInputs(s0, st(0, (N, H, dk), dtype), st(1, (N, H, dk), dtype), st(2, (N, H, dv), dtype),
+                        st(3, (N, H, dk), "fp32"), st(4, (N, H), "fp32"), dtype)
 
 
 @dataclass

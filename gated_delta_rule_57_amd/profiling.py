@@ -8,9 +8,20 @@
         what the same counter reads for a device copy of 1 GiB. <pmc_root> holds the
         rocprofv3 output directories copy_FETCH_SIZE, copy_WRITE_SIZE, bench_FETCH_SIZE
         and bench_WRITE_SIZE.
+    python -m gated_delta_rule_57_amd.profiling mfma <pmc_root> <trace_dir> <out.json> "<commands>"
+        MFMA use per kernel from counter runs bench_<COUNTER> under <pmc_root> (one
+        counter per run: SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32,
+        SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CU_CYCLES; any may be
+        missing) and the average kernel durations of a kernel-trace run of the same
+        command in <trace_dir>. The MOPS counters count MFMA work in units of 512
+        flops, so counted flops over the kernel's duration, against the chip's dense
+        peak for that type, is the MFMA utilisation; the busy-cycle ratio is kept
+        beside it.
 
 Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode,
-outnorm, bwd_local, bwd_state, bwd_chunk); the intra-chunk kernel's scalar-gate and
+outnorm, bwd_local, bwd_state, bwd_chunk; seg_plan, seg_first, seg_scan and
+seg_second for the segment-parallel state kernels, single_first and single_second for
+the single pass); the intra-chunk kernel's scalar-gate and
 no-decay instantiations become intra_gdn and intra_deltanet, its 16-token-chunk
 instantiation (the backward's forward pass) intra16, and the 16-token state
 kernel inter16. The general-DPLR forward's kernels are dplr_intra and dplr_inter
@@ -26,12 +37,20 @@ import os
 import re
 import sys
 
-KERNELS = (("plan_kernel", "plan"), ("dplr_intra_kernel", "dplr_intra"), ("intra_kernel", "intra"),
+KERNELS = (("seg_plan_kernel", "seg_plan"), ("seg_scan_kernel", "seg_scan"), ("rec_seg_kernel", "seg"),
+           ("seg_pass_kernel", "single"),
+           ("plan_kernel", "plan"), ("dplr_intra_kernel", "dplr_intra"), ("intra_kernel", "intra"),
            ("inter_wg_kernel", "inter"),
            ("inter16_kernel", "inter16"), ("fwd_state_kernel", "inter16"), ("inter_kernel", "inter"), ("decode_kernel", "decode"),
            ("output_norm_gate_kernel", "outnorm"), ("bwd_local_kernel", "bwd_local"),
            ("bwd_state_kernel", "bwd_state"), ("bwd_chunk_kernel", "bwd_chunk"))
 COPY_BYTES = 1 << 30
+PEAK_FLOPS = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 2.5e15, "SQ_INSTS_VALU_MFMA_MOPS_F32": 157.3e12}
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
+# kernels of the bf16 64-token prefill (any path) and the decode step
+PREFILL_PATH = ("plan", "intra", "inter", "seg_plan", "seg_first", "seg_scan", "seg_second", "single_first",
+                "single_second", "outnorm")
 
 
 def kernel_source_hash(root=None):
@@ -52,9 +71,16 @@ def kernel_source_hash(root=None):
 _GATE_ARG = re.compile(r"intra_kernel(?:I\w*?Li(\d+)ELi(\d)E|<[^>]*,\s*(\d+),\s*(\d)>)")
 
 
+# the SECOND flag of the segment-parallel pass kernels (..Lb1E.. / ..true>): the later
+# segments' pass
+_SECOND = re.compile(r"(?:Lb1E|true>)")
+
+
 def short_name(name):
     for key, short in KERNELS:
         if key in name:
+            if short in ("seg", "single"):
+                return short + ("_second" if _SECOND.search(name) else "_first")
             if short == "intra":
                 m = _GATE_ARG.search(name)
                 chunk = (m.group(1) or m.group(3)) if m else None
@@ -130,8 +156,66 @@ def summarize_traffic(pmc_root, out_json, commands):
     print(json.dumps(out, indent=1))
 
 
+def trace_durations(trace_dir):
+    """{short name: (average ns, calls)} from a kernel-trace statistics run."""
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    out = {}
+    for r in csv.DictReader(open(stats[0])):
+        s = short_name(r["Name"])
+        if s is None:
+            continue
+        tot, calls = out.get(s, (0.0, 0))
+        out[s] = (tot + float(r["TotalDurationNs"]), calls + int(r["Calls"]))
+    return {s: (tot / calls, calls) for s, (tot, calls) in out.items()}
+
+
+def summarize_mfma(pmc_root, trace_dir, out_json, commands):
+    dur = trace_durations(trace_dir)
+    kernels = {}
+    for counter in MFMA_COUNTERS:
+        run = os.path.join(pmc_root, f"bench_{counter}")
+        if not os.path.isdir(run):
+            continue
+        for name, vs in _counter(run, counter).items():
+            s = short_name(name)
+            if s is not None:
+                kernels.setdefault(s, {}).setdefault(counter, []).extend(vs)
+    per = {}
+    for s, cs in kernels.items():
+        ent = {c: sum(v) / len(v) for c, v in cs.items()}
+        if s in dur:
+            ns = dur[s][0]
+            ent["avg_ns"] = ns
+            util = 0.0
+            for c, peak in PEAK_FLOPS.items():
+                if c in ent:
+                    flops = ent[c] * 512
+                    ent[c.replace("SQ_INSTS_VALU_MFMA_MOPS_", "mfma_flops_").lower()] = flops
+                    util += flops / (ns * 1e-9) / peak
+            ent["mfma_util"] = util
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in ent and ent.get("SQ_BUSY_CU_CYCLES"):
+            ent["mfma_busy_over_cu_busy"] = ent["SQ_VALU_MFMA_BUSY_CYCLES"] / ent["SQ_BUSY_CU_CYCLES"]
+        per[s] = ent
+    path = [s for s in PREFILL_PATH if s in per and "avg_ns" in per[s]]
+    summary = None
+    if path:
+        ns = sum(per[s]["avg_ns"] for s in path)
+        util = sum(per[s].get("mfma_util", 0.0) * per[s]["avg_ns"] for s in path) / ns
+        flops = sum(per[s].get("mfma_flops_bf16", 0.0) + per[s].get("mfma_flops_f32", 0.0) for s in path)
+        summary = {"prefill_kernels": path, "prefill_mfma_util": round(util, 4),
+                   "prefill_mfma_flops_counted": flops, "prefill_kernel_ns": ns,
+                   "per_kernel_mfma_util": {s: round(per[s].get("mfma_util", 0.0), 4) for s in path}}
+    out = {"kernel_source_hash": kernel_source_hash(), "kernels": per, "summary": summary, "commands": commands,
+           "peaks_flops": PEAK_FLOPS, "mops_unit_flops": 512}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 if __name__ == "__main__":
-    if len(sys.argv) not in (5, 6) or sys.argv[1] not in ("trace", "traffic") or \
-            (sys.argv[1] == "traffic" and len(sys.argv) != 5):
+    modes = {"trace": (summarize_trace, (5, 6)), "traffic": (summarize_traffic, (5,)), "mfma": (summarize_mfma, (6,))}
+    if len(sys.argv) < 2 or sys.argv[1] not in modes or len(sys.argv) not in modes[sys.argv[1]][1]:
         raise SystemExit(__doc__)
-    {"trace": summarize_trace, "traffic": summarize_traffic}[sys.argv[1]](*sys.argv[2:])
+    modes[sys.argv[1]][0](*sys.argv[2:])
