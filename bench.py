@@ -23,11 +23,11 @@ events on the stream the library's kernels run on. Beside it:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import glob
 import json
 import os
 import platform
 import statistics
-import subprocess
 import sys
 import time
 
@@ -150,13 +150,18 @@ def environment(torch):
         env["amdgpu_driver"] = open("/sys/module/amdgpu/version").read().strip()
     except OSError:
         pass
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        clocks = [ln.strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln]
-        if clocks:
-            env["rocm_smi_clocks"] = clocks[:4]
-    except Exception:  # noqa: BLE001
-        pass
+    # current shader and memory clock levels (the '*' entry of the DPM tables), read
+    # from sysfs so no other program is started from this GPU process
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+            try:
+                cur = [ln.strip() for ln in open(os.path.join(os.path.dirname(path), name)) if "*" in ln]
+            except OSError:
+                continue
+            if cur:
+                env.setdefault("dpm_clocks", {})[key] = cur[0]
+        if "dpm_clocks" in env:
+            break
     env.update(host_cpu=cpu_model(), host_cores=host_cores(), omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
     return env
 
@@ -568,7 +573,9 @@ def main():
     design = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD + rec_moved,
               "inter": rec_moved + tok_heads * 2 * D,
               "seg_first": seg_a, "seg_second": seg_b,
-              "seg_scan": H * max(0, ns - 2) * 3 * 4 * D * D,
+              # each of a head's 8 column work-groups reads a middle segment's whole M and
+              # its slice of B and writes its slice of the next entry state
+              "seg_scan": H * (max(0, ns - 2) * 10 + 1) * 4 * D * D,
               "decode": DEC_N * DEC_H * DECODE_BYTES_PER_HEAD}
     share = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD}  # the method's bytes each kernel is responsible for
     share["seg_second" if "seg_second" in kms else "inter"] = tok_heads * 2 * D
@@ -598,6 +605,7 @@ def main():
     if mfma_prof and mfma_prof.get("summary"):
         mfma["rocprof"] = mfma_prof["summary"]
         mfma["mfma_util_rocprof"] = mfma_prof["summary"].get("prefill_mfma_util")
+        mfma["mfma_busy_rocprof"] = mfma_prof["summary"].get("prefill_mfma_busy")
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + %MFMA peak; decode GB/s %HBM peak",
