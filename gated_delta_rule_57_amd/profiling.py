@@ -9,14 +9,15 @@
         rocprofv3 output directories copy_FETCH_SIZE, copy_WRITE_SIZE, bench_FETCH_SIZE
         and bench_WRITE_SIZE.
     python -m gated_delta_rule_57_amd.profiling mfma <pmc_root> <trace_dir> <out.json> "<commands>"
-        MFMA use per kernel from counter runs bench_<COUNTER> under <pmc_root> (one
-        counter per run: SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32,
-        SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CU_CYCLES; any may be
-        missing) and the average kernel durations of a kernel-trace run of the same
-        command in <trace_dir>. The MOPS counters count MFMA work in units of 512
-        flops, so counted flops over the kernel's duration, against the chip's dense
-        peak for that type, is the MFMA utilisation; the busy-cycle ratio is kept
-        beside it.
+        MFMA use per kernel from counter runs bench_<RUN> under <pmc_root> (RUN one of
+        MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32,
+        SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES; any may be missing, and a run may
+        hold several counters) and the average kernel durations of a kernel-trace run
+        of the same command in <trace_dir>. The MOPS counters count MFMA work in units
+        of 512 flops, so counted flops over the kernel's duration, against the chip's
+        dense peak for that type, is the MFMA utilisation (mfma_util); rocprofv3's
+        MfmaUtil, the fraction of SIMD cycles the MFMA unit is busy, is kept beside it
+        (mfma_busy).
 
 Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode,
 outnorm, bwd_local, bwd_state, bwd_chunk; seg_plan, seg_first, seg_scan and
@@ -46,8 +47,10 @@ KERNELS = (("seg_plan_kernel", "seg_plan"), ("seg_scan_kernel", "seg_scan"), ("r
            ("bwd_state_kernel", "bwd_state"), ("bwd_chunk_kernel", "bwd_chunk"))
 COPY_BYTES = 1 << 30
 PEAK_FLOPS = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 2.5e15, "SQ_INSTS_VALU_MFMA_MOPS_F32": 157.3e12}
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
-                 "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
+# MFMA counter runs: the raw MOPS counters, and rocprofv3's derived MfmaUtil (MFMA busy
+# cycles summed over SIMDs over busy GPU cycles times the SIMD count, in percent)
+MFMA_RUNS = ("MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
+             "SQ_BUSY_CU_CYCLES")
 # kernels of the bf16 64-token prefill (any path) and the decode step
 PREFILL_PATH = ("plan", "intra", "inter", "seg_plan", "seg_first", "seg_scan", "seg_second", "single_first",
                 "single_second", "outnorm")
@@ -115,15 +118,18 @@ def summarize_trace(trace_dir, out_md, command, names=None):
     print("\n".join(lines))
 
 
-def _counter(run_dir, counter):
+def _counter(run_dir, counter=None):
+    """{kernel name: [value per dispatch]} of one counter, or with counter=None
+    {counter: {kernel name: [...]}} of every counter in the run."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
     per = {}
     for r in csv.DictReader(open(files[0])):
-        if r["Counter_Name"] != counter:
+        if counter is not None and r["Counter_Name"] != counter:
             continue
-        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        d = per if counter is not None else per.setdefault(r["Counter_Name"], {})
+        d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return per
 
 
@@ -174,14 +180,15 @@ def trace_durations(trace_dir):
 def summarize_mfma(pmc_root, trace_dir, out_json, commands):
     dur = trace_durations(trace_dir)
     kernels = {}
-    for counter in MFMA_COUNTERS:
-        run = os.path.join(pmc_root, f"bench_{counter}")
+    for run_name in MFMA_RUNS:
+        run = os.path.join(pmc_root, f"bench_{run_name}")
         if not os.path.isdir(run):
             continue
-        for name, vs in _counter(run, counter).items():
-            s = short_name(name)
-            if s is not None:
-                kernels.setdefault(s, {}).setdefault(counter, []).extend(vs)
+        for counter, by_kernel in _counter(run).items():
+            for name, vs in by_kernel.items():
+                s = short_name(name)
+                if s is not None:
+                    kernels.setdefault(s, {}).setdefault(counter, []).extend(vs)
     per = {}
     for s, cs in kernels.items():
         ent = {c: sum(v) / len(v) for c, v in cs.items()}
@@ -197,6 +204,8 @@ def summarize_mfma(pmc_root, trace_dir, out_json, commands):
             ent["mfma_util"] = util
         if "SQ_VALU_MFMA_BUSY_CYCLES" in ent and ent.get("SQ_BUSY_CU_CYCLES"):
             ent["mfma_busy_over_cu_busy"] = ent["SQ_VALU_MFMA_BUSY_CYCLES"] / ent["SQ_BUSY_CU_CYCLES"]
+        if "MfmaUtil" in ent:
+            ent["mfma_busy"] = ent["MfmaUtil"] / 100.0
         per[s] = ent
     path = [s for s in PREFILL_PATH if s in per and "avg_ns" in per[s]]
     summary = None
@@ -207,6 +216,9 @@ def summarize_mfma(pmc_root, trace_dir, out_json, commands):
         summary = {"prefill_kernels": path, "prefill_mfma_util": round(util, 4),
                    "prefill_mfma_flops_counted": flops, "prefill_kernel_ns": ns,
                    "per_kernel_mfma_util": {s: round(per[s].get("mfma_util", 0.0), 4) for s in path}}
+        if all("mfma_busy" in per[s] for s in path):
+            summary["prefill_mfma_busy"] = round(sum(per[s]["mfma_busy"] * per[s]["avg_ns"] for s in path) / ns, 4)
+            summary["per_kernel_mfma_busy"] = {s: round(per[s]["mfma_busy"], 4) for s in path}
     out = {"kernel_source_hash": kernel_source_hash(), "kernels": per, "summary": summary, "commands": commands,
            "peaks_flops": PEAK_FLOPS, "mops_unit_flops": 512}
     with open(out_json, "w") as f:

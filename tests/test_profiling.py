@@ -140,3 +140,26 @@ def test_mfma_summary(tmp_path):
     assert abs(k["mfma_util"] - 5.0e6 * 512 / 1e-3 / 2.5e15) < 1e-12
     assert abs(k["mfma_busy_over_cu_busy"] - 0.25) < 1e-12
     assert d["summary"]["prefill_kernels"] == ["intra"]
+
+
+def test_mfma_summary_reads_the_derived_busy_counter(tmp_path):
+    import json
+    root = str(tmp_path)
+    name = "_ZN3kda14rec_seg_kernelILb1EEEvNS_7SegArgsE"
+    _write_counters(os.path.join(root, "bench_MfmaUtil"), [[name, "MfmaUtil", 12.0], [name, "MfmaUtil", 14.0]])
+    _write_counters(os.path.join(root, "bench_SQ_INSTS_VALU_MFMA_MOPS_BF16"),
+                    [[name, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1.0e6], [name, "SQ_INSTS_VALU_MFMA_MOPS_F32", 1.0e5]])
+    trace = os.path.join(root, "trace")
+    os.makedirs(trace)
+    with open(os.path.join(trace, "x_kernel_stats.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"])
+        w.writerow([name, 1, 5.0e5, 5.0e5, 100.0, 5.0e5, 5.0e5])
+    out = os.path.join(root, "m.json")
+    profiling.summarize_mfma(root, trace, out, "cmd")
+    d = json.load(open(out))
+    k = d["kernels"]["seg_second"]
+    assert abs(k["mfma_busy"] - 0.13) < 1e-12
+    want = 1.0e6 * 512 / 5e-4 / 2.5e15 + 1.0e5 * 512 / 5e-4 / 157.3e12
+    assert abs(k["mfma_util"] - want) < 1e-12
+    assert d["summary"]["prefill_mfma_busy"] == 0.13
