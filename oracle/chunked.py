@@ -81,22 +81,55 @@ def forward(q, k, v, log_alpha, beta, S0=None, chunk=64, step=chunk_step):
 # into e^{g_r} * e^{-g_s}, which overflows for fast decays (the GeekNews summary,
 # section "일반 DPLR보다 줄어든 연산량", notes that fine-grained decay makes in-chunk
 # division numerically delicate; GLA handles it with log-space, full-precision
-# secondary chunking). The scheme here works in log2 units, splits the chunk into
-# sub-chunks of `sub` rows, and chooses reference points so that no factor can
-# overflow:
-#   b_0 = 0, b_I = gh[sub*I - 1]  (gh = log2-domain cumsum, b at each sub-chunk's top)
-#   plus_r  = 2^(gh_r - b_I)      (r in sub-chunk I)      in (0, 1]
-#   minus_s = 2^(b_{J+1} - gh_s)  (s in sub-chunk J)      in (0, 1]
-#   block (I, J <= I): 2^(gh_r - gh_s) = plus_r * [minus_s 2^(b_I - b_{J+1})]
-#     off the diagonal the block scale 2^(b_I - b_{J+1}) is <= 1;
-#     on the diagonal it is 2^(R_I), R_I = b_I - b_{I+1} per channel
-#   when max_c R_I > threshold for some sub-chunk, the chunk takes an exact path:
-#   every block uses plus_r * 2^(b_I - gh_s) (exponent <= 0 off the diagonal), and
-#   the diagonal blocks past the threshold fall back to 2^(gh_r - gh_s) element by
-#   element (exponent <= 0). Masked entries are discarded by selection.
-#   Q~ = q * plus * 2^(b_I);  K~ = k * plus * 2^(b_I);  K~end_s = k_s * minus_s * 2^(b_n - b_{J+1});
-#   gamma = 2^(b_n).
+# secondary chunking). The scheme here works in log2 units (x = log2 alpha), splits
+# the chunk into sub-chunks of `sub` rows, and keeps every exponent a sum of the
+# decays it spans, never the difference of two long sums, so rounding stays
+# relative to the exponent itself:
+#   loc_r = x over rows [start of r's sub-chunk, r]        (running sum, <= 0)
+#   suf_s = x over rows (s, end of s's sub-chunk]          (reverse running sum, <= 0)
+#   R_I   = x over sub-chunk I (= loc at its last row);  b_I = R_0 + ... + R_{I-1}
+#   pair r >= s, r in sub-chunk I, s in sub-chunk J:
+#     gh_r - gh_s = loc_r + E_IJ + suf_s,   E_IJ = R_{J+1} + ... + R_{I-1} (J < I),
+#                                           E_II = -R_I
+#   the operands: plus_r = 2^(loc_r), minus_s = 2^(suf_s), both in (0, 1]; the block
+#   scale 2^(E_IJ) is <= 1 off the diagonal and 2^(-R_I) on it.
+#   When -R_I > threshold for some sub-chunk its diagonal block is formed element by
+#   element with 2^(gh_r - gh_s) (exponent <= 0), the exponent taken as
+#   loc_r - loc_s or suf_s - suf_r, whichever subtracts the smaller sum (the decay
+#   before s or after r inside the sub-chunk).
+#   Q~ = q * 2^(b_I + loc);  K~ = k * 2^(b_I + loc);
+#   K~end_s = k_s * minus_s * 2^(R_{J+1} + ... + R_{n-1});  gamma = 2^(b_n).
 # ---------------------------------------------------------------------------
+
+def _local_sums(x, sub, dtype):
+    """Running sums of x inside each sub-chunk, forward (loc) and backward (suf),
+    and the sub-chunk totals R, all accumulated row by row in ``dtype``."""
+    C, dk = x.shape
+    n_sub = (C + sub - 1) // sub
+    loc = np.zeros((C, dk), dtype=dtype)
+    suf = np.zeros((C, dk), dtype=dtype)
+    R = np.zeros((n_sub, dk), dtype=dtype)
+    for I in range(n_sub):
+        rows = range(sub * I, min(C, sub * (I + 1)))
+        acc = np.zeros(dk, dtype=dtype)
+        for r in rows:
+            acc = (acc + x[r]).astype(dtype)
+            loc[r] = acc
+        R[I] = acc
+        acc = np.zeros(dk, dtype=dtype)
+        for s in reversed(rows):
+            suf[s] = acc
+            acc = (acc + x[s]).astype(dtype)
+    return loc, suf, R
+
+
+def _span(R, lo, hi, dtype):
+    """R_lo + ... + R_{hi-1} (zero when empty), accumulated in ``dtype``."""
+    acc = np.zeros(R.shape[1], dtype=dtype)
+    for K in range(lo, hi):
+        acc = (acc + R[K]).astype(dtype)
+    return acc
+
 
 def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.float64):
     """Forms A, P, Q~, K~, K~end, gamma of one chunk with the factored scheme, in
@@ -104,25 +137,20 @@ def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.f
     diagonal sub-blocks that took the element-wise path)."""
     C, dk = q.shape
     n_sub = (C + sub - 1) // sub
-    la2 = (np.asarray(log_alpha, dtype=np.float64) * LOG2E).astype(dtype)
-    gh = np.cumsum(la2, axis=0, dtype=dtype)
+    x = (np.asarray(log_alpha, dtype=np.float64) * LOG2E).astype(dtype)
+    loc, suf, R = _local_sums(x, sub, dtype)
     b = np.zeros((n_sub + 1, dk), dtype=dtype)
-    for I in range(1, n_sub + 1):
-        b[I] = gh[min(sub * I, C) - 1]
+    for I in range(n_sub):
+        b[I + 1] = (b[I] + R[I]).astype(dtype)
     q = np.asarray(q, dtype=dtype)
     k = np.asarray(k, dtype=dtype)
     beta = np.asarray(beta, dtype=dtype)
-    plus = np.zeros((C, dk), dtype=dtype)
-    minus = np.zeros((C, dk), dtype=dtype)
-    for r in range(C):
-        I = r // sub
-        plus[r] = np.exp2(gh[r] - b[I])
-        minus[r] = np.exp2(b[I + 1] - gh[r])
+    plus = np.exp2(loc)
+    minus = np.exp2(suf)
     A = np.zeros((C, C), dtype=dtype)
     P = np.zeros((C, C), dtype=dtype)
     fallback = []
-    over = [I for I in range(n_sub) if np.max(b[I] - b[I + 1]) > threshold]
-    exact = len(over) > 0
+    over = [I for I in range(n_sub) if np.max(-R[I]) > threshold]
     with np.errstate(over="raise", invalid="raise"):
         for I in range(n_sub):
             rI = slice(sub * I, min(C, sub * (I + 1)))
@@ -130,42 +158,36 @@ def factored_operands(q, k, log_alpha, beta, sub=16, threshold=120.0, dtype=np.f
             lhs_q = q[rI] * plus[rI]
             for J in range(I + 1):
                 sJ = slice(sub * J, min(C, sub * (J + 1)))
-                if J < I:
-                    if exact:
-                        rhs = k[sJ] * np.exp2(b[I][None, :] - gh[sJ])
-                    else:
-                        rhs = k[sJ] * minus[sJ] * np.exp2(b[I] - b[J + 1])
-                    A[rI, sJ] = lhs_k @ rhs.T
-                    P[rI, sJ] = lhs_q @ rhs.T
+                if J < I or I not in over:
+                    scale = np.exp2(_span(R, J + 1, I, dtype) if J < I else -R[I])
+                    rhs = k[sJ] * minus[sJ] * scale
+                    blkA = lhs_k @ rhs.T
+                    blkP = lhs_q @ rhs.T
                 else:
-                    if I not in over:
-                        if exact:
-                            rhs = k[sJ] * np.exp2(b[I][None, :] - gh[sJ])
-                        else:
-                            rhs = k[sJ] * minus[sJ] * np.exp2(b[I] - b[I + 1])
-                        blkA = lhs_k @ rhs.T
-                        blkP = lhs_q @ rhs.T
-                    else:
-                        fallback.append(I)
-                        rows = range(rI.start, rI.stop)
-                        cols = range(sJ.start, sJ.stop)
-                        blkA = np.zeros((len(rows), len(cols)), dtype=dtype)
-                        blkP = np.zeros_like(blkA)
-                        for a, r in enumerate(rows):
-                            for c, s in enumerate(cols):
-                                if s <= r:
-                                    e = np.exp2(gh[r] - gh[s])
-                                    blkA[a, c] = np.sum(k[r] * k[s] * e)
-                                    blkP[a, c] = np.sum(q[r] * k[s] * e)
+                    fallback.append(I)
+                    rows = range(rI.start, rI.stop)
+                    blkA = np.zeros((len(rows), len(rows)), dtype=dtype)
+                    blkP = np.zeros_like(blkA)
+                    for a, r in enumerate(rows):
+                        for c, s in enumerate(rows):
+                            if s <= r:
+                                near = np.abs(loc[s]) <= np.abs(suf[r])
+                                e = np.exp2(np.where(near, loc[r] - loc[s], suf[s] - suf[r]))
+                                blkA[a, c] = np.sum(k[r] * k[s] * e)
+                                blkP[a, c] = np.sum(q[r] * k[s] * e)
+                if J == I:
                     n = blkA.shape[0]
-                    A[rI, sJ] = np.where(np.tril(np.ones((n, n), bool), -1), blkA, 0)
-                    P[rI, sJ] = np.where(np.tril(np.ones((n, n), bool), 0), blkP, 0)
+                    blkA = np.where(np.tril(np.ones((n, n), bool), -1), blkA, 0)
+                    blkP = np.where(np.tril(np.ones((n, n), bool), 0), blkP, 0)
+                A[rI, sJ] = blkA
+                P[rI, sJ] = blkP
         A = beta[:, None] * A
         blk_of = np.arange(C) // sub
-        top = b[blk_of]
-        Qt = q * plus * np.exp2(top)
-        Kt = k * plus * np.exp2(top)
-        Kend = k * minus * np.exp2(b[n_sub][None, :] - b[blk_of + 1])
+        eg = np.exp2(b[blk_of] + loc)
+        Qt = q * eg
+        Kt = k * eg
+        tail = np.stack([_span(R, J + 1, n_sub, dtype) for J in range(n_sub)])
+        Kend = k * minus * np.exp2(tail[blk_of])
         gamma = np.exp2(b[n_sub])
     return dict(A=A, P=P, Qt=Qt, Kt=Kt, Kend=Kend, gamma=gamma, fallback=fallback)
 

@@ -101,3 +101,58 @@ def test_factored_operands_stay_finite_in_float32():
             assert np.all(np.isfinite(ops[name])), (la_case, name)
             scale = max(1.0, np.abs(ref[name]).max())
             np.testing.assert_allclose(ops[name], ref[name], rtol=0, atol=2e-4 * scale, err_msg=f"{la_case} {name}")
+
+
+def _direct_operands(q, k, la, beta):
+    """A, P and the decay-scaled operands of one chunk straight from their
+    definition in fp64, each pair's exponent summed over the rows it spans."""
+    C = q.shape[0]
+    x = la * chunked.LOG2E
+    A = np.zeros((C, C))
+    P = np.zeros((C, C))
+    for r in range(C):
+        for s in range(r + 1):
+            e = np.exp2(x[s + 1:r + 1].sum(axis=0))
+            P[r, s] = np.sum(q[r] * k[s] * e)
+            if s < r:
+                A[r, s] = beta[r] * np.sum(k[r] * k[s] * e)
+    g = np.cumsum(x, axis=0)
+    tail = np.stack([x[s + 1:].sum(axis=0) for s in range(C)])
+    return dict(A=A, P=P, Qt=q * np.exp2(g), Kt=k * np.exp2(g), Kend=k * np.exp2(tail), gamma=np.exp2(g[-1]))
+
+
+@pytest.mark.parametrize("case", ["fast12", "fast6", "two_sided", "near_limit", "mixed"])
+def test_factored_operands_float32_accuracy(case):
+    """In float32 the factored scheme keeps A, P and the scaled operands within 1e-5
+    (normwise) of their fp64 definition, also where long runs of fast decays sit
+    beside slow ones inside one sub-chunk: every exponent is a running sum of the
+    decays it spans, not a difference of two long sums."""
+    rng = np.random.default_rng(24)
+    C, dk = 64, 128
+    q = rng.standard_normal((C, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((C, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    la = -0.1 * np.log1p(np.exp(rng.standard_normal((C, dk))))
+    if case == "fast12":
+        la[20:32] = -200.0          # 12 tokens, every channel, then slow rows in the same sub-chunk
+    elif case == "fast6":
+        la[0:6] = -1000.0
+    elif case == "two_sided":
+        la[16] = -200.0             # fast rows at both ends of one sub-chunk
+        la[31] = -200.0
+    elif case == "near_limit":
+        la -= 4.5                   # sub-chunk totals just inside the factoring range
+    else:
+        la = -np.log1p(np.exp(rng.standard_normal((C, dk))))
+        la[:, rng.permutation(dk)[:64]] = -1e-3
+    beta = 1 / (1 + np.exp(-rng.standard_normal(C)))
+    with np.errstate(under="ignore"):
+        ops = chunked.factored_operands(q, k, la, beta, dtype=np.float32)
+        ref = _direct_operands(q, k, la, beta)
+    assert bool(ops["fallback"]) == (case in ("fast12", "fast6", "two_sided"))
+    for name in ("A", "P", "Qt", "Kt", "Kend", "gamma"):
+        # values below float32's smallest normal number are out of its range: zero
+        want = np.where(np.abs(ref[name]) < np.finfo(np.float32).tiny, 0.0, ref[name])
+        nref = np.linalg.norm(want)
+        err = np.linalg.norm(np.where(np.abs(want) > 0, ops[name], 0.0) - want) / (nref if nref > 0 else 1.0)
+        assert err <= 1e-5, (case, name, err)
+        assert np.all(np.abs(ops[name][want == 0]) <= np.finfo(np.float32).tiny), (case, name)
