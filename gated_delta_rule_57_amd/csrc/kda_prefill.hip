@@ -34,20 +34,24 @@
 //                 ahead; inter_kernel (fp32, 64-token chunks) uses one wave.
 //
 // In-chunk decay (the pages note that fine-grained decay makes the in-chunk
-// division numerically delicate): everything is done in log2 units, and the
-// chunk's rows are grouped in sub-chunks of 16 with reference points at the
-// sub-chunk boundaries, b_0 = 0 and b_I = gh[16 I - 1]. For an A / P block (I, J),
-// r in sub-chunk I and s in sub-chunk J <= I:
-//   2^(gh_r - gh_s) = 2^(gh_r - b_I) * 2^(b_I - b_{J+1}) * 2^(b_{J+1} - gh_s)
-// The first and last factors have exponents <= 0 and belong to one row each, so
-// they are applied once per row (lhs_r = x_r 2^(gh_r - b_I), x = k for A, q for P;
-// rhs_s = k_s 2^(b_{J+1} - gh_s)); the middle one is a per-channel scale of the
-// block, <= 1 off the diagonal and 2^(R_I) on it, R_I = b_I - b_{I+1}. When max
-// over channels of R_I exceeds 120 for some sub-chunk, the chunk instead takes an
-// exact path: off-diagonal blocks with rhs_s = k_s 2^(b_I - gh_s) built per block,
-// and that diagonal block summed on the VALU with 2^(gh_r - gh_s) per element,
-// so no factor can overflow for any input. Q e^G, K e^G, K e^{g_C-G} and e^{g_C}
-// only need exponents <= 0 and are taken directly.
+// division numerically delicate): everything is done in log2 units (x = log2 alpha)
+// and the chunk's rows are grouped in sub-chunks of 16. Every exponent is kept a
+// sum of the decays it spans, never the difference of two long cumulative sums, so
+// fp32 rounding stays relative to the exponent itself:
+//   loc_r = x over rows [first row of r's sub-chunk, r]    (running sum, <= 0)
+//   suf_s = x over rows (s, last row of s's sub-chunk]     (reverse running sum, <= 0)
+//   R_I   = x over sub-chunk I;  b_I = R_0 + ... + R_{I-1}
+// For an A / P block (I, J), r in sub-chunk I and s in sub-chunk J <= I:
+//   gh_r - gh_s = loc_r + E_IJ + suf_s,  E_IJ = R_{J+1} + ... + R_{I-1}, E_II = -R_I
+// The first and last terms belong to one row each, so they are applied once per row
+// (lhs_r = x_r 2^(loc_r), x = k for A, q for P; rhs_s = k_s 2^(suf_s)); 2^(E_IJ) is a
+// per-channel scale of the block, <= 1 off the diagonal and 2^(-R_I) on it. When
+// -R_I exceeds 120 for some sub-chunk, the chunk instead takes an exact path whose
+// operands are built per block from the raw inputs, and that diagonal block is
+// summed on the VALU with 2^(gh_r - gh_s) per element, the exponent taken as
+// loc_r - loc_s or suf_s - suf_r, whichever subtracts the smaller sum; no factor can
+// overflow for any input. Q e^G, K e^G (exponent b_I + loc_r), K e^{g_C-G}
+// (suf_s + E_{J,n}) and e^{g_C} only need exponents <= 0 and are taken directly.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -83,19 +87,22 @@ struct Smem {
   static constexpr int GLD = D + 4;            // row stride of the fp32 decay cumsum
   static constexpr int LDC = C + 4;            // row stride of the fp32 A matrix
   static constexpr int LDK = CK + 8;           // row stride of E matrices indexed by chunk row
-  // phase A, exact path: log2-decay cumsum, raw k and q
+  // phase A: per-channel decays. G holds the log2 decays, then their running sums
+  // inside each sub-chunk (loc); SUF the reverse running sums (suf). Scalar gates
+  // keep their row sums at G and raw k and q at K and Q.
   static constexpr size_t G = 0;                                          // float[C][GLD]
   static constexpr size_t K = G + al16((size_t)C * GLD * 4);              // E[C][LD]
   static constexpr size_t Q = K + al16((size_t)C * LD * sizeof(E));       // E[C][LD]
   static constexpr size_t A_END = Q + al16((size_t)C * LD * sizeof(E));
-  // phase A, factored path: the cumsum (at G) is replaced by the per-row factored
-  // operands once every thread holds its own decays in registers; RR does not
-  // overlap G, so it is written before that hand-over
-  static constexpr size_t LK = 0;                                         // E[C][LD]     k_r 2^(gh_r - b_I)
-  static constexpr size_t LQ = LK + al16((size_t)C * LD * sizeof(E));     // E[C][LD]     q_r 2^(gh_r - b_I)
-  static constexpr size_t RR = LQ + al16((size_t)C * LD * sizeof(E));     // float[C][GLD] k_s 2^(b_{J+1} - gh_s)
+  // phase A, factored path: loc (at G) is replaced by the per-row factored operands
+  // once every thread holds its own decays in registers; suf sits where the right
+  // operands go (RR) and each thread replaces its own entries
+  static constexpr size_t LK = 0;                                         // E[C][LD]     k_r 2^(loc_r)
+  static constexpr size_t LQ = LK + al16((size_t)C * LD * sizeof(E));     // E[C][LD]     q_r 2^(loc_r)
+  static constexpr size_t RR = LQ + al16((size_t)C * LD * sizeof(E));     // float[C][GLD] k_s 2^(suf_s)
+  static constexpr size_t SUF = RR;                                       // float[C][GLD] suf
   static constexpr size_t F_END = RR + al16((size_t)C * GLD * 4);
-  static_assert(G + (size_t)C * GLD * 4 <= RR, "the factored rhs must not overlap the cumsum");
+  static_assert(G + (size_t)C * GLD * 4 <= RR, "the suffix sums must not overlap the prefix sums");
   // phase B: A, diagonal blocks of T, T diag(beta), K e^G, V
   static constexpr size_t MA = 0;                                         // float[C][LDC]
   static constexpr size_t TD = MA + al16((size_t)C * LDC * 4);            // float[NSUB][16][20]
@@ -111,7 +118,8 @@ struct Smem {
   static constexpr int NSCALE = NBLK + NSUB;
   static constexpr size_t SCL = BND + (size_t)(NSUB + 1) * D * 4;  // float[NSCALE][D]
   static constexpr size_t BETA = SCL + (size_t)NSCALE * D * 4;     // float[CK]
-  static constexpr size_t FLAG = BETA + (size_t)CK * 4;           // int[NSUB]
+  static constexpr size_t NRM = BETA + (size_t)CK * 4;            // float[2][CK] prologue scales of k, q
+  static constexpr size_t FLAG = NRM + (size_t)2 * CK * 4;        // int[NSUB]
   static constexpr size_t TOTAL = al16(FLAG + 4 * NSUB);
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
@@ -246,6 +254,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   float* sBnd = reinterpret_cast<float*>(smem + SM::BND);
   float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
   int* sFlag = reinterpret_cast<int*>(smem + SM::FLAG);
+  float* sNrm = reinterpret_cast<float*>(smem + SM::NRM);
 
   // heads vary fastest over the work-group ids: the work-groups in flight together
   // cover whole token rows of q, k, v and the gates, not one head's 256-byte pieces
@@ -306,6 +315,16 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
         kr[i][j] *= ik;
         qr[i][j] *= iq;
       }
+      if (GATE == GATE_CHANNEL && cq == 0) {  // the row's scales, for the exact path's reloads of raw k and q
+        sNrm[rbase + 8 * i] = ik;
+        sNrm[CK + rbase + 8 * i] = iq;
+      }
+    }
+  } else if (GATE == GATE_CHANNEL && cq == 0) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      sNrm[rbase + 8 * i] = 1.f;
+      sNrm[CK + rbase + 8 * i] = 1.f;
     }
   }
 #pragma unroll
@@ -371,45 +390,69 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     *reinterpret_cast<floatx4*>(sG + r * GLD + ch0) = l2;
   }
   __syncthreads();
-  {  // ---- P1b: cumulative sum over the rows per channel: two halves, then a carry
+  float* sSuf = reinterpret_cast<float*>(smem + SM::SUF);
+  {  // ---- P1b: per channel and sub-chunk, running sums of the log2 decays from the
+     //      sub-chunk's first row (loc, over the decays at sG) and to its last row
+     //      (suf, to sSuf); the two halves of the work-group take half the sub-chunks
     const int chn = t & 127, half = t >> 7;
-    constexpr int HR = C / 2;
-    float vals[HR];
+    constexpr int SPH = NSUB >= 2 ? NSUB / 2 : 1;
+    if (NSUB >= 2 || half == 0) {
 #pragma unroll
-    for (int r = 0; r < HR; ++r) vals[r] = sG[(half * HR + r) * GLD + chn];
+      for (int u = 0; u < SPH; ++u) {
+        const int r0 = 16 * (half * SPH + u);
+        float x[16];
 #pragma unroll
-    for (int r = 1; r < HR; ++r) vals[r] += vals[r - 1];
-    if (half == 0) {
+        for (int j = 0; j < 16; ++j) x[j] = sG[(r0 + j) * GLD + chn];
+        float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < HR; ++r) sG[r * GLD + chn] = vals[r];
-    }
-    __syncthreads();
-    if (half == 1) {
-      const float carry = sG[(HR - 1) * GLD + chn];
+        for (int j = 0; j < 16; ++j) {
+          acc += x[j];
+          sG[(r0 + j) * GLD + chn] = acc;
+        }
+        acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < HR; ++r) sG[(HR + r) * GLD + chn] = vals[r] + carry;
+        for (int j = 15; j >= 0; --j) {
+          sSuf[(r0 + j) * GLD + chn] = acc;
+          acc += x[j];
+        }
+      }
     }
   }
   __syncthreads();
   float* sScl = reinterpret_cast<float*>(smem + SM::SCL);
   if (t < D) {
-    float bnd[NSUB + 1];
+    float R[NSUB], bnd[NSUB + 1];
     bnd[0] = 0.f;
 #pragma unroll
-    for (int I = 1; I <= NSUB; ++I) bnd[I] = sG[(16 * I - 1) * GLD + t];
+    for (int I = 0; I < NSUB; ++I) {
+      R[I] = sG[(16 * I + 15) * GLD + t];
+      bnd[I + 1] = bnd[I] + R[I];
+    }
 #pragma unroll
     for (int I = 0; I <= NSUB; ++I) sBnd[I * D + t] = bnd[I];
     rec_gamma[t] = fast_exp2(bnd[NSUB]);
 #pragma unroll
     for (int I = 0; I < NSUB; ++I)
-      if (!(bnd[I] - bnd[I + 1] <= DIAG_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
-    // block scales: <= 1 off the diagonal, 2^(R_I) on it (used only while R_I <= the limit)
+      if (!(-R[I] <= DIAG_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
+    // block scales 2^(E_IJ): sums of the whole sub-chunks strictly between J and I
+    // (<= 1), 2^(-R_I) on the diagonal (used only while -R_I <= the limit); then
+    // 2^(R_{J+1} + ... + R_{n-1}) for the chunk end
 #pragma unroll
-    for (int I = 0; I < NSUB; ++I)
+    for (int I = 0; I < NSUB; ++I) {
+      float e = 0.f;
 #pragma unroll
-      for (int J = 0; J <= I; ++J) sScl[(I * (I + 1) / 2 + J) * D + t] = fast_exp2(bnd[I] - bnd[J + 1]);
+      for (int J = I - 1; J >= 0; --J) {
+        sScl[(I * (I + 1) / 2 + J) * D + t] = fast_exp2(e);
+        e += R[J];
+      }
+      sScl[(I * (I + 1) / 2 + I) * D + t] = fast_exp2(-R[I]);
+    }
+    float e = 0.f;
 #pragma unroll
-    for (int J = 0; J < NSUB; ++J) sScl[(SM::NBLK + J) * D + t] = fast_exp2(bnd[NSUB] - bnd[J + 1]);
+    for (int J = NSUB - 1; J >= 0; --J) {
+      sScl[(SM::NBLK + J) * D + t] = fast_exp2(e);
+      e += R[J];
+    }
   }
   __syncthreads();
   bool exact = false;  // some diagonal block exceeds the range limit: per-element path
@@ -419,10 +462,11 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   if (!exact) {
     // ---- P2 (factored path): Q e^G to the record, K e^G kept for B0, and per row
     //      the operands of every A / P block:
-    //        lhs_r = x_r 2^(gh_r - b_I)        (x = k or q; I = r's sub-chunk)
-    //        rhs_s = k_s 2^(b_{J+1} - gh_s)    (J = s's sub-chunk)
-    //      both with exponents <= 0. Block (I, J) is lhs_I diag(2^(b_I - b_{J+1})) rhs_J^T,
-    //      the per-channel scale taken from the table above.
+    //        lhs_r = x_r 2^(loc_r)    (x = k or q)
+    //        rhs_s = k_s 2^(suf_s)
+    //      both with exponents <= 0. Block (I, J) is lhs_I diag(2^(E_IJ)) rhs_J^T,
+    //      the per-channel scale taken from the table above. rhs_s replaces suf_s in
+    //      place (each thread its own entries).
     E* sLK = reinterpret_cast<E*>(smem + SM::LK);
     E* sLQ = reinterpret_cast<E*>(smem + SM::LQ);
     float* sRR = reinterpret_cast<float*>(smem + SM::RR);
@@ -430,21 +474,21 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rbase + 8 * i, I = r >> 4;
-      const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const floatx4 loc = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const floatx4 suf = *reinterpret_cast<const floatx4*>(sSuf + r * GLD + ch0);
       const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
-      const floatx4 b1 = *reinterpret_cast<const floatx4*>(sBnd + (I + 1) * D + ch0);
       float qt[4];
       floatx4 rr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float kk = kr[i][j], qq = qr[i][j];
-        const float eg = fast_exp2(gr[j]);          // exponent <= 0
-        const float pl = fast_exp2(gr[j] - b0[j]);  // exponent <= 0
+        const float eg = fast_exp2(b0[j] + loc[j]);  // exponent <= 0
+        const float pl = fast_exp2(loc[j]);          // exponent <= 0
         qt[j] = qq * eg;
         ktr[i][j] = kk * eg;
         lkv[i][j] = from_f<E>(kk * pl);
         lqv[i][j] = from_f<E>(qq * pl);
-        rr[j] = kk * fast_exp2(b1[j] - gr[j]);     // exponent <= 0
+        rr[j] = kk * fast_exp2(suf[j]);             // exponent <= 0
       }
       *reinterpret_cast<floatx4*>(sRR + r * GLD + ch0) = rr;
       const int kb = ch0 >> 5, co = ch0 & 31;
@@ -496,30 +540,42 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     emit_ke([&](int s, int ch) { return sRR[s * GLD + ch] * sScl[(NBLK + (s >> 4)) * D + ch]; });
   } else {
     // ---- P2 (exact path): Q e^G straight to its fragment slot (4 consecutive channels are half of a
-    //          lane's fragment); K e^G kept for B0; raw q, k to LDS ----------------------
+    //          lane's fragment); K e^G kept for B0. loc and suf stay in LDS for P3,
+    //          which takes raw q and k from global memory (the rows just loaded) --------
   #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rbase + 8 * i;
-      const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const int r = rbase + 8 * i, I = r >> 4;
+      const floatx4 loc = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
       float qt[4];
   #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float eg = fast_exp2(gr[j]);  // exponent <= 0
+        const float eg = fast_exp2(b0[j] + loc[j]);  // exponent <= 0
         qt[j] = qr[i][j] * eg;
         ktr[i][j] = kr[i][j] * eg;
       }
-      store4f(sK + r * LD + ch0, kr[i]);
-      store4f(sQ + r * LD + ch0, qr[i]);
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
       store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
-    __syncthreads();
+    // raw (prologue-scaled) k (which 0) or q (which 1) of chunk row r, channels ch .. ch + 3;
+    // zero past len
+    auto raw4 = [&](int which, int r, int ch, float out[4]) {
+      if (r < len) {
+        load4f((which ? q : k) + (size_t)(tok0 + r) * HD + (size_t)h * D + ch, out);
+        const float f = sNrm[which * CK + r];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] *= f;
+      } else {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = 0.f;
+      }
+    };
 
     // ---- P3: A and P, one 16 x 16 block (I, J <= I) per wave at a time. Computed
     //          transposed: lane (m, g), element ii holds entry (r = 16 I + m,
-    //          s = 16 J + 4 g + ii). lhs_r = x_r 2^(gh_r - b_I) (x = k or q),
-    //          rhs_s = k_s 2^(b_I - gh_s). -----------------------------------------------
+    //          s = 16 J + 4 g + ii). lhs_r = x_r 2^(loc_r) (x = k or q),
+    //          rhs_s = k_s 2^(suf_s) 2^(E_IJ). -------------------------------------------
   #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -527,24 +583,41 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       int I, J;
       if (!wave_block<NSUB>(w, bi, I, J)) break;
       if (J == I && sFlag[I]) {
-        // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry
+        // element-wise path: 2^(gh_r - gh_s) with exponent <= 0 for every kept entry,
+        // as loc_r - loc_s or suf_s - suf_r, whichever subtracts the smaller sum
         const int r = 16 * I + m;
+        float sa[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < D; ch += 4) {
+          float kk[4], qq[4];
+          raw4(0, r, ch, kk);
+          raw4(1, r, ch, qq);
+          const floatx4 lr = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch);
+          const floatx4 fr = *reinterpret_cast<const floatx4*>(sSuf + r * GLD + ch);
   #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int s = 16 * J + 4 * g + ii;
-          float sa = 0.f, sp = 0.f;
-          if (s <= r) {
-            for (int ch = 0; ch < D; ++ch) {
-              const float ks = to_f(sK[s * LD + ch]) * fast_exp2(sG[r * GLD + ch] - sG[s * GLD + ch]);
-              sa += to_f(sK[r * LD + ch]) * ks;
-              sp += to_f(sQ[r * LD + ch]) * ks;
+          for (int ii = 0; ii < 4; ++ii) {
+            const int s = 16 * J + 4 * g + ii;
+            if (s > r) continue;
+            float ks[4];
+            raw4(0, s, ch, ks);
+            const floatx4 ls = *reinterpret_cast<const floatx4*>(sG + s * GLD + ch);
+            const floatx4 fs = *reinterpret_cast<const floatx4*>(sSuf + s * GLD + ch);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float ex = fabsf(ls[j]) <= fabsf(fr[j]) ? lr[j] - ls[j] : fs[j] - fr[j];
+              const float kd = ks[j] * fast_exp2(ex);
+              sa[ii] += kk[j] * kd;
+              sp[ii] += qq[j] * kd;
             }
           }
-          accA[bi][ii] = sa;
-          accP[bi][ii] = sp;
+        }
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          accA[bi][ii] = sa[ii];
+          accP[bi][ii] = sp[ii];
         }
       } else {
         const int rrow = 16 * I + m, srow = 16 * J + m;
+        const float* scl = sScl + (size_t)(I * (I + 1) / 2 + J) * D;
   #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           FragT lk, lq, rhs;
@@ -552,18 +625,18 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
           for (int hh = 0; hh < 2; ++hh) {
             const int ch = 32 * kb + 16 * hh + 4 * g;
             float kk[4], qq[4], ks[4];
-            load4f(sK + rrow * LD + ch, kk);
-            load4f(sQ + rrow * LD + ch, qq);
-            load4f(sK + srow * LD + ch, ks);
-            const floatx4 gr = *reinterpret_cast<const floatx4*>(sG + rrow * GLD + ch);
-            const floatx4 gs = *reinterpret_cast<const floatx4*>(sG + srow * GLD + ch);
-            const floatx4 bI = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch);
+            raw4(0, rrow, ch, kk);
+            raw4(1, rrow, ch, qq);
+            raw4(0, srow, ch, ks);
+            const floatx4 lr = *reinterpret_cast<const floatx4*>(sG + rrow * GLD + ch);
+            const floatx4 fs = *reinterpret_cast<const floatx4*>(sSuf + srow * GLD + ch);
+            const floatx4 sc = *reinterpret_cast<const floatx4*>(scl + ch);
   #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float pl = fast_exp2(gr[j] - bI[j]);
+              const float pl = fast_exp2(lr[j]);
               lk[4 * hh + j] = from_f<E>(kk[j] * pl);
               lq[4 * hh + j] = from_f<E>(qq[j] * pl);
-              rhs[4 * hh + j] = from_f<E>(ks[j] * fast_exp2(bI[j] - gs[j]));
+              rhs[4 * hh + j] = from_f<E>(ks[j] * fast_exp2(fs[j]) * sc[j]);
             }
           }
           mma(accA[bi], rhs, lk);
@@ -572,24 +645,34 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       emit_p(I, J, accP[bi]);
     }
-    // (K e^{g_C - G})^T to the record
-    emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * fast_exp2(sBnd[NSUB * D + ch] - sG[s * GLD + ch]); });
+    // (K e^{g_C - G})^T to the record: k_s 2^(suf_s) 2^(R_{J+1} + ... + R_{n-1})
+    emit_ke([&](int s, int ch) {
+      const float ks = s < len ? to_f(k[(size_t)(tok0 + s) * HD + (size_t)h * D + ch]) * sNrm[s] : 0.f;
+      return ks * fast_exp2(sSuf[s * GLD + ch]) * sScl[(NBLK + (s >> 4)) * D + ch];
+    });
   }
   } else {
     // ---- scalar gate: one decay per (token, head) (GATE_HEAD), or none (GATE_NONE).
     //      The decay of a row pair is the scalar 2^(gh_r - gh_s), exponent <= 0 for
     //      s <= r, so the raw products k k^T and q k^T are scaled per element after
     //      the MFMA and no factoring or fallback is needed ------------------------
-    float* sGs = sG;  // float[CK]: log2-domain cumsum of the row decays
-    if (w == 0) {     // one wave holds every row (CK <= 64)
+    float* sGs = sG;        // float[CK]: running sums of the row decays (log2) from row 0
+    float* sGf = sG + 64;   // float[CK]: running sums over the rows after s to the chunk end
+    if (w == 0) {           // one wave holds every row (CK <= 64)
       float x = 0.f;
       if constexpr (GATE == GATE_HEAD) x = la_row * LOG2E_F;  // zero past len
+      float f = __shfl_down(x, 1, 64);
+      if (lane == 63) f = 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
+        const float y = __shfl_up(x, off, 64), z = __shfl_down(f, off, 64);
         if (lane >= off) x += y;
+        if (lane + off < 64) f += z;
       }
-      if (lane < CK) sGs[lane] = x;
+      if (lane < CK) {
+        sGs[lane] = x;
+        sGf[lane] = f;
+      }
     }
     __syncthreads();
     const float gC = sGs[C - 1];
@@ -643,14 +726,16 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int s = 16 * J + 4 * g + ii;
-        const float f = s <= r ? (GATE == GATE_NONE ? 1.f : fast_exp2(sGs[r] - sGs[s])) : 0.f;
+        // 2^(gh_r - gh_s) from whichever running sums subtract the smaller total
+        const float ex = fabsf(sGs[s]) <= fabsf(sGf[r]) ? sGs[r] - sGs[s] : sGf[s] - sGf[r];
+        const float f = s <= r ? (GATE == GATE_NONE ? 1.f : fast_exp2(ex)) : 0.f;
         accA[bi][ii] *= f;
         accP[bi][ii] *= f;
       }
       emit_p(I, J, accP[bi]);
     }
     // (K e^{g_C - G})^T to the record
-    emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(gC - sGs[s])); });
+    emit_ke([&](int s, int ch) { return to_f(sK[s * LD + ch]) * (GATE == GATE_NONE ? 1.f : fast_exp2(sGf[s])); });
   }
   __syncthreads();  // phase A buffers are dead from here on
 

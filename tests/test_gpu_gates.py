@@ -57,6 +57,25 @@ def test_varlen(gate):
     compare(inp, "varlen")
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_fp32_scalar_fast_decay_runs(chunk):
+    """fp32 scalar gate: runs of -200 beside slow rows inside one chunk; the pair
+    decay takes its exponent from whichever running sum subtracts the smaller
+    total, so the fp32 result stays well inside its gate."""
+    inp = inputs.make_prefill(33, B=1, T=192, H=2, dtype="fp32", la_scale=0.1, s0_std=0.3, gate="head")
+    inp.log_alpha[:, 2:8] = -200.0
+    inp.log_alpha[:, 90:93, 1] = -200.0
+    inp.log_alpha[:, 150] = -200.0
+    o, fin = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.log_alpha, inp.beta, initial_state=inp.initial_state, chunk=chunk)
+    torch.cuda.synchronize()
+    x = inp.numpy()
+    o_ref, f_ref = oracle.forward(x["q"], x["k"], x["v"], channel_log_alpha(x, x["log_alpha"]), x["beta"],
+                                  x["initial_state"].astype(np.float64))
+    eo, ef = normwise(o.float().cpu().numpy(), o_ref), normwise(fin.cpu().numpy(), f_ref)
+    say(f"[gates] fp32 scalar fast runs c{chunk}: err_o={eo:.3e} err_state={ef:.3e}")
+    assert eo <= 1e-5 and ef <= 1e-5
+
+
 def test_strong_scalar_decay_stays_finite():
     """Decays of ~20 nats per token: the pair factor 2^(gh_r - gh_s) underflows to 0
     for distant rows, never overflows."""

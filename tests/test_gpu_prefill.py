@@ -93,6 +93,30 @@ def test_adversarial_decay_takes_fallback(dtype):
     compare_prefill(inp, label=f"adversarial-{dtype}")
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("case", ["fast12", "fast6", "two_sided"])
+def test_fp32_fast_decay_runs(case, chunk):
+    """fp32, every key channel: 12 tokens of -200 or 6 of -1000 next to slow rows of
+    the same sub-chunk, and -200 rows at both ends of one sub-chunk. Every in-chunk
+    exponent is a running sum of the decays it spans, so pairs of slow rows next to
+    a fast run keep full fp32 accuracy: well inside the 1e-4 gate."""
+    inp = small(19, T=192, H=2, dtype="fp32", chunk=chunk, la_scale=0.1)
+    la = inp.log_alpha
+    if case == "fast12":
+        la[:, 20:32] = -200.0
+        la[:, 130:142, 1] = -200.0
+    elif case == "fast6":
+        la[:, 0:6] = -1000.0
+        la[:, 100:106, 0] = -1000.0
+    else:
+        la[:, 16] = -200.0
+        la[:, 31] = -200.0
+        la[:, 144, 1] = -200.0
+        la[:, 159, 1] = -200.0
+    eo, ef = compare_prefill(inp, label=f"fp32-{case}-c{chunk}")
+    assert eo <= 1e-5 and ef <= 1e-5, (eo, ef)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_chunk_size_does_not_change_result(dtype):
     inp = small(16, T=300, H=2, dtype=dtype, chunk=64)
