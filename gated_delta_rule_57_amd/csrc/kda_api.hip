@@ -207,10 +207,18 @@ size_t kda_chunk_fwd_fused_workspace_size(int B, int T, int H, int num_seqs, int
 }
 
 
-int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                        const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
-                        float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
-                        const kda_fusion* fusion, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The prefill behind kda_chunk_fwd, kda_chunk_fwd_fused and kda_chunk_fwd_noalloc.
+// With `scratch` set (and workspace NULL) the kernels use that buffer of
+// `scratch_bytes` and nothing is allocated; a configuration that needs more returns
+// KDA_ERR_WORKSPACE before any HIP call. `get_scratch` is then called once the
+// arguments are checked and returns the current device's buffer.
+int prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                 const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state,
+                 int B, int T, int H, int dk, int dv, int chunk, int dtype, const kda_fusion* fusion, void* workspace,
+                 size_t workspace_bytes, int (*get_scratch)(void**), size_t scratch_bytes, void* stream) {
   const bool varlen = cu_seqlens != nullptr;
   int st = check_prefill(B, T, H, num_seqs, varlen, dk, dv, chunk, dtype);
   if (st != KDA_OK) return st;
@@ -238,21 +246,80 @@ int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float
   const size_t need = kda::prefill_workspace_bytes(B, T, H, num_seqs, varlen, chunk, dtype, path);
   if (workspace && workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (get_scratch && need > scratch_bytes)
+    return fail(KDA_ERR_WORKSPACE, "this prefill needs %zu bytes of scratch; the static scratch holds %zu", need,
+                scratch_bytes);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* ws = workspace;
-  if (!ws) {
+  bool allocated = false;
+  if (!ws && get_scratch) {
+    const int st2 = get_scratch(&ws);
+    if (st2 != KDA_OK) return st2;
+  } else if (!ws) {
     hipError_t e = hipMallocAsync(&ws, need, s);
     if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+    allocated = true;
   }
   hipError_t e = kda::launch_prefill(dtype, chunk, q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o,
                                      final_state, B, T, H, to_internal(fusion), ws, s);
-  if (!workspace) {
+  if (allocated) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;
   }
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Scratch of kda_chunk_fwd_noalloc. Each GPU the library runs on holds its own copy
+// until the process ends. In host code the array's name is only a host-side stand-in:
+// host code uses the per-device address from hipGetSymbolAddress, never the name.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, looked up once per device (with that
+// device current) and kept.
+int current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(KDA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KDA_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
+                        float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                        const kda_fusion* fusion, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o, final_state, B, T, H, dk, dv,
+                      chunk, dtype, fusion, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                          const float* initial_state, const int32_t* cu_seqlens, int num_seqs, void* o,
+                          float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype, void* stream) {
+  kda_fusion f{};
+  f.gate_kind = KDA_GATE_CHANNEL;
+  f.prefill_path = (dtype == KDA_BF16 && chunk == 64) ? KDA_PATH_SINGLE_PASS : KDA_PATH_AUTO;
+  return prefill_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o, final_state, B, T, H, dk, dv,
+                      chunk, dtype, &f, nullptr, 0, current_scratch, KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int num_seqs, int dtype) {

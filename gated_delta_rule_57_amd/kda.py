@@ -26,7 +26,7 @@ EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_chunk_
            "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused", "kda_decode_step_fused",
            "kda_output_norm_gate", "kda_timing_enable", "kda_timing_read", "kda_chunk_bwd_workspace_size",
            "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd",
-           "kda_chunk_fwd_fused_workspace_size")
+           "kda_chunk_fwd_fused_workspace_size", "kda_chunk_fwd_noalloc")
 
 KERNEL_NAMES = ("plan", "intra", "inter", "decode", "outnorm", "bwd_local", "bwd_state",
                 "bwd_chunk", "seg_first", "seg_scan", "seg_second")  # KDA_KERNEL_* ids
@@ -75,6 +75,8 @@ def _load():
     lib.kda_chunk_fwd_fused_workspace_size.argtypes = [I, I, I, I, I, I, P]
     lib.kda_chunk_fwd_fused.restype = I
     lib.kda_chunk_fwd_fused.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, P, Z, P]
+    lib.kda_chunk_fwd_noalloc.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]
     lib.kda_decode_step_fused.restype = I
     lib.kda_decode_step_fused.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.kda_output_norm_gate.restype = I
@@ -202,18 +204,9 @@ def _check_out_gate(f, o):
             raise ValueError(f"out_gate must match o: {tuple(o.shape)} {o.dtype}")
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
-              output_final_state=True, o=None, final_state=None, workspace=None, fusion=None, path="auto"):
-    """Chunked KDA prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_fused`` when
-    ``fusion`` is given, see ``fusion()``, the gate is not per channel or ``path`` is
-    "record").
-
-    q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
-    log_alpha: [B, T, H, 128] fp32 (KDA), [B, T, H] fp32 (one decay per token and
-    head: Gated DeltaNet) or None (no decay: DeltaNet); beta: [B, T, H] fp32;
-    initial_state: [N, H, 128, 128] fp32 or None; cu_seqlens: int32 [N+1] device
-    tensor (B must be 1) or None. Returns (o, final_state or None).
-    """
+def _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, output_final_state, o, final_state):
+    """Checks the prefill tensors; returns (B, T, H, dk, dv, dtype code, N, o, final_state)
+    with o and final_state allocated when not given."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -223,9 +216,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
     _need(q, "q", dt, (B, T, H, dk))
     _need(k, "k", dt, (B, T, H, dk))
     _need(v, "v", dt, (B, T, H, dv))
-    gate = _gate_kind(log_alpha, (B, T, H), dk)
     _need(beta, "beta", torch.float32, (B, T, H))
-    fusion = _with_gate(fusion, gate, path)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
             raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
@@ -242,6 +233,25 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     elif final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    return B, T, H, dk, dv, dcode, N, o, final_state
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
+              output_final_state=True, o=None, final_state=None, workspace=None, fusion=None, path="auto"):
+    """Chunked KDA prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_fused`` when
+    ``fusion`` is given, see ``fusion()``, the gate is not per channel or ``path`` is
+    "record").
+
+    q, k: [B, T, H, 128]; v: [B, T, H, 128] (bf16 or fp32, all the same);
+    log_alpha: [B, T, H, 128] fp32 (KDA), [B, T, H] fp32 (one decay per token and
+    head: Gated DeltaNet) or None (no decay: DeltaNet); beta: [B, T, H] fp32;
+    initial_state: [N, H, 128, 128] fp32 or None; cu_seqlens: int32 [N+1] device
+    tensor (B must be 1) or None. Returns (o, final_state or None).
+    """
+    B, T, H, dk, dv, dcode, N, o, final_state = _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
+                                                              output_final_state, o, final_state)
+    gate = _gate_kind(log_alpha, (B, T, H), dk)
+    fusion = _with_gate(fusion, gate, path)
     ws_bytes = 0
     if workspace is not None:
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -258,6 +268,27 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chu
             _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
             N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
             ctypes.byref(fusion), _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, final_state
+
+
+#: bytes of the static scratch behind ``chunk_fwd_noalloc`` (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, chunk=64,
+                      output_final_state=True, o=None, final_state=None):
+    """Chunked KDA prefill through ``kda_chunk_fwd_noalloc``: the library allocates
+    nothing (its scratch is a static per-device array of NOALLOC_SCRATCH_BYTES).
+    Tensors as in ``chunk_fwd`` with a per-channel log_alpha; pass ``o`` and
+    ``final_state`` to keep this call free of allocations on the Python side too.
+    Calls that overlap on one GPU race on the shared scratch."""
+    B, T, H, dk, dv, dcode, N, o, final_state = _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
+                                                              output_final_state, o, final_state)
+    _need(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _check(lib.kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), B, T, H, dk, dv, chunk, dcode,
+        _stream(q.device)))
     return o, final_state
 
 

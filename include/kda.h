@@ -233,6 +233,28 @@ int kda_chunk_fwd_fused(const void *q, const void *k, const void *v, const float
 size_t kda_chunk_fwd_fused_workspace_size(int B, int T, int H, int num_seqs, int chunk, int dtype,
                                           const kda_fusion *fusion);
 
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments and
+ * results as kda_chunk_fwd without the workspace; nothing is allocated. The kernels'
+ * scratch is a static device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * the library runs on holds from the first call until the process ends; its address
+ * is looked up once per device. bf16 with 64-token chunks runs the single-pass
+ * kernels (KDA_PATH_SINGLE_PASS), whose scratch is a few 128 x 128 fp32 states per
+ * (segment, head): about 60 MiB at 128K tokens x 32 heads; fp32 and 16-token chunks
+ * run the record path, whose scratch grows with B*T*H (kda_chunk_fwd_fused_workspace_size
+ * with that prefill_path gives the need of any configuration). A configuration that
+ * needs more than the array holds returns KDA_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host threads) race.
+ * With kda_timing_enable on, the timing records still create host-side events.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int num_seqs, void *o, float *final_state, int B, int T, int H, int dk,
+                          int dv, int chunk, int dtype, void *stream);
+
 /* kda_decode_step with the prologue / epilogue of `fusion` (NULL = kda_decode_step). */
 int kda_decode_step_fused(const void *q, const void *k, const void *v, const float *log_alpha,
                           const float *beta, float *state, void *o, int N, int H, int dk, int dv,

@@ -313,3 +313,38 @@ def test_dplr_workspace_size():
     assert kda.dplr_workspace_size(1, 4096, 16, num_seqs=3) >= n
     assert kda.dplr_workspace_size(1, 64, 0) == 0
     assert kda.dplr_workspace_size(1, 64, 2) > kda.workspace_size(1, 64, 2, path="record")
+
+
+def noalloc_call(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, s0=None, cu=None, num_seqs=0, o=FAKE, fin=FAKE,
+                 B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0):
+    return L.kda_chunk_fwd_noalloc(q, k, v, la, beta, s0, cu, num_seqs, o, fin, B, T, H, dk, dv, chunk, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(la=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=MISALIGNED), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu=FAKE, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
+    # more scratch than the static array holds: 64 sequences x 64 heads (single pass),
+    # and fp32 16-token chunks over 65536 tokens x 32 heads (records)
+    (dict(B=64, T=8192, H=64), kda.KDA_ERR_WORKSPACE),
+    (dict(dtype=1, chunk=16, T=65536, H=32), kda.KDA_ERR_WORKSPACE),
+])
+def test_chunk_fwd_noalloc_rejects(kw, status):
+    """Every check, the scratch limit included, runs before any HIP call."""
+    assert noalloc_call(**kw) == status
+    assert L.kda_last_error().decode() != ""
+
+
+def test_chunk_fwd_noalloc_limit():
+    """The static scratch (KDA_NOALLOC_SCRATCH_BYTES) holds the single pass of the
+    131072-token x 32-head workload; the rejected cases above need more."""
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == kda.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert kda.workspace_size(1, 131072, 32, path="single") <= limit
+    assert kda.workspace_size(64, 8192, 64, path="single") > limit
+    assert kda.workspace_size(1, 65536, 32, chunk=16, dtype=kda.KDA_FP32) > limit
+    assert noalloc_call(B=0, q=None, k=None, v=None, la=None, beta=None, o=None, fin=None) == kda.KDA_OK
