@@ -51,5 +51,43 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+# host-side AddressSanitizer and UndefinedBehaviorSanitizer; every -fsanitize goes to
+# the host pass only (the device code is built as usual and never run by these checks)
+SANITIZE_HOST_FLAGS = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                       "-shared-libsan")
+
+
+def sanitizer_runtime_dir() -> str:
+    """Directory of the ROCm LLVM sanitizer runtimes a host-sanitized build links to."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    res = subprocess.run([clang, "-print-resource-dir"], capture_output=True, text=True, check=True)
+    return os.path.join(res.stdout.strip(), "lib", "linux")
+
+
+def build_host_sanitized(out_path: str, verbose: bool = False) -> str:
+    """The same library with the host code (the C ABI, argument checks, workspace
+    sizing, launch set-up) built under AddressSanitizer and UndefinedBehaviorSanitizer,
+    written to ``out_path``; the in-tree libkda.so is left alone."""
+    cmd = [
+        hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1", *SANITIZE_HOST_FLAGS,
+        "-o", out_path + ".tmp", *[os.path.join(CSRC, s) for s in SOURCES],
+    ]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build the host-sanitized library")
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
 if __name__ == "__main__":
-    build_library(verbose=True)
+    if len(sys.argv) == 3 and sys.argv[1] == "--sanitize-host":
+        build_host_sanitized(sys.argv[2], verbose=True)
+    else:
+        build_library(verbose=True)

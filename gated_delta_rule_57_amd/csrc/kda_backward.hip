@@ -2,8 +2,8 @@
 //     L = sum_t <o_t, do_t> + sum_n <S_final[n], dS_final[n]>
 // with respect to q, k, v, log_alpha, beta and the initial state. The pages present
 // the chunked WY / UT form as what makes KDA efficient to train ("From GPT-2 to Kimi
-// K3" digest, section on chunked computation; GeekNews "Kimi Linear" summary,
-// section "청크 단위 병렬화"); these are the derivatives of that map.
+// K3" digest, section "DeltaNet 병렬화 -- 청크 단위 학습"; GeekNews "Kimi Linear" summary,
+// section "청크 단위 병렬 알고리듬"); these are the derivatives of that map.
 //
 // Per chunk of C = 16 tokens (rows r, s), with S0 the state entering the chunk and
 // G the in-chunk cumulative log decay (per channel), the forward is

@@ -276,8 +276,8 @@ int kda_output_norm_gate(const void *o, const void *gate, const float *weight, v
  *
  * with respect to q, k, v, log_alpha, beta and initial_state. The pages present
  * the chunked WY / UT form as what makes KDA efficient to train ("From GPT-2 to
- * Kimi K3" digest, section on chunked computation; GeekNews "Kimi Linear" summary,
- * section "청크 단위 병렬화"). It recomputes the forward internally (16-token
+ * Kimi K3" digest, section "DeltaNet 병렬화 -- 청크 단위 학습"; GeekNews "Kimi Linear" summary,
+ * section "청크 단위 병렬 알고리듬"). It recomputes the forward internally (16-token
  * chunks, keeping each chunk's entry state), runs the state gradient backwards
  * through the chunks, then forms every chunk's gradients in parallel.
  *

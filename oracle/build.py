@@ -30,3 +30,18 @@ def build_oracle(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
+
+
+SANITIZE_FLAGS = ("-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer")
+
+
+def build_sanitized_program(driver_c: str, out_path: str, verbose: bool = False) -> str:
+    """Links a C driver with the oracle's source into an executable built under gcc's
+    AddressSanitizer and UndefinedBehaviorSanitizer (the oracle's C checked for
+    out-of-bounds access, leaks and undefined behaviour)."""
+    cmd = ["gcc", "-O1", "-g", *SANITIZE_FLAGS, "-ffp-contract=off", "-fopenmp", "-o", out_path, driver_c, _SRC,
+           "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out_path

@@ -262,8 +262,8 @@ int kda_oracle_decode_step(const float *q, const float *k, const float *v,
  *
  * with respect to q, k, v, log_alpha, beta and the initial state. The pages present
  * the chunked form as the device that makes KDA efficient to train ("From GPT-2 to
- * Kimi K3" digest, section on chunked computation; GeekNews "Kimi Linear" summary,
- * section "청크 단위 병렬화"), so its gradients are the derivatives of this map.
+ * Kimi K3" digest, section "DeltaNet 병렬화 -- 청크 단위 학습"; GeekNews "Kimi Linear" summary,
+ * section "청크 단위 병렬 알고리듬"), so its gradients are the derivatives of this map.
  *
  * One token, forward (as above):  S' = Diag(a) S ;  e = v - S'^T k ;
  * S_t = S' + b k e^T ;  o_t = S_t^T q.  Backward, with L_t the gradient of L with
