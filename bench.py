@@ -54,8 +54,10 @@ RECORD_MOVED_BYTES_BF16_C64 = RECORD_BYTES_BF16_C64 - 2048
 # U tiles of its B columns
 SEG_OUT_READ = RECORD_BYTES_BF16_C64
 SEG_MAP_READ = 16384 + 16384 + 512 + 16384
-# segment length rule of the library (SEG_TARGET_GROUPS, SEG_MIN_CHUNKS in kda_internal.h)
+# segment length rule of the library (SEG_TARGET_GROUPS, SEG_MIN_CHUNKS, SEG_FIRST_PCT_* in
+# kda_internal.h): the first segment of a sequence is a share of the later ones
 SEG_TARGET_GROUPS, SEG_MIN_CHUNKS = 256, 1
+SEG_FIRST_PCT = {"record": 55, "single": 80}
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
@@ -105,23 +107,26 @@ def committed_profile(name, src_hash):
     return data if data.get("kernel_source_hash") == src_hash else None
 
 
-def seg_plan(T, H, N=1):
-    """Segments per sequence of the segment-parallel state kernels for N sequences of T
-    tokens (the library's rule): (chunks per segment, segments)."""
-    mc = N * ((T + CHUNK - 1) // CHUNK)
-    target = SEG_TARGET_GROUPS + N * H
+def seg_plan(T, H, N=1, kernels="record"):
+    """The library's segment plan for N sequences of T tokens and H heads: (chunks per
+    segment after the first, chunks in the first, segments per sequence)."""
+    pct = SEG_FIRST_PCT[kernels]
+    nc = (T + CHUNK - 1) // CHUNK
+    mc = N * nc
+    target = SEG_TARGET_GROUPS + (N * H * pct + 99) // 100
     lseg = max(SEG_MIN_CHUNKS, (mc * H + target - 1) // target)
     lseg = min(lseg, mc) if mc > 0 else 1
-    nc = (T + CHUNK - 1) // CHUNK
-    return lseg, max(1, (nc + lseg - 1) // lseg)
+    l0 = max(1, (lseg * pct + 50) // 100)
+    ns = 1 if nc <= l0 else 1 + (nc - l0 + lseg - 1) // lseg
+    return lseg, l0, ns
 
 
 def seg_design_bytes(T, H):
-    """Bytes the segment-parallel state kernels read and write by construction for one
-    T-token sequence of H heads: (first pass, second pass)."""
-    lseg, ns = seg_plan(T, H)
+    """Bytes the record-fed segment-parallel state kernels read and write by
+    construction for one T-token sequence of H heads: (first pass, second pass)."""
+    lseg, l0, ns = seg_plan(T, H)
     nc = (T + CHUNK - 1) // CHUNK
-    lens = [min(lseg, nc - j * lseg) for j in range(ns)]
+    lens = [min(l0, nc)] + [min(lseg, nc - l0 - (j - 1) * lseg) for j in range(1, ns)]
     o_per_chunk = CHUNK * 2 * D
     first = H * (lens[0] * (SEG_OUT_READ + o_per_chunk) + sum(lens[1:ns - 1]) * SEG_MAP_READ)
     second = H * sum(lens[1:]) * (SEG_OUT_READ + o_per_chunk)
@@ -569,7 +574,7 @@ def main():
     n_chunks = (T + CHUNK - 1) // CHUNK
     rec_moved = n_chunks * H * RECORD_MOVED_BYTES_BF16_C64
     seg_a, seg_b = seg_design_bytes(T, H)
-    lseg, ns = seg_plan(T, H)
+    lseg, l0, ns = seg_plan(T, H)
     design = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD + rec_moved,
               "inter": rec_moved + tok_heads * 2 * D,
               "seg_first": seg_a, "seg_second": seg_b,
@@ -626,7 +631,7 @@ def main():
         "prefill": {"ms": pst, "tokens_per_s": round(tokens_per_s, 1),
                     "path_hbm_frac": roof["frac"],
                     "kernel_ms": {n: round(kms[n], 4) for n in path_kernels},
-                    "segments": {"chunks_per_segment": lseg, "segments_per_head": ns}},
+                    "segments": {"chunks_first_segment": l0, "chunks_per_segment": lseg, "segments_per_head": ns}},
         "mfma": mfma,
         "decode": {"ms_per_step": dst, "GBps": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                    "tokens_per_s": round(DEC_N / (dec_ms * 1e-3), 1)},

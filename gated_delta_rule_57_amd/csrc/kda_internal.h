@@ -73,16 +73,24 @@ inline int prefill_kernels(int dtype, int chunk, int path, int64_t max_chunks, i
 // pass, segments of at least SEG_MIN_CHUNKS chunks.
 constexpr int SEG_TARGET_GROUPS = 256;
 constexpr int SEG_MIN_CHUNKS = 1;
-int seg_chunks_per_segment(int64_t max_chunks, int N, int H);
+// The first segment of a sequence is this share (percent) of the later ones: in pass
+// A its work-groups write outputs while the others only compose maps (record-fed: a
+// map chunk moves about 0.55 of an output chunk's bytes; single pass: about 0.8 of its
+// work), so both finish together.
+constexpr int SEG_FIRST_PCT_RECORD = 55;
+constexpr int SEG_FIRST_PCT_SINGLE = 80;
+int seg_chunks_per_segment(int64_t max_chunks, int N, int H, int first_pct);
+int seg_first_chunks(int lseg, int first_pct);
 // Workspace: segment offsets [N+1] int32, segment table [segments] int2, entry
 // states [segments][H][128*128] fp32, segment maps [segments][H][2][128*128] fp32.
 struct SegWs {
-  int lseg;
+  int lseg, l0;  // chunks per segment after the first, and in the first
   int64_t max_segments;
   size_t off_seg_off, off_seg_info, off_seg_in, off_seg_map, total;
 };
-SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen);
-SegWs seg_ws_layout_for(int lseg, int64_t max_segments, int N, int H);
+// single: the plan of the single pass (else the record-fed kernels)
+SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single);
+SegWs seg_ws_layout_for(int lseg, int l0, int64_t max_segments, int N, int H);
 // The single pass: every step of the prefill for bf16, 64-token chunks.
 hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const float* log_alpha,
                               const float* beta, const float* initial_state, const int32_t* cu_seqlens,
@@ -92,8 +100,7 @@ hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const
 // pass, scan, second pass), with the output epilogue of `fusion` fused in.
 hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64_t mc, const int32_t* cu_seqlens,
                             int N, int T, int H, const float* initial_state, float* final_state, void* o,
-                            const Fusion& fusion, void* seg_workspace, int lseg, int64_t max_segments,
-                            hipStream_t stream);
+                            const Fusion& fusion, void* seg_workspace, const SegWs& plan, hipStream_t stream);
 
 hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* initial_state,

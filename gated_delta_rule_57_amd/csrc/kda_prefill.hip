@@ -945,9 +945,9 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
     if (slots > 0 && prefill_kernels(0, 64, fusion.prefill_path, mc, N) == KERNELS_RECORD_SEG) {
       // segment-parallel full-width state kernels on the records (output epilogue fused in)
       int B = cu_seqlens ? 1 : N;
-      const SegWs sl = seg_ws_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr);
+      const SegWs sl = seg_ws_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr, false);
       return launch_state_seg(records, chunk_off, mc, cu_seqlens, N, T, H, initial_state, final_state, o, fusion,
-                              ws + al256(l.total), sl.lseg, sl.max_segments, stream);
+                              ws + al256(l.total), sl, stream);
     }
   }
   if (slots > 0) {
@@ -1018,9 +1018,9 @@ hipError_t launch_forward_records(int dtype, const void* q, const void* k, const
 
 size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path) {
   const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), varlen ? num_seqs : B);
-  if (kern == KERNELS_SINGLE) return seg_ws_layout(B, T, H, num_seqs, varlen).total;
+  if (kern == KERNELS_SINGLE) return seg_ws_layout(B, T, H, num_seqs, varlen, true).total;
   const size_t rec = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;
-  if (kern == KERNELS_RECORD_SEG) return al256(rec) + seg_ws_layout(B, T, H, num_seqs, varlen).total;
+  if (kern == KERNELS_RECORD_SEG) return al256(rec) + seg_ws_layout(B, T, H, num_seqs, varlen, false).total;
   return rec;
 }
 

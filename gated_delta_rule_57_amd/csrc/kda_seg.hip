@@ -16,8 +16,8 @@
 // consecutive chunks and the full 128 x 128 fp32 state. For every chunk it forms
 // the chunk's matrices in LDS from q, k, v, the gates and beta, then advances the
 // state in registers, so nothing but the inputs, the outputs and a few states per
-// segment goes through HBM. A sequence is cut into segments of `lseg` chunks so
-// that enough work-groups run at once:
+// segment goes through HBM. A sequence is cut into a first segment of `l0` chunks
+// and further segments of `lseg` chunks so that enough work-groups run at once:
 //   pass A  segment 0 of a sequence runs the output pass from the initial state
 //           and writes the state at its end; every middle segment composes its
 //           chunk maps into (M, B) (state columns from the identity and from zero);
@@ -26,6 +26,9 @@
 //           writes the final state.
 // The two passes each have about one work-group per (sequence, head, segment), so
 // the segment length is chosen to give about as many work-groups as compute units.
+// In pass A the first segments write outputs while the others only compose maps,
+// which costs less per chunk, so the first segment is shorter (l0 = a fixed share of
+// lseg, per kernel set) and both kinds of work-group finish together.
 //
 // In-chunk decay: everything in log2 units; rows are grouped in sub-chunks of 16
 // with b_I the cumulative decay before sub-chunk I. Decays inside a sub-chunk are
@@ -133,7 +136,7 @@ struct SegArgs {
   const int32_t* cu_seqlens;
   int T;             // tokens per sequence (fixed-length batches)
   int total_tokens;  // tokens in the packed axis
-  int N, H, lseg;
+  int N, H, lseg, l0;      // chunks per segment after the first, and in the first
   const int32_t* seg_off;  // [N + 1]
   const int2* seg_info;    // [segments] (sequence, index in sequence)
   float* seg_in;           // [segments][H][128 * 128] state entering the segment
@@ -222,27 +225,36 @@ struct ChainOps {
 // columns. Two work-group barriers (three with the epilogue).
 // `mid` runs between the two barriers (the record-fed passes stage the next chunk's
 // operands there).
+// The output epilogue's gate values of one chunk for wave half HR (rows 32 HR + 16 j
+// + m, columns col0 + 16 c + 4 g .. + 3); rows past len read the chunk's first row.
+// Nothing is loaded without an output gate or for an empty chunk.
+template <int HR>
+__device__ __forceinline__ void load_out_gate(bf16x4 (&zv)[2][2], const Fusion& fu, size_t HD, int h, int tok0,
+                                              int len, int w, int lane) {
+  if (!fu.out_gate || len <= 0) return;
+  const int m = lane & 15, g = lane >> 4, col0 = 32 * (w & 3);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 32 * HR + 16 * j + m, rr = row < len ? row : 0;
+      zv[j][c] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(fu.out_gate) +
+                                                 (size_t)(tok0 + rr) * HD + (size_t)h * D + col0 + 16 * c + 4 * g);
+    }
+}
+
+// zv holds this chunk's gate values on entry (see load_out_gate) and the next chunk's
+// (next_len tokens from tok0 + 64) on return, so each load has a whole step to land.
 template <int HR, typename Mid>
 __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4 (&au)[2][2], const ChainOps& op,
                                                const Fusion& fu, __bf16* __restrict__ o, size_t HD, int h, int tok0,
-                                               int len, int w, int lane, Mid&& mid) {
+                                               int len, int next_len, bf16x4 (&zv)[2][2], int w, int lane,
+                                               Mid&& mid) {
   constexpr int hr = HR, ho = 1 - HR;
   const int m = lane & 15, g = lane >> 4;
   const int c4 = w & 3, col0 = 32 * c4;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  // output epilogue gate values of this lane's rows, loaded before the products
-  bf16x4 zv[2][2];
   const bool gated = fu.out_gate != nullptr;
-  if (gated) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int row = 32 * hr + 16 * j + m, rr = row < len ? row : 0;
-        zv[j][c] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(fu.out_gate) +
-                                                   (size_t)(tok0 + rr) * HD + (size_t)h * D + col0 + 16 * c + 4 * g);
-      }
-  }
   // own state rows as operand fragments: k-blocks 2 hr, 2 hr + 1
   bf16x8 Sb[4][2];
 #pragma unroll
@@ -349,6 +361,7 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
         for (int i = 0; i < 4; ++i) xt[j][c][i] = xt[j][c][i] * inv * nw[i] * sigmoid_f((float)zv[j][c][i]);
       }
     }
+    load_out_gate<HR>(zv, fu, HD, h, tok0 + SC, next_len, w, lane);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1037,8 +1050,16 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
     // ---- the state step (the exchange buffers of the output pass reuse the scratch
     //      region, dead until the next chunk's decay phase) ----------------------------
     if constexpr (OUTP) {
-      if (w >> 2) out_state_step<1>(S, au, ops, fu, a.o, HD, h, tok0, len, w, lane, [] {});
-      else out_state_step<0>(S, au, ops, fu, a.o, HD, h, tok0, len, w, lane, [] {});
+      // the output gate values are loaded at the step (registers here are too tight to
+      // hold the next chunk's across the chunk's matrix phases)
+      bf16x4 zv[2][2];
+      if (w >> 2) {
+        load_out_gate<1>(zv, fu, HD, h, tok0, len, w, lane);
+        out_state_step<1>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, w, lane, [] {});
+      } else {
+        load_out_gate<0>(zv, fu, HD, h, tok0, len, w, lane);
+        out_state_step<0>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, w, lane, [] {});
+      }
     } else {
       map_state_step(S, au, ops, w, lane);
     }
@@ -1145,7 +1166,13 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
           for (int i = 0; i < 4; ++i) u[c][j][i] = (float)x.u[c][j][i];
       }
   };
+  bf16x4 zv[2][2];  // output gate values of the chunk being stepped (epilogue)
   if (nchunks > 0) {
+    if constexpr (OUTP) {
+      const int l0 = min(SC, tok_end - tok_begin);
+      if (w >> 2) load_out_gate<1>(zv, a.fu, HD, h, tok_begin, l0, w, lane);
+      else load_out_gate<0>(zv, a.fu, HD, h, tok_begin, l0, w, lane);
+    }
     load_record<PASS>(x, head_rec + (size_t)c_first * RC::BYTES, threadIdx.x);
     take(threadIdx.x, 0);
     take_u(au, w);
@@ -1169,8 +1196,9 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
       load_record<PASS>(x, head_rec + (size_t)(c_first + min(ci + 2, nchunks - 1)) * RC::BYTES, t);
     };
     if constexpr (OUTP) {
-      if (w_ >> 2) out_state_step<1>(S, au, ops, a.fu, a.o, HD, h, tok0, len, w_, lane_, mid);
-      else out_state_step<0>(S, au, ops, a.fu, a.o, HD, h, tok0, len, w_, lane_, mid);
+      const int next_len = ci + 1 < nchunks ? min(SC, tok_end - tok0 - SC) : 0;
+      if (w_ >> 2) out_state_step<1>(S, au, ops, a.fu, a.o, HD, h, tok0, len, next_len, zv, w_, lane_, mid);
+      else out_state_step<0>(S, au, ops, a.fu, a.o, HD, h, tok0, len, next_len, zv, w_, lane_, mid);
     } else {
       mid();
       map_state_step(S, au, ops, w_, lane_);
@@ -1210,8 +1238,8 @@ __global__ void __launch_bounds__(NTHR) seg_pass_kernel(SegArgs a) {
   int s0, s1;
   seq_range(a, n, s0, s1);
   const int nc = (s1 - s0 + SC - 1) / SC;
-  const int c0 = j * a.lseg;
-  const int cnt = max(0, min(a.lseg, nc - c0));
+  const int c0 = j == 0 ? 0 : a.l0 + (j - 1) * a.lseg;
+  const int cnt = max(0, min(j == 0 ? a.l0 : a.lseg, nc - c0));
   const int tb = s0 + c0 * SC;
   const size_t uh = (size_t)n * a.H + h;
   const size_t sh = (size_t)s * a.H + h;
@@ -1243,8 +1271,8 @@ __global__ void __launch_bounds__(NTHR) rec_seg_kernel(SegArgs a) {
   seq_range(a, n, s0, s1);
   const int c_seq = a.chunk_off[n];
   const int nc = a.chunk_off[n + 1] - c_seq;
-  const int c0 = j * a.lseg;
-  const int cnt = max(0, min(a.lseg, nc - c0));
+  const int c0 = j == 0 ? 0 : a.l0 + (j - 1) * a.lseg;
+  const int cnt = max(0, min(j == 0 ? a.l0 : a.lseg, nc - c0));
   const int tb = s0 + c0 * SC;
   const size_t uh = (size_t)n * a.H + h;
   const size_t sh = (size_t)s * a.H + h;
@@ -1329,11 +1357,11 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(const int32_t* __restrict
   }
 }
 
-// Segment plan: per sequence its chunk count nc and segment count max(1, ceil(nc /
-// lseg)); seg_off = exclusive prefix of the segment counts (clamped to the table's
+// Segment plan: per sequence its chunk count nc and segment count (one when nc <= l0,
+// else 1 + ceil((nc - l0) / lseg)); seg_off = exclusive prefix of the segment counts (clamped to the table's
 // capacity), seg_info[s] = (sequence, index within it). One work-group of 1024.
 __global__ void __launch_bounds__(1024) seg_plan_kernel(const int32_t* __restrict__ cu_seqlens, int N, int T,
-                                                        int total_tokens, int lseg, int capacity,
+                                                        int total_tokens, int lseg, int l0, int capacity,
                                                         int32_t* __restrict__ seg_off, int2* __restrict__ seg_info) {
   __shared__ int s_scan[1024];
   __shared__ int s_carry;
@@ -1348,7 +1376,7 @@ __global__ void __launch_bounds__(1024) seg_plan_kernel(const int32_t* __restric
       int len = T;
       if (cu_seqlens) len = max(0, clampt(cu_seqlens[n + 1]) - clampt(cu_seqlens[n]));
       const int nc = (len + SC - 1) / SC;
-      cnt = max(1, (nc + lseg - 1) / lseg);
+      cnt = nc <= l0 ? 1 : 1 + (nc - l0 + lseg - 1) / lseg;
     }
     s_scan[t] = cnt;
     __syncthreads();
@@ -1383,19 +1411,25 @@ __global__ void __launch_bounds__(1024) seg_plan_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int seg_chunks_per_segment(int64_t mc, int N, int H) {
-  // about SEG_TARGET_GROUPS work-groups per pass: mc * H / lseg segment-heads beyond
-  // the first segment of each (sequence, head)
-  const int64_t target = SEG_TARGET_GROUPS + (int64_t)N * H;
+int seg_chunks_per_segment(int64_t mc, int N, int H, int first_pct) {
+  // about SEG_TARGET_GROUPS work-groups per pass: the segments after the first number
+  // (mc - N l0) / lseg per head, with l0 = first_pct % of lseg
+  const int64_t target = SEG_TARGET_GROUPS + ((int64_t)N * H * first_pct + 99) / 100;
   int64_t l = (mc * H + target - 1) / target;
   if (l < SEG_MIN_CHUNKS) l = SEG_MIN_CHUNKS;
   if (l > mc) l = mc > 0 ? mc : 1;
   return (int)l;
 }
 
-SegWs seg_ws_layout_for(int lseg, int64_t msg, int N, int H) {
+int seg_first_chunks(int lseg, int first_pct) {
+  const int l0 = (lseg * first_pct + 50) / 100;
+  return l0 < 1 ? 1 : l0;
+}
+
+SegWs seg_ws_layout_for(int lseg, int l0, int64_t msg, int N, int H) {
   SegWs l;
   l.lseg = lseg;
+  l.l0 = l0;
   l.max_segments = msg;
   l.off_seg_off = 0;
   l.off_seg_info = al256((size_t)(N + 1) * sizeof(int32_t));
@@ -1405,13 +1439,23 @@ SegWs seg_ws_layout_for(int lseg, int64_t msg, int N, int H) {
   return l;
 }
 
-SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen) {
+SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single) {
   const int N = varlen ? num_seqs : B;
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, SC);
-  const int lseg = seg_chunks_per_segment(mc, N, H);
-  // every sequence has at most ceil(nc / lseg) <= nc / lseg + 1 segments, and at least one
-  const int64_t msg = (int64_t)N + (mc + lseg - 1) / lseg;
-  return seg_ws_layout_for(lseg, msg, N, H);
+  const int pct = single ? SEG_FIRST_PCT_SINGLE : SEG_FIRST_PCT_RECORD;
+  const int lseg = seg_chunks_per_segment(mc, N, H, pct);
+  const int l0 = seg_first_chunks(lseg, pct);
+  // a sequence of nc chunks has 1 + ceil((nc - l0) / lseg) segments (one if nc <= l0):
+  // exactly that for N sequences of T tokens; at most 2 + (nc - l0) / lseg each when
+  // packed, so 2 N + ceil(mc / lseg) over all
+  int64_t msg;
+  if (!varlen) {
+    const int64_t nc = ((int64_t)T + SC - 1) / SC;
+    msg = (int64_t)N * (nc <= l0 ? 1 : 1 + (nc - l0 + lseg - 1) / lseg);
+  } else {
+    msg = 2 * (int64_t)N + (mc + lseg - 1) / lseg;
+  }
+  return seg_ws_layout_for(lseg, l0, msg, N, H);
 }
 
 namespace {
@@ -1436,9 +1480,9 @@ hipError_t launch_seg_typed(const SegArgs& a, int64_t msg, bool any_multi, hipSt
 
 hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64_t mc, const int32_t* cu_seqlens,
                             int N, int T, int H, const float* initial_state, float* final_state, void* o,
-                            const Fusion& fusion, void* seg_workspace, int lseg, int64_t max_segments,
-                            hipStream_t stream) {
-  const SegWs l = seg_ws_layout_for(lseg, max_segments, N, H);
+                            const Fusion& fusion, void* seg_workspace, const SegWs& l, hipStream_t stream) {
+  const int lseg = l.lseg;
+  const int64_t max_segments = l.max_segments;
   char* ws = reinterpret_cast<char*>(seg_workspace);
   SegArgs a{};
   a.initial_state = initial_state;
@@ -1450,6 +1494,7 @@ hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64
   a.N = N;
   a.H = H;
   a.lseg = lseg;
+  a.l0 = l.l0;
   a.seg_off = reinterpret_cast<int32_t*>(ws + l.off_seg_off);
   a.seg_info = reinterpret_cast<int2*>(ws + l.off_seg_info);
   a.seg_in = reinterpret_cast<float*>(ws + l.off_seg_in);
@@ -1458,7 +1503,7 @@ hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64
   a.records = records;
   a.chunk_off = chunk_off;
   a.mc = (int)mc;
-  hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, a.total_tokens, lseg,
+  hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, a.total_tokens, lseg, l.l0,
                      (int)max_segments, const_cast<int32_t*>(a.seg_off), const_cast<int2*>(a.seg_info));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1466,7 +1511,7 @@ hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64
   hipLaunchKernelGGL((rec_seg_kernel<false>), dim3(grid), dim3(NTHR), 0, stream, a);
   e = hipGetLastError();
   trace_mark(stream, 8);
-  if (e != hipSuccess || (int64_t)lseg >= mc) return e;
+  if (e != hipSuccess || (int64_t)l.l0 >= mc) return e;
   hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((int64_t)N * H * 8)), dim3(256), 0, stream, a.seg_off, N, H,
                      a.seg_in, a.seg_map);
   e = hipGetLastError();
@@ -1484,7 +1529,7 @@ hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const
                               void* workspace, hipStream_t stream) {
   const bool varlen = cu_seqlens != nullptr;
   const int N = varlen ? num_seqs : B;
-  const SegWs l = seg_ws_layout(B, T, H, num_seqs, varlen);
+  const SegWs l = seg_ws_layout(B, T, H, num_seqs, varlen, true);
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, SC);
   char* ws = reinterpret_cast<char*>(workspace);
   SegArgs a;
@@ -1502,19 +1547,20 @@ hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const
   a.N = N;
   a.H = H;
   a.lseg = l.lseg;
+  a.l0 = l.l0;
   a.seg_off = reinterpret_cast<int32_t*>(ws + l.off_seg_off);
   a.seg_info = reinterpret_cast<int2*>(ws + l.off_seg_info);
   a.seg_in = reinterpret_cast<float*>(ws + l.off_seg_in);
   a.seg_map = reinterpret_cast<float*>(ws + l.off_seg_map);
   a.fu = fusion;
   trace_begin(stream);
-  hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, a.total_tokens, l.lseg,
+  hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, a.total_tokens, l.lseg, l.l0,
                      (int)l.max_segments, const_cast<int32_t*>(a.seg_off), const_cast<int2*>(a.seg_info));
   hipError_t e = hipGetLastError();
   trace_mark(stream, 0);
   if (e != hipSuccess) return e;
   // some sequence can have more than one segment unless one segment holds every chunk
-  const bool any_multi = (int64_t)l.lseg < mc;
+  const bool any_multi = (int64_t)l.l0 < mc;
   if (fusion.gate_kind == G_HEAD) return launch_seg_typed<G_HEAD>(a, l.max_segments, any_multi, stream);
   if (fusion.gate_kind == G_NONE) return launch_seg_typed<G_NONE>(a, l.max_segments, any_multi, stream);
   return launch_seg_typed<G_CHANNEL>(a, l.max_segments, any_multi, stream);
