@@ -298,46 +298,50 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     sBeta[t] = bt;
   }
   if (t < NSUB) sFlag[t] = 0;
-  // prologue on raw inputs: a row's 128 channels are spread over the 32 lanes of one
-  // half-wave (4 each), so its squared norm is a half-wave sum
-  if (fu.normalize_qk) {
+  // Rows past len are zeroed and (prologue on raw inputs) q and k rows L2-normalised
+  // where they are first needed, after the decay phases: nothing before the first
+  // barrier waits for the q, k and v loads. A row's 128 channels are spread over the
+  // 32 lanes of one half-wave (4 each), so its squared norm is a half-wave sum.
+  auto prep_rows = [&] {
+    if (fu.normalize_qk) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sk += kr[i][j] * kr[i][j];
+          sq += qr[i][j] * qr[i][j];
+        }
+        const float ik = rsqrtf(half_wave_sum(sk) + fu.qk_eps), iq = rsqrtf(half_wave_sum(sq) + fu.qk_eps);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kr[i][j] *= ik;
+          qr[i][j] *= iq;
+        }
+        if (GATE == GATE_CHANNEL && cq == 0) {  // the row's scales, for the exact path's reloads of raw k and q
+          sNrm[rbase + 8 * i] = ik;
+          sNrm[CK + rbase + 8 * i] = iq;
+        }
+      }
+    } else if (GATE == GATE_CHANNEL && cq == 0) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        sNrm[rbase + 8 * i] = 1.f;
+        sNrm[CK + rbase + 8 * i] = 1.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      float sk = 0.f, sq = 0.f;
+      const int r = rbase + 8 * i;
+      const bool valid = r < len;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sk += kr[i][j] * kr[i][j];
-        sq += qr[i][j] * qr[i][j];
-      }
-      const float ik = rsqrtf(half_wave_sum(sk) + fu.qk_eps), iq = rsqrtf(half_wave_sum(sq) + fu.qk_eps);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kr[i][j] *= ik;
-        qr[i][j] *= iq;
-      }
-      if (GATE == GATE_CHANNEL && cq == 0) {  // the row's scales, for the exact path's reloads of raw k and q
-        sNrm[rbase + 8 * i] = ik;
-        sNrm[CK + rbase + 8 * i] = iq;
+        kr[i][j] = valid ? kr[i][j] : 0.f;
+        qr[i][j] = valid ? qr[i][j] : 0.f;
+        vr[i][j] = valid ? vr[i][j] : 0.f;
       }
     }
-  } else if (GATE == GATE_CHANNEL && cq == 0) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      sNrm[rbase + 8 * i] = 1.f;
-      sNrm[CK + rbase + 8 * i] = 1.f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
-    const bool valid = r < len;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kr[i][j] = valid ? kr[i][j] : 0.f;
-      qr[i][j] = valid ? qr[i][j] : 0.f;
-      vr[i][j] = valid ? vr[i][j] : 0.f;
-    }
-  }
+  };
   constexpr int NBLK = SM::NBLK;
   constexpr int BPW = (NBLK + 3) / 4;
   static_assert(NBLK <= 10, "wave_block covers up to four sub-chunks");
@@ -458,6 +462,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   bool exact = false;  // some diagonal block exceeds the range limit: per-element path
 #pragma unroll
   for (int I = 0; I < NSUB; ++I) exact |= sFlag[I] != 0;
+  prep_rows();
 
   if (!exact) {
     // ---- P2 (factored path): Q e^G to the record, K e^G kept for B0, and per row
@@ -677,6 +682,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     __syncthreads();
     const float gC = sGs[C - 1];
     if (t < D) rec_gamma[t] = fast_exp2(gC);
+    prep_rows();
     // ---- P2 (scalar): Q e^G to the record, K e^G kept for B0, raw q, k to LDS --
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
