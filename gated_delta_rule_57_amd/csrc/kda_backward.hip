@@ -74,13 +74,7 @@ __host__ __device__ constexpr size_t bal256(size_t x) { return (x + 255) & ~(siz
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // sum over the 16 lanes l with equal l >> 4 (one row of the element-wise phases)
-__device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 1);
-  return x;
-}
+__device__ __forceinline__ float sum16(float x) { return row16_sum(x); }
 
 // Per-(head, chunk) record for the reverse state pass, in the MFMA operand order
 // reverse state pass consumes (lane l = m + 16 g; the fragment convention of
@@ -908,11 +902,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
   // dbeta = sum over channels of (dB_K o K e^G + dB_V o V) + sum_s dA_rs M_rs
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float x = dbr[i];
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    const float x = row16_sum(dbr[i]);
     if (m == 0) S.dbp[w][4 * g + i] = x;
   }
   __syncthreads();

@@ -158,4 +158,21 @@ __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
 }
 
+// x plus the value of another lane of its 16-lane row, chosen by a DPP control word
+// (row-local patterns only, so every lane has a source)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of x's row (lanes with equal lane >> 4), in every lane: quad
+// swaps xor 1 and xor 2, then the half-row and row mirrors, which pair each quad and
+// each half-row with the other one. DPP moves, no trip through the LDS unit.
+__device__ __forceinline__ float row16_sum(float x) {
+  x = dpp_add<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_add<0x141>(x);  // row_half_mirror
+  return dpp_add<0x140>(x);  // row_mirror
+}
+
 }  // namespace kda

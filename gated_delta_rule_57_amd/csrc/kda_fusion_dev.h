@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "kda_device.h"
+
 namespace kda {
 
 // log2(1 + 2^y) without overflow, from the hardware exp2 and log2: max(y, 0) +
@@ -28,23 +30,11 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return x >= 0.f ? r : e * r;
 }
 
-// x plus the value of another lane of its 16-lane row, chosen by a DPP control word
-// (row-local patterns only, so every lane has a source)
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// sum over the 32 lanes that share (lane & 32), i.e. one half of the wave. Inside each
-// 16-lane row by DPP (quad swaps xor 1 and xor 2, then the half-row and row mirrors,
-// which pair each quad or half-row with the other one); across the two rows by one
-// swizzle that exchanges lanes 16 apart. A chain of five lane permutes through the
-// LDS unit costs several times more.
+// sum over the 32 lanes that share (lane & 32), i.e. one half of the wave: the
+// 16-lane row sums (row16_sum, by DPP), then one swizzle that exchanges lanes 16
+// apart. A chain of five lane permutes through the LDS unit costs several times more.
 __device__ __forceinline__ float half_wave_sum(float x) {
-  x = dpp_add<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-  x = dpp_add<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-  x = dpp_add<0x141>(x);  // row_half_mirror
-  x = dpp_add<0x140>(x);  // row_mirror
+  x = row16_sum(x);
   // ds_swizzle bit mode on 32-lane groups: and 0x1F, or 0, xor 0x10
   return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
 }

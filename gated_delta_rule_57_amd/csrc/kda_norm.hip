@@ -33,8 +33,7 @@ __global__ void __launch_bounds__(256) output_norm_gate_kernel(const E* __restri
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  ss = row16_sum(ss);
   const float inv = rsqrtf(ss * (1.f / D) + eps);
   float y[8];
 #pragma unroll
