@@ -175,4 +175,44 @@ __device__ __forceinline__ float row16_sum(float x) {
   return dpp_add<0x140>(x);  // row_mirror
 }
 
+// X^T Y for 16 x 16 fp32 matrices both held in accumulator layout (lane (n, g),
+// element i: row 4 g + i of column n): k-step i pairs row 4 g + i of X (as the A
+// operand's column) with row 4 g + i of Y (the B operand), on fp32 MFMA.
+__device__ __forceinline__ floatx4 mm16_tn(const floatx4& x, const floatx4& y) {
+  floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[i], y[i], c, 0, 0, 0);
+  return c;
+}
+
+// (I + A)^{-1} of a strictly lower-triangular 16 x 16 fp32 block A (row-major at a,
+// row stride lda, zeros on and above the diagonal), returned in accumulator layout.
+// With N = -A nilpotent (N^16 = 0), (I + A)^{-1} = sum_{k<16} N^k =
+// (I + N)(I + N^2)(I + N^4)(I + N^8): eight 16 x 16 products on fp32 MFMA (powers
+// formed with their transposes, so that every product finds its operands in
+// accumulator layout), in place of a 16-step row-by-row substitution on 16 lanes. Its
+// rounding grows with the powers' entries, so the bf16-operand paths use it.
+__device__ __forceinline__ floatx4 unit_lower_inverse16(const float* a, int lda, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  floatx4 N, Nt;
+  const floatx4 arow = *reinterpret_cast<const floatx4*>(a + n * lda + 4 * g);  // A[n][4g + i]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    N[i] = -a[(4 * g + i) * lda + n];  // N[4g + i][n]
+    Nt[i] = -arow[i];                  // N^T[4g + i][n] = N[n][4g + i]
+  }
+  auto plus_i = [&](floatx4 x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] += (4 * g + i == n) ? 1.f : 0.f;
+    return x;
+  };
+  const floatx4 N2 = mm16_tn(Nt, N), N2t = mm16_tn(N, Nt);      // N N, (N N)^T
+  const floatx4 N4 = mm16_tn(N2t, N2), N4t = mm16_tn(N2, N2t);  // N^4, (N^4)^T
+  const floatx4 N8 = mm16_tn(N4t, N4);
+  const floatx4 E1t = plus_i(Nt), E2 = plus_i(N2), E4 = plus_i(N4), E8 = plus_i(N8);
+  const floatx4 R1t = mm16_tn(E2, E1t);  // ((I + N)(I + N^2))^T
+  const floatx4 R2t = mm16_tn(E4, R1t);  // ((I + N)(I + N^2)(I + N^4))^T
+  return mm16_tn(R2t, E8);
+}
+
 }  // namespace kda

@@ -777,8 +777,21 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   }
   __syncthreads();
 
-  // ---- B1: diagonal blocks T_II = (I + A_II)^{-1}, row by row (lane j = column j) ---
-  if (w < NSUB && lane < 16) {
+  // ---- B1: diagonal blocks T_II = (I + A_II)^{-1}: bf16 operands by the power
+  //      product on MFMA (all 64 lanes), fp32 row by row (lane j = column j) ---------
+  if constexpr (std::is_same<E, __bf16>::value) {
+    if (w < NSUB) {
+      const int o0 = 16 * w;
+      const floatx4 tb = unit_lower_inverse16(sA + o0 * LDC + o0, LDC, lane);
+      const float bn = sBeta[o0 + m];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g + ii;
+        sTd[(w * 16 + r) * 20 + m] = tb[ii];
+        sTb[(o0 + r) * LDK + o0 + m] = from_f<E>(tb[ii] * bn);
+      }
+    }
+  } else if (w < NSUB && lane < 16) {
     const int j = lane, o0 = 16 * w;
     float col[16];
 #pragma unroll

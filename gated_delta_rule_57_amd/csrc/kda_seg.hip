@@ -940,34 +940,17 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
     }
     __syncthreads();
 
-    // ---- B1: diagonal blocks T_II = (I + A_II)^{-1} by forward substitution -------
-    if (w < NSUBC && lane < 16) {
-      const int j = lane, o0 = 16 * w;
-      float col[16];
-      // rows 4 b .. 4 b + 3 of the block, the lower-triangle part only, as 16-byte
-      // broadcast reads issued before the substitution steps that use them
+    // ---- B1: diagonal blocks T_II = (I + A_II)^{-1} by the power product on fp32
+    //      MFMA, one wave per block ---------------------------------------------------
+    if (w < NSUBC) {
+      const int o0 = 16 * w;
+      const floatx4 tb = unit_lower_inverse16(sA + o0 * LDC + o0, LDC, lane);
+      const float bn = sBeta[o0 + m];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        floatx4 arow[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int q4 = 0; q4 <= b; ++q4)
-            arow[rr][q4] = *reinterpret_cast<const floatx4*>(sA + (o0 + 4 * b + rr) * LDC + o0 + 4 * q4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 4 * b + rr;
-          float val = (r == j) ? 1.f : 0.f;
-#pragma unroll
-          for (int s = 0; s < r; ++s) val -= arow[rr][s >> 2][s & 3] * col[s];
-          col[r] = val;
-        }
-      }
-      const float bj = sBeta[o0 + j];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sTd[(w * 16 + r) * 20 + j] = col[r];
-        sTb[(o0 + r) * LDK + o0 + j] = (__bf16)(col[r] * bj);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g + ii;
+        sTd[(w * 16 + r) * 20 + m] = tb[ii];
+        sTb[(o0 + r) * LDK + o0 + m] = (__bf16)(tb[ii] * bn);
       }
     }
     __syncthreads();
