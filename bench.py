@@ -138,8 +138,9 @@ def environment(torch):
            "hip": getattr(torch.version, "hip", None)}
     try:
         p = torch.cuda.get_device_properties(0)
-        env.update(gpu=p.name, gcn_arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
-                   hbm_gib=round(p.total_memory / 2**30, 1))
+        arch = getattr(p, "gcnArchName", None)
+        env.update(gpu=p.name or (arch.split(":")[0] if arch else None), gcn_arch=arch,
+                   compute_units=p.multi_processor_count, hbm_gib=round(p.total_memory / 2**30, 1))
         clk = getattr(p, "clock_rate", None)
         if clk:
             env["gpu_clock_mhz"] = round(clk / 1000)
