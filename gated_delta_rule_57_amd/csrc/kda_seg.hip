@@ -57,6 +57,10 @@ constexpr int NSUBC = 4;         // 16-row sub-chunks per chunk
 constexpr int NTHR = 512;        // threads per work-group (eight waves)
 constexpr float L2E = 1.4426950408889634f;
 constexpr float SUB_RANGE_LIMIT = 120.f;  // log2 units
+// A chunk whose total decay stays within this range (log2 units) in every channel
+// takes the direct form: x_r 2^(gh_r) >= x_r 2^-96 stays a normal number for any
+// component above 2^-30, and k_s 2^(-gh_s) <= 2^96 is far from overflow
+constexpr float DIRECT_RANGE_LIMIT = 96.f;
 constexpr int G_CHANNEL = 0, G_HEAD = 1, G_NONE = 2;
 constexpr int ST = D * D;        // floats in one 128 x 128 state
 
@@ -97,9 +101,9 @@ struct SegSmem {
   static constexpr size_t SCL = RS + (size_t)NSUBC * D * 4;         // float[NBLK + 4][128] block scales
   static constexpr size_t BETA = SCL + (size_t)(NBLK + NSUBC) * D * 4;  // float[64]
   static constexpr size_t GS = BETA + SC * 4;                       // float[64] scalar-gate cumsum
-  static constexpr size_t FLAG = GS + SC * 4;                       // int[4]
+  static constexpr size_t FLAG = GS + SC * 4;                       // int[8]: sub-chunk range flags, direct-form flag
   // chain operands, in MFMA fragment order (kda_device.h)
-  static constexpr size_t CW = al16(FLAG + 16);                     // bf16[4 rt][4 kb][64][8]  -W
+  static constexpr size_t CW = al16(FLAG + 32);                     // bf16[4 rt][4 kb][64][8]  -W
   static constexpr size_t CQ = CW + 16384;                          // bf16[4 rt][4 kb][64][8]  Q e^G
   static constexpr size_t CK = CQ + 16384;                          // bf16[8 rt][2 kb][64][8]  (K e^{g_C-G})^T
   static constexpr size_t CP = CK + 16384;                          // bf16[4 rt][2 kb][64][8]  P
@@ -508,15 +512,15 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
                      reinterpret_cast<const float*>(smem + SM::CG), reinterpret_cast<bf16x8*>(smem + SM::G),
                      reinterpret_cast<float*>(smem + SM::ON)};
 
-  // x holds the inputs of the chunk being processed; each part is reloaded with the
-  // next chunk's as soon as it has been consumed, so the loads overlap the rest of
-  // the chunk without a second register copy
+  // x holds the inputs of the chunk being processed; the decays and k, q are reloaded
+  // with the next chunk's as soon as they have been consumed, so the loads overlap the
+  // rest of the chunk without a second register copy; v is loaded at the start of its
+  // own chunk
   InRegs x;
   if (nchunks > 0) {
     const int l0 = min(SC, tok_end - tok_begin);
     load_gate<GATE>(a, x, tok_begin, l0, h, threadIdx.x);
     load_kq<PASS>(a, x, tok_begin, l0, h, threadIdx.x);
-    load_v(a, x, tok_begin, l0, h, threadIdx.x);
   }
 
   for (int ci = 0; ci < nchunks; ++ci) {
@@ -567,7 +571,7 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       }
       sBeta[t] = bt;
     }
-    if (t < NSUBC) sFlag[t] = 0;
+    if (t <= NSUBC) sFlag[t] = 0;
     if constexpr (GATE == G_CHANNEL) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -585,6 +589,9 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       if (t < SC) sGs[t] = la_row * L2E;  // zero past len
     }
     load_gate<GATE>(a, x, tokn, lenn, h, t);
+    // v of this chunk: first used after the decay and A / P phases, so its load has
+    // them to land, and it does not hold registers across the state step
+    load_v(a, x, tok0, len, h, t);
     __syncthreads();
     // k and q of this thread's rows, normalised and zeroed past the chunk's end; taken
     // where the decay operands are formed, then reloaded with the next chunk's
@@ -665,6 +672,7 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
 #pragma unroll
         for (int I = 0; I < NSUBC; ++I)
           if (!(-R[I] <= SUB_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
+        if (!(-b[NSUBC] <= DIRECT_RANGE_LIMIT)) atomicOr(&sFlag[NSUBC], 1);
         // 2^(b_I - b_{J+1}): the sum of the whole sub-chunks strictly between J and I,
         // or 2^(-R_I) on the diagonal
 #pragma unroll
@@ -693,9 +701,77 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       bool exact = false;
 #pragma unroll
       for (int I = 0; I < NSUBC; ++I) exact |= sFlag[I] != 0;
+      const bool direct = sFlag[NSUBC] == 0;  // implies !exact: -R_I <= -b_4 <= the direct range
 
       take_kq();
-      if (!exact) {
+      if (direct) {
+        // ---- P2 (direct): the whole chunk's decay is within the direct range, so
+        //      2^(gh_r - gh_s) = 2^(gh_r) 2^(-gh_s) splits with no scale table:
+        //      lhs_r = x_r 2^(gh_r) (x = k, q; also K e^G and Q e^G), rhs_s = k_s 2^(-gh_s),
+        //      gh = b_I + loc --------------------------------------------------------
+        __bf16* sRK = reinterpret_cast<__bf16*>(smem + SM::RR);  // bf16[64][LD], inside RR
+        bf16x4 lkv[4], lqv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + 16 * i;
+          const floatx4 loc = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+          const floatx4 bI = *reinterpret_cast<const floatx4*>(sBnd + i * D + ch0);
+          float qt[4];
+          bf16x4 rk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gh = bI[j] + loc[j];
+            const float eg = ex2(gh);  // >= 2^-96
+            qt[j] = qr[i][j] * eg;
+            ktr[i][j] = kr[i][j] * eg;
+            lkv[i][j] = (__bf16)ktr[i][j];
+            lqv[i][j] = (__bf16)qt[j];
+            rk[j] = (__bf16)(kr[i][j] * ex2(-gh));  // <= 2^96
+          }
+          *reinterpret_cast<bf16x4*>(sRK + r * LD + ch0) = rk;
+          if constexpr (OUTP) store4f(q_slot(r), qt);
+        }
+        __syncthreads();  // every thread has its decays: the left operands overwrite the prefix
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + 16 * i;
+          *reinterpret_cast<bf16x4*>(sLK + r * LD + ch0) = lkv[i];
+          if constexpr (OUTP) *reinterpret_cast<bf16x4*>(sLQ + r * LD + ch0) = lqv[i];
+        }
+        __syncthreads();
+        // ---- P3 (direct): the blocks straight from the bf16 operands; entries above
+        //      the diagonal (up to 2^96) are dropped by selection where A and P are taken
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+          accA[bi] = accP[bi] = zero4;
+          int I, J;
+          if (!seg_block(w, bi, I, J)) break;
+          const int rrow = 16 * I + m, srow = 16 * J + m;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 lk, lq, rhs;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int ch = 32 * kb + 16 * hh + 4 * g;
+              const bf16x4 xa = *reinterpret_cast<const bf16x4*>(sLK + rrow * LD + ch);
+              const bf16x4 xr = *reinterpret_cast<const bf16x4*>(sRK + srow * LD + ch);
+              bf16x4 xq;
+              if constexpr (OUTP) xq = *reinterpret_cast<const bf16x4*>(sLQ + rrow * LD + ch);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                lk[4 * hh + j] = xa[j];
+                if constexpr (OUTP) lq[4 * hh + j] = xq[j];
+                rhs[4 * hh + j] = xr[j];
+              }
+            }
+            mma(accA[bi], rhs, lk);
+            if constexpr (OUTP) mma(accP[bi], rhs, lq);
+          }
+          if constexpr (OUTP) emit_p(I, J, accP[bi]);
+        }
+        // (K e^{g_C - G})^T = rhs_s 2^(g_C)
+        emit_ke([&](int s, int ch) { return (float)sRK[s * LD + ch] * cG[ch]; });
+      } else if (!exact) {
         // ---- P2 (factored): Q e^G to its slots, K e^G kept, and per row
         //      lhs_r = x_r 2^(loc_r) (x = k, q) and rhs_s = k_s 2^(R_J - loc_s) --------
         bf16x4 lkv[4], lqv[4];
@@ -933,7 +1009,6 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       if (!vrow[i]) vv = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
       *reinterpret_cast<bf16x4*>(sV + r * LD + ch0) = vv;
     }
-    load_v(a, x, tokn, lenn, h, t);
     {  // the products read T's blocks (0, 1) and (2, 3) above the diagonal: zero them
       const int blk = t >> 8, e = t & 255;
       sTb[(32 * blk + (e >> 4)) * LDK + 32 * blk + 16 + (e & 15)] = (__bf16)0.f;
