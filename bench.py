@@ -113,10 +113,10 @@ def seg_plan(T, H, N=1, kernels="record"):
     pct = SEG_FIRST_PCT[kernels]
     nc = (T + CHUNK - 1) // CHUNK
     mc = N * nc
-    target = SEG_TARGET_GROUPS + (N * H * pct + 99) // 100
-    lseg = max(SEG_MIN_CHUNKS, (mc * H + target - 1) // target)
+    den = SEG_TARGET_GROUPS * 100 + N * H * pct
+    lseg = max(SEG_MIN_CHUNKS, (mc * H * 100 + den - 1) // den)
     lseg = min(lseg, mc) if mc > 0 else 1
-    l0 = max(1, (lseg * pct + 50) // 100)
+    l0 = max(1, (lseg * pct + 99) // 100)
     ns = 1 if nc <= l0 else 1 + (nc - l0 + lseg - 1) // lseg
     return lseg, l0, ns
 

@@ -1471,16 +1471,17 @@ __global__ void __launch_bounds__(1024) seg_plan_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------
 int seg_chunks_per_segment(int64_t mc, int N, int H, int first_pct) {
   // about SEG_TARGET_GROUPS work-groups per pass: the segments after the first number
-  // (mc - N l0) / lseg per head, with l0 = first_pct % of lseg
-  const int64_t target = SEG_TARGET_GROUPS + ((int64_t)N * H * first_pct + 99) / 100;
-  int64_t l = (mc * H + target - 1) / target;
+  // (mc - N l0) / lseg per head, with l0 = first_pct % of lseg, so
+  // lseg = mc H / (SEG_TARGET_GROUPS + N H first_pct / 100), rounded up
+  const int64_t den = (int64_t)SEG_TARGET_GROUPS * 100 + (int64_t)N * H * first_pct;
+  int64_t l = (mc * H * 100 + den - 1) / den;
   if (l < SEG_MIN_CHUNKS) l = SEG_MIN_CHUNKS;
   if (l > mc) l = mc > 0 ? mc : 1;
   return (int)l;
 }
 
 int seg_first_chunks(int lseg, int first_pct) {
-  const int l0 = (lseg * first_pct + 50) / 100;
+  const int l0 = (lseg * first_pct + 99) / 100;
   return l0 < 1 ? 1 : l0;
 }
 
