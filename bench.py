@@ -121,15 +121,23 @@ def seg_plan(T, H, N=1, kernels="record"):
     return lseg, l0, ns
 
 
-def seg_design_bytes(T, H):
-    """Bytes the record-fed segment-parallel state kernels read and write by
-    construction for one T-token sequence of H heads: (first pass, second pass)."""
-    lseg, l0, ns = seg_plan(T, H)
+def seg_design_bytes(T, H, kernels="record"):
+    """Bytes the segment-parallel passes read and write by construction for one T-token
+    sequence of H heads: (first pass, second pass). Record-fed: a record and o per
+    output chunk, the map parts of the record per middle chunk. Single pass: the inputs
+    and o per output chunk, the inputs but q per middle chunk."""
+    lseg, l0, ns = seg_plan(T, H, kernels=kernels)
     nc = (T + CHUNK - 1) // CHUNK
     lens = [min(l0, nc)] + [min(lseg, nc - l0 - (j - 1) * lseg) for j in range(1, ns)]
     o_per_chunk = CHUNK * 2 * D
-    first = H * (lens[0] * (SEG_OUT_READ + o_per_chunk) + sum(lens[1:ns - 1]) * SEG_MAP_READ)
-    second = H * sum(lens[1:]) * (SEG_OUT_READ + o_per_chunk)
+    if kernels == "single":
+        out_chunk = CHUNK * (IN_BYTES_PER_TOK_HEAD + 2 * D)
+        map_chunk = CHUNK * (IN_BYTES_PER_TOK_HEAD - 2 * D)
+    else:
+        out_chunk = SEG_OUT_READ + o_per_chunk
+        map_chunk = SEG_MAP_READ
+    first = H * (lens[0] * out_chunk + sum(lens[1:ns - 1]) * map_chunk)
+    second = H * sum(lens[1:]) * out_chunk
     return first, second
 
 
@@ -461,6 +469,10 @@ def main():
     ap.add_argument("--decode-per-step", type=int, default=8)
     ap.add_argument("--decode-inputs", type=int, default=256, help="distinct decode tokens, cycled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=("auto", "record", "segmented", "single"),
+                    help="prefill kernel set of the headline steps (kda_prefill_path)")
+    ap.add_argument("--extras", default="configs,paths,fused,gates,backward,dplr",
+                    help="comma-separated sections timed after the headline steps")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline steps (no configs, paths, fused, gates, backward, DPLR)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
@@ -500,7 +512,8 @@ def main():
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     B, T, H = pre.q.shape[:3]
-    ws = torch.empty(kda.workspace_size(B, T, H, 0, CHUNK, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda.workspace_size(B, T, H, 0, CHUNK, kda.KDA_BF16, path=args.path), dtype=torch.uint8,
+                     device=dev)
     o = torch.empty_like(pre.v)
     fin = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
     state = dec.initial_state.clone()
@@ -510,7 +523,8 @@ def main():
     tm = StreamTimer(torch)
 
     def prefill():
-        kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws)
+        kda.chunk_fwd(pre.q, pre.k, pre.v, pre.log_alpha, pre.beta, chunk=CHUNK, o=o, final_state=fin, workspace=ws,
+                      path=args.path)
 
     def decode():
         i = dec_i[0] % n_dec_in
@@ -550,7 +564,9 @@ def main():
     tok_heads = T * H
     kms = {n: tot / cnt for n, (tot, cnt) in timing.items() if cnt}
     src_hash = kernel_source_hash()
-    traffic = committed_profile("pmc_traffic.json", src_hash)
+    # counters of the default kernel set, and of the single pass in a file of its own
+    traffic = committed_profile("pmc_traffic.json" if args.path in ("auto", "segmented")
+                                else f"pmc_traffic_{args.path}.json", src_hash)
     mfma_prof = committed_profile("pmc_mfma.json", src_hash)
 
     # the whole prefill path against the HBM roofline, on the method's bytes
@@ -559,12 +575,16 @@ def main():
     achieved = path_bytes / (prefill_ms * 1e-3) / 1e9
     t_bound_ms = max(flops / (BF16_MFMA_PEAK_TFLOPS * 1e12), path_bytes / (HBM_PEAK_GBS * 1e9)) * 1e3
     path_kernels = [n for n in PREFILL_KERNELS if n in kms]
+    # the single pass runs under the segment kernels' timing slots; its counters are
+    # kept under names of its own
+    kernel_set = "single" if args.path == "single" else "record"
+    prof_name = {"seg_first": "single_first", "seg_second": "single_second"} if kernel_set == "single" else {}
     path_traffic = None
     if traffic:
         per = traffic.get("kernels", {})
-        names = set(path_kernels) | ({"seg_plan"} if "seg_first" in path_kernels else set())
-        if all(n in per for n in path_kernels):
-            path_traffic = round(sum(per[n]["hbm_bytes_per_launch"] for n in names if n in per), 0)
+        names = {prof_name.get(n, n) for n in path_kernels} | ({"seg_plan"} if "seg_first" in path_kernels else set())
+        if all(n in per for n in names):
+            path_traffic = round(sum(per[n]["hbm_bytes_per_launch"] for n in names), 0)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": path_traffic,
             "kernel": "prefill path (" + ", ".join(path_kernels) + ")",
@@ -574,8 +594,8 @@ def main():
     # each kernel of the path: design bytes (what it moves by construction) and counter traffic
     n_chunks = (T + CHUNK - 1) // CHUNK
     rec_moved = n_chunks * H * RECORD_MOVED_BYTES_BF16_C64
-    seg_a, seg_b = seg_design_bytes(T, H)
-    lseg, l0, ns = seg_plan(T, H)
+    seg_a, seg_b = seg_design_bytes(T, H, kernels=kernel_set)
+    lseg, l0, ns = seg_plan(T, H, kernels=kernel_set)
     design = {"intra": tok_heads * IN_BYTES_PER_TOK_HEAD + rec_moved,
               "inter": rec_moved + tok_heads * 2 * D,
               "seg_first": seg_a, "seg_second": seg_b,
@@ -595,8 +615,9 @@ def main():
             ent["design_frac_of_hbm_peak"] = round(design[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         if name in share:
             ent["algorithmic_bytes_per_launch"] = share[name]
-        if traffic and name in traffic.get("kernels", {}):
-            tb = traffic["kernels"][name]["hbm_bytes_per_launch"]
+        pname = prof_name.get(name, name)
+        if traffic and pname in traffic.get("kernels", {}):
+            tb = traffic["kernels"][pname]["hbm_bytes_per_launch"]
             ent["traffic_bytes"] = round(tb, 0)
             if name in design:
                 ent["traffic_over_design"] = round(tb / design[name], 3)
@@ -628,7 +649,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "kda_prefill_T131072_H32_bf16", "T": T, "H": H, "d": D, "chunk": CHUNK,
                    "decode_workload": "kda_decode_N256_H32_bf16", "decode_per_step": args.decode_per_step,
-                   "parallelism": "single GPU"},
+                   "prefill_path": args.path, "parallelism": "single GPU"},
         "prefill": {"ms": pst, "tokens_per_s": round(tokens_per_s, 1),
                     "path_hbm_frac": roof["frac"],
                     "kernel_ms": {n: round(kms[n], 4) for n in path_kernels},
@@ -640,18 +661,26 @@ def main():
         "kernels": kernels,
         "kernel_source_hash": src_hash,
     }
-    if not args.no_extras:
+    extras = set() if args.no_extras else {x for x in args.extras.split(",") if x}
+    if args.no_backward:
+        extras.discard("backward")
+    if args.no_dplr:
+        extras.discard("dplr")
+    if "configs" in extras:
         result["configs"] = config_timing(inputs, kda, torch, dev)
+    if "paths" in extras:
         result["paths"] = path_timing(kda, torch, pre)
+    if "fused" in extras:
         result["fused"] = fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec)
+    if "gates" in extras:
         result["gates"] = gate_timing(kda, torch, pre, dec, state, o_dec)
-        if not args.no_backward:
-            del ws
-            torch.cuda.empty_cache()
-            result["backward"] = backward_timing(inputs, kda, torch, pre)
-        if not args.no_dplr:
-            lengths = tuple(int(x) for x in args.dplr_lengths.split(",") if x)
-            result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, lengths=lengths)
+    if "backward" in extras:
+        del ws
+        torch.cuda.empty_cache()
+        result["backward"] = backward_timing(inputs, kda, torch, pre)
+    if "dplr" in extras:
+        lengths = tuple(int(x) for x in args.dplr_lengths.split(",") if x)
+        result["dplr_comparison"] = dplr_comparison(inputs, kda, torch, dev, pre, lengths=lengths)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         base, threads = cpu_baselines(inputs, pre, dec)
