@@ -57,7 +57,7 @@ SEG_MAP_READ = 16384 + 16384 + 512 + 16384
 # segment length rule of the library (SEG_TARGET_GROUPS, SEG_MIN_CHUNKS, SEG_FIRST_PCT_* in
 # kda_internal.h): the first segment of a sequence is a share of the later ones
 SEG_TARGET_GROUPS, SEG_MIN_CHUNKS = 256, 1
-SEG_FIRST_PCT = {"record": 55, "single": 80}
+SEG_FIRST_PCT = {("record", False): 55, ("single", False): 80, ("record", True): 42, ("single", True): 70}
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
@@ -107,10 +107,11 @@ def committed_profile(name, src_hash):
     return data if data.get("kernel_source_hash") == src_hash else None
 
 
-def seg_plan(T, H, N=1, kernels="record"):
+def seg_plan(T, H, N=1, kernels="record", gated=False):
     """The library's segment plan for N sequences of T tokens and H heads: (chunks per
-    segment after the first, chunks in the first, segments per sequence)."""
-    pct = SEG_FIRST_PCT[kernels]
+    segment after the first, chunks in the first, segments per sequence); gated: with
+    the output epilogue, whose output chunks cost more."""
+    pct = SEG_FIRST_PCT[(kernels, gated)]
     nc = (T + CHUNK - 1) // CHUNK
     mc = N * nc
     den = SEG_TARGET_GROUPS * 100 + N * H * pct

@@ -30,13 +30,24 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return x >= 0.f ? r : e * r;
 }
 
-// sum over the 32 lanes that share (lane & 32), i.e. one half of the wave: the
-// 16-lane row sums (row16_sum, by DPP), then one swizzle that exchanges lanes 16
-// apart. A chain of five lane permutes through the LDS unit costs several times more.
-__device__ __forceinline__ float half_wave_sum(float x) {
-  x = row16_sum(x);
-  // ds_swizzle bit mode on 32-lane groups: and 0x1F, or 0, xor 0x10
-  return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+// x + (x of the lane 16 apart within each half-wave), with no trip through the LDS
+// unit: gfx950's v_permlane16_swap exchanges the odd 16-lane rows of one register with
+// the even rows of another, so on two copies of x it leaves rows (x0, x0, x2, x2) in
+// one and (x1, x1, x3, x3) in the other, and their sum is the pair sum in every lane
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// x + (x of the lane 32 apart), by v_permlane32_swap (the upper 32 lanes of one register
+// with the lower 32 of another) on two copies of x
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// sum over the 32 lanes that share (lane & 32), i.e. one half of the wave: the 16-lane
+// row sums (row16_sum, by DPP), then the two rows of the half added
+__device__ __forceinline__ float half_wave_sum(float x) { return xor16_sum(row16_sum(x)); }
 
 }  // namespace kda

@@ -76,9 +76,13 @@ constexpr int SEG_MIN_CHUNKS = 1;
 // The first segment of a sequence is this share (percent) of the later ones: in pass
 // A its work-groups write outputs while the others only compose maps (record-fed: a
 // map chunk moves about 0.55 of an output chunk's bytes; single pass: about 0.8 of its
-// work), so both finish together.
+// work), so both finish together. With the output epilogue (RMSNorm and gate) an
+// output chunk costs more (record-fed: it also reads the gate, about 1.3 times the time
+// of a plain one; single pass: about 1.17 times), so the first segment is shorter.
 constexpr int SEG_FIRST_PCT_RECORD = 55;
 constexpr int SEG_FIRST_PCT_SINGLE = 80;
+constexpr int SEG_FIRST_PCT_RECORD_GATED = 42;
+constexpr int SEG_FIRST_PCT_SINGLE_GATED = 70;
 int seg_chunks_per_segment(int64_t max_chunks, int N, int H, int first_pct);
 int seg_first_chunks(int lseg, int first_pct);
 // Workspace: segment offsets [N+1] int32, segment table [segments] int2, entry
@@ -88,8 +92,9 @@ struct SegWs {
   int64_t max_segments;
   size_t off_seg_off, off_seg_info, off_seg_in, off_seg_map, total;
 };
-// single: the plan of the single pass (else the record-fed kernels)
-SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single);
+// single: the plan of the single pass (else the record-fed kernels); gated: with the
+// output epilogue
+SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single, bool gated);
 SegWs seg_ws_layout_for(int lseg, int l0, int64_t max_segments, int N, int H);
 // The single pass: every step of the prefill for bf16, 64-token chunks.
 hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -52,6 +52,7 @@
 // loc_r - loc_s or suf_s - suf_r, whichever subtracts the smaller sum; no factor can
 // overflow for any input. Q e^G, K e^G (exponent b_I + loc_r), K e^{g_C-G}
 // (suf_s + E_{J,n}) and e^{g_C} only need exponents <= 0 and are taken directly.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -964,7 +965,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
     if (slots > 0 && prefill_kernels(0, 64, fusion.prefill_path, mc, N) == KERNELS_RECORD_SEG) {
       // segment-parallel full-width state kernels on the records (output epilogue fused in)
       int B = cu_seqlens ? 1 : N;
-      const SegWs sl = seg_ws_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr, false);
+      const SegWs sl =
+          seg_ws_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr, false, fusion.out_gate != nullptr);
       return launch_state_seg(records, chunk_off, mc, cu_seqlens, N, T, H, initial_state, final_state, o, fusion,
                               ws + al256(l.total), sl, stream);
     }
@@ -1037,9 +1039,14 @@ hipError_t launch_forward_records(int dtype, const void* q, const void* k, const
 
 size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path) {
   const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), varlen ? num_seqs : B);
-  if (kern == KERNELS_SINGLE) return seg_ws_layout(B, T, H, num_seqs, varlen, true).total;
+  // the plans with and without the output epilogue differ: room for either
+  auto seg_bytes = [&](bool single) {
+    return std::max(seg_ws_layout(B, T, H, num_seqs, varlen, single, false).total,
+                    seg_ws_layout(B, T, H, num_seqs, varlen, single, true).total);
+  };
+  if (kern == KERNELS_SINGLE) return seg_bytes(true);
   const size_t rec = ws_layout(B, T, H, num_seqs, varlen, chunk, dtype).total;
-  if (kern == KERNELS_RECORD_SEG) return al256(rec) + seg_ws_layout(B, T, H, num_seqs, varlen, false).total;
+  if (kern == KERNELS_RECORD_SEG) return al256(rec) + seg_bytes(false);
   return rec;
 }
 

@@ -222,51 +222,55 @@ struct ChainOps {
   float* sON;        // [4 groups][64] output row sums (epilogue)
 };
 
-// One chunk of the output pass for wave half HR (see seg_pass): U~ = U - W S,
+// One chunk of the output pass for wave half hr (see seg_pass): U~ = U - W S,
 // O = (Q e^G) S + P U~, S <- Diag(e^{g_C}) S + (K e^{g_C-G})^T U~, with the output
-// RMSNorm and gate when fu.out_gate is set. S holds the wave's key rows 64 HR ..
-// 64 HR + 63 of columns col0 .. col0 + 31; au the U rows 32 HR .. of the same
+// RMSNorm and gate when fu.out_gate is set. S holds the wave's key rows 64 hr ..
+// 64 hr + 63 of columns col0 .. col0 + 31; au the U rows 32 hr .. of the same
 // columns. Two work-group barriers (three with the epilogue).
 // `mid` runs between the two barriers (the record-fed passes stage the next chunk's
 // operands there).
-// The output epilogue's gate values of one chunk for wave half HR (rows 32 HR + 16 j
-// + m, columns col0 + 16 c + 4 g .. + 3); rows past len read the chunk's first row.
-// Nothing is loaded without an output gate or for an empty chunk.
-template <int HR>
+// hr is a run-time (wave-uniform) value, not a template argument: both wave halves run
+// one copy of the code, so loads issued in `mid` or for the next chunk's gate land in
+// the same registers for every wave and stay in flight across the loop's back edge (two
+// inlined copies would be merged by register copies that wait for every load).
+// The output epilogue's gate values of one chunk (len >= 1 tokens from tok0) for wave
+// half hr (rows 32 hr + 16 j + m, columns col0 + 16 c + 4 g .. + 3); rows past len read
+// the chunk's first row. Only the passes instantiated for an output gate call it, and
+// they call it on every path, so its loads are never merged with a path without them.
 __device__ __forceinline__ void load_out_gate(bf16x4 (&zv)[2][2], const Fusion& fu, size_t HD, int h, int tok0,
                                               int len, int w, int lane) {
-  if (!fu.out_gate || len <= 0) return;
-  const int m = lane & 15, g = lane >> 4, col0 = 32 * (w & 3);
+  const int m = lane & 15, g = lane >> 4, col0 = 32 * (w & 3), hr = w >> 2;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int row = 32 * HR + 16 * j + m, rr = row < len ? row : 0;
+      const int row = 32 * hr + 16 * j + m, rr = row < len ? row : 0;
       zv[j][c] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(fu.out_gate) +
                                                  (size_t)(tok0 + rr) * HD + (size_t)h * D + col0 + 16 * c + 4 * g);
     }
 }
 
-// zv holds this chunk's gate values on entry (see load_out_gate) and the next chunk's
-// (next_len tokens from tok0 + 64) on return, so each load has a whole step to land.
-template <int HR, typename Mid>
+// OG: the output epilogue runs (fu.out_gate is set). zv holds this chunk's gate values
+// on entry (see load_out_gate); with PF it holds the next chunk's (next_len tokens from
+// tok0 + 64; this chunk's again if there is none) on return, so each load has a whole
+// step to land. nw holds the norm weight of columns col0 + 16 c + 4 g .. + 3.
+template <bool OG, bool PF, typename Mid>
 __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4 (&au)[2][2], const ChainOps& op,
                                                const Fusion& fu, __bf16* __restrict__ o, size_t HD, int h, int tok0,
-                                               int len, int next_len, bf16x4 (&zv)[2][2], int w, int lane,
-                                               Mid&& mid) {
-  constexpr int hr = HR, ho = 1 - HR;
+                                               int len, int next_len, bf16x4 (&zv)[2][2], const floatx4 (&nw)[2],
+                                               int w, int lane, Mid&& mid) {
+  const int hr = w >> 2, ho = 1 - hr;
   const int m = lane & 15, g = lane >> 4;
   const int c4 = w & 3, col0 = 32 * c4;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  const bool gated = fu.out_gate != nullptr;
-  // own state rows as operand fragments: k-blocks 2 hr, 2 hr + 1
-  bf16x8 Sb[4][2];
+  // the state's rows as operand fragments: own k-blocks 2 hr + j, the partner's 2 ho + j
+  bf16x8 Sown[2][2], Spar[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      Sb[2 * hr + j][c] = acc_pair_to_frag<__bf16>(S[2 * j][c], S[2 * j + 1][c]);
-      op.xS[((c4 * 2 + hr) * 4 + j * 2 + c) * 64 + lane] = Sb[2 * hr + j][c];
+      Sown[j][c] = acc_pair_to_frag<__bf16>(S[2 * j][c], S[2 * j + 1][c]);
+      op.xS[((c4 * 2 + hr) * 4 + j * 2 + c) * 64 + lane] = Sown[j][c];
     }
   // U~ = U - W S and O^T = S^T (Q e^G)^T for chunk rows 32 hr .. 32 hr + 31 (row tiles
   // rt = 2 hr + j); the own key rows first, the partner's after the exchange
@@ -278,7 +282,7 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
       Ut[j][c] = au[c][j];
       xt[j][c] = zero4;
     }
-  auto state_products = [&](int kb) {
+  auto state_products = [&](int kb, const bf16x8 (&sb)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rt = 2 * hr + j;
@@ -286,42 +290,51 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
       const bf16x8 qf = op.cQ[(rt * 4 + kb) * 64 + lane];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        mma(Ut[j][c], wf, Sb[kb][c]);
-        mma(xt[j][c], Sb[kb][c], qf);
+        mma(Ut[j][c], wf, sb[c]);
+        mma(xt[j][c], sb[c], qf);
       }
     }
   };
-  state_products(2 * hr);
-  state_products(2 * hr + 1);
+  state_products(2 * hr, Sown[0]);
+  state_products(2 * hr + 1, Sown[1]);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) Sb[2 * ho + j][c] = op.xS[((c4 * 2 + ho) * 4 + j * 2 + c) * 64 + lane];
+    for (int c = 0; c < 2; ++c) Spar[j][c] = op.xS[((c4 * 2 + ho) * 4 + j * 2 + c) * 64 + lane];
   mid();
-  state_products(2 * ho);
-  state_products(2 * ho + 1);
+  state_products(2 * ho, Spar[0]);
+  state_products(2 * ho + 1, Spar[1]);
   // U~ rows 32 hr .. as the operand fragment of k-block hr, for both waves of the pair:
   // written over the partner's state slot, which only this wave reads and has read
-  bf16x8 Ub[2][2];
+  bf16x8 Uown[2], Upar[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    Ub[hr][c] = acc_pair_to_frag<__bf16>(Ut[0][c], Ut[1][c]);
-    op.xS[((c4 * 2 + ho) * 4 + c) * 64 + lane] = Ub[hr][c];
+    Uown[c] = acc_pair_to_frag<__bf16>(Ut[0][c], Ut[1][c]);
+    op.xS[((c4 * 2 + ho) * 4 + c) * 64 + lane] = Uown[c];
   }
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < 2; ++c) Ub[ho][c] = op.xS[((c4 * 2 + hr) * 4 + c) * 64 + lane];
-  // O^T += U~^T P^T, causal k-blocks only
+  for (int c = 0; c < 2; ++c) Upar[c] = op.xS[((c4 * 2 + hr) * 4 + c) * 64 + lane];
+  // U~ by k-block: rows 0 .. 31 and 32 .. 63 of the chunk
+  bf16x8 U0[2], U1[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    U0[c] = hr ? Upar[c] : Uown[c];
+    U1[c] = hr ? Uown[c] : Upar[c];
+  }
+  // O^T += U~^T P^T, causal k-blocks only: k-block 0 for every row tile, k-block 1 for
+  // the row tiles of the second half
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int rt = 2 * hr + j;
+    const bf16x8 pf0 = op.cP[(rt * 2 + 0) * 64 + lane];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb > ((2 * hr + j) >> 1)) continue;
-      const bf16x8 pf = op.cP[(rt * 2 + kb) * 64 + lane];
+    for (int c = 0; c < 2; ++c) mma(xt[j][c], U0[c], pf0);
+    if (hr) {
+      const bf16x8 pf1 = op.cP[(rt * 2 + 1) * 64 + lane];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) mma(xt[j][c], Ub[kb][c], pf);
+      for (int c = 0; c < 2; ++c) mma(xt[j][c], U1[c], pf1);
     }
   }
   // S = Diag(e^{g_C}) S + (K e^{g_C-G})^T U~ for key rows 64 hr ..
@@ -333,11 +346,11 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       S[j][c] = gv * S[j][c];
-      mma(S[j][c], k0, Ub[0][c]);
-      mma(S[j][c], k1, Ub[1][c]);
+      mma(S[j][c], k0, U0[c]);
+      mma(S[j][c], k1, U1[c]);
     }
   }
-  if (gated) {
+  if constexpr (OG) {
     // RMSNorm over the row's 128 values (four column groups hold 32 each) times the gate
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -346,8 +359,7 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss += xt[j][c][i] * xt[j][c][i];
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
+      ss = xor32_sum(xor16_sum(ss));  // over the lanes of equal m
       if (g == 0) op.sON[c4 * SC + 32 * hr + 16 * j + m] = ss;
     }
     __syncthreads();
@@ -359,13 +371,20 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
       for (int q4 = 0; q4 < 4; ++q4) tot += op.sON[q4 * SC + row];
       const float inv = rsqrtf(tot * (1.f / D) + fu.norm_eps);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const floatx4 nw = *reinterpret_cast<const floatx4*>(fu.norm_weight + col0 + 16 * c + 4 * g);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xt[j][c][i] = xt[j][c][i] * inv * nw[i] * sigmoid_f((float)zv[j][c][i]);
-      }
+        for (int i = 0; i < 4; ++i) xt[j][c][i] = xt[j][c][i] * inv * nw[c][i] * sigmoid_f((float)zv[j][c][i]);
     }
-    load_out_gate<HR>(zv, fu, HD, h, tok0 + SC, next_len, w, lane);
+    if constexpr (PF) {  // one load on every path: a select of the chunk, not a branch around it
+      // the gate values are used up before the loads that overwrite them are issued (see
+      // the record prefetch of the record-fed passes)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(xt[j][c])::"memory");
+      const bool nx = next_len > 0;
+      load_out_gate(zv, fu, HD, h, nx ? tok0 + SC : tok0, nx ? next_len : len, w, lane);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -416,6 +435,17 @@ __device__ __forceinline__ void map_state_step(floatx4 (&S)[8][2], const floatx4
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) mma(S[rt][c], op.cK[(rt * 2 + kb) * 64 + lane], Ub[kb][c]);
     }
+  }
+}
+
+// The output norm weight of this wave's columns col0 + 16 c + 4 g .. + 3, held for the
+// whole pass (zero when there is no epilogue).
+template <bool LOAD>
+__device__ __forceinline__ void load_norm_weight(floatx4 (&nw)[2], const Fusion& fu, int w, int lane) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    nw[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (LOAD) nw[c] = *reinterpret_cast<const floatx4*>(fu.norm_weight + 32 * (w & 3) + 16 * c + 4 * (lane >> 4));
   }
 }
 
@@ -471,7 +501,7 @@ __device__ __forceinline__ void store_state(const floatx4 (&S)[NRS][2], float* _
 // fragments) and the other 32 rows of U~ cross through LDS. Map pass: wave w owns
 // 32 columns of [M | B] over all key rows.
 // ---------------------------------------------------------------------------
-template <int GATE, int PASS>
+template <int GATE, int PASS, bool OG>
 __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int tok_end, int nchunks,
                          const float* __restrict__ init, float* __restrict__ out) {
   using SM = SegSmem;
@@ -507,6 +537,8 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
 
   floatx4 S[NRS][2];
   init_state<NRS, OUTP>(S, init, w, lane);
+  floatx4 nw[2];
+  load_norm_weight<OG && OUTP>(nw, fu, w, lane);
   const ChainOps ops{reinterpret_cast<const bf16x8*>(smem + SM::CW), reinterpret_cast<const bf16x8*>(smem + SM::CQ),
                      reinterpret_cast<const bf16x8*>(smem + SM::CK), reinterpret_cast<const bf16x8*>(smem + SM::CP),
                      reinterpret_cast<const float*>(smem + SM::CG), reinterpret_cast<bf16x8*>(smem + SM::G),
@@ -536,25 +568,7 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
     const int len = min(SC, tok_end - tok0);
     const int tokn = tok_begin + SC * min(ci + 1, nchunks - 1);  // the next chunk (this one again at the end)
     const int lenn = min(SC, tok_end - tokn);
-    // ---- S0: row norms (prologue), log2 decays, beta -------------------------------
-    float ik[4] = {1.f, 1.f, 1.f, 1.f}, iq[4] = {1.f, 1.f, 1.f, 1.f};
-    if (fu.normalize_qk) {  // a row's 128 channels are the 32 lanes of one half-wave
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float kk = (float)x.k[i][j];
-          sk += kk * kk;
-          if constexpr (OUTP) {
-            const float qq = (float)x.q[i][j];
-            sq += qq * qq;
-          }
-        }
-        ik[i] = rsqrtf(half_wave_sum(sk) + fu.qk_eps);
-        if constexpr (OUTP) iq[i] = rsqrtf(half_wave_sum(sq) + fu.qk_eps);
-      }
-    }
+    // ---- S0: log2 decays, beta -------------------------------------------------------
     bool vrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vrow[i] = rbase + 16 * i < len;
@@ -593,10 +607,36 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
     // them to land, and it does not hold registers across the state step
     load_v(a, x, tok0, len, h, t);
     __syncthreads();
-    // k and q of this thread's rows, normalised and zeroed past the chunk's end; taken
-    // where the decay operands are formed, then reloaded with the next chunk's
+    // k and q of this thread's rows, L2-normalised (prologue) and zeroed past the
+    // chunk's end; taken where the decay operands are formed, then reloaded with the
+    // next chunk's
     float kr[4][4], qr[4][4];
     auto take_kq = [&]() {
+      // k and q are used from here on, not from the top of the chunk: a wait for them
+      // there would also wait for the previous chunk's output stores
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(x.k[i]));
+        if constexpr (OUTP) asm volatile("" : "+v"(x.q[i]));
+      }
+      float ik[4] = {1.f, 1.f, 1.f, 1.f}, iq[4] = {1.f, 1.f, 1.f, 1.f};
+      if (fu.normalize_qk) {  // a row's 128 channels are the 32 lanes of one half-wave
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sk = 0.f, sq = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float kk = (float)x.k[i][j];
+            sk += kk * kk;
+            if constexpr (OUTP) {
+              const float qq = (float)x.q[i][j];
+              sq += qq * qq;
+            }
+          }
+          ik[i] = rsqrtf(half_wave_sum(sk) + fu.qk_eps);
+          if constexpr (OUTP) iq[i] = rsqrtf(half_wave_sum(sq) + fu.qk_eps);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1111,13 +1151,8 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       // the output gate values are loaded at the step (registers here are too tight to
       // hold the next chunk's across the chunk's matrix phases)
       bf16x4 zv[2][2];
-      if (w >> 2) {
-        load_out_gate<1>(zv, fu, HD, h, tok0, len, w, lane);
-        out_state_step<1>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, w, lane, [] {});
-      } else {
-        load_out_gate<0>(zv, fu, HD, h, tok0, len, w, lane);
-        out_state_step<0>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, w, lane, [] {});
-      }
+      if constexpr (OG) load_out_gate(zv, fu, HD, h, tok0, len, w, lane);
+      out_state_step<OG, false>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, nw, w, lane, [] {});
     } else {
       map_state_step(S, au, ops, w, lane);
     }
@@ -1179,7 +1214,7 @@ __device__ __forceinline__ void load_record(RecRegs<PASS>& x, const char* __rest
     }
 }
 
-template <int PASS>
+template <int PASS, bool OG>
 __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int tok_begin, int tok_end, int nchunks,
                          const float* __restrict__ init, float* __restrict__ out) {
   using RS = RecSmem;
@@ -1191,6 +1226,8 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
   const char* head_rec = a.records + (size_t)h * a.mc * RC::BYTES;
   floatx4 S[NRS][2];
   init_state<NRS, OUTP>(S, init, w, lane);
+  floatx4 nw[2];
+  load_norm_weight<OG && OUTP>(nw, a.fu, w, lane);
   auto stage_ops = [&](int b) {
     char* st = smem + b * RS::STAGE;
     return ChainOps{reinterpret_cast<const bf16x8*>(st + RS::CW), reinterpret_cast<const bf16x8*>(st + RS::CQ),
@@ -1226,10 +1263,9 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
   };
   bf16x4 zv[2][2];  // output gate values of the chunk being stepped (epilogue)
   if (nchunks > 0) {
-    if constexpr (OUTP) {
+    if constexpr (OUTP && OG) {
       const int l0 = min(SC, tok_end - tok_begin);
-      if (w >> 2) load_out_gate<1>(zv, a.fu, HD, h, tok_begin, l0, w, lane);
-      else load_out_gate<0>(zv, a.fu, HD, h, tok_begin, l0, w, lane);
+      load_out_gate(zv, a.fu, HD, h, tok_begin, l0, w, lane);
     }
     load_record<PASS>(x, head_rec + (size_t)c_first * RC::BYTES, threadIdx.x);
     take(threadIdx.x, 0);
@@ -1251,12 +1287,18 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
     auto mid = [&] {
       take(t, b ^ 1);
       take_u(au_next, w_);
+      // the U tiles are converted before the loads that overwrite x are issued, so the
+      // loads can land in x's own registers (a conversion moved past them would keep the
+      // old x live, and the loop would then copy the loaded registers, waiting for them)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < NU; ++j) asm volatile("" : "+v"(au_next[c][j])::"memory");
       load_record<PASS>(x, head_rec + (size_t)(c_first + min(ci + 2, nchunks - 1)) * RC::BYTES, t);
     };
     if constexpr (OUTP) {
       const int next_len = ci + 1 < nchunks ? min(SC, tok_end - tok0 - SC) : 0;
-      if (w_ >> 2) out_state_step<1>(S, au, ops, a.fu, a.o, HD, h, tok0, len, next_len, zv, w_, lane_, mid);
-      else out_state_step<0>(S, au, ops, a.fu, a.o, HD, h, tok0, len, next_len, zv, w_, lane_, mid);
+      out_state_step<OG, true>(S, au, ops, a.fu, a.o, HD, h, tok0, len, next_len, zv, nw, w_, lane_, mid);
     } else {
       mid();
       map_state_step(S, au, ops, w_, lane_);
@@ -1285,7 +1327,7 @@ __device__ __forceinline__ void seq_range(const SegArgs& a, int n, int& s0, int&
 // Pass A (SECOND = false) or pass B (SECOND = true): one work-group per (segment,
 // head), heads varying fastest so that the work-groups in flight together read
 // whole token rows.
-template <int GATE, bool SECOND>
+template <int GATE, bool SECOND, bool OG>
 __global__ void __launch_bounds__(NTHR) seg_pass_kernel(SegArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[SegSmem::TOTAL];
   const int s = blockIdx.x / a.H, h = blockIdx.x - s * a.H;
@@ -1305,19 +1347,19 @@ __global__ void __launch_bounds__(NTHR) seg_pass_kernel(SegArgs a) {
     if (j == 0) {
       const float* init = a.initial_state ? a.initial_state + uh * ST : nullptr;
       float* out = ns == 1 ? (a.final_state ? a.final_state + uh * ST : nullptr) : a.seg_in + (sh + a.H) * ST;
-      seg_pass<GATE, PASS_OUT>(a, smem, h, tb, s1, cnt, init, out);
+      seg_pass<GATE, PASS_OUT, OG>(a, smem, h, tb, s1, cnt, init, out);
     } else if (j < ns - 1) {
-      seg_pass<GATE, PASS_MAP>(a, smem, h, tb, s1, cnt, nullptr, a.seg_map + sh * 2 * ST);
+      seg_pass<GATE, PASS_MAP, OG>(a, smem, h, tb, s1, cnt, nullptr, a.seg_map + sh * 2 * ST);
     }
   } else {
     if (j == 0) return;
     float* out = (j == ns - 1 && a.final_state) ? a.final_state + uh * ST : nullptr;
-    seg_pass<GATE, PASS_OUT>(a, smem, h, tb, s1, cnt, a.seg_in + sh * ST, out);
+    seg_pass<GATE, PASS_OUT, OG>(a, smem, h, tb, s1, cnt, a.seg_in + sh * ST, out);
   }
 }
 
 // Record-fed pass A / pass B, one work-group per (segment, head) as seg_pass_kernel.
-template <bool SECOND>
+template <bool SECOND, bool OG>
 __global__ void __launch_bounds__(NTHR) rec_seg_kernel(SegArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[RecSmem::TOTAL];
   const int s = blockIdx.x / a.H, h = blockIdx.x - s * a.H;
@@ -1338,14 +1380,14 @@ __global__ void __launch_bounds__(NTHR) rec_seg_kernel(SegArgs a) {
     if (j == 0) {
       const float* init = a.initial_state ? a.initial_state + uh * ST : nullptr;
       float* out = ns == 1 ? (a.final_state ? a.final_state + uh * ST : nullptr) : a.seg_in + (sh + a.H) * ST;
-      rec_pass<PASS_OUT>(a, smem, h, c_seq + c0, tb, s1, cnt, init, out);
+      rec_pass<PASS_OUT, OG>(a, smem, h, c_seq + c0, tb, s1, cnt, init, out);
     } else if (j < ns - 1) {
-      rec_pass<PASS_MAP>(a, smem, h, c_seq + c0, tb, s1, cnt, nullptr, a.seg_map + sh * 2 * ST);
+      rec_pass<PASS_MAP, OG>(a, smem, h, c_seq + c0, tb, s1, cnt, nullptr, a.seg_map + sh * 2 * ST);
     }
   } else {
     if (j == 0) return;
     float* out = (j == ns - 1 && a.final_state) ? a.final_state + uh * ST : nullptr;
-    rec_pass<PASS_OUT>(a, smem, h, c_seq + c0, tb, s1, cnt, a.seg_in + sh * ST, out);
+    rec_pass<PASS_OUT, OG>(a, smem, h, c_seq + c0, tb, s1, cnt, a.seg_in + sh * ST, out);
   }
 }
 
@@ -1498,10 +1540,11 @@ SegWs seg_ws_layout_for(int lseg, int l0, int64_t msg, int N, int H) {
   return l;
 }
 
-SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single) {
+SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single, bool gated) {
   const int N = varlen ? num_seqs : B;
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, SC);
-  const int pct = single ? SEG_FIRST_PCT_SINGLE : SEG_FIRST_PCT_RECORD;
+  const int pct = single ? (gated ? SEG_FIRST_PCT_SINGLE_GATED : SEG_FIRST_PCT_SINGLE)
+                         : (gated ? SEG_FIRST_PCT_RECORD_GATED : SEG_FIRST_PCT_RECORD);
   const int lseg = seg_chunks_per_segment(mc, N, H, pct);
   const int l0 = seg_first_chunks(lseg, pct);
   // a sequence of nc chunks has 1 + ceil((nc - l0) / lseg) segments (one if nc <= l0):
@@ -1518,10 +1561,10 @@ SegWs seg_ws_layout(int B, int T, int H, int num_seqs, bool varlen, bool single)
 }
 
 namespace {
-template <int GATE>
+template <int GATE, bool OG>
 hipError_t launch_seg_typed(const SegArgs& a, int64_t msg, bool any_multi, hipStream_t stream) {
   const unsigned grid = (unsigned)(msg * a.H);
-  hipLaunchKernelGGL((seg_pass_kernel<GATE, false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL((seg_pass_kernel<GATE, false, OG>), dim3(grid), dim3(NTHR), 0, stream, a);
   hipError_t e = hipGetLastError();
   trace_mark(stream, 8);
   if (e != hipSuccess || !any_multi) return e;
@@ -1530,7 +1573,7 @@ hipError_t launch_seg_typed(const SegArgs& a, int64_t msg, bool any_multi, hipSt
   e = hipGetLastError();
   trace_mark(stream, 9);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((seg_pass_kernel<GATE, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL((seg_pass_kernel<GATE, true, OG>), dim3(grid), dim3(NTHR), 0, stream, a);
   e = hipGetLastError();
   trace_mark(stream, 10);
   return e;
@@ -1567,7 +1610,9 @@ hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(max_segments * H);
-  hipLaunchKernelGGL((rec_seg_kernel<false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  const bool og = fusion.out_gate != nullptr;
+  if (og) hipLaunchKernelGGL((rec_seg_kernel<false, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  else hipLaunchKernelGGL((rec_seg_kernel<false, false>), dim3(grid), dim3(NTHR), 0, stream, a);
   e = hipGetLastError();
   trace_mark(stream, 8);
   if (e != hipSuccess || (int64_t)l.l0 >= mc) return e;
@@ -1576,7 +1621,8 @@ hipError_t launch_state_seg(const char* records, const int32_t* chunk_off, int64
   e = hipGetLastError();
   trace_mark(stream, 9);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rec_seg_kernel<true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  if (og) hipLaunchKernelGGL((rec_seg_kernel<true, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  else hipLaunchKernelGGL((rec_seg_kernel<true, false>), dim3(grid), dim3(NTHR), 0, stream, a);
   e = hipGetLastError();
   trace_mark(stream, 10);
   return e;
@@ -1588,7 +1634,7 @@ hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const
                               void* workspace, hipStream_t stream) {
   const bool varlen = cu_seqlens != nullptr;
   const int N = varlen ? num_seqs : B;
-  const SegWs l = seg_ws_layout(B, T, H, num_seqs, varlen, true);
+  const SegWs l = seg_ws_layout(B, T, H, num_seqs, varlen, true, fusion.out_gate != nullptr);
   const int64_t mc = max_chunks(B, T, num_seqs, varlen, SC);
   char* ws = reinterpret_cast<char*>(workspace);
   SegArgs a;
@@ -1620,9 +1666,15 @@ hipError_t launch_prefill_seg(const void* q, const void* k, const void* v, const
   if (e != hipSuccess) return e;
   // some sequence can have more than one segment unless one segment holds every chunk
   const bool any_multi = (int64_t)l.l0 < mc;
-  if (fusion.gate_kind == G_HEAD) return launch_seg_typed<G_HEAD>(a, l.max_segments, any_multi, stream);
-  if (fusion.gate_kind == G_NONE) return launch_seg_typed<G_NONE>(a, l.max_segments, any_multi, stream);
-  return launch_seg_typed<G_CHANNEL>(a, l.max_segments, any_multi, stream);
+  const bool og = fusion.out_gate != nullptr;
+  if (fusion.gate_kind == G_HEAD)
+    return og ? launch_seg_typed<G_HEAD, true>(a, l.max_segments, any_multi, stream)
+              : launch_seg_typed<G_HEAD, false>(a, l.max_segments, any_multi, stream);
+  if (fusion.gate_kind == G_NONE)
+    return og ? launch_seg_typed<G_NONE, true>(a, l.max_segments, any_multi, stream)
+              : launch_seg_typed<G_NONE, false>(a, l.max_segments, any_multi, stream);
+  return og ? launch_seg_typed<G_CHANNEL, true>(a, l.max_segments, any_multi, stream)
+            : launch_seg_typed<G_CHANNEL, false>(a, l.max_segments, any_multi, stream);
 }
 
 }  // namespace kda

@@ -100,21 +100,24 @@ def test_short_names_of_the_segment_parallel_kernels():
 def test_bench_segment_plan_matches_the_workspace_query():
     """bench.py's copy of the segment plan (a shorter first segment, then segments of
     lseg chunks) gives the segment count the library sizes its segmented workspace
-    for (per-segment maps and entry states), for both kernel sets."""
+    for (per-segment maps and entry states), for both kernel sets: room for the plan
+    with the output epilogue and the one without."""
     import bench
     from gated_delta_rule_57_amd import kda
     al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    st = 128 * 128 * 4
     for T, H in ((131072, 32), (4096, 16), (32768, 32), (64 * 40 + 37, 2), (64, 4)):
         for kernels, path in (("record", "segmented"), ("single", "single")):
-            lseg, l0, ns = bench.seg_plan(T, H, kernels=kernels)
             nc = (T + 63) // 64
-            assert 1 <= l0 <= lseg and (ns == 1 or l0 + (ns - 2) * lseg < nc <= l0 + (ns - 1) * lseg)
-            st = 128 * 128 * 4
-            seg = al(2 * 4) + al(ns * 8) + al(ns * H * st) + al(ns * H * 2 * st)
+            seg = 0
+            for gated in (False, True):
+                lseg, l0, ns = bench.seg_plan(T, H, kernels=kernels, gated=gated)
+                assert 1 <= l0 <= lseg and (ns == 1 or l0 + (ns - 2) * lseg < nc <= l0 + (ns - 1) * lseg)
+                seg = max(seg, al(2 * 4) + al(ns * 8) + al(ns * H * st) + al(ns * H * 2 * st))
             rec = al(kda.workspace_size(1, T, H, chunk=64, path="record")) if path == "segmented" else 0
             assert kda.workspace_size(1, T, H, chunk=64, path=path) - rec == seg, (T, H, kernels)
-    lseg, l0, ns = bench.seg_plan(131072, 32)
-    assert (lseg, l0, ns) == (240, 132, 9)
+    assert bench.seg_plan(131072, 32) == (240, 132, 9)
+    assert bench.seg_plan(131072, 32, gated=True) == (244, 103, 9)
 
 
 def test_mfma_summary(tmp_path):
