@@ -108,8 +108,9 @@ struct SegSmem {
   static constexpr size_t CK = CQ + 16384;                          // bf16[8 rt][2 kb][64][8]  (K e^{g_C-G})^T
   static constexpr size_t CP = CK + 16384;                          // bf16[4 rt][2 kb][64][8]  P
   static constexpr size_t CG = CP + 8192;                           // float[128] e^{g_C}
-  static constexpr size_t ON = CG + D * 4;                          // float[8][64] output row sums
-  static constexpr size_t TOTAL = ON + 8 * SC * 4;
+  static constexpr size_t ON = CG + D * 4;                          // float[4][64] output row sums
+  static constexpr size_t NW = ON + 4 * SC * 4;                     // float[128] output norm weight
+  static constexpr size_t TOTAL = NW + D * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
@@ -537,8 +538,10 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
 
   floatx4 S[NRS][2];
   init_state<NRS, OUTP>(S, init, w, lane);
-  floatx4 nw[2];
-  load_norm_weight<OG && OUTP>(nw, fu, w, lane);
+  // the output norm weight waits in LDS (registers are tight here); the first chunk's
+  // barriers order its store before the epilogue reads it
+  if (OG && OUTP && threadIdx.x < D / 4)
+    reinterpret_cast<floatx4*>(smem + SM::NW)[threadIdx.x] = reinterpret_cast<const floatx4*>(fu.norm_weight)[threadIdx.x];
   const ChainOps ops{reinterpret_cast<const bf16x8*>(smem + SM::CW), reinterpret_cast<const bf16x8*>(smem + SM::CQ),
                      reinterpret_cast<const bf16x8*>(smem + SM::CK), reinterpret_cast<const bf16x8*>(smem + SM::CP),
                      reinterpret_cast<const float*>(smem + SM::CG), reinterpret_cast<bf16x8*>(smem + SM::G),
@@ -1151,7 +1154,13 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
       // the output gate values are loaded at the step (registers here are too tight to
       // hold the next chunk's across the chunk's matrix phases)
       bf16x4 zv[2][2];
-      if constexpr (OG) load_out_gate(zv, fu, HD, h, tok0, len, w, lane);
+      floatx4 nw[2];
+      if constexpr (OG) {
+        load_out_gate(zv, fu, HD, h, tok0, len, w, lane);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          nw[c] = *reinterpret_cast<const floatx4*>(smem + SM::NW + 4 * (32 * (w & 3) + 16 * c + 4 * g));
+      }
       out_state_step<OG, false>(S, au, ops, fu, a.o, HD, h, tok0, len, 0, zv, nw, w, lane, [] {});
     } else {
       map_state_step(S, au, ops, w, lane);
