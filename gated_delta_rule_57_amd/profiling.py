@@ -22,7 +22,8 @@
 Kernel names are shortened to the library's kernel ids (plan, intra, inter, decode,
 outnorm, bwd_local, bwd_state, bwd_chunk; seg_plan, seg_first, seg_scan and
 seg_second for the segment-parallel state kernels, single_first and single_second for
-the single pass); the intra-chunk kernel's scalar-gate and
+the single pass, each with _gated appended for its output-epilogue variant); the
+intra-chunk kernel's scalar-gate and
 no-decay instantiations become intra_gdn and intra_deltanet, its 16-token-chunk
 instantiation (the backward's forward pass) intra16, and the 16-token state
 kernel inter16. The general-DPLR forward's kernels are dplr_intra and dplr_inter
@@ -74,16 +75,23 @@ def kernel_source_hash(root=None):
 _GATE_ARG = re.compile(r"intra_kernel(?:I\w*?Li(\d+)ELi(\d)E|<[^>]*,\s*(\d+),\s*(\d)>)")
 
 
-# the SECOND flag of the segment-parallel pass kernels (..Lb1E.. / ..true>): the later
-# segments' pass
-_SECOND = re.compile(r"(?:Lb1E|true>)")
+# the segment-parallel pass kernels' template flags, mangled (..Lb1E..) or demangled
+# (<true, ..>): the second pass (the later segments), then the output-epilogue variant
+# (absent from names of kernels built without it)
+_PASS_FLAGS = {
+    "seg": re.compile(r"rec_seg_kernel(?:ILb([01])E(?:Lb([01])E)?|<(true|false)(?:, (true|false))?>)"),
+    "single": re.compile(r"seg_pass_kernel(?:ILi\d+ELb([01])E(?:Lb([01])E)?|<\d+, (true|false)(?:, (true|false))?>)"),
+}
 
 
 def short_name(name):
     for key, short in KERNELS:
         if key in name:
             if short in ("seg", "single"):
-                return short + ("_second" if _SECOND.search(name) else "_first")
+                m = _PASS_FLAGS[short].search(name)
+                second = bool(m) and (m.group(1) == "1" or m.group(3) == "true")
+                gated = bool(m) and (m.group(2) == "1" or m.group(4) == "true")
+                return short + ("_second" if second else "_first") + ("_gated" if gated else "")
             if short == "intra":
                 m = _GATE_ARG.search(name)
                 chunk = (m.group(1) or m.group(3)) if m else None

@@ -95,6 +95,14 @@ def test_short_names_of_the_segment_parallel_kernels():
     assert s("_ZN3kda15seg_pass_kernelILi0ELb0EEEvNS_7SegArgsE") == "single_first"
     assert s("_ZN3kda15seg_pass_kernelILi0ELb1EEEvNS_7SegArgsE") == "single_second"
     assert s("void kda::seg_pass_kernel<1, false>(kda::SegArgs)") == "single_first"
+    # with the output-epilogue flag after the pass flag
+    assert s("_ZN3kda12_GLOBAL__N_114rec_seg_kernelILb1ELb0EEEvNS0_7SegArgsE") == "seg_second"
+    assert s("_ZN3kda12_GLOBAL__N_114rec_seg_kernelILb0ELb1EEEvNS0_7SegArgsE") == "seg_first_gated"
+    assert s("void kda::(anonymous namespace)::rec_seg_kernel<false, false>(kda::SegArgs)") == "seg_first"
+    assert s("void kda::(anonymous namespace)::rec_seg_kernel<true, true>(kda::SegArgs)") == "seg_second_gated"
+    assert s("_ZN3kda12_GLOBAL__N_115seg_pass_kernelILi0ELb1ELb0EEEvNS0_7SegArgsE") == "single_second"
+    assert s("_ZN3kda12_GLOBAL__N_115seg_pass_kernelILi2ELb0ELb1EEEvNS0_7SegArgsE") == "single_first_gated"
+    assert s("void kda::(anonymous namespace)::seg_pass_kernel<0, true, true>(kda::SegArgs)") == "single_second_gated"
 
 
 def test_bench_segment_plan_matches_the_workspace_query():
