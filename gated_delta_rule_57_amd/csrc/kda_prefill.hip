@@ -68,6 +68,10 @@ namespace {
 
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float DIAG_RANGE_LIMIT = 120.f;  // log2 units
+// A bf16 64-token chunk whose total decay stays within this range (log2 units) in every
+// channel takes the direct form: x_r 2^(gh_r) >= x_r 2^-96 stays a normal number for any
+// component above 2^-30, and k_s 2^(-gh_s) <= 2^96 is far from overflow
+constexpr float DIRECT_RANGE_LIMIT = 96.f;
 
 // decay granularity (kda_fusion.gate_kind): one per key channel (KDA), one per
 // (token, head) (Gated DeltaNet), none (DeltaNet)
@@ -120,8 +124,9 @@ struct Smem {
   static constexpr size_t SCL = BND + (size_t)(NSUB + 1) * D * 4;  // float[NSCALE][D]
   static constexpr size_t BETA = SCL + (size_t)NSCALE * D * 4;     // float[CK]
   static constexpr size_t NRM = BETA + (size_t)CK * 4;            // float[2][CK] prologue scales of k, q
-  static constexpr size_t FLAG = NRM + (size_t)2 * CK * 4;        // int[NSUB]
-  static constexpr size_t TOTAL = al16(FLAG + 4 * NSUB);
+  static constexpr size_t FLAG = NRM + (size_t)2 * CK * 4;        // int[NSUB + 1]: range flags, direct-form flag
+  static constexpr size_t GAM = al16(FLAG + 4 * (NSUB + 1));      // float[D] e^{g_C} (direct form)
+  static constexpr size_t TOTAL = GAM + (size_t)D * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
@@ -298,7 +303,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
     }
     sBeta[t] = bt;
   }
-  if (t < NSUB) sFlag[t] = 0;
+  if (t <= NSUB) sFlag[t] = 0;
   // Rows past len are zeroed and (prologue on raw inputs) q and k rows L2-normalised
   // where they are first needed, after the decay phases: nothing before the first
   // barrier waits for the q, k and v loads. A row's 128 channels are spread over the
@@ -436,9 +441,11 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
     for (int I = 0; I <= NSUB; ++I) sBnd[I * D + t] = bnd[I];
     rec_gamma[t] = fast_exp2(bnd[NSUB]);
+    reinterpret_cast<float*>(smem + SM::GAM)[t] = fast_exp2(bnd[NSUB]);
 #pragma unroll
     for (int I = 0; I < NSUB; ++I)
       if (!(-R[I] <= DIAG_RANGE_LIMIT)) atomicOr(&sFlag[I], 1);
+    if (!(-bnd[NSUB] <= DIRECT_RANGE_LIMIT)) atomicOr(&sFlag[NSUB], 1);
     // block scales 2^(E_IJ): sums of the whole sub-chunks strictly between J and I
     // (<= 1), 2^(-R_I) on the diagonal (used only while -R_I <= the limit); then
     // 2^(R_{J+1} + ... + R_{n-1}) for the chunk end
@@ -463,9 +470,84 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   bool exact = false;  // some diagonal block exceeds the range limit: per-element path
 #pragma unroll
   for (int I = 0; I < NSUB; ++I) exact |= sFlag[I] != 0;
+  // the whole chunk within the direct range (implies !exact: -R_I <= -b_n <= the range)
+  constexpr bool HAS_DIRECT = std::is_same<E, __bf16>::value && C == 64;
+  const bool direct = HAS_DIRECT && sFlag[NSUB] == 0;
   prep_rows();
 
-  if (!exact) {
+  if (direct) {
+    // ---- P2 (direct): the chunk's decay is within the direct range, so
+    //      2^(gh_r - gh_s) = 2^(gh_r) 2^(-gh_s) splits with no scale table:
+    //      lhs_r = x_r 2^(gh_r) (x = k, q: also K e^G and Q e^G), rhs_s = k_s 2^(-gh_s),
+    //      gh = b_I + loc ------------------------------------------------------------
+    E* sLK = reinterpret_cast<E*>(smem + SM::LK);
+    E* sLQ = reinterpret_cast<E*>(smem + SM::LQ);
+    E* sRK = reinterpret_cast<E*>(smem + SM::RR);  // E[C][LD], inside RR
+    V4 lkv[RPT], lqv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i, I = r >> 4;
+      const floatx4 loc = *reinterpret_cast<const floatx4*>(sG + r * GLD + ch0);
+      const floatx4 b0 = *reinterpret_cast<const floatx4*>(sBnd + I * D + ch0);
+      float qt[4];
+      V4 rk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gh = b0[j] + loc[j];
+        const float eg = fast_exp2(gh);  // >= 2^-96
+        qt[j] = qr[i][j] * eg;
+        ktr[i][j] = kr[i][j] * eg;
+        lkv[i][j] = from_f<E>(ktr[i][j]);
+        lqv[i][j] = from_f<E>(qt[j]);
+        rk[j] = from_f<E>(kr[i][j] * fast_exp2(-gh));  // <= 2^96 |k|
+      }
+      *reinterpret_cast<V4*>(sRK + r * LD + ch0) = rk;
+      const int kb = ch0 >> 5, co = ch0 & 31;
+      const int fg = (co & 15) >> 2, fh = co >> 4;
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+    }
+    __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rbase + 8 * i;
+      *reinterpret_cast<V4*>(sLK + r * LD + ch0) = lkv[i];
+      *reinterpret_cast<V4*>(sLQ + r * LD + ch0) = lqv[i];
+    }
+    __syncthreads();
+    // ---- P3 (direct): the blocks straight from the operands; entries above the
+    //      diagonal (up to 2^96 |x| |k|) are dropped where A and P are taken
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      accA[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accP[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      int I, J;
+      if (!wave_block<NSUB>(w, bi, I, J)) break;
+      const int rrow = 16 * I + m, srow = 16 * J + m;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        FragT lk, lq, rhs;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ch = 32 * kb + 16 * hh + 4 * g;
+          const V4 a = *reinterpret_cast<const V4*>(sLK + rrow * LD + ch);
+          const V4 bq = *reinterpret_cast<const V4*>(sLQ + rrow * LD + ch);
+          const V4 rv = *reinterpret_cast<const V4*>(sRK + srow * LD + ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            lk[4 * hh + j] = a[j];
+            lq[4 * hh + j] = bq[j];
+            rhs[4 * hh + j] = rv[j];
+          }
+        }
+        mma(accA[bi], rhs, lk);
+        mma(accP[bi], rhs, lq);
+      }
+      emit_p(I, J, accP[bi]);
+    }
+    // (K e^{g_C - G})^T = rhs_s 2^(g_C) to the record
+    const float* sGam = reinterpret_cast<const float*>(smem + SM::GAM);
+    emit_ke([&](int s, int ch) { return to_f(sRK[s * LD + ch]) * sGam[ch]; });
+  } else if (!exact) {
     // ---- P2 (factored path): Q e^G to the record, K e^G kept for B0, and per row
     //      the operands of every A / P block:
     //        lhs_r = x_r 2^(loc_r)    (x = k or q)
