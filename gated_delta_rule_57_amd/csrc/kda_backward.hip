@@ -199,23 +199,51 @@ __device__ __forceinline__ typename Frag<E>::T rows_frag(int g, F f) {
   return x;
 }
 
-template <typename E, bool WANT_P, typename KT>
-__device__ void local_forward(LocalLds<KT>& L, const E* __restrict__ q, const E* __restrict__ k,
-                              const float* __restrict__ log_alpha, const float* __restrict__ beta, int tok0, int len,
-                              int h, int H, int t) {
-  typedef typename Frag<E>::T FragT;
+// The chunk inputs local_forward starts from, as this thread loads them (row RowMap(t).r,
+// channels c0 .. c0 + 7; rows past len read the chunk's first row and are zeroed when
+// stored; beta of row t < 16): loaded apart from their use, so that a kernel can issue
+// them together with its other loads.
+template <typename E>
+struct LocalIn {
+  typename Vec4<E>::T k[2], q[2];
+  floatx4 la[2];
+  float beta;
+};
+template <typename E>
+__device__ __forceinline__ void local_load(LocalIn<E>& in, const E* __restrict__ q, const E* __restrict__ k,
+                                           const float* __restrict__ log_alpha, const float* __restrict__ beta,
+                                           int tok0, int len, int h, int H, int t) {
+  typedef typename Vec4<E>::T V4;
   const size_t HD = (size_t)H * D;
+  const RowMap rm(t);
+  const size_t off = (size_t)tok0 * HD + (size_t)h * D + (size_t)(rm.r < len ? rm.r : 0) * HD + rm.c0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    in.k[u] = *reinterpret_cast<const V4*>(k + off + 4 * u);
+    in.q[u] = *reinterpret_cast<const V4*>(q + off + 4 * u);
+    in.la[u] = *reinterpret_cast<const floatx4*>(log_alpha + off + 4 * u);
+  }
+  in.beta = 0.f;
+  if (t < BC && t < len) in.beta = beta[(size_t)(tok0 + t) * H + h];
+}
+
+template <typename E, bool WANT_P, typename KT>
+__device__ void local_forward_in(LocalLds<KT>& L, const LocalIn<E>& in, int len, int t) {
+  typedef typename Frag<E>::T FragT;
   const RowMap rm(t);
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   {
-    const size_t base = (size_t)tok0 * HD + (size_t)h * D;
-    copy8(k + base, HD, rm.r, len, rm.c0, &L.K[rm.r][rm.c0]);
-    copy8(q + base, HD, rm.r, len, rm.c0, &L.Q[rm.r][rm.c0]);
-    float x[8];
-    load8(log_alpha + base, HD, rm.r, len, rm.c0, x);
+    const bool valid = rm.r < len;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) L.G[rm.r][rm.c0 + i] = x[i];
-    if (t < BC) L.beta[t] = t < len ? beta[(size_t)(tok0 + t) * H + h] : 0.f;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = rm.c0 + 4 * u + i;
+        L.K[rm.r][c] = valid ? from_f<KT>(to_f(in.k[u][i])) : from_f<KT>(0.f);
+        L.Q[rm.r][c] = valid ? from_f<KT>(to_f(in.q[u][i])) : from_f<KT>(0.f);
+        L.G[rm.r][c] = valid ? in.la[u][i] : 0.f;
+      }
+    if (t < BC) L.beta[t] = in.beta;
     if (t == 0) L.exact = 0;
   }
   __syncthreads();
@@ -296,6 +324,15 @@ __device__ void local_forward(LocalLds<KT>& L, const E* __restrict__ q, const E*
     }
   }
   __syncthreads();
+}
+
+template <typename E, bool WANT_P, typename KT>
+__device__ void local_forward(LocalLds<KT>& L, const E* __restrict__ q, const E* __restrict__ k,
+                              const float* __restrict__ log_alpha, const float* __restrict__ beta, int tok0, int len,
+                              int h, int H, int t) {
+  LocalIn<E> in;
+  local_load(in, q, k, log_alpha, beta, tok0, len, h, H, t);
+  local_forward_in<E, WANT_P>(L, in, len, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,29 +747,53 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
   const E* dUt = dut + cix * BC * D;
   const RowMap rm(t);
 
+  // Every global load of the chunk is issued here, before anything waits for one: the
+  // local forward's inputs, the v and dU~ rows, and (bf16: they fit in registers) the
+  // operands of the state products, so the chunk pays one memory latency, not three.
+  // (raw loads, converted where they are stored: a conversion next to its load would
+  // wait for it, and for every load issued before it)
+  typedef typename Vec4<E>::T V4;
+  LocalIn<E> lin;
+  local_load(lin, q, k, log_alpha, beta, tok0, len, h, H, t);
+  V4 xv[2], xdu[2];
   {
-    float x[8];
-    load8(v + rowbase, HD, rm.r, len, rm.c0, x);
+    const size_t vo = rowbase + (size_t)(rm.r < len ? rm.r : 0) * HD + rm.c0;  // rows past len zeroed below
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S.V[rm.r][rm.c0 + i] = x[i];
-    load4f(dUt + row_tile_index(rm.r, rm.c0), x);
-    load4f(dUt + row_tile_index(rm.r, rm.c0 + 4), x + 4);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) S.dU[rm.r][rm.c0 + i] = x[i];
+    for (int u = 0; u < 2; ++u) {
+      xv[u] = *reinterpret_cast<const V4*>(v + vo + 4 * u);
+      xdu[u] = *reinterpret_cast<const V4*>(dUt + row_tile_index(rm.r, rm.c0 + 4 * u));
+    }
   }
-  local_forward<E, false>(L, q, k, log_alpha, beta, tok0, len, h, H, t);
-
-  // ---- state products: wave w forms channel tiles 2w and 2w+1 of
-  //      X1 = dO S0^T, X2 = dU~ S0^T, X3 = U~ dS_C^T, and dgamma = rowsum(dS_C o S0)
-  floatx4 x1r[2], x3r[2];
-  {
-    FragT a1[4], a2[4], a3[4];
+  constexpr bool HOIST = std::is_same<E, __bf16>::value;
+  // state-product operands: rows of dO, U~ and dU~ (A), and the 16 x 16 tiles of S0 and
+  // dS_C over row 16 nt + m, columns 32 kb + koff(g, s) (B; tiles (nt, 2 kb), (nt, 2 kb + 1))
+  FragT a1[4], a2[4], a3[4], bsf[2][4], bdf[2][4];
+  auto load_ops = [&] {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       a1[kb] = m < len ? frag_rowk<E>(dout + rowbase, (int)HD, m, 32 * kb, g) : zero_frag<E>();
       a2[kb] = tile_frag<E, 1>(dUt, 0, kb, lane);
       a3[kb] = tile_frag<E, 1>(Ut, 0, kb, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bsf[j][kb] = tile_frag<E, 8>(S0, 2 * w + j, kb, lane);
+        bdf[j][kb] = tile_frag<E, 8>(dSC, 2 * w + j, kb, lane);
+      }
     }
+  };
+  if constexpr (HOIST) load_ops();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    S.V[rm.r][rm.c0 + i] = rm.r < len ? to_f(xv[i >> 2][i & 3]) : 0.f;
+    S.dU[rm.r][rm.c0 + i] = to_f(xdu[i >> 2][i & 3]);
+  }
+  local_forward_in<E, false>(L, lin, len, t);
+
+  // ---- state products: wave w forms channel tiles 2w and 2w+1 of
+  //      X1 = dO S0^T, X2 = dU~ S0^T, X3 = U~ dS_C^T, and dgamma = rowsum(dS_C o S0)
+  floatx4 x1r[2], x3r[2];
+  {
+    if constexpr (!HOIST) load_ops();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nt = 2 * w + j;
@@ -740,9 +801,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       float dg = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        // row 16 nt + m over columns 32 kb + koff(g, s): tiles (nt, 2 kb) and (nt, 2 kb + 1)
-        const FragT bs = tile_frag<E, 8>(S0, nt, kb, lane);
-        const FragT bd = tile_frag<E, 8>(dSC, nt, kb, lane);
+        const FragT bs = bsf[j][kb];
+        const FragT bd = bdf[j][kb];
         mma(x1, a1[kb], bs);
         mma(x2, a2[kb], bs);
         mma(x3, a3[kb], bd);
