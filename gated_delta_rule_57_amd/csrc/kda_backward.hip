@@ -164,6 +164,7 @@ struct LocalLds {
   float M[BC][LDS16], T[BC][LDS16], Pm[BC][LDS16];
   float beta[BC];
   float bref[D];
+  alignas(16) float Ta[BC][20];  // diag(beta) M, the operand of the MFMA inverse (16-byte rows)
   int exact;
 };
 
@@ -311,7 +312,18 @@ __device__ void local_forward_in(LocalLds<KT>& L, const LocalIn<E>& in, int len,
     }
   }
   __syncthreads();
-  if (t < BC) {  // T = (I + A)^-1 by forward substitution, one column per thread, in registers
+  if constexpr (std::is_same<E, __bf16>::value) {
+    // T = (I + A)^-1 by the power product on fp32 MFMA (kda_device.h), one wave: A =
+    // diag(beta) M to Ta, then T from it in accumulator layout (lane (m, g) holds rows
+    // 4 g .. 4 g + 3 of column m); the wave's LDS accesses run in order
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.Ta[4 * g + i][m] = L.beta[4 * g + i] * L.M[4 * g + i][m];
+      const floatx4 tb = unit_lower_inverse16(&L.Ta[0][0], 20, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.T[4 * g + i][m] = tb[i];
+    }
+  } else if (t < BC) {  // T = (I + A)^-1 by forward substitution, one column per thread, in registers
     const int cc = t;
     float tc[BC];
 #pragma unroll
