@@ -821,8 +821,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
 #pragma unroll
         for (int s = 0; s < 8; ++s) dg += to_f(bs[s]) * to_f(bd[s]);
       }
-      dg += __shfl_xor(dg, 16);
-      dg += __shfl_xor(dg, 32);
+      dg = xor32_sum(xor16_sum(dg));
       if (g == 0) S.dgam[16 * nt + m] = dg;
       x1r[j] = x1;
       x3r[j] = x3;
@@ -955,13 +954,17 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     // m + 16 g in order), plus the terms of g_C (the last row): sum_r K e^{g_C-G}
     // terms and dgamma e^{g_C}, which every row's sum includes
     const float blk = dgr[0] + dgr[1] + dgr[2] + dgr[3];
-    kexs += __shfl_xor(kexs, 16);
-    kexs += __shfl_xor(kexs, 32);
-    float above = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const float b = __shfl(blk, m + 16 * gg);
-      if (gg > g) above += b;
+    kexs = xor32_sum(xor16_sum(kexs));
+    // the row blocks below this lane's (lanes m + 16 gg, gg > g), by lane swaps: the
+    // other row of this row's pair, then the other pair's sum
+    float above;
+    {
+      const unsigned u = __float_as_uint(blk);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 2p, 2p + 1
+      const float e0 = __uint_as_float(r16[0]), e1 = __uint_as_float(r16[1]);
+      const unsigned ps = __float_as_uint(e0 + e1);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(ps, ps, false, false);  // pairs 0 and 1
+      above = ((g & 1) ? 0.f : e1) + (g < 2 ? __uint_as_float(r32[1]) : 0.f);
     }
     float run = above + kexs + S.dgam[ch] * exp2_hw(gl);
 #pragma unroll

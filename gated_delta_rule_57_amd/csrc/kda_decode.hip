@@ -42,8 +42,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
   for (int i = 0; i < 16; ++i)
     srow[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (size_t)(16 * rg + i) * D + 4 * cg));
 
-  // k^T k, q^T q and k^T q over the 128 channels: wave-level tree reductions in
-  // waves 0 and 1, combined through LDS
+  // k^T k, q^T q and k^T q over the 128 channels: wave-level reductions in waves 0
+  // and 1, combined through LDS
   float kk = 0.f, qq = 0.f, a = 0.f;
   if (t < D) {
     // decay: per key channel, one per (sequence, head), or none (alpha = 1)
@@ -54,13 +54,10 @@ __global__ void __launch_bounds__(256) decode_kernel(const E* __restrict__ q, co
     a = __expf(la);
     kk = to_f(k[nh * D + t]);
     qq = to_f(q[nh * D + t]);
-    float pk = kk * kk, pq = qq * qq, pkq = kk * qq;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      pk += __shfl_xor(pk, off, 64);
-      pq += __shfl_xor(pq, off, 64);
-      pkq += __shfl_xor(pkq, off, 64);
-    }
+    // wave sums by DPP inside 16-lane rows and lane swaps across them (no LDS trips)
+    const float pk = xor32_sum(xor16_sum(row16_sum(kk * kk)));
+    const float pq = xor32_sum(xor16_sum(row16_sum(qq * qq)));
+    const float pkq = xor32_sum(xor16_sum(row16_sum(kk * qq)));
     if ((t & 63) == 0) {
       s_red[t >> 6][0] = pk;
       s_red[t >> 6][1] = pq;

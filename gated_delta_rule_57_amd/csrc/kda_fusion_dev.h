@@ -30,22 +30,6 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return x >= 0.f ? r : e * r;
 }
 
-// x + (x of the lane 16 apart within each half-wave), with no trip through the LDS
-// unit: gfx950's v_permlane16_swap exchanges the odd 16-lane rows of one register with
-// the even rows of another, so on two copies of x it leaves rows (x0, x0, x2, x2) in
-// one and (x1, x1, x3, x3) in the other, and their sum is the pair sum in every lane
-__device__ __forceinline__ float xor16_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// x + (x of the lane 32 apart), by v_permlane32_swap (the upper 32 lanes of one register
-// with the lower 32 of another) on two copies of x
-__device__ __forceinline__ float xor32_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 // sum over the 32 lanes that share (lane & 32), i.e. one half of the wave: the 16-lane
 // row sums (row16_sum, by DPP), then the two rows of the half added
 __device__ __forceinline__ float half_wave_sum(float x) { return xor16_sum(row16_sum(x)); }
