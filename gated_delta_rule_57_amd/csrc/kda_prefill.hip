@@ -278,26 +278,41 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 
   // ---- P1: every load of the chunk in flight at once (rows past len read row 0 and
   //          are zeroed), then log2-domain decays into sG ----------------------------
+  // The decays and beta are issued first and k, q, v after a compiler fence: memory
+  // counters count in issue order, so the decay phases wait for the decays only, and
+  // k, q, v (raw, converted where first used) land while those phases run.
   float kr[RPT][4], qr[RPT][4], vr[RPT][4];
+  typename Vec4<E>::T kraw[RPT], qraw[RPT], vraw[RPT];
   floatx4 la[RPT];
+  auto row_off = [&](int i) {
+    const int r = rbase + 8 * i;
+    return (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D + ch0;
+  };
+  if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) la[i] = *reinterpret_cast<const floatx4*>(log_alpha + row_off(i));
+  }
+  float braw = 0.f, lraw = 0.f;
+  if (t < CK && t < len) {
+    braw = beta[(size_t)(tok0 + t) * H + h];
+    if constexpr (GATE == GATE_HEAD) lraw = log_alpha[(size_t)(tok0 + t) * H + h];
+  }
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + 8 * i;
-    const int rr = r < len ? r : 0;
-    const size_t off = (size_t)(tok0 + rr) * HD + (size_t)h * D + ch0;
-    if constexpr (GATE == GATE_CHANNEL) la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
-    load4f(k + off, kr[i]);
-    load4f(q + off, qr[i]);
-    load4f(v + off, vr[i]);
+    const size_t off = row_off(i);
+    kraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(k + off);
+    qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
+    vraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(v + off);
   }
   float la_row = 0.f;  // scalar gate: log decay of row t (t < CK), natural-log units
   if (t < CK) {
     float bt = 0.f;
     if (t < len) {
-      bt = beta[(size_t)(tok0 + t) * H + h];
+      bt = braw;
       if (fu.beta_preactivation) bt = sigmoid_f(bt);
       if constexpr (GATE == GATE_HEAD) {
-        la_row = log_alpha[(size_t)(tok0 + t) * H + h];
+        la_row = lraw;
         if (fu.gate_preactivation) la_row = -softplus_f(la_row);
       }
     }
@@ -309,6 +324,16 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   // barrier waits for the q, k and v loads. A row's 128 channels are spread over the
   // 32 lanes of one half-wave (4 each), so its squared norm is a half-wave sum.
   auto prep_rows = [&] {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      asm volatile("" : "+v"(kraw[i]), "+v"(qraw[i]), "+v"(vraw[i]));  // converted here, not earlier
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kr[i][j] = to_f(kraw[i][j]);
+        qr[i][j] = to_f(qraw[i][j]);
+        vr[i][j] = to_f(vraw[i][j]);
+      }
+    }
     if (fu.normalize_qk) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
