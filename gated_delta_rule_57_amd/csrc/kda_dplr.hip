@@ -159,13 +159,20 @@ __global__ void __launch_bounds__(DTHREADS) dplr_intra_kernel(const E* __restric
   float* rec_gamma = reinterpret_cast<float*>(rec_base + RC::GAMMA_BYTES);
 
   // ---- P1: all loads in flight (rows past len read row 0 and are zeroed at use) --
+  //      the decays first, behind a compiler fence: memory counters count in issue
+  //      order, so the decay phases then wait for the decays only
   V4 qv[RPT], kv[RPT], vv[RPT], av[RPT], bv[RPT];
   floatx4 la[RPT];
+  auto row_off = [&](int i) {
+    const int r = rbase + RG * i;
+    return (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D + ch0;
+  };
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) la[i] = *reinterpret_cast<const floatx4*>(log_alpha + row_off(i));
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rbase + RG * i;
-    const size_t off = (size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D + ch0;
-    la[i] = *reinterpret_cast<const floatx4*>(log_alpha + off);
+    const size_t off = row_off(i);
     qv[i] = *reinterpret_cast<const V4*>(q + off);
     kv[i] = *reinterpret_cast<const V4*>(k + off);
     vv[i] = *reinterpret_cast<const V4*>(v + off);
