@@ -148,7 +148,8 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
 // The first part of the forward pass at BWD_CHUNK-token chunks, for the backward:
 // the chunk plan and the per-(head, chunk) records, in a workspace laid out by
 // prefill_ws_layout(..., BWD_CHUNK, dtype). The backward launches the forward
-// state pass (chunk-entry states and U~) itself.
+// state pass (chunk-entry states and U~) itself. The records hold what that pass
+// reads only: their Q e^G and P slots are not written.
 hipError_t launch_forward_records(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
                                   const float* beta, const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
                                   void* workspace, hipStream_t stream);

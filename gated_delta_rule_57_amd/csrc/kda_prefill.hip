@@ -231,8 +231,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 //   B1  diagonal 16 x 16 blocks of T = (I + A)^{-1} by forward substitution
 //   B2  off-diagonal blocks of T, one block column per wave, by fp32 MFMA
 //   B3  W = T diag(beta) K e^G (stored as -W) and U = T diag(beta) V
+// STATE_ONLY: the record for a state pass that forms no outputs (the backward's
+// forward pass): q is not read and Q e^G and P are not stored (their record slots
+// stay unwritten); every other part is the same. Launched without the prologue.
 // ---------------------------------------------------------------------------
-template <typename E, int C, int GATE>
+template <typename E, int C, int GATE, bool STATE_ONLY = false>
 __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const float* __restrict__ log_alpha,
                                                     const float* __restrict__ beta,
@@ -302,7 +305,12 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   for (int i = 0; i < RPT; ++i) {
     const size_t off = row_off(i);
     kraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(k + off);
-    qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
+    if constexpr (STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qraw[i][j] = from_f<E>(0.f);
+    } else {
+      qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
+    }
     vraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(v + off);
   }
   float la_row = 0.f;  // scalar gate: log decay of row t (t < CK), natural-log units
@@ -385,6 +393,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= 16 * I + m) ? acc[ii] : 0.f;
     E* dst = rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8;
+    if constexpr (STATE_ONLY) return;
     if (J & 1)
       store_frag<E>(dst, acc_pair_to_frag<E>(p_lo, pv));
     else if (J == I)
@@ -529,7 +538,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       *reinterpret_cast<V4*>(sRK + r * LD + ch0) = rk;
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
 #pragma unroll
@@ -606,7 +615,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       *reinterpret_cast<floatx4*>(sRR + r * GLD + ch0) = rr;
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
 #pragma unroll
@@ -669,7 +678,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     // raw (prologue-scaled) k (which 0) or q (which 1) of chunk row r, channels ch .. ch + 3;
     // zero past len
@@ -806,7 +815,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       store4f(sQ + r * LD + ch0, qr[i]);
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();
     // ---- P3 (scalar): raw block products, then the pair decay per element ------
@@ -1120,7 +1129,7 @@ hipError_t launch_records_typed(const void* q, const void* k, const void* v, con
   if (e != hipSuccess) return e;
   if (mc > 0) {
     const Fusion plain{};
-    hipLaunchKernelGGL((intra_kernel<E, C, GATE_CHANNEL>), dim3((unsigned)(mc * H)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((intra_kernel<E, C, GATE_CHANNEL, true>), dim3((unsigned)(mc * H)), dim3(256), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
                        records, plain);
     e = hipGetLastError();
