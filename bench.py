@@ -61,14 +61,15 @@ SEG_FIRST_PCT = {("record", False): 55, ("single", False): 80, ("record", True):
 # one decode (sequence, head): fp32 state read + written, q, k, v bf16, log_alpha fp32, beta, o bf16
 DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 
-# backward (16-token chunks, bf16): per (chunk, head) the forward record (22016 B), the
-# backward record (13312 B), the chunk-entry state and the chunk-end state gradient
+# backward (16-token chunks, bf16): per (chunk, head) the forward state pass's record
+# (-W 4096 B, (K e^{g_C-G})^T 8192 B, U 4096 B, e^{g_C} 512 B: 16896 B), the backward
+# record (13312 B), the chunk-entry state and the chunk-end state gradient
 # (2 x 32768 B) and U~, dU~ (2 x 4096 B); per (token, head) algorithmic bytes of each kernel
 BWD_CHUNK = 16
+BWD_FWD_RECORD = 16896
 BWD_BYTES_PER_TOK_HEAD = {
-    "intra": 3 * 2 * D + 4 * D + 4 + 22016 // BWD_CHUNK,                    # inputs in, record out
-    "inter": 22016 // BWD_CHUNK + (32768 + 4096) // BWD_CHUNK,              # record in, states and U~ out
-    "bwd_local": 2 * 2 * D + 4 * D + 4 + 13312 // BWD_CHUNK,                # q, k, gate in, record out
+    "bwd_local": 3 * 2 * D + 4 * D + 4 + (13312 + BWD_FWD_RECORD) // BWD_CHUNK,  # inputs in, both records out
+    "inter": BWD_FWD_RECORD // BWD_CHUNK + (32768 + 4096) // BWD_CHUNK,     # record in, states and U~ out
     "bwd_state": 13312 // BWD_CHUNK + 2 * D + (32768 + 4096) // BWD_CHUNK,  # record, grad_o in, dS_C, dU~ out
     "bwd_chunk": 4 * 2 * D + 4 * D + 4 + 2 * (32768 + 4096) // BWD_CHUNK + 3 * 2 * D + 4 * D + 4,
 }
@@ -404,7 +405,7 @@ def backward_timing(inputs, kda, torch, pre, runs=3):
     t = kda.timing_read()
     kda.timing_enable(False)
     ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items() if cnt}
-    names = ("plan", "intra", "inter", "bwd_local", "bwd_state", "bwd_chunk")
+    names = ("plan", "bwd_local", "inter", "bwd_state", "bwd_chunk")
     total = sum(ms.get(n, 0.0) for n in names)
     tok_heads = T * H
     gbps = {n: round(BWD_BYTES_PER_TOK_HEAD[n] * tok_heads / (ms[n] * 1e-3) / 1e9, 1)

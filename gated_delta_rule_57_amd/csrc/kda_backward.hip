@@ -21,12 +21,14 @@
 // dlog_alpha = reverse cumulative sum of dG over the chunk's rows.
 //
 // Kernels, in launch order:
-//   the forward's plan and records at 16-token chunks (plan_kernel, intra_kernel);
+//   the forward's chunk plan at 16-token chunks (plan_kernel);
+//   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
+//                      e^{g_C}, in the fragment order the reverse state pass reads,
+//                      and the record the forward state pass reads (-W, its
+//                      (K e^{g_C-G})^T, U = T diag(beta) V and e^{g_C}; kda_record.h);
 //   fwd_state_kernel   the forward state pass (inter16_body), four compute waves
 //                      and a store wave per (sequence, head, 16-column slab): keeps
 //                      the state entering every chunk and U~;
-//   bwd_local_kernel   one work-group per (chunk, head): W, Q e^G, K e^{g_C-G}, P and
-//                      e^{g_C}, in the fragment order the reverse state pass reads;
 //   bwd_state_kernel   the reverse state pass (bwd_state_body), four compute waves
 //                      and a store wave per (sequence, head, 16-column slab), over
 //                      the chunks in reverse
@@ -348,18 +350,24 @@ __device__ void local_forward(LocalLds<KT>& L, const E* __restrict__ q, const E*
 }
 
 // ---------------------------------------------------------------------------
-// bwd_local_kernel: the backward record of one (chunk, head). W = T diag(beta) K e^G
-// is one MFMA per 16-channel tile; its accumulator layout is the fragment order of
-// the record, so W, Q e^G and P leave as one 8-byte store per lane and tile.
+// bwd_local_kernel: the backward record of one (chunk, head), and the chunk's record
+// for the forward state pass. W = T diag(beta) K e^G is one MFMA per 16-channel tile;
+// its accumulator layout is the fragment order of the backward record, so W, Q e^G and
+// P leave as one 8-byte store per lane and tile. The forward record takes W the other
+// way round (the same MFMA with its operands swapped gives W^T, whose accumulator
+// layout is the forward record's -W fragment), U = T diag(beta) V likewise in its
+// accumulator order, and (K e^{g_C-G})^T as one lane's whole fragment slot.
 // ---------------------------------------------------------------------------
 template <typename E>
 __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                        const E* __restrict__ v,
                                                         const float* __restrict__ log_alpha,
                                                         const float* __restrict__ beta,
                                                         const int32_t* __restrict__ total_chunks,
                                                         const int2* __restrict__ info, int H, int mc,
-                                                        char* __restrict__ brec) {
+                                                        char* __restrict__ brec, char* __restrict__ records) {
   using BR = BRec<E>;
+  using RC = Rec<E, BC>;
   typedef typename Frag<E>::T FragT;
   typedef typename Vec4<E>::T V4;
   __shared__ LocalLds<E> L;
@@ -368,7 +376,24 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   const int2 inf = info[c];
-  local_forward<E, true>(L, q, k, log_alpha, beta, inf.x, inf.y, h, H, t);
+  const int tok0 = inf.x, len = inf.y;
+  LocalIn<E> lin;
+  local_load(lin, q, k, log_alpha, beta, tok0, len, h, H, t);
+  // v as the B operand of U = T diag(beta) V for value tiles 2w and 2w + 1: lane (m, g)
+  // takes rows 4g .. 4g + 3 of column 16 ct + m (rows past len zeroed where used),
+  // issued after the local forward's loads so that its first wait does not wait for them
+  E vv[2][4];
+  {
+    const size_t HD = (size_t)H * D;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = 4 * g + s;
+        vv[j][s] = v[(size_t)(tok0 + (r < len ? r : 0)) * HD + (size_t)h * D + 16 * (2 * w + j) + m];
+      }
+  }
+  local_forward_in<E, true>(L, lin, len, t);
 
   char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
   E* wt = reinterpret_cast<E*>(rb + BR::WT);
@@ -407,7 +432,46 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
     for (int i = 0; i < 4; ++i) pv[i] = from_f<E>(L.Pm[4 * g + i][m]);
     *reinterpret_cast<V4*>(reinterpret_cast<E*>(rb + BR::PT) + (size_t)lane * 4) = pv;
   }
-  if (t < D) reinterpret_cast<float*>(rb + BR::GAM)[t] = exp2_hw(L.G[BC - 1][t]);
+  // the forward state pass's record
+  char* fb = records + ((size_t)h * mc + c) * RC::BYTES;
+  E* fr = reinterpret_cast<E*>(fb);
+  {
+    FragT wn, ke[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ct = 2 * w + j, ch = 16 * ct + m;
+      // W^T tile: lane (m, g), element i = W[row m][channel 16 ct + 4 g + i]
+      floatx4 wt = {0.f, 0.f, 0.f, 0.f};
+      mma(wt, rows_frag<E>(g, [&](int u) { return L.beta[u] * to_f(L.K[u][ch]) * exp2_hw(L.G[u][ch]); }), ta);
+      // U tile: element i = U[row 4 g + i][value column 16 ct + m]
+      FragT bv;  // B operand: slot s = beta_u V[u][16 ct + m], u = 4 g + s (k = 16..31 zero)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int u = 4 * g + s2;
+        bv[s2] = from_f<E>(u < len ? L.beta[u] * to_f(vv[j][s2]) : 0.f);
+        bv[4 + s2] = from_f<E>(0.f);
+      }
+      floatx4 uacc = {0.f, 0.f, 0.f, 0.f};
+      mma(uacc, ta, bv);
+      const float uo[4] = {uacc[0], uacc[1], uacc[2], uacc[3]};
+      store4f(fr + RC::UU + ((size_t)ct * 64 + lane) * 4, uo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wn[4 * j + i] = from_f<E>(-wt[i]);
+        // (K e^{g_C-G})^T over channel tile ct: rows 4 g + i (rows 16.. of the k-block are zero)
+        const int r = 4 * g + i;
+        ke[j][i] = from_f<E>(to_f(L.K[r][ch]) * exp2_hw(L.G[BC - 1][ch] - L.G[r][ch]));
+        ke[j][4 + i] = from_f<E>(0.f);
+      }
+      store_frag<E>(fr + RC::KE + ((size_t)ct * 64 + lane) * 8, ke[j]);
+    }
+    store_frag<E>(fr + RC::WN + ((size_t)w * 64 + lane) * 8, wn);  // k-block w: tiles 2w, 2w + 1
+  }
+  if (t < D) {
+    const float gc = exp2_hw(L.G[BC - 1][t]);
+    reinterpret_cast<float*>(rb + BR::GAM)[t] = gc;
+    reinterpret_cast<float*>(fb + RC::GAMMA_BYTES)[t] = gc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,26 +1089,26 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   E* dstates = reinterpret_cast<E*>(ws + l.off_dstates);
   E* ut = reinterpret_cast<E*>(ws + l.off_ut);
   E* dut = reinterpret_cast<E*>(ws + l.off_dut);
-  const int dtype = std::is_same<E, float>::value ? 1 : 0;
-
   trace_begin(stream);
-  hipError_t e = launch_forward_records(dtype, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, B, T, H, workspace,
-                                        stream);
+  hipError_t e = launch_plan(cu_seqlens, N, T, varlen ? T : N * T, BC, mc,
+                             reinterpret_cast<int32_t*>(ws + l.fwd.off_chunk_off),
+                             reinterpret_cast<int2*>(ws + l.fwd.off_info), stream);
+  trace_mark(stream, 0);
   if (e != hipSuccess) return e;
-  const char* records = ws + l.fwd.off_records;
+  char* records = ws + l.fwd.off_records;
+  if (mc > 0) {
+    hipLaunchKernelGGL(bwd_local_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
+                       (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, brec, records);
+    e = hipGetLastError();
+    trace_mark(stream, 5);
+    if (e != hipSuccess) return e;
+  }
   const int64_t slots = ((int64_t)N * H + 7) / 8;
   if (slots > 0) {
     hipLaunchKernelGGL(fwd_state_kernel<E>, dim3((unsigned)(slots * 64)), dim3(320), 0, stream, records, chunk_off,
                        info, initial_state, N, H, (int)mc, states, ut);
     e = hipGetLastError();
     trace_mark(stream, 2);
-    if (e != hipSuccess) return e;
-  }
-  if (mc > 0) {
-    hipLaunchKernelGGL(bwd_local_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
-                       (const E*)k, log_alpha, beta, chunk_off + N, info, H, (int)mc, brec);
-    e = hipGetLastError();
-    trace_mark(stream, 5);
     if (e != hipSuccess) return e;
   }
   if (slots > 0) {

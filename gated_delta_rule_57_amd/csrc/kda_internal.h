@@ -145,15 +145,6 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
                            float* dbeta, float* d_initial, int B, int T, int H, void* workspace,
                            hipStream_t stream);
 
-// The first part of the forward pass at BWD_CHUNK-token chunks, for the backward:
-// the chunk plan and the per-(head, chunk) records, in a workspace laid out by
-// prefill_ws_layout(..., BWD_CHUNK, dtype). The backward launches the forward
-// state pass (chunk-entry states and U~) itself. The records hold what that pass
-// reads only: their Q e^G and P slots are not written.
-hipError_t launch_forward_records(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                                  const float* beta, const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
-                                  void* workspace, hipStream_t stream);
-
 // The general diagonal-plus-low-rank forward (see kda_dplr_chunk_fwd in
 // include/kda.h), 64-token chunks.
 size_t dplr_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int dtype);

@@ -231,11 +231,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 //   B1  diagonal 16 x 16 blocks of T = (I + A)^{-1} by forward substitution
 //   B2  off-diagonal blocks of T, one block column per wave, by fp32 MFMA
 //   B3  W = T diag(beta) K e^G (stored as -W) and U = T diag(beta) V
-// STATE_ONLY: the record for a state pass that forms no outputs (the backward's
-// forward pass): q is not read and Q e^G and P are not stored (their record slots
-// stay unwritten); every other part is the same. Launched without the prologue.
 // ---------------------------------------------------------------------------
-template <typename E, int C, int GATE, bool STATE_ONLY = false>
+template <typename E, int C, int GATE>
 __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const float* __restrict__ log_alpha,
                                                     const float* __restrict__ beta,
@@ -305,12 +302,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   for (int i = 0; i < RPT; ++i) {
     const size_t off = row_off(i);
     kraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(k + off);
-    if constexpr (STATE_ONLY) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qraw[i][j] = from_f<E>(0.f);
-    } else {
-      qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
-    }
+    qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
     vraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(v + off);
   }
   float la_row = 0.f;  // scalar gate: log decay of row t (t < CK), natural-log units
@@ -393,7 +385,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) pv[ii] = (16 * J + 4 * g + ii <= 16 * I + m) ? acc[ii] : 0.f;
     E* dst = rec + RC::PP + ((size_t)(I * NKC + (J >> 1)) * 64 + lane) * 8;
-    if constexpr (STATE_ONLY) return;
     if (J & 1)
       store_frag<E>(dst, acc_pair_to_frag<E>(p_lo, pv));
     else if (J == I)
@@ -538,7 +529,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       *reinterpret_cast<V4*>(sRK + r * LD + ch0) = rk;
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
 #pragma unroll
@@ -615,7 +606,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       *reinterpret_cast<floatx4*>(sRR + r * GLD + ch0) = rr;
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
 #pragma unroll
@@ -678,7 +669,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       }
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     // raw (prologue-scaled) k (which 0) or q (which 1) of chunk row r, channels ch .. ch + 3;
     // zero past len
@@ -815,7 +806,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       store4f(sQ + r * LD + ch0, qr[i]);
       const int kb = ch0 >> 5, co = ch0 & 31;
       const int fg = (co & 15) >> 2, fh = co >> 4;
-      if constexpr (!STATE_ONLY) store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
+      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();
     // ---- P3 (scalar): raw block products, then the pair decay per element ------
@@ -1111,47 +1102,6 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   return e;
 }
 }  // namespace
-
-namespace {
-template <typename E>
-hipError_t launch_records_typed(const void* q, const void* k, const void* v, const float* log_alpha,
-                                const float* beta, const int32_t* cu_seqlens, int N, int T, int H, int64_t mc,
-                                const WsLayout& l, char* ws, hipStream_t stream) {
-  constexpr int C = BWD_CHUNK;
-  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + l.off_chunk_off);
-  int2* info = reinterpret_cast<int2*>(ws + l.off_info);
-  char* records = ws + l.off_records;
-  const int total_tokens = cu_seqlens ? T : N * T;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, total_tokens, C, (int)mc,
-                     chunk_off, info);
-  hipError_t e = hipGetLastError();
-  trace_mark(stream, 0);
-  if (e != hipSuccess) return e;
-  if (mc > 0) {
-    const Fusion plain{};
-    hipLaunchKernelGGL((intra_kernel<E, C, GATE_CHANNEL, true>), dim3((unsigned)(mc * H)), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc,
-                       records, plain);
-    e = hipGetLastError();
-    trace_mark(stream, 1);
-    if (e != hipSuccess) return e;
-  }
-  return e;
-}
-}  // namespace
-
-hipError_t launch_forward_records(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                                  const float* beta, const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
-                                  void* workspace, hipStream_t stream) {
-  const bool varlen = cu_seqlens != nullptr;
-  const int N = varlen ? num_seqs : B;
-  const WsLayout l = ws_layout(B, T, H, num_seqs, varlen, BWD_CHUNK, dtype);
-  const int64_t mc = max_chunks(B, T, num_seqs, varlen, BWD_CHUNK);
-  char* ws = reinterpret_cast<char*>(workspace);
-  if (dtype == 0)
-    return launch_records_typed<__bf16>(q, k, v, log_alpha, beta, cu_seqlens, N, T, H, mc, l, ws, stream);
-  return launch_records_typed<float>(q, k, v, log_alpha, beta, cu_seqlens, N, T, H, mc, l, ws, stream);
-}
 
 size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path) {
   const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), varlen ? num_seqs : B);

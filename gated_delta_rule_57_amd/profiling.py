@@ -25,8 +25,7 @@ seg_second for the segment-parallel state kernels, single_first and single_secon
 the single pass, each with _gated appended for its output-epilogue variant); the
 intra-chunk kernel's scalar-gate and
 no-decay instantiations become intra_gdn and intra_deltanet, its 16-token-chunk
-instantiation (the backward's forward pass) intra16, and the 16-token state
-kernel inter16. The general-DPLR forward's kernels are dplr_intra and dplr_inter
+instantiation intra16, and the 16-token state kernel inter16. The general-DPLR forward's kernels are dplr_intra and dplr_inter
 (the inter kernels instantiated with their DPLR flag set).
 The traffic summary records a hash of the kernel sources it was taken on; bench.py
 reports the traffic only while that hash matches the sources.

@@ -347,8 +347,9 @@ int kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *
  * ids: KDA_KERNEL_PLAN (chunk or segment plan), KDA_KERNEL_INTRA (intra-chunk),
  * KDA_KERNEL_INTER (inter-chunk state and output), KDA_KERNEL_DECODE,
  * KDA_KERNEL_OUTNORM (output RMSNorm and gate), for kda_chunk_bwd, whose internal
- * forward reports under the first three, KDA_KERNEL_BWD_LOCAL (per-chunk backward
- * record), KDA_KERNEL_BWD_STATE (state gradient through the chunks) and
+ * forward reports its plan and state pass under KDA_KERNEL_PLAN and KDA_KERNEL_INTER,
+ * KDA_KERNEL_BWD_LOCAL (per-chunk records of both state passes), KDA_KERNEL_BWD_STATE
+ * (state gradient through the chunks) and
  * KDA_KERNEL_BWD_CHUNK (per-chunk gradients), and for the segment-parallel prefill
  * KDA_KERNEL_SEG_FIRST (first segments' outputs and the middle segments' maps),
  * KDA_KERNEL_SEG_SCAN (segment entry states) and KDA_KERNEL_SEG_SECOND (the other
