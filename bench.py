@@ -64,14 +64,16 @@ DECODE_BYTES_PER_HEAD = 2 * 4 * D * D + 3 * 2 * D + 4 * D + 4 + 2 * D
 # backward (16-token chunks, bf16): per (chunk, head) the forward state pass's record
 # (-W 4096 B, (K e^{g_C-G})^T 8192 B, U 4096 B, e^{g_C} 512 B: 16896 B), the backward
 # record (13312 B), the chunk-entry state and the chunk-end state gradient
-# (2 x 32768 B) and U~, dU~ (2 x 4096 B); per (token, head) algorithmic bytes of each kernel
+# (2 x 32768 B), U~, dU~ (2 x 4096 B) and T, M (2 x 16 x 16 fp32); per (token, head)
+# algorithmic bytes of each kernel
 BWD_CHUNK = 16
 BWD_FWD_RECORD = 16896
+BWD_TM_BYTES = 2 * 16 * 16 * 4
 BWD_BYTES_PER_TOK_HEAD = {
-    "bwd_local": 3 * 2 * D + 4 * D + 4 + (13312 + BWD_FWD_RECORD) // BWD_CHUNK,  # inputs in, both records out
+    "bwd_local": 3 * 2 * D + 4 * D + 4 + (13312 + BWD_FWD_RECORD + BWD_TM_BYTES) // BWD_CHUNK,  # inputs in, records out
     "inter": BWD_FWD_RECORD // BWD_CHUNK + (32768 + 4096) // BWD_CHUNK,     # record in, states and U~ out
     "bwd_state": 13312 // BWD_CHUNK + 2 * D + (32768 + 4096) // BWD_CHUNK,  # record, grad_o in, dS_C, dU~ out
-    "bwd_chunk": 4 * 2 * D + 4 * D + 4 + 2 * (32768 + 4096) // BWD_CHUNK + 3 * 2 * D + 4 * D + 4,
+    "bwd_chunk": 4 * 2 * D + 4 * D + 4 + (2 * (32768 + 4096) + BWD_TM_BYTES) // BWD_CHUNK + 3 * 2 * D + 4 * D + 4,
 }
 # bytes any backward must move per (token, head): q, k, v, grad_o, log_alpha, beta in; the five gradients out
 BWD_PATH_BYTES_PER_TOK_HEAD = 4 * 2 * D + 4 * D + 4 + 3 * 2 * D + 4 * D + 4

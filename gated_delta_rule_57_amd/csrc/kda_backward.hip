@@ -230,11 +230,18 @@ __device__ __forceinline__ void local_load(LocalIn<E>& in, const E* __restrict__
   if (t < BC && t < len) in.beta = beta[(size_t)(tok0 + t) * H + h];
 }
 
-template <typename E, bool WANT_P, typename KT>
-__device__ void local_forward_in(LocalLds<KT>& L, const LocalIn<E>& in, int len, int t) {
+// TM_IN: T and M are given (this thread's element (t / 16, t % 16) of each, as
+// bwd_local_kernel stored them) and are put in LDS instead of being formed again.
+template <typename E, bool WANT_P, typename KT, bool TM_IN = false>
+__device__ void local_forward_in(LocalLds<KT>& L, const LocalIn<E>& in, int len, int t, float t_in = 0.f,
+                                 float m_in = 0.f) {
   typedef typename Frag<E>::T FragT;
   const RowMap rm(t);
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
+  if constexpr (TM_IN) {
+    L.T[t >> 4][t & 15] = t_in;
+    L.M[t >> 4][t & 15] = m_in;
+  }
   {
     const bool valid = rm.r < len;
 #pragma unroll
@@ -262,6 +269,7 @@ __device__ void local_forward_in(LocalLds<KT>& L, const LocalIn<E>& in, int len,
     if (g0 - run > FACTOR_MAX_RANGE) L.exact = 1;
   }
   __syncthreads();
+  if constexpr (TM_IN) return;
   if (!L.exact) {
     if (w == 0) {  // M (and P) as factored products over the 128 channels
       floatx4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
@@ -365,7 +373,8 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
                                                         const float* __restrict__ beta,
                                                         const int32_t* __restrict__ total_chunks,
                                                         const int2* __restrict__ info, int H, int mc,
-                                                        char* __restrict__ brec, char* __restrict__ records) {
+                                                        char* __restrict__ brec, char* __restrict__ records,
+                                                        float* __restrict__ tm) {
   using BR = BRec<E>;
   using RC = Rec<E, BC>;
   typedef typename Frag<E>::T FragT;
@@ -394,6 +403,11 @@ __global__ void __launch_bounds__(256) bwd_local_kernel(const E* __restrict__ q,
       }
   }
   local_forward_in<E, true>(L, lin, len, t);
+  {  // T and M for the gradient kernel, which would otherwise form them again
+    float* tmc = tm + ((size_t)h * mc + c) * 2 * BC * BC;
+    tmc[t] = L.T[t >> 4][t & 15];
+    tmc[BC * BC + t] = L.M[t >> 4][t & 15];
+  }
 
   char* rb = brec + ((size_t)h * mc + c) * BR::BYTES;
   E* wt = reinterpret_cast<E*>(rb + BR::WT);
@@ -803,7 +817,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const E* __restrict__ dout, const E* __restrict__ states,
     const E* __restrict__ dstates, const E* __restrict__ ut, const E* __restrict__ dut,
-    const int32_t* __restrict__ total_chunks, const int2* __restrict__ info, int H, int mc, E* __restrict__ dq,
+    const float* __restrict__ tm, const int32_t* __restrict__ total_chunks, const int2* __restrict__ info, int H,
+    int mc, E* __restrict__ dq,
     E* __restrict__ dk, E* __restrict__ dv, float* __restrict__ dlog_alpha, float* __restrict__ dbeta) {
   typedef typename Frag<E>::T FragT;
   __shared__ ChunkLds S;
@@ -831,6 +846,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
   typedef typename Vec4<E>::T V4;
   LocalIn<E> lin;
   local_load(lin, q, k, log_alpha, beta, tok0, len, h, H, t);
+  const float t_in = tm[cix * 2 * BC * BC + t], m_in = tm[cix * 2 * BC * BC + BC * BC + t];  // T, M (bwd_local)
   V4 xv[2], xdu[2];
   {
     const size_t vo = rowbase + (size_t)(rm.r < len ? rm.r : 0) * HD + rm.c0;  // rows past len zeroed below
@@ -863,7 +879,7 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
     S.V[rm.r][rm.c0 + i] = rm.r < len ? to_f(xv[i >> 2][i & 3]) : 0.f;
     S.dU[rm.r][rm.c0 + i] = to_f(xdu[i >> 2][i & 3]);
   }
-  local_forward_in<E, false>(L, lin, len, t);
+  local_forward_in<E, false, float, true>(L, lin, len, t, t_in, m_in);
 
   // ---- state products: wave w forms channel tiles 2w and 2w+1 of
   //      X1 = dO S0^T, X2 = dU~ S0^T, X3 = U~ dS_C^T, and dgamma = rowsum(dS_C o S0)
@@ -1066,7 +1082,8 @@ BackwardWs backward_ws_layout(int B, int T, int H, int num_seqs, bool varlen, in
   l.off_dstates = l.off_states + bal256((size_t)mc * H * D * D * es);
   l.off_ut = l.off_dstates + bal256((size_t)mc * H * D * D * es);
   l.off_dut = l.off_ut + bal256((size_t)mc * H * BC * D * es);
-  l.total = l.off_dut + bal256((size_t)mc * H * BC * D * es);
+  l.off_tm = l.off_dut + bal256((size_t)mc * H * BC * D * es);
+  l.total = l.off_tm + bal256((size_t)mc * H * 2 * BC * BC * sizeof(float));
   return l;
 }
 
@@ -1089,6 +1106,7 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   E* dstates = reinterpret_cast<E*>(ws + l.off_dstates);
   E* ut = reinterpret_cast<E*>(ws + l.off_ut);
   E* dut = reinterpret_cast<E*>(ws + l.off_dut);
+  float* tm = reinterpret_cast<float*>(ws + l.off_tm);
   trace_begin(stream);
   hipError_t e = launch_plan(cu_seqlens, N, T, varlen ? T : N * T, BC, mc,
                              reinterpret_cast<int32_t*>(ws + l.fwd.off_chunk_off),
@@ -1098,7 +1116,8 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   char* records = ws + l.fwd.off_records;
   if (mc > 0) {
     hipLaunchKernelGGL(bwd_local_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
-                       (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, brec, records);
+                       (const E*)k, (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, brec, records,
+                       tm);
     e = hipGetLastError();
     trace_mark(stream, 5);
     if (e != hipSuccess) return e;
@@ -1120,7 +1139,7 @@ hipError_t launch_backward_typed(const void* q, const void* k, const void* v, co
   }
   if (mc > 0) {
     hipLaunchKernelGGL(bwd_chunk_kernel<E>, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q,
-                       (const E*)k, (const E*)v, log_alpha, beta, (const E*)dout, states, dstates, ut, dut,
+                       (const E*)k, (const E*)v, log_alpha, beta, (const E*)dout, states, dstates, ut, dut, tm,
                        chunk_off + N, info, H, (int)mc, (E*)dq, (E*)dk, (E*)dv, dlog_alpha, dbeta);
     e = hipGetLastError();
     trace_mark(stream, 7);

@@ -130,10 +130,11 @@ hipError_t launch_plan(const int32_t* cu_seqlens, int N, int T, int total_tokens
 constexpr int BWD_CHUNK = 16;
 
 // Backward workspace: the forward's (at BWD_CHUNK), then the backward records, the
-// chunk-entry states, the chunk-end state gradients, U~ and dU~ per (head, chunk).
+// chunk-entry states, the chunk-end state gradients, U~ and dU~, and T and M (two
+// fp32 16 x 16 matrices) per (head, chunk).
 struct BackwardWs {
   PrefillWs fwd;
-  size_t off_brec, off_states, off_dstates, off_ut, off_dut, total;
+  size_t off_brec, off_states, off_dstates, off_ut, off_dut, off_tm, total;
 };
 BackwardWs backward_ws_layout(int B, int T, int H, int num_seqs, bool varlen, int dtype);
 size_t backward_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int dtype);

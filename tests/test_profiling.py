@@ -62,8 +62,8 @@ def test_traffic_scaling(tmp_path):
 
 def test_bench_backward_byte_counts_match_the_workspace_layout():
     """The per-(chunk, head) sizes behind bench.py's backward byte counts (forward
-    record 22016 B; backward record, two 128 x 128 bf16 matrices and two 16 x 128
-    ones 87040 B) agree with the library's workspace queries."""
+    record 22016 B; backward record, two 128 x 128 bf16 matrices, two 16 x 128 ones
+    and the fp32 16 x 16 T and M, 89088 B) agree with the library's workspace queries."""
     import bench
     from gated_delta_rule_57_amd import kda
     T, H = 4096, 16
@@ -71,7 +71,7 @@ def test_bench_backward_byte_counts_match_the_workspace_layout():
     fwd = kda.workspace_size(1, T, H, chunk=16)
     bwd = kda.bwd_workspace_size(1, T, H)
     assert abs(fwd / (mc * H) - 22016) < 1
-    assert (bwd - fwd) == mc * H * (13312 + 2 * 32768 + 2 * 4096)
+    assert (bwd - fwd) == mc * H * (13312 + 2 * 32768 + 2 * 4096 + bench.BWD_TM_BYTES)
 
 
 def test_bench_record_byte_counts_match_the_workspace_queries():
