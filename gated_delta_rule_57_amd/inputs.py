@@ -27,8 +27,9 @@ Distributions (the plainest reading of the workloads the library is measured on)
   beta      = sigmoid(N(0, 1)) per (token, head), float32
   S_0       ~ N(0, s0_std) float32, or None (zeros)
 
-The other inputs (raw layer inputs, DPLR inputs, cotangents) use a seeded
-``torch.Generator`` on the target device.
+The raw layer inputs of the fused path (``make_raw_prefill``), the general-DPLR
+inputs (``make_dplr``) and the backward's cotangents (``make_cotangents``) are drawn
+the same way, each with the draw order its docstring states.
 """
 import math
 import os
@@ -159,30 +160,6 @@ def _host_composition(rng, total: int, parts: int) -> np.ndarray:
     return np.concatenate([[0], cuts, [total]]).astype(np.int32)
 
 
-def _gen(seed, device):
-    g = torch.Generator(device=device)
-    g.manual_seed(int(seed))
-    return g
-
-
-def _normal(g, shape, device):
-    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-
-
-def _unit_rows(x):
-    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
-
-
-def uniform_composition(g, total: int, parts: int, device) -> torch.Tensor:
-    """cu_seqlens of ``parts`` positive lengths summing to ``total``: distinct cut
-    points drawn uniformly from [1, total-1] and sorted."""
-    cuts = torch.randperm(total - 1, generator=g, device=device)[: parts - 1] + 1
-    cuts, _ = torch.sort(cuts)
-    z = torch.zeros(1, dtype=cuts.dtype, device=device)
-    e = torch.full((1,), total, dtype=cuts.dtype, device=device)
-    return torch.cat([z, cuts, e]).to(torch.int32)
-
-
 def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64, la_mode: str = "scaled",
                  la_scale: float = 0.1, s0_std: float = 0.0, num_seqs: Optional[int] = None,
                  cu_seqlens=None, device="cuda", dk: int = D, dv: int = D, gate: str = "channel") -> PrefillInputs:
@@ -231,14 +208,17 @@ def make_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int = 64,
 
 
 def make_cotangents(seed: int, inp: PrefillInputs, final_std: float = 0.1, device="cuda"):
-    """Cotangents for a backward call on ``inp``: grad_o ~ N(0, 1) in the input dtype,
-    shaped like o, and grad_final_state ~ N(0, final_std^2) fp32 [N, H, dk, dv]
-    (None when final_std is 0)."""
-    g = _gen(seed + 1000, device)
+    """Cotangents for a backward call on ``inp``: grad_o ~ N(0, 1) rounded to the input
+    dtype, shaped like o, and grad_final_state ~ N(0, final_std^2) fp32 [N, H, dk, dv]
+    (None when final_std is 0). Host draws from ``SeedSequence(seed + 1000)``, in that
+    order."""
+    dr = HostDraws(seed + 1000)
     B, T, H, dk = inp.q.shape
     dv = inp.v.shape[-1]
-    grad_o = _normal(g, (B, T, H, dv), device).to(inp.q.dtype).contiguous()
-    gf = final_std * _normal(g, (inp.num_seqs, H, dk, dv), device) if final_std > 0 else None
+    grad_o = _to_device(dr.fill(B * T * H * dv, _h_normal), (B, T, H, dv), inp.dtype, device).contiguous()
+    n = inp.num_seqs * H * dk * dv
+    gf = (_to_device(dr.fill(n, lambda r, c: final_std * r.standard_normal(c)), (inp.num_seqs, H, dk, dv), "fp32",
+                     device) if final_std > 0 else None)
     return grad_o, gf
 
 
@@ -321,25 +301,29 @@ def make_raw_prefill(seed: int, B: int, T: int, H: int, dtype: str, chunk: int =
     """Raw layer inputs: q, k ~ qk_scale * N(0, 1) (not normalised); v ~ N(0, 1);
     gate ~ N(gate_shift, 1) (gate_shift = -3 gives log alpha = -softplus(gate) near
     -0.05, the decay range of the standard workloads); beta, out_gate ~ N(0, 1);
-    norm_weight ~ U(0.5, 1.5). Draw order: cut points, q, k, v, gate, beta, out_gate,
-    norm_weight, initial state."""
-    g = _gen(seed, device)
+    norm_weight ~ U(0.5, 1.5). Host draws in the order: cut points, q, k, v, gate,
+    beta, out_gate, norm_weight, initial state."""
+    dr = HostDraws(seed)
     cu = None
     if num_seqs is not None:
         assert B == 1
-        cu = uniform_composition(g, T, num_seqs, device)
-    td = TORCH_DTYPE[dtype]
-    q = (qk_scale * _normal(g, (B, T, H, dk), device)).to(td)
-    k = (qk_scale * _normal(g, (B, T, H, dk), device)).to(td)
-    v = _normal(g, (B, T, H, dv), device).to(td)
-    gate = _normal(g, (B, T, H, dk), device) + gate_shift
-    beta = _normal(g, (B, T, H), device)
-    out_gate = _normal(g, (B, T, H, dv), device).to(td)
-    w = 0.5 + torch.rand((dv,), generator=g, device=device, dtype=torch.float32)
+        cu = torch.from_numpy(_host_composition(np.random.default_rng(dr.child()), T, num_seqs)).to(device)
+    shape_k, shape_v = (B, T, H, dk), (B, T, H, dv)
+    nk, nv = B * T * H * dk, B * T * H * dv
+    q = _to_device(dr.fill(nk, lambda r, c: qk_scale * r.standard_normal(c)), shape_k, dtype, device)
+    k = _to_device(dr.fill(nk, lambda r, c: qk_scale * r.standard_normal(c)), shape_k, dtype, device)
+    v = _to_device(dr.fill(nv, _h_normal), shape_v, dtype, device)
+    gate = _to_device(dr.fill(nk, lambda r, c: r.standard_normal(c) + gate_shift), shape_k, "fp32", device)
+    beta = _to_device(dr.fill(B * T * H, _h_normal), (B, T, H), "fp32", device)
+    out_gate = _to_device(dr.fill(nv, _h_normal), shape_v, dtype, device)
+    w = _to_device(dr.fill(dv, lambda r, c: 0.5 + r.random(c)), (dv,), "fp32", device)
     N = B if cu is None else cu.numel() - 1
-    s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
+    s0 = None
+    if s0_std > 0:
+        s0 = _to_device(dr.fill(N * H * dk * dv, lambda r, c: s0_std * r.standard_normal(c)), (N, H, dk, dv), "fp32",
+                        device)
     return RawPrefillInputs(q.contiguous(), k.contiguous(), v.contiguous(), gate.contiguous(), beta.contiguous(),
-                            out_gate.contiguous(), w, s0, cu, dtype, chunk)
+                            out_gate.contiguous(), w.contiguous(), s0, cu, dtype, chunk)
 
 
 @dataclass
@@ -379,39 +363,48 @@ def make_dplr(seed: int, B: int, T: int, H: int, dtype: str, la_mode: str = "sca
               transition Diag(alpha) - 2^-j b b^T is then symmetric with eigenvalues
               in (-1, 1] whatever the rounding, so the state stays bounded at any length.
       "free": a, b ~ ab_scale N(0, 1/dk) independently (short sequences only).
-    Draw order: cut points, q, k, v, log-decay normals, slow-channel choice (mixed),
-    then u and the strength normals (tied) or a and b (free), then the initial state."""
-    g = _gen(seed, device)
+    Host draws in the order: cut points, q, k, v, log-decay normals, slow-channel
+    choice (mixed), then u and the strength normals (tied) or a and b (free), then the
+    initial state."""
+    dr = HostDraws(seed)
     cu = None
     if num_seqs is not None:
         assert B == 1
-        cu = uniform_composition(g, T, num_seqs, device)
-    td = TORCH_DTYPE[dtype]
-    q = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
-    k = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
-    v = _normal(g, (B, T, H, dv), device).to(td)
-    z = _normal(g, (B, T, H, dk), device)
+        cu = torch.from_numpy(_host_composition(np.random.default_rng(dr.child()), T, num_seqs)).to(device)
+    shape_k, shape_v = (B, T, H, dk), (B, T, H, dv)
+    nk, nv = B * T * H * dk, B * T * H * dv
+    q = _to_device(dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk)), shape_k, dtype, device)
+    k = _to_device(dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk)), shape_k, dtype, device)
+    v = _to_device(dr.fill(nv, _h_normal), shape_v, dtype, device)
     if la_mode == "scaled":
-        log_alpha = -la_scale * torch.nn.functional.softplus(z)
+        la = dr.fill(nk, lambda r, c: -la_scale * _h_softplus(r.standard_normal(c)))
     elif la_mode == "mixed":
-        log_alpha = -torch.nn.functional.softplus(z)
+        la = dr.fill(nk, lambda r, c: -_h_softplus(r.standard_normal(c))).reshape(B * T, H, dk)
+        rs = np.random.default_rng(dr.child())
         for h in range(H):
-            slow = torch.randperm(dk, generator=g, device=device)[: dk // 2]
-            log_alpha[:, :, h, slow] = -1e-3
+            slow = rs.permutation(dk)[: dk // 2]
+            la[:, h, slow] = np.float32(-1e-3)
+        la = la.reshape(-1)
     else:
         raise ValueError(la_mode)
+    log_alpha = _to_device(la, shape_k, "fp32", device)
     if lowrank == "tied":
-        b = _unit_rows(_normal(g, (B, T, H, dk), device)).to(td)
-        strength = torch.sigmoid(_normal(g, (B, T, H), device))
-        j = torch.clamp(torch.round(-torch.log2(strength)), min=1.0)
-        a = (-torch.exp2(-j)[..., None] * b.float()).to(td)
+        b = _to_device(dr.fill(nk, lambda r, c: _h_unit_rows(r, c, dk)), shape_k, dtype, device)
+        # 2^-j = sigmoid(z) rounded to a power of two, j >= 1: exact in every dtype
+        j = dr.fill(B * T * H, lambda r, c: np.maximum(np.round(-np.log2(_h_sigmoid(r.standard_normal(c)))), 1.0))
+        scale = torch.from_numpy(-np.exp2(-j.astype(np.float64)).astype(np.float32)).view(B, T, H, 1).to(device)
+        a = (scale * b.float()).to(b.dtype)
     elif lowrank == "free":
-        a = (ab_scale / dk ** 0.5 * _normal(g, (B, T, H, dk), device)).to(td)
-        b = (ab_scale / dk ** 0.5 * _normal(g, (B, T, H, dk), device)).to(td)
+        sd = ab_scale / dk ** 0.5
+        a = _to_device(dr.fill(nk, lambda r, c: sd * r.standard_normal(c)), shape_k, dtype, device)
+        b = _to_device(dr.fill(nk, lambda r, c: sd * r.standard_normal(c)), shape_k, dtype, device)
     else:
         raise ValueError(lowrank)
     N = B if cu is None else cu.numel() - 1
-    s0 = s0_std * _normal(g, (N, H, dk, dv), device) if s0_std > 0 else None
+    s0 = None
+    if s0_std > 0:
+        s0 = _to_device(dr.fill(N * H * dk * dv, lambda r, c: s0_std * r.standard_normal(c)), (N, H, dk, dv), "fp32",
+                        device)
     return DplrInputs(q.contiguous(), k.contiguous(), v.contiguous(), a.contiguous(), b.contiguous(),
                       log_alpha.contiguous(), s0, cu, dtype,
                       dict(seed=seed, la_mode=la_mode, la_scale=la_scale, lowrank=lowrank))

@@ -158,3 +158,30 @@ def test_paths_agree_at_4k():
     inp = inputs.make_workload(1)
     for path in PATHS:
         compare_prefill(inp, label=f"workload1-{path}", path=path)
+
+
+def _many_lengths(seed, n, hi):
+    """n sequence lengths drawn uniformly from [0, hi], about one in ten of them zero."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, hi + 1, size=n)
+    lens[rng.random(n) < 0.1] = 0
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_many_sequences(path):
+    """1,500 packed sequences of 0 to 150 tokens (more than one 1,024-sequence block of
+    the chunk and segment plans), random initial states."""
+    cu = _many_lengths(61, 1500, 150)
+    inp = inputs.make_prefill(61, B=1, T=int(cu[-1]), H=2, dtype="bf16", la_scale=0.3, s0_std=0.2,
+                              cu_seqlens=cu)
+    check(inp, path, "many-seqs")
+
+
+@pytest.mark.parametrize("dtype,chunk", [("fp32", 16), ("fp32", 64), ("bf16", 16)])
+def test_many_sequences_other_kernels(dtype, chunk):
+    """The same packing on the fp32 and 16-token kernels."""
+    cu = _many_lengths(62, 1300, 100)
+    inp = inputs.make_prefill(62, B=1, T=int(cu[-1]), H=2, dtype=dtype, chunk=chunk, la_scale=0.3, s0_std=0.2,
+                              cu_seqlens=cu)
+    compare_prefill(inp, label=f"many-seqs {dtype} C={chunk}")
