@@ -175,11 +175,13 @@ struct LocalLds {
 // (nt, 2 kb + 1), lane m + 16 g in both, so each is one contiguous load per wave.
 // TS: tile (r, t) starts at element (t * TS + r) * 256 (state_tile_index: TS = 8;
 // row_tile_index, one row of tiles: TS = 1, nt = 0).
-template <typename E, int TS>
+template <typename E, int TS, bool NT = false>
 __device__ __forceinline__ typename Frag<E>::T tile_frag(const E* __restrict__ M, int nt, int kb, int lane) {
   typedef typename Vec4<E>::T V4;
-  const V4 lo = *reinterpret_cast<const V4*>(M + ((size_t)(2 * kb * TS + nt) * 64 + lane) * 4);
-  const V4 hi = *reinterpret_cast<const V4*>(M + ((size_t)((2 * kb + 1) * TS + nt) * 64 + lane) * 4);
+  const V4* plo = reinterpret_cast<const V4*>(M + ((size_t)(2 * kb * TS + nt) * 64 + lane) * 4);
+  const V4* phi = reinterpret_cast<const V4*>(M + ((size_t)((2 * kb + 1) * TS + nt) * 64 + lane) * 4);
+  const V4 lo = NT ? load_nt(plo) : *plo;
+  const V4 hi = NT ? load_nt(phi) : *phi;
   typename Frag<E>::T f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -868,8 +870,8 @@ __global__ void __launch_bounds__(256, 2) bwd_chunk_kernel(
       a3[kb] = tile_frag<E, 1>(Ut, 0, kb, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bsf[j][kb] = tile_frag<E, 8>(S0, 2 * w + j, kb, lane);
-        bdf[j][kb] = tile_frag<E, 8>(dSC, 2 * w + j, kb, lane);
+        bsf[j][kb] = tile_frag<E, 8, true>(S0, 2 * w + j, kb, lane);
+        bdf[j][kb] = tile_frag<E, 8, true>(dSC, 2 * w + j, kb, lane);
       }
     }
   };

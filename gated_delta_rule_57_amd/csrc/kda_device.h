@@ -148,6 +148,13 @@ __device__ __forceinline__ void store_nt(V* p, const V& x) {
   typedef unsigned int U __attribute__((ext_vector_type(sizeof(V) / 4)));
   __builtin_nontemporal_store(__builtin_bit_cast(U, x), reinterpret_cast<U*>(p));
 }
+// Non-temporal vector load of data read once, long after it was written (the
+// per-chunk records and states, the inputs of the intra-chunk kernel).
+template <typename V>
+__device__ __forceinline__ V load_nt(const V* p) {
+  typedef unsigned int U __attribute__((ext_vector_type(sizeof(V) / 4)));
+  return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const U*>(p)));
+}
 // s_waitcnt with lgkmcnt(0) and the vector-memory counter left free
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // work-group barrier for LDS exchanges that leaves in-flight global loads alone

@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   };
   if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) la[i] = *reinterpret_cast<const floatx4*>(log_alpha + row_off(i));
+    for (int i = 0; i < RPT; ++i) la[i] = load_nt(reinterpret_cast<const floatx4*>(log_alpha + row_off(i)));
   }
   float braw = 0.f, lraw = 0.f;
   if (t < CK && t < len) {
@@ -301,9 +301,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const size_t off = row_off(i);
-    kraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(k + off);
-    qraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(q + off);
-    vraw[i] = *reinterpret_cast<const typename Vec4<E>::T*>(v + off);
+    kraw[i] = load_nt(reinterpret_cast<const typename Vec4<E>::T*>(k + off));
+    qraw[i] = load_nt(reinterpret_cast<const typename Vec4<E>::T*>(q + off));
+    vraw[i] = load_nt(reinterpret_cast<const typename Vec4<E>::T*>(v + off));
   }
   float la_row = 0.f;  // scalar gate: log decay of row t (t < CK), natural-log units
   if (t < CK) {

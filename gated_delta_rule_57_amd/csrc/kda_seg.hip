@@ -1209,9 +1209,9 @@ __device__ __forceinline__ void load_record(RecRegs<PASS>& x, const char* __rest
     // output pass: pieces 0 .. 3583 (-W, Q e^G, K, P); map pass: -W (0 .. 1023) and
     // (K e^{g_C-G})^T (2048 .. 3071)
     const int piece = PASS == PASS_OUT ? t + NTHR * q : (q < 2 ? t + NTHR * q : 2048 + t + NTHR * (q - 2));
-    x.d[q] = src[piece];
+    x.d[q] = load_nt(src + piece);
   }
-  if (t < 32) x.gm = reinterpret_cast<const u32x4*>(rb + RC::GAMMA_BYTES)[t];
+  if (t < 32) x.gm = load_nt(reinterpret_cast<const u32x4*>(rb + RC::GAMMA_BYTES) + t);
   const bf16x4* uu = reinterpret_cast<const bf16x4*>(rb + RC::UU * 2);
   const int c4 = w & 3, hr = w >> 2;
 #pragma unroll
@@ -1219,7 +1219,7 @@ __device__ __forceinline__ void load_record(RecRegs<PASS>& x, const char* __rest
 #pragma unroll
     for (int j = 0; j < RecRegs<PASS>::NU; ++j) {
       const int ct = 2 * c4 + c, rt = PASS == PASS_OUT ? 2 * hr + j : j;
-      if (PASS == PASS_OUT || w >= 4) x.u[c][j] = uu[(ct * 4 + rt) * 64 + lane];
+      if (PASS == PASS_OUT || w >= 4) x.u[c][j] = load_nt(uu + (ct * 4 + rt) * 64 + lane);
     }
 }
 
