@@ -956,7 +956,10 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   // ---- B3: W (computed transposed, stored as -W in fragment order) and U, two
   //      16-column slabs per wave. T is block lower triangular, so row tile rt needs
   //      k-blocks kb <= rt / 2 only. A slab's products are all issued before its
-  //      stores, so their MFMA latencies overlap. ---------------------------------------
+  //      stores, so their MFMA latencies overlap. The wave's two slabs are the two
+  //      halves of its -W slots, so each slot leaves as one 16-byte store after the
+  //      second slab. ---------------------------------------------------------------------
+  floatx4 aw[2][NRT];
 #pragma unroll
   for (int cl = 0; cl < 2; ++cl) {
     const int ct = 2 * w + cl;
@@ -966,25 +969,26 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
       bK[kb] = frag_colk(sKt, LD, 16 * ct + m, 32 * kb, g);
       bV[kb] = frag_colk(sV, LD, 16 * ct + m, 32 * kb, g);
     }
-    floatx4 aw[NRT], au[NRT];
+    floatx4 au[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      aw[rt] = au[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      aw[cl][rt] = au[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb <= (rt >> 1); ++kb) {
         const FragT aT = frag_rowk(sTb, LDK, 16 * rt + m, 32 * kb, g);
-        mma(aw[rt], bK[kb], aT);   // lane (m, g): W[16 rt + m][16 ct + 4 g + ii]
-        mma(au[rt], aT, bV[kb]);   // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
+        mma(aw[cl][rt], bK[kb], aT);  // lane (m, g): W[16 rt + m][16 ct + 4 g + ii]
+        mma(au[rt], aT, bV[kb]);      // lane (m, g): U[16 rt + 4 g + ii][16 ct + m]
       }
     }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      const float wn[4] = {-aw[rt][0], -aw[rt][1], -aw[rt][2], -aw[rt][3]};
-      store4f(rec + RC::WN + ((size_t)(rt * 4 + (ct >> 1)) * 64 + lane) * 8 + 4 * (ct & 1), wn);
       const float uo[4] = {au[rt][0], au[rt][1], au[rt][2], au[rt][3]};
       store4f(rec + RC::UU + ((size_t)(ct * NRT + rt) * 64 + lane) * 4, uo);
     }
   }
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+    store_frag<E>(rec + RC::WN + ((size_t)(rt * 4 + w) * 64 + lane) * 8, acc_pair_to_frag<E>(-aw[0][rt], -aw[1][rt]));
 }
 
 // Inter-chunk kernel for 16-token chunks (the body and its description are in
