@@ -235,20 +235,22 @@ struct ChainOps {
 // the same registers for every wave and stay in flight across the loop's back edge (two
 // inlined copies would be merged by register copies that wait for every load).
 // The output epilogue's gate values of one chunk (len >= 1 tokens from tok0) for wave
-// half hr (rows 32 hr + 16 j + m, columns col0 + 16 c + 4 g .. + 3); rows past len read
-// the chunk's first row. Only the passes instantiated for an output gate call it, and
-// they call it on every path, so its loads are never merged with a path without them.
-__device__ __forceinline__ void load_out_gate(bf16x4 (&zv)[2][2], const Fusion& fu, size_t HD, int h, int tok0,
+// half hr: rows 32 hr + 16 j + m, one 16-byte load of 8 consecutive columns per row
+// (col0 + 4 g .. for even g, col0 + 4 g + 12 .. for odd g: the same columns the lane
+// writes of o); rows past len read the chunk's first row. The epilogue trades halves
+// between lanes g and g ^ 1 where it uses them. Only the passes instantiated for an
+// output gate call it, and they call it on every path, so its loads are never merged
+// with a path without them.
+typedef bf16x8 GateRegs[2];
+__device__ __forceinline__ void load_out_gate(GateRegs& zv, const Fusion& fu, size_t HD, int h, int tok0,
                                               int len, int w, int lane) {
   const int m = lane & 15, g = lane >> 4, col0 = 32 * (w & 3), hr = w >> 2;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int row = 32 * hr + 16 * j + m, rr = row < len ? row : 0;
-      zv[j][c] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(fu.out_gate) +
-                                                 (size_t)(tok0 + rr) * HD + (size_t)h * D + col0 + 16 * c + 4 * g);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int row = 32 * hr + 16 * j + m, rr = row < len ? row : 0;
+    zv[j] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(fu.out_gate) + (size_t)(tok0 + rr) * HD +
+                                             (size_t)h * D + col0 + 4 * g + ((g & 1) ? 12 : 0));
+  }
 }
 
 // OG: the output epilogue runs (fu.out_gate is set). zv holds this chunk's gate values
@@ -258,7 +260,7 @@ __device__ __forceinline__ void load_out_gate(bf16x4 (&zv)[2][2], const Fusion& 
 template <bool OG, bool PF, typename Mid>
 __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4 (&au)[2][2], const ChainOps& op,
                                                const Fusion& fu, __bf16* __restrict__ o, size_t HD, int h, int tok0,
-                                               int len, int next_len, bf16x4 (&zv)[2][2], const floatx4 (&nw)[2],
+                                               int len, int next_len, GateRegs& zv, const floatx4 (&nw)[2],
                                                int w, int lane, Mid&& mid) {
   const int hr = w >> 2, ho = 1 - hr;
   const int m = lane & 15, g = lane >> 4;
@@ -371,10 +373,22 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) tot += op.sON[q4 * SC + row];
       const float inv = rsqrtf(tot * (1.f / D) + fu.norm_eps);
+      // the lane loaded 8 consecutive columns (see load_out_gate): it keeps the half of
+      // its own 16-column tile and trades the other with lane g ^ 1
+      const bool godd = (g & 1) != 0;
+      typedef unsigned u32x4g __attribute__((ext_vector_type(4)));
+      const u32x4g zu = __builtin_bit_cast(u32x4g, zv[j]);
+      const unsigned give0 = godd ? zu[0] : zu[2], give1 = godd ? zu[1] : zu[3];
+      const auto r0 = __builtin_amdgcn_permlane16_swap(give0, give0, false, false);
+      const auto r1 = __builtin_amdgcn_permlane16_swap(give1, give1, false, false);
+      const unsigned got0 = godd ? r0[0] : r0[1], got1 = godd ? r1[0] : r1[1];
+      typedef unsigned u32x2g __attribute__((ext_vector_type(2)));
+      const u32x2g keep = godd ? u32x2g{zu[2], zu[3]} : u32x2g{zu[0], zu[1]}, got = {got0, got1};
+      const bf16x4 zc[2] = {__builtin_bit_cast(bf16x4, godd ? got : keep), __builtin_bit_cast(bf16x4, godd ? keep : got)};
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xt[j][c][i] = xt[j][c][i] * inv * nw[c][i] * sigmoid_f((float)zv[j][c][i]);
+        for (int i = 0; i < 4; ++i) xt[j][c][i] = xt[j][c][i] * inv * nw[c][i] * sigmoid_f((float)zc[c][i]);
     }
     if constexpr (PF) {  // one load on every path: a select of the chunk, not a branch around it
       // the gate values are used up before the loads that overwrite them are issued (see
@@ -387,18 +401,35 @@ __device__ __forceinline__ void out_state_step(floatx4 (&S)[4][2], const floatx4
       load_out_gate(zv, fu, HD, h, nx ? tok0 + SC : tok0, nx ? next_len : len, w, lane);
     }
   }
+  // Each lane writes 8 consecutive columns of its row as one 16-byte store: lanes g and
+  // g ^ 1 (16 lanes apart) trade the half they do not write, so even g writes columns
+  // 4 g .. 4 g + 7 of the first 16-column tile and odd g columns 4 g + 12 .. 4 g + 19
+  // (the second tile), and a row's 64 bytes leave in one instruction.
+  const bool godd = (g & 1) != 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int row = 32 * hr + 16 * j + m;
-    if (row < len) {
+    const floatx4 keep = godd ? xt[j][1] : xt[j][0], give = godd ? xt[j][0] : xt[j][1];
+    bf16x4 kb4, gb4;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x4 ov;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)xt[j][c][i];
-        *reinterpret_cast<bf16x4*>(o + (size_t)(tok0 + row) * HD + (size_t)h * D + col0 + 16 * c + 4 * g) = ov;
-      }
+    for (int i = 0; i < 4; ++i) {
+      kb4[i] = (__bf16)keep[i];
+      gb4[i] = (__bf16)give[i];
     }
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 gu = __builtin_bit_cast(u32x2, gb4);
+    const auto r0 = __builtin_amdgcn_permlane16_swap(gu[0], gu[0], false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(gu[1], gu[1], false, false);
+    const u32x2 ru = {godd ? r0[0] : r0[1], godd ? r1[0] : r1[1]};
+    const bf16x4 rb4 = __builtin_bit_cast(bf16x4, ru);
+    bf16x8 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ov[i] = godd ? rb4[i] : kb4[i];
+      ov[4 + i] = godd ? kb4[i] : rb4[i];
+    }
+    const int row = 32 * hr + 16 * j + m;
+    if (row < len)
+      *reinterpret_cast<bf16x8*>(o + (size_t)(tok0 + row) * HD + (size_t)h * D + col0 + 4 * g + (godd ? 12 : 0)) = ov;
   }
 }
 
@@ -1153,7 +1184,7 @@ __device__ void seg_pass(const SegArgs& a, char* smem, int h, int tok_begin, int
     if constexpr (OUTP) {
       // the output gate values are loaded at the step (registers here are too tight to
       // hold the next chunk's across the chunk's matrix phases)
-      bf16x4 zv[2][2];
+      GateRegs zv;
       floatx4 nw[2];
       if constexpr (OG) {
         load_out_gate(zv, fu, HD, h, tok0, len, w, lane);
@@ -1270,7 +1301,7 @@ __device__ void rec_pass(const SegArgs& a, char* smem, int h, int c_first, int t
           for (int i = 0; i < 4; ++i) u[c][j][i] = (float)x.u[c][j][i];
       }
   };
-  bf16x4 zv[2][2];  // output gate values of the chunk being stepped (epilogue)
+  GateRegs zv;  // output gate values of the chunk being stepped (epilogue)
   if (nchunks > 0) {
     if constexpr (OUTP && OG) {
       const int l0 = min(SC, tok_end - tok_begin);
