@@ -311,7 +311,7 @@ def config_timing(inputs, kda, torch, dev, runs=20):
     return res
 
 
-def path_timing(kda, torch, pre, runs=5):
+def path_timing(kda, torch, pre, runs=20):
     """The headline prefill on each kernel set (kda_prefill_path)."""
     B, T, H = pre.q.shape[:3]
     out = {}
@@ -340,7 +340,7 @@ def path_timing(kda, torch, pre, runs=5):
     return out
 
 
-def fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec, runs=5):
+def fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec, runs=20):
     """The fused layer core on the same shapes: the prefill on raw q, k and gate /
     beta pre-activations with the output RMSNorm and gate, and the fused decode
     step."""
@@ -369,7 +369,7 @@ def fused_timing(inputs, kda, torch, dev, pre, dec, state, o_dec, runs=5):
             "decode_GBps": round(dec_bytes / (statistics.median(dms) * 1e-3) / 1e9, 1)}
 
 
-def gate_timing(kda, torch, pre, dec, state, o_dec, runs=5):
+def gate_timing(kda, torch, pre, dec, state, o_dec, runs=20):
     """The scalar-gate (one decay per token and head) and no-decay paths on the
     headline prefill shape and the decode batch."""
     B, T, H = pre.q.shape[:3]
@@ -393,7 +393,7 @@ def gate_timing(kda, torch, pre, dec, state, o_dec, runs=5):
     return out
 
 
-def backward_timing(inputs, kda, torch, pre, runs=3):
+def backward_timing(inputs, kda, torch, pre, runs=20):
     """The backward (kda_chunk_bwd) on the headline prefill shape: gradients of q, k,
     v, log_alpha, beta and the initial state for a random output cotangent and a
     final-state cotangent, timed by the library's events."""
@@ -407,12 +407,13 @@ def backward_timing(inputs, kda, torch, pre, runs=3):
 
     g = run()
     torch.cuda.synchronize()
+    del g
     kda.timing_enable(True)
-    for _ in range(runs):
-        g = run()
-    torch.cuda.synchronize()
+    calls = time_fn(torch, run, runs=runs, warmup=0)  # events around each whole call
     t = kda.timing_read()
     kda.timing_enable(False)
+    g = run()
+    torch.cuda.synchronize()
     ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in t.items() if cnt}
     names = ("plan", "bwd_local", "inter", "bwd_state", "bwd_chunk")
     total = sum(ms.get(n, 0.0) for n in names)
@@ -426,13 +427,14 @@ def backward_timing(inputs, kda, torch, pre, runs=3):
     return {"workload": "kda_backward_T131072_H32_bf16 (gradients of q, k, v, log_alpha, beta and the initial "
                         "state; 16-token chunks)",
             "ms": round(total, 4), "tokens_per_s": round(T / (total * 1e-3), 1),
+            "call_ms": stats(calls),  # whole calls, output allocation included
             "kernel_ms": {n: round(ms.get(n, 0.0), 4) for n in names},
             "kernel_GBps_design": gbps,
             "path_hbm_frac": round(BWD_PATH_BYTES_PER_TOK_HEAD * tok_heads / (total * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "finite": finite}
 
 
-def dplr_comparison(inputs, kda, torch, dev, pre, lengths=(4096, 16384, 65536, 131072), runs=3):
+def dplr_comparison(inputs, kda, torch, dev, pre, lengths=(4096, 16384, 65536, 131072), runs=20):
     """KDA's chunked forward against the general DPLR chunked forward
     (kda_dplr_chunk_fwd) on the same shapes: H = 32, d = 128, bf16, 64-token chunks,
     over input lengths. KDA runs the same kernel structure as the DPLR forward (the
