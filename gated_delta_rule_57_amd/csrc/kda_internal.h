@@ -56,17 +56,20 @@ enum PrefillKernels {
   KERNELS_RECORD_SEG = 1,   // intra-chunk records, segment-parallel full-width state kernels
   KERNELS_SINGLE = 2        // segment-parallel single pass, no records
 };
-// The automatic path takes the segment-parallel state kernels when sequences average
-// at least SEG_MIN_AVG_CHUNKS chunks (measured on MI355X: they win from about 8K tokens
-// per sequence; below that the segment scan and the short segments cost more than the
-// slab kernels' repeated record reads).
-constexpr int SEG_MIN_AVG_CHUNKS = 96;
-inline int prefill_kernels(int dtype, int chunk, int path, int64_t max_chunks, int N) {
+// The automatic path takes the segment-parallel state kernels when the prefill has at
+// least SEG_MIN_CHUNK_HEADS (chunk, head) pairs, counting the chunk bound of a packed
+// batch: below that a slab work-group per (sequence, head, 16 value columns) leaves the
+// chip's CUs free for one serial walk each, and the segment scan and short segments
+// cost more (1 x 4K tokens x 32 heads: 0.155 against 0.189 ms); above it the slab
+// work-groups share CUs and walk their chains in turn (8 x 4K x 32 heads: 1.14 against
+// 0.87 ms; 1024 x 64 tokens x 32 heads: 4.75 against 3.26 ms; measured on MI355X).
+constexpr int64_t SEG_MIN_CHUNK_HEADS = 4096;
+inline int prefill_kernels(int dtype, int chunk, int path, int64_t max_chunks, int H) {
   if (dtype != 0 || chunk != 64) return KERNELS_RECORD_SLAB;
   if (path == 1) return KERNELS_RECORD_SLAB;
   if (path == 2) return KERNELS_SINGLE;
   if (path == 3) return KERNELS_RECORD_SEG;
-  return max_chunks >= (int64_t)SEG_MIN_AVG_CHUNKS * (N > 0 ? N : 1) ? KERNELS_RECORD_SEG : KERNELS_RECORD_SLAB;
+  return max_chunks * H >= SEG_MIN_CHUNK_HEADS ? KERNELS_RECORD_SEG : KERNELS_RECORD_SLAB;
 }
 
 // Segment-parallel passes (kda_seg.hip): about SEG_TARGET_GROUPS work-groups per

@@ -1073,7 +1073,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   const int64_t units = (int64_t)N * H;
   const int64_t slots = (units + 7) / 8;
   if constexpr (std::is_same<E, __bf16>::value && C == 64) {
-    if (slots > 0 && prefill_kernels(0, 64, fusion.prefill_path, mc, N) == KERNELS_RECORD_SEG) {
+    if (slots > 0 && prefill_kernels(0, 64, fusion.prefill_path, mc, H) == KERNELS_RECORD_SEG) {
       // segment-parallel full-width state kernels on the records (output epilogue fused in)
       int B = cu_seqlens ? 1 : N;
       const SegWs sl =
@@ -1108,7 +1108,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int T, int H, int num_seqs, bool varlen, int chunk, int dtype, int path) {
-  const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), varlen ? num_seqs : B);
+  const int kern = prefill_kernels(dtype, chunk, path, max_chunks(B, T, num_seqs, varlen, chunk), H);
   // the plans with and without the output epilogue differ: room for either
   auto seg_bytes = [&](bool single) {
     return std::max(seg_ws_layout(B, T, H, num_seqs, varlen, single, false).total,
@@ -1125,8 +1125,7 @@ hipError_t launch_prefill(int dtype, int chunk, const void* q, const void* k, co
                           const int32_t* cu_seqlens, int num_seqs, void* o, float* final_state, int B,
                           int T, int H, const Fusion& fusion, void* workspace, hipStream_t stream) {
   const bool varlen = cu_seqlens != nullptr;
-  const int kern = prefill_kernels(dtype, chunk, fusion.prefill_path, max_chunks(B, T, num_seqs, varlen, chunk),
-                                   varlen ? num_seqs : B);
+  const int kern = prefill_kernels(dtype, chunk, fusion.prefill_path, max_chunks(B, T, num_seqs, varlen, chunk), H);
   if (kern == KERNELS_SINGLE)
     return launch_prefill_seg(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, o, final_state, B, T,
                               H, fusion, workspace, stream);

@@ -180,7 +180,8 @@ typedef struct kda_fusion {
  * Which kernels a prefill runs (kda_fusion.prefill_path). Only bf16 with 64-token
  * chunks has a choice; every other dtype and chunk runs the record path.
  *   KDA_PATH_AUTO         an intra-chunk kernel writes a record per (chunk, head); when
- *                         sequences average at least 96 chunks (6144 tokens) the
+ *                         the call has at least 4096 (chunk, head) pairs (counting the
+ *                         chunk bound ceil(T / 64) + num_seqs of a packed batch) the
  *                         segment-parallel full-width state kernels read each record
  *                         once per sequence segment, otherwise the KDA_PATH_RECORD state
  *                         kernels run (the default; the faster of the two at each size)

@@ -140,6 +140,14 @@ def test_workspace_size():
     assert record_ws(*big) < ws(*big) < record_ws(*big) + single_ws(*big) + 4096
     assert single_ws(*big) < 64 * 2**20 < record_ws(*big)
     assert single_ws(*big) <= single_ws(1, 8192, 32, 0, 64, 0) * 1.5
+    # the automatic choice: the segment-parallel kernels from 4096 (chunk, head) pairs,
+    # whatever the sequence length (the chunk bound of a packed batch counts)
+    seg = lambda *a: path_ws(kda.KDA_PATH_RECORD_SEGMENTED, *a)  # noqa: E731
+    for shape in ((1, 4096, 32, 0, 64, 0), (1, 8192, 16, 0, 64, 0), (1, 4096, 16, 0, 64, 0), (2, 4096, 16, 0, 64, 0)):
+        assert ws(*shape) == record_ws(*shape) < seg(*shape)
+    for shape in ((2, 4096, 32, 0, 64, 0), (8, 4096, 32, 0, 64, 0), (1024, 64, 32, 0, 64, 0), (1, 8192, 32, 0, 64, 0),
+                  (1, 32768, 32, 4, 64, 0), (1, 4000, 32, 100, 64, 0)):
+        assert ws(*shape) == seg(*shape) > record_ws(*shape)
     # a varlen query bounds every split of the same tokens
     for path in (kda.KDA_PATH_AUTO, kda.KDA_PATH_RECORD, kda.KDA_PATH_SINGLE_PASS, kda.KDA_PATH_RECORD_SEGMENTED):
         assert path_ws(path, 1, 32768, 32, 4, 64, 0) >= path_ws(path, 1, 32768, 32, 0, 64, 0)
