@@ -236,9 +236,9 @@ template <typename E, int C, int GATE>
 __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const float* __restrict__ log_alpha,
                                                     const float* __restrict__ beta,
-                                                    const int32_t* __restrict__ total_chunks,
-                                                    const int2* __restrict__ info, int H, int mc,
-                                                    char* __restrict__ records, Fusion fu) {
+                                                    int32_t* __restrict__ chunk_off, int2* __restrict__ info,
+                                                    int N, int uni_T, int H, int mc, char* __restrict__ records,
+                                                    Fusion fu) {
   using SM = Smem<E, C>;
   using RC = Rec<E, C>;
   typedef typename Frag<E>::T FragT;
@@ -265,12 +265,29 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
   // heads vary fastest over the work-group ids: the work-groups in flight together
   // cover whole token rows of q, k, v and the gates, not one head's 256-byte pieces
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
-  if (c >= *total_chunks) return;
   const int t = threadIdx.x;
+  int tok0, len;
+  if (uni_T > 0) {
+    // N sequences of uni_T tokens, no plan kernel: the chunk table is arithmetic (the
+    // grid covers it exactly), and head 0's work-groups write it for the state kernels
+    // that run after this one
+    const int ncs = (uni_T + C - 1) / C;
+    const int n = c / ncs, jc = c - n * ncs;
+    tok0 = n * uni_T + jc * C;
+    len = min(C, uni_T - jc * C);
+    if (h == 0 && t == 0) {
+      info[c] = make_int2(tok0, len);
+      if (jc == 0) chunk_off[n] = c;
+      if (c == 0) chunk_off[N] = N * ncs;
+    }
+  } else {
+    if (c >= chunk_off[N]) return;
+    const int2 inf = info[c];
+    tok0 = inf.x;
+    len = inf.y;
+  }
   const int lane = t & 63, w = t >> 6, m = lane & 15, g = lane >> 4;
   const int cq = t & 31, ch0 = 4 * cq, rbase = t >> 5;
-  const int2 inf = info[c];
-  const int tok0 = inf.x, len = inf.y;
   const size_t HD = (size_t)H * D;
   char* rec_base = records + ((size_t)h * mc + c) * RC::BYTES;  // head-major: a head's chunks are contiguous
   E* rec = reinterpret_cast<E*>(rec_base);
@@ -1055,17 +1072,24 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const float
   char* records = ws + l.off_records;
   trace_begin(stream);
   const int total_tokens = cu_seqlens ? T : N * T;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, total_tokens, C, (int)mc,
-                     chunk_off, info);
-  hipError_t e = hipGetLastError();
-  trace_mark(stream, 0);
-  if (e != hipSuccess) return e;
+  // A batch of equal sequences needs no plan kernel: the intra-chunk kernel writes the
+  // chunk table itself (uni_T). Packed sequences, and calls with no chunks (whose state
+  // kernels still read the table), run the plan first.
+  const int uni_T = (!cu_seqlens && mc > 0) ? T : 0;
+  hipError_t e = hipSuccess;
+  if (uni_T == 0) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, T, total_tokens, C, (int)mc,
+                       chunk_off, info);
+    e = hipGetLastError();
+    trace_mark(stream, 0);
+    if (e != hipSuccess) return e;
+  }
   if (mc > 0) {
     auto* kern = fusion.gate_kind == GATE_HEAD   ? intra_kernel<E, C, GATE_HEAD>
                  : fusion.gate_kind == GATE_NONE ? intra_kernel<E, C, GATE_NONE>
                                                  : intra_kernel<E, C, GATE_CHANNEL>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(mc * H)), dim3(256), 0, stream, (const E*)q, (const E*)k,
-                       (const E*)v, log_alpha, beta, chunk_off + N, info, H, (int)mc, records, fusion);
+                       (const E*)v, log_alpha, beta, chunk_off, info, N, uni_T, H, (int)mc, records, fusion);
     e = hipGetLastError();
     trace_mark(stream, 1);
     if (e != hipSuccess) return e;
