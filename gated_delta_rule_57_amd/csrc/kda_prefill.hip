@@ -544,9 +544,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
         rk[j] = from_f<E>(kr[i][j] * fast_exp2(-gh));  // <= 2^96 |k|
       }
       *reinterpret_cast<V4*>(sRK + r * LD + ch0) = rk;
-      const int kb = ch0 >> 5, co = ch0 & 31;
-      const int fg = (co & 15) >> 2, fh = co >> 4;
-      store4f(rec + RC::QT + ((size_t)((r >> 4) * 4 + kb) * 64 + (r & 15) + 16 * fg) * 8 + 4 * fh, qt);
     }
     __syncthreads();  // every thread has its decays; the left operands overwrite the cumsum
 #pragma unroll
@@ -583,6 +580,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const E* __restrict__ q, con
         }
         mma(accA[bi], rhs, lk);
         mma(accP[bi], rhs, lq);
+        // lq is Q e^G of row tile I, k-block kb in the record's slot order: the wave
+        // with the tile's J = 0 block stores it, 1 KiB contiguous per instruction
+        if (J == 0) store_frag<E>(rec + RC::QT + ((size_t)(I * 4 + kb) * 64 + lane) * 8, lq);
       }
       emit_p(I, J, accP[bi]);
     }
