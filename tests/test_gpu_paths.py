@@ -185,3 +185,23 @@ def test_many_sequences_other_kernels(dtype, chunk):
     inp = inputs.make_prefill(62, B=1, T=int(cu[-1]), H=2, dtype=dtype, chunk=chunk, la_scale=0.3, s0_std=0.2,
                               cu_seqlens=cu)
     compare_prefill(inp, label=f"many-seqs {dtype} C={chunk}")
+
+
+@pytest.mark.parametrize("path", PATHS + ["auto"])
+def test_workspace_shared_by_uniform_and_packed_calls(path):
+    """One workspace for a batch of equal sequences (whose chunk table the intra-chunk
+    kernel writes) and then a packed batch (whose table the plan kernel writes), and
+    back: every call matches the oracle."""
+    uni = inputs.make_prefill(71, B=3, T=300, H=2, dtype="bf16", la_scale=0.3, s0_std=0.2)
+    cu = np.array([0, 70, 70, 300, 641], dtype=np.int64)
+    pk = inputs.make_prefill(72, B=1, T=641, H=2, dtype="bf16", la_scale=0.3, s0_std=0.2, cu_seqlens=cu)
+    n = max(kda.workspace_size(3, 300, 2, 0, 64, kda.KDA_BF16, path=path),
+            kda.workspace_size(1, 641, 2, 4, 64, kda.KDA_BF16, path=path))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for inp, label in ((uni, "uniform"), (pk, "packed"), (uni, "uniform again")):
+        say(f"[paths] shared workspace {label} path={path}")
+        o, fin = run(inp, path, workspace=ws)
+        o_ref, f_ref = oracle_prefill(inp)
+        eo, ef = normwise(o.float().cpu().numpy(), o_ref), normwise(fin.cpu().numpy(), f_ref)
+        say(f"[paths] shared workspace {label} path={path}: err_o={eo:.3e} err_state={ef:.3e}")
+        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
